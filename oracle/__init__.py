@@ -1,0 +1,101 @@
+"""Oracle: plain CPU reference implementations of the tiled GEMM and of the
+layout algebra that describes its operand storage.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  It shares
+no code with the HIP library and never imports it; the two meet only through
+the seeded inputs the callers pass to both.
+
+* ``gemm_f64``  -- FP64 triple loop (C, OpenMP over rows), see ``gemm_f64.c``.
+* ``layout_ref`` -- the layout algebra written out by enumeration in Python.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import layout_ref  # noqa: F401  (re-exported for the tests)
+
+BF16 = 0
+F16 = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    from .build import LIB, build
+    if not os.path.exists(LIB):
+        build()
+    lib = ctypes.CDLL(LIB)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.oracle_gemm_f64.argtypes = [i64, i64, i64, vp, ctypes.c_int, i64, vp, ctypes.c_int, i64,
+                                    vp, i64, ctypes.c_double, ctypes.c_double, vp, i64, ctypes.c_int]
+    lib.oracle_gemm_f64.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [vp, ctypes.c_int, i64, vp]
+    lib.oracle_decode.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _type_code(kind: str) -> int:
+    if kind == "bf16":
+        return BF16
+    if kind == "f16":
+        return F16
+    raise ValueError("oracle inputs are 16-bit patterns of kind 'bf16' or 'f16', got %r" % (kind,))
+
+
+def _as_u16(x) -> np.ndarray:
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.uint16:
+        raise TypeError("pass raw 16-bit patterns as a uint16 array, got %s" % a.dtype)
+    return a
+
+
+def decode(bits, kind: str) -> np.ndarray:
+    """Exact float64 values of 16-bit patterns of the given format."""
+    b = _as_u16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode(b.ctypes.data, _type_code(kind), b.size, out.ctypes.data)
+    return out
+
+
+def gemm_f64(a_bits, a_kind, b_bits, b_kind, alpha=1.0, beta=0.0, c=None, nthreads=0):
+    """out = alpha * A @ B + beta * C in FP64 (k ascending), from 16-bit patterns.
+
+    ``a_bits`` is (M, K) uint16, ``b_bits`` is (K, N) uint16 (N contiguous),
+    ``c`` is (M, N) float32 or None (only read when beta != 0).
+    Returns an (M, N) float64 array.
+    """
+    a = _as_u16(a_bits)
+    b = _as_u16(b_bits)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("shape mismatch: A %s, B %s" % (a.shape, b.shape))
+    M, K = a.shape
+    N = b.shape[1]
+    out = np.empty((M, N), dtype=np.float64)
+    cptr, ldc = None, max(N, 1)
+    if beta != 0.0:
+        if c is None:
+            raise ValueError("beta != 0 needs the existing C")
+        cc = np.ascontiguousarray(c, dtype=np.float32)
+        if cc.shape != (M, N):
+            raise ValueError("C shape %s, expected %s" % (cc.shape, (M, N)))
+        cptr = cc.ctypes.data
+    rc = _load().oracle_gemm_f64(M, N, K, a.ctypes.data, _type_code(a_kind), max(K, 1),
+                                 b.ctypes.data, _type_code(b_kind), max(N, 1),
+                                 cptr, ldc, float(alpha), float(beta),
+                                 out.ctypes.data, max(N, 1), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_f64 failed (rc=%d)" % rc)
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())

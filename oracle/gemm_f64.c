@@ -1,0 +1,132 @@
+/*
+ * Oracle for the tiled GEMM: a plain, slow FP64 triple loop on the CPU.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header, table or constant with
+ * the HIP library.
+ *
+ * What it computes (for 0 <= i < M, 0 <= j < N):
+ *
+ *     out[i,j] = alpha * sum_{k=0}^{K-1} a(i,k) * b(k,j)  +  beta * c(i,j)
+ *
+ * with every product and partial sum in IEEE binary64, k ascending, a(i,k)
+ * and b(k,j) the exact values of the 16-bit input patterns, and c(i,j) the
+ * FP32 value of the existing output.  The beta term is left out entirely when
+ * beta == 0 (the existing output is then never read, so NaN there cannot leak
+ * in).  This is the epilogue form "alpha * accumulator + beta * old C" of the
+ * Phobos page "Tiles and shared memory" (section "var and let") and the
+ * scaling epilogue of the Tylo.jl page "Layouts, storage and ownership"
+ * (section "Plans describe work, callers establish readiness"), over an
+ * accumulator that is the plain dot product of row i of A and column j of B.
+ *
+ * Storage: A is row-major with row stride lda (element (i,k) at i*lda + k);
+ * B is K-outer/N-inner with row stride ldb (element (k,j) at k*ldb + j);
+ * C and out are row-major with strides ldc and ldo.
+ *
+ * The 16-bit decoders below are written from the formats' definitions:
+ *   bfloat16 = the upper half of an IEEE binary32 pattern;
+ *   binary16 = 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits,
+ *              subnormals scaled by 2^-24, exponent 31 = Inf/NaN.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_BF16 0
+#define ORACLE_F16 1
+
+double oracle_bf16_to_f64(uint16_t bits) {
+  uint32_t word = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &word, sizeof f);
+  return (double)f;
+}
+
+double oracle_f16_to_f64(uint16_t bits) {
+  int sign = (bits >> 15) & 1;
+  int expo = (bits >> 10) & 0x1f;
+  int frac = bits & 0x3ff;
+  double mag;
+  if (expo == 0) {
+    mag = ldexp((double)frac, -24);               /* zero or subnormal */
+  } else if (expo == 31) {
+    mag = frac ? NAN : INFINITY;
+  } else {
+    mag = ldexp((double)(frac | 0x400), expo - 25); /* (1 + f/1024) * 2^(e-15) */
+  }
+  return sign ? -mag : mag;
+}
+
+static double decode(uint16_t bits, int type) {
+  return type == ORACLE_BF16 ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);
+}
+
+/* Decode n 16-bit patterns (test helper: lets the suite compare the decoders
+ * with other implementations of the same formats). */
+void oracle_decode(const uint16_t* src, int type, int64_t n, double* dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = decode(src[i], type);
+}
+
+/*
+ * Returns 0 on success, -1 on a bad argument.  nthreads <= 0 lets OpenMP pick.
+ * C may be NULL when beta == 0.
+ */
+int oracle_gemm_f64(int64_t M, int64_t N, int64_t K,
+                    const uint16_t* A, int a_type, int64_t lda,
+                    const uint16_t* B, int b_type, int64_t ldb,
+                    const float* C, int64_t ldc,
+                    double alpha, double beta,
+                    double* out, int64_t ldo, int nthreads) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  if ((a_type != ORACLE_BF16 && a_type != ORACLE_F16) ||
+      (b_type != ORACLE_BF16 && b_type != ORACLE_F16)) return -1;
+  if (beta != 0.0 && C == NULL && M > 0 && N > 0) return -1;
+  if (M == 0 || N == 0) return 0;
+
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* acc = (double*)malloc((size_t)N * sizeof(double));
+    if (!acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const double a = decode(A[i * lda + k], a_type);
+          const uint16_t* brow = B + k * ldb;
+          for (int64_t j = 0; j < N; ++j) acc[j] += a * decode(brow[j], b_type);
+        }
+        for (int64_t j = 0; j < N; ++j) {
+          double v = alpha * acc[j];
+          if (beta != 0.0) v += beta * (double)C[i * ldc + j];
+          out[i * ldo + j] = v;
+        }
+      }
+      free(acc);
+    }
+  }
+  return failed ? -1 : 0;
+}
+
+/* Threads an OpenMP parallel region would use (reported with timings). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

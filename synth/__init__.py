@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module only draws random numbers and names shapes; it holds none of the
+method's arithmetic.  Both the HIP path (through its callers) and the oracle
+receive the very same 16-bit patterns produced here.
+
+Recipe: values are sampled in float32 on the CPU with a seeded
+``torch.Generator`` (uniform via ``rand``, normal via ``randn`` scaled by the
+standard deviation) and rounded once to bf16/fp16 with torch's
+round-to-nearest-even conversion.
+"""
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def torch_dtype(kind: str) -> torch.dtype:
+    return _TORCH[kind]
+
+
+@dataclass(frozen=True)
+class Dist:
+    kind: str          # "uniform" or "normal"
+    a: float           # uniform: low;  normal: mean
+    b: float           # uniform: high; normal: standard deviation
+
+    def sample(self, shape, seed: int, dtype: torch.dtype) -> torch.Tensor:
+        g = torch.Generator().manual_seed(int(seed))
+        if self.kind == "uniform":
+            x = torch.rand(shape, generator=g, dtype=torch.float32) * (self.b - self.a) + self.a
+        elif self.kind == "normal":
+            x = torch.randn(shape, generator=g, dtype=torch.float32) * self.b + self.a
+        else:
+            raise ValueError(self.kind)
+        return x.to(dtype)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    in_kind: str                 # "bf16" or "f16"
+    out_kind: str                # "f32" or "bf16"
+    alpha: float
+    beta: float
+    dist_a: Dist
+    dist_b: Dist
+    seeds: tuple
+    dist_c: Dist = None          # existing C when beta != 0
+    gate_up: bool = False
+    notes: str = ""
+    extra: dict = field(default_factory=dict)
+
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K * (2 if self.gate_up else 1)
+
+
+WORKLOADS = {
+    "square256": Workload(
+        "square256", 256, 256, 256, "bf16", "f32", 1.0, 0.0,
+        Dist("uniform", -1.0, 1.0), Dist("uniform", -1.0, 1.0), (1001, 1002),
+        notes="single 256^3 GEMM, bf16 in, fp32 out"),
+    "square4096": Workload(
+        "square4096", 4096, 4096, 4096, "bf16", "bf16", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0 / math.sqrt(4096)), Dist("normal", 0.0, 1.0 / math.sqrt(4096)),
+        (2001, 2002), notes="4096^3 GEMM, bf16 in, bf16 out"),
+    "ragged": Workload(
+        "ragged", 1000, 1537, 999, "f16", "f32", 1.5, -0.5,
+        Dist("uniform", -2.0, 2.0), Dist("uniform", -2.0, 2.0), (3001, 3002, 3003),
+        dist_c=Dist("uniform", -1.0, 1.0), notes="ragged edges, in-place fp32 C"),
+    "gate_up": Workload(
+        "gate_up", 4096, 11008, 4096, "bf16", "bf16", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (4001, 4002, 4003),
+        gate_up=True, notes="x[4096,4096] times W_gate and W_up [4096,11008]"),
+    "skinny": Workload(
+        "skinny", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5001, 5002, 5003),
+        notes="M=16 bandwidth-bound GEMM"),
+}
+
+
+def make_inputs(w: Workload):
+    """CPU tensors: dict with A [M,K], B [K,N] (N contiguous) or Wg/Wu, and C_in."""
+    dt = torch_dtype(w.in_kind)
+    out = {"A": w.dist_a.sample((w.M, w.K), w.seeds[0], dt)}
+    if w.gate_up:
+        out["Wg"] = w.dist_b.sample((w.K, w.N), w.seeds[1], dt)
+        out["Wu"] = w.dist_b.sample((w.K, w.N), w.seeds[2], dt)
+    else:
+        out["B"] = w.dist_b.sample((w.K, w.N), w.seeds[1], dt)
+    if w.dist_c is not None:
+        out["C"] = w.dist_c.sample((w.M, w.N), w.seeds[2], torch.float32)
+    return out
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit patterns of a CPU bf16/fp16 tensor as a uint16 numpy array."""
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(t.dtype)
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def uniform(shape, seed, kind, lo=-1.0, hi=1.0):
+    return Dist("uniform", lo, hi).sample(shape, seed, torch_dtype(kind))
+
+
+def normal(shape, seed, kind, std=1.0):
+    return Dist("normal", 0.0, std).sample(shape, seed, torch_dtype(kind))

@@ -1,0 +1,168 @@
+"""Pins for the FP64 oracle GEMM (oracle/gemm_f64.c).
+
+The oracle is checked against things it does not compute itself:
+  * torch's and numpy's own bf16/fp16 decoding, for all 65,536 patterns;
+  * exact rational arithmetic (fractions) on tiny shapes;
+  * closed forms: ones x ones = K, identity and permutation B, alpha = 0;
+  * numpy's float64 matmul (a library routine) on moderate shapes.
+A dropped term, a transposed operand, a wrong stride or a wrong sign in the
+epilogue fails at least one of these.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def _bits_all():
+    return np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+def test_decode_bf16_exhaustive():
+    b = _bits_all()
+    mine = oracle.decode(b, "bf16")
+    ref = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def test_decode_f16_exhaustive():
+    b = _bits_all()
+    mine = oracle.decode(b, "f16")
+    ref = b.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def _exact(a_t, b_t, alpha, beta, c):
+    """Exact rational alpha*A@B + beta*C from torch's decoding."""
+    A = [[Fraction(float(v)) for v in row] for row in a_t.to(torch.float64).tolist()]
+    B = [[Fraction(float(v)) for v in row] for row in b_t.to(torch.float64).tolist()]
+    M, K, N = len(A), len(B), len(B[0]) if B else 0
+    al, be = Fraction(float(alpha)), Fraction(float(beta))
+    out, mag = [], []
+    for i in range(M):
+        row, mrow = [], []
+        for j in range(N):
+            s = sum((A[i][k] * B[k][j] for k in range(K)), Fraction(0))
+            m = sum((abs(A[i][k] * B[k][j]) for k in range(K)), Fraction(0))
+            v = al * s
+            mm = abs(al) * m
+            if beta != 0:
+                cv = Fraction(float(c[i, j]))
+                v += be * cv
+                mm += abs(be * cv)
+            row.append(v)
+            mrow.append(mm)
+        out.append(row)
+        mag.append(mrow)
+    return out, mag
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+def test_exact_rational_tiny_shapes(kind):
+    seed = 100
+    for M in range(1, 5):
+        for N in range(1, 5):
+            for K in range(1, 5):
+                seed += 1
+                a = synth.uniform((M, K), seed, kind, -2.0, 2.0)
+                b = synth.uniform((K, N), seed + 5000, kind, -2.0, 2.0)
+                c = synth.uniform((M, N), seed + 9000, "f32")
+                alpha = float(np.float32(1.0 + 0.37 * (seed % 5)))
+                beta = float(np.float32(-0.5 + 0.25 * (seed % 3)))
+                got = oracle.gemm_f64(synth.bits(a), kind, synth.bits(b), kind, alpha, beta, c.numpy())
+                exact, mag = _exact(a, b, alpha, beta, c.numpy())
+                for i in range(M):
+                    for j in range(N):
+                        bound = float(mag[i][j]) * (K + 3) * 2.0 ** -53
+                        assert abs(got[i, j] - float(exact[i][j])) <= bound, (M, N, K, i, j)
+
+
+def test_exact_rational_odd_shapes_with_beta_zero():
+    for (M, N, K) in [(3, 7, 5), (7, 3, 9), (1, 9, 17)]:
+        a = synth.uniform((M, K), M * 100 + K, "bf16")
+        b = synth.uniform((K, N), N * 100 + K, "bf16")
+        got = oracle.gemm_f64(synth.bits(a), "bf16", synth.bits(b), "bf16", 1.0, 0.0)
+        exact, mag = _exact(a, b, 1.0, 0.0, None)
+        for i in range(M):
+            for j in range(N):
+                assert abs(got[i, j] - float(exact[i][j])) <= float(mag[i][j]) * (K + 3) * 2.0 ** -53
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+def test_ones_times_ones_is_K(kind):
+    for (M, N, K) in [(5, 7, 13), (3, 4, 4096)]:
+        a = torch.ones((M, K), dtype=synth.torch_dtype(kind))
+        b = torch.ones((K, N), dtype=synth.torch_dtype(kind))
+        got = oracle.gemm_f64(synth.bits(a), kind, synth.bits(b), kind)
+        assert np.all(got == K)
+
+
+def test_ones_A_gives_column_sums():
+    b = synth.uniform((33, 10), 77, "bf16")
+    a = torch.ones((4, 33), dtype=torch.bfloat16)
+    got = oracle.gemm_f64(synth.bits(a), "bf16", synth.bits(b), "bf16")
+    colsum = b.to(torch.float64).sum(dim=0).numpy()
+    np.testing.assert_allclose(got, np.broadcast_to(colsum, got.shape), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+def test_identity_and_permutation_B(kind):
+    K, M = 48, 20
+    a = synth.uniform((M, K), 5, kind)
+    eye = torch.eye(K, dtype=synth.torch_dtype(kind))
+    got = oracle.gemm_f64(synth.bits(a), kind, synth.bits(eye), kind)
+    assert np.array_equal(got, a.to(torch.float64).numpy())
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(9))
+    P = torch.zeros((K, K), dtype=synth.torch_dtype(kind))
+    P[perm, torch.arange(K)] = 1          # column j of A@P is column perm[j] of A
+    got = oracle.gemm_f64(synth.bits(a), kind, synth.bits(P), kind)
+    assert np.array_equal(got, a.to(torch.float64).numpy()[:, perm.numpy()])
+
+
+def test_alpha_beta_special_cases():
+    M, N, K = 9, 11, 13
+    a = synth.uniform((M, K), 1, "f16")
+    b = synth.uniform((K, N), 2, "f16")
+    c = synth.uniform((M, N), 3, "f32").numpy()
+    got = oracle.gemm_f64(synth.bits(a), "f16", synth.bits(b), "f16", 0.0, 1.0, c)
+    assert np.array_equal(got, c.astype(np.float64))
+    nan_c = np.full((M, N), np.nan, dtype=np.float32)
+    got = oracle.gemm_f64(synth.bits(a), "f16", synth.bits(b), "f16", 1.0, 0.0, nan_c)
+    assert np.all(np.isfinite(got))
+    # K = 0: the sum is empty
+    a0 = torch.zeros((M, 0), dtype=torch.float16)
+    b0 = torch.zeros((0, N), dtype=torch.float16)
+    got = oracle.gemm_f64(synth.bits(a0), "f16", synth.bits(b0), "f16", 2.0, -0.5, c)
+    assert np.array_equal(got, -0.5 * c.astype(np.float64))
+    # M = 0 / N = 0 are empty results
+    assert oracle.gemm_f64(synth.bits(a[:0]), "f16", synth.bits(b), "f16").shape == (0, N)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+def test_matches_numpy_float64_matmul(kind):
+    for (M, N, K), seed in [((37, 53, 129), 1), ((64, 80, 257), 2), ((5, 300, 64), 3)]:
+        a = synth.normal((M, K), seed, kind)
+        b = synth.normal((K, N), seed + 50, kind, 0.5)
+        c = synth.uniform((M, N), seed + 99, "f32").numpy()
+        got = oracle.gemm_f64(synth.bits(a), kind, synth.bits(b), kind, 1.5, -0.25, c)
+        ref = 1.5 * (a.to(torch.float64).numpy() @ b.to(torch.float64).numpy()) - 0.25 * c.astype(np.float64)
+        scale = 1.5 * (np.abs(a.to(torch.float64).numpy()) @ np.abs(b.to(torch.float64).numpy())) + 0.25 * np.abs(c)
+        assert np.all(np.abs(got - ref) <= scale * 1e-13)
+
+
+def test_thread_count_does_not_change_bits():
+    a = synth.normal((70, 300), 4, "bf16")
+    b = synth.normal((300, 90), 5, "bf16")
+    r1 = oracle.gemm_f64(synth.bits(a), "bf16", synth.bits(b), "bf16", nthreads=1)
+    r4 = oracle.gemm_f64(synth.bits(a), "bf16", synth.bits(b), "bf16", nthreads=4)
+    assert np.array_equal(r1, r4)
