@@ -1,0 +1,197 @@
+"""Benchmark of the tiled GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one GEMM (one launch of the library's kernel) over inputs already
+resident in HBM.  Prints ONE JSON line with the throughput, the roofline of
+the kernel (achieved vs peak, from HIP events around every launch) and the
+oracle's CPU throughput on a bounded sample of the same workload, whose
+output also cross-checks the sampled GPU rows.
+
+Workloads (seeded synthetic inputs, see synth/):
+  square4096  4096^3 bf16 -> bf16            (default; metric workload)
+  gate_up     x[4096,4096] @ W_gate, W_up [4096,11008] -> bf16
+  skinny      16 x 28672 x 8192 bf16 -> fp32 (HBM-bound; two B buffers rotate)
+  square256, ragged
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E
+METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
+
+
+def algorithmic_bytes(w):
+    """Compulsory HBM bytes of one step: every operand read once, C written (and read if beta != 0)."""
+    eb = 2
+    ob = 4 if w.out_kind == "f32" else 2
+    nb = 2 if w.gate_up else 1
+    b = w.M * w.K * eb + nb * w.K * w.N * eb + nb * w.M * w.N * ob
+    if w.beta != 0.0:
+        b += w.M * w.N * ob
+    return b
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (each output tile is "
+              "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import layout_algebra_amd as la
+    w = synth.WORKLOADS[args.workload]
+    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = synth.make_inputs(w)
+    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up)
+    A = x["A"].to(dev)
+    out_dt = synth.torch_dtype(w.out_kind)
+    if w.gate_up:
+        Wg, Wu = x["Wg"].to(dev), x["Wu"].to(dev)
+        G = torch.empty((w.M, w.N), dtype=out_dt, device=dev)
+        U = torch.empty_like(G)
+
+        def step(i):
+            la.gemm_gate_up_run(plan, A, Wg, Wu, G, U)
+        result = G
+        b_cpu = x["Wg"]
+    else:
+        Bs = [x["B"].to(dev)]
+        if w.name == "skinny":
+            # a second B buffer so consecutive steps do not hit B in the 256 MB last-level cache
+            Bs.append(synth.Dist("normal", 0.0, 0.02).sample((w.K, w.N), w.seeds[2], synth.torch_dtype(w.in_kind)).to(dev))
+        C0 = x["C"].to(dev) if "C" in x else None
+        C = torch.empty((w.M, w.N), dtype=out_dt, device=dev) if C0 is None else C0.clone()
+
+        def step(i):
+            la.gemm_run(plan, A, Bs[i % len(Bs)], C, w.alpha, w.beta)
+        result = C
+        b_cpu = x["B"]
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # parity of the timed launch configuration: run once on the first B, keep the result
+    if w.beta == 0.0:
+        step(0)
+        torch.cuda.synchronize()
+        check = result.detach().clone()
+    else:
+        check = None
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = total_ms / args.steps
+
+    flops = w.flops()
+    value_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    kern_ms = float(per_launch.mean())
+    if w.name == "skinny":
+        metric, unit = "achieved HBM GB/s, skinny 16x28672x8192 GEMM", "GB/s"
+        bytes_ = algorithmic_bytes(w)
+        value = bytes_ / (ms_per_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": bytes_ / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        metric, unit = (METRIC, "TFLOP/s") if w.name == "square4096" else ("TFLOP/s, %s GEMM" % w.name, "TFLOP/s")
+        value = value_tflops
+        roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[w.in_kind],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_avg_ms"] = kern_ms
+    roof["kernel_min_ms"] = float(per_launch.min())
+
+    line = {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "strong",
+        "vs_baseline": None, "dtype": w.in_kind, "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "out": w.out_kind,
+                   "alpha": w.alpha, "beta": w.beta, "gate_up": w.gate_up,
+                   "kernel": plan.describe()["kernel"], "grid": plan.describe()["grid"]},
+        "roofline": roof,
+        "wall_s_timed": wall,
+        "tflops": value_tflops,
+        "pct_of_bf16_peak": 100.0 * value_tflops / PEAK_TFLOPS[w.in_kind],
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):
+    """Time the oracle (as it is) on the first R output rows; R sized to ~budget_s."""
+    import oracle
+    threads = oracle.max_threads()
+    a = x["A"]
+    t0 = time.perf_counter()
+    probe_rows = list(range(min(4, w.M)))
+    oracle.gemm_f64(synth.bits(a[probe_rows]), w.in_kind, synth.bits(b_cpu), w.in_kind)
+    per_row = (time.perf_counter() - t0) / len(probe_rows)
+    R = int(max(len(probe_rows), min(w.M, budget_s / max(per_row, 1e-9))))
+    rows = list(range(R))
+    c_in = x["C"][rows].numpy() if "C" in x else None
+    t0 = time.perf_counter()
+    ref = oracle.gemm_f64(synth.bits(a[rows]), w.in_kind, synth.bits(b_cpu), w.in_kind, w.alpha, w.beta, c_in)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * R * w.N * w.K
+    if unit == "GB/s":
+        bytes_ = (R * w.K + w.K * w.N) * 2 + R * w.N * 4
+        value = bytes_ / dt / 1e9
+    else:
+        value = flops / dt / 1e12
+    base = {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": "output rows 0..%d of %d (%d x %d outputs, K=%d%s), FP64 triple loop, %.1f s"
+                      % (R - 1, w.M, R, w.N, w.K, ", W_gate product only" if w.gate_up else "", dt),
+            "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
+    parity = None
+    if check is not None:
+        got = check[:R].to("cpu", torch.float64).numpy()
+        tol = 2.0 ** -20 * w.K * float(a.abs().max()) * float(b_cpu.abs().max()) + \
+            {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}[w.out_kind] * np.abs(ref)
+        err = np.abs(got - ref)
+        parity = {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol))}
+    return base, parity
+
+
+if __name__ == "__main__":
+    main()

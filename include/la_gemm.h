@@ -1,0 +1,148 @@
+/*
+ * la_gemm.h -- C ABI of the MI355X (gfx950) tiled GEMM library.
+ *
+ * One operation: C = alpha * A * B + beta * C with bf16 or fp16 inputs and
+ * FP32 accumulation, plus a fused gate/up variant that multiplies one
+ * activation matrix by two weight matrices.  The epilogue form follows the
+ * Phobos page "Tiles and shared memory" (section "var and let": new C is
+ * alpha times the accumulator plus beta times the old C) and the Tylo.jl page
+ * "Layouts, storage and ownership" (section "Plans describe work, callers
+ * establish readiness": scaling is composed into the epilogue, no separate
+ * kernel).  The fused gate/up projection is the consumer named on the Tylo.jl
+ * page "TMA and Hopper WGMMA" (opening paragraph and section "Worked
+ * consumers and current validation").
+ *
+ * Storage (all row-major, element strides, zero-based, as on the Tylo.jl page
+ * "Layouts, storage and ownership", section "A layout is a function"):
+ *   A  [M, K]  element (i, k) at A[i * lda + k]          (K contiguous)
+ *   B  [K, N]  element (k, j) at B[k * ldb + j]          (N contiguous)
+ *   C  [M, N]  element (i, j) at C[i * ldc + j]
+ * B is addressed in its mathematical (K, N) coordinates throughout.
+ *
+ * Ownership and lifetime (Tylo.jl "TMEM tiles and transfers", section
+ * "Completion and validation"; "Layouts, storage and ownership", section
+ * "Plans describe work, callers establish readiness"): the caller owns every
+ * buffer, its size, its lifetime and its reuse.  A plan is an immutable host
+ * object describing the work; it never touches device memory.  Device
+ * pointers are passed per run, so one plan serves any number of runs with
+ * changed values or other buffers of the same shape.
+ *
+ * Errors: every entry point returns a gemm_status.  On an error nothing is
+ * launched and nothing is written.  Requests the kernels do not support are
+ * rejected, never silently routed elsewhere (Tylo.jl "TMEM tiles and
+ * transfers", section "Storage units": no silent substitution of another
+ * instruction).  gemm_last_error() gives a thread-local description of the
+ * most recent failure.  Device faults surface at the caller's next
+ * synchronisation, as with any asynchronous launch.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Runs are asynchronous, never allocate, never synchronise and
+ * never read device memory on the host, so they may be captured in a HIP
+ * graph.
+ */
+#ifndef LA_GEMM_H
+#define LA_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_NULL = 1,          /* a required pointer argument is NULL */
+  GEMM_ERR_INVALID_ARG = 2,   /* negative size, leading dimension too small, bad enum */
+  GEMM_ERR_UNSUPPORTED = 3,   /* a well-formed request no kernel implements */
+  GEMM_ERR_ALIGNMENT = 4,     /* a pointer breaks the plan's alignment class */
+  GEMM_ERR_RESOURCE = 5,      /* a layout or tile would not fit (e.g. LDS) */
+  GEMM_ERR_HIP = 6            /* the HIP runtime reported an error */
+} gemm_status;
+
+typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
+
+/* Flags for gemm_desc.flags. */
+#define GEMM_FLAG_GATE_UP 0x1u   /* plan is for gemm_gate_up_run */
+
+typedef struct {
+  int64_t m, n, k;             /* problem sizes, each >= 0 */
+  int32_t a_type, b_type;      /* gemm_dtype; equal, BF16 or F16 */
+  int32_t c_type;              /* gemm_dtype of C (and of G, U): F32, BF16 or F16 */
+  int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k), ldb >= max(1,n), ldc >= max(1,n) */
+  uint32_t flags;              /* GEMM_FLAG_* */
+} gemm_desc;
+
+typedef struct gemm_plan_s* gemm_plan_t;   /* opaque, immutable, host-only */
+
+/* Validate `desc`, choose a kernel configuration and build its layouts.
+ * On success *out_plan owns a new plan (free with gemm_plan_destroy). */
+gemm_status gemm_plan(const gemm_desc* desc, gemm_plan_t* out_plan);
+
+/* Release a plan.  NULL is ignored.  Runs already enqueued are unaffected. */
+void gemm_plan_destroy(gemm_plan_t plan);
+
+/* C = alpha * A * B + beta * C on `stream`.
+ * A, B, C are device pointers laid out as described above; A and B must be
+ * aligned to the plan's alignment class (see gemm_plan_describe); C may be
+ * read (beta != 0) and written only inside [0,m) x [0,n).  When beta == 0, C
+ * is not read (NaN there does not propagate).  k == 0 gives C = beta * C.
+ * m == 0 or n == 0 launches nothing.  Outputs are rounded to nearest even. */
+gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
+                     float alpha, float beta, void* stream);
+
+/* G = X * W_gate and U = X * W_up (alpha = 1, beta = 0) in one launch that
+ * stages each X tile once for both products.  Needs a plan made with
+ * GEMM_FLAG_GATE_UP; X is [m, k] (lda), W_gate and W_up are [k, n] (ldb),
+ * G and U are [m, n] (ldc). */
+gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate,
+                             const void* W_up, void* G, void* U, void* stream);
+
+/* JSON description of the plan (kernel, tile sizes, grid, LDS layouts and
+ * swizzle, alignment class).  Writes at most len bytes including the NUL;
+ * returns GEMM_ERR_RESOURCE if it did not fit. */
+gemm_status gemm_plan_describe(gemm_plan_t plan, char* buf, size_t len);
+
+/* Element offset, inside one LDS pipeline stage, at which the plan's kernel
+ * stores operand element (row, col) of a tile.  operand 0 = A with (row, col)
+ * = (m, k) inside the tile; operand 1 = B (and W_gate) with (row, col) = (k, n);
+ * operand 2 = W_up.  Host-only; used to check the kernel's LDS image. */
+gemm_status gemm_plan_lds_offset(gemm_plan_t plan, int operand, int64_t row, int64_t col,
+                                 int64_t* out_elem_offset);
+
+/* Debug: copy tile (tile_m, tile_n) of stage 0 -- the first K block -- of the
+ * plan's kernel LDS image to `out` (device memory of at least
+ * gemm_plan_lds_stage_bytes bytes), using the kernel's own staging code.
+ * A, B (and B2 for gate/up plans, else NULL) are as for a run. */
+gemm_status gemm_debug_lds_image(gemm_plan_t plan, const void* A, const void* B, const void* B2,
+                                 int64_t tile_m, int64_t tile_n, void* out, void* stream);
+gemm_status gemm_plan_lds_stage_bytes(gemm_plan_t plan, int64_t* out_bytes);
+
+/* ---- layout algebra, host only (Tylo.jl "Layouts, storage and ownership") ----
+ * Shapes and strides are flat arrays of `rank` int64 values (one mode each).
+ * la_layout_eval: offset of the zero-based coordinate `coord` (rank values),
+ *   "A layout is a function".
+ * la_layout_eval_index: offset of integer index `idx`, split first mode
+ *   fastest over the flat modes.
+ * la_swizzle_apply: Swizzle{B,M,S} of an element offset, section "Swizzle phase
+ *   belongs to the allocation"; GEMM_ERR_INVALID_ARG if the fields overlap.
+ * la_tile_plan_offset: shared-tile plan of the Tylo.jl page "TMA and Hopper
+ *   WGMMA" (section "The same storage contract on both sides"): element size
+ *   1/2/4 bytes, tile (d1, d2), inner axis 1 or 2, swizzle row 128/64/32 bytes;
+ *   returns the swizzled element offset of (c1, c2) and the transfer bytes. */
+gemm_status la_layout_eval(const int64_t* shape, const int64_t* stride, int rank,
+                           const int64_t* coord, int64_t* out_offset);
+gemm_status la_layout_eval_index(const int64_t* shape, const int64_t* stride, int rank,
+                                 int64_t idx, int64_t* out_offset);
+gemm_status la_swizzle_apply(int b, int m, int s, int64_t offset, int64_t* out_offset);
+gemm_status la_tile_plan_offset(int elem_bytes, int64_t d1, int64_t d2, int inner_axis,
+                                int row_bytes, int64_t c1, int64_t c2,
+                                int64_t* out_offset, int64_t* out_transfer_bytes);
+
+const char* gemm_status_string(gemm_status s);
+const char* gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LA_GEMM_H */

@@ -1,0 +1,222 @@
+"""ctypes marshalling for liblagemm.so (see include/la_gemm.h for contracts)."""
+import ctypes
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liblagemm.so")
+
+BF16, F16, F32 = 0, 1, 2
+FLAG_GATE_UP = 0x1
+
+EXPORTED_SYMBOLS = (
+    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_gate_up_run", "gemm_plan_describe",
+    "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
+    "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
+    "gemm_status_string", "gemm_last_error",
+)
+
+STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_NULL", 2: "GEMM_ERR_INVALID_ARG", 3: "GEMM_ERR_UNSUPPORTED",
+          4: "GEMM_ERR_ALIGNMENT", 5: "GEMM_ERR_RESOURCE", 6: "GEMM_ERR_HIP"}
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (STATUS.get(status, status), msg))
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32), ("c_type", ctypes.c_int32),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+                ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load():
+    """Load liblagemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("liblagemm.so is not built (run __graft_entry__.build() or "
+                           "python layout_algebra_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "gemm_plan": ([ctypes.POINTER(_Desc), ctypes.POINTER(vp)], i32),
+        "gemm_plan_destroy": ([vp], None),
+        "gemm_run": ([vp, vp, vp, vp, f32, f32, vp], i32),
+        "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
+        "gemm_plan_describe": ([vp, ctypes.c_char_p, ctypes.c_size_t], i32),
+        "gemm_plan_lds_offset": ([vp, i32, i64, i64, p64], i32),
+        "gemm_plan_lds_stage_bytes": ([vp, p64], i32),
+        "gemm_debug_lds_image": ([vp, vp, vp, vp, i64, i64, vp, vp], i32),
+        "la_layout_eval": ([p64, p64, i32, p64, p64], i32),
+        "la_layout_eval_index": ([p64, p64, i32, i64, p64], i32),
+        "la_swizzle_apply": ([i32, i32, i32, i64, p64], i32),
+        "la_tile_plan_offset": ([i32, i64, i64, i32, i32, i64, i64, p64, p64], i32),
+        "gemm_status_string": ([i32], ctypes.c_char_p),
+        "gemm_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise GemmError(rc, load().gemm_last_error().decode())
+
+
+def _i64s(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
+# ------------------------------------------------------------------ plans
+class Plan:
+    """Owns a gemm_plan_t.  Immutable; reusable for any number of runs."""
+
+    def __init__(self, handle, desc):
+        self._h = ctypes.c_void_p(handle)
+        self.desc = desc
+
+    @property
+    def handle(self):
+        return self._h
+
+    def describe(self):
+        return gemm_plan_describe(self)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.gemm_plan_destroy(h)
+            self._h = ctypes.c_void_p(0)
+
+
+def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False):
+    d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type),
+              int(lda if lda is not None else max(1, k)),
+              int(ldb if ldb is not None else max(1, n)),
+              int(ldc if ldc is not None else max(1, n)),
+              FLAG_GATE_UP if gate_up else 0)
+    h = ctypes.c_void_p()
+    _check(load().gemm_plan(ctypes.byref(d), ctypes.byref(h)))
+    return Plan(h.value, d)
+
+
+def gemm_plan_describe(plan):
+    buf = ctypes.create_string_buffer(4096)
+    _check(load().gemm_plan_describe(plan.handle, buf, len(buf)))
+    return json.loads(buf.value.decode())
+
+
+def gemm_plan_lds_offset(plan, operand, row, col):
+    out = ctypes.c_int64()
+    _check(load().gemm_plan_lds_offset(plan.handle, int(operand), int(row), int(col), ctypes.byref(out)))
+    return out.value
+
+
+def gemm_plan_lds_stage_bytes(plan):
+    out = ctypes.c_int64()
+    _check(load().gemm_plan_lds_stage_bytes(plan.handle, ctypes.byref(out)))
+    return out.value
+
+
+# ------------------------------------------------------------------ runs (torch tensors)
+_KIND = {}
+
+
+def _torch():
+    import torch
+    if not _KIND:
+        _KIND.update({torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32})
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_matrix(t, name, rows, cols, ld, kind):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a tensor on the GPU" % name)
+    if _KIND.get(t.dtype) != kind:
+        raise ValueError("%s has dtype %s, plan expects type code %d" % (name, t.dtype, kind))
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError("%s must have shape (%d, %d), got %s" % (name, rows, cols, tuple(t.shape)))
+    if rows > 0 and cols > 0:
+        if t.stride(1) != 1 or (rows > 1 and t.stride(0) != ld):
+            raise ValueError("%s must be row-major with leading dimension %d (strides %s)" % (name, ld, t.stride()))
+
+
+def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """C = alpha * A @ B + beta * C, enqueued on `stream` (default: current)."""
+    d = plan.desc
+    _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type)
+    _check_matrix(B, "B", d.k, d.n, d.ldb, d.b_type)
+    _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type)
+    _check(load().gemm_run(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                           ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), _stream_ptr(stream)))
+
+
+def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
+    """G = X @ W_gate and U = X @ W_up in one launch."""
+    d = plan.desc
+    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type)
+    _check_matrix(W_gate, "W_gate", d.k, d.n, d.ldb, d.b_type)
+    _check_matrix(W_up, "W_up", d.k, d.n, d.ldb, d.b_type)
+    _check_matrix(G, "G", d.m, d.n, d.ldc, d.c_type)
+    _check_matrix(U, "U", d.m, d.n, d.ldc, d.c_type)
+    _check(load().gemm_gate_up_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, G, U)],
+                                   _stream_ptr(stream)))
+
+
+def gemm_debug_lds_image(plan, A, B, B2, tile_m, tile_n, out, stream=None):
+    """Copy the kernel's LDS stage for K block 0 of tile (tile_m, tile_n) into `out` (uint8/int16 tensor)."""
+    _check(load().gemm_debug_lds_image(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                                       ctypes.c_void_p(B2.data_ptr() if B2 is not None else 0),
+                                       int(tile_m), int(tile_n), ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+
+
+# ------------------------------------------------------------------ layout algebra (host)
+def la_layout_eval(shape, stride, coord):
+    out = ctypes.c_int64()
+    _check(load().la_layout_eval(_i64s(shape), _i64s(stride), len(shape), _i64s(coord), ctypes.byref(out)))
+    return out.value
+
+
+def la_layout_eval_index(shape, stride, idx):
+    out = ctypes.c_int64()
+    _check(load().la_layout_eval_index(_i64s(shape), _i64s(stride), len(shape), int(idx), ctypes.byref(out)))
+    return out.value
+
+
+def la_swizzle_apply(b, m, s, offset):
+    out = ctypes.c_int64()
+    _check(load().la_swizzle_apply(int(b), int(m), int(s), int(offset), ctypes.byref(out)))
+    return out.value
+
+
+def la_tile_plan_offset(elem_bytes, shape, inner_axis, row_bytes, coord):
+    off, tb = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().la_tile_plan_offset(int(elem_bytes), int(shape[0]), int(shape[1]), int(inner_axis), int(row_bytes),
+                                      int(coord[0]), int(coord[1]), ctypes.byref(off), ctypes.byref(tb)))
+    return off.value, tb.value

@@ -1,0 +1,215 @@
+// extern "C" boundary of the GEMM library (declarations and contracts in
+// include/la_gemm.h).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/la_gemm.h"
+#include "launch.hpp"
+#include "layout.hpp"
+#include "planner.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gemm_status set_err(gemm_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) % uintptr_t(bytes)) == 0; }
+
+lak::TiledArgs base_args(const gemm_plan_s& p) {
+  lak::TiledArgs a{};
+  a.M = p.d.m;
+  a.N = p.d.n;
+  a.K = p.d.k;
+  a.lda = p.d.lda;
+  a.ldb = p.d.ldb;
+  a.ldc = p.d.ldc;
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.group_m = p.group_m;
+  return a;
+}
+
+gemm_status launch(const gemm_plan_s& p, const lak::TiledArgs& a, void* stream, bool image) {
+  const hipError_t e = lak::launch_tiled(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, a, p.grid,
+                                         static_cast<hipStream_t>(stream), image);
+  if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_status_string(gemm_status s) {
+  switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_NULL: return "GEMM_ERR_NULL";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_ALIGNMENT: return "GEMM_ERR_ALIGNMENT";
+    case GEMM_ERR_RESOURCE: return "GEMM_ERR_RESOURCE";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+  }
+  return "GEMM_ERR_UNKNOWN";
+}
+
+const char* gemm_last_error(void) { return g_last_error.c_str(); }
+
+gemm_status gemm_plan(const gemm_desc* desc, gemm_plan_t* out_plan) {
+  if (!desc || !out_plan) return set_err(GEMM_ERR_NULL, "desc and out_plan must not be NULL");
+  *out_plan = nullptr;
+  gemm_plan_s* p = new (std::nothrow) gemm_plan_s();
+  if (!p) return set_err(GEMM_ERR_RESOURCE, "out of host memory");
+  std::string err;
+  const gemm_status s = plan::build(*desc, *p, &err);
+  if (s != GEMM_OK) {
+    delete p;
+    return set_err(s, err);
+  }
+  *out_plan = p;
+  return GEMM_OK;
+}
+
+void gemm_plan_destroy(gemm_plan_t plan) { delete plan; }
+
+gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha, float beta, void* stream) {
+  if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");
+  const gemm_plan_s& p = *plan;
+  if (p.gate_up) return set_err(GEMM_ERR_INVALID_ARG, "plan was made for gemm_gate_up_run");
+  if (p.d.m == 0 || p.d.n == 0) return GEMM_OK;
+  if (!C) return set_err(GEMM_ERR_NULL, "C is NULL");
+  if (p.d.k > 0 && (!A || !B)) return set_err(GEMM_ERR_NULL, "A or B is NULL");
+  if (!aligned(A, p.align_bytes) || !aligned(B, p.align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "A and B must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
+  if (!aligned(C, p.out_bytes)) return set_err(GEMM_ERR_ALIGNMENT, "C must be aligned to its element size");
+  lak::TiledArgs a = base_args(p);
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.C = C;
+  a.alpha = alpha;
+  a.beta = beta;
+  return launch(p, a, stream, false);
+}
+
+gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate, const void* W_up, void* G, void* U,
+                             void* stream) {
+  if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");
+  const gemm_plan_s& p = *plan;
+  if (!p.gate_up) return set_err(GEMM_ERR_INVALID_ARG, "plan was not made with GEMM_FLAG_GATE_UP");
+  if (p.d.m == 0 || p.d.n == 0) return GEMM_OK;
+  if (!G || !U) return set_err(GEMM_ERR_NULL, "G or U is NULL");
+  if (p.d.k > 0 && (!X || !W_gate || !W_up)) return set_err(GEMM_ERR_NULL, "X, W_gate or W_up is NULL");
+  if (!aligned(X, p.align_bytes) || !aligned(W_gate, p.align_bytes) || !aligned(W_up, p.align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "X, W_gate and W_up must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
+  if (!aligned(G, p.out_bytes) || !aligned(U, p.out_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "G and U must be aligned to their element size");
+  lak::TiledArgs a = base_args(p);
+  a.A = static_cast<const uint16_t*>(X);
+  a.B = static_cast<const uint16_t*>(W_gate);
+  a.B2 = static_cast<const uint16_t*>(W_up);
+  a.C = G;
+  a.C2 = U;
+  a.alpha = 1.0f;
+  a.beta = 0.0f;
+  return launch(p, a, stream, false);
+}
+
+gemm_status gemm_plan_describe(gemm_plan_t plan, char* buf, size_t len) {
+  if (!plan || !buf) return set_err(GEMM_ERR_NULL, "plan and buf must not be NULL");
+  if (plan->json.size() + 1 > len) return set_err(GEMM_ERR_RESOURCE, "buffer too small for the plan description");
+  std::memcpy(buf, plan->json.c_str(), plan->json.size() + 1);
+  return GEMM_OK;
+}
+
+gemm_status gemm_plan_lds_offset(gemm_plan_t plan, int operand, int64_t row, int64_t col, int64_t* out_elem_offset) {
+  if (!plan || !out_elem_offset) return set_err(GEMM_ERR_NULL, "plan and out_elem_offset must not be NULL");
+  std::string err;
+  const gemm_status s = plan::lds_offset(*plan, operand, row, col, out_elem_offset, &err);
+  return s == GEMM_OK ? s : set_err(s, err);
+}
+
+gemm_status gemm_plan_lds_stage_bytes(gemm_plan_t plan, int64_t* out_bytes) {
+  if (!plan || !out_bytes) return set_err(GEMM_ERR_NULL, "plan and out_bytes must not be NULL");
+  *out_bytes = plan->stage_elems * 2;
+  return GEMM_OK;
+}
+
+gemm_status gemm_debug_lds_image(gemm_plan_t plan, const void* A, const void* B, const void* B2, int64_t tile_m,
+                                 int64_t tile_n, void* out, void* stream) {
+  if (!plan || !out || !A || !B) return set_err(GEMM_ERR_NULL, "plan, A, B and out must not be NULL");
+  const gemm_plan_s& p = *plan;
+  if (p.gate_up && !B2) return set_err(GEMM_ERR_NULL, "gate/up plans need B2");
+  if (tile_m < 0 || tile_m >= p.tiles_m || tile_n < 0 || tile_n >= p.tiles_n)
+    return set_err(GEMM_ERR_INVALID_ARG, "tile index outside the plan's tile grid");
+  if (!aligned(A, p.align_bytes) || !aligned(B, p.align_bytes) || (B2 && !aligned(B2, p.align_bytes)))
+    return set_err(GEMM_ERR_ALIGNMENT, "operands break the plan's alignment class");
+  if (!aligned(out, 16)) return set_err(GEMM_ERR_ALIGNMENT, "out must be 16-byte aligned");
+  lak::TiledArgs a = base_args(p);
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.B2 = static_cast<const uint16_t*>(B2);
+  a.dbg_tm = static_cast<int>(tile_m);
+  a.dbg_tn = static_cast<int>(tile_n);
+  a.dbg_out = static_cast<uint16_t*>(out);
+  return launch(p, a, stream, true);
+}
+
+// ---- layout algebra entry points (host only) ----
+
+gemm_status la_layout_eval(const int64_t* shape, const int64_t* stride, int rank, const int64_t* coord,
+                           int64_t* out_offset) {
+  if (!shape || !stride || !coord || !out_offset) return set_err(GEMM_ERR_NULL, "NULL argument");
+  if (rank <= 0 || rank > 16) return set_err(GEMM_ERR_INVALID_ARG, "rank must be 1..16");
+  try {
+    const la::Layout l = la::Layout::flat(std::vector<int64_t>(shape, shape + rank), std::vector<int64_t>(stride, stride + rank));
+    *out_offset = l.at(std::vector<int64_t>(coord, coord + rank));
+  } catch (const la::LayoutError& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+  return GEMM_OK;
+}
+
+gemm_status la_layout_eval_index(const int64_t* shape, const int64_t* stride, int rank, int64_t idx,
+                                 int64_t* out_offset) {
+  if (!shape || !stride || !out_offset) return set_err(GEMM_ERR_NULL, "NULL argument");
+  if (rank <= 0 || rank > 16) return set_err(GEMM_ERR_INVALID_ARG, "rank must be 1..16");
+  try {
+    const la::Layout l = la::Layout::flat(std::vector<int64_t>(shape, shape + rank), std::vector<int64_t>(stride, stride + rank));
+    *out_offset = l(idx);
+  } catch (const la::LayoutError& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+  return GEMM_OK;
+}
+
+gemm_status la_swizzle_apply(int b, int m, int s, int64_t offset, int64_t* out_offset) {
+  if (!out_offset) return set_err(GEMM_ERR_NULL, "NULL argument");
+  if (!la::Swizzle::valid(b, m, s) || offset < 0 || b > 16 || m > 30 || s > 30)
+    return set_err(GEMM_ERR_INVALID_ARG, "Swizzle fields overlap, a parameter is out of range or the offset is negative");
+  *out_offset = la::Swizzle(b, m, s)(offset);
+  return GEMM_OK;
+}
+
+gemm_status la_tile_plan_offset(int elem_bytes, int64_t d1, int64_t d2, int inner_axis, int row_bytes, int64_t c1,
+                                int64_t c2, int64_t* out_offset, int64_t* out_transfer_bytes) {
+  if (!out_offset || !out_transfer_bytes) return set_err(GEMM_ERR_NULL, "NULL argument");
+  try {
+    const la::SharedTilePlan tp(elem_bytes, d1, d2, inner_axis, row_bytes);
+    *out_offset = tp.layout.at({c1, c2});
+    *out_transfer_bytes = tp.transfer_bytes();
+  } catch (const la::LayoutError& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+  return GEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,303 @@
+// Tiled GEMM kernels for gfx950: C = alpha * A * B + beta * C.
+//
+// Structure (per workgroup, one BM x BN output tile):
+//   * K is walked in blocks of 64.  A block of A (BM x 64) and of B (64 x BN)
+//     is staged cooperatively by every thread, global -> registers -> LDS,
+//     with 16-byte vector loads where the alignment class allows and a zero
+//     for every element outside [0,M) x [0,K) or [0,K) x [0,N) (the
+//     zero-filled edge semantics of the Tylo.jl page "TMA and Hopper WGMMA",
+//     section "Copy and completion").
+//   * In LDS both operands are stored K-contiguous, one 128-byte row of 64
+//     16-bit values per M row (A) or N column (B), under the swizzle
+//     Swizzle{3,3,3}: element (r, k) sits at 64 r + (k XOR 8 (r mod 8)), the
+//     128-byte row map of the Tylo.jl page "TMA and Hopper WGMMA" (section
+//     "The same storage contract on both sides").  B arrives N-contiguous, so
+//     each thread transposes a 4 (k) x 8 (n) block in registers while staging.
+//   * Two LDS stages: while the MFMAs consume stage s the next block is
+//     loaded into registers and written to stage s^1; one workgroup barrier
+//     per block separates "all waves finished reading" from "overwrite"
+//     (the two synchronisations the Tylo.jl page "Layouts, storage and
+//     ownership" requires in section "Plans describe work, callers establish
+//     readiness").
+//   * Each wave owns a (BM/WM) x (BN/WN) sub-tile as a grid of
+//     v_mfma_f32_32x32x16 blocks whose FP32 accumulators stay in registers
+//     for the whole K loop (Phobos "Tiles and shared memory", section "Tiles in
+//     registers"); A and B fragments are reused across that grid.
+//   * Epilogue: alpha * acc + beta * C_old in FP32 (C_old read only when
+//     beta != 0), rounded to nearest even for 16-bit outputs, written only
+//     inside [0,M) x [0,N).
+#include "kernel_common.hpp"
+#include "launch.hpp"
+
+namespace lak {
+
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+struct Tiled {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int BK = 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int NB = GU ? 2 : 1;
+  static constexpr int A_ELEMS = BM * BK;
+  static constexpr int B_ELEMS = BN * BK;
+  static constexpr int STAGE = A_ELEMS + NB * B_ELEMS;
+  static constexpr int A_CHUNKS = BM * BK / 8 / NT;
+  static constexpr int BN8 = BN / 8;
+  static constexpr int B_BLOCKS = (BK / 4) * BN8 / NT;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(A_CHUNKS * NT * 8 == BM * BK, "A block must split evenly over threads");
+  static_assert(B_BLOCKS * NT == (BK / 4) * BN8, "B block must split evenly over threads");
+  static_assert(V == 8 || V == 4 || V == 2 || V == 1, "vector width");
+
+  // LDS element offset of (row, k) inside one operand block.
+  static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 3>(row * BK + k); }
+
+  struct Regs {
+    u32x4 a[A_CHUNKS];
+    u32x4 b[NB][B_BLOCKS][4];
+  };
+
+  static __device__ __forceinline__ u32x4 pack8(const uint16_t* e) {
+    u32x4 w;
+    w.x = e[0] | (uint32_t(e[1]) << 16);
+    w.y = e[2] | (uint32_t(e[3]) << 16);
+    w.z = e[4] | (uint32_t(e[5]) << 16);
+    w.w = e[6] | (uint32_t(e[7]) << 16);
+    return w;
+  }
+
+  // Eight consecutive elements starting at p; `nvalid` of them are in range.
+  static __device__ __forceinline__ u32x4 load8(const uint16_t* p, int nvalid) {
+    if (nvalid >= 8) {
+      if constexpr (V == 8) {
+        return *reinterpret_cast<const u32x4*>(p);
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = p[q];
+        return pack8(e);
+      }
+    }
+    uint16_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = q < nvalid ? p[q] : uint16_t(0);
+    return pack8(e);
+  }
+
+  static __device__ __forceinline__ void load(Regs& r, const TiledArgs& g, int m0, int n0, int k0, int tid) {
+#pragma unroll
+    for (int j = 0; j < A_CHUNKS; ++j) {
+      const int idx = tid + NT * j;
+      const int row = idx >> 3, ch = idx & 7;
+      const int64_t gm = m0 + row;
+      const int64_t gk = k0 + ch * 8;
+      int nvalid = gm < g.M ? int(min<int64_t>(8, g.K - gk)) : 0;
+      r.a[j] = load8(g.A + gm * g.lda + gk, nvalid);
+    }
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const uint16_t* B = s == 0 ? g.B : g.B2;
+#pragma unroll
+      for (int j = 0; j < B_BLOCKS; ++j) {
+        const int idx = tid + NT * j;
+        const int nb = idx % BN8, kb = idx / BN8;
+        const int64_t gn = n0 + nb * 8;
+        const int nval = int(min<int64_t>(8, g.N - gn));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gk = k0 + kb * 4 + q;
+          r.b[s][j][q] = load8(B + gk * g.ldb + gn, gk < g.K ? nval : 0);
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store(const Regs& r, uint16_t* stage, int tid) {
+#pragma unroll
+    for (int j = 0; j < A_CHUNKS; ++j) {
+      const int idx = tid + NT * j;
+      const int row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(stage + lds_off(row, ch * 8)) = r.a[j];
+    }
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      uint16_t* dst = stage + A_ELEMS + s * B_ELEMS;
+#pragma unroll
+      for (int j = 0; j < B_BLOCKS; ++j) {
+        const int idx = tid + NT * j;
+        const int nb = idx % BN8, kb = idx / BN8;
+        const u32x4* q = r.b[s][j];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          // columns 2p (low halves) and 2p+1 (high halves) of the 4 x 8 block
+          u32x2 lo, hi;
+          lo.x = (q[0][p] & 0xffffu) | (q[1][p] << 16);
+          lo.y = (q[2][p] & 0xffffu) | (q[3][p] << 16);
+          hi.x = (q[0][p] >> 16) | (q[1][p] & 0xffff0000u);
+          hi.y = (q[2][p] >> 16) | (q[3][p] & 0xffff0000u);
+          *reinterpret_cast<u32x2*>(dst + lds_off(nb * 8 + 2 * p, kb * 4)) = lo;
+          *reinterpret_cast<u32x2*>(dst + lds_off(nb * 8 + 2 * p + 1, kb * 4)) = hi;
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void compute(const uint16_t* stage, f32x16 (&acc)[NB][FM][FN], int wm, int wn, int lane) {
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      u32x4 a[FM], b[NB][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const u32x4*>(stage + lds_off(wm * TM + i * 32 + lr, s * 16 + lk));
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          b[t][j] = *reinterpret_cast<const u32x4*>(stage + A_ELEMS + t * B_ELEMS + lds_off(wn * TN + j * 32 + lr, s * 16 + lk));
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[t][i][j] = mfma_32x32x16<TI>(a[i], b[t][j], acc[t][i][j]);
+    }
+  }
+};
+
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g) {
+  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  int tm, tn;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  f32x16 acc[T::NB][T::FM][T::FN];
+#pragma unroll
+  for (int t = 0; t < T::NB; ++t)
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[t][i][j] = f32x16{};
+
+  const int nk = int((g.K + T::BK - 1) / T::BK);
+  typename T::Regs r;
+  if (nk > 0) {
+    T::load(r, g, m0, n0, 0, tid);
+    T::store(r, lds, tid);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* cur = lds + (kt & 1) * T::STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) T::load(r, g, m0, n0, (kt + 1) * T::BK, tid);
+    T::compute(cur, acc, wm, wn, lane);
+    if (more) T::store(r, lds + ((kt + 1) & 1) * T::STAGE, tid);
+    __syncthreads();
+  }
+
+  // Epilogue straight from the accumulator lane map.
+  typedef typename TO::storage St;
+  const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int64_t col = n0 + wn * T::TN + j * 32 + lc;
+      const int64_t rbase = m0 + wm * T::TM + i * 32 + lr4;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = rbase + 8 * (e >> 2) + (e & 3);
+        if (row >= g.M) continue;
+        const int64_t idx = row * g.ldc + col;
+        if constexpr (GU) {
+          static_cast<St*>(g.C)[idx] = to_out<TO>(acc[0][i][j][e]);
+          static_cast<St*>(g.C2)[idx] = to_out<TO>(acc[1][i][j][e]);
+        } else {
+          St* C = static_cast<St*>(g.C);
+          float v = g.alpha * acc[0][i][j][e];
+          if (g.beta != 0.0f) v += g.beta * from_out<TO>(C[idx]);
+          C[idx] = to_out<TO>(v);
+        }
+      }
+    }
+  }
+}
+
+// Debug: stage K block 0 of tile (dbg_tm, dbg_tn) with the kernel's own
+// staging code and copy the LDS stage out verbatim.
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const TiledArgs g) {
+  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[T::STAGE];
+  const int tid = threadIdx.x;
+  typename T::Regs r;
+  T::load(r, g, g.dbg_tm * BM, g.dbg_tn * BN, 0, tid);
+  T::store(r, lds, tid);
+  __syncthreads();
+  for (int i = tid; i < T::STAGE; i += T::NT) g.dbg_out[i] = lds[i];
+}
+
+// ------------------------------------------------------------------ dispatch
+KernelShape kernel_shape(int kid) {
+  switch (kid) {
+    case KID_TILED_128: return KernelShape{128, 128, 64, 2, 2, 256, 32, 32, 16, 3, 3, 3, 2};
+    default: return KernelShape{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+int64_t stage_elems(int kid, bool gate_up) {
+  const KernelShape s = kernel_shape(kid);
+  return int64_t(s.bm) * s.bk + (gate_up ? 2 : 1) * int64_t(s.bn) * s.bk;
+}
+
+namespace {
+
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+hipError_t go(const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (img) {
+    hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU>), dim3(1), dim3(WM * WN * 64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU>), dim3(grid), dim3(WM * WN * 64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <class TI, class TO, int BM, int BN, int WM, int WN>
+hipError_t by_vec_gu(int vec, bool gu, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (vec == 8) return gu ? go<TI, TO, BM, BN, WM, WN, 8, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, 8, false>(a, grid, s, img);
+  if (vec == 1) return gu ? go<TI, TO, BM, BN, WM, WN, 1, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, 1, false>(a, grid, s, img);
+  return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (in_kind == IN_BF16) {
+    if (out_kind == OUT_F32) return by_vec_gu<InBF16, OutF32, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+    if (out_kind == OUT_BF16) return by_vec_gu<InBF16, OutBF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+    if (out_kind == OUT_F16) return by_vec_gu<InBF16, OutF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+  } else if (in_kind == IN_F16) {
+    if (out_kind == OUT_F32) return by_vec_gu<InF16, OutF32, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+    if (out_kind == OUT_BF16) return by_vec_gu<InF16, OutBF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+    if (out_kind == OUT_F16) return by_vec_gu<InF16, OutF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up,
+                        const TiledArgs& args, int grid, hipStream_t stream, bool lds_image) {
+  switch (kid) {
+    case KID_TILED_128: return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, args, grid, stream, lds_image);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lak

@@ -1,0 +1,103 @@
+// Device-side building blocks shared by the gfx950 GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lak {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Input element tags: both are 16-bit patterns in memory.
+struct InBF16 {};
+struct InF16 {};
+
+// Output element tags.
+struct OutF32 { typedef float storage; };
+struct OutBF16 { typedef uint16_t storage; };
+struct OutF16 { typedef uint16_t storage; };
+
+// v_mfma_f32_32x32x16_{bf16,f16}: 32x32 FP32 block += (32x16) x (16x32).
+// Operand lane map: lane l holds row (A) / column (B) l % 32 and eight
+// consecutive K values starting at 8 * (l / 32).  Result lane map: register r
+// of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+template <class TI>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma_32x32x16<InBF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma_32x32x16<InF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_{bf16,f16}: lane l holds row/column l % 16 and eight
+// consecutive K values starting at 8 * (l / 16); result register r of lane l
+// is row 4*(l/16) + r, column l % 16.
+template <class TI>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<InBF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<InF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even conversions of the FP32 result (the language's own
+// float -> __bf16 / _Float16 conversions, which gfx950 implements in hardware).
+template <class TO>
+__device__ __forceinline__ typename TO::storage to_out(float v);
+template <>
+__device__ __forceinline__ float to_out<OutF32>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t to_out<OutBF16>(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+template <>
+__device__ __forceinline__ uint16_t to_out<OutF16>(float v) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v)); }
+
+template <class TO>
+__device__ __forceinline__ float from_out(typename TO::storage v);
+template <>
+__device__ __forceinline__ float from_out<OutF32>(float v) { return v; }
+template <>
+__device__ __forceinline__ float from_out<OutBF16>(uint16_t v) { return static_cast<float>(__builtin_bit_cast(__bf16, v)); }
+template <>
+__device__ __forceinline__ float from_out<OutF16>(uint16_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, v)); }
+
+// Swizzle{B,M,S} on element offsets: XOR bits [M+S, M+S+B) into [M, M+B).
+template <int B, int M, int S>
+__device__ __forceinline__ constexpr int swz(int off) {
+  return off ^ ((off >> S) & (((1 << B) - 1) << M));
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Renumber so that each XCD receives one contiguous range of tile
+// ids, keeping neighbouring tiles -- which share A rows and B columns -- in the
+// same L2.  Ids past the last multiple of 8 keep their own number.
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+  const int full = nb & ~7;
+  if (b >= full) return b;
+  const int per = full >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+// Grouped ordering: walk `group` tile-rows together, column by column, so
+// that consecutive ids reuse the same A panels and nearby B panels.
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
+  const int per_group = group * tiles_n;
+  const int g = id / per_group;
+  const int first = g * group;
+  const int rows = min(group, tiles_m - first);
+  const int in = id - g * per_group;
+  tm = first + in % rows;
+  tn = in / rows;
+}
+
+}  // namespace lak

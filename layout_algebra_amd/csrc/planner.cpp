@@ -1,0 +1,226 @@
+// GEMM planner.  Host only; touches no device memory.
+//
+// Steps, in order (constructors check domains before anything is launched, as
+// the Tylo.jl page "Layouts, storage and ownership" requires in section "Swizzle
+// phase belongs to the allocation"):
+//   1. validate the descriptor (sizes, leading dimensions, dtypes, flags);
+//   2. derive the alignment class: 16-byte vectors only when every row start
+//      is 16-byte aligned, else element-wide accesses (Tylo.jl, section "Three
+//      representations, three addressing rules": vector width follows the
+//      declared alignment of pointer and strides);
+//   3. choose a kernel and its tile grid;
+//   4. build each operand's LDS map as Swizzle o Layout in the operand's own
+//      mathematical coordinates (B in (K, N), section "Three representations,
+//      three addressing rules") and check it: injective, cosize inside its
+//      block, block bases on the swizzle period (the allocation fixes the
+//      phase), total LDS within the 160 KiB a gfx950 workgroup may use;
+//   5. check the copy plans (every 16-byte LDS vector written exactly once,
+//      contiguous and aligned; section "Plans describe work, callers establish
+//      readiness") and the MFMA ownership (every C element of the tile owned by
+//      exactly one (wave, lane, register)).
+#include "planner.hpp"
+
+#include <algorithm>
+#include <cstdio>
+#include <sstream>
+#include <vector>
+
+namespace plan {
+namespace {
+
+constexpr int64_t kMaxLdsBytes = 163840;   // gfx950 per-workgroup LDS
+
+bool fail(std::string* err, const std::string& msg) {
+  if (err) *err = msg;
+  return false;
+}
+
+// 16-byte copy plan of an A block: thread t, slot j covers (row, 8-element chunk).
+bool check_copy_a(const gemm_plan_s& p, std::string* err) {
+  const auto& s = p.shape;
+  const int chunks = s.bm * s.bk / 8;
+  if (chunks % s.threads) return fail(err, "A block does not split evenly into 16-byte vectors per thread");
+  std::vector<int> hits(static_cast<size_t>(s.bm) * s.bk, 0);
+  for (int t = 0; t < s.threads; ++t) {
+    for (int j = 0; j < chunks / s.threads; ++j) {
+      const int idx = t + s.threads * j;
+      const int row = idx / (s.bk / 8), ch = idx % (s.bk / 8);
+      const int64_t o0 = p.lds_a.at({row, ch * 8});
+      if (o0 % 8) return fail(err, "A copy destination is not 16-byte aligned");
+      for (int e = 0; e < 8; ++e) {
+        const int64_t o = p.lds_a.at({row, ch * 8 + e});
+        if (o != o0 + e) return fail(err, "A copy destination is not contiguous");
+        if (hits[o]++) return fail(err, "A copy plan writes an LDS element twice");
+      }
+    }
+  }
+  for (int h : hits)
+    if (h != 1) return fail(err, "A copy plan leaves an LDS element unwritten");
+  return true;
+}
+
+// B block: thread t, slot j covers a 4 (k) x 8 (n) block, written as eight
+// 4-element K runs (one per n).
+bool check_copy_b(const gemm_plan_s& p, const la::View& v, std::string* err) {
+  const auto& s = p.shape;
+  const int blocks = (s.bk / 4) * (s.bn / 8);
+  if (blocks % s.threads) return fail(err, "B block does not split evenly over threads");
+  std::vector<int> hits(static_cast<size_t>(s.bn) * s.bk, 0);
+  for (int t = 0; t < s.threads; ++t) {
+    for (int j = 0; j < blocks / s.threads; ++j) {
+      const int idx = t + s.threads * j;
+      const int nb = idx % (s.bn / 8), kb = idx / (s.bn / 8);
+      for (int nn = 0; nn < 8; ++nn) {
+        const int64_t o0 = v.at({kb * 4, nb * 8 + nn});
+        if (o0 % 4) return fail(err, "B copy destination is not 8-byte aligned");
+        for (int q = 0; q < 4; ++q) {
+          const int64_t o = v.at({kb * 4 + q, nb * 8 + nn});
+          if (o != o0 + q) return fail(err, "B copy destination is not contiguous along K");
+          if (hits[o]++) return fail(err, "B copy plan writes an LDS element twice");
+        }
+      }
+    }
+  }
+  for (int h : hits)
+    if (h != 1) return fail(err, "B copy plan leaves an LDS element unwritten");
+  return true;
+}
+
+// MFMA 32x32 result ownership: register r of lane l of fragment (i, j) of wave
+// (wm, wn) holds tile element (wm*TM + 32 i + 8 (r/4) + 4 (l/32) + r%4,
+//                              wn*TN + 32 j + l%32).
+bool check_ownership(const gemm_plan_s& p, std::string* err) {
+  const auto& s = p.shape;
+  const int tm = s.bm / s.waves_m, tn = s.bn / s.waves_n;
+  if (tm % 32 || tn % 32) return fail(err, "wave tile is not a multiple of the 32x32 MFMA block");
+  std::vector<int> hits(static_cast<size_t>(s.bm) * s.bn, 0);
+  for (int w = 0; w < s.waves_m * s.waves_n; ++w) {
+    const int wm = w % s.waves_m, wn = w / s.waves_m;
+    for (int i = 0; i < tm / 32; ++i)
+      for (int j = 0; j < tn / 32; ++j)
+        for (int l = 0; l < 64; ++l)
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * tm + 32 * i + 8 * (r / 4) + 4 * (l / 32) + r % 4;
+            const int col = wn * tn + 32 * j + l % 32;
+            ++hits[static_cast<size_t>(row) * s.bn + col];
+          }
+  }
+  for (int h : hits)
+    if (h != 1) return fail(err, "MFMA ownership does not cover the C tile exactly once");
+  return true;
+}
+
+bool check_block(const la::View& v, int64_t base, int64_t block_elems, const char* name, std::string* err) {
+  if (!la::injective(v)) return fail(err, std::string(name) + " LDS map is not injective");
+  if (la::cosize(v) > block_elems) return fail(err, std::string(name) + " LDS map overruns its block");
+  if (base % v.swizzle().period()) return fail(err, std::string(name) + " block base breaks the swizzle phase");
+  return true;
+}
+
+const char* dtype_name(int t) {
+  switch (t) {
+    case GEMM_BF16: return "bf16";
+    case GEMM_F16: return "f16";
+    case GEMM_F32: return "f32";
+    default: return "?";
+  }
+}
+
+}  // namespace
+
+gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
+  p = gemm_plan_s{};
+  p.d = d;
+  if (d.m < 0 || d.n < 0 || d.k < 0) { fail(err, "m, n and k must be >= 0"); return GEMM_ERR_INVALID_ARG; }
+  if (d.lda < std::max<int64_t>(1, d.k)) { fail(err, "lda must be >= max(1, k)"); return GEMM_ERR_INVALID_ARG; }
+  if (d.ldb < std::max<int64_t>(1, d.n)) { fail(err, "ldb must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
+  if (d.ldc < std::max<int64_t>(1, d.n)) { fail(err, "ldc must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
+  if ((d.a_type != GEMM_BF16 && d.a_type != GEMM_F16 && d.a_type != GEMM_F32) ||
+      (d.b_type != GEMM_BF16 && d.b_type != GEMM_F16 && d.b_type != GEMM_F32) ||
+      (d.c_type != GEMM_BF16 && d.c_type != GEMM_F16 && d.c_type != GEMM_F32)) {
+    fail(err, "unknown dtype");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (d.flags & ~GEMM_FLAG_GATE_UP) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
+  if (d.a_type != d.b_type || d.a_type == GEMM_F32) {
+    fail(err, "A and B must both be bf16 or both be f16");
+    return GEMM_ERR_UNSUPPORTED;
+  }
+  // 32-bit tile ids and in-tile offsets; global offsets are 64-bit.
+  if (d.m > (int64_t{1} << 31) - 256 || d.n > (int64_t{1} << 31) - 256 || d.k > (int64_t{1} << 31) - 256) {
+    fail(err, "dimension too large");
+    return GEMM_ERR_UNSUPPORTED;
+  }
+
+  p.gate_up = (d.flags & GEMM_FLAG_GATE_UP) != 0;
+  p.in_kind = d.a_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16;
+  p.out_kind = d.c_type == GEMM_F32 ? lak::OUT_F32 : d.c_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16;
+  p.out_bytes = d.c_type == GEMM_F32 ? 4 : 2;
+  p.vec = (d.lda % 8 == 0 && d.ldb % 8 == 0) ? 8 : 1;
+  p.align_bytes = 2 * p.vec;
+
+  p.kid = lak::KID_TILED_128;
+  p.shape = lak::kernel_shape(p.kid);
+  const auto& s = p.shape;
+  p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
+  p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
+  if (int64_t(p.tiles_m) * p.tiles_n > (int64_t{1} << 31) - 1) { fail(err, "too many tiles"); return GEMM_ERR_UNSUPPORTED; }
+  p.grid = p.tiles_m * p.tiles_n;
+  p.group_m = 8;
+
+  try {
+    const la::Swizzle sw(s.sw_b, s.sw_m, s.sw_s);
+    p.lds_a = la::View(sw, la::Layout::row_major(s.bm, s.bk, s.bk));   // (m, k) -> m*BK + k
+    p.lds_b = la::View(sw, la::Layout::col_major(s.bk, s.bn, s.bk));   // (k, n) -> n*BK + k
+    p.lds_b2 = p.lds_b;
+    p.base_a = 0;
+    p.base_b = int64_t(s.bm) * s.bk;
+    p.base_b2 = p.base_b + int64_t(s.bn) * s.bk;
+    p.stage_elems = lak::stage_elems(p.kid, p.gate_up);
+    p.lds_bytes = int64_t(s.stages) * p.stage_elems * 2;
+    if (p.lds_bytes > kMaxLdsBytes) { fail(err, "LDS footprint exceeds 160 KiB"); return GEMM_ERR_RESOURCE; }
+    if (!check_block(p.lds_a, p.base_a, int64_t(s.bm) * s.bk, "A", err) ||
+        !check_block(p.lds_b, p.base_b, int64_t(s.bn) * s.bk, "B", err) ||
+        (p.gate_up && !check_block(p.lds_b2, p.base_b2, int64_t(s.bn) * s.bk, "W_up", err)))
+      return GEMM_ERR_RESOURCE;
+    if (!check_copy_a(p, err) || !check_copy_b(p, p.lds_b, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
+  } catch (const la::LayoutError& e) {
+    fail(err, e.what());
+    return GEMM_ERR_RESOURCE;
+  }
+
+  std::ostringstream js;
+  js << "{\"kernel\":\"tiled_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
+     << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
+     << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc
+     << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"out\":\"" << dtype_name(d.c_type) << "\""
+     << ",\"gate_up\":" << (p.gate_up ? "true" : "false")
+     << ",\"tile\":[" << s.bm << "," << s.bn << "," << s.bk << "]"
+     << ",\"waves\":[" << s.waves_m << "," << s.waves_n << "],\"threads\":" << s.threads
+     << ",\"mfma\":\"" << s.mfma_m << "x" << s.mfma_n << "x" << s.mfma_k << "\""
+     << ",\"tiles\":[" << p.tiles_m << "," << p.tiles_n << "],\"grid\":" << p.grid << ",\"group_m\":" << p.group_m
+     << ",\"stages\":" << s.stages << ",\"stage_elems\":" << p.stage_elems << ",\"lds_bytes\":" << p.lds_bytes
+     << ",\"swizzle\":[" << s.sw_b << "," << s.sw_m << "," << s.sw_s << "]"
+     << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
+     << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes << "}";
+  p.json = js.str();
+  return GEMM_OK;
+}
+
+gemm_status lds_offset(const gemm_plan_s& p, int operand, int64_t row, int64_t col, int64_t* out, std::string* err) {
+  const la::View* v = nullptr;
+  int64_t base = 0;
+  if (operand == 0) { v = &p.lds_a; base = p.base_a; }
+  else if (operand == 1) { v = &p.lds_b; base = p.base_b; }
+  else if (operand == 2 && p.gate_up) { v = &p.lds_b2; base = p.base_b2; }
+  else { fail(err, "operand must be 0 (A), 1 (B) or 2 (W_up of a gate/up plan)"); return GEMM_ERR_INVALID_ARG; }
+  try {
+    *out = base + v->at({row, col});
+  } catch (const la::LayoutError& e) {
+    fail(err, e.what());
+    return GEMM_ERR_INVALID_ARG;
+  }
+  return GEMM_OK;
+}
+
+}  // namespace plan

@@ -1,0 +1,34 @@
+// Host-side GEMM planner: picks a kernel, builds and validates its layouts.
+#pragma once
+
+#include <string>
+
+#include "../../include/la_gemm.h"
+#include "launch.hpp"
+#include "layout.hpp"
+
+struct gemm_plan_s {
+  gemm_desc d;
+  int kid = 0;
+  int in_kind = 0, out_kind = 0;
+  int vec = 1;               // elements per global vector load of A and B
+  int align_bytes = 2;       // required alignment of the A / B / W pointers
+  int out_bytes = 4;         // bytes per C element
+  bool gate_up = false;
+  int tiles_m = 0, tiles_n = 0, grid = 0, group_m = 8;
+  int64_t stage_elems = 0, lds_bytes = 0;
+  lak::KernelShape shape{};
+  la::View lds_a, lds_b, lds_b2;     // operand block maps in (row, col) tile coordinates
+  int64_t base_a = 0, base_b = 0, base_b2 = 0;  // element offsets of each block in a stage
+  std::string json;
+};
+
+namespace plan {
+
+// Build a plan; on failure returns a status and sets *err.
+gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err);
+
+// Element offset of operand (0 = A, 1 = B / W_gate, 2 = W_up) element (row, col) in a stage.
+gemm_status lds_offset(const gemm_plan_s& p, int operand, int64_t row, int64_t col, int64_t* out, std::string* err);
+
+}  // namespace plan

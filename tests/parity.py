@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU parity tests: running the HIP path, running the
+oracle on the same 16-bit patterns, and the agreement bound.
+
+Agreement bound (elementwise):
+    |gpu - oracle| <= 2^-20 * K * max|A| * max|B|  +  r * |oracle|
+with r = 2^-8 for bf16 outputs (the output's own rounding), 2^-11 for fp16
+outputs, and 2^-22 for fp32 outputs.  The first term is the FP32
+accumulation allowance; the second covers the final rounding into the output
+format (for fp32 outputs it only matters when K = 0, where the first term is
+zero and the result is beta * C rounded to fp32).
+"""
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}
+
+
+def max_abs(t):
+    return float(t.abs().max()) if t.numel() else 0.0
+
+
+def bound(K, a, b, ref, out_kind):
+    return 2.0 ** -20 * K * max_abs(a) * max_abs(b) + REL[out_kind] * np.abs(ref)
+
+
+def assert_close(gpu, ref, K, a, b, out_kind, what=""):
+    g = gpu.detach().to("cpu", torch.float64).numpy()
+    tol = bound(K, a, b, ref, out_kind)
+    err = np.abs(g - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d elements out of tolerance; first at %s: gpu=%r oracle=%r tol=%r"
+                             % (what, int(bad.sum()), tuple(i), g[tuple(i)], ref[tuple(i)], tol[tuple(i)]))
+    return float(err.max()) if err.size else 0.0, float(tol.min()) if np.size(tol) else 0.0
+
+
+def oracle_gemm(a_cpu, b_cpu, in_kind, alpha=1.0, beta=0.0, c_cpu=None, rows=None):
+    """Oracle on CPU tensors; `rows` restricts to a subset of output rows."""
+    a = a_cpu if rows is None else a_cpu[rows]
+    c = None
+    if c_cpu is not None:
+        c = (c_cpu if rows is None else c_cpu[rows]).numpy()
+    return oracle.gemm_f64(synth.bits(a), in_kind, synth.bits(b_cpu), in_kind, alpha, beta, c)
+
+
+def sample_rows(M, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    pick = torch.randperm(M, generator=g)[:n].tolist()
+    return sorted(set(pick) | {0, M - 1})

@@ -1,0 +1,158 @@
+"""Host-side tests of the C ABI library (no GPU needed, no kernel launched).
+
+* the library loads and exports every symbol include/la_gemm.h declares;
+* the planner's layout algebra reproduces the pages' printed values and
+  agrees with the oracle's independent Python layout reference;
+* plans for every workload build and describe themselves; invalid requests
+  are rejected with the documented status before anything is launched.
+"""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import layout_algebra_amd as la
+from golden_cases import layout_cases, tup
+from oracle import layout_ref as L
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "la_gemm.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:gemm_status|void|const char\*)\s+(\w+)\s*\(", text, re.M))
+    assert declared, "no declarations parsed"
+    lib = la.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(la.EXPORTED_SYMBOLS)
+
+
+@pytest.mark.parametrize("case", [c for c in layout_cases() if c["kind"] in ("eval", "tile_plan", "closed_form_128B")],
+                         ids=lambda c: c["id"])
+def test_page_values_through_the_c_abi(case):
+    if case["kind"] == "eval":
+        shape, stride, coord = tup(case["shape"]), tup(case["stride"]), tup(case["coord"])
+        if any(isinstance(s, tuple) for s in shape):
+            # flatten the nested pin into flat modes: ((8,4),5) -> (8,4,5)
+            fs, fd, fc = L.leaves(shape), L.leaves(stride), L.leaves(coord)
+            assert la.la_layout_eval(fs, fd, fc) == case["expect"]
+        else:
+            assert la.la_layout_eval(shape, stride, coord) == case["expect"]
+    elif case["kind"] == "tile_plan":
+        if "probe" in case:
+            off, tb = la.la_tile_plan_offset(case["elem_bytes"], case["shape"], case["inner_axis"],
+                                             case["row_bytes"], case["probe"])
+            assert off == case["probe_offset"]
+            assert tb == case["transfer_bytes"]
+        else:
+            off, tb = la.la_tile_plan_offset(case["elem_bytes"], case["shape"], case["inner_axis"],
+                                             case["row_bytes"], (0, 0))
+            assert tb == case["shape"][0] * case["shape"][1] * case["elem_bytes"]
+    else:
+        for r in range(64):
+            for k in range(64):
+                off, _ = la.la_tile_plan_offset(2, (64, 64), 2, 128, (r, k))
+                assert off == 64 * r + (k ^ (8 * (r % 8)))
+
+
+def test_swizzle_matches_reference_and_rejects_overlap():
+    rng = random.Random(5)
+    for B, M, S in [(3, 3, 3), (2, 3, 2), (2, 4, 3), (1, 2, 4), (0, 3, 3), (3, 0, 5)]:
+        ref = L.Swizzle(B, M, S)
+        for _ in range(500):
+            o = rng.randrange(0, 1 << 20)
+            assert la.la_swizzle_apply(B, M, S, o) == ref(o)
+    with pytest.raises(la.GemmError) as e:
+        la.la_swizzle_apply(3, 3, 2, 1)
+    assert e.value.name == "GEMM_ERR_INVALID_ARG"
+
+
+def test_layout_eval_matches_reference_on_random_layouts():
+    rng = random.Random(9)
+    for _ in range(200):
+        rank = rng.randint(1, 4)
+        shape = [rng.randint(1, 6) for _ in range(rank)]
+        stride = [rng.randint(0, 40) for _ in range(rank)]
+        ref = L.Layout(tuple(shape), tuple(stride))
+        for _ in range(10):
+            idx = rng.randrange(0, ref.size())
+            coord = L.split_index(idx, tuple(shape))
+            assert la.la_layout_eval_index(shape, stride, idx) == ref(idx)
+            assert la.la_layout_eval(shape, stride, list(coord)) == ref(idx)
+    with pytest.raises(la.GemmError):
+        la.la_layout_eval([4, 4], [4, 1], [4, 0])
+
+
+def test_tile_plan_rejects_what_the_page_forbids():
+    for args in [(3, (64, 64), 2, 128), (2, (64, 32), 2, 128), (2, (12, 64), 2, 128),
+                 (2, (512, 64), 2, 128), (2, (64, 64), 2, 96)]:
+        with pytest.raises(la.GemmError):
+            la.la_tile_plan_offset(args[0], args[1], args[2], args[3], (0, 0))
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_plans_build(name):
+    w = synth.WORKLOADS[name]
+    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+    p = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up)
+    d = p.describe()
+    assert d["m"] == w.M and d["n"] == w.N and d["k"] == w.K
+    assert d["lds_bytes"] <= 163840
+    assert d["grid"] >= 1
+
+
+def test_planner_lds_map_agrees_with_reference():
+    p = la.gemm_plan(4096, 4096, 4096, la.BF16, la.BF16)
+    d = p.describe()
+    bm, bn, bk = d["tile"]
+    sw = L.Swizzle(*d["swizzle"])
+    a_ref = L.compose(sw, L.Layout((bm, bk), (bk, 1)))
+    b_ref = L.compose(sw, L.Layout((bk, bn), (1, bk)))
+    seen = set()
+    for r in range(bm):
+        for c in range(bk):
+            o = la.gemm_plan_lds_offset(p, 0, r, c)
+            assert o == a_ref((r, c))
+            seen.add(o)
+    for r in range(bk):
+        for c in range(bn):
+            o = la.gemm_plan_lds_offset(p, 1, r, c)
+            assert o == bm * bk + b_ref((r, c))
+            seen.add(o)
+    assert len(seen) == d["stage_elems"]
+
+
+def test_invalid_requests_are_rejected():
+    bad = [dict(m=-1, n=4, k=4), dict(m=4, n=4, k=4, lda=3), dict(m=4, n=4, k=4, ldb=2),
+           dict(m=4, n=4, k=4, ldc=1)]
+    for kw in bad:
+        with pytest.raises(la.GemmError) as e:
+            la.gemm_plan(**kw)
+        assert e.value.name == "GEMM_ERR_INVALID_ARG"
+    with pytest.raises(la.GemmError) as e:
+        la.gemm_plan(4, 4, 4, la.F32, la.F32)
+    assert e.value.name == "GEMM_ERR_UNSUPPORTED"
+
+
+def test_run_argument_errors_are_caught_before_launch():
+    lib = la.load()
+    p = la.gemm_plan(64, 64, 64, la.BF16, la.F32)
+    vp = ctypes.c_void_p
+    # misaligned A for a 16-byte alignment class: rejected on the host
+    rc = lib.gemm_run(p.handle, vp(0x1002), vp(0x2000), vp(0x3000), 1.0, 0.0, vp(0))
+    assert la._lib.STATUS[rc] == "GEMM_ERR_ALIGNMENT"
+    rc = lib.gemm_run(p.handle, vp(0x1000), vp(0), vp(0x3000), 1.0, 0.0, vp(0))
+    assert la._lib.STATUS[rc] == "GEMM_ERR_NULL"
+    rc = lib.gemm_gate_up_run(p.handle, vp(0x1000), vp(0x1000), vp(0x1000), vp(0x1000), vp(0x1000), vp(0))
+    assert la._lib.STATUS[rc] == "GEMM_ERR_INVALID_ARG"
+    # m == 0 is a no-op success that never touches the pointers
+    p0 = la.gemm_plan(0, 64, 64, la.BF16, la.F32)
+    assert lib.gemm_run(p0.handle, vp(0), vp(0), vp(0), 1.0, 0.0, vp(0)) == 0
+    # tile index outside the grid for the debug image
+    rc = lib.gemm_debug_lds_image(p.handle, vp(0x1000), vp(0x1000), vp(0), 5, 0, vp(0x1000), vp(0))
+    assert la._lib.STATUS[rc] == "GEMM_ERR_INVALID_ARG"

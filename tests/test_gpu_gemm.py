@@ -1,0 +1,266 @@
+"""GPU parity tests: the HIP path (through the C ABI) against the FP64 oracle.
+
+Every test calls the library through its Python binding, which only marshals
+pointers and the current stream.  Inputs come from the seeded generators in
+`synth`; the oracle sees the same 16-bit patterns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import layout_algebra_amd as la
+import synth
+from parity import assert_close, oracle_gemm, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+CODE = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+
+
+def run_gemm(a, b, out_kind, alpha=1.0, beta=0.0, c=None):
+    """a, b CPU tensors; returns the GPU result on the CPU."""
+    M, K = a.shape
+    N = b.shape[1]
+    in_kind = "bf16" if a.dtype == torch.bfloat16 else "f16"
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind])
+    A, B = a.to(DEV), b.to(DEV)
+    if c is None:
+        C = torch.full((M, N), float("nan"), dtype=synth.torch_dtype(out_kind), device=DEV)
+    else:
+        C = c.to(DEV).clone()
+    la.gemm_run(plan, A, B, C, alpha, beta)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+def test_library_is_the_native_one():
+    import os
+    assert os.path.exists(la.lib_path())
+    la.load()
+
+
+@pytest.mark.parametrize("name", ["square256", "ragged"])
+def test_workload_full_parity(name):
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w)
+    print("case", name, flush=True)
+    got = run_gemm(x["A"], x["B"], w.out_kind, w.alpha, w.beta, x.get("C"))
+    ref = oracle_gemm(x["A"], x["B"], w.in_kind, w.alpha, w.beta, x.get("C"))
+    assert_close(got, ref, w.K, x["A"], x["B"], w.out_kind, name)
+
+
+def test_square4096_sampled_rows():
+    w = synth.WORKLOADS["square4096"]
+    x = synth.make_inputs(w)
+    got = run_gemm(x["A"], x["B"], w.out_kind)
+    rows = sample_rows(w.M, 40, 2003)
+    ref = oracle_gemm(x["A"], x["B"], w.in_kind, rows=rows)
+    assert_close(got[rows], ref, w.K, x["A"], x["B"], w.out_kind, "square4096")
+
+
+def test_skinny_full():
+    w = synth.WORKLOADS["skinny"]
+    x = synth.make_inputs(w)
+    got = run_gemm(x["A"], x["B"], w.out_kind)
+    ref = oracle_gemm(x["A"], x["B"], w.in_kind)
+    assert_close(got, ref, w.K, x["A"], x["B"], w.out_kind, "skinny")
+
+
+def test_gate_up_sampled_rows():
+    w = synth.WORKLOADS["gate_up"]
+    x = synth.make_inputs(w)
+    plan = la.gemm_plan(w.M, w.N, w.K, la.BF16, la.BF16, gate_up=True)
+    X, Wg, Wu = x["A"].to(DEV), x["Wg"].to(DEV), x["Wu"].to(DEV)
+    G = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=DEV)
+    U = torch.empty_like(G)
+    la.gemm_gate_up_run(plan, X, Wg, Wu, G, U)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 24, 4004)
+    for name, W, out in (("G", x["Wg"], G), ("U", x["Wu"], U)):
+        ref = oracle_gemm(x["A"], W, "bf16", rows=rows)
+        assert_close(out.cpu()[rows], ref, w.K, x["A"], W, "bf16", "gate_up " + name)
+
+
+SHAPES = [(1, 1, 1), (1, 7, 3), (33, 65, 17), (64, 64, 64), (127, 129, 65), (129, 257, 130),
+          (200, 72, 1000), (300, 300, 8), (5, 1000, 333), (257, 31, 64)]
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_shapes_and_types(shape, in_kind, out_kind):
+    M, N, K = shape
+    seed = M * 7 + N * 13 + K
+    a = synth.uniform((M, K), seed, in_kind)
+    b = synth.uniform((K, N), seed + 1, in_kind)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    alpha, beta = 0.75, 1.25
+    got = run_gemm(a, b, out_kind, alpha, beta, c)
+    ref = oracle_gemm(a, b, in_kind, alpha, beta, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "shape %s" % (shape,))
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+def test_identity_and_permutation_B_are_exact(in_kind):
+    K, M = 256, 192
+    a = synth.uniform((M, K), 17, in_kind)
+    eye = torch.eye(K, dtype=synth.torch_dtype(in_kind))
+    got = run_gemm(a, eye, "f32")
+    assert torch.equal(got, a.to(torch.float32))
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(18))
+    P = torch.zeros((K, K), dtype=synth.torch_dtype(in_kind))
+    P[perm, torch.arange(K)] = 1
+    got = run_gemm(a, P, "f32")
+    assert torch.equal(got, a.to(torch.float32)[:, perm])
+    got16 = run_gemm(a, P, in_kind)          # 16-bit output of an exact value is exact
+    assert torch.equal(got16, a[:, perm])
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+def test_ones_times_ones_is_K(in_kind):
+    for (M, N, K) in [(100, 300, 4096), (130, 70, 999)]:
+        a = torch.ones((M, K), dtype=synth.torch_dtype(in_kind))
+        b = torch.ones((K, N), dtype=synth.torch_dtype(in_kind))
+        got = run_gemm(a, b, "f32")
+        assert torch.all(got == K)
+
+
+def test_beta_zero_never_reads_C():
+    M, N, K = 150, 170, 90
+    a = synth.uniform((M, K), 1, "bf16")
+    b = synth.uniform((K, N), 2, "bf16")
+    c = torch.full((M, N), float("nan"))
+    got = run_gemm(a, b, "f32", 1.0, 0.0, c)
+    assert torch.isfinite(got).all()
+    ref = oracle_gemm(a, b, "bf16")
+    assert_close(got, ref, K, a, b, "f32", "beta=0")
+
+
+def test_k_zero_and_empty_outputs():
+    M, N = 70, 90
+    c = synth.uniform((M, N), 3, "f32")
+    a = torch.zeros((M, 0), dtype=torch.bfloat16)
+    b = torch.zeros((0, N), dtype=torch.bfloat16)
+    got = run_gemm(a, b, "f32", 3.0, -0.5, c)
+    assert torch.equal(got, c * -0.5)
+    for (m, n, k) in [(0, 5, 7), (5, 0, 7), (0, 0, 0)]:
+        plan = la.gemm_plan(m, n, k, la.BF16, la.F32)
+        A = torch.zeros((m, k), dtype=torch.bfloat16, device=DEV)
+        B = torch.zeros((k, n), dtype=torch.bfloat16, device=DEV)
+        C = torch.zeros((m, n), dtype=torch.float32, device=DEV)
+        la.gemm_run(plan, A, B, C)
+    torch.cuda.synchronize()
+
+
+def test_ragged_never_writes_outside_C():
+    """C is a window of a bigger buffer: padding columns and rows stay untouched."""
+    w = synth.WORKLOADS["ragged"]
+    x = synth.make_inputs(w)
+    M, N, K, ldc = w.M, w.N, w.K, w.N + 63
+    big = torch.full((M + 5, ldc), 12345.0, dtype=torch.float32, device=DEV)
+    C = big[:M, :N]
+    C.copy_(x["C"].to(DEV))
+    plan = la.gemm_plan(M, N, K, la.F16, la.F32, ldc=ldc)
+    la.gemm_run(plan, x["A"].to(DEV), x["B"].to(DEV), C, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    big = big.cpu()
+    assert torch.all(big[:M, N:] == 12345.0)
+    assert torch.all(big[M:, :] == 12345.0)
+    ref = oracle_gemm(x["A"], x["B"], "f16", w.alpha, w.beta, x["C"])
+    assert_close(big[:M, :N], ref, K, x["A"], x["B"], "f32", "ragged window")
+
+
+def test_deterministic_and_plan_reuse():
+    M, N, K = 512, 384, 700
+    a = synth.normal((M, K), 5, "bf16")
+    b = synth.normal((K, N), 6, "bf16")
+    plan = la.gemm_plan(M, N, K, la.BF16, la.F32)
+    A, B = a.to(DEV), b.to(DEV)
+    C1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    C2 = torch.empty_like(C1)
+    la.gemm_run(plan, A, B, C1)
+    la.gemm_run(plan, A, B, C2)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    # same plan, modified input values
+    a2 = synth.normal((M, K), 7, "bf16")
+    A.copy_(a2.to(DEV))
+    la.gemm_run(plan, A, B, C2)
+    torch.cuda.synchronize()
+    ref = oracle_gemm(a2, b, "bf16")
+    assert_close(C2.cpu(), ref, K, a2, b, "f32", "reuse")
+
+
+def test_graph_capture_replay():
+    M, N, K = 384, 512, 320
+    a = synth.normal((M, K), 8, "bf16")
+    b = synth.normal((K, N), 9, "bf16")
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16)
+    A, B = a.to(DEV), b.to(DEV)
+    C = torch.zeros((M, N), dtype=torch.bfloat16, device=DEV)
+    eager = torch.empty_like(C)
+    la.gemm_run(plan, A, B, eager)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        la.gemm_run(plan, A, B, C)       # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.gemm_run(plan, A, B, C)
+    for it in range(4):
+        C.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, eager), "replay %d" % it
+        A.add_(0)                        # unrelated eager work between replays
+
+
+def _lds_image(plan, A, B, B2, tm, tn):
+    nbytes = la.gemm_plan_lds_stage_bytes(plan)
+    out = torch.zeros(nbytes // 2, dtype=torch.int16, device=DEV)
+    la.gemm_debug_lds_image(plan, A, B, B2, tm, tn, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def _expected_image(plan, ops, tm, tn):
+    """Build the predicted stage from the planner's offsets and the host operands."""
+    d = la.gemm_plan_describe(plan)
+    bm, bn, bk = d["tile"]
+    img = np.full(d["stage_elems"], 0xDEAD, dtype=np.uint32)
+    for operand, (mat, rows, cols, r0, c0) in enumerate(ops):
+        bits = synth.bits(mat)
+        for r in range(rows):
+            for c in range(cols):
+                gr, gc = r0 + r, c0 + c
+                v = bits[gr, gc] if gr < bits.shape[0] and gc < bits.shape[1] else 0
+                img[la.gemm_plan_lds_offset(plan, operand, r, c)] = v
+    return img, (bm, bn, bk)
+
+
+@pytest.mark.parametrize("case", ["bf16_interior", "f16_ragged_edge", "gate_up"])
+def test_lds_image_matches_planner(case):
+    if case == "bf16_interior":
+        M, N, K, kind, gu, tm, tn = 256, 256, 256, "bf16", False, 1, 1
+    elif case == "f16_ragged_edge":
+        M, N, K, kind, gu, tm, tn = 1000, 1537, 999, "f16", False, 7, 12
+    else:
+        M, N, K, kind, gu, tm, tn = 256, 384, 128, "bf16", True, 1, 2
+    a = synth.uniform((M, K), 21, kind)
+    b = synth.uniform((K, N), 22, kind)
+    b2 = synth.uniform((K, N), 23, kind) if gu else None
+    plan = la.gemm_plan(M, N, K, CODE[kind], la.F32, gate_up=gu)
+    d = la.gemm_plan_describe(plan)
+    bm, bn, bk = d["tile"]
+    ops = [(a, bm, bk, tm * bm, 0), (b, bk, bn, 0, tn * bn)]
+    if gu:
+        ops.append((b2, bk, bn, 0, tn * bn))
+    want, _ = _expected_image(plan, ops, tm, tn)
+    got = _lds_image(plan, a.to(DEV), b.to(DEV), b2.to(DEV) if gu else None, tm, tn)
+    assert not np.any(want == 0xDEAD), "planner map does not cover the stage"
+    assert np.array_equal(got.astype(np.uint32), want)
