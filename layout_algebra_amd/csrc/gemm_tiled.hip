@@ -245,18 +245,6 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
 }
 
 // ------------------------------------------------------------------ dispatch
-KernelShape kernel_shape(int kid) {
-  switch (kid) {
-    case KID_TILED_128: return KernelShape{128, 128, 64, 2, 2, 256, 32, 32, 16, 3, 3, 3, 2};
-    default: return KernelShape{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  }
-}
-
-int64_t stage_elems(int kid, bool gate_up) {
-  const KernelShape s = kernel_shape(kid);
-  return int64_t(s.bm) * s.bk + (gate_up ? 2 : 1) * int64_t(s.bn) * s.bk;
-}
-
 namespace {
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>

@@ -1,0 +1,37 @@
+// Kernel table and dispatch across kernel families (host code).
+#include "launch.hpp"
+
+namespace lak {
+
+template <class C>
+static KernelShape fast_shape() {
+  return KernelShape{C::BM, C::BN, 64, C::NB, C::WM, C::WN, C::WM * C::WN * 64, 32, 32, 16,
+                     {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS}, 0, 1, 1, 2};
+}
+
+KernelShape kernel_shape(int kid) {
+  switch (kid) {
+    case KID_TILED_128:
+      return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 3}, {3, 3, 3}, 1, 0, 0, 2};
+    case KID_FAST_256: return fast_shape<CfgFast256>();
+    case KID_FAST_GU: return fast_shape<CfgFastGU>();
+    default:
+      return KernelShape{};
+  }
+}
+
+int64_t stage_elems(const KernelShape& s, bool gate_up) {
+  return int64_t(s.bm) * s.bk + int64_t(gate_up ? 2 : 1) * s.bn * s.bk;
+}
+
+hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, const TiledArgs& args, int grid,
+                         hipStream_t stream, bool lds_image) {
+  switch (kid) {
+    case KID_TILED_128: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, args, grid, stream, lds_image);
+    case KID_FAST_256:
+    case KID_FAST_GU: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lak

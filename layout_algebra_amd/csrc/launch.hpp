@@ -6,7 +6,7 @@
 
 namespace lak {
 
-// Everything one launch of a tiled kernel needs; plain values only.
+// Everything one launch needs; plain values only.
 struct TiledArgs {
   const uint16_t* A;     // [M, K] row-major, lda
   const uint16_t* B;     // [K, N] N contiguous, ldb (W_gate for gate/up)
@@ -21,30 +21,56 @@ struct TiledArgs {
 };
 
 enum KernelId : int {
-  KID_TILED_128 = 0,     // 128x128x64 tile, 4 waves of 64x64
+  KID_TILED_128 = 0,     // any shape: 128x128x64, 4 waves of 64x64, register-staged, B transposed while staging
+  KID_FAST_256 = 1,      // full tiles: 256x256x64, 8 waves of 128x64, direct-to-LDS, transposing B reads
+  KID_FAST_GU = 2,       // full tiles, gate/up: 256 x (128 + 128) x 64, 8 waves of 128 x (32 + 32)
   KID_COUNT
 };
 
 enum InKind : int { IN_BF16 = 0, IN_F16 = 1 };
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
+// Compile-time parameters of the fast kernels (one source of truth for the
+// template instantiations and the planner's table).
+struct CfgFast256 {
+  static constexpr int BM = 256, BN = 256, NB = 1, WM = 2, WN = 4;
+  static constexpr int AB = 3, AM = 3, AS = 3;   // A: Swizzle{3,3,3}
+  static constexpr int BB = 3, BMb = 3, BS = 5;  // B: Swizzle{3,3,5}
+};
+struct CfgFastGU {
+  static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4;
+  static constexpr int AB = 3, AM = 3, AS = 3;
+  static constexpr int BB = 3, BMb = 3, BS = 4;
+};
+
 struct KernelShape {
-  int bm, bn, bk;
+  int bm, bn, bk;          // bn is per weight matrix
+  int nb;                  // weight matrices per launch (2 for gate/up)
   int waves_m, waves_n;
   int threads;
   int mfma_m, mfma_n, mfma_k;
-  int sw_b, sw_m, sw_s;    // LDS swizzle (element offsets)
+  int sw_a[3];             // Swizzle{B,M,S} of the A block, element offsets over (bm,bk):(bk,1)
+  int sw_b[3];             // Swizzle{B,M,S} of a B block
+  int b_kmajor;            // 1: B block stored (bn,bk):(bk,1) (K contiguous); 0: (bk,bn):(bn,1)
+  int direct;              // 1: global -> LDS direct loads (whole 1 KB per wave instruction)
+  int full_tiles_only;     // 1: M % bm == 0, N % bn == 0, K % bk == 0 required
   int stages;
 };
 
-// Static description of each kernel id (host and device agree through this table).
+// Static description of each kernel id; the planner validates these maps.
 KernelShape kernel_shape(int kid);
 
-// LDS elements (16-bit) of one pipeline stage for a kernel id.
-int64_t stage_elems(int kid, bool gate_up);
+// LDS elements (16-bit) of one pipeline stage (one A block and one B block per weight).
+int64_t stage_elems(const KernelShape& s, bool gate_up);
 
 // Enqueue a GEMM (or, with lds_image, the debug stage dump) on `stream`.
+hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up,
+                         const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
+
+// Per-family launchers.
 hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up,
                         const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
+hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, int grid,
+                       hipStream_t stream, bool lds_image);
 
 }  // namespace lak

@@ -86,6 +86,66 @@ bool check_copy_b(const gemm_plan_s& p, const la::View& v, std::string* err) {
   return true;
 }
 
+// Direct global -> LDS copy: wave instruction `blk` writes the contiguous
+// kilobyte [512 blk, 512 blk + 512) (elements) with lane l at 8 l.  The lane's
+// 8 elements must be 8 consecutive elements of one row of the operand as it
+// sits in global memory (K for A, N for B), so one 16-byte load feeds them.
+bool check_copy_direct(const la::View& v, int64_t rows, int64_t cols, bool contiguous_in_cols, const char* name,
+                       std::string* err) {
+  const int64_t n = rows * cols;
+  if (n % 512) return fail(err, std::string(name) + " block is not a whole number of kilobytes");
+  std::vector<int64_t> inv(n, -1);   // physical offset -> row * cols + col
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      const int64_t o = v.at({r, c});
+      if (o < 0 || o >= n || inv[o] != -1) return fail(err, std::string(name) + " LDS map is not a bijection onto its block");
+      inv[o] = r * cols + c;
+    }
+  for (int64_t p = 0; p < n; p += 8) {
+    const int64_t r0 = inv[p] / cols, c0 = inv[p] % cols;
+    for (int e = 1; e < 8; ++e) {
+      const int64_t r = inv[p + e] / cols, c = inv[p + e] % cols;
+      const bool ok = contiguous_in_cols ? (r == r0 && c == c0 + e) : (c == c0 && r == r0 + e);
+      if (!ok) return fail(err, std::string(name) + " direct copy: a 16-byte LDS chunk is not 8 contiguous source elements");
+    }
+  }
+  return true;
+}
+
+// LDS -> register reads of the fast kernels.  A: lane l of fragment row block
+// reads 8 consecutive K values of row l % 32 as one 16-byte chunk.  B:
+// transposing reads, where lanes 4e..4e+3 of each 16-lane group address 4
+// consecutive N values (8 bytes) of K row e.  Both need those runs to be
+// contiguous and aligned in the LDS map.
+bool check_fragment_reads(const gemm_plan_s& p, std::string* err) {
+  const auto& s = p.shape;
+  for (int64_t r = 0; r < s.bm; ++r)
+    for (int64_t k = 0; k < s.bk; k += 8) {
+      const int64_t o = p.lds_a.at({r, k});
+      if (o % 8) return fail(err, "A fragment read is not 16-byte aligned");
+      for (int e = 1; e < 8; ++e)
+        if (p.lds_a.at({r, k + e}) != o + e) return fail(err, "A fragment read is not contiguous");
+    }
+  if (!s.b_kmajor) {
+    for (int64_t k = 0; k < s.bk; ++k)
+      for (int64_t n = 0; n < s.bn; n += 4) {
+        const int64_t o = p.lds_b.at({k, n});
+        if (o % 4) return fail(err, "B transposing read is not 8-byte aligned");
+        for (int e = 1; e < 4; ++e)
+          if (p.lds_b.at({k, n + e}) != o + e) return fail(err, "B transposing read is not contiguous");
+      }
+  } else {
+    for (int64_t n = 0; n < s.bn; ++n)
+      for (int64_t k = 0; k < s.bk; k += 8) {
+        const int64_t o = p.lds_b.at({k, n});
+        if (o % 8) return fail(err, "B fragment read is not 16-byte aligned");
+        for (int e = 1; e < 8; ++e)
+          if (p.lds_b.at({k + e, n}) != o + e) return fail(err, "B fragment read is not contiguous");
+      }
+  }
+  return true;
+}
+
 // MFMA 32x32 result ownership: register r of lane l of fragment (i, j) of wave
 // (wm, wn) holds tile element (wm*TM + 32 i + 8 (r/4) + 4 (l/32) + r%4,
 //                              wn*TN + 32 j + l%32).
@@ -159,7 +219,18 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p.vec = (d.lda % 8 == 0 && d.ldb % 8 == 0) ? 8 : 1;
   p.align_bytes = 2 * p.vec;
 
+  // Kernel choice: the full-tile direct-load kernels when every tile is whole
+  // and every row starts on 16 bytes; otherwise the general kernel, which
+  // masks edges and narrows its loads to the alignment class.
   p.kid = lak::KID_TILED_128;
+  {
+    const int fk = p.gate_up ? lak::KID_FAST_GU : lak::KID_FAST_256;
+    const lak::KernelShape fs = lak::kernel_shape(fk);
+    const bool whole = d.m > 0 && d.n > 0 && d.k > 0 && d.m % fs.bm == 0 && d.n % fs.bn == 0 && d.k % fs.bk == 0;
+    const bool rows16 = d.lda % 8 == 0 && d.ldb % 8 == 0;
+    const bool off32 = int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && int64_t(fs.bk) * d.ldb < (int64_t{1} << 32);
+    if (whole && rows16 && off32) p.kid = fk;
+  }
   p.shape = lak::kernel_shape(p.kid);
   const auto& s = p.shape;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
@@ -169,28 +240,38 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p.group_m = 8;
 
   try {
-    const la::Swizzle sw(s.sw_b, s.sw_m, s.sw_s);
-    p.lds_a = la::View(sw, la::Layout::row_major(s.bm, s.bk, s.bk));   // (m, k) -> m*BK + k
-    p.lds_b = la::View(sw, la::Layout::col_major(s.bk, s.bn, s.bk));   // (k, n) -> n*BK + k
+    const la::Swizzle swa(s.sw_a[0], s.sw_a[1], s.sw_a[2]);
+    const la::Swizzle swb(s.sw_b[0], s.sw_b[1], s.sw_b[2]);
+    p.lds_a = la::View(swa, la::Layout::row_major(s.bm, s.bk, s.bk));           // (m, k) -> m*BK + k
+    p.lds_b = s.b_kmajor ? la::View(swb, la::Layout::col_major(s.bk, s.bn, s.bk))   // (k, n) -> n*BK + k
+                         : la::View(swb, la::Layout::row_major(s.bk, s.bn, s.bn));  // (k, n) -> k*BN + n
     p.lds_b2 = p.lds_b;
     p.base_a = 0;
     p.base_b = int64_t(s.bm) * s.bk;
     p.base_b2 = p.base_b + int64_t(s.bn) * s.bk;
-    p.stage_elems = lak::stage_elems(p.kid, p.gate_up);
+    p.stage_elems = lak::stage_elems(s, p.gate_up);
     p.lds_bytes = int64_t(s.stages) * p.stage_elems * 2;
     if (p.lds_bytes > kMaxLdsBytes) { fail(err, "LDS footprint exceeds 160 KiB"); return GEMM_ERR_RESOURCE; }
     if (!check_block(p.lds_a, p.base_a, int64_t(s.bm) * s.bk, "A", err) ||
         !check_block(p.lds_b, p.base_b, int64_t(s.bn) * s.bk, "B", err) ||
         (p.gate_up && !check_block(p.lds_b2, p.base_b2, int64_t(s.bn) * s.bk, "W_up", err)))
       return GEMM_ERR_RESOURCE;
-    if (!check_copy_a(p, err) || !check_copy_b(p, p.lds_b, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
+    if (s.direct) {
+      if (!check_copy_direct(p.lds_a, s.bm, s.bk, true, "A", err) ||
+          !check_copy_direct(p.lds_b, s.bk, s.bn, !s.b_kmajor, "B", err))
+        return GEMM_ERR_RESOURCE;
+    } else if (!check_copy_a(p, err) || !check_copy_b(p, p.lds_b, err)) {
+      return GEMM_ERR_RESOURCE;
+    }
+    if (!check_fragment_reads(p, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
   } catch (const la::LayoutError& e) {
     fail(err, e.what());
     return GEMM_ERR_RESOURCE;
   }
 
   std::ostringstream js;
-  js << "{\"kernel\":\"tiled_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
+  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up"};
+  js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
      << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc
      << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"out\":\"" << dtype_name(d.c_type) << "\""
@@ -200,7 +281,9 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
      << ",\"mfma\":\"" << s.mfma_m << "x" << s.mfma_n << "x" << s.mfma_k << "\""
      << ",\"tiles\":[" << p.tiles_m << "," << p.tiles_n << "],\"grid\":" << p.grid << ",\"group_m\":" << p.group_m
      << ",\"stages\":" << s.stages << ",\"stage_elems\":" << p.stage_elems << ",\"lds_bytes\":" << p.lds_bytes
-     << ",\"swizzle\":[" << s.sw_b << "," << s.sw_m << "," << s.sw_s << "]"
+     << ",\"swizzle_a\":[" << s.sw_a[0] << "," << s.sw_a[1] << "," << s.sw_a[2] << "]"
+     << ",\"swizzle_b\":[" << s.sw_b[0] << "," << s.sw_b[1] << "," << s.sw_b[2] << "]"
+     << ",\"direct_loads\":" << (s.direct ? "true" : "false")
      << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
      << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes << "}";
   p.json = js.str();

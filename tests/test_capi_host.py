@@ -106,24 +106,32 @@ def test_workload_plans_build(name):
     assert d["grid"] >= 1
 
 
-def test_planner_lds_map_agrees_with_reference():
-    p = la.gemm_plan(4096, 4096, 4096, la.BF16, la.BF16)
+@pytest.mark.parametrize("shape", [(4096, 4096, 4096, False), (1000, 1537, 999, False), (4096, 11008, 4096, True)],
+                         ids=["fast", "tiled", "fast_gate_up"])
+def test_planner_lds_map_agrees_with_reference(shape):
+    m, n, k, gu = shape
+    p = la.gemm_plan(m, n, k, la.BF16, la.BF16, gate_up=gu)
     d = p.describe()
     bm, bn, bk = d["tile"]
-    sw = L.Swizzle(*d["swizzle"])
-    a_ref = L.compose(sw, L.Layout((bm, bk), (bk, 1)))
-    b_ref = L.compose(sw, L.Layout((bk, bn), (1, bk)))
+    a_ref = L.compose(L.Swizzle(*d["swizzle_a"]), L.Layout((bm, bk), (bk, 1)))
+    if d["lds_b"] == "(%d,%d):(1,%d)" % (bk, bn, bk):          # K-contiguous B block
+        b_ref = L.compose(L.Swizzle(*d["swizzle_b"]), L.Layout((bk, bn), (1, bk)))
+    else:                                                      # N-contiguous B block
+        assert d["lds_b"] == "(%d,%d):(%d,1)" % (bk, bn, bn)
+        b_ref = L.compose(L.Swizzle(*d["swizzle_b"]), L.Layout((bk, bn), (bn, 1)))
     seen = set()
     for r in range(bm):
         for c in range(bk):
             o = la.gemm_plan_lds_offset(p, 0, r, c)
             assert o == a_ref((r, c))
             seen.add(o)
-    for r in range(bk):
-        for c in range(bn):
-            o = la.gemm_plan_lds_offset(p, 1, r, c)
-            assert o == bm * bk + b_ref((r, c))
-            seen.add(o)
+    for operand in ([1, 2] if gu else [1]):
+        base = bm * bk + (operand - 1) * bk * bn
+        for r in range(bk):
+            for c in range(bn):
+                o = la.gemm_plan_lds_offset(p, operand, r, c)
+                assert o == base + b_ref((r, c))
+                seen.add(o)
     assert len(seen) == d["stage_elems"]
 
 

@@ -243,19 +243,26 @@ def _expected_image(plan, ops, tm, tn):
     return img, (bm, bn, bk)
 
 
-@pytest.mark.parametrize("case", ["bf16_interior", "f16_ragged_edge", "gate_up"])
+LDS_CASES = {
+    # name: (M, N, K, kind, gate_up, tile_m, tile_n, expected kernel prefix)
+    "fast_bf16": (512, 512, 256, "bf16", False, 1, 1, "fast_"),
+    "fast_f16_last_tile": (768, 512, 128, "f16", False, 2, 1, "fast_"),
+    "tiled_bf16_interior": (384, 384, 200, "bf16", False, 1, 1, "tiled_"),
+    "tiled_f16_ragged_edge": (1000, 1537, 999, "f16", False, 7, 12, "tiled_"),
+    "fast_gate_up": (512, 256, 128, "bf16", True, 1, 1, "fast_gate_up_"),
+    "tiled_gate_up_edge": (300, 200, 100, "bf16", True, 2, 1, "tiled_"),
+}
+
+
+@pytest.mark.parametrize("case", list(LDS_CASES))
 def test_lds_image_matches_planner(case):
-    if case == "bf16_interior":
-        M, N, K, kind, gu, tm, tn = 256, 256, 256, "bf16", False, 1, 1
-    elif case == "f16_ragged_edge":
-        M, N, K, kind, gu, tm, tn = 1000, 1537, 999, "f16", False, 7, 12
-    else:
-        M, N, K, kind, gu, tm, tn = 256, 384, 128, "bf16", True, 1, 2
+    M, N, K, kind, gu, tm, tn, prefix = LDS_CASES[case]
     a = synth.uniform((M, K), 21, kind)
     b = synth.uniform((K, N), 22, kind)
     b2 = synth.uniform((K, N), 23, kind) if gu else None
     plan = la.gemm_plan(M, N, K, CODE[kind], la.F32, gate_up=gu)
     d = la.gemm_plan_describe(plan)
+    assert d["kernel"].startswith(prefix), d["kernel"]
     bm, bn, bk = d["tile"]
     ops = [(a, bm, bk, tm * bm, 0), (b, bk, bn, 0, tn * bn)]
     if gu:
@@ -264,3 +271,52 @@ def test_lds_image_matches_planner(case):
     got = _lds_image(plan, a.to(DEV), b.to(DEV), b2.to(DEV) if gu else None, tm, tn)
     assert not np.any(want == 0xDEAD), "planner map does not cover the stage"
     assert np.array_equal(got.astype(np.uint32), want)
+
+
+FAST_SHAPES = [(256, 256, 64), (512, 768, 320), (768, 512, 1024), (256, 1024, 4096)]
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", FAST_SHAPES, ids=[str(s) for s in FAST_SHAPES])
+def test_fast_kernel_shapes(shape, in_kind, out_kind):
+    M, N, K = shape
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind])
+    assert plan.describe()["kernel"].startswith("fast_")
+    seed = M + 3 * N + 7 * K
+    a = synth.normal((M, K), seed, in_kind)
+    b = synth.normal((K, N), seed + 1, in_kind, 0.5)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got = run_gemm(a, b, out_kind, -1.25, 0.5, c)
+    ref = oracle_gemm(a, b, in_kind, -1.25, 0.5, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "fast %s" % (shape,))
+
+
+@pytest.mark.parametrize("shape", [(512, 256, 192), (300, 200, 100), (256, 384, 64)],
+                         ids=["fast", "tiled_edges", "fast_min_k"])
+def test_gate_up_small(shape):
+    M, N, K = shape
+    x = synth.normal((M, K), 31, "bf16")
+    wg = synth.normal((K, N), 32, "bf16", 0.3)
+    wu = synth.normal((K, N), 33, "bf16", 0.3)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True)
+    G = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    U = torch.full_like(G, float("nan"))
+    la.gemm_gate_up_run(plan, x.to(DEV), wg.to(DEV), wu.to(DEV), G, U)
+    torch.cuda.synchronize()
+    for name, w, out in (("G", wg, G), ("U", wu, U)):
+        assert_close(out.cpu(), oracle_gemm(x, w, "bf16"), K, x, w, "bf16", "gate_up %s %s" % (name, shape))
+
+
+def test_fast_kernel_identity_is_exact():
+    K = 512
+    a = synth.uniform((256, K), 41, "bf16")
+    eye = torch.eye(K, dtype=torch.bfloat16)
+    plan = la.gemm_plan(256, K, K, la.BF16, la.F32)
+    assert plan.describe()["kernel"].startswith("fast_")
+    got = run_gemm(a, eye, "f32")
+    assert torch.equal(got, a.to(torch.float32))
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(42))
+    P = torch.zeros((K, K), dtype=torch.bfloat16)
+    P[perm, torch.arange(K)] = 1
+    assert torch.equal(run_gemm(a, P, "bf16"), a[:, perm])
