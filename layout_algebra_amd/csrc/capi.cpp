@@ -90,7 +90,8 @@ gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, fl
   if (p.d.k > 0 && (!A || !B)) return set_err(GEMM_ERR_NULL, "A or B is NULL");
   if (!aligned(A, p.align_bytes) || !aligned(B, p.align_bytes))
     return set_err(GEMM_ERR_ALIGNMENT, "A and B must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
-  if (!aligned(C, p.out_bytes)) return set_err(GEMM_ERR_ALIGNMENT, "C must be aligned to its element size");
+  if (!aligned(C, p.out_align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "C must be " + std::to_string(p.out_align_bytes) + "-byte aligned for this plan");
   lak::TiledArgs a = base_args(p);
   a.A = static_cast<const uint16_t*>(A);
   a.B = static_cast<const uint16_t*>(B);
@@ -110,8 +111,8 @@ gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate
   if (p.d.k > 0 && (!X || !W_gate || !W_up)) return set_err(GEMM_ERR_NULL, "X, W_gate or W_up is NULL");
   if (!aligned(X, p.align_bytes) || !aligned(W_gate, p.align_bytes) || !aligned(W_up, p.align_bytes))
     return set_err(GEMM_ERR_ALIGNMENT, "X, W_gate and W_up must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
-  if (!aligned(G, p.out_bytes) || !aligned(U, p.out_bytes))
-    return set_err(GEMM_ERR_ALIGNMENT, "G and U must be aligned to their element size");
+  if (!aligned(G, p.out_align_bytes) || !aligned(U, p.out_align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "G and U must be " + std::to_string(p.out_align_bytes) + "-byte aligned for this plan");
   lak::TiledArgs a = base_args(p);
   a.A = static_cast<const uint16_t*>(X);
   a.B = static_cast<const uint16_t*>(W_gate);

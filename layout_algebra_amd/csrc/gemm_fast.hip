@@ -8,13 +8,14 @@ template <class C, class TI, class TO>
 hipError_t go_fast(const TiledArgs& a, int grid, hipStream_t s, bool img) {
   constexpr int NT = C::WM * C::WN * 64;
   if (img) {
-    hipLaunchKernelGGL((gemm_fast_lds_image<TI, TO, C::BM, C::BN, C::NB, C::WM, C::WN, C::AB, C::AM, C::AS, C::BB,
-                                            C::BMb, C::BS>),
+    hipLaunchKernelGGL((gemm_fast_lds_image<TI, TO, C>),
                        dim3(1), dim3(NT), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_fast_kernel<TI, TO, C::BM, C::BN, C::NB, C::WM, C::WN, C::AB, C::AM, C::AS, C::BB,
-                                         C::BMb, C::BS>),
-                       dim3(grid), dim3(NT), 0, s, a);
+    if constexpr (C::SCHED == 2) {
+      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((gemm_fast_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

@@ -1,5 +1,5 @@
 // Fast tiled GEMM for gfx950: full tiles only (M % BM == 0, N % BN == 0,
-// K % 64 == 0, 16-byte aligned rows).
+// K % BK == 0, 16-byte aligned rows).
 //
 // Differences from the general kernel (gemm_tiled.hip):
 //  * Operands go global -> LDS directly (global_load_lds_dwordx4): each wave
@@ -15,11 +15,15 @@
 //    lanes 4e..4e+3 of the group point at row e (16 values) and lane i
 //    receives element i of rows 0..3.  Two such reads give the 8 K values.
 //  * A fragments are plain 16-byte LDS reads (K is contiguous in A).
-//  * 256 x 256 (or 256 x 2*128 for gate/up) tiles with 8 waves: one tile per
-//    CU at 4096^2, two waves per SIMD so one wave's MFMAs cover the other's
-//    LDS traffic.
-// The LDS maps are Swizzle{AB,AM,AS} o (BM,64):(64,1) for A and
-// Swizzle{BB,BMb,BS} o (64,BN):(BN,1) for B (element offsets).
+//  * Large tiles (256 x 256, or 256 x 2*128 for gate/up) with 8 waves: one
+//    tile per CU at 4096^2, two waves per SIMD.
+//  * A multi-stage LDS ring (STAGES buffers) keeps STAGES-1 K blocks in
+//    flight; one workgroup barrier per K block.
+//  * Inside a K block the fragments of sub-step s+1 are read while the MFMAs
+//    of sub-step s run (two register sets), and the instruction scheduler is
+//    told to alternate MFMAs with LDS reads so neither unit idles.
+// The LDS maps are Swizzle{AB,AM,AS} o (BM,BK):(BK,1) for A and
+// Swizzle{BB,BMb,BS} o (BK,BN):(BN,1) for B (element offsets).
 #pragma once
 
 #include "kernel_common.hpp"
@@ -31,25 +35,34 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LAK_LDS __attribute__((address_space(3)))
 #define LAK_GLB __attribute__((address_space(1)))
 
-template <class TI, class TO, int BM, int BN, int NB, int WM, int WN,
-          int AB, int AM, int AS, int BB, int BMb, int BS>
+// Scheduler group masks (LLVM AMDGPU sched_group_barrier).
+enum : int { SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100 };
+
+template <class TI, class C>
 struct Fast {
+  static constexpr int BM = C::BM, BN = C::BN, NB = C::NB, WM = C::WM, WN = C::WN, BK = C::BK;
+  static constexpr int STAGES = C::STAGES;
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
-  static constexpr int BK = 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int SUB = BK / 16;                      // MFMA K sub-steps per K block
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BK * BN;
-  static constexpr int STAGE = A_ELEMS + NB * B_ELEMS;   // 16-bit elements
+  static constexpr int STAGE = A_ELEMS + NB * B_ELEMS;     // 16-bit elements
   static constexpr int A_LOADS = A_ELEMS / 512 / NW;       // 1 KB (512 elements) per wave instruction
   static constexpr int B_LOADS = B_ELEMS / 512 / NW;
+  static constexpr int LOADS_PER_STAGE = A_LOADS + NB * B_LOADS;
+  static constexpr int READS_PER_SUB = FM + 2 * NB * FN;   // LDS read instructions per sub-step
+  static constexpr int MFMA_PER_SUB = NB * FM * FN;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_LOADS * 512 * NW == A_ELEMS && B_LOADS * 512 * NW == B_ELEMS, "blocks must split into whole KB per wave");
-  static_assert(AM >= 3 && BMb >= 3, "swizzles must keep 16-byte chunks whole");
+  static_assert(C::AM >= 3 && C::BMb >= 3, "swizzles must keep 16-byte chunks whole");
+  static_assert(BK % 16 == 0 && STAGES >= 2, "K block and pipeline depth");
+  static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
 
-  static __device__ __forceinline__ int a_off(int r, int k) { return swz<AB, AM, AS>(r * BK + k); }
-  static __device__ __forceinline__ int b_off(int k, int n) { return swz<BB, BMb, BS>(k * BN + n); }
+  static __device__ __forceinline__ int a_off(int r, int k) { return swz<C::AB, C::AM, C::AS>(r * BK + k); }
+  static __device__ __forceinline__ int b_off(int k, int n) { return swz<C::BB, C::BMb, C::BS>(k * BN + n); }
 
   // Per-lane source offsets (elements, relative to the tile's origin in the
   // current K block) of every direct load this lane issues.
@@ -62,32 +75,44 @@ struct Fast {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int P = (wave * A_LOADS + i) * 512 + lane * 8;     // physical element this lane fills
-      const int L = swz<AB, AM, AS>(P);                        // logical element it must hold
+      const int L = swz<C::AB, C::AM, C::AS>(P);               // logical element it must hold
       s.a[i] = uint32_t((L / BK) * lda + (L % BK));
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int P = (wave * B_LOADS + i) * 512 + lane * 8;
-      const int L = swz<BB, BMb, BS>(P);
+      const int L = swz<C::BB, C::BMb, C::BS>(P);
       s.b[i] = uint32_t((L / BN) * ldb + (L % BN));
     }
   }
 
-  // Issue this wave's direct loads of one K block into `stage` (byte address space 3).
+  // One direct load: 64 lanes x 16 bytes from base + voff (bytes, per lane)
+  // into the kilobyte of LDS at byte address `lds_addr` (wave-uniform, via M0).
+  // Written as inline assembly so that the compiler's wait-count pass does not
+  // see an LDS write it cannot disambiguate: it would otherwise stall every
+  // later LDS read until all loads in flight have landed.  Completion is
+  // tracked explicitly with vmcnt waits before each barrier.
+  static __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, const LAK_LDS uint16_t* dst) {
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_addr), "v"(voff), "s"(base)
+        : "memory", "m0");
+  }
+
+  // Issue this wave's direct loads of one K block into `stage`.
   static __device__ __forceinline__ void issue(const Src& s, LAK_LDS uint16_t* stage, const uint16_t* a_blk,
                                                const uint16_t* b_blk, const uint16_t* b2_blk, int wave) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const LAK_GLB void*)(a_blk + s.a[i]),
-                                       (LAK_LDS void*)(stage + (wave * A_LOADS + i) * 512), 16, 0, 0);
+    for (int i = 0; i < A_LOADS; ++i) dma16(a_blk, s.a[i] * 2u, stage + (wave * A_LOADS + i) * 512);
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const uint16_t* bb = t == 0 ? b_blk : b2_blk;
 #pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const LAK_GLB void*)(bb + s.b[i]),
-                                         (LAK_LDS void*)(stage + A_ELEMS + t * B_ELEMS + (wave * B_LOADS + i) * 512),
-                                         16, 0, 0);
+      for (int i = 0; i < B_LOADS; ++i) dma16(bb, s.b[i] * 2u, stage + A_ELEMS + t * B_ELEMS + (wave * B_LOADS + i) * 512);
     }
   }
 
@@ -99,55 +124,291 @@ struct Fast {
     return __builtin_bit_cast(u32x2, v);
   }
 
-  static __device__ __forceinline__ void compute(const LAK_LDS uint16_t* stage, f32x16 (&acc)[NB][FM][FN], int wm, int wn,
-                                                 int lane) {
-    const int ar = wm * TM + (lane & 31);
-    const int ak = (lane >> 5) * 8;
-    const int g = lane >> 4;
-    const int bn = wn * TN + 16 * (g & 1) + 4 * (lane & 3);
-    const int bk = 8 * (g >> 1) + ((lane >> 2) & 3);
+  // Lane-dependent parts of the fragment addresses.
+  struct Lane {
+    int ar, ak, bn, bk;
+    __device__ __forceinline__ Lane(int wm, int wn, int lane) {
+      ar = wm * TM + (lane & 31);                // A: row l % 32 of each 32-row block
+      ak = (lane >> 5) * 8;                      // A: K half of the 16-wide sub-step
+      const int g = lane >> 4;                   // B: 16-lane group
+      bn = wn * TN + 16 * (g & 1) + 4 * (lane & 3);
+      bk = 8 * (g >> 1) + ((lane >> 2) & 3);
+    }
+  };
+
+  struct Frags {
+    u32x4 a[FM];
+    u32x4 b[NB][FN];
+  };
+
+  static __device__ __forceinline__ void read_frags(const LAK_LDS uint16_t* stage, int s, const Lane& ln, Frags& f) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      u32x4 a[FM];
-      u32x4 b[NB][FN];
+    for (int i = 0; i < FM; ++i) f.a[i] = read_b128(stage + a_off(ln.ar + i * 32, s * 16 + ln.ak));
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = read_b128(stage + a_off(ar + i * 32, s * 16 + ak));
+    for (int t = 0; t < NB; ++t) {
+      const LAK_LDS uint16_t* bs = stage + A_ELEMS + t * B_ELEMS;
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const LAK_LDS uint16_t* bs = stage + A_ELEMS + t * B_ELEMS;
+      for (int j = 0; j < FN; ++j) {
+        const u32x2 lo = read_tr(bs + b_off(s * 16 + ln.bk, ln.bn + j * 32));
+        const u32x2 hi = read_tr(bs + b_off(s * 16 + ln.bk + 4, ln.bn + j * 32));
+        f.b[t][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[NB][FM][FN]) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const u32x2 lo = read_tr(bs + b_off(s * 16 + bk, bn + j * 32));
-          const u32x2 hi = read_tr(bs + b_off(s * 16 + bk + 4, bn + j * 32));
-          b[t][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[t][i][j] = mfma_32x32x16<TI>(f.a[i], f.b[t][j], acc[t][i][j]);
+  }
+
+  // Ask the scheduler to alternate the MFMAs of one sub-step with the LDS
+  // reads of the next.
+  static __device__ __forceinline__ void interleave() {
+    if constexpr (C::SCHED) {
+      constexpr int pairs = MFMA_PER_SUB < READS_PER_SUB ? MFMA_PER_SUB : READS_PER_SUB;
+#pragma unroll
+      for (int i = 0; i < pairs; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      }
+      if constexpr (MFMA_PER_SUB > pairs) __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFMA_PER_SUB - pairs, 0);
+      if constexpr (READS_PER_SUB > pairs) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, READS_PER_SUB - pairs, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void compute(const LAK_LDS uint16_t* stage, f32x16 (&acc)[NB][FM][FN], const Lane& ln) {
+    if constexpr (C::SCHED) {
+      Frags f0, f1;
+      read_frags(stage, 0, ln, f0);
+#pragma unroll
+      for (int s = 0; s < SUB; s += 2) {
+        if (s + 1 < SUB) read_frags(stage, s + 1, ln, f1);
+        mma(f0, acc);
+        interleave();
+        if (s + 1 < SUB) {
+          if (s + 2 < SUB) read_frags(stage, s + 2, ln, f0);
+          mma(f1, acc);
+          interleave();
         }
       }
+    } else {
 #pragma unroll
-      for (int t = 0; t < NB; ++t)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[t][i][j] = mfma_32x32x16<TI>(a[i], b[t][j], acc[t][i][j]);
+      for (int s = 0; s < SUB; ++s) {
+        Frags f;
+        read_frags(stage, s, ln, f);
+        mma(f, acc);
+      }
     }
   }
 };
 
-template <class TI, class TO, int BM, int BN, int NB, int WM, int WN, int AB, int AM, int AS, int BB, int BMb, int BS>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_fast_kernel(const TiledArgs g) {
-  using F = Fast<TI, TO, BM, BN, NB, WM, WN, AB, AM, AS, BB, BMb, BS>;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[2 * F::STAGE];
+// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// direct loads still in flight).  The empty asm statements with a memory
+// clobber keep the compiler from moving LDS accesses across it; LDS reads
+// issued before it have been waited for by their consumers.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are complete
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
+// Epilogue through LDS: each wave writes alpha * acc of one 32-row band of its
+// sub-tile (32 x TN, FP32) into its own padded LDS window, reads it back as
+// rows, and writes 8 consecutive outputs per lane (16 bytes for 16-bit types),
+// so every row segment leaves as whole vectors instead of one element per lane
+// and register.  beta * C_old is added on the way out, reading C_old with the
+// same vectors (only when beta != 0).  All LDS reads of the main loop must be
+// finished before the first wave writes its window.
+template <class TO, class F>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, float alpha, float beta,
+                                           bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane) {
+  constexpr int TN = F::TN;
+  constexpr int PITCH = TN + 8;                      // floats: rows r and r+4 land 32 banks apart
+  typedef typename TO::storage St;
+  St* C = static_cast<St*>(Cv);
+  const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < F::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < F::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) win[(8 * (e >> 2) + lr4 + (e & 3)) * PITCH + j * 32 + lc] = alpha * acc[i][j][e];
+    __builtin_amdgcn_s_waitcnt(0xC07F);              // this wave's LDS writes are done
+    constexpr int CH = TN / 8;                       // 8-element chunks per row
+    constexpr int ROWS_PER_PASS = 64 / CH;
+#pragma unroll
+    for (int q = 0; q < 32 / ROWS_PER_PASS; ++q) {
+      const int r = q * ROWS_PER_PASS + lane / CH;
+      const int c = (lane % CH) * 8;
+      const LAK_LDS float* src = win + r * PITCH + c;
+      const f32x4 lo = *reinterpret_cast<const LAK_LDS f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const LAK_LDS f32x4*>(src + 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      St* dst = C + (row0 + i * 32 + r) * ldc + col0 + c;
+      if (use_beta) {
+        if constexpr (sizeof(St) == 4) {
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(dst);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(dst + 4);
+          const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += beta * o[e];
+        } else {
+          const u32x4 ow = *reinterpret_cast<const u32x4*>(dst);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+        }
+      }
+      if constexpr (sizeof(St) == 4) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      } else {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = uint32_t(to_out<TO>(v[2 * e])) | (uint32_t(to_out<TO>(v[2 * e + 1])) << 16);
+        *reinterpret_cast<u32x4*>(dst) = w;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);              // reads done before the next band overwrites the window
+  }
+}
+
+template <class TO, class F, int NB>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[NB][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
+                                         int wm, int wn, int wave, int lane, LAK_LDS uint16_t* lds) {
+  LAK_LDS float* win = reinterpret_cast<LAK_LDS float*>(lds) + wave * 32 * (F::TN + 8);
+  const int64_t row0 = m0 + wm * F::TM, col0 = n0 + wn * F::TN;
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+    store_tile<TO, F>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0, col0, win, lane);
+}
+
+template <class TI, class TO, class C>
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const TiledArgs g) {
+  using F = Fast<TI, C>;
+  constexpr int NB = C::NB;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
   LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % WM, wn = wave / WM;
+  const int wm = wave % C::WM, wn = wave / C::WM;
   int tm, tn;
   grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t m0 = int64_t(tm) * C::BM, n0 = int64_t(tn) * C::BN;
 
   typename F::Src src;
   F::make_src(src, wave, lane, g.lda, g.ldb);
+  const typename F::Lane ln(wm, wn, lane);
+  const uint16_t* a_tile = g.A + m0 * g.lda;
+  const uint16_t* b_tile = g.B + n0;
+  const uint16_t* b2_tile = NB > 1 ? g.B2 + n0 : nullptr;
+
+  f32x16 acc[NB][F::FM][F::FN];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int i = 0; i < F::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < F::FN; ++j) acc[t][i][j] = f32x16{};
+
+  // Pipeline over K blocks with STAGES LDS buffers.  Iteration kt: wait until
+  // this wave's loads of block kt have landed, barrier (then every wave's
+  // loads of block kt are visible and every wave has finished reading block
+  // kt-1), refill the buffer of block kt-1 with block kt+STAGES-1, compute kt.
+  const int nk = int(g.K / F::BK);
+#pragma unroll
+  for (int p = 0; p < F::STAGES - 1; ++p) {
+    if (p < nk) {
+      const int64_t k1 = int64_t(p) * F::BK;
+      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb, NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+    }
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    // loads issued after block kt: blocks kt+1 .. min(kt+STAGES-2, nk-1)
+    if (kt + F::STAGES - 2 <= nk - 1) {
+      wait_vmcnt<(F::STAGES - 2) * F::LOADS_PER_STAGE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    const int kn = kt + F::STAGES - 1;
+    if (kn < nk) {
+      const int64_t k1 = int64_t(kn) * F::BK;
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
+               NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+    }
+    F::compute(lds + (kt % F::STAGES) * F::STAGE, acc, ln);
+  }
+
+  block_barrier();                         // every wave is done with the stage buffers
+  epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
+}
+
+// Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each
+// group per SIMD).  Each K block is handled in two phases per group:
+//   M: read all fragments of the block from LDS into registers and issue this
+//      wave's share of the global->LDS loads of a later block;
+//   C: run the block's MFMAs back to back at raised wave priority.
+// Group 1 runs one phase behind group 0, so on every SIMD one wave feeds the
+// matrix core while the other moves data.  Every phase starts with a
+// workgroup barrier (s_barrier without a memory fence, so direct loads stay in
+// flight); group 1 adds one barrier at the start, group 0 one at the end.
+// Phase t = 2j is group 0's M(j): before its barrier every wave has waited
+// for its own loads of block j.  M(kt) refills the buffer of block kt-1, which
+// both groups finished reading before the barrier that opened it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class F>
+__device__ __forceinline__ void wait_block(int kt, int nk) {
+  // loads issued after block kt: blocks kt+1 .. min(kt+STAGES-2, nk-1)
+  if (kt + F::STAGES - 2 <= nk - 1) {
+    wait_vmcnt<(F::STAGES - 2) * F::LOADS_PER_STAGE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <class TI, class TO, class C>
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const TiledArgs g) {
+  using F = Fast<TI, C>;
+  constexpr int NB = C::NB;
+  static_assert(C::WM * C::WN == 8, "ping-pong needs two groups of four waves");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
+  LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  int tm, tn;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int64_t m0 = int64_t(tm) * C::BM, n0 = int64_t(tn) * C::BN;
+
+  typename F::Src src;
+  F::make_src(src, wave, lane, g.lda, g.ldb);
+  const typename F::Lane ln(wm, wn, lane);
   const uint16_t* a_tile = g.A + m0 * g.lda;
   const uint16_t* b_tile = g.B + n0;
   const uint16_t* b2_tile = NB > 1 ? g.B2 + n0 : nullptr;
@@ -161,47 +422,50 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_fast_kernel(const TiledArgs
       for (int j = 0; j < F::FN; ++j) acc[t][i][j] = f32x16{};
 
   const int nk = int(g.K / F::BK);
-  F::issue(src, lds, a_tile, b_tile, b2_tile, wave);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < F::STAGES - 1; ++p) {
+    if (p < nk) {
+      const int64_t k1 = int64_t(p) * F::BK;
+      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb, NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+    }
+  }
+  if (group == 1) {
+    wait_block<F>(0, nk);
+    phase_barrier();                       // t = 0: group 1 idles while group 0 reads block 0
+  }
+  typename F::Frags f[F::SUB];
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      const int64_t k1 = int64_t(kt + 1) * F::BK;
-      F::issue(src, lds + ((kt + 1) & 1) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
+    if (group == 0) wait_block<F>(kt, nk);
+    phase_barrier();                       // M(kt)
+#pragma unroll
+    for (int s = 0; s < F::SUB; ++s) F::read_frags(lds + (kt % F::STAGES) * F::STAGE, s, ln, f[s]);
+    const int kn = kt + F::STAGES - 1;
+    if (kn < nk) {
+      const int64_t k1 = int64_t(kn) * F::BK;
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
                NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
     }
-    F::compute(lds + (kt & 1) * F::STAGE, acc, wm, wn, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next stage has landed
-    __syncthreads();
-  }
-
-  typedef typename TO::storage St;
-  const int lc = lane & 31, lr4 = (lane >> 5) * 4;
-#pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    St* C = static_cast<St*>(t == 0 ? g.C : g.C2);
-#pragma unroll
-    for (int i = 0; i < F::FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < F::FN; ++j) {
-        const int64_t col = n0 + wn * F::TN + j * 32 + lc;
-        const int64_t rbase = m0 + wm * F::TM + i * 32 + lr4;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t idx = (rbase + 8 * (e >> 2) + (e & 3)) * g.ldc + col;
-          float v = g.alpha * acc[t][i][j][e];
-          if (NB == 1 && g.beta != 0.0f) v += g.beta * from_out<TO>(C[idx]);
-          C[idx] = to_out<TO>(v);
-        }
-      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): fragments in registers
+    if (group == 1) {
+      if (kt + 1 < nk) wait_block<F>(kt + 1, nk);
     }
+    phase_barrier();                       // C(kt)
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < F::SUB; ++s) F::mma(f[s], acc);
+    __builtin_amdgcn_s_setprio(0);
   }
+  if (group == 0) phase_barrier();         // t = 2 nk: group 0 idles while group 1 finishes
+
+  // After the last phase barrier every M phase (all LDS reads) is complete,
+  // so the waves may reuse the stage buffers as epilogue windows.
+  epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 
 // Debug: K block 0 of tile (dbg_tm, dbg_tn) staged by the kernel's own code, then copied out.
-template <class TI, class TO, int BM, int BN, int NB, int WM, int WN, int AB, int AM, int AS, int BB, int BMb, int BS>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_fast_lds_image(const TiledArgs g) {
-  using F = Fast<TI, TO, BM, BN, NB, WM, WN, AB, AM, AS, BB, BMb, BS>;
+template <class TI, class TO, class C>
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_lds_image(const TiledArgs g) {
+  using F = Fast<TI, C>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGE];
   LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
   const int tid = threadIdx.x;
@@ -209,10 +473,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_fast_lds_image(const TiledA
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   typename F::Src src;
   F::make_src(src, wave, lane, g.lda, g.ldb);
-  const int64_t m0 = int64_t(g.dbg_tm) * BM, n0 = int64_t(g.dbg_tn) * BN;
-  F::issue(src, lds, g.A + m0 * g.lda, g.B + n0, NB > 1 ? g.B2 + n0 : nullptr, wave);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  const int64_t m0 = int64_t(g.dbg_tm) * C::BM, n0 = int64_t(g.dbg_tn) * C::BN;
+  F::issue(src, lds, g.A + m0 * g.lda, g.B + n0, C::NB > 1 ? g.B2 + n0 : nullptr, wave);
+  wait_vmcnt<0>();
+  block_barrier();
   for (int i = tid; i < F::STAGE; i += F::NT) g.dbg_out[i] = lds[i];
 }
 

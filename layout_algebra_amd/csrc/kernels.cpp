@@ -5,8 +5,8 @@ namespace lak {
 
 template <class C>
 static KernelShape fast_shape() {
-  return KernelShape{C::BM, C::BN, 64, C::NB, C::WM, C::WN, C::WM * C::WN * 64, 32, 32, 16,
-                     {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS}, 0, 1, 1, 2};
+  return KernelShape{C::BM, C::BN, C::BK, C::NB, C::WM, C::WN, C::WM * C::WN * 64, 32, 32, 16,
+                     {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS}, 0, 1, 1, C::STAGES};
 }
 
 KernelShape kernel_shape(int kid) {

@@ -227,12 +227,15 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     const int fk = p.gate_up ? lak::KID_FAST_GU : lak::KID_FAST_256;
     const lak::KernelShape fs = lak::kernel_shape(fk);
     const bool whole = d.m > 0 && d.n > 0 && d.k > 0 && d.m % fs.bm == 0 && d.n % fs.bn == 0 && d.k % fs.bk == 0;
-    const bool rows16 = d.lda % 8 == 0 && d.ldb % 8 == 0;
-    const bool off32 = int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && int64_t(fs.bk) * d.ldb < (int64_t{1} << 32);
+    const bool rows16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && d.ldc % 8 == 0;
+    // per-lane source offsets of the direct loads are 32-bit byte offsets
+    const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * int64_t(fs.bk) * d.ldb < (int64_t{1} << 32);
     if (whole && rows16 && off32) p.kid = fk;
   }
   p.shape = lak::kernel_shape(p.kid);
   const auto& s = p.shape;
+  // The fast kernels write C with 16-byte vectors, so C rows start on 16 bytes.
+  p.out_align_bytes = p.kid == lak::KID_TILED_128 ? p.out_bytes : 16;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
   if (int64_t(p.tiles_m) * p.tiles_n > (int64_t{1} << 31) - 1) { fail(err, "too many tiles"); return GEMM_ERR_UNSUPPORTED; }
@@ -285,7 +288,8 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
      << ",\"swizzle_b\":[" << s.sw_b[0] << "," << s.sw_b[1] << "," << s.sw_b[2] << "]"
      << ",\"direct_loads\":" << (s.direct ? "true" : "false")
      << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
-     << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes << "}";
+     << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes
+     << ",\"out_align_bytes\":" << p.out_align_bytes << "}";
   p.json = js.str();
   return GEMM_OK;
 }

@@ -14,6 +14,7 @@ struct gemm_plan_s {
   int vec = 1;               // elements per global vector load of A and B
   int align_bytes = 2;       // required alignment of the A / B / W pointers
   int out_bytes = 4;         // bytes per C element
+  int out_align_bytes = 4;   // required alignment of the C / G / U pointers
   bool gate_up = false;
   int tiles_m = 0, tiles_n = 0, grid = 0, group_m = 8;
   int64_t stage_elems = 0, lds_bytes = 0;
