@@ -289,6 +289,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], vo
 template <class TO, class F, int NB>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[NB][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
                                          int wm, int wn, int wave, int lane, LAK_LDS uint16_t* lds) {
+  static_assert(F::NW * 32 * (F::TN + 8) * 4 <= F::STAGES * F::STAGE * 2, "epilogue windows must fit in the stage buffers");
   LAK_LDS float* win = reinterpret_cast<LAK_LDS float*>(lds) + wave * 32 * (F::TN + 8);
   const int64_t row0 = m0 + wm * F::TM, col0 = n0 + wn * F::TN;
 #pragma unroll

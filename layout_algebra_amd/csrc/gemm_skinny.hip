@@ -1,0 +1,203 @@
+// Skinny GEMM for gfx950: M <= 16 rows, the whole problem streams B once.
+//
+// With M = 16 every byte of B is used by 16 rows only (about 16 FLOP per byte
+// of B), so the kernel is bound by HBM bandwidth, not by the matrix cores.
+// Structure:
+//  * one workgroup per 128-column strip of C and of B; the strip's B panel
+//    (K x 128) streams through a ring of STAGES LDS buffers by direct
+//    global -> LDS loads (1 KB per wave instruction, source-side swizzle as
+//    in the fast kernel), keeping STAGES-1 K blocks (over 100 KB per CU) in
+//    flight so HBM latency is covered;
+//  * the 16 x BK slice of A rides along in the same stage (A is 256 KB in
+//    total and stays in L2); rows >= M are fetched from row M-1 and their
+//    results discarded;
+//  * each of the 4 waves owns 32 columns: two v_mfma_f32_16x16x32 blocks per
+//    32-wide K step, A fragments as 16-byte LDS reads, B fragments through
+//    the transposing ds_read_b64_tr_b16 (B is N-contiguous);
+//  * FP32 accumulators stay in registers; the epilogue applies alpha/beta
+//    and writes only rows < M.
+#include "kernel_common.hpp"
+#include "launch.hpp"
+
+namespace lak {
+namespace {
+
+typedef short i16x4_s __attribute__((ext_vector_type(4)));
+#define SK_LDS __attribute__((address_space(3)))
+
+template <int N>
+__device__ __forceinline__ void sk_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void sk_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void sk_dma16(const uint16_t* base, uint32_t voff, const SK_LDS uint16_t* dst) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+
+template <class TI, class TO, class C>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g) {
+  constexpr int BM = 16, BN = C::BN, BK = C::BK, S = C::STAGES;
+  constexpr int NW = 4;
+  constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
+  constexpr int A_LOADS = A_ELEMS / 512 / NW, B_LOADS = B_ELEMS / 512 / NW;
+  constexpr int LPS = A_LOADS + B_LOADS;
+  constexpr int TN = BN / NW, FN = TN / 16;
+  static_assert(A_LOADS * 512 * NW == A_ELEMS && B_LOADS * 512 * NW == B_ELEMS, "whole KB per wave");
+  static_assert((S - 2) * LPS < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[S * STAGE];
+  SK_LDS uint16_t* lds = (SK_LDS uint16_t*)lds_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), 1, g.tiles_n, 1, tm, tn);
+  const int64_t n0 = int64_t(tn) * BN;
+
+  // per-lane source offsets (bytes, 32-bit) of the direct loads
+  uint32_t sa[A_LOADS], sb[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int L = swz<C::AB, C::AM, C::AS>((wave * A_LOADS + i) * 512 + lane * 8);
+    const int r = min(L / BK, int(g.M) - 1);
+    sa[i] = uint32_t((r * g.lda + L % BK) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int L = swz<C::BB, C::BMb, C::BS>((wave * B_LOADS + i) * 512 + lane * 8);
+    sb[i] = uint32_t(((L / BN) * g.ldb + L % BN) * 2);
+  }
+  auto issue = [&](int kb, int buf) {
+    const int64_t k1 = int64_t(kb) * BK;
+    const uint16_t* a_blk = g.A + k1;
+    const uint16_t* b_blk = g.B + k1 * g.ldb + n0;
+    SK_LDS uint16_t* st = lds + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) sk_dma16(a_blk, sa[i], st + (wave * A_LOADS + i) * 512);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) sk_dma16(b_blk, sb[i], st + A_ELEMS + (wave * B_LOADS + i) * 512);
+  };
+
+  f32x4 acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) acc[j] = f32x4{};
+  const int ar = lane & 15, ak = (lane >> 4) * 8;          // A: row l % 16, 8 K values from 8 (l / 16)
+  const int g4 = lane >> 4;
+  const int bk = 8 * g4 + ((lane >> 2) & 3);              // B: K row this lane addresses
+  const int bn = wave * TN + 4 * (lane & 3);               // B: first of its 4 N values
+
+  const int nk = int(g.K / BK);
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < nk) issue(p, p);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + S - 2 <= nk - 1) {
+      sk_wait_vmcnt<(S - 2) * LPS>();
+    } else {
+      sk_wait_vmcnt<0>();
+    }
+    sk_barrier();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    const SK_LDS uint16_t* st = lds + (kt % S) * STAGE;
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+      const u32x4 a = *reinterpret_cast<const SK_LDS u32x4*>(st + swz<C::AB, C::AM, C::AS>(ar * BK + s * 32 + ak));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const SK_LDS uint16_t* bs = st + A_ELEMS;
+        const i16x4_s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SK_LDS i16x4_s*)(bs + swz<C::BB, C::BMb, C::BS>((s * 32 + bk) * BN + bn + j * 16)));
+        const i16x4_s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SK_LDS i16x4_s*)(bs + swz<C::BB, C::BMb, C::BS>((s * 32 + bk + 4) * BN + bn + j * 16)));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        acc[j] = mfma_16x16x32<TI>(a, u32x4{l2.x, l2.y, h2.x, h2.y}, acc[j]);
+      }
+    }
+  }
+
+  // 16x16 result lane map: register r of lane l is row 4 (l / 16) + r, column l % 16.
+  typedef typename TO::storage St;
+  St* Cp = static_cast<St*>(g.C);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = n0 + wave * TN + j * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = 4 * (lane >> 4) + r;
+      if (row < g.M) {
+        const int64_t idx = row * g.ldc + col;
+        float v = g.alpha * acc[j][r];
+        if (g.beta != 0.0f) v += g.beta * from_out<TO>(Cp[idx]);
+        Cp[idx] = to_out<TO>(v);
+      }
+    }
+  }
+}
+
+// Debug: K block 0 of column strip dbg_tn, staged by the kernel's own code.
+template <class TI, class TO, class C>
+__global__ void __launch_bounds__(256) gemm_skinny_lds_image(const TiledArgs g) {
+  constexpr int BM = 16, BN = C::BN, BK = C::BK, NW = 4;
+  constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
+  constexpr int A_LOADS = A_ELEMS / 512 / NW, B_LOADS = B_ELEMS / 512 / NW;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[STAGE];
+  SK_LDS uint16_t* lds = (SK_LDS uint16_t*)lds_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = int64_t(g.dbg_tn) * BN;
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int L = swz<C::AB, C::AM, C::AS>((wave * A_LOADS + i) * 512 + lane * 8);
+    const int r = min(L / BK, int(g.M) - 1);
+    sk_dma16(g.A, uint32_t((r * g.lda + L % BK) * 2), lds + (wave * A_LOADS + i) * 512);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int L = swz<C::BB, C::BMb, C::BS>((wave * B_LOADS + i) * 512 + lane * 8);
+    sk_dma16(g.B + n0, uint32_t(((L / BN) * g.ldb + L % BN) * 2), lds + A_ELEMS + (wave * B_LOADS + i) * 512);
+  }
+  sk_wait_vmcnt<0>();
+  sk_barrier();
+  for (int i = tid; i < STAGE; i += 256) g.dbg_out[i] = lds[i];
+}
+
+template <class TI, class TO>
+hipError_t go_skinny(const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (img) {
+    hipLaunchKernelGGL((gemm_skinny_lds_image<TI, TO, CfgSkinny16>), dim3(1), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<TI, TO, CfgSkinny16>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (in_kind == IN_BF16) {
+    if (out_kind == OUT_F32) return go_skinny<InBF16, OutF32>(a, grid, s, img);
+    if (out_kind == OUT_BF16) return go_skinny<InBF16, OutBF16>(a, grid, s, img);
+    if (out_kind == OUT_F16) return go_skinny<InBF16, OutF16>(a, grid, s, img);
+  } else if (in_kind == IN_F16) {
+    if (out_kind == OUT_F32) return go_skinny<InF16, OutF32>(a, grid, s, img);
+    if (out_kind == OUT_BF16) return go_skinny<InF16, OutBF16>(a, grid, s, img);
+    if (out_kind == OUT_F16) return go_skinny<InF16, OutF16>(a, grid, s, img);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lak

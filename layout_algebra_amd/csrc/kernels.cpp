@@ -15,6 +15,11 @@ KernelShape kernel_shape(int kid) {
       return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 3}, {3, 3, 3}, 1, 0, 0, 2};
     case KID_FAST_256: return fast_shape<CfgFast256>();
     case KID_FAST_GU: return fast_shape<CfgFastGU>();
+    case KID_SKINNY_16: {
+      using C = CfgSkinny16;
+      return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
+                         0, 1, 1, C::STAGES};
+    }
     default:
       return KernelShape{};
   }
@@ -30,6 +35,7 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_TILED_128: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, args, grid, stream, lds_image);
     case KID_FAST_256:
     case KID_FAST_GU: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_SKINNY_16: return launch_skinny(in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,7 +23,8 @@ struct TiledArgs {
 enum KernelId : int {
   KID_TILED_128 = 0,     // any shape: 128x128x64, 4 waves of 64x64, register-staged, B transposed while staging
   KID_FAST_256 = 1,      // full tiles: 256x256x64, 8 waves of 128x64, direct-to-LDS, transposing B reads
-  KID_FAST_GU = 2,       // full tiles, gate/up: 256 x (128 + 128) x 64, 8 waves of 128 x (32 + 32)
+  KID_FAST_GU = 2,       // full tiles, gate/up: 256 x (128 + 128) x 32, 8 waves of 128 x (32 + 32)
+  KID_SKINNY_16 = 3,     // M <= 16: 16 x 128 column strips over all of K, 4 waves of 16 x 32, HBM-bound
   KID_COUNT
 };
 
@@ -45,6 +46,12 @@ struct CfgFastGU {
   static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4, BK = 32, STAGES = 4, SCHED = 2;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 2;  // B: Swizzle{2,5,2} over 256-byte rows
+};
+
+struct CfgSkinny16 {
+  static constexpr int BN = 128, BK = 128, STAGES = 4;
+  static constexpr int AB = 4, AM = 3, AS = 4;   // A: Swizzle{4,3,4} over 256-byte rows (16 rows -> 16 slots)
+  static constexpr int BB = 3, BMb = 4, BS = 3;  // B: Swizzle{3,4,3} over 256-byte rows
 };
 
 struct KernelShape {
@@ -76,5 +83,7 @@ hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_u
                         const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
 hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, int grid,
                        hipStream_t stream, bool lds_image);
+hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, int grid, hipStream_t stream,
+                         bool lds_image);
 
 }  // namespace lak

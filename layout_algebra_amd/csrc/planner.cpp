@@ -146,22 +146,26 @@ bool check_fragment_reads(const gemm_plan_s& p, std::string* err) {
   return true;
 }
 
-// MFMA 32x32 result ownership: register r of lane l of fragment (i, j) of wave
-// (wm, wn) holds tile element (wm*TM + 32 i + 8 (r/4) + 4 (l/32) + r%4,
-//                              wn*TN + 32 j + l%32).
+// MFMA result ownership.  32x32 blocks: register r of lane l of fragment
+// (i, j) of wave (wm, wn) holds tile element
+//   (wm*TM + 32 i + 8 (r/4) + 4 (l/32) + r%4,  wn*TN + 32 j + l%32);
+// 16x16 blocks: (wm*TM + 16 i + 4 (l/16) + r,  wn*TN + 16 j + l%16).
 bool check_ownership(const gemm_plan_s& p, std::string* err) {
   const auto& s = p.shape;
+  const int mm = s.mfma_m;
   const int tm = s.bm / s.waves_m, tn = s.bn / s.waves_n;
-  if (tm % 32 || tn % 32) return fail(err, "wave tile is not a multiple of the 32x32 MFMA block");
+  if (tm % mm || tn % mm) return fail(err, "wave tile is not a multiple of the MFMA block");
+  const int regs = mm == 32 ? 16 : 4;
   std::vector<int> hits(static_cast<size_t>(s.bm) * s.bn, 0);
   for (int w = 0; w < s.waves_m * s.waves_n; ++w) {
     const int wm = w % s.waves_m, wn = w / s.waves_m;
-    for (int i = 0; i < tm / 32; ++i)
-      for (int j = 0; j < tn / 32; ++j)
+    for (int i = 0; i < tm / mm; ++i)
+      for (int j = 0; j < tn / mm; ++j)
         for (int l = 0; l < 64; ++l)
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * tm + 32 * i + 8 * (r / 4) + 4 * (l / 32) + r % 4;
-            const int col = wn * tn + 32 * j + l % 32;
+          for (int r = 0; r < regs; ++r) {
+            const int row = mm == 32 ? wm * tm + 32 * i + 8 * (r / 4) + 4 * (l / 32) + r % 4
+                                     : wm * tm + 16 * i + 4 * (l / 16) + r;
+            const int col = mm == 32 ? wn * tn + 32 * j + l % 32 : wn * tn + 16 * j + l % 16;
             ++hits[static_cast<size_t>(row) * s.bn + col];
           }
   }
@@ -231,11 +235,18 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // per-lane source offsets of the direct loads are 32-bit byte offsets
     const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * int64_t(fs.bk) * d.ldb < (int64_t{1} << 32);
     if (whole && rows16 && off32) p.kid = fk;
+    // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
+    const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
+    const bool skinny_fit = !p.gate_up && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
+                            d.k % ks.bk == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0 &&
+                            2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
+                            2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
+    if (skinny_fit) p.kid = lak::KID_SKINNY_16;
   }
   p.shape = lak::kernel_shape(p.kid);
   const auto& s = p.shape;
   // The fast kernels write C with 16-byte vectors, so C rows start on 16 bytes.
-  p.out_align_bytes = p.kid == lak::KID_TILED_128 ? p.out_bytes : 16;
+  p.out_align_bytes = (p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU) ? 16 : p.out_bytes;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
   if (int64_t(p.tiles_m) * p.tiles_n > (int64_t{1} << 31) - 1) { fail(err, "too many tiles"); return GEMM_ERR_UNSUPPORTED; }
@@ -273,7 +284,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   }
 
   std::ostringstream js;
-  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up"};
+  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny"};
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
      << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc

@@ -251,6 +251,7 @@ LDS_CASES = {
     "tiled_f16_ragged_edge": (1000, 1537, 999, "f16", False, 7, 12, "tiled_"),
     "fast_gate_up": (512, 256, 128, "bf16", True, 1, 1, "fast_gate_up_"),
     "tiled_gate_up_edge": (300, 200, 100, "bf16", True, 2, 1, "tiled_"),
+    "skinny_bf16": (16, 512, 256, "bf16", False, 0, 2, "skinny_"),
 }
 
 
@@ -320,3 +321,31 @@ def test_fast_kernel_identity_is_exact():
     P = torch.zeros((K, K), dtype=torch.bfloat16)
     P[perm, torch.arange(K)] = 1
     assert torch.equal(run_gemm(a, P, "bf16"), a[:, perm])
+
+
+SKINNY_SHAPES = [(16, 128, 128), (1, 256, 256), (7, 384, 1024), (16, 1024, 2048), (13, 128, 8192)]
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SKINNY_SHAPES, ids=[str(s) for s in SKINNY_SHAPES])
+def test_skinny_kernel_shapes(shape, in_kind, out_kind):
+    M, N, K = shape
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind])
+    assert plan.describe()["kernel"].startswith("skinny_")
+    seed = 11 * M + N + K
+    a = synth.normal((M, K), seed, in_kind)
+    b = synth.normal((K, N), seed + 1, in_kind, 0.05)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got = run_gemm(a, b, out_kind, 0.5, -2.0, c)
+    ref = oracle_gemm(a, b, in_kind, 0.5, -2.0, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "skinny %s" % (shape,))
+
+
+def test_skinny_identity_is_exact():
+    K = 256
+    a = synth.uniform((16, K), 51, "bf16")
+    eye = torch.eye(K, dtype=torch.bfloat16)
+    plan = la.gemm_plan(16, K, K, la.BF16, la.F32)
+    assert plan.describe()["kernel"].startswith("skinny_")
+    assert torch.equal(run_gemm(a, eye, "f32"), a.to(torch.float32))
