@@ -38,15 +38,29 @@ __device__ __forceinline__ void sk_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Direct load of 64 x 16 bytes into one LDS kilobyte.  NT marks the access
+// non-temporal: B is read exactly once, so it should not displace A (and
+// whatever else is resident) from the caches.
+template <bool NT>
 __device__ __forceinline__ void sk_dma16(const uint16_t* base, uint32_t voff, const SK_LDS uint16_t* dst) {
   const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(base)
-      : "memory", "m0");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(lds_addr), "v"(voff), "s"(base)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_addr), "v"(voff), "s"(base)
+        : "memory", "m0");
+  }
 }
 
 template <class TI, class TO, class C>
@@ -87,9 +101,9 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g) {
     const uint16_t* b_blk = g.B + k1 * g.ldb + n0;
     SK_LDS uint16_t* st = lds + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) sk_dma16(a_blk, sa[i], st + (wave * A_LOADS + i) * 512);
+    for (int i = 0; i < A_LOADS; ++i) sk_dma16<false>(a_blk, sa[i], st + (wave * A_LOADS + i) * 512);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) sk_dma16(b_blk, sb[i], st + A_ELEMS + (wave * B_LOADS + i) * 512);
+    for (int i = 0; i < B_LOADS; ++i) sk_dma16<C::B_NT>(b_blk, sb[i], st + A_ELEMS + (wave * B_LOADS + i) * 512);
   };
 
   f32x4 acc[FN];
@@ -163,12 +177,12 @@ __global__ void __launch_bounds__(256) gemm_skinny_lds_image(const TiledArgs g) 
   for (int i = 0; i < A_LOADS; ++i) {
     const int L = swz<C::AB, C::AM, C::AS>((wave * A_LOADS + i) * 512 + lane * 8);
     const int r = min(L / BK, int(g.M) - 1);
-    sk_dma16(g.A, uint32_t((r * g.lda + L % BK) * 2), lds + (wave * A_LOADS + i) * 512);
+    sk_dma16<false>(g.A, uint32_t((r * g.lda + L % BK) * 2), lds + (wave * A_LOADS + i) * 512);
   }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int L = swz<C::BB, C::BMb, C::BS>((wave * B_LOADS + i) * 512 + lane * 8);
-    sk_dma16(g.B + n0, uint32_t(((L / BN) * g.ldb + L % BN) * 2), lds + A_ELEMS + (wave * B_LOADS + i) * 512);
+    sk_dma16<false>(g.B + n0, uint32_t(((L / BN) * g.ldb + L % BN) * 2), lds + A_ELEMS + (wave * B_LOADS + i) * 512);
   }
   sk_wait_vmcnt<0>();
   sk_barrier();
