@@ -33,6 +33,39 @@ PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
 
+def kernel_source_hash():
+    """sha1 (first 16 hex) over the HIP sources; identifies the kernels the traffic figures belong to."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "layout_algebra_amd", "csrc")
+    h = hashlib.sha1()
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from profiles/traffic.md, or None when the
+    kernels changed since the counters were taken (or none were taken for this workload)."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    recorded, table = None, {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("source_hash:"):
+                recorded = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic "):
+                name, val = line[len("traffic "):].split(":")
+                table[name.strip()] = int(val)
+    if recorded != kernel_source_hash():
+        return None
+    return table.get(workload)
+
+
 def algorithmic_bytes(w):
     """Compulsory HBM bytes of one step: every operand read once, C written (and read if beta != 0)."""
     eb = 2
@@ -52,6 +85,9 @@ def main():
     ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed region, run a plain elementwise copy of 256 MiB (reads 256 MiB, writes "
+                         "256 MiB) three times: the reference dispatch for scaling HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -130,6 +166,14 @@ def main():
     torch.cuda.synchronize()
     per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
+    if args.copy_probe:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     flops = w.flops()
     value_tflops = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = ms_per_step
@@ -144,7 +188,7 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[w.in_kind],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
     roof["kernel_avg_ms"] = kern_ms
     roof["single_launch_ms"] = {"min": float(per_launch.min()), "median": float(np.median(per_launch))}
 
@@ -167,20 +211,24 @@ def main():
 
 
 def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):
-    """Time the oracle (as it is) on the first R output rows; R sized to ~budget_s."""
+    """Time the oracle (as it is) on the first R output rows, R sized to about budget_s seconds;
+    when the whole workload takes less than that, repeat it."""
     import oracle
     threads = oracle.max_threads()
     a = x["A"]
+    probe_rows = list(range(min(w.M, 2 * threads)))
     t0 = time.perf_counter()
-    probe_rows = list(range(min(4, w.M)))
     oracle.gemm_f64(synth.bits(a[probe_rows]), w.in_kind, synth.bits(b_cpu), w.in_kind)
     per_row = (time.perf_counter() - t0) / len(probe_rows)
     R = int(max(len(probe_rows), min(w.M, budget_s / max(per_row, 1e-9))))
+    reps = max(1, int(budget_s / max(per_row * R, 1e-9))) if R == w.M else 1
     rows = list(range(R))
     c_in = x["C"][rows].numpy() if "C" in x else None
+    a_bits, b_bits = synth.bits(a[rows]), synth.bits(b_cpu)
     t0 = time.perf_counter()
-    ref = oracle.gemm_f64(synth.bits(a[rows]), w.in_kind, synth.bits(b_cpu), w.in_kind, w.alpha, w.beta, c_in)
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        ref = oracle.gemm_f64(a_bits, w.in_kind, b_bits, w.in_kind, w.alpha, w.beta, c_in)
+    dt = (time.perf_counter() - t0) / reps
     flops = 2.0 * R * w.N * w.K
     if unit == "GB/s":
         bytes_ = (R * w.K + w.K * w.N) * 2 + R * w.N * 4
@@ -188,8 +236,8 @@ def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):
     else:
         value = flops / dt / 1e12
     base = {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": "output rows 0..%d of %d (%d x %d outputs, K=%d%s), FP64 triple loop, %.1f s"
-                      % (R - 1, w.M, R, w.N, w.K, ", W_gate product only" if w.gate_up else "", dt),
+            "sample": "output rows 0..%d of %d (%d x %d outputs, K=%d%s), FP64 triple loop, %.2f s per run, %d run(s)"
+                      % (R - 1, w.M, R, w.N, w.K, ", W_gate product only" if w.gate_up else "", dt, reps),
             "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
     parity = None
     if check is not None:
