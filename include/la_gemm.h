@@ -63,7 +63,7 @@ typedef enum {
 typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
 
 /* Flags for gemm_desc.flags. */
-#define GEMM_FLAG_GATE_UP 0x1u   /* plan is for gemm_gate_up_run */
+#define GEMM_FLAG_GATE_UP 0x1u   /* plan is for gemm_gate_up_run / gemm_gate_up_swiglu_run */
 
 typedef struct {
   int64_t m, n, k;             /* problem sizes, each >= 0 */
@@ -97,6 +97,15 @@ gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
  * G and U are [m, n] (ldc). */
 gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate,
                              const void* W_up, void* G, void* U, void* stream);
+
+/* H = silu(X * W_gate) (.) (X * W_up), silu(g) = g / (1 + e^-g), evaluated
+ * in FP32 on the two accumulators of each element and rounded once to H's
+ * type: the activation composed into the gate/up epilogue (Tylo.jl "Layouts,
+ * storage and ownership", section "Plans describe work, callers establish
+ * readiness": scaling and activation fuse into the epilogue).  Same plan and
+ * operands as gemm_gate_up_run; H is [m, n] (ldc). */
+gemm_status gemm_gate_up_swiglu_run(gemm_plan_t plan, const void* X, const void* W_gate,
+                                    const void* W_up, void* H, void* stream);
 
 /* JSON description of the plan (kernel, tile sizes, grid, LDS layouts and
  * swizzle, alignment class).  Writes at most len bytes including the NUL;

@@ -10,7 +10,7 @@ BF16, F16, F32 = 0, 1, 2
 FLAG_GATE_UP = 0x1
 
 EXPORTED_SYMBOLS = (
-    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_gate_up_run", "gemm_plan_describe",
+    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
     "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "gemm_status_string", "gemm_last_error",
@@ -57,6 +57,7 @@ def load():
         "gemm_plan_destroy": ([vp], None),
         "gemm_run": ([vp, vp, vp, vp, f32, f32, vp], i32),
         "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
+        "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
         "gemm_plan_describe": ([vp, ctypes.c_char_p, ctypes.c_size_t], i32),
         "gemm_plan_lds_offset": ([vp, i32, i64, i64, p64], i32),
         "gemm_plan_lds_stage_bytes": ([vp, p64], i32),
@@ -187,6 +188,17 @@ def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
     _check_matrix(U, "U", d.m, d.n, d.ldc, d.c_type)
     _check(load().gemm_gate_up_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, G, U)],
                                    _stream_ptr(stream)))
+
+
+def gemm_gate_up_swiglu_run(plan, X, W_gate, W_up, H, stream=None):
+    """H = silu(X @ W_gate) * (X @ W_up) in one launch (activation fused into the epilogue)."""
+    d = plan.desc
+    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type)
+    _check_matrix(W_gate, "W_gate", d.k, d.n, d.ldb, d.b_type)
+    _check_matrix(W_up, "W_up", d.k, d.n, d.ldb, d.b_type)
+    _check_matrix(H, "H", d.m, d.n, d.ldc, d.c_type)
+    _check(load().gemm_gate_up_swiglu_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, H)],
+                                          _stream_ptr(stream)))
 
 
 def gemm_debug_lds_image(plan, A, B, B2, tile_m, tile_n, out, stream=None):

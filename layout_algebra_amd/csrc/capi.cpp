@@ -124,6 +124,30 @@ gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate
   return launch(p, a, stream, false);
 }
 
+gemm_status gemm_gate_up_swiglu_run(gemm_plan_t plan, const void* X, const void* W_gate, const void* W_up, void* H,
+                                    void* stream) {
+  if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");
+  const gemm_plan_s& p = *plan;
+  if (!p.gate_up) return set_err(GEMM_ERR_INVALID_ARG, "plan was not made with GEMM_FLAG_GATE_UP");
+  if (p.d.m == 0 || p.d.n == 0) return GEMM_OK;
+  if (!H) return set_err(GEMM_ERR_NULL, "H is NULL");
+  if (p.d.k > 0 && (!X || !W_gate || !W_up)) return set_err(GEMM_ERR_NULL, "X, W_gate or W_up is NULL");
+  if (!aligned(X, p.align_bytes) || !aligned(W_gate, p.align_bytes) || !aligned(W_up, p.align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "X, W_gate and W_up must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
+  if (!aligned(H, p.out_align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "H must be " + std::to_string(p.out_align_bytes) + "-byte aligned for this plan");
+  lak::TiledArgs a = base_args(p);
+  a.A = static_cast<const uint16_t*>(X);
+  a.B = static_cast<const uint16_t*>(W_gate);
+  a.B2 = static_cast<const uint16_t*>(W_up);
+  a.C = H;
+  a.C2 = nullptr;
+  a.alpha = 1.0f;
+  a.beta = 0.0f;
+  a.act = 1;
+  return launch(p, a, stream, false);
+}
+
 gemm_status gemm_plan_describe(gemm_plan_t plan, char* buf, size_t len) {
   if (!plan || !buf) return set_err(GEMM_ERR_NULL, "plan and buf must not be NULL");
   if (plan->json.size() + 1 > len) return set_err(GEMM_ERR_RESOURCE, "buffer too small for the plan description");

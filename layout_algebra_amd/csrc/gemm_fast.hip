@@ -13,6 +13,8 @@ hipError_t go_fast(const TiledArgs& a, int grid, hipStream_t s, bool img) {
   } else {
     if constexpr (C::SCHED == 2) {
       hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
+    } else if constexpr (C::SCHED == 3) {
+      hipLaunchKernelGGL((gemm_fast_sp_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
     } else {
       hipLaunchKernelGGL((gemm_fast_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
     }

@@ -42,6 +42,7 @@ template <class TI, class C>
 struct Fast {
   static constexpr int BM = C::BM, BN = C::BN, NB = C::NB, WM = C::WM, WN = C::WN, BK = C::BK;
   static constexpr int STAGES = C::STAGES;
+  static constexpr bool SCHED_HINTS = C::SCHED != 4;     // 4: software pipeline without scheduler groups
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -287,14 +288,35 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], vo
 }
 
 template <class TO, class F, int NB>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[NB][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[NB][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
                                          int wm, int wn, int wave, int lane, LAK_LDS uint16_t* lds) {
   static_assert(F::NW * 32 * (F::TN + 8) * 4 <= F::STAGES * F::STAGE * 2, "epilogue windows must fit in the stage buffers");
   LAK_LDS float* win = reinterpret_cast<LAK_LDS float*>(lds) + wave * 32 * (F::TN + 8);
   const int64_t row0 = m0 + wm * F::TM, col0 = n0 + wn * F::TN;
+  if constexpr (NB == 2) {
+    if (g.act == 1) {
+      // fused activation: the gate and up accumulators of one element sit in the same lane
+#pragma unroll
+      for (int i = 0; i < F::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < F::FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[0][i][j][e] = swiglu(acc[0][i][j][e], acc[1][i][j][e]);
+      store_tile<TO, F>(acc[0], g.C, g.ldc, 1.0f, 0.0f, false, row0, col0, win, lane);
+      return;
+    }
+  }
 #pragma unroll
   for (int t = 0; t < NB; ++t)
     store_tile<TO, F>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0, col0, win, lane);
+}
+
+// The same barrier without waiting for this wave's outstanding LDS reads, for
+// schedules whose in-flight reads only target buffers nobody refills next.
+__device__ __forceinline__ void block_barrier_nowait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <class TI, class TO, class C>
@@ -460,6 +482,115 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
 
   // After the last phase barrier every M phase (all LDS reads) is complete,
   // so the waves may reuse the stage buffers as epilogue windows.
+  epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
+}
+
+// Software-pipelined schedule.  Every wave keeps two fragment sets of one
+// 16-deep MFMA sub-step each: while the MFMAs of sub-step s run on one set,
+// the LDS reads of the next sub-step fill the other, alternating one MFMA and
+// one LDS read (scheduler groups), so LDS latency hides behind the wave's own
+// matrix work.  The next sub-step of the last one in block kt is sub-step 0
+// of block kt+1; one barrier per K block, placed before that last sub-step,
+// guarantees that block kt+1 has landed (each wave waited for its own loads
+// of it) and that every wave has finished reading block kt-1, whose buffer is
+// then refilled with block kt+STAGES-1.
+template <class F>
+__device__ __forceinline__ void wait_block_ahead(int kb, int nk) {
+  // loads issued so far: blocks .. min(kb+STAGES-3, nk-1); those newer than kb may stay in flight
+  if (kb + F::STAGES - 3 <= nk - 1) {
+    wait_vmcnt<(F::STAGES - 3) * F::LOADS_PER_STAGE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <class F, class TI>
+__device__ __forceinline__ void sp_substep(const LAK_LDS uint16_t* next_stage, int next_s, const typename F::Lane& ln,
+                                           const typename F::Frags& cur, typename F::Frags& nxt,
+                                           f32x16 (&acc)[F::NB][F::FM][F::FN]) {
+  F::read_frags(next_stage, next_s, ln, nxt);
+  F::mma(cur, acc);
+  if constexpr (F::SCHED_HINTS) F::interleave();
+}
+
+template <class TI, class TO, class C>
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const TiledArgs g) {
+  using F = Fast<TI, C>;
+  constexpr int NB = C::NB;
+  static_assert(C::STAGES >= 3, "the software pipeline reads one block ahead");
+  static_assert(F::SUB % 2 == 0, "sub-steps alternate between two fragment sets");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
+  LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  int tm, tn;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int64_t m0 = int64_t(tm) * C::BM, n0 = int64_t(tn) * C::BN;
+
+  typename F::Src src;
+  F::make_src(src, wave, lane, g.lda, g.ldb);
+  const typename F::Lane ln(wm, wn, lane);
+  const uint16_t* a_tile = g.A + m0 * g.lda;
+  const uint16_t* b_tile = g.B + n0;
+  const uint16_t* b2_tile = NB > 1 ? g.B2 + n0 : nullptr;
+
+  f32x16 acc[NB][F::FM][F::FN];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int i = 0; i < F::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < F::FN; ++j) acc[t][i][j] = f32x16{};
+
+  const int nk = int(g.K / F::BK);
+#pragma unroll
+  for (int p = 0; p < F::STAGES - 1; ++p) {
+    if (p < nk) {
+      const int64_t k1 = int64_t(p) * F::BK;
+      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb, NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+    }
+  }
+  if (F::STAGES - 2 <= nk - 1) {          // block 0 landed; blocks 1 .. STAGES-2 may still fly
+    wait_vmcnt<(F::STAGES - 2) * F::LOADS_PER_STAGE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  block_barrier();
+  typename F::Frags f0, f1;
+  F::read_frags(lds, 0, ln, f0);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    const LAK_LDS uint16_t* cur = lds + (kt % F::STAGES) * F::STAGE;
+    // after the last block the look-ahead reads re-read the current buffer (valid, unused)
+    const LAK_LDS uint16_t* nxt = more ? lds + ((kt + 1) % F::STAGES) * F::STAGE : cur;
+#pragma unroll
+    for (int s = 0; s < F::SUB; s += 2) {
+      // even sub-step s: compute from f0, read sub-step s+1 (same block) into f1
+      sp_substep<F, TI>(cur, s + 1, ln, f0, f1, acc);
+      if (s + 2 == F::SUB) {
+        // last sub-step of the block reads block kt+1: make it visible, recycle block kt-1's buffer
+        // (this wave's reads of block kt-1 were consumed by its MFMAs of block kt-1; the reads
+        // still in flight target block kt, which is not refilled here)
+        if (more) wait_block_ahead<F>(kt + 1, nk);
+        block_barrier_nowait();
+        const int kn = kt + F::STAGES - 1;
+        if (kn < nk) {
+          const int64_t k1 = int64_t(kn) * F::BK;
+          F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
+                   NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+        }
+        sp_substep<F, TI>(nxt, 0, ln, f1, f0, acc);
+      } else {
+        sp_substep<F, TI>(cur, s + 2, ln, f1, f0, acc);
+      }
+    }
+  }
+
+  block_barrier();                         // every wave is done with the stage buffers
   epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 

@@ -217,8 +217,12 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
         if (row >= g.M) continue;
         const int64_t idx = row * g.ldc + col;
         if constexpr (GU) {
-          static_cast<St*>(g.C)[idx] = to_out<TO>(acc[0][i][j][e]);
-          static_cast<St*>(g.C2)[idx] = to_out<TO>(acc[1][i][j][e]);
+          if (g.act == 1) {
+            static_cast<St*>(g.C)[idx] = to_out<TO>(swiglu(acc[0][i][j][e], acc[1][i][j][e]));
+          } else {
+            static_cast<St*>(g.C)[idx] = to_out<TO>(acc[0][i][j][e]);
+            static_cast<St*>(g.C2)[idx] = to_out<TO>(acc[1][i][j][e]);
+          }
         } else {
           St* C = static_cast<St*>(g.C);
           float v = g.alpha * acc[0][i][j][e];

@@ -71,6 +71,10 @@ __device__ __forceinline__ float from_out<OutBF16>(uint16_t v) { return static_c
 template <>
 __device__ __forceinline__ float from_out<OutF16>(uint16_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, v)); }
 
+// SwiGLU combination of one gate and one up accumulator, in FP32:
+// silu(g) * u with silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float swiglu(float gate, float up) { return gate / (1.0f + expf(-gate)) * up; }
+
 // Swizzle{B,M,S} on element offsets: XOR bits [M+S, M+S+B) into [M, M+B).
 template <int B, int M, int S>
 __device__ __forceinline__ constexpr int swz(int off) {

@@ -15,6 +15,7 @@ struct TiledArgs {
   void* C2;              // U for gate/up
   int64_t M, N, K, lda, ldb, ldc;
   float alpha, beta;
+  int act;               // gate/up only: 0 = write G and U, 1 = write silu(G) * U to C
   int tiles_m, tiles_n, group_m;
   int dbg_tm, dbg_tn;    // LDS-image debug launch: tile to stage
   uint16_t* dbg_out;     // LDS-image debug launch: destination of one stage

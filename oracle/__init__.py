@@ -99,3 +99,19 @@ def gemm_f64(a_bits, a_kind, b_bits, b_kind, alpha=1.0, beta=0.0, c=None, nthrea
 
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
+
+
+def gate_up_swiglu_f64(x_bits, w_gate_bits, w_up_bits, kind, nthreads=0):
+    """H = silu(X @ W_gate) * (X @ W_up) with silu(g) = g / (1 + exp(-g)), all in binary64.
+
+    The activation composed into the gate/up epilogue (Tylo.jl "Layouts, storage
+    and ownership", section "Plans describe work, callers establish readiness":
+    scaling and activation become part of the epilogue).  G and U are the
+    oracle's own FP64 products; the activation is applied elementwise.
+    Returns (H, G, U) as float64 arrays.
+    """
+    g = gemm_f64(x_bits, kind, w_gate_bits, kind, nthreads=nthreads)
+    u = gemm_f64(x_bits, kind, w_up_bits, kind, nthreads=nthreads)
+    with np.errstate(over="ignore"):
+        h = g / (1.0 + np.exp(-g)) * u
+    return h, g, u

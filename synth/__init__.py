@@ -54,6 +54,7 @@ class Workload:
     seeds: tuple
     dist_c: Dist = None          # existing C when beta != 0
     gate_up: bool = False
+    act: str = ""                # gate/up epilogue activation: "" (G and U) or "swiglu" (one output)
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -78,6 +79,10 @@ WORKLOADS = {
         "gate_up", 4096, 11008, 4096, "bf16", "bf16", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (4001, 4002, 4003),
         gate_up=True, notes="x[4096,4096] times W_gate and W_up [4096,11008]"),
+    "gate_up_swiglu": Workload(
+        "gate_up_swiglu", 4096, 11008, 4096, "bf16", "bf16", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (4001, 4002, 4003),
+        gate_up=True, act="swiglu", notes="silu(x W_gate) * (x W_up), one bf16 output"),
     "skinny": Workload(
         "skinny", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5001, 5002, 5003),

@@ -10,7 +10,8 @@ import torch
 
 import layout_algebra_amd as la
 import synth
-from parity import assert_close, oracle_gemm, sample_rows
+from parity import assert_close, oracle_gemm, sample_rows, swiglu_bound
+import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -349,3 +350,28 @@ def test_skinny_identity_is_exact():
     plan = la.gemm_plan(16, K, K, la.BF16, la.F32)
     assert plan.describe()["kernel"].startswith("skinny_")
     assert torch.equal(run_gemm(a, eye, "f32"), a.to(torch.float32))
+
+
+@pytest.mark.parametrize("shape", [(512, 256, 192), (300, 200, 100), (4096, 11008, 4096)],
+                         ids=["fast", "tiled_edges", "gate_up_workload"])
+def test_gate_up_swiglu(shape):
+    M, N, K = shape
+    if (M, N, K) == (4096, 11008, 4096):
+        w = synth.WORKLOADS["gate_up"]
+        inp = synth.make_inputs(w)
+        x, wg, wu = inp["A"], inp["Wg"], inp["Wu"]
+        rows = sample_rows(M, 16, 4005)
+    else:
+        x = synth.normal((M, K), 71, "bf16")
+        wg = synth.normal((K, N), 72, "bf16", 0.3)
+        wu = synth.normal((K, N), 73, "bf16", 0.3)
+        rows = list(range(M))
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True)
+    H = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    la.gemm_gate_up_swiglu_run(plan, x.to(DEV), wg.to(DEV), wu.to(DEV), H)
+    torch.cuda.synchronize()
+    h_ref, g_ref, u_ref = oracle.gate_up_swiglu_f64(synth.bits(x[rows]), synth.bits(wg), synth.bits(wu), "bf16")
+    got = H.cpu()[rows].to(torch.float64).numpy()
+    tol = swiglu_bound(K, x, wg, wu, g_ref, u_ref, h_ref, "bf16")
+    err = np.abs(got - h_ref)
+    assert np.all(err <= tol), "max err %g at %s" % (err.max(), np.unravel_index(np.argmax(err - tol), err.shape))

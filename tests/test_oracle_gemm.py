@@ -166,3 +166,23 @@ def test_thread_count_does_not_change_bits():
     r1 = oracle.gemm_f64(synth.bits(a), "bf16", synth.bits(b), "bf16", nthreads=1)
     r4 = oracle.gemm_f64(synth.bits(a), "bf16", synth.bits(b), "bf16", nthreads=4)
     assert np.array_equal(r1, r4)
+
+
+def test_swiglu_oracle_against_hand_values():
+    """X = identity picks rows of the weights, so G and U are the weight values
+    themselves and H = w_g / (1 + e^-w_g) * w_u can be written out by hand."""
+    import math
+    K = N = 8
+    x = torch.eye(K, dtype=torch.bfloat16)
+    wg_vals = [-20.0, -1.0, -0.5, 0.0, 0.5, 1.0, 2.0, 20.0]
+    wg = torch.tensor([wg_vals] * K, dtype=torch.bfloat16)
+    wu = synth.uniform((K, N), 61, "bf16", -3.0, 3.0)
+    h, g, u = oracle.gate_up_swiglu_f64(synth.bits(x), synth.bits(wg), synth.bits(wu), "bf16")
+    for i in range(K):
+        for j in range(N):
+            gv = float(wg[i, j]); uv = float(wu[i, j])
+            want = gv / (1.0 + math.exp(-gv)) * uv
+            assert abs(h[i, j] - want) <= 1e-15 * max(1.0, abs(want))
+    assert abs(h[0, 1] / float(wu[0, 1]) - (-0.2689414213699951)) < 1e-15     # silu(-1)
+    assert abs(h[0, 5] / float(wu[0, 5]) - 0.7310585786300049) < 1e-15       # silu(1)
+    assert h[0, 3] == 0.0                                                     # silu(0)
