@@ -43,6 +43,8 @@ struct Fast {
   static constexpr int BM = C::BM, BN = C::BN, NB = C::NB, WM = C::WM, WN = C::WN, BK = C::BK;
   static constexpr int STAGES = C::STAGES;
   static constexpr bool SCHED_HINTS = C::SCHED != 4;     // 4: software pipeline without scheduler groups
+  static constexpr bool DMA_IN_C = C::DMA_IN_C;           // ping-pong: issue direct loads in the C phase
+  static constexpr int PRIO = C::PRIO;                    // ping-pong: 0 none, 1 raise C phase, 2 raise M phase
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -460,23 +462,31 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   for (int kt = 0; kt < nk; ++kt) {
     if (group == 0) wait_block<F>(kt, nk);
     phase_barrier();                       // M(kt)
+    if (F::PRIO == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < F::SUB; ++s) F::read_frags(lds + (kt % F::STAGES) * F::STAGE, s, ln, f[s]);
     const int kn = kt + F::STAGES - 1;
-    if (kn < nk) {
+    if (!F::DMA_IN_C && kn < nk) {
       const int64_t k1 = int64_t(kn) * F::BK;
       F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
                NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): fragments in registers
+    if (F::PRIO == 2) __builtin_amdgcn_s_setprio(0);
     if (group == 1) {
       if (kt + 1 < nk) wait_block<F>(kt + 1, nk);
     }
     phase_barrier();                       // C(kt)
-    __builtin_amdgcn_s_setprio(1);
+    if (F::DMA_IN_C && kn < nk) {
+      // the buffer of block kt-1 was read by both groups before this phase began
+      const int64_t k1 = int64_t(kn) * F::BK;
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
+               NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+    }
+    if (F::PRIO == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < F::SUB; ++s) F::mma(f[s], acc);
-    __builtin_amdgcn_s_setprio(0);
+    if (F::PRIO == 1) __builtin_amdgcn_s_setprio(0);
   }
   if (group == 0) phase_barrier();         // t = 2 nk: group 0 idles while group 1 finishes
 
