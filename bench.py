@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--b-kmajor", action="store_true",
+                    help="hand B (or the gate/up weights) to the library as [N,K] (K contiguous)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed region, run a plain elementwise copy of 256 MiB (reads 256 MiB, writes "
                          "256 MiB) three times: the reference dispatch for scaling HBM byte counters")
@@ -104,11 +106,12 @@ def main():
     torch.cuda.set_device(dev)
 
     x = synth.make_inputs(w)
-    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up)
+    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up, b_kmajor=args.b_kmajor)
+    dev_b = (lambda t: t.t().contiguous().to(dev)) if args.b_kmajor else (lambda t: t.to(dev))
     A = x["A"].to(dev)
     out_dt = synth.torch_dtype(w.out_kind)
     if w.gate_up:
-        Wg, Wu = x["Wg"].to(dev), x["Wu"].to(dev)
+        Wg, Wu = dev_b(x["Wg"]), dev_b(x["Wu"])
         G = torch.empty((w.M, w.N), dtype=out_dt, device=dev)
         if w.act == "swiglu":
             def step(i):
@@ -121,10 +124,10 @@ def main():
         result = G
         b_cpu = x["Wg"]
     else:
-        Bs = [x["B"].to(dev)]
+        Bs = [dev_b(x["B"])]
         if w.name == "skinny":
             # a second B buffer so consecutive steps do not hit B in the 256 MB last-level cache
-            Bs.append(synth.Dist("normal", 0.0, 0.02).sample((w.K, w.N), w.seeds[2], synth.torch_dtype(w.in_kind)).to(dev))
+            Bs.append(dev_b(synth.Dist("normal", 0.0, 0.02).sample((w.K, w.N), w.seeds[2], synth.torch_dtype(w.in_kind))))
         C0 = x["C"].to(dev) if "C" in x else None
         C = torch.empty((w.M, w.N), dtype=out_dt, device=dev) if C0 is None else C0.clone()
 
@@ -203,6 +206,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "strong",
         "vs_baseline": None, "dtype": w.in_kind, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "out": w.out_kind,
+                   "b_order": "nk" if args.b_kmajor else "kn",
                    "alpha": w.alpha, "beta": w.beta, "gate_up": w.gate_up,
                    "kernel": plan.describe()["kernel"], "grid": plan.describe()["grid"]},
         "roofline": roof,

@@ -15,7 +15,8 @@
  * Storage (all row-major, element strides, zero-based, as on the Tylo.jl page
  * "Layouts, storage and ownership", section "A layout is a function"):
  *   A  [M, K]  element (i, k) at A[i * lda + k]          (K contiguous)
- *   B  [K, N]  element (k, j) at B[k * ldb + j]          (N contiguous)
+ *   B  [K, N]  element (k, j) at B[k * ldb + j]          (N contiguous; or, with
+ *              GEMM_FLAG_B_KMAJOR, at B[j * ldb + k], K contiguous)
  *   C  [M, N]  element (i, j) at C[i * ldc + j]
  * B is addressed in its mathematical (K, N) coordinates throughout.
  *
@@ -64,12 +65,17 @@ typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
 
 /* Flags for gemm_desc.flags. */
 #define GEMM_FLAG_GATE_UP 0x1u   /* plan is for gemm_gate_up_run / gemm_gate_up_swiglu_run */
+#define GEMM_FLAG_B_KMAJOR 0x2u  /* B (and W_gate, W_up) stored [N, K]: element (k, n) at
+                                    B[n * ldb + k], ldb >= max(1, k) -- the K-contiguous operand
+                                    storage of the Tylo.jl page "TMA and Hopper WGMMA" (section
+                                    "The same storage contract on both sides") */
 
 typedef struct {
   int64_t m, n, k;             /* problem sizes, each >= 0 */
   int32_t a_type, b_type;      /* gemm_dtype; equal, BF16 or F16 */
   int32_t c_type;              /* gemm_dtype of C (and of G, U): F32, BF16 or F16 */
-  int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k), ldb >= max(1,n), ldc >= max(1,n) */
+  int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k), ldb >= max(1,n) (max(1,k) for
+                                  K-major B), ldc >= max(1,n) */
   uint32_t flags;              /* GEMM_FLAG_* */
 } gemm_desc;
 

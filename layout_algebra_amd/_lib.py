@@ -8,6 +8,7 @@ _LIB_PATH = os.path.join(HERE, "liblagemm.so")
 
 BF16, F16, F32 = 0, 1, 2
 FLAG_GATE_UP = 0x1
+FLAG_B_KMAJOR = 0x2
 
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
@@ -108,12 +109,13 @@ class Plan:
             self._h = ctypes.c_void_p(0)
 
 
-def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False):
+def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False, b_kmajor=False):
+    """Plan C[m,n] = A[m,k] @ B.  B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed)."""
     d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type),
               int(lda if lda is not None else max(1, k)),
-              int(ldb if ldb is not None else max(1, n)),
+              int(ldb if ldb is not None else max(1, k if b_kmajor else n)),
               int(ldc if ldc is not None else max(1, n)),
-              FLAG_GATE_UP if gate_up else 0)
+              (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0))
     h = ctypes.c_void_p()
     _check(load().gemm_plan(ctypes.byref(d), ctypes.byref(h)))
     return Plan(h.value, d)
@@ -168,11 +170,18 @@ def _check_matrix(t, name, rows, cols, ld, kind):
             raise ValueError("%s must be row-major with leading dimension %d (strides %s)" % (name, ld, t.stride()))
 
 
+def _check_b(t, name, d):
+    if d.flags & FLAG_B_KMAJOR:
+        _check_matrix(t, name + " ([n,k], K-major)", d.n, d.k, d.ldb, d.b_type)
+    else:
+        _check_matrix(t, name, d.k, d.n, d.ldb, d.b_type)
+
+
 def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
     """C = alpha * A @ B + beta * C, enqueued on `stream` (default: current)."""
     d = plan.desc
     _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type)
-    _check_matrix(B, "B", d.k, d.n, d.ldb, d.b_type)
+    _check_b(B, "B", d)
     _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type)
     _check(load().gemm_run(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                            ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), _stream_ptr(stream)))
@@ -182,8 +191,8 @@ def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
     """G = X @ W_gate and U = X @ W_up in one launch."""
     d = plan.desc
     _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type)
-    _check_matrix(W_gate, "W_gate", d.k, d.n, d.ldb, d.b_type)
-    _check_matrix(W_up, "W_up", d.k, d.n, d.ldb, d.b_type)
+    _check_b(W_gate, "W_gate", d)
+    _check_b(W_up, "W_up", d)
     _check_matrix(G, "G", d.m, d.n, d.ldc, d.c_type)
     _check_matrix(U, "U", d.m, d.n, d.ldc, d.c_type)
     _check(load().gemm_gate_up_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, G, U)],
@@ -194,8 +203,8 @@ def gemm_gate_up_swiglu_run(plan, X, W_gate, W_up, H, stream=None):
     """H = silu(X @ W_gate) * (X @ W_up) in one launch (activation fused into the epilogue)."""
     d = plan.desc
     _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type)
-    _check_matrix(W_gate, "W_gate", d.k, d.n, d.ldb, d.b_type)
-    _check_matrix(W_up, "W_up", d.k, d.n, d.ldb, d.b_type)
+    _check_b(W_gate, "W_gate", d)
+    _check_b(W_up, "W_up", d)
     _check_matrix(H, "H", d.m, d.n, d.ldc, d.c_type)
     _check(load().gemm_gate_up_swiglu_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, H)],
                                           _stream_ptr(stream)))

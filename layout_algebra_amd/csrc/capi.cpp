@@ -39,7 +39,7 @@ lak::TiledArgs base_args(const gemm_plan_s& p) {
 }
 
 gemm_status launch(const gemm_plan_s& p, const lak::TiledArgs& a, void* stream, bool image) {
-  const hipError_t e = lak::launch_kernel(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, a, p.grid,
+  const hipError_t e = lak::launch_kernel(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, p.b_kmajor, a, p.grid,
                                          static_cast<hipStream_t>(stream), image);
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GEMM_OK;

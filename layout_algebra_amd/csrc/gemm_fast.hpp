@@ -44,6 +44,7 @@ struct Fast {
   static constexpr int STAGES = C::STAGES;
   static constexpr bool SCHED_HINTS = C::SCHED != 4;     // 4: software pipeline without scheduler groups
   static constexpr bool DMA_IN_C = C::DMA_IN_C;           // ping-pong: issue direct loads in the C phase
+  static constexpr bool BKM = C::BKMAJOR;                 // B stored [N, K] (K contiguous) instead of [K, N]
   static constexpr int PRIO = C::PRIO;                    // ping-pong: 0 none, 1 raise C phase, 2 raise M phase
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
@@ -56,7 +57,7 @@ struct Fast {
   static constexpr int A_LOADS = A_ELEMS / 512 / NW;       // 1 KB (512 elements) per wave instruction
   static constexpr int B_LOADS = B_ELEMS / 512 / NW;
   static constexpr int LOADS_PER_STAGE = A_LOADS + NB * B_LOADS;
-  static constexpr int READS_PER_SUB = FM + 2 * NB * FN;   // LDS read instructions per sub-step
+  static constexpr int READS_PER_SUB = FM + (C::BKMAJOR ? 1 : 2) * NB * FN;   // LDS read instructions per sub-step
   static constexpr int MFMA_PER_SUB = NB * FM * FN;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_LOADS * 512 * NW == A_ELEMS && B_LOADS * 512 * NW == B_ELEMS, "blocks must split into whole KB per wave");
@@ -65,7 +66,15 @@ struct Fast {
   static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
 
   static __device__ __forceinline__ int a_off(int r, int k) { return swz<C::AB, C::AM, C::AS>(r * BK + k); }
-  static __device__ __forceinline__ int b_off(int k, int n) { return swz<C::BB, C::BMb, C::BS>(k * BN + n); }
+  // B block in LDS: N-contiguous rows of BN per k, or (K-major B) K-contiguous rows of BK per n.
+  static __device__ __forceinline__ int b_off(int k, int n) {
+    return BKM ? swz<C::BB, C::BMb, C::BS>(n * BK + k) : swz<C::BB, C::BMb, C::BS>(k * BN + n);
+  }
+  // Global B: origin of the tile at column n0, and the element step of K block k1.
+  static __device__ __forceinline__ const uint16_t* b_origin(const uint16_t* B, int64_t n0, int64_t ldb) {
+    return BKM ? B + n0 * ldb : B + n0;
+  }
+  static __device__ __forceinline__ int64_t b_step(int64_t k1, int64_t ldb) { return BKM ? k1 : k1 * ldb; }
 
   // Per-lane source offsets (elements, relative to the tile's origin in the
   // current K block) of every direct load this lane issues.
@@ -85,7 +94,7 @@ struct Fast {
     for (int i = 0; i < B_LOADS; ++i) {
       const int P = (wave * B_LOADS + i) * 512 + lane * 8;
       const int L = swz<C::BB, C::BMb, C::BS>(P);
-      s.b[i] = uint32_t((L / BN) * ldb + (L % BN));
+      s.b[i] = BKM ? uint32_t((L / BK) * ldb + (L % BK)) : uint32_t((L / BN) * ldb + (L % BN));
     }
   }
 
@@ -129,13 +138,14 @@ struct Fast {
 
   // Lane-dependent parts of the fragment addresses.
   struct Lane {
-    int ar, ak, bn, bk;
+    int ar, ak, bn, bk, br;
     __device__ __forceinline__ Lane(int wm, int wn, int lane) {
       ar = wm * TM + (lane & 31);                // A: row l % 32 of each 32-row block
       ak = (lane >> 5) * 8;                      // A: K half of the 16-wide sub-step
-      const int g = lane >> 4;                   // B: 16-lane group
+      const int g = lane >> 4;                   // B (N-contiguous): 16-lane group
       bn = wn * TN + 16 * (g & 1) + 4 * (lane & 3);
       bk = 8 * (g >> 1) + ((lane >> 2) & 3);
+      br = wn * TN + (lane & 31);                // B (K-contiguous): column l % 32 of each 32-column block
     }
   };
 
@@ -152,9 +162,14 @@ struct Fast {
       const LAK_LDS uint16_t* bs = stage + A_ELEMS + t * B_ELEMS;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const u32x2 lo = read_tr(bs + b_off(s * 16 + ln.bk, ln.bn + j * 32));
-        const u32x2 hi = read_tr(bs + b_off(s * 16 + ln.bk + 4, ln.bn + j * 32));
-        f.b[t][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        if constexpr (BKM) {
+          // K-contiguous B rows: one plain 16-byte read gives the lane its 8 K values
+          f.b[t][j] = read_b128(bs + b_off(s * 16 + ln.ak, ln.br + j * 32));
+        } else {
+          const u32x2 lo = read_tr(bs + b_off(s * 16 + ln.bk, ln.bn + j * 32));
+          const u32x2 hi = read_tr(bs + b_off(s * 16 + ln.bk + 4, ln.bn + j * 32));
+          f.b[t][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
       }
     }
   }
@@ -340,8 +355,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const Til
   F::make_src(src, wave, lane, g.lda, g.ldb);
   const typename F::Lane ln(wm, wn, lane);
   const uint16_t* a_tile = g.A + m0 * g.lda;
-  const uint16_t* b_tile = g.B + n0;
-  const uint16_t* b2_tile = NB > 1 ? g.B2 + n0 : nullptr;
+  const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
+  const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
 
   f32x16 acc[NB][F::FM][F::FN];
 #pragma unroll
@@ -360,7 +375,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const Til
   for (int p = 0; p < F::STAGES - 1; ++p) {
     if (p < nk) {
       const int64_t k1 = int64_t(p) * F::BK;
-      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb, NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb), NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
   }
   for (int kt = 0; kt < nk; ++kt) {
@@ -374,8 +389,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const Til
     const int kn = kt + F::STAGES - 1;
     if (kn < nk) {
       const int64_t k1 = int64_t(kn) * F::BK;
-      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
-               NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
+               NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
     F::compute(lds + (kt % F::STAGES) * F::STAGE, acc, ln);
   }
@@ -435,8 +450,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   F::make_src(src, wave, lane, g.lda, g.ldb);
   const typename F::Lane ln(wm, wn, lane);
   const uint16_t* a_tile = g.A + m0 * g.lda;
-  const uint16_t* b_tile = g.B + n0;
-  const uint16_t* b2_tile = NB > 1 ? g.B2 + n0 : nullptr;
+  const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
+  const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
 
   f32x16 acc[NB][F::FM][F::FN];
 #pragma unroll
@@ -451,7 +466,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   for (int p = 0; p < F::STAGES - 1; ++p) {
     if (p < nk) {
       const int64_t k1 = int64_t(p) * F::BK;
-      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb, NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb), NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
   }
   if (group == 1) {
@@ -468,8 +483,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
     const int kn = kt + F::STAGES - 1;
     if (!F::DMA_IN_C && kn < nk) {
       const int64_t k1 = int64_t(kn) * F::BK;
-      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
-               NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
+               NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): fragments in registers
     if (F::PRIO == 2) __builtin_amdgcn_s_setprio(0);
@@ -480,8 +495,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
     if (F::DMA_IN_C && kn < nk) {
       // the buffer of block kt-1 was read by both groups before this phase began
       const int64_t k1 = int64_t(kn) * F::BK;
-      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
-               NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
+               NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
     if (F::PRIO == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -544,8 +559,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const 
   F::make_src(src, wave, lane, g.lda, g.ldb);
   const typename F::Lane ln(wm, wn, lane);
   const uint16_t* a_tile = g.A + m0 * g.lda;
-  const uint16_t* b_tile = g.B + n0;
-  const uint16_t* b2_tile = NB > 1 ? g.B2 + n0 : nullptr;
+  const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
+  const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
 
   f32x16 acc[NB][F::FM][F::FN];
 #pragma unroll
@@ -560,7 +575,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const 
   for (int p = 0; p < F::STAGES - 1; ++p) {
     if (p < nk) {
       const int64_t k1 = int64_t(p) * F::BK;
-      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb, NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb), NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
   }
   if (F::STAGES - 2 <= nk - 1) {          // block 0 landed; blocks 1 .. STAGES-2 may still fly
@@ -590,8 +605,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const 
         const int kn = kt + F::STAGES - 1;
         if (kn < nk) {
           const int64_t k1 = int64_t(kn) * F::BK;
-          F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + k1 * g.ldb,
-                   NB > 1 ? b2_tile + k1 * g.ldb : nullptr, wave);
+          F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
+                   NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
         }
         sp_substep<F, TI>(nxt, 0, ln, f1, f0, acc);
       } else {
@@ -616,7 +631,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_lds_image(const 
   typename F::Src src;
   F::make_src(src, wave, lane, g.lda, g.ldb);
   const int64_t m0 = int64_t(g.dbg_tm) * C::BM, n0 = int64_t(g.dbg_tn) * C::BN;
-  F::issue(src, lds, g.A + m0 * g.lda, g.B + n0, C::NB > 1 ? g.B2 + n0 : nullptr, wave);
+  F::issue(src, lds, g.A + m0 * g.lda, F::b_origin(g.B, n0, g.ldb), C::NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr,
+           wave);
   wait_vmcnt<0>();
   block_barrier();
   for (int i = tid; i < F::STAGE; i += F::NT) g.dbg_out[i] = lds[i];

@@ -31,7 +31,7 @@
 
 namespace lak {
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
 struct Tiled {
   static constexpr int NT = WM * WN * 64;
   static constexpr int BK = 64;
@@ -44,6 +44,7 @@ struct Tiled {
   static constexpr int A_CHUNKS = BM * BK / 8 / NT;
   static constexpr int BN8 = BN / 8;
   static constexpr int B_BLOCKS = (BK / 4) * BN8 / NT;
+  static constexpr int B_CHUNKS = BN * BK / 8 / NT;         // K-major B: 8-element K chunks per thread
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_CHUNKS * NT * 8 == BM * BK, "A block must split evenly over threads");
   static_assert(B_BLOCKS * NT == (BK / 4) * BN8, "B block must split evenly over threads");
@@ -54,7 +55,7 @@ struct Tiled {
 
   struct Regs {
     u32x4 a[A_CHUNKS];
-    u32x4 b[NB][B_BLOCKS][4];
+    u32x4 b[NB][BKM ? B_CHUNKS : B_BLOCKS][BKM ? 1 : 4];
   };
 
   static __device__ __forceinline__ u32x4 pack8(const uint16_t* e) {
@@ -97,6 +98,19 @@ struct Tiled {
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       const uint16_t* B = s == 0 ? g.B : g.B2;
+      if constexpr (BKM) {
+        // B stored [N, K]: rows n of K values, staged exactly like A
+#pragma unroll
+        for (int j = 0; j < B_CHUNKS; ++j) {
+          const int idx = tid + NT * j;
+          const int row = idx >> 3, ch = idx & 7;
+          const int64_t gn = n0 + row;
+          const int64_t gk = k0 + ch * 8;
+          const int nvalid = gn < g.N ? int(min<int64_t>(8, g.K - gk)) : 0;
+          r.b[s][j][0] = load8(B + gn * g.ldb + gk, nvalid);
+        }
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < B_BLOCKS; ++j) {
         const int idx = tid + NT * j;
@@ -122,6 +136,15 @@ struct Tiled {
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       uint16_t* dst = stage + A_ELEMS + s * B_ELEMS;
+      if constexpr (BKM) {
+#pragma unroll
+        for (int j = 0; j < B_CHUNKS; ++j) {
+          const int idx = tid + NT * j;
+          const int row = idx >> 3, ch = idx & 7;
+          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = r.b[s][j][0];
+        }
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < B_BLOCKS; ++j) {
         const int idx = tid + NT * j;
@@ -165,9 +188,9 @@ struct Tiled {
   }
 };
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g) {
-  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU>;
+  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * T::STAGE];
 
   const int tid = threadIdx.x;
@@ -236,9 +259,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
 
 // Debug: stage K block 0 of tile (dbg_tm, dbg_tn) with the kernel's own
 // staging code and copy the LDS stage out verbatim.
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const TiledArgs g) {
-  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU>;
+  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[T::STAGE];
   const int tid = threadIdx.x;
   typename T::Regs r;
@@ -251,43 +274,51 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
 // ------------------------------------------------------------------ dispatch
 namespace {
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
 hipError_t go(const TiledArgs& a, int grid, hipStream_t s, bool img) {
   if (img) {
-    hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU>), dim3(1), dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU, BKM>), dim3(1), dim3(WM * WN * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU>), dim3(grid), dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM>), dim3(grid), dim3(WM * WN * 64), 0, s, a);
   }
   return hipGetLastError();
 }
 
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V>
+hipError_t by_gu_km(bool gu, bool km, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (gu) return km ? go<TI, TO, BM, BN, WM, WN, V, true, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, V, true, false>(a, grid, s, img);
+  return km ? go<TI, TO, BM, BN, WM, WN, V, false, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, V, false, false>(a, grid, s, img);
+}
+
 template <class TI, class TO, int BM, int BN, int WM, int WN>
-hipError_t by_vec_gu(int vec, bool gu, const TiledArgs& a, int grid, hipStream_t s, bool img) {
-  if (vec == 8) return gu ? go<TI, TO, BM, BN, WM, WN, 8, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, 8, false>(a, grid, s, img);
-  if (vec == 1) return gu ? go<TI, TO, BM, BN, WM, WN, 1, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, 1, false>(a, grid, s, img);
+hipError_t by_vec_gu(int vec, bool gu, bool km, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+  if (vec == 8) return by_gu_km<TI, TO, BM, BN, WM, WN, 8>(gu, km, a, grid, s, img);
+  if (vec == 1) return by_gu_km<TI, TO, BM, BN, WM, WN, 1>(gu, km, a, grid, s, img);
   return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, int grid, hipStream_t s,
+                    bool img) {
   if (in_kind == IN_BF16) {
-    if (out_kind == OUT_F32) return by_vec_gu<InBF16, OutF32, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
-    if (out_kind == OUT_BF16) return by_vec_gu<InBF16, OutBF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
-    if (out_kind == OUT_F16) return by_vec_gu<InBF16, OutF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+    if (out_kind == OUT_F32) return by_vec_gu<InBF16, OutF32, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_BF16) return by_vec_gu<InBF16, OutBF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_F16) return by_vec_gu<InBF16, OutF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
   } else if (in_kind == IN_F16) {
-    if (out_kind == OUT_F32) return by_vec_gu<InF16, OutF32, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
-    if (out_kind == OUT_BF16) return by_vec_gu<InF16, OutBF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
-    if (out_kind == OUT_F16) return by_vec_gu<InF16, OutF16, BM, BN, WM, WN>(vec, gu, a, grid, s, img);
+    if (out_kind == OUT_F32) return by_vec_gu<InF16, OutF32, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_BF16) return by_vec_gu<InF16, OutBF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_F16) return by_vec_gu<InF16, OutF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up,
+hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
                         const TiledArgs& args, int grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
-    case KID_TILED_128: return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, args, grid, stream, lds_image);
+    case KID_TILED_128:
+      return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

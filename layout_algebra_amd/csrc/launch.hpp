@@ -26,6 +26,8 @@ enum KernelId : int {
   KID_FAST_256 = 1,      // full tiles: 256x256x64, 8 waves of 128x64, direct-to-LDS, transposing B reads
   KID_FAST_GU = 2,       // full tiles, gate/up: 256 x (128 + 128) x 32, 8 waves of 128 x (32 + 32)
   KID_SKINNY_16 = 3,     // M <= 16: 16 x 128 column strips over all of K, 4 waves of 16 x 32, HBM-bound
+  KID_FAST_256_KM = 4,   // KID_FAST_256 for B stored [N, K] (K contiguous)
+  KID_FAST_GU_KM = 5,    // KID_FAST_GU for weights stored [N, K]
   KID_COUNT
 };
 
@@ -40,17 +42,27 @@ enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 // 16 lanes must touch 16 distinct 16-byte slots of a 256-byte window.
 struct CfgFast256 {
   static constexpr int BM = 256, BN = 256, NB = 1, WM = 2, WN = 4, BK = 32, STAGES = 4, SCHED = 2;
-  static constexpr bool DMA_IN_C = false;
+  static constexpr bool DMA_IN_C = false, BKMAJOR = false;
   static constexpr int PRIO = 0;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 3;  // B: Swizzle{2,5,3} over 512-byte rows
 };
 struct CfgFastGU {
   static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4, BK = 32, STAGES = 4, SCHED = 2;
-  static constexpr bool DMA_IN_C = false;
+  static constexpr bool DMA_IN_C = false, BKMAJOR = false;
   static constexpr int PRIO = 0;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 2;  // B: Swizzle{2,5,2} over 256-byte rows
+};
+// K-major B ([N, K], the storage of the Tylo.jl Hopper page): B blocks are K-contiguous rows
+// like A blocks, read with plain 16-byte LDS reads, under the same swizzle as A.
+struct CfgFast256KM : CfgFast256 {
+  static constexpr bool BKMAJOR = true;
+  static constexpr int BB = 2, BMb = 3, BS = 4;
+};
+struct CfgFastGUKM : CfgFastGU {
+  static constexpr bool BKMAJOR = true;
+  static constexpr int BB = 2, BMb = 3, BS = 4;
 };
 
 struct CfgSkinny16 {
@@ -81,11 +93,11 @@ KernelShape kernel_shape(int kid);
 int64_t stage_elems(const KernelShape& s, bool gate_up);
 
 // Enqueue a GEMM (or, with lds_image, the debug stage dump) on `stream`.
-hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up,
+hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
                          const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
 
 // Per-family launchers.
-hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up,
+hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
                         const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
 hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, int grid,
                        hipStream_t stream, bool lds_image);

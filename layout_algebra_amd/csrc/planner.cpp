@@ -86,6 +86,31 @@ bool check_copy_b(const gemm_plan_s& p, const la::View& v, std::string* err) {
   return true;
 }
 
+// K-major B in the general kernel: like A, thread t, slot j covers
+// (column n, 8-element K chunk), written as one 16-byte vector.
+bool check_copy_b_rows(const gemm_plan_s& p, const la::View& v, std::string* err) {
+  const auto& s = p.shape;
+  const int chunks = s.bn * s.bk / 8;
+  if (chunks % s.threads) return fail(err, "B block does not split evenly into 16-byte vectors per thread");
+  std::vector<int> hits(static_cast<size_t>(s.bn) * s.bk, 0);
+  for (int t = 0; t < s.threads; ++t) {
+    for (int j = 0; j < chunks / s.threads; ++j) {
+      const int idx = t + s.threads * j;
+      const int n = idx / (s.bk / 8), ch = idx % (s.bk / 8);
+      const int64_t o0 = v.at({ch * 8, n});
+      if (o0 % 8) return fail(err, "B copy destination is not 16-byte aligned");
+      for (int e = 0; e < 8; ++e) {
+        const int64_t o = v.at({ch * 8 + e, n});
+        if (o != o0 + e) return fail(err, "B copy destination is not contiguous along K");
+        if (hits[o]++) return fail(err, "B copy plan writes an LDS element twice");
+      }
+    }
+  }
+  for (int h : hits)
+    if (h != 1) return fail(err, "B copy plan leaves an LDS element unwritten");
+  return true;
+}
+
 // Direct global -> LDS copy: wave instruction `blk` writes the contiguous
 // kilobyte [512 blk, 512 blk + 512) (elements) with lane l at 8 l.  The lane's
 // 8 elements must be 8 consecutive elements of one row of the operand as it
@@ -197,7 +222,9 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p.d = d;
   if (d.m < 0 || d.n < 0 || d.k < 0) { fail(err, "m, n and k must be >= 0"); return GEMM_ERR_INVALID_ARG; }
   if (d.lda < std::max<int64_t>(1, d.k)) { fail(err, "lda must be >= max(1, k)"); return GEMM_ERR_INVALID_ARG; }
-  if (d.ldb < std::max<int64_t>(1, d.n)) { fail(err, "ldb must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
+  const bool kmajor = (d.flags & GEMM_FLAG_B_KMAJOR) != 0;
+  if (!kmajor && d.ldb < std::max<int64_t>(1, d.n)) { fail(err, "ldb must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
+  if (kmajor && d.ldb < std::max<int64_t>(1, d.k)) { fail(err, "ldb must be >= max(1, k) for K-major B"); return GEMM_ERR_INVALID_ARG; }
   if (d.ldc < std::max<int64_t>(1, d.n)) { fail(err, "ldc must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
   if ((d.a_type != GEMM_BF16 && d.a_type != GEMM_F16 && d.a_type != GEMM_F32) ||
       (d.b_type != GEMM_BF16 && d.b_type != GEMM_F16 && d.b_type != GEMM_F32) ||
@@ -205,7 +232,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     fail(err, "unknown dtype");
     return GEMM_ERR_INVALID_ARG;
   }
-  if (d.flags & ~GEMM_FLAG_GATE_UP) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
+  if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR)) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
   if (d.a_type != d.b_type || d.a_type == GEMM_F32) {
     fail(err, "A and B must both be bf16 or both be f16");
     return GEMM_ERR_UNSUPPORTED;
@@ -217,6 +244,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   }
 
   p.gate_up = (d.flags & GEMM_FLAG_GATE_UP) != 0;
+  p.b_kmajor = kmajor;
   p.in_kind = d.a_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16;
   p.out_kind = d.c_type == GEMM_F32 ? lak::OUT_F32 : d.c_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16;
   p.out_bytes = d.c_type == GEMM_F32 ? 4 : 2;
@@ -228,16 +256,18 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   // masks edges and narrows its loads to the alignment class.
   p.kid = lak::KID_TILED_128;
   {
-    const int fk = p.gate_up ? lak::KID_FAST_GU : lak::KID_FAST_256;
+    const int fk = p.gate_up ? (kmajor ? lak::KID_FAST_GU_KM : lak::KID_FAST_GU)
+                             : (kmajor ? lak::KID_FAST_256_KM : lak::KID_FAST_256);
     const lak::KernelShape fs = lak::kernel_shape(fk);
     const bool whole = d.m > 0 && d.n > 0 && d.k > 0 && d.m % fs.bm == 0 && d.n % fs.bn == 0 && d.k % fs.bk == 0;
     const bool rows16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && d.ldc % 8 == 0;
     // per-lane source offsets of the direct loads are 32-bit byte offsets
-    const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * int64_t(fs.bk) * d.ldb < (int64_t{1} << 32);
+    const int64_t b_rows = kmajor ? fs.bn : fs.bk;   // rows of B one block spans in memory
+    const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
     if (whole && rows16 && off32) p.kid = fk;
     // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
     const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
-    const bool skinny_fit = !p.gate_up && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
+    const bool skinny_fit = !p.gate_up && !kmajor && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
                             d.k % ks.bk == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0 &&
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
@@ -246,7 +276,9 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p.shape = lak::kernel_shape(p.kid);
   const auto& s = p.shape;
   // The fast kernels write C with 16-byte vectors, so C rows start on 16 bytes.
-  p.out_align_bytes = (p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU) ? 16 : p.out_bytes;
+  const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
+                    p.kid == lak::KID_FAST_GU_KM;
+  p.out_align_bytes = fast ? 16 : p.out_bytes;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
   if (int64_t(p.tiles_m) * p.tiles_n > (int64_t{1} << 31) - 1) { fail(err, "too many tiles"); return GEMM_ERR_UNSUPPORTED; }
@@ -274,7 +306,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
       if (!check_copy_direct(p.lds_a, s.bm, s.bk, true, "A", err) ||
           !check_copy_direct(p.lds_b, s.bk, s.bn, !s.b_kmajor, "B", err))
         return GEMM_ERR_RESOURCE;
-    } else if (!check_copy_a(p, err) || !check_copy_b(p, p.lds_b, err)) {
+    } else if (!check_copy_a(p, err) || !(p.b_kmajor ? check_copy_b_rows(p, p.lds_b, err) : check_copy_b(p, p.lds_b, err))) {
       return GEMM_ERR_RESOURCE;
     }
     if (!check_fragment_reads(p, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
@@ -284,12 +316,13 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   }
 
   std::ostringstream js;
-  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny"};
+  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor"};
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
      << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc
      << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"out\":\"" << dtype_name(d.c_type) << "\""
      << ",\"gate_up\":" << (p.gate_up ? "true" : "false")
+     << ",\"b_order\":\"" << (p.b_kmajor ? "nk" : "kn") << "\""
      << ",\"tile\":[" << s.bm << "," << s.bn << "," << s.bk << "]"
      << ",\"waves\":[" << s.waves_m << "," << s.waves_n << "],\"threads\":" << s.threads
      << ",\"mfma\":\"" << s.mfma_m << "x" << s.mfma_n << "x" << s.mfma_k << "\""

@@ -16,6 +16,7 @@ struct gemm_plan_s {
   int out_bytes = 4;         // bytes per C element
   int out_align_bytes = 4;   // required alignment of the C / G / U pointers
   bool gate_up = false;
+  bool b_kmajor = false;     // B (and the gate/up weights) stored [N, K]
   int tiles_m = 0, tiles_n = 0, grid = 0, group_m = 8;
   int64_t stage_elems = 0, lds_bytes = 0;
   lak::KernelShape shape{};

@@ -19,13 +19,17 @@ DEV = "cuda:0"
 CODE = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
 
 
-def run_gemm(a, b, out_kind, alpha=1.0, beta=0.0, c=None):
-    """a, b CPU tensors; returns the GPU result on the CPU."""
+def run_gemm(a, b, out_kind, alpha=1.0, beta=0.0, c=None, b_kmajor=False, expect=None):
+    """a [M,K], b [K,N] CPU tensors (b is handed to the GPU as [N,K] when b_kmajor);
+    returns the GPU result on the CPU."""
     M, K = a.shape
     N = b.shape[1]
     in_kind = "bf16" if a.dtype == torch.bfloat16 else "f16"
-    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind])
-    A, B = a.to(DEV), b.to(DEV)
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], b_kmajor=b_kmajor)
+    if expect is not None:
+        assert plan.describe()["kernel"].startswith(expect), plan.describe()["kernel"]
+    A = a.to(DEV)
+    B = b.t().contiguous().to(DEV) if b_kmajor else b.to(DEV)
     if c is None:
         C = torch.full((M, N), float("nan"), dtype=synth.torch_dtype(out_kind), device=DEV)
     else:
@@ -253,16 +257,20 @@ LDS_CASES = {
     "fast_gate_up": (512, 256, 128, "bf16", True, 1, 1, "fast_gate_up_"),
     "tiled_gate_up_edge": (300, 200, 100, "bf16", True, 2, 1, "tiled_"),
     "skinny_bf16": (16, 512, 256, "bf16", False, 0, 2, "skinny_"),
+    "fast_bkmajor": (512, 512, 256, "bf16", False, 1, 1, "fast_bkmajor_", True),
+    "fast_gate_up_bkmajor": (512, 256, 128, "f16", True, 1, 1, "fast_gate_up_bkmajor_", True),
+    "tiled_bkmajor_edge": (300, 200, 100, "bf16", False, 2, 1, "tiled_", True),
 }
 
 
 @pytest.mark.parametrize("case", list(LDS_CASES))
 def test_lds_image_matches_planner(case):
-    M, N, K, kind, gu, tm, tn, prefix = LDS_CASES[case]
+    M, N, K, kind, gu, tm, tn, prefix = LDS_CASES[case][:8]
+    km = len(LDS_CASES[case]) > 8 and LDS_CASES[case][8]
     a = synth.uniform((M, K), 21, kind)
     b = synth.uniform((K, N), 22, kind)
     b2 = synth.uniform((K, N), 23, kind) if gu else None
-    plan = la.gemm_plan(M, N, K, CODE[kind], la.F32, gate_up=gu)
+    plan = la.gemm_plan(M, N, K, CODE[kind], la.F32, gate_up=gu, b_kmajor=km)
     d = la.gemm_plan_describe(plan)
     assert d["kernel"].startswith(prefix), d["kernel"]
     bm, bn, bk = d["tile"]
@@ -270,7 +278,8 @@ def test_lds_image_matches_planner(case):
     if gu:
         ops.append((b2, bk, bn, 0, tn * bn))
     want, _ = _expected_image(plan, ops, tm, tn)
-    got = _lds_image(plan, a.to(DEV), b.to(DEV), b2.to(DEV) if gu else None, tm, tn)
+    dev_b = (lambda t: t.t().contiguous().to(DEV)) if km else (lambda t: t.to(DEV))
+    got = _lds_image(plan, a.to(DEV), dev_b(b), dev_b(b2) if gu else None, tm, tn)
     assert not np.any(want == 0xDEAD), "planner map does not cover the stage"
     assert np.array_equal(got.astype(np.uint32), want)
 
@@ -375,3 +384,46 @@ def test_gate_up_swiglu(shape):
     tol = swiglu_bound(K, x, wg, wu, g_ref, u_ref, h_ref, "bf16")
     err = np.abs(got - h_ref)
     assert np.all(err <= tol), "max err %g at %s" % (err.max(), np.unravel_index(np.argmax(err - tol), err.shape))
+
+
+KM_SHAPES = [((256, 256, 64), "fast_bkmajor_"), ((512, 768, 320), "fast_bkmajor_"), ((33, 65, 17), "tiled_"),
+             ((1000, 1537, 999), "tiled_"), ((16, 1024, 2048), "tiled_"), ((256, 1024, 4096), "fast_bkmajor_")]
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("case", KM_SHAPES, ids=[str(c[0]) for c in KM_SHAPES])
+def test_bkmajor_shapes(case, in_kind, out_kind):
+    (M, N, K), expect = case
+    seed = 5 * M + 3 * N + K
+    a = synth.normal((M, K), seed, in_kind)
+    b = synth.normal((K, N), seed + 1, in_kind, 0.5)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got = run_gemm(a, b, out_kind, 0.5, 1.5, c, b_kmajor=True, expect=expect)
+    ref = oracle_gemm(a, b, in_kind, 0.5, 1.5, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "K-major B %s" % ((M, N, K),))
+
+
+def test_bkmajor_permutation_is_exact():
+    K = 512
+    a = synth.uniform((256, K), 81, "bf16")
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(82))
+    P = torch.zeros((K, K), dtype=torch.bfloat16)
+    P[perm, torch.arange(K)] = 1
+    got = run_gemm(a, P, "bf16", b_kmajor=True, expect="fast_bkmajor_")
+    assert torch.equal(got, a[:, perm])
+
+
+@pytest.mark.parametrize("shape", [(512, 256, 192), (300, 200, 100)], ids=["fast", "tiled_edges"])
+def test_gate_up_bkmajor(shape):
+    M, N, K = shape
+    x = synth.normal((M, K), 91, "bf16")
+    wg = synth.normal((K, N), 92, "bf16", 0.3)
+    wu = synth.normal((K, N), 93, "bf16", 0.3)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, b_kmajor=True)
+    G = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    U = torch.full_like(G, float("nan"))
+    la.gemm_gate_up_run(plan, x.to(DEV), wg.t().contiguous().to(DEV), wu.t().contiguous().to(DEV), G, U)
+    torch.cuda.synchronize()
+    for name, w, out in (("G", wg, G), ("U", wu, U)):
+        assert_close(out.cpu(), oracle_gemm(x, w, "bf16"), K, x, w, "bf16", "gate_up K-major %s %s" % (name, shape))
