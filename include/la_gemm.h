@@ -77,6 +77,15 @@ typedef struct {
   int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k), ldb >= max(1,n) (max(1,k) for
                                   K-major B), ldc >= max(1,n) */
   uint32_t flags;              /* GEMM_FLAG_* */
+  int64_t batch;               /* >= 1: independent GEMMs per run (1..65535); matrix b of each operand
+                                  starts stride_* elements after matrix b-1 (a batch coordinate, as the
+                                  Tylo.jl page "TMA and Hopper WGMMA" binds a batch of matrices with a
+                                  third origin coordinate, section "The same storage contract on both
+                                  sides") */
+  int64_t stride_a, stride_b, stride_c;  /* element strides between matrices, >= 0, read only when
+                                  batch > 1; inputs may alias (0 broadcasts one matrix), outputs may
+                                  not: stride_c >= (m-1)*ldc + n.  They join lda/ldb/ldc in the
+                                  alignment class (16-byte vectors need multiples of 8) */
 } gemm_desc;
 
 typedef struct gemm_plan_s* gemm_plan_t;   /* opaque, immutable, host-only */
@@ -93,7 +102,9 @@ void gemm_plan_destroy(gemm_plan_t plan);
  * aligned to the plan's alignment class (see gemm_plan_describe); C may be
  * read (beta != 0) and written only inside [0,m) x [0,n).  When beta == 0, C
  * is not read (NaN there does not propagate).  k == 0 gives C = beta * C.
- * m == 0 or n == 0 launches nothing.  Outputs are rounded to nearest even. */
+ * m == 0 or n == 0 launches nothing.  Outputs are rounded to nearest even.
+ * With batch > 1 the pointers address matrix 0 and matrix b sits at
+ * b * stride_* elements further on; all matrices run in one launch. */
 gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
                      float alpha, float beta, void* stream);
 

@@ -32,7 +32,8 @@ class _Desc(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32), ("c_type", ctypes.c_int32),
                 ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("batch", ctypes.c_int64),
+                ("stride_a", ctypes.c_int64), ("stride_b", ctypes.c_int64), ("stride_c", ctypes.c_int64)]
 
 
 _lib = None
@@ -109,13 +110,18 @@ class Plan:
             self._h = ctypes.c_void_p(0)
 
 
-def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False, b_kmajor=False):
-    """Plan C[m,n] = A[m,k] @ B.  B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed)."""
-    d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type),
-              int(lda if lda is not None else max(1, k)),
-              int(ldb if ldb is not None else max(1, k if b_kmajor else n)),
-              int(ldc if ldc is not None else max(1, n)),
-              (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0))
+def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False, b_kmajor=False,
+              batch=1, stride_a=None, stride_b=None, stride_c=None):
+    """Plan C[m,n] = A[m,k] @ B.  B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed).
+    batch > 1: tensors gain a leading batch dimension with the given element strides (default: packed)."""
+    lda = int(lda if lda is not None else max(1, k))
+    ldb = int(ldb if ldb is not None else max(1, k if b_kmajor else n))
+    ldc = int(ldc if ldc is not None else max(1, n))
+    d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type), lda, ldb, ldc,
+              (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0), int(batch),
+              int(stride_a if stride_a is not None else m * lda),
+              int(stride_b if stride_b is not None else (n if b_kmajor else k) * ldb),
+              int(stride_c if stride_c is not None else m * ldc))
     h = ctypes.c_void_p()
     _check(load().gemm_plan(ctypes.byref(d), ctypes.byref(h)))
     return Plan(h.value, d)
@@ -157,32 +163,39 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _check_matrix(t, name, rows, cols, ld, kind):
+_BATCH = {}
+
+
+def _check_matrix(t, name, rows, cols, ld, kind, batch=1, bstride=0):
+    """2-D [rows, cols] tensor, or for batch > 1 a 3-D [batch, rows, cols] tensor with batch stride bstride."""
     torch = _torch()
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise ValueError("%s must be a tensor on the GPU" % name)
     if _KIND.get(t.dtype) != kind:
         raise ValueError("%s has dtype %s, plan expects type code %d" % (name, t.dtype, kind))
-    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
-        raise ValueError("%s must have shape (%d, %d), got %s" % (name, rows, cols, tuple(t.shape)))
+    want = (rows, cols) if batch == 1 else (batch, rows, cols)
+    if tuple(t.shape) != want:
+        raise ValueError("%s must have shape %s, got %s" % (name, want, tuple(t.shape)))
     if rows > 0 and cols > 0:
-        if t.stride(1) != 1 or (rows > 1 and t.stride(0) != ld):
+        if t.stride(-1) != 1 or (rows > 1 and t.stride(-2) != ld):
             raise ValueError("%s must be row-major with leading dimension %d (strides %s)" % (name, ld, t.stride()))
+        if batch > 1 and t.stride(0) != bstride:
+            raise ValueError("%s must have batch stride %d (strides %s)" % (name, bstride, t.stride()))
 
 
 def _check_b(t, name, d):
     if d.flags & FLAG_B_KMAJOR:
-        _check_matrix(t, name + " ([n,k], K-major)", d.n, d.k, d.ldb, d.b_type)
+        _check_matrix(t, name + " ([n,k], K-major)", d.n, d.k, d.ldb, d.b_type, d.batch, d.stride_b)
     else:
-        _check_matrix(t, name, d.k, d.n, d.ldb, d.b_type)
+        _check_matrix(t, name, d.k, d.n, d.ldb, d.b_type, d.batch, d.stride_b)
 
 
 def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
     """C = alpha * A @ B + beta * C, enqueued on `stream` (default: current)."""
     d = plan.desc
-    _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type)
+    _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
     _check_b(B, "B", d)
-    _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type)
+    _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_run(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                            ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), _stream_ptr(stream)))
 
@@ -190,11 +203,11 @@ def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
 def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
     """G = X @ W_gate and U = X @ W_up in one launch."""
     d = plan.desc
-    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type)
+    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
     _check_b(W_gate, "W_gate", d)
     _check_b(W_up, "W_up", d)
-    _check_matrix(G, "G", d.m, d.n, d.ldc, d.c_type)
-    _check_matrix(U, "U", d.m, d.n, d.ldc, d.c_type)
+    _check_matrix(G, "G", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
+    _check_matrix(U, "U", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_gate_up_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, G, U)],
                                    _stream_ptr(stream)))
 
@@ -202,10 +215,10 @@ def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
 def gemm_gate_up_swiglu_run(plan, X, W_gate, W_up, H, stream=None):
     """H = silu(X @ W_gate) * (X @ W_up) in one launch (activation fused into the epilogue)."""
     d = plan.desc
-    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type)
+    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
     _check_b(W_gate, "W_gate", d)
     _check_b(W_up, "W_up", d)
-    _check_matrix(H, "H", d.m, d.n, d.ldc, d.c_type)
+    _check_matrix(H, "H", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_gate_up_swiglu_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, H)],
                                           _stream_ptr(stream)))
 

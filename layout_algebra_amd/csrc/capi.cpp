@@ -35,11 +35,16 @@ lak::TiledArgs base_args(const gemm_plan_s& p) {
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
   a.group_m = p.group_m;
+  a.sa = p.d.stride_a;
+  a.sb = p.d.stride_b;
+  a.sc = p.d.stride_c;
+  a.out_bytes = p.out_bytes;
   return a;
 }
 
 gemm_status launch(const gemm_plan_s& p, const lak::TiledArgs& a, void* stream, bool image) {
-  const hipError_t e = lak::launch_kernel(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, p.b_kmajor, a, p.grid,
+  const dim3 grid(static_cast<unsigned>(p.grid), image ? 1u : static_cast<unsigned>(p.d.batch));
+  const hipError_t e = lak::launch_kernel(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, p.b_kmajor, a, grid,
                                          static_cast<hipStream_t>(stream), image);
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GEMM_OK;

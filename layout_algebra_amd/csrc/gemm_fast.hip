@@ -5,25 +5,25 @@ namespace lak {
 namespace {
 
 template <class C, class TI, class TO>
-hipError_t go_fast(const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t go_fast(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   constexpr int NT = C::WM * C::WN * 64;
   if (img) {
     hipLaunchKernelGGL((gemm_fast_lds_image<TI, TO, C>),
                        dim3(1), dim3(NT), 0, s, a);
   } else {
     if constexpr (C::SCHED == 2) {
-      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
+      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
     } else if constexpr (C::SCHED == 3) {
-      hipLaunchKernelGGL((gemm_fast_sp_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
+      hipLaunchKernelGGL((gemm_fast_sp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
     } else {
-      hipLaunchKernelGGL((gemm_fast_kernel<TI, TO, C>), dim3(grid), dim3(NT), 0, s, a);
+      hipLaunchKernelGGL((gemm_fast_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
     }
   }
   return hipGetLastError();
 }
 
 template <class C>
-hipError_t by_types(int in_kind, int out_kind, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t by_types(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (in_kind == IN_BF16) {
     if (out_kind == OUT_F32) return go_fast<C, InBF16, OutF32>(a, grid, s, img);
     if (out_kind == OUT_BF16) return go_fast<C, InBF16, OutBF16>(a, grid, s, img);
@@ -38,7 +38,7 @@ hipError_t by_types(int in_kind, int out_kind, const TiledArgs& a, int grid, hip
 
 }  // namespace
 
-hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, int grid, hipStream_t stream,
+hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                        bool lds_image) {
   switch (kid) {
     case KID_FAST_256: return by_types<CfgFast256>(in_kind, out_kind, args, grid, stream, lds_image);

@@ -337,7 +337,8 @@ __device__ __forceinline__ void block_barrier_nowait() {
 }
 
 template <class TI, class TO, class C>
-__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const TiledArgs g) {
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const TiledArgs g_in) {
+  const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
   constexpr int NB = C::NB;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
@@ -430,7 +431,8 @@ __device__ __forceinline__ void wait_block(int kt, int nk) {
 }
 
 template <class TI, class TO, class C>
-__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const TiledArgs g) {
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const TiledArgs g_in) {
+  const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
   constexpr int NB = C::NB;
   static_assert(C::WM * C::WN == 8, "ping-pong needs two groups of four waves");
@@ -539,7 +541,8 @@ __device__ __forceinline__ void sp_substep(const LAK_LDS uint16_t* next_stage, i
 }
 
 template <class TI, class TO, class C>
-__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const TiledArgs g) {
+__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const TiledArgs g_in) {
+  const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
   constexpr int NB = C::NB;
   static_assert(C::STAGES >= 3, "the software pipeline reads one block ahead");

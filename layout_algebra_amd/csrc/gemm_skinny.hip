@@ -64,7 +64,8 @@ __device__ __forceinline__ void sk_dma16(const uint16_t* base, uint32_t voff, co
 }
 
 template <class TI, class TO, class C>
-__global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g) {
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) {
+  const TiledArgs g = at_batch(g_in);
   constexpr int BM = 16, BN = C::BN, BK = C::BK, S = C::STAGES;
   constexpr int NW = 4;
   constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
@@ -190,18 +191,18 @@ __global__ void __launch_bounds__(256) gemm_skinny_lds_image(const TiledArgs g) 
 }
 
 template <class TI, class TO>
-hipError_t go_skinny(const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t go_skinny(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (img) {
     hipLaunchKernelGGL((gemm_skinny_lds_image<TI, TO, CfgSkinny16>), dim3(1), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_skinny_kernel<TI, TO, CfgSkinny16>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<TI, TO, CfgSkinny16>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (in_kind == IN_BF16) {
     if (out_kind == OUT_F32) return go_skinny<InBF16, OutF32>(a, grid, s, img);
     if (out_kind == OUT_BF16) return go_skinny<InBF16, OutBF16>(a, grid, s, img);

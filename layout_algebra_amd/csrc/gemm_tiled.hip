@@ -189,7 +189,8 @@ struct Tiled {
 };
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g) {
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g_in) {
+  const TiledArgs g = at_batch(g_in);
   using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * T::STAGE];
 
@@ -275,30 +276,30 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
 namespace {
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
-hipError_t go(const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t go(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (img) {
     hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU, BKM>), dim3(1), dim3(WM * WN * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM>), dim3(grid), dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM>), grid, dim3(WM * WN * 64), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V>
-hipError_t by_gu_km(bool gu, bool km, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t by_gu_km(bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (gu) return km ? go<TI, TO, BM, BN, WM, WN, V, true, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, V, true, false>(a, grid, s, img);
   return km ? go<TI, TO, BM, BN, WM, WN, V, false, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, V, false, false>(a, grid, s, img);
 }
 
 template <class TI, class TO, int BM, int BN, int WM, int WN>
-hipError_t by_vec_gu(int vec, bool gu, bool km, const TiledArgs& a, int grid, hipStream_t s, bool img) {
+hipError_t by_vec_gu(int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (vec == 8) return by_gu_km<TI, TO, BM, BN, WM, WN, 8>(gu, km, a, grid, s, img);
   if (vec == 1) return by_gu_km<TI, TO, BM, BN, WM, WN, 1>(gu, km, a, grid, s, img);
   return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, int grid, hipStream_t s,
+hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s,
                     bool img) {
   if (in_kind == IN_BF16) {
     if (out_kind == OUT_F32) return by_vec_gu<InBF16, OutF32, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
@@ -315,7 +316,7 @@ hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const 
 }  // namespace
 
 hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
-                        const TiledArgs& args, int grid, hipStream_t stream, bool lds_image) {
+                        const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
     case KID_TILED_128:
       return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);

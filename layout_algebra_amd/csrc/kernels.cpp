@@ -32,7 +32,7 @@ int64_t stage_elems(const KernelShape& s, bool gate_up) {
 }
 
 hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, const TiledArgs& args,
-                         int grid, hipStream_t stream, bool lds_image) {
+                         dim3 grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
     case KID_TILED_128: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     case KID_FAST_256:

@@ -16,10 +16,24 @@ struct TiledArgs {
   int64_t M, N, K, lda, ldb, ldc;
   float alpha, beta;
   int act;               // gate/up only: 0 = write G and U, 1 = write silu(G) * U to C
+  int64_t sa, sb, sc;    // batched launches: element strides between consecutive A, B (and B2), C (and C2)
+  int out_bytes;         // bytes per C element (for the C batch stride)
   int tiles_m, tiles_n, group_m;
   int dbg_tm, dbg_tn;    // LDS-image debug launch: tile to stage
   uint16_t* dbg_out;     // LDS-image debug launch: destination of one stage
 };
+
+// The matrices of batch entry blockIdx.y (grid dimension y = batch count).
+__device__ __forceinline__ TiledArgs at_batch(const TiledArgs& g) {
+  TiledArgs r = g;
+  const int64_t z = blockIdx.y;
+  r.A = g.A + z * g.sa;
+  r.B = g.B + z * g.sb;
+  r.B2 = g.B2 ? g.B2 + z * g.sb : nullptr;
+  r.C = g.C ? static_cast<void*>(static_cast<char*>(g.C) + z * g.sc * g.out_bytes) : nullptr;
+  r.C2 = g.C2 ? static_cast<void*>(static_cast<char*>(g.C2) + z * g.sc * g.out_bytes) : nullptr;
+  return r;
+}
 
 enum KernelId : int {
   KID_TILED_128 = 0,     // any shape: 128x128x64, 4 waves of 64x64, register-staged, B transposed while staging
@@ -94,14 +108,14 @@ int64_t stage_elems(const KernelShape& s, bool gate_up);
 
 // Enqueue a GEMM (or, with lds_image, the debug stage dump) on `stream`.
 hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
-                         const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
+                         const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
 
 // Per-family launchers.
 hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
-                        const TiledArgs& args, int grid, hipStream_t stream, bool lds_image);
-hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, int grid,
+                        const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
+hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid,
                        hipStream_t stream, bool lds_image);
-hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, int grid, hipStream_t stream,
+hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                          bool lds_image);
 
 }  // namespace lak

@@ -233,6 +233,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     return GEMM_ERR_INVALID_ARG;
   }
   if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR)) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
+  if (d.batch < 1 || d.batch > 65535) { fail(err, "batch must be in 1..65535"); return GEMM_ERR_INVALID_ARG; }
+  if (d.stride_a < 0 || d.stride_b < 0 || d.stride_c < 0) { fail(err, "batch strides must be >= 0"); return GEMM_ERR_INVALID_ARG; }
+  if (d.batch > 1 && d.m > 0 && d.n > 0 && __int128(d.stride_c) < __int128(d.m - 1) * d.ldc + d.n) {
+    fail(err, "batched outputs would overlap: stride_c must be >= (m-1)*ldc + n");
+    return GEMM_ERR_INVALID_ARG;
+  }
   if (d.a_type != d.b_type || d.a_type == GEMM_F32) {
     fail(err, "A and B must both be bf16 or both be f16");
     return GEMM_ERR_UNSUPPORTED;
@@ -248,7 +254,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p.in_kind = d.a_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16;
   p.out_kind = d.c_type == GEMM_F32 ? lak::OUT_F32 : d.c_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16;
   p.out_bytes = d.c_type == GEMM_F32 ? 4 : 2;
-  p.vec = (d.lda % 8 == 0 && d.ldb % 8 == 0) ? 8 : 1;
+  // Batch strides move every row start of matrix b by b*stride, so with more
+  // than one matrix they join the leading dimensions in the alignment class.
+  const bool many = d.batch > 1;
+  const bool in16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && (!many || (d.stride_a % 8 == 0 && d.stride_b % 8 == 0));
+  const bool out16 = d.ldc % 8 == 0 && (!many || d.stride_c % 8 == 0);
+  p.vec = in16 ? 8 : 1;
   p.align_bytes = 2 * p.vec;
 
   // Kernel choice: the full-tile direct-load kernels when every tile is whole
@@ -260,7 +271,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
                              : (kmajor ? lak::KID_FAST_256_KM : lak::KID_FAST_256);
     const lak::KernelShape fs = lak::kernel_shape(fk);
     const bool whole = d.m > 0 && d.n > 0 && d.k > 0 && d.m % fs.bm == 0 && d.n % fs.bn == 0 && d.k % fs.bk == 0;
-    const bool rows16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && d.ldc % 8 == 0;
+    const bool rows16 = in16 && out16;
     // per-lane source offsets of the direct loads are 32-bit byte offsets
     const int64_t b_rows = kmajor ? fs.bn : fs.bk;   // rows of B one block spans in memory
     const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
@@ -268,7 +279,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
     const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
     const bool skinny_fit = !p.gate_up && !kmajor && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
-                            d.k % ks.bk == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0 &&
+                            d.k % ks.bk == 0 && in16 &&
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
     if (skinny_fit) p.kid = lak::KID_SKINNY_16;
@@ -323,6 +334,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
      << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"out\":\"" << dtype_name(d.c_type) << "\""
      << ",\"gate_up\":" << (p.gate_up ? "true" : "false")
      << ",\"b_order\":\"" << (p.b_kmajor ? "nk" : "kn") << "\""
+     << ",\"batch\":" << d.batch
      << ",\"tile\":[" << s.bm << "," << s.bn << "," << s.bk << "]"
      << ",\"waves\":[" << s.waves_m << "," << s.waves_n << "],\"threads\":" << s.threads
      << ",\"mfma\":\"" << s.mfma_m << "x" << s.mfma_n << "x" << s.mfma_k << "\""

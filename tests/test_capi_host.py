@@ -147,6 +147,29 @@ def test_invalid_requests_are_rejected():
     assert e.value.name == "GEMM_ERR_UNSUPPORTED"
 
 
+def test_batch_descriptor_is_validated():
+    """Batch count and strides: a batch of independent matrices, each addressed by a
+    third origin coordinate (Tylo.jl, "TMA and Hopper WGMMA", section "The same
+    storage contract on both sides")."""
+    bad = [dict(batch=0), dict(batch=65536), dict(batch=2, stride_a=-8),
+           dict(batch=2, stride_c=64 * 64 - 1)]          # matrix 1 of C would overlap matrix 0
+    for kw in bad:
+        with pytest.raises(la.GemmError) as e:
+            la.gemm_plan(64, 64, 64, la.BF16, la.F32, **kw)
+        assert e.value.name == "GEMM_ERR_INVALID_ARG", kw
+    # inputs may alias: stride 0 broadcasts one B to every matrix of the batch
+    d = la.gemm_plan(4096, 4096, 4096, la.BF16, la.BF16, batch=3, stride_b=0).describe()
+    assert d["batch"] == 3 and d["kernel"].startswith("fast_") and d["align_bytes"] == 16
+    # a stride that is not a multiple of 8 elements leaves the 16-byte class
+    d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=2, stride_a=256 * 256 + 4).describe()
+    assert d["kernel"].startswith("tiled") and d["align_bytes"] == 2
+    # the same stride is ignored for a single matrix
+    d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=1, stride_a=256 * 256 + 4).describe()
+    assert d["kernel"].startswith("fast_")
+    d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=2, stride_c=256 * 256 + 4).describe()
+    assert d["kernel"].startswith("tiled") and d["align_bytes"] == 16 and d["out_align_bytes"] == 2
+
+
 def test_run_argument_errors_are_caught_before_launch():
     lib = la.load()
     p = la.gemm_plan(64, 64, 64, la.BF16, la.F32)
