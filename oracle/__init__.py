@@ -7,6 +7,8 @@ no code with the HIP library and never imports it; the two meet only through
 the seeded inputs the callers pass to both.
 
 * ``gemm_f64``  -- FP64 triple loop (C, OpenMP over rows), see ``gemm_f64.c``.
+* ``gate_up_swiglu_f64`` -- the gate/up products with the SwiGLU activation.
+* ``rms_norm_f64`` -- the row normalisation, numpy in binary64.
 * ``layout_ref`` -- the layout algebra written out by enumeration in Python.
 """
 import ctypes
@@ -115,3 +117,26 @@ def gate_up_swiglu_f64(x_bits, w_gate_bits, w_up_bits, kind, nthreads=0):
     with np.errstate(over="ignore"):
         h = g / (1.0 + np.exp(-g)) * u
     return h, g, u
+
+
+def rms_norm_f64(x, g, eps):
+    """Row normalisation in binary64, the kernel of the Phobos page "Tiles and
+    shared memory" (section "A complete kernel"): for every row i,
+    ss[i] = sum_j x[i, j]^2, inv[i] = 1 / sqrt(ss[i] / D + eps), and
+    y[i, j] = x[i, j] * inv[i] * g[j].
+
+    ``x`` is an (M, D) array of the exact input values, ``g`` the D gains.
+    Returns (y, inv) as float64 arrays; with D == 0 there is nothing to
+    normalise and inv is NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64).reshape(-1)
+    if x.ndim != 2 or g.shape[0] != x.shape[1]:
+        raise ValueError("x must be (M, D) and g (D,), got %s and %s" % (x.shape, g.shape))
+    M, D = x.shape
+    if D == 0:
+        return np.empty((M, 0)), np.full(M, np.nan)
+    ss = np.sum(x * x, axis=1)
+    inv = 1.0 / np.sqrt(ss / D + float(eps))
+    y = x * inv[:, None] * g[None, :]
+    return y, inv

@@ -90,6 +90,49 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class NormWorkload:
+    """Row normalisation Y = X * inv_rms(X) * G over [M, D] rows."""
+    name: str
+    M: int
+    D: int
+    in_kind: str                 # X and G: "f32", "bf16" or "f16"
+    out_kind: str                # Y
+    eps: float
+    dist_x: Dist
+    dist_g: Dist
+    seeds: tuple
+    notes: str = ""
+
+    def bytes(self) -> int:
+        isz = 4 if self.in_kind == "f32" else 2
+        osz = 4 if self.out_kind == "f32" else 2
+        return self.M * self.D * (isz + osz) + self.D * isz
+
+
+NORM_WORKLOADS = {
+    # the Phobos example's shape: f32 rows of D = 256, eps = 1e-6; a million rows (1 GiB each way)
+    "rms_norm": NormWorkload(
+        "rms_norm", 1 << 20, 256, "f32", "f32", 1e-6,
+        Dist("normal", 0.0, 1.0), Dist("uniform", 0.5, 1.5), (6001, 6002),
+        notes="f32 rows of 256, as in the page's rms_norm kernel"),
+    # the step before a projection in a transformer block: bf16 activations, D = 4096
+    "rms_norm_bf16": NormWorkload(
+        "rms_norm_bf16", 65536, 4096, "bf16", "bf16", 1e-6,
+        Dist("normal", 0.0, 1.0), Dist("uniform", 0.5, 1.5), (6101, 6102),
+        notes="bf16 rows of 4096 (512 MiB each way)"),
+}
+
+
+def make_norm_inputs(w: NormWorkload, rows=None):
+    """CPU tensors X [M, D] (or only the listed rows, drawn from the same stream) and G [D]."""
+    dt = torch_dtype(w.in_kind)
+    x = w.dist_x.sample((w.M, w.D), w.seeds[0], dt)
+    if rows is not None:
+        x = x[rows].contiguous()
+    return {"X": x, "G": w.dist_g.sample((w.D,), w.seeds[1], dt)}
+
+
 def make_inputs(w: Workload):
     """CPU tensors: dict with A [M,K], B [K,N] (N contiguous) or Wg/Wu, and C_in."""
     dt = torch_dtype(w.in_kind)
