@@ -14,6 +14,8 @@ Workloads (seeded synthetic inputs, see synth/):
   gate_up_swiglu  the same with silu(G) * U fused into the epilogue (one output)
   skinny      16 x 28672 x 8192 bf16 -> fp32 (HBM-bound; two B buffers rotate)
   square256, ragged
+  rms_norm       row normalisation of 2^20 f32 rows of 256 (HBM-bound)
+  rms_norm_bf16  row normalisation of 65536 bf16 rows of 4096 (HBM-bound)
 """
 import argparse
 import json
@@ -34,13 +36,23 @@ PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
 
-def kernel_source_hash():
-    """sha1 (first 16 hex) over the HIP sources; identifies the kernels the traffic figures belong to."""
+NORM_SOURCES = ("rms_norm.hip", "norm.hpp", "kernel_common.hpp", "launch.hpp")
+
+
+def kernel_source_hash(workload):
+    """sha1 (first 16 hex) over the HIP sources of the kernels a workload runs: the row
+    normalisation's own files, or every other kernel source for the GEMM workloads.
+    Identifies the kernels the traffic figures belong to."""
     import glob
     import hashlib
     csrc = os.path.join(ROOT, "layout_algebra_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp")))
+    if workload in synth.NORM_WORKLOADS:
+        files = [f for f in files if os.path.basename(f) in NORM_SOURCES]
+    else:
+        files = [f for f in files if os.path.basename(f) not in ("rms_norm.hip", "norm.hpp")]
     h = hashlib.sha1()
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+    for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
@@ -49,22 +61,17 @@ def kernel_source_hash():
 
 def measured_traffic(workload):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from profiles/traffic.md, or None when the
-    kernels changed since the counters were taken (or none were taken for this workload)."""
+    workload's kernels changed since the counters were taken (or none were taken for it)."""
     path = os.path.join(ROOT, "profiles", "traffic.md")
     if not os.path.exists(path):
         return None
-    recorded, table = None, {}
     with open(path) as f:
         for line in f:
-            line = line.strip()
-            if line.startswith("source_hash:"):
-                recorded = line.split(":", 1)[1].strip()
-            elif line.startswith("traffic "):
-                name, val = line[len("traffic "):].split(":")
-                table[name.strip()] = int(val)
-    if recorded != kernel_source_hash():
-        return None
-    return table.get(workload)
+            parts = line.split()
+            # "traffic <workload>: <bytes> <source hash>"
+            if len(parts) == 4 and parts[0] == "traffic" and parts[1] == workload + ":":
+                return int(parts[2]) if parts[3] == kernel_source_hash(workload) else None
+    return None
 
 
 def algorithmic_bytes(w):
@@ -84,7 +91,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS) + sorted(synth.NORM_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--b-kmajor", action="store_true",
@@ -98,6 +105,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (each output tile is "
               "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in synth.NORM_WORKLOADS:
+        return bench_norm(args, synth.NORM_WORKLOADS[args.workload])
 
     import layout_algebra_amd as la
     w = synth.WORKLOADS[args.workload]
@@ -218,6 +228,105 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit)
     print(json.dumps(line), flush=True)
+
+
+def timed_steps(step, steps, warmup):
+    """Warm-up, then `steps` back-to-back steps between two HIP events on the current stream
+    (synchronised on both sides); then up to 20 single steps each between its own event pair."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(min(steps, 20))]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(len(starts))]
+    for i in range(len(starts)):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return ms, wall, per_launch
+
+
+def bench_norm(args, w):
+    """Row normalisation: one launch per step over inputs resident in HBM."""
+    import layout_algebra_amd as la
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_norm_inputs(w)
+    X, G = inp["X"].to(dev), inp["G"].to(dev)
+    Y = torch.empty((w.M, w.D), dtype=synth.torch_dtype(w.out_kind), device=dev)
+
+    def step(i):
+        la.la_rms_norm_run(X, G, Y, w.eps)
+
+    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup)
+    if args.copy_probe:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    bytes_ = w.bytes()
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "achieved HBM GB/s, row normalisation %d x %d %s" % (w.M, w.D, w.in_kind),
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "D": w.D, "in": w.in_kind, "out": w.out_kind, "eps": w.eps},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
+                     "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["parity_sample"] = cpu_baseline_norm(w, inp, Y, args.cpu_seconds, gbs)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):
+    """Time the oracle (numpy, binary64) on the first R rows, R sized to about budget_s seconds,
+    and compare those rows of the GPU output with it."""
+    import oracle
+
+    def exact(t):
+        return t.double().numpy() if t.dtype == torch.float32 else oracle.decode(synth.bits(t), w.in_kind)
+
+    x, g = inp["X"], exact(inp["G"])
+    probe = min(w.M, 4096)
+    t0 = time.perf_counter()
+    oracle.rms_norm_f64(exact(x[:probe]), g, w.eps)
+    per_row = (time.perf_counter() - t0) / probe
+    R = int(max(probe, min(w.M, budget_s / max(per_row, 1e-12))))
+    reps = max(1, int(budget_s / max(per_row * R, 1e-9))) if R == w.M else 1
+    xs = exact(x[:R])
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ref, _ = oracle.rms_norm_f64(xs, g, w.eps)
+    dt = (time.perf_counter() - t0) / reps
+    isz = 4 if w.in_kind == "f32" else 2
+    osz = 4 if w.out_kind == "f32" else 2
+    value = (R * w.D * (isz + osz) + w.D * isz) / dt / 1e9
+    base = {"value": value, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "rows 0..%d of %d (D=%d), numpy binary64, %.2f s per run, %d run(s)" % (R - 1, w.M, w.D, dt, reps),
+            "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
+    got = Y[:R].to("cpu", torch.float64).numpy()
+    rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}[w.out_kind]
+    tol = ((w.D + 8) * 2.0 ** -24 + rel) * np.abs(ref) + (2.0 ** -25 if w.out_kind == "f16" else 0.0)
+    err = np.abs(got - ref)
+    return base, {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol))}
 
 
 def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):

@@ -124,6 +124,21 @@ gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate
 gemm_status gemm_gate_up_swiglu_run(gemm_plan_t plan, const void* X, const void* W_gate,
                                     const void* W_up, void* H, void* stream);
 
+/* Row normalisation, the kernel of the Phobos page "Tiles and shared memory"
+ * (section "A complete kernel"): for each row i < m,
+ *   inv[i] = 1 / sqrt((sum_j X[i,j]^2) / d + eps),   Y[i,j] = X[i,j] * inv[i] * G[j].
+ * X is [m, d] row-major with row stride ldx >= max(1, d), G is [d] (same type
+ * as X), Y is [m, d] with row stride ldy >= max(1, d); x_type, y_type are
+ * GEMM_F32, GEMM_BF16 or GEMM_F16 (device pointers, caller-owned, aligned to
+ * their element size; 16-byte aligned rows take the vector path).  The sum,
+ * the root and the scaling run in FP32 (squares summed with fused
+ * multiply-adds), Y is rounded once to nearest even.  eps must be finite and
+ * >= 0.  Y may be X itself (same ld, same element size: in place); any other
+ * overlap of Y with X or G is rejected.  m == 0 or d == 0 launches nothing;
+ * d <= 2^24.  Asynchronous on `stream`, allocates nothing. */
+gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type, const void* X,
+                            int64_t ldx, const void* G, void* Y, int64_t ldy, float eps, void* stream);
+
 /* JSON description of the plan (kernel, tile sizes, grid, LDS layouts and
  * swizzle, alignment class).  Writes at most len bytes including the NUL;
  * returns GEMM_ERR_RESOURCE if it did not fit. */

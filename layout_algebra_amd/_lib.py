@@ -12,7 +12,7 @@ FLAG_B_KMAJOR = 0x2
 
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
-    "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
+    "la_rms_norm_run", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "gemm_status_string", "gemm_last_error",
 )
@@ -60,6 +60,7 @@ def load():
         "gemm_run": ([vp, vp, vp, vp, f32, f32, vp], i32),
         "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
+        "la_rms_norm_run": ([i64, i64, i32, i32, vp, i64, vp, vp, i64, f32, vp], i32),
         "gemm_plan_describe": ([vp, ctypes.c_char_p, ctypes.c_size_t], i32),
         "gemm_plan_lds_offset": ([vp, i32, i64, i64, p64], i32),
         "gemm_plan_lds_stage_bytes": ([vp, p64], i32),
@@ -163,9 +164,6 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-_BATCH = {}
-
-
 def _check_matrix(t, name, rows, cols, ld, kind, batch=1, bstride=0):
     """2-D [rows, cols] tensor, or for batch > 1 a 3-D [batch, rows, cols] tensor with batch stride bstride."""
     torch = _torch()
@@ -221,6 +219,28 @@ def gemm_gate_up_swiglu_run(plan, X, W_gate, W_up, H, stream=None):
     _check_matrix(H, "H", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_gate_up_swiglu_run(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in (X, W_gate, W_up, H)],
                                           _stream_ptr(stream)))
+
+
+def la_rms_norm_run(X, G, Y, eps=1e-6, stream=None):
+    """Y = X * (1 / sqrt(mean(X^2 along a row) + eps)) * G for an [m, d] X (rows may be padded:
+    stride(0) >= d, stride(1) == 1), a contiguous [d] G of X's dtype and an [m, d] Y (may be X itself)."""
+    torch = _torch()
+    for name, t in (("X", X), ("G", G), ("Y", Y)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype not in _KIND:
+            raise ValueError("%s must be an f32/bf16/f16 tensor on the GPU" % name)
+    if X.dim() != 2 or Y.dim() != 2 or tuple(Y.shape) != tuple(X.shape):
+        raise ValueError("X and Y must be [m, d] tensors of the same shape, got %s and %s" % (tuple(X.shape), tuple(Y.shape)))
+    m, d = X.shape
+    if G.dim() != 1 or G.shape[0] != d or G.dtype != X.dtype or (d > 1 and G.stride(0) != 1):
+        raise ValueError("G must be a contiguous [%d] tensor of X's dtype" % d)
+    for name, t in (("X", X), ("Y", Y)):
+        if m > 0 and d > 0 and (t.stride(1) != 1 or (m > 1 and t.stride(0) < d)):
+            raise ValueError("%s rows must be contiguous with stride(0) >= d (strides %s)" % (name, t.stride()))
+    ldx = X.stride(0) if m > 1 else max(1, d)
+    ldy = Y.stride(0) if m > 1 else max(1, d)
+    _check(load().la_rms_norm_run(int(m), int(d), _KIND[X.dtype], _KIND[Y.dtype], ctypes.c_void_p(X.data_ptr()), int(ldx),
+                                  ctypes.c_void_p(G.data_ptr()), ctypes.c_void_p(Y.data_ptr()), int(ldy), float(eps),
+                                  _stream_ptr(stream)))
 
 
 def gemm_debug_lds_image(plan, A, B, B2, tile_m, tile_n, out, stream=None):

@@ -2,6 +2,7 @@
 // include/la_gemm.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -11,6 +12,7 @@
 #include "../../include/la_gemm.h"
 #include "launch.hpp"
 #include "layout.hpp"
+#include "norm.hpp"
 #include "planner.hpp"
 
 namespace {
@@ -151,6 +153,40 @@ gemm_status gemm_gate_up_swiglu_run(gemm_plan_t plan, const void* X, const void*
   a.beta = 0.0f;
   a.act = 1;
   return launch(p, a, stream, false);
+}
+
+gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type, const void* X, int64_t ldx,
+                            const void* G, void* Y, int64_t ldy, float eps, void* stream) {
+  auto kind = [](int32_t t) {
+    return t == GEMM_F32 ? lak::OUT_F32 : t == GEMM_BF16 ? lak::OUT_BF16 : t == GEMM_F16 ? lak::OUT_F16 : -1;
+  };
+  const int xk = kind(x_type), yk = kind(y_type);
+  if (xk < 0 || yk < 0) return set_err(GEMM_ERR_INVALID_ARG, "x_type and y_type must be GEMM_F32, GEMM_BF16 or GEMM_F16");
+  if (m < 0 || d < 0) return set_err(GEMM_ERR_INVALID_ARG, "m and d must be >= 0");
+  if (ldx < std::max<int64_t>(1, d) || ldy < std::max<int64_t>(1, d))
+    return set_err(GEMM_ERR_INVALID_ARG, "ldx and ldy must be >= max(1, d)");
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return set_err(GEMM_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (m > (int64_t{1} << 40) || d > (int64_t{1} << 24))
+    return set_err(GEMM_ERR_UNSUPPORTED, "d must be <= 2^24 (exact as FP32) and m <= 2^40");
+  if (m == 0 || d == 0) return GEMM_OK;
+  if (!X || !G || !Y) return set_err(GEMM_ERR_NULL, "X, G and Y must not be NULL");
+  const int xs = x_type == GEMM_F32 ? 4 : 2, ys = y_type == GEMM_F32 ? 4 : 2;
+  if (!aligned(X, xs) || !aligned(G, xs) || !aligned(Y, ys))
+    return set_err(GEMM_ERR_ALIGNMENT, "X, G and Y must be aligned to their element size");
+  // Byte ranges: Y may be X itself (same rows, same element size); no other overlap.
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), y0 = reinterpret_cast<uintptr_t>(Y);
+  const uintptr_t g0 = reinterpret_cast<uintptr_t>(G);
+  const uintptr_t x1 = x0 + uintptr_t(((m - 1) * ldx + d) * xs), y1 = y0 + uintptr_t(((m - 1) * ldy + d) * ys);
+  const uintptr_t g1 = g0 + uintptr_t(d * xs);
+  const bool in_place = x0 == y0 && ldx == ldy && xs == ys;
+  if (!in_place && x0 < y1 && y0 < x1) return set_err(GEMM_ERR_INVALID_ARG, "Y overlaps X without being X itself");
+  if (g0 < y1 && y0 < g1) return set_err(GEMM_ERR_INVALID_ARG, "Y overlaps G");
+  const int v = lak::rms_norm_vec_elems(xk);
+  const bool vec = aligned(X, 16) && aligned(G, 16) && aligned(Y, 16) && ldx % v == 0 && ldy % v == 0;
+  lak::NormArgs a{X, G, Y, m, d, ldx, ldy, eps};
+  const hipError_t e = lak::launch_rms_norm(a, xk, yk, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GEMM_OK;
 }
 
 gemm_status gemm_plan_describe(gemm_plan_t plan, char* buf, size_t len) {

@@ -63,3 +63,22 @@ def swiglu_bound(K, x, w_gate, w_up, g_ref, u_ref, h_ref, out_kind):
     with np.errstate(over="ignore"):
         silu = g_ref / (1.0 + np.exp(-g_ref))
     return 1.1 * np.abs(u_ref) * e_g + np.abs(silu) * e_u + (2.0 ** -20 + REL[out_kind]) * np.abs(h_ref)
+
+
+def exact_values(t):
+    """Exact float64 values of a CPU tensor of f32 / bf16 / f16 elements."""
+    if t.dtype == torch.float32:
+        return t.double().numpy()
+    return oracle.decode(synth.bits(t), "bf16" if t.dtype == torch.bfloat16 else "f16")
+
+
+def norm_bound(D, y_ref, out_kind):
+    """Agreement bound for the row normalisation: the FP32 sum of D squares is off
+    by at most (D-1) units of 2^-24 relatively (all terms are non-negative), the
+    divide, add, root and reciprocal by one unit each, the half-power of the root
+    halves the sum's share, and the two products add two units; 8 units cover the
+    fixed steps.  Then the output's own rounding, and for f16 outputs half its
+    smallest subnormal."""
+    r = np.abs(y_ref)
+    absolute = 2.0 ** -25 if out_kind == "f16" else 0.0
+    return (D + 8) * 2.0 ** -24 * r + REL[out_kind] * r + absolute

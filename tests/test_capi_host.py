@@ -187,3 +187,30 @@ def test_run_argument_errors_are_caught_before_launch():
     # tile index outside the grid for the debug image
     rc = lib.gemm_debug_lds_image(p.handle, vp(0x1000), vp(0x1000), vp(0), 5, 0, vp(0x1000), vp(0))
     assert la._lib.STATUS[rc] == "GEMM_ERR_INVALID_ARG"
+
+
+def test_rms_norm_argument_errors_are_caught_before_launch():
+    lib = la.load()
+    vp = ctypes.c_void_p
+    st = la._lib.STATUS
+
+    def call(m=8, d=256, xt=la.F32, yt=la.F32, X=0x10000, ldx=256, G=0x80000, Y=0x40000, ldy=256, eps=1e-6):
+        return st[lib.la_rms_norm_run(m, d, xt, yt, vp(X), ldx, vp(G), vp(Y), ldy, eps, vp(0))]
+
+    assert call(xt=7) == "GEMM_ERR_INVALID_ARG"
+    assert call(m=-1) == "GEMM_ERR_INVALID_ARG"
+    assert call(ldx=255) == "GEMM_ERR_INVALID_ARG"
+    assert call(ldy=0) == "GEMM_ERR_INVALID_ARG"
+    assert call(eps=-1.0) == "GEMM_ERR_INVALID_ARG"
+    assert call(eps=float("nan")) == "GEMM_ERR_INVALID_ARG"
+    assert call(eps=float("inf")) == "GEMM_ERR_INVALID_ARG"
+    assert call(d=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1) == "GEMM_ERR_UNSUPPORTED"
+    assert call(G=0) == "GEMM_ERR_NULL"
+    assert call(X=0x10002) == "GEMM_ERR_ALIGNMENT"                  # f32 X on a 2-byte boundary
+    assert call(Y=0x10000 + 1024) == "GEMM_ERR_INVALID_ARG"         # Y overlaps X, shifted by one row
+    assert call(Y=0x10000, ldy=512) == "GEMM_ERR_INVALID_ARG"       # same start, other rows
+    assert call(Y=0x10000, yt=la.BF16) == "GEMM_ERR_INVALID_ARG"    # same start, other element size
+    assert call(G=0x40000 + 64) == "GEMM_ERR_INVALID_ARG"           # Y overlaps G
+    # nothing to do: no launch, pointers never touched
+    assert call(m=0, X=0, G=0, Y=0) == "GEMM_OK"
+    assert call(d=0, ldx=1, ldy=1, X=0, G=0, Y=0) == "GEMM_OK"

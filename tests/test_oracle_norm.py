@@ -94,6 +94,7 @@ def _wrong(kind):
     return f
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
 @pytest.mark.parametrize("kind", ["sum", "d-1", "no-eps", "no-gain", "reversed-gain"])
 def test_planted_mistakes_fail(kind, monkeypatch):
     monkeypatch.setattr(oracle, "rms_norm_f64", _wrong(kind))
