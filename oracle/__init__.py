@@ -9,6 +9,7 @@ the seeded inputs the callers pass to both.
 * ``gemm_f64``  -- FP64 triple loop (C, OpenMP over rows), see ``gemm_f64.c``.
 * ``gate_up_swiglu_f64`` -- the gate/up products with the SwiGLU activation.
 * ``rms_norm_f64`` -- the row normalisation, numpy in binary64.
+* ``gemm_row_reduce_f64`` -- the GEMM with a sum / max / min of every output row.
 * ``layout_ref`` -- the layout algebra written out by enumeration in Python.
 """
 import ctypes
@@ -140,3 +141,25 @@ def rms_norm_f64(x, g, eps):
     inv = 1.0 / np.sqrt(ss / D + float(eps))
     y = x * inv[:, None] * g[None, :]
     return y, inv
+
+
+REDUCE_OPS = ("sum", "max", "min")
+
+
+def gemm_row_reduce_f64(a_bits, a_kind, b_bits, b_kind, op, alpha=1.0, beta=0.0, c=None, nthreads=0):
+    """out = alpha * A @ B + beta * C (the FP64 loop above) and, for every row i,
+    r[i] = sum, maximum or minimum over j of out[i, j], in binary64.
+
+    Reductions of a finished accumulator along its second axis (Tylo.jl "TMA and
+    Hopper WGMMA", section "WGMMA values and ownership": sum, maximum and
+    minimum along axis 2 of the finished fragment), taken here over whole
+    output rows.  Returns (out, r).
+    """
+    if op not in REDUCE_OPS:
+        raise ValueError("op must be one of %s, got %r" % (REDUCE_OPS, op))
+    out = gemm_f64(a_bits, a_kind, b_bits, b_kind, alpha, beta, c, nthreads)
+    if out.shape[1] == 0:
+        ident = {"sum": 0.0, "max": -np.inf, "min": np.inf}[op]
+        return out, np.full(out.shape[0], ident)
+    r = {"sum": np.sum, "max": np.max, "min": np.min}[op](out, axis=1)
+    return out, r
