@@ -108,6 +108,24 @@ void gemm_plan_destroy(gemm_plan_t plan);
 gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
                      float alpha, float beta, void* stream);
 
+/* Row reductions for gemm_run_reduce. */
+typedef enum { GEMM_REDUCE_SUM = 1, GEMM_REDUCE_MAX = 2, GEMM_REDUCE_MIN = 3 } gemm_reduce_op;
+
+/* gemm_run that also reduces every output row: R[b*m + i] = sum, maximum or
+ * minimum over j < n of out[i, j] of matrix b, where out is the FP32 value
+ * alpha * acc + beta * C_old before it is rounded to C's type -- the sum /
+ * maximum / minimum along the second axis of a finished accumulator of the
+ * Tylo.jl page "TMA and Hopper WGMMA" (section "WGMMA values and ownership"),
+ * taken over whole rows.  R is a device array of m * batch floats, written
+ * whole (n == 0 leaves the identity: 0, -inf, +inf).  Each workgroup folds
+ * its rows' partial results into R with atomics, so sums may differ in the
+ * last bits from run to run; maximum and minimum are exact (NaN outputs give
+ * an unspecified result).  A plan with GEMM_FLAG_GATE_UP is rejected.
+ * R must not overlap A, B or C.  Same stream, graph and error rules as
+ * gemm_run (a fill kernel prepares R on the stream first). */
+gemm_status gemm_run_reduce(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha,
+                            float beta, int32_t op, float* R, void* stream);
+
 /* G = X * W_gate and U = X * W_up (alpha = 1, beta = 0) in one launch that
  * stages each X tile once for both products.  Needs a plan made with
  * GEMM_FLAG_GATE_UP; X is [m, k] (lda), W_gate and W_up are [k, n] (ldb),

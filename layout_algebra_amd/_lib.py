@@ -11,7 +11,7 @@ FLAG_GATE_UP = 0x1
 FLAG_B_KMAJOR = 0x2
 
 EXPORTED_SYMBOLS = (
-    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
+    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
     "la_rms_norm_run", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "gemm_status_string", "gemm_last_error",
@@ -58,6 +58,7 @@ def load():
         "gemm_plan": ([ctypes.POINTER(_Desc), ctypes.POINTER(vp)], i32),
         "gemm_plan_destroy": ([vp], None),
         "gemm_run": ([vp, vp, vp, vp, f32, f32, vp], i32),
+        "gemm_run_reduce": ([vp, vp, vp, vp, f32, f32, i32, vp, vp], i32),
         "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
         "la_rms_norm_run": ([i64, i64, i32, i32, vp, i64, vp, vp, i64, f32, vp], i32),
@@ -196,6 +197,27 @@ def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
     _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_run(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                            ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), _stream_ptr(stream)))
+
+
+REDUCE_OPS = {"sum": 1, "max": 2, "min": 3}
+
+
+def gemm_run_reduce(plan, A, B, C, alpha=1.0, beta=0.0, op="sum", R=None, stream=None):
+    """gemm_run plus R[i] = op over j of the FP32 output row i (R: float32 [m], or [batch, m])."""
+    torch = _torch()
+    d = plan.desc
+    if op not in REDUCE_OPS:
+        raise ValueError("op must be one of %s" % sorted(REDUCE_OPS))
+    _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
+    _check_b(B, "B", d)
+    _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
+    want = (d.m,) if d.batch == 1 else (d.batch, d.m)
+    if not isinstance(R, torch.Tensor) or R.device.type != "cuda" or R.dtype != torch.float32 or \
+            tuple(R.shape) != want or not R.is_contiguous():
+        raise ValueError("R must be a contiguous float32 GPU tensor of shape %s" % (want,))
+    _check(load().gemm_run_reduce(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                                  ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), REDUCE_OPS[op],
+                                  ctypes.c_void_p(R.data_ptr()), _stream_ptr(stream)))
 
 
 def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):

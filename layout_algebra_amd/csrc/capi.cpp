@@ -108,6 +108,40 @@ gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, fl
   return launch(p, a, stream, false);
 }
 
+gemm_status gemm_run_reduce(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha, float beta,
+                            int32_t op, float* R, void* stream) {
+  if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");
+  const gemm_plan_s& p = *plan;
+  if (op != GEMM_REDUCE_SUM && op != GEMM_REDUCE_MAX && op != GEMM_REDUCE_MIN)
+    return set_err(GEMM_ERR_INVALID_ARG, "op must be GEMM_REDUCE_SUM, GEMM_REDUCE_MAX or GEMM_REDUCE_MIN");
+  if (p.gate_up) return set_err(GEMM_ERR_INVALID_ARG, "row reductions need a plan without GEMM_FLAG_GATE_UP");
+  if (p.d.m == 0) return GEMM_OK;
+  if (!R) return set_err(GEMM_ERR_NULL, "R is NULL");
+  if (!aligned(R, 4)) return set_err(GEMM_ERR_ALIGNMENT, "R must be 4-byte aligned");
+  const int red = op == GEMM_REDUCE_SUM ? lak::RED_SUM : op == GEMM_REDUCE_MAX ? lak::RED_MAX : lak::RED_MIN;
+  if (p.d.n > 0) {
+    // validate before anything is enqueued: on an error nothing runs and nothing is written
+    if (!C) return set_err(GEMM_ERR_NULL, "C is NULL");
+    if (p.d.k > 0 && (!A || !B)) return set_err(GEMM_ERR_NULL, "A or B is NULL");
+    if (!aligned(A, p.align_bytes) || !aligned(B, p.align_bytes))
+      return set_err(GEMM_ERR_ALIGNMENT, "A and B must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
+    if (!aligned(C, p.out_align_bytes))
+      return set_err(GEMM_ERR_ALIGNMENT, "C must be " + std::to_string(p.out_align_bytes) + "-byte aligned for this plan");
+  }
+  const hipError_t e = lak::launch_reduce_init(R, p.d.m * p.d.batch, red, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  if (p.d.n == 0) return GEMM_OK;     // empty rows: R holds the identity
+  lak::TiledArgs a = base_args(p);
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.C = C;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.red = red;
+  a.R = R;
+  return launch(p, a, stream, false);
+}
+
 gemm_status gemm_gate_up_run(gemm_plan_t plan, const void* X, const void* W_gate, const void* W_up, void* G, void* U,
                              void* stream) {
   if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");

@@ -253,7 +253,8 @@ __device__ __forceinline__ void block_barrier() {
 // finished before the first wave writes its window.
 template <class TO, class F>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, float alpha, float beta,
-                                           bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane) {
+                                           bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane,
+                                           int red = RED_NONE, float* R = nullptr) {
   constexpr int TN = F::TN;
   constexpr int PITCH = TN + 8;                      // floats: rows r and r+4 land 32 banks apart
   typedef typename TO::storage St;
@@ -290,6 +291,14 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], vo
           for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
         }
       }
+      if (red != RED_NONE) {
+        // row reduction: the lane's 8 values, then the CH lanes sharing row r
+        float p = v[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) p = red_combine(red, p, v[e]);
+        p = red_lanes<CH>(red, p);
+        if (lane % CH == 0) red_commit(red, R + row0 + i * 32 + r, p);
+      }
       if constexpr (sizeof(St) == 4) {
         *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -325,7 +334,8 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[NB][F::FM][F::FN], const 
   }
 #pragma unroll
   for (int t = 0; t < NB; ++t)
-    store_tile<TO, F>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0, col0, win, lane);
+    store_tile<TO, F>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0, col0, win, lane,
+                      NB == 1 ? g.red : RED_NONE, g.R);
 }
 
 // The same barrier without waiting for this wave's outstanding LDS reads, for

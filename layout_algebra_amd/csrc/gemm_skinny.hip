@@ -147,6 +147,10 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
   // 16x16 result lane map: register r of lane l is row 4 (l / 16) + r, column l % 16.
   typedef typename TO::storage St;
   St* Cp = static_cast<St*>(g.C);
+  const int red = g.red;
+  float part[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[r] = red_identity(red);
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int64_t col = n0 + wave * TN + j * 16 + (lane & 15);
@@ -158,7 +162,17 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
         float v = g.alpha * acc[j][r];
         if (g.beta != 0.0f) v += g.beta * from_out<TO>(Cp[idx]);
         Cp[idx] = to_out<TO>(v);
+        if (red != RED_NONE) part[r] = red_combine(red, part[r], v);
       }
+    }
+  }
+  if (red != RED_NONE) {
+    // the 16 lanes of a row group hold its 16 columns of each j block
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = red_lanes<16>(red, part[r]);
+      const int64_t row = 4 * (lane >> 4) + r;
+      if ((lane & 15) == 0 && row < g.M) red_commit(red, g.R + row, p);
     }
   }
 }

@@ -228,6 +228,14 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
   // Epilogue straight from the accumulator lane map.
   typedef typename TO::storage St;
   const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+  // row reduction: per-lane partials of the 16 rows of each 32-row block
+  // (columns j*32 + lc of the wave's sub-tile), then across the 32 lanes of each half
+  const int red = GU ? RED_NONE : g.red;
+  float part[T::FM][16];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[i][e] = red_identity(red);
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
@@ -252,9 +260,20 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
           float v = g.alpha * acc[0][i][j][e];
           if (g.beta != 0.0f) v += g.beta * from_out<TO>(C[idx]);
           C[idx] = to_out<TO>(v);
+          if (red != RED_NONE) part[i][e] = red_combine(red, part[i][e], v);
         }
       }
     }
+  }
+  if (red != RED_NONE) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = red_lanes<32>(red, part[i][e]);
+        const int64_t row = m0 + wm * T::TM + i * 32 + lr4 + 8 * (e >> 2) + (e & 3);
+        if (lc == 0 && row < g.M) red_commit(red, g.R + row, p);
+      }
   }
 }
 

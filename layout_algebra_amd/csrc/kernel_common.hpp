@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace lak {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -70,6 +72,34 @@ template <>
 __device__ __forceinline__ float from_out<OutBF16>(uint16_t v) { return static_cast<float>(__builtin_bit_cast(__bf16, v)); }
 template <>
 __device__ __forceinline__ float from_out<OutF16>(uint16_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, v)); }
+
+// Row reductions of the FP32 outputs (sum, maximum, minimum along a row);
+// the operation codes RED_* live in launch.hpp.
+
+__device__ __forceinline__ float red_identity(int op) {
+  return op == RED_SUM ? 0.0f : op == RED_MAX ? -__builtin_inff() : __builtin_inff();
+}
+__device__ __forceinline__ float red_combine(int op, float a, float b) {
+  return op == RED_SUM ? a + b : op == RED_MAX ? fmaxf(a, b) : fminf(a, b);
+}
+// Combine v over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of a group ends with the group's value.
+template <int W>
+__device__ __forceinline__ float red_lanes(int op, float v) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) v = red_combine(op, v, __shfl_xor(v, m, 64));
+  return v;
+}
+// Fold one partial into the row's result in global memory.
+__device__ __forceinline__ void red_commit(int op, float* p, float v) {
+  if (op == RED_SUM) {
+    atomicAdd(p, v);
+  } else if (op == RED_MAX) {
+    atomicMax(p, v);
+  } else {
+    atomicMin(p, v);
+  }
+}
 
 // SwiGLU combination of one gate and one up accumulator, in FP32:
 // silu(g) * u with silu(g) = g / (1 + e^-g).

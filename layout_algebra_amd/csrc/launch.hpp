@@ -6,6 +6,9 @@
 
 namespace lak {
 
+// Row-reduction operations of the GEMM epilogue.
+enum : int { RED_NONE = 0, RED_SUM = 1, RED_MAX = 2, RED_MIN = 3 };
+
 // Everything one launch needs; plain values only.
 struct TiledArgs {
   const uint16_t* A;     // [M, K] row-major, lda
@@ -16,6 +19,8 @@ struct TiledArgs {
   int64_t M, N, K, lda, ldb, ldc;
   float alpha, beta;
   int act;               // gate/up only: 0 = write G and U, 1 = write silu(G) * U to C
+  int red;               // row reduction of the FP32 outputs into R: RED_NONE, RED_SUM, RED_MAX, RED_MIN
+  float* R;              // [M] per matrix (batch entry z at R + z * M), prefilled with the identity of `red`
   int64_t sa, sb, sc;    // batched launches: element strides between consecutive A, B (and B2), C (and C2)
   int out_bytes;         // bytes per C element (for the C batch stride)
   int tiles_m, tiles_n, group_m;
@@ -32,6 +37,7 @@ __device__ __forceinline__ TiledArgs at_batch(const TiledArgs& g) {
   r.B2 = g.B2 ? g.B2 + z * g.sb : nullptr;
   r.C = g.C ? static_cast<void*>(static_cast<char*>(g.C) + z * g.sc * g.out_bytes) : nullptr;
   r.C2 = g.C2 ? static_cast<void*>(static_cast<char*>(g.C2) + z * g.sc * g.out_bytes) : nullptr;
+  r.R = g.R ? g.R + z * g.M : nullptr;
   return r;
 }
 
@@ -99,6 +105,10 @@ struct KernelShape {
   int full_tiles_only;     // 1: M % bm == 0, N % bn == 0, K % bk == 0 required
   int stages;
 };
+
+// Fill R[0, n) with the identity of `red` (0, -inf or +inf) on `stream`: a
+// kernel, not a memset, so that HIP graphs may capture it.
+hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
 
 // Static description of each kernel id; the planner validates these maps.
 KernelShape kernel_shape(int kid);
