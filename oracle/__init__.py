@@ -10,6 +10,7 @@ the seeded inputs the callers pass to both.
 * ``gate_up_swiglu_f64`` -- the gate/up products with the SwiGLU activation.
 * ``rms_norm_f64`` -- the row normalisation, numpy in binary64.
 * ``gemm_row_reduce_f64`` -- the GEMM with a sum / max / min of every output row.
+* ``attention_f64`` -- softmax attention, numpy in binary64.
 * ``layout_ref`` -- the layout algebra written out by enumeration in Python.
 """
 import ctypes
@@ -163,3 +164,26 @@ def gemm_row_reduce_f64(a_bits, a_kind, b_bits, b_kind, op, alpha=1.0, beta=0.0,
         return out, np.full(out.shape[0], ident)
     r = {"sum": np.sum, "max": np.max, "min": np.min}[op](out, axis=1)
     return out, r
+
+
+def attention_f64(q, k, v, scale):
+    """Softmax attention in binary64, the computation the Phobos page "Tiles and
+    shared memory" streams over key tiles (section "How long a tile lives": a
+    query tile, a running maximum and a running sum live through the key loop,
+    s = dot_t(q, k), and the accumulator is divided by the sum at the end):
+
+        s[i, j] = scale * sum_d q[i, d] k[j, d]
+        p[i, j] = exp(s[i, j] - max_j s[i, j])
+        o[i, :] = sum_j p[i, j] v[j, :] / sum_j p[i, j]
+
+    The whole row is formed at once (the exact value the streamed form reaches).
+    q: (..., Sq, D), k and v: (..., Sk, D) float64 values; returns o (..., Sq, D).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if k.shape[-2] == 0:
+        raise ValueError("attention over zero keys is undefined")
+    s = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
+    p = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return np.matmul(p, v) / np.sum(p, axis=-1, keepdims=True)
