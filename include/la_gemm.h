@@ -84,8 +84,10 @@ typedef struct {
                                   sides") */
   int64_t stride_a, stride_b, stride_c;  /* element strides between matrices, >= 0, read only when
                                   batch > 1; inputs may alias (0 broadcasts one matrix), outputs may
-                                  not: stride_c >= (m-1)*ldc + n.  They join lda/ldb/ldc in the
-                                  alignment class (16-byte vectors need multiples of 8) */
+                                  not: stride_c >= (m-1)*ldc + n (blocks), or stride_c >= n and
+                                  ldc >= (batch-1)*stride_c + n (interleaved rows).  They join
+                                  lda/ldb/ldc in the alignment class (16-byte vectors need
+                                  multiples of 8) */
 } gemm_desc;
 
 typedef struct gemm_plan_s* gemm_plan_t;   /* opaque, immutable, host-only */
@@ -156,6 +158,39 @@ gemm_status gemm_gate_up_swiglu_run(gemm_plan_t plan, const void* X, const void*
  * d <= 2^24.  Asynchronous on `stream`, allocates nothing. */
 gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type, const void* X,
                             int64_t ldx, const void* G, void* Y, int64_t ldy, float eps, void* stream);
+
+/* Softmax attention over a batch of (query, key, value) sets -- the
+ * computation the Phobos page "Tiles and shared memory" streams over key tiles
+ * (section "How long a tile lives": the query tile, its accumulator and the
+ * running maximum and sum live through the key loop) -- with the batch of
+ * matrices addressed by a third coordinate as on the Tylo.jl page "TMA and
+ * Hopper WGMMA" (section "The same storage contract on both sides"):
+ *   O[b,i,:] = sum_j p[b,i,j] V[b,j,:] / sum_j p[b,i,j],
+ *   p[b,i,j] = exp(scale * Q[b,i,:].K[b,j,:] - max_j(...)).
+ * Element (b, i, e) of X lives at X[b * stride_x + i * ld_x + e]. */
+typedef struct {
+  int64_t batch;               /* >= 0 */
+  int64_t sq, sk;              /* query and key counts; sk >= 1 unless batch * sq == 0 */
+  int64_t d;                   /* head dimension: 64 or 128 */
+  int32_t in_type;             /* GEMM_BF16 or GEMM_F16 (Q, K, V) */
+  int32_t out_type;            /* GEMM_F32, GEMM_BF16 or GEMM_F16 (O) */
+  int64_t ld_q, ld_k, ld_v, ld_o;                  /* row strides, >= d, multiples of 8 */
+  int64_t stride_q, stride_k, stride_v, stride_o;  /* batch strides, >= 0, multiples of 8; entries of O
+                                                      are disjoint blocks (stride_o >= (sq-1)*ld_o + d)
+                                                      or interleaved rows (stride_o >= d,
+                                                      ld_o >= (batch-1)*stride_o + d) */
+  float scale;                 /* finite; 1/sqrt(d) is the usual choice */
+} attn_desc;
+
+/* O for every batch entry and query, on `stream`.  Scores and the softmax run
+ * in FP32 (exp through exp2 with scale*log2(e) folded in), P is rounded to
+ * the input type for the product with V, the running sum uses the unrounded
+ * P, O is rounded once to out_type.  Q, K, V, O are device pointers, 16-byte
+ * aligned; O must not overlap Q, K or V, and batch entries of O must not
+ * overlap each other (see stride_o).  Row strides times 128 bytes must stay below 2^32.
+ * batch * sq == 0 launches nothing. */
+gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K, const void* V, void* O,
+                             void* stream);
 
 /* JSON description of the plan (kernel, tile sizes, grid, LDS layouts and
  * swizzle, alignment class).  Writes at most len bytes including the NUL;

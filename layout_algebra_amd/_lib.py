@@ -12,7 +12,7 @@ FLAG_B_KMAJOR = 0x2
 
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
-    "la_rms_norm_run", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
+    "la_rms_norm_run", "la_attention_run", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "gemm_status_string", "gemm_last_error",
 )
@@ -26,6 +26,14 @@ class GemmError(RuntimeError):
         super().__init__("%s: %s" % (STATUS.get(status, status), msg))
         self.status = status
         self.name = STATUS.get(status, str(status))
+
+
+class _AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("sq", ctypes.c_int64), ("sk", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("in_type", ctypes.c_int32), ("out_type", ctypes.c_int32),
+                ("ld_q", ctypes.c_int64), ("ld_k", ctypes.c_int64), ("ld_v", ctypes.c_int64), ("ld_o", ctypes.c_int64),
+                ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64), ("stride_v", ctypes.c_int64),
+                ("stride_o", ctypes.c_int64), ("scale", ctypes.c_float)]
 
 
 class _Desc(ctypes.Structure):
@@ -62,6 +70,7 @@ def load():
         "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
         "la_rms_norm_run": ([i64, i64, i32, i32, vp, i64, vp, vp, i64, f32, vp], i32),
+        "la_attention_run": ([ctypes.POINTER(_AttnDesc), vp, vp, vp, vp, vp], i32),
         "gemm_plan_describe": ([vp, ctypes.c_char_p, ctypes.c_size_t], i32),
         "gemm_plan_lds_offset": ([vp, i32, i64, i64, p64], i32),
         "gemm_plan_lds_stage_bytes": ([vp, p64], i32),
@@ -263,6 +272,39 @@ def la_rms_norm_run(X, G, Y, eps=1e-6, stream=None):
     _check(load().la_rms_norm_run(int(m), int(d), _KIND[X.dtype], _KIND[Y.dtype], ctypes.c_void_p(X.data_ptr()), int(ldx),
                                   ctypes.c_void_p(G.data_ptr()), ctypes.c_void_p(Y.data_ptr()), int(ldy), float(eps),
                                   _stream_ptr(stream)))
+
+
+def la_attention_run(Q, K, V, O, scale=None, stream=None):
+    """O = softmax(scale * Q K^T) V per batch entry.  Q [batch, sq, d], K and V [batch, sk, d], O [batch, sq, d]
+    (2-D tensors are one batch entry); rows may be padded (stride(-2) >= d, stride(-1) == 1).
+    scale defaults to 1/sqrt(d)."""
+    torch = _torch()
+    ts = {"Q": Q, "K": K, "V": V, "O": O}
+    for name, t in ts.items():
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype not in _KIND:
+            raise ValueError("%s must be a bf16/f16/f32 tensor on the GPU" % name)
+        if t.dim() not in (2, 3):
+            raise ValueError("%s must be [batch, seq, d] or [seq, d]" % name)
+    if not (Q.dim() == K.dim() == V.dim() == O.dim()):
+        raise ValueError("Q, K, V and O must all be 2-D or all 3-D")
+    v3 = {n: (t if t.dim() == 3 else t.unsqueeze(0)) for n, t in ts.items()}
+    b, sq, d = v3["Q"].shape
+    sk = v3["K"].shape[1]
+    if tuple(v3["K"].shape) != (b, sk, d) or tuple(v3["V"].shape) != (b, sk, d) or tuple(v3["O"].shape) != (b, sq, d):
+        raise ValueError("shapes: Q %s, K %s, V %s, O %s" % tuple(tuple(t.shape) for t in ts.values()))
+    if Q.dtype != K.dtype or Q.dtype != V.dtype or Q.dtype == torch.float32:
+        raise ValueError("Q, K and V must share one 16-bit dtype")
+    for n, t in v3.items():
+        if t.shape[1] > 0 and d > 0 and t.stride(2) != 1:
+            raise ValueError("%s rows must be contiguous (stride(-1) == 1)" % n)
+    ld = {n: (t.stride(1) if t.shape[1] > 1 else d) for n, t in v3.items()}
+    st = {n: (t.stride(0) if t.shape[0] > 1 else 0) for n, t in v3.items()}
+    desc = _AttnDesc(int(b), int(sq), int(sk), int(d), _KIND[Q.dtype], _KIND[O.dtype],
+                     int(ld["Q"]), int(ld["K"]), int(ld["V"]), int(ld["O"]),
+                     int(st["Q"]), int(st["K"]), int(st["V"]), int(st["O"]),
+                     float(scale if scale is not None else 1.0 / (d ** 0.5)))
+    _check(load().la_attention_run(ctypes.byref(desc), *[ctypes.c_void_p(t.data_ptr()) for t in (Q, K, V, O)],
+                                   _stream_ptr(stream)))
 
 
 def gemm_debug_lds_image(plan, A, B, B2, tile_m, tile_n, out, stream=None):

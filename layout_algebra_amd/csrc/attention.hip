@@ -1,0 +1,302 @@
+// Streaming softmax attention for gfx950, O = softmax(scale * Q K^T) V per
+// batch entry, the computation the Phobos page "Tiles and shared memory" uses
+// to illustrate tile lifetimes (section "How long a tile lives"): a query tile,
+// its accumulator and the running maximum and sum live through the whole key
+// loop; key and value tiles live for one iteration; the accumulator is divided
+// by the running sum at the end.
+//
+// MI355X mapping (one workgroup = 4 waves = 128 queries, 2 workgroups per CU):
+//  * Each wave owns 32 queries.  Their Q^T fragments stay in registers for the
+//    whole key loop (global -> registers once).
+//  * Key and value tiles of 64 rows are staged global -> LDS with direct loads
+//    (global_load_lds_dwordx4, 1 KB per wave instruction, swizzle applied on
+//    the source side as in the GEMM), two stages, one barrier per tile.
+//  * Scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16): in the
+//    32x32 result layout a lane holds 16 keys of ONE query, so the row maximum
+//    and sum are in-lane reductions plus one swap with the other half-wave,
+//    and the rescaling of the output accumulator (also kept transposed,
+//    O^T = V^T P^T) is a per-lane multiply.
+//  * P^T feeds the second product straight from registers: the key order of
+//    the 32x32 result layout is used as the MFMA k order, and the V^T
+//    fragments are read in that same key order with transposing LDS reads
+//    (ds_read_b64_tr_b16: 4 consecutive keys of one head-dimension column per
+//    lane), so no shuffle or LDS round trip is needed for P.
+//  * exp goes through exp2 with scale * log2(e) folded into the scores; the
+//    running sum uses the FP32 probabilities, the product with V their
+//    bf16/fp16 rounding (the MFMA input type).
+//  * Keys past the end of the sequence read the last valid key and value row
+//    (no out-of-bounds access) and get a score of -inf; queries past the end
+//    compute on zeros and are not stored.
+//  * Workgroups are numbered so that each XCD takes a contiguous run of
+//    (batch entry, query tile) pairs: the query tiles of one batch entry
+//    share its K and V through one L2.
+// LDS bank conflicts: K tiles use Swizzle{4,3,4} (D = 128) / {3,3,4} (D = 64)
+// for 16-byte fragment reads of 16 consecutive keys; V tiles use
+// Swizzle{2,5,2} for the transposing reads of 4 keys x 16 columns.
+#include "attention.hpp"
+#include "kernel_common.hpp"
+
+namespace lak {
+namespace {
+
+#define AT_LDS __attribute__((address_space(3)))
+typedef short i16x4_a __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct AttnCfg;
+template <>
+struct AttnCfg<128> {
+  static constexpr int KB = 4, KM = 3, KS = 4;
+  static constexpr int VB = 2, VM = 5, VS = 2;
+};
+template <>
+struct AttnCfg<64> {
+  static constexpr int KB = 3, KM = 3, KS = 4;
+  static constexpr int VB = 2, VM = 5, VS = 2;
+};
+
+constexpr int BR = 128, BC = 64, NW = 4, NTHREADS = NW * 64;
+
+// One direct load: 64 lanes x 16 bytes from base + voff (bytes) into the KB of
+// LDS at lds_addr (wave-uniform, through M0).  Inline assembly keeps the
+// compiler's wait-count pass from stalling later LDS reads on it; completion
+// is waited for explicitly before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const AT_LDS uint16_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ void barrier_after_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <class TI>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<InBF16>(float lo, float hi) {
+  return uint32_t(to_out<OutBF16>(lo)) | (uint32_t(to_out<OutBF16>(hi)) << 16);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<InF16>(float lo, float hi) {
+  return uint32_t(to_out<OutF16>(lo)) | (uint32_t(to_out<OutF16>(hi)) << 16);
+}
+
+template <class TO>
+__device__ __forceinline__ void store4(void* O, int64_t off, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<OutF32>(void* O, int64_t off, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(static_cast<float*>(O) + off) = f32x4{a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<OutBF16>(void* O, int64_t off, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(O) + off) = u32x2{pack2<InBF16>(a, b), pack2<InBF16>(c, d)};
+}
+template <>
+__device__ __forceinline__ void store4<OutF16>(void* O, int64_t off, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(O) + off) = u32x2{pack2<InF16>(a, b), pack2<InF16>(c, d)};
+}
+
+template <class TI, class TO, int D>
+__global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a) {
+  using Cfg = AttnCfg<D>;
+  constexpr int KE = BC * D;                   // elements of one K (or V) tile
+  constexpr int STAGE = 2 * KE;
+  constexpr int CHUNKS = KE / 512 / NW;        // 1 KB direct loads per wave per tile and operand
+  constexpr int DS = D / 16;                   // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;                   // 32-row blocks of O^T
+  static_assert(CHUNKS * 512 * NW == KE, "tile must split into whole KB per wave");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[2 * STAGE];
+  AT_LDS uint16_t* lds = (AT_LDS uint16_t*)lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c = lane & 31;
+  const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t z = id / a.q_tiles;
+  const int64_t q0 = int64_t(id % a.q_tiles) * BR + wave * 32;
+  const uint16_t* Qz = a.Q + z * a.bq;
+  const uint16_t* Kz = a.K + z * a.bk;
+  const uint16_t* Vz = a.V + z * a.bv;
+
+  // Q^T fragments of this wave's 32 queries: lane (c, h) holds query q0 + c,
+  // head-dimension elements 16 s + 8 h .. + 7 for every k-step s.
+  u32x4 qf[DS];
+  {
+    const int64_t q = q0 + c;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qf[s] = q < a.sq ? *reinterpret_cast<const u32x4*>(Qz + q * a.ldq + 16 * s + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Direct-load lane maps: the lane that fills physical element P of a tile
+  // fetches logical element Sw(P) = key * D + d.
+  int k_key[CHUNKS], k_d[CHUNKS], v_key[CHUNKS], v_d[CHUNKS];
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    const int P = (wave * CHUNKS + i) * 512 + lane * 8;
+    const int Lk = swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
+    const int Lv = swz<Cfg::VB, Cfg::VM, Cfg::VS>(P);
+    k_key[i] = Lk / D;
+    k_d[i] = Lk % D;
+    v_key[i] = Lv / D;
+    v_d[i] = Lv % D;
+  }
+  auto issue = [&](int t, int st) {
+    const int64_t kbase = int64_t(t) * BC;
+    const int64_t last = a.sk - 1 - kbase;     // rows past the end repeat the last key / value
+    const uint16_t* kb = Kz + kbase * a.ldk;
+    const uint16_t* vb = Vz + kbase * a.ldv;
+    AT_LDS uint16_t* dst = lds + st * STAGE + wave * CHUNKS * 512;
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int64_t r = k_key[i] < last ? k_key[i] : last;
+      dma16(kb, uint32_t((r * a.ldk + k_d[i]) * 2), lds_address(dst + i * 512));
+    }
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int64_t r = v_key[i] < last ? v_key[i] : last;
+      dma16(vb, uint32_t((r * a.ldv + v_d[i]) * 2), lds_address(dst + KE + i * 512));
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+  float m = -__builtin_inff(), l = 0.0f;
+
+  const int nt = int((a.sk + BC - 1) / BC);
+  issue(0, 0);
+  for (int t = 0; t < nt; ++t) {
+    barrier_after_loads();                     // tile t is in LDS; every wave is done with tile t - 1
+    if (t + 1 < nt) issue(t + 1, (t + 1) & 1);
+    const AT_LDS uint16_t* ks = lds + (t & 1) * STAGE;
+    const AT_LDS uint16_t* vs = ks + KE;
+
+    // S^T = K Q^T: two 32-key blocks x 32 queries.
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kf = *reinterpret_cast<const AT_LDS u32x4*>(ks + swz<Cfg::KB, Cfg::KM, Cfg::KS>((kb * 32 + c) * D + 16 * s + 8 * h));
+        sacc[kb] = mfma_32x32x16<TI>(kf, qf[s], sacc[kb]);
+      }
+    }
+
+    // Online softmax for query c: register r of block kb is key
+    // kb * 32 + 8 (r / 4) + 4 h + r % 4 of this tile; the other half-wave holds the rest.
+    const int64_t kbase = int64_t(t) * BC;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t key = kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float v = key < a.sk ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
+        sacc[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);          // finite: every tile holds at least one valid key
+    const float corr = __builtin_amdgcn_exp2f(m - m_new);
+    float sum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+        sacc[kb][r] = p;
+        sum += p;
+      }
+    sum += __shfl_xor(sum, 32, 64);
+    l = l * corr + sum;
+    m = m_new;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][r] *= corr;
+
+    // O^T += V^T P^T over four 16-key steps; slot e of the lane's 8 k values is
+    // key 16 u + 8 (e / 4) + 4 h + e % 4, the order of the score registers.
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x16& sp = sacc[u >> 1];
+      const int rr = (u & 1) * 8;
+      const u32x4 pf = u32x4{pack2<TI>(sp[rr + 0], sp[rr + 1]), pack2<TI>(sp[rr + 2], sp[rr + 3]),
+                             pack2<TI>(sp[rr + 4], sp[rr + 5]), pack2<TI>(sp[rr + 6], sp[rr + 7])};
+      const int vk = 16 * u + 4 * h + ((lane >> 2) & 3);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const int vd = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const i16x4_a lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (AT_LDS i16x4_a*)(vs + swz<Cfg::VB, Cfg::VM, Cfg::VS>(vk * D + vd)));
+        const i16x4_a hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (AT_LDS i16x4_a*)(vs + swz<Cfg::VB, Cfg::VM, Cfg::VS>((vk + 8) * D + vd)));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        acc[b] = mfma_32x32x16<TI>(u32x4{l2.x, l2.y, h2.x, h2.y}, pf, acc[b]);
+      }
+    }
+  }
+
+  // O[q, d] = acc / l: register r of block b is d = 32 b + 8 (r / 4) + 4 h + r % 4.
+  const int64_t q = q0 + c;
+  if (q < a.sq) {
+    const float inv = 1.0f / l;
+    const int64_t row = z * a.bo + q * a.ldo;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * b + 8 * g4 + 4 * h;
+        store4<TO>(a.O, row + d0, acc[b][4 * g4] * inv, acc[b][4 * g4 + 1] * inv, acc[b][4 * g4 + 2] * inv,
+                   acc[b][4 * g4 + 3] * inv);
+      }
+  }
+}
+
+template <class TI, class TO, int D>
+hipError_t go(const AttnArgs& a, hipStream_t s) {
+  const int64_t blocks = a.batch * a.q_tiles;
+  hipLaunchKernelGGL((attn_fwd_kernel<TI, TO, D>), dim3(static_cast<unsigned>(blocks)), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class TI, int D>
+hipError_t by_out(const AttnArgs& a, int out_kind, hipStream_t s) {
+  switch (out_kind) {
+    case OUT_F32: return go<TI, OutF32, D>(a, s);
+    case OUT_BF16: return go<TI, OutBF16, D>(a, s);
+    case OUT_F16: return go<TI, OutF16, D>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class TI>
+hipError_t by_d(const AttnArgs& a, int d, int out_kind, hipStream_t s) {
+  if (d == 128) return by_out<TI, 128>(a, out_kind, s);
+  if (d == 64) return by_out<TI, 64>(a, out_kind, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int d, int in_kind, int out_kind, hipStream_t stream) {
+  if (a.batch * a.q_tiles == 0) return hipSuccess;
+  return in_kind == IN_BF16 ? by_d<InBF16>(a, d, out_kind, stream) : by_d<InF16>(a, d, out_kind, stream);
+}
+
+}  // namespace lak

@@ -7,9 +7,11 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/la_gemm.h"
+#include "attention.hpp"
 #include "launch.hpp"
 #include "layout.hpp"
 #include "norm.hpp"
@@ -219,6 +221,67 @@ gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type
   const bool vec = aligned(X, 16) && aligned(G, 16) && aligned(Y, 16) && ldx % v == 0 && ldy % v == 0;
   lak::NormArgs a{X, G, Y, m, d, ldx, ldy, eps};
   const hipError_t e = lak::launch_rms_norm(a, xk, yk, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GEMM_OK;
+}
+
+gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K, const void* V, void* O,
+                             void* stream) {
+  if (!desc) return set_err(GEMM_ERR_NULL, "desc is NULL");
+  const attn_desc& d = *desc;
+  if (d.batch < 0 || d.sq < 0 || d.sk < 0) return set_err(GEMM_ERR_INVALID_ARG, "batch, sq and sk must be >= 0");
+  if (d.d != 64 && d.d != 128) return set_err(GEMM_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
+  if (d.in_type != GEMM_BF16 && d.in_type != GEMM_F16) return set_err(GEMM_ERR_INVALID_ARG, "in_type must be GEMM_BF16 or GEMM_F16");
+  if (d.out_type != GEMM_F32 && d.out_type != GEMM_BF16 && d.out_type != GEMM_F16)
+    return set_err(GEMM_ERR_INVALID_ARG, "out_type must be GEMM_F32, GEMM_BF16 or GEMM_F16");
+  if (!(d.scale == d.scale) || d.scale == __builtin_inff() || d.scale == -__builtin_inff())
+    return set_err(GEMM_ERR_INVALID_ARG, "scale must be finite");
+  const int64_t lds[4] = {d.ld_q, d.ld_k, d.ld_v, d.ld_o};
+  const int64_t strides[4] = {d.stride_q, d.stride_k, d.stride_v, d.stride_o};
+  for (int i = 0; i < 4; ++i) {
+    if (lds[i] < d.d || strides[i] < 0) return set_err(GEMM_ERR_INVALID_ARG, "row strides must be >= d and batch strides >= 0");
+    if (lds[i] % 8 || strides[i] % 8) return set_err(GEMM_ERR_ALIGNMENT, "row and batch strides must be multiples of 8 elements");
+  }
+  if (d.batch * d.sq == 0) return GEMM_OK;
+  if (d.sk == 0) return set_err(GEMM_ERR_INVALID_ARG, "attention over zero keys is undefined (sk must be >= 1)");
+  if (!Q || !K || !V || !O) return set_err(GEMM_ERR_NULL, "Q, K, V and O must not be NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return set_err(GEMM_ERR_ALIGNMENT, "Q, K, V and O must be 16-byte aligned");
+  if (128 * d.ld_k >= (int64_t{1} << 32) || 128 * d.ld_v >= (int64_t{1} << 32))
+    return set_err(GEMM_ERR_UNSUPPORTED, "K and V row strides must keep 64 rows below 4 GiB");
+  const int64_t q_tiles = (d.sq + 127) / 128;
+  if (d.batch > (int64_t{1} << 31) / q_tiles - 1) return set_err(GEMM_ERR_UNSUPPORTED, "too many query tiles");
+  const int osz = d.out_type == GEMM_F32 ? 4 : 2;
+  // batch entries of O: disjoint blocks, or rows interleaved with disjoint segments
+  const bool o_blocks = d.stride_o >= (d.sq - 1) * d.ld_o + d.d;
+  const bool o_interleaved = d.stride_o >= d.d && d.ld_o >= (d.batch - 1) * d.stride_o + d.d;
+  if (d.batch > 1 && !o_blocks && !o_interleaved)
+    return set_err(GEMM_ERR_INVALID_ARG, "batch entries of O overlap");
+  // O must not overlap any input (byte ranges of everything each pointer may touch)
+  auto span = [&](const void* p, int64_t stride, int64_t rows, int64_t ld, int esz) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return std::pair<uintptr_t, uintptr_t>(b, b + uintptr_t(((d.batch - 1) * stride + (rows - 1) * ld + d.d) * esz));
+  };
+  const auto o = span(O, d.stride_o, d.sq, d.ld_o, osz);
+  const std::pair<uintptr_t, uintptr_t> ins[3] = {span(Q, d.stride_q, d.sq, d.ld_q, 2), span(K, d.stride_k, d.sk, d.ld_k, 2),
+                                                  span(V, d.stride_v, d.sk, d.ld_v, 2)};
+  for (const auto& r : ins)
+    if (o.first < r.second && r.first < o.second) return set_err(GEMM_ERR_INVALID_ARG, "O overlaps Q, K or V");
+  lak::AttnArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.O = O;
+  a.batch = d.batch;
+  a.sq = d.sq;
+  a.sk = d.sk;
+  a.ldq = d.ld_q; a.ldk = d.ld_k; a.ldv = d.ld_v; a.ldo = d.ld_o;
+  a.bq = d.stride_q; a.bk = d.stride_k; a.bv = d.stride_v; a.bo = d.stride_o;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.q_tiles = static_cast<int>(q_tiles);
+  const hipError_t e = lak::launch_attention(a, static_cast<int>(d.d), d.in_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16,
+                                             d.out_type == GEMM_F32 ? lak::OUT_F32 : d.out_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16,
+                                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GEMM_OK;
 }

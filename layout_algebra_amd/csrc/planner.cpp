@@ -235,9 +235,15 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR)) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
   if (d.batch < 1 || d.batch > 65535) { fail(err, "batch must be in 1..65535"); return GEMM_ERR_INVALID_ARG; }
   if (d.stride_a < 0 || d.stride_b < 0 || d.stride_c < 0) { fail(err, "batch strides must be >= 0"); return GEMM_ERR_INVALID_ARG; }
-  if (d.batch > 1 && d.m > 0 && d.n > 0 && __int128(d.stride_c) < __int128(d.m - 1) * d.ldc + d.n) {
-    fail(err, "batched outputs would overlap: stride_c must be >= (m-1)*ldc + n");
-    return GEMM_ERR_INVALID_ARG;
+  if (d.batch > 1 && d.m > 0 && d.n > 0) {
+    // disjoint blocks, or rows of the matrices interleaved with disjoint segments
+    const bool blocks = __int128(d.stride_c) >= __int128(d.m - 1) * d.ldc + d.n;
+    const bool interleaved = d.stride_c >= d.n && __int128(d.ldc) >= __int128(d.batch - 1) * d.stride_c + d.n;
+    if (!blocks && !interleaved) {
+      fail(err, "batched outputs would overlap: use stride_c >= (m-1)*ldc + n, or interleaved rows with "
+                "stride_c >= n and ldc >= (batch-1)*stride_c + n");
+      return GEMM_ERR_INVALID_ARG;
+    }
   }
   if (d.a_type != d.b_type || d.a_type == GEMM_F32) {
     fail(err, "A and B must both be bf16 or both be f16");

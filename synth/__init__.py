@@ -133,6 +133,44 @@ def make_norm_inputs(w: NormWorkload, rows=None):
     return {"X": x, "G": w.dist_g.sample((w.D,), w.seeds[1], dt)}
 
 
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Softmax attention over `batch` independent (query, key, value) sets."""
+    name: str
+    batch: int
+    sq: int
+    sk: int
+    d: int
+    in_kind: str                 # Q, K, V: "bf16" or "f16"
+    out_kind: str                # O
+    dist: Dist                   # entries of Q, K and V
+    seeds: tuple                 # Q, K, V
+    notes: str = ""
+
+    def flops(self) -> float:
+        return 4.0 * self.batch * self.sq * self.sk * self.d
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+ATTN_WORKLOADS = {
+    # a transformer prefill: 4 sequences x 16 heads, 4096 tokens, head dimension 128
+    "attention": AttnWorkload(
+        "attention", 64, 4096, 4096, 128, "bf16", "bf16", Dist("normal", 0.0, 1.0), (7001, 7002, 7003),
+        notes="64 (batch x head) entries, 4096 queries and keys, d = 128, scale 1/sqrt(d)"),
+}
+
+
+def make_attn_inputs(w: AttnWorkload):
+    """CPU tensors Q [batch, sq, d], K and V [batch, sk, d]."""
+    dt = torch_dtype(w.in_kind)
+    return {"Q": w.dist.sample((w.batch, w.sq, w.d), w.seeds[0], dt),
+            "K": w.dist.sample((w.batch, w.sk, w.d), w.seeds[1], dt),
+            "V": w.dist.sample((w.batch, w.sk, w.d), w.seeds[2], dt)}
+
+
 def make_inputs(w: Workload):
     """CPU tensors: dict with A [M,K], B [K,N] (N contiguous) or Wg/Wu, and C_in."""
     dt = torch_dtype(w.in_kind)

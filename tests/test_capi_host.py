@@ -214,3 +214,36 @@ def test_rms_norm_argument_errors_are_caught_before_launch():
     # nothing to do: no launch, pointers never touched
     assert call(m=0, X=0, G=0, Y=0) == "GEMM_OK"
     assert call(d=0, ldx=1, ldy=1, X=0, G=0, Y=0) == "GEMM_OK"
+
+
+def test_attention_argument_errors_are_caught_before_launch():
+    lib = la.load()
+    vp = ctypes.c_void_p
+    st = la._lib.STATUS
+
+    def call(**kw):
+        f = dict(batch=2, sq=256, sk=300, d=128, in_type=la.BF16, out_type=la.BF16, ld_q=128, ld_k=128, ld_v=128,
+                 ld_o=128, stride_q=256 * 128, stride_k=300 * 128, stride_v=300 * 128, stride_o=256 * 128, scale=0.088)
+        ptrs = dict(Q=0x1000000, K=0x2000000, V=0x3000000, O=0x4000000)
+        for k in list(kw):
+            if k in ptrs:
+                ptrs[k] = kw.pop(k)
+        f.update(kw)
+        desc = la._lib._AttnDesc(*[f[n] for n, _ in la._lib._AttnDesc._fields_])
+        return st[lib.la_attention_run(ctypes.byref(desc), vp(ptrs["Q"]), vp(ptrs["K"]), vp(ptrs["V"]), vp(ptrs["O"]),
+                                       vp(0))]
+
+    assert call(d=96) == "GEMM_ERR_UNSUPPORTED"
+    assert call(in_type=la.F32) == "GEMM_ERR_INVALID_ARG"
+    assert call(out_type=9) == "GEMM_ERR_INVALID_ARG"
+    assert call(scale=float("nan")) == "GEMM_ERR_INVALID_ARG"
+    assert call(ld_k=100) == "GEMM_ERR_INVALID_ARG"
+    assert call(ld_k=132) == "GEMM_ERR_ALIGNMENT"
+    assert call(sk=0) == "GEMM_ERR_INVALID_ARG"
+    assert call(V=0) == "GEMM_ERR_NULL"
+    assert call(Q=0x1000008) == "GEMM_ERR_ALIGNMENT"
+    assert call(stride_o=128) == "GEMM_ERR_INVALID_ARG"            # batch entries of O overlap
+    assert call(O=0x3000000 + 4096) == "GEMM_ERR_INVALID_ARG"      # O overlaps V
+    assert call(ld_k=1 << 25, stride_k=0) == "GEMM_ERR_UNSUPPORTED"
+    assert call(batch=0, Q=0, K=0, V=0, O=0) == "GEMM_OK"            # nothing to do, nothing touched
+    assert call(sq=0, sk=0, Q=0, K=0, V=0, O=0) == "GEMM_OK"
