@@ -16,6 +16,7 @@ Workloads (seeded synthetic inputs, see synth/):
   square256, ragged
   rms_norm       row normalisation of 2^20 f32 rows of 256 (HBM-bound)
   rms_norm_bf16  row normalisation of 65536 bf16 rows of 4096 (HBM-bound)
+  attention      softmax attention, 64 entries x 4096 queries x 4096 keys, d = 128, bf16
 """
 import argparse
 import json
@@ -37,6 +38,8 @@ METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
 
 NORM_SOURCES = ("rms_norm.hip", "norm.hpp", "kernel_common.hpp", "launch.hpp")
+ATTN_SOURCES = ("attention.hip", "attention.hpp", "kernel_common.hpp", "launch.hpp")
+OWN_SOURCES = ("rms_norm.hip", "norm.hpp", "attention.hip", "attention.hpp")
 
 
 def kernel_source_hash(workload):
@@ -49,8 +52,10 @@ def kernel_source_hash(workload):
     files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp")))
     if workload in synth.NORM_WORKLOADS:
         files = [f for f in files if os.path.basename(f) in NORM_SOURCES]
+    elif workload in synth.ATTN_WORKLOADS:
+        files = [f for f in files if os.path.basename(f) in ATTN_SOURCES]
     else:
-        files = [f for f in files if os.path.basename(f) not in ("rms_norm.hip", "norm.hpp")]
+        files = [f for f in files if os.path.basename(f) not in OWN_SOURCES]
     h = hashlib.sha1()
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -91,7 +96,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS) + sorted(synth.NORM_WORKLOADS))
+    ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS) + sorted(synth.NORM_WORKLOADS) + sorted(synth.ATTN_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--b-kmajor", action="store_true",
@@ -108,6 +113,8 @@ def main():
 
     if args.workload in synth.NORM_WORKLOADS:
         return bench_norm(args, synth.NORM_WORKLOADS[args.workload])
+    if args.workload in synth.ATTN_WORKLOADS:
+        return bench_attention(args, synth.ATTN_WORKLOADS[args.workload])
 
     import layout_algebra_amd as la
     w = synth.WORKLOADS[args.workload]
@@ -294,6 +301,82 @@ def bench_norm(args, w):
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline_norm(w, inp, Y, args.cpu_seconds, gbs)
     print(json.dumps(line), flush=True)
+
+
+def bench_attention(args, w):
+    """Softmax attention: one launch per step over Q, K, V resident in HBM."""
+    import layout_algebra_amd as la
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = synth.make_attn_inputs(w)
+    Q, K, V = x["Q"].to(dev), x["K"].to(dev), x["V"].to(dev)
+    O = torch.empty((w.batch, w.sq, w.d), dtype=synth.torch_dtype(w.out_kind), device=dev)
+
+    def step(i):
+        la.la_attention_run(Q, K, V, O, w.scale)
+
+    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "TFLOP/s, softmax attention %d x %d x %d, d=%d" % (w.batch, w.sq, w.sk, w.d),
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
+        "dtype": w.in_kind, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "sq": w.sq, "sk": w.sk, "d": w.d, "in": w.in_kind,
+                   "out": w.out_kind, "scale": w.scale},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[w.in_kind], "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_TFLOPS[w.in_kind], "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
+                     "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["parity_sample"] = cpu_baseline_attention(w, x, O, args.cpu_seconds, tflops)
+    print(json.dumps(line), flush=True)
+
+
+def blas_threads():
+    """Threads numpy's BLAS runs its matrix products on."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def cpu_baseline_attention(w, x, O, budget_s, gpu_value):
+    """Time the oracle (numpy, binary64) on the first R queries of batch entry 0 (all keys),
+    R sized to about budget_s seconds, and compare those GPU output rows with it."""
+    import oracle
+
+    def exact(t):
+        return oracle.decode(synth.bits(t), w.in_kind)
+
+    k, v = exact(x["K"][0]), exact(x["V"][0])
+    probe = min(w.sq, 64)
+    t0 = time.perf_counter()
+    oracle.attention_f64(exact(x["Q"][0, :probe]), k, v, w.scale)
+    per_row = (time.perf_counter() - t0) / probe
+    R = int(max(probe, min(w.sq, budget_s / max(per_row, 1e-12))))
+    q = exact(x["Q"][0, :R])
+    t0 = time.perf_counter()
+    ref = oracle.attention_f64(q, k, v, w.scale)
+    dt = time.perf_counter() - t0
+    value = 4.0 * R * w.sk * w.d / dt / 1e12
+    base = {"value": value, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": "queries 0..%d of batch entry 0 against all %d keys, numpy binary64 (BLAS matmul), %.2f s"
+                      % (R - 1, w.sk, dt),
+            "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
+    got = O[0, :R].to("cpu", torch.float64).numpy()
+    delta = w.scale * 2.0 ** -20 * w.d * float(x["Q"].abs().max()) * float(x["K"].abs().max())
+    in_rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}[w.in_kind]
+    out_rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}[w.out_kind]
+    tol = (in_rel + 4.0 * delta + 2.0 ** -20) * float(x["V"][0].abs().max()) + out_rel * np.abs(ref)
+    err = np.abs(got - ref)
+    return base, {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol))}
 
 
 def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):

@@ -179,7 +179,7 @@ typedef struct {
                                                       are disjoint blocks (stride_o >= (sq-1)*ld_o + d)
                                                       or interleaved rows (stride_o >= d,
                                                       ld_o >= (batch-1)*stride_o + d) */
-  float scale;                 /* finite; 1/sqrt(d) is the usual choice */
+  float scale;                 /* finite, >= 0; 1/sqrt(d) is the usual choice */
 } attn_desc;
 
 /* O for every batch entry and query, on `stream`.  Scores and the softmax run

@@ -21,12 +21,16 @@
 //    fragments are read in that same key order with transposing LDS reads
 //    (ds_read_b64_tr_b16: 4 consecutive keys of one head-dimension column per
 //    lane), so no shuffle or LDS round trip is needed for P.
-//  * exp goes through exp2 with scale * log2(e) folded into the scores; the
-//    running sum uses the FP32 probabilities, the product with V their
-//    bf16/fp16 rounding (the MFMA input type).
+//  * exp goes through exp2 with scale * log2(e) folded into one fused
+//    multiply-add per score (scale >= 0); the running sum uses the FP32
+//    probabilities, the product with V their bf16/fp16 rounding (the MFMA
+//    input type).  The reference maximum is updated lazily (only when a tile
+//    exceeds it by more than 8 in log2 units, a factor 256), which skips the
+//    rescaling of the output accumulator on most tiles; the result acc / sum
+//    does not depend on the reference.
 //  * Keys past the end of the sequence read the last valid key and value row
-//    (no out-of-bounds access) and get a score of -inf; queries past the end
-//    compute on zeros and are not stored.
+//    (no out-of-bounds access), are left out of the maximum and get
+//    probability 0; queries past the end compute on zeros and are not stored.
 //  * Workgroups are numbered so that each XCD takes a contiguous run of
 //    (batch entry, query tile) pairs: the query tiles of one batch entry
 //    share its K and V through one L2.
@@ -83,15 +87,19 @@ __device__ __forceinline__ void barrier_after_loads() {
   asm volatile("" ::: "memory");
 }
 
+typedef __bf16 bf16x2_a __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_a __attribute__((ext_vector_type(2)));
+
+// Two FP32 values rounded to nearest even and packed (one conversion instruction for bf16).
 template <class TI>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi);
 template <>
 __device__ __forceinline__ uint32_t pack2<InBF16>(float lo, float hi) {
-  return uint32_t(to_out<OutBF16>(lo)) | (uint32_t(to_out<OutBF16>(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, bf16x2_a{static_cast<__bf16>(lo), static_cast<__bf16>(hi)});
 }
 template <>
 __device__ __forceinline__ uint32_t pack2<InF16>(float lo, float hi) {
-  return uint32_t(to_out<OutF16>(lo)) | (uint32_t(to_out<OutF16>(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, f16x2_a{static_cast<_Float16>(lo), static_cast<_Float16>(hi)});
 }
 
 template <class TO>
@@ -199,36 +207,55 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
 
     // Online softmax for query c: register r of block kb is key
     // kb * 32 + 8 (r / 4) + 4 h + r % 4 of this tile; the other half-wave holds the rest.
-    const int64_t kbase = int64_t(t) * BC;
+    // Scores stay raw; with c = scale * log2(e) >= 0, max(c s) = c max(s) and
+    // p = exp2(c s - m) is one fused multiply-add and one exp2 per score.
+    const int rem = a.sk - int64_t(t) * BC < BC ? int(a.sk - int64_t(t) * BC) : BC;   // valid keys in the tile
     float mx = -__builtin_inff();
+    if (rem == BC) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float v = key < a.sk ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
-        sacc[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          mx = key < rem ? fmaxf(mx, sacc[kb][r]) : mx;
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);          // finite: every tile holds at least one valid key
-    const float corr = __builtin_amdgcn_exp2f(m - m_new);
+    // Lazy reference maximum (log2 units): it moves only when the tile's maximum
+    // exceeds it by more than 8, so probabilities stay <= 2^8 and the rescaling
+    // of the accumulator and the running sum is skipped for most tiles; the
+    // quotient acc / l does not depend on the reference.
+    const float m_tile = mx * a.scale_log2;
+    if (__any(m_tile > m + 8.0f)) {
+      const float m_new = m_tile > m + 8.0f ? m_tile : m;
+      const float corr = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile (m = -inf)
+      l *= corr;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] *= corr;
+      m = m_new;
+    }
     float sum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -m));
+        if (rem != BC) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          p = key < rem ? p : 0.0f;
+        }
         sacc[kb][r] = p;
         sum += p;
       }
     sum += __shfl_xor(sum, 32, 64);
-    l = l * corr + sum;
-    m = m_new;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[b][r] *= corr;
+    l += sum;
 
     // O^T += V^T P^T over four 16-key steps; slot e of the lane's 8 k values is
     // key 16 u + 8 (e / 4) + 4 h + e % 4, the order of the score registers.

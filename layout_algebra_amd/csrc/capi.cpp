@@ -236,6 +236,7 @@ gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K
     return set_err(GEMM_ERR_INVALID_ARG, "out_type must be GEMM_F32, GEMM_BF16 or GEMM_F16");
   if (!(d.scale == d.scale) || d.scale == __builtin_inff() || d.scale == -__builtin_inff())
     return set_err(GEMM_ERR_INVALID_ARG, "scale must be finite");
+  if (d.scale < 0.0f) return set_err(GEMM_ERR_UNSUPPORTED, "scale must be >= 0");
   const int64_t lds[4] = {d.ld_q, d.ld_k, d.ld_v, d.ld_o};
   const int64_t strides[4] = {d.stride_q, d.stride_k, d.stride_v, d.stride_o};
   for (int i = 0; i < 4; ++i) {
