@@ -193,12 +193,7 @@ def main():
     per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
     if args.copy_probe:
-        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(dev)
 
     flops = w.flops()
     value_tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -235,6 +230,17 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit)
     print(json.dumps(line), flush=True)
+
+
+def copy_probe(dev):
+    """A plain elementwise copy of 256 MiB (reads 256 MiB, writes 256 MiB), three times: the
+    reference dispatch for scaling HBM byte counters."""
+    src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def timed_steps(step, steps, warmup):
@@ -279,12 +285,7 @@ def bench_norm(args, w):
 
     ms, wall, per_launch = timed_steps(step, args.steps, args.warmup)
     if args.copy_probe:
-        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(dev)
     bytes_ = w.bytes()
     gbs = bytes_ / (ms * 1e-3) / 1e9
     line = {
@@ -316,6 +317,8 @@ def bench_attention(args, w):
         la.la_attention_run(Q, K, V, O, w.scale)
 
     ms, wall, per_launch = timed_steps(step, args.steps, args.warmup)
+    if args.copy_probe:
+        copy_probe(dev)
     tflops = w.flops() / (ms * 1e-3) / 1e12
     line = {
         "metric": "TFLOP/s, softmax attention %d x %d x %d, d=%d" % (w.batch, w.sq, w.sk, w.d),

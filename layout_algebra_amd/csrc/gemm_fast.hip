@@ -11,6 +11,13 @@ hipError_t go_fast(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
     hipLaunchKernelGGL((gemm_fast_lds_image<TI, TO, C>),
                        dim3(1), dim3(NT), 0, s, a);
   } else {
+    if constexpr (C::NB == 1) {
+      // row reductions (single-output plans only) run their own instantiation
+      if (a.red != RED_NONE) {
+        hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, true>), grid, dim3(NT), 0, s, a);
+        return hipGetLastError();
+      }
+    }
     if constexpr (C::SCHED == 2) {
       hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
     } else if constexpr (C::SCHED == 3) {

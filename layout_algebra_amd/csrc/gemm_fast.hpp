@@ -251,7 +251,9 @@ __device__ __forceinline__ void block_barrier() {
 // and register.  beta * C_old is added on the way out, reading C_old with the
 // same vectors (only when beta != 0).  All LDS reads of the main loop must be
 // finished before the first wave writes its window.
-template <class TO, class F>
+// RED: also fold the row reduction `red` of the FP32 values into R (a separate
+// instantiation, so that launches without it run exactly the plain epilogue).
+template <class TO, class F, bool RED = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, float alpha, float beta,
                                            bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane,
                                            int red = RED_NONE, float* R = nullptr) {
@@ -291,7 +293,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], vo
           for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
         }
       }
-      if (red != RED_NONE) {
+      if constexpr (RED) {
         // row reduction: the lane's 8 values, then the CH lanes sharing row r
         float p = v[0];
 #pragma unroll
@@ -313,7 +315,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], vo
   }
 }
 
-template <class TO, class F, int NB>
+template <class TO, class F, int NB, bool RED = false>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[NB][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
                                          int wm, int wn, int wave, int lane, LAK_LDS uint16_t* lds) {
   static_assert(F::NW * 32 * (F::TN + 8) * 4 <= F::STAGES * F::STAGE * 2, "epilogue windows must fit in the stage buffers");
@@ -334,8 +336,8 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[NB][F::FM][F::FN], const 
   }
 #pragma unroll
   for (int t = 0; t < NB; ++t)
-    store_tile<TO, F>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0, col0, win, lane,
-                      NB == 1 ? g.red : RED_NONE, g.R);
+    store_tile<TO, F, RED && NB == 1>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0,
+                                      col0, win, lane, g.red, g.R);
 }
 
 // The same barrier without waiting for this wave's outstanding LDS reads, for
@@ -346,7 +348,7 @@ __device__ __forceinline__ void block_barrier_nowait() {
   asm volatile("" ::: "memory");
 }
 
-template <class TI, class TO, class C>
+template <class TI, class TO, class C, bool RED = false>
 __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
@@ -407,7 +409,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const Til
   }
 
   block_barrier();                         // every wave is done with the stage buffers
-  epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
+  epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each
@@ -440,7 +442,7 @@ __device__ __forceinline__ void wait_block(int kt, int nk) {
   }
 }
 
-template <class TI, class TO, class C>
+template <class TI, class TO, class C, bool RED = false>
 __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
@@ -519,7 +521,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
 
   // After the last phase barrier every M phase (all LDS reads) is complete,
   // so the waves may reuse the stage buffers as epilogue windows.
-  epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
+  epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 
 // Software-pipelined schedule.  Every wave keeps two fragment sets of one
@@ -550,7 +552,7 @@ __device__ __forceinline__ void sp_substep(const LAK_LDS uint16_t* next_stage, i
   if constexpr (F::SCHED_HINTS) F::interleave();
 }
 
-template <class TI, class TO, class C>
+template <class TI, class TO, class C, bool RED = false>
 __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
@@ -629,7 +631,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const 
   }
 
   block_barrier();                         // every wave is done with the stage buffers
-  epilogue<TO, F, NB>(acc, g, m0, n0, wm, wn, wave, lane, lds);
+  epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 
 // Debug: K block 0 of tile (dbg_tm, dbg_tn) staged by the kernel's own code, then copied out.
