@@ -202,8 +202,8 @@ gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type
   if (ldx < std::max<int64_t>(1, d) || ldy < std::max<int64_t>(1, d))
     return set_err(GEMM_ERR_INVALID_ARG, "ldx and ldy must be >= max(1, d)");
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return set_err(GEMM_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (m > (int64_t{1} << 40) || d > (int64_t{1} << 24))
-    return set_err(GEMM_ERR_UNSUPPORTED, "d must be <= 2^24 (exact as FP32) and m <= 2^40");
+  if (m > (int64_t{1} << 40) || d > (int64_t{1} << 24) || ldx > (int64_t{1} << 40) || ldy > (int64_t{1} << 40))
+    return set_err(GEMM_ERR_UNSUPPORTED, "d must be <= 2^24 (exact as FP32), m, ldx and ldy <= 2^40");
   if (m == 0 || d == 0) return GEMM_OK;
   if (!X || !G || !Y) return set_err(GEMM_ERR_NULL, "X, G and Y must not be NULL");
   const int xs = x_type == GEMM_F32 ? 4 : 2, ys = y_type == GEMM_F32 ? 4 : 2;
@@ -212,7 +212,9 @@ gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type
   // Byte ranges: Y may be X itself (same rows, same element size); no other overlap.
   const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), y0 = reinterpret_cast<uintptr_t>(Y);
   const uintptr_t g0 = reinterpret_cast<uintptr_t>(G);
-  const uintptr_t x1 = x0 + uintptr_t(((m - 1) * ldx + d) * xs), y1 = y0 + uintptr_t(((m - 1) * ldy + d) * ys);
+  const __int128 xb = (__int128(m - 1) * ldx + d) * xs, yb = (__int128(m - 1) * ldy + d) * ys;
+  if (xb > (__int128(1) << 56) || yb > (__int128(1) << 56)) return set_err(GEMM_ERR_UNSUPPORTED, "X or Y spans more than 2^56 bytes");
+  const uintptr_t x1 = x0 + uintptr_t(xb), y1 = y0 + uintptr_t(yb);
   const uintptr_t g1 = g0 + uintptr_t(d * xs);
   const bool in_place = x0 == y0 && ldx == ldy && xs == ys;
   if (!in_place && x0 < y1 && y0 < x1) return set_err(GEMM_ERR_INVALID_ARG, "Y overlaps X without being X itself");
@@ -239,8 +241,12 @@ gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K
   if (d.scale < 0.0f) return set_err(GEMM_ERR_UNSUPPORTED, "scale must be >= 0");
   const int64_t lds[4] = {d.ld_q, d.ld_k, d.ld_v, d.ld_o};
   const int64_t strides[4] = {d.stride_q, d.stride_k, d.stride_v, d.stride_o};
+  if (d.batch > (int64_t{1} << 31) || d.sq > (int64_t{1} << 31) || d.sk > (int64_t{1} << 31))
+    return set_err(GEMM_ERR_UNSUPPORTED, "batch, sq and sk must be <= 2^31");
   for (int i = 0; i < 4; ++i) {
     if (lds[i] < d.d || strides[i] < 0) return set_err(GEMM_ERR_INVALID_ARG, "row strides must be >= d and batch strides >= 0");
+    if (lds[i] > (int64_t{1} << 40) || strides[i] > (int64_t{1} << 40))
+      return set_err(GEMM_ERR_UNSUPPORTED, "row and batch strides must be <= 2^40 elements");
     if (lds[i] % 8 || strides[i] % 8) return set_err(GEMM_ERR_ALIGNMENT, "row and batch strides must be multiples of 8 elements");
   }
   if (d.batch * d.sq == 0) return GEMM_OK;
@@ -254,14 +260,15 @@ gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K
   if (d.batch > (int64_t{1} << 31) / q_tiles - 1) return set_err(GEMM_ERR_UNSUPPORTED, "too many query tiles");
   const int osz = d.out_type == GEMM_F32 ? 4 : 2;
   // batch entries of O: disjoint blocks, or rows interleaved with disjoint segments
-  const bool o_blocks = d.stride_o >= (d.sq - 1) * d.ld_o + d.d;
-  const bool o_interleaved = d.stride_o >= d.d && d.ld_o >= (d.batch - 1) * d.stride_o + d.d;
+  const bool o_blocks = __int128(d.stride_o) >= __int128(d.sq - 1) * d.ld_o + d.d;
+  const bool o_interleaved = d.stride_o >= d.d && __int128(d.ld_o) >= __int128(d.batch - 1) * d.stride_o + d.d;
   if (d.batch > 1 && !o_blocks && !o_interleaved)
     return set_err(GEMM_ERR_INVALID_ARG, "batch entries of O overlap");
   // O must not overlap any input (byte ranges of everything each pointer may touch)
   auto span = [&](const void* p, int64_t stride, int64_t rows, int64_t ld, int esz) {
     const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-    return std::pair<uintptr_t, uintptr_t>(b, b + uintptr_t(((d.batch - 1) * stride + (rows - 1) * ld + d.d) * esz));
+    const __int128 bytes = (__int128(d.batch - 1) * stride + __int128(rows - 1) * ld + d.d) * esz;
+    return std::pair<uintptr_t, uintptr_t>(b, b + uintptr_t(bytes < (__int128(1) << 62) ? bytes : (__int128(1) << 62)));
   };
   const auto o = span(O, d.stride_o, d.sq, d.ld_o, osz);
   const std::pair<uintptr_t, uintptr_t> ins[3] = {span(Q, d.stride_q, d.sq, d.ld_q, 2), span(K, d.stride_k, d.sk, d.ld_k, 2),

@@ -226,6 +226,13 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   if (!kmajor && d.ldb < std::max<int64_t>(1, d.n)) { fail(err, "ldb must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
   if (kmajor && d.ldb < std::max<int64_t>(1, d.k)) { fail(err, "ldb must be >= max(1, k) for K-major B"); return GEMM_ERR_INVALID_ARG; }
   if (d.ldc < std::max<int64_t>(1, d.n)) { fail(err, "ldc must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
+  // element offsets are 64-bit: keep every stride far below the point where row * ld could wrap
+  constexpr int64_t kMaxStride = int64_t{1} << 40;
+  if (d.lda > kMaxStride || d.ldb > kMaxStride || d.ldc > kMaxStride || d.stride_a > kMaxStride ||
+      d.stride_b > kMaxStride || d.stride_c > kMaxStride) {
+    fail(err, "leading dimensions and batch strides must be <= 2^40 elements");
+    return GEMM_ERR_UNSUPPORTED;
+  }
   if ((d.a_type != GEMM_BF16 && d.a_type != GEMM_F16 && d.a_type != GEMM_F32) ||
       (d.b_type != GEMM_BF16 && d.b_type != GEMM_F16 && d.b_type != GEMM_F32) ||
       (d.c_type != GEMM_BF16 && d.c_type != GEMM_F16 && d.c_type != GEMM_F32)) {
