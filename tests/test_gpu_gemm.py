@@ -197,6 +197,39 @@ def test_deterministic_and_plan_reuse():
     assert_close(C2.cpu(), ref, K, a2, b, "f32", "reuse")
 
 
+def test_one_plan_on_concurrent_streams():
+    """A plan is immutable host data: the same plan runs on two streams at once
+    (and a second plan beside it) with the same results as one after another."""
+    M, N, K = 1024, 1024, 512
+    a = synth.normal((M, K), 11, "bf16")
+    b = synth.normal((K, N), 12, "bf16")
+    b2 = synth.normal((K, N), 13, "bf16")
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16)
+    plan2 = la.gemm_plan(M - 1, N, K, la.BF16, la.F32, lda=K)     # a second plan (general kernel)
+    A, B, B2 = a.to(DEV), b.to(DEV), b2.to(DEV)
+    ref1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ref2 = torch.empty_like(ref1)
+    ref3 = torch.empty((M - 1, N), dtype=torch.float32, device=DEV)
+    la.gemm_run(plan, A, B, ref1)
+    la.gemm_run(plan, A, B2, ref2)
+    la.gemm_run(plan2, A[:M - 1], B, ref3)
+    torch.cuda.synchronize()
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for it in range(3):
+        C1, C2 = torch.empty_like(ref1), torch.empty_like(ref2)
+        C3 = torch.empty_like(ref3)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            la.gemm_run(plan, A, B, C1)
+        with torch.cuda.stream(s2):
+            la.gemm_run(plan, A, B2, C2)
+        with torch.cuda.stream(s3):
+            la.gemm_run(plan2, A[:M - 1], B, C3)
+        torch.cuda.synchronize()
+        assert torch.equal(C1, ref1) and torch.equal(C2, ref2) and torch.equal(C3, ref3), "iteration %d" % it
+
+
 def test_graph_capture_replay():
     M, N, K = 384, 512, 320
     a = synth.normal((M, K), 8, "bf16")
