@@ -107,8 +107,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (each output tile is "
-              "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (every output tile is "
+              "independent, so the work would shard by output columns without communication). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.workload in synth.NORM_WORKLOADS:
