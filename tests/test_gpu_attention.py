@@ -132,3 +132,30 @@ def test_deterministic():
     k = synth.normal((2, 512, 128), 72, "bf16")
     v = synth.normal((2, 512, 128), 73, "bf16")
     assert torch.equal(run(q, k, v, "f32", 0.09), run(q, k, v, "f32", 0.09))
+
+
+def test_graph_replay():
+    """Captured in a HIP graph, attention replays to the eager result each time."""
+    q = synth.normal((2, 300, 128), 81, "bf16")
+    k = synth.normal((2, 700, 128), 82, "bf16")
+    v = synth.normal((2, 700, 128), 83, "bf16")
+    Q, K, V = q.to(DEV), k.to(DEV), v.to(DEV)
+    O = torch.empty_like(Q)
+    la.la_attention_run(Q, K, V, O)
+    torch.cuda.synchronize()
+    eager = O.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        la.la_attention_run(Q, K, V, O)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        la.la_attention_run(Q, K, V, O)
+    for it in range(3):
+        O.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O, eager), "replay %d" % it

@@ -448,6 +448,21 @@ def test_bkmajor_permutation_is_exact():
 
 
 @pytest.mark.parametrize("shape", [(512, 256, 192), (300, 200, 100)], ids=["fast", "tiled_edges"])
+def test_gate_up_swiglu_bkmajor(shape):
+    M, N, K = shape
+    x = synth.normal((M, K), 97, "bf16")
+    wg = synth.normal((K, N), 98, "bf16", 0.3)
+    wu = synth.normal((K, N), 99, "bf16", 0.3)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, b_kmajor=True)
+    H = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    la.gemm_gate_up_swiglu_run(plan, x.to(DEV), wg.t().contiguous().to(DEV), wu.t().contiguous().to(DEV), H)
+    torch.cuda.synchronize()
+    h_ref, g_ref, u_ref = oracle.gate_up_swiglu_f64(synth.bits(x), synth.bits(wg), synth.bits(wu), "bf16")
+    err = np.abs(H.cpu().to(torch.float64).numpy() - h_ref)
+    assert np.all(err <= swiglu_bound(K, x, wg, wu, g_ref, u_ref, h_ref, "bf16"))
+
+
+@pytest.mark.parametrize("shape", [(512, 256, 192), (300, 200, 100)], ids=["fast", "tiled_edges"])
 def test_gate_up_bkmajor(shape):
     M, N, K = shape
     x = synth.normal((M, K), 91, "bf16")

@@ -114,3 +114,29 @@ def test_deterministic_and_empty():
     e = torch.empty((0, 64), device=DEV)
     la.la_rms_norm_run(e, torch.ones(64, device=DEV), torch.empty((0, 64), device=DEV))
     torch.cuda.synchronize()
+
+
+def test_graph_replay():
+    """Captured in a HIP graph, the normalisation replays to the eager result each time."""
+    x = synth.normal((512, 1024), 95, "bf16")
+    g = synth.uniform((1024,), 96, "bf16", 0.5, 1.5)
+    X, G = x.to(DEV), g.to(DEV)
+    Y = torch.empty_like(X)
+    la.la_rms_norm_run(X, G, Y, 1e-6)
+    torch.cuda.synchronize()
+    eager = Y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        la.la_rms_norm_run(X, G, Y, 1e-6)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        la.la_rms_norm_run(X, G, Y, 1e-6)
+    for it in range(3):
+        Y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager), "replay %d" % it
