@@ -209,22 +209,23 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     // kb * 32 + 8 (r / 4) + 4 h + r % 4 of this tile; the other half-wave holds the rest.
     // Scores stay raw; with c = scale * log2(e) >= 0, max(c s) = c max(s) and
     // p = exp2(c s - m) is one fused multiply-add and one exp2 per score.
-    const int rem = a.sk - int64_t(t) * BC < BC ? int(a.sk - int64_t(t) * BC) : BC;   // valid keys in the tile
-    float mx = -__builtin_inff();
-    if (rem == BC) {
+    // Keys past the end (only in the last tile) score -inf: they drop out of the
+    // maximum and exp2(k * -inf - m) = 0 (k > 0; a zero scale is passed as the
+    // smallest normal float, which leaves every valid probability at exactly 1).
+    const int64_t remaining = a.sk - int64_t(t) * BC;
+    if (remaining < BC) {
+      const int rem = int(remaining);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          mx = key < rem ? fmaxf(mx, sacc[kb][r]) : mx;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= rem) sacc[kb][r] = -__builtin_inff();
     }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // Lazy reference maximum (log2 units): it moves only when the tile's maximum
     // exceeds it by more than 8, so probabilities stay <= 2^8 and the rescaling
@@ -246,11 +247,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -m));
-        if (rem != BC) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          p = key < rem ? p : 0.0f;
-        }
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -m));
         sacc[kb][r] = p;
         sum += p;
       }

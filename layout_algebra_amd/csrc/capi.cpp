@@ -285,7 +285,10 @@ gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K
   a.sk = d.sk;
   a.ldq = d.ld_q; a.ldk = d.ld_k; a.ldv = d.ld_v; a.ldo = d.ld_o;
   a.bq = d.stride_q; a.bk = d.stride_k; a.bv = d.stride_v; a.bo = d.stride_o;
-  a.scale_log2 = d.scale * 1.4426950408889634f;
+  // the kernel needs a positive factor to push masked keys to -inf; a zero scale
+  // (uniform weights) becomes the smallest normal float, for which every valid
+  // score still gives probability exactly 1
+  a.scale_log2 = d.scale > 0.0f ? d.scale * 1.4426950408889634f : 1.17549435e-38f;
   a.q_tiles = static_cast<int>(q_tiles);
   const hipError_t e = lak::launch_attention(a, static_cast<int>(d.d), d.in_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16,
                                              d.out_type == GEMM_F32 ? lak::OUT_F32 : d.out_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16,

@@ -56,6 +56,7 @@ CASES = [
     (1, 1, 1, 128, "bf16", "f32", None),          # one query, one key
     (2, 77, 1000, 64, "bf16", "f16", 0.5),        # many key tiles, larger scale
     (4, 300, 129, 128, "f16", "bf16", None),      # key count one past two tiles
+    (1, 50, 70, 64, "bf16", "f32", 0.0),          # zero scale: uniform weights over the valid keys
 ]
 
 
