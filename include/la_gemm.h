@@ -183,9 +183,9 @@ typedef struct {
 } attn_desc;
 
 /* O for every batch entry and query, on `stream`.  Scores and the softmax run
- * in FP32 (exp through exp2 with scale*log2(e) folded in), P is rounded to
- * the input type for the product with V, the running sum uses the unrounded
- * P, O is rounded once to out_type.  Q, K, V, O are device pointers, 16-byte
+ * in FP32 (exp through exp2 with scale*log2(e) folded in), P is rounded once
+ * to the input type and both the product with V and the running sum use the
+ * rounded values, O is rounded once to out_type.  Q, K, V, O are device pointers, 16-byte
  * aligned; O must not overlap Q, K or V, and batch entries of O must not
  * overlap each other (see stride_o).  Row strides times 128 bytes must stay below 2^32.
  * batch * sq == 0 launches nothing. */

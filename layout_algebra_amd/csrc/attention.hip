@@ -22,9 +22,9 @@
 //    (ds_read_b64_tr_b16: 4 consecutive keys of one head-dimension column per
 //    lane), so no shuffle or LDS round trip is needed for P.
 //  * exp goes through exp2 with scale * log2(e) folded into one fused
-//    multiply-add per score (scale >= 0); the running sum uses the FP32
-//    probabilities, the product with V their bf16/fp16 rounding (the MFMA
-//    input type).  The reference maximum is updated lazily (only when a tile
+//    multiply-add per score (scale >= 0); the probabilities are rounded once
+//    to the input type, and both the product with V and the running sum use
+//    those rounded values (the sum through packed dot products).  The reference maximum is updated lazily (only when a tile
 //    exceeds it by more than 8 in log2 units, a factor 256), which skips the
 //    rescaling of the output accumulator on most tiles; the result acc / sum
 //    does not depend on the reference.
@@ -102,6 +102,18 @@ __device__ __forceinline__ uint32_t pack2<InF16>(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, f16x2_a{static_cast<_Float16>(lo), static_cast<_Float16>(hi)});
 }
 
+// c + x.lo + x.hi for a packed pair of the input type (one dot-product instruction).
+template <class TI>
+__device__ __forceinline__ float dot2_ones(uint32_t x, float c);
+template <>
+__device__ __forceinline__ float dot2_ones<InBF16>(uint32_t x, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_a, x), bf16x2_a{(__bf16)1.0f, (__bf16)1.0f}, c, false);
+}
+template <>
+__device__ __forceinline__ float dot2_ones<InF16>(uint32_t x, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_a, x), f16x2_a{(_Float16)1.0f, (_Float16)1.0f}, c, false);
+}
+
 template <class TO>
 __device__ __forceinline__ void store4(void* O, int64_t off, float a, float b, float c, float d);
 template <>
@@ -150,36 +162,47 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
       qf[s] = q < a.sq ? *reinterpret_cast<const u32x4*>(Qz + q * a.ldq + 16 * s + 8 * h) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Direct-load lane maps: the lane that fills physical element P of a tile
-  // fetches logical element Sw(P) = key * D + d.
-  int k_key[CHUNKS], k_d[CHUNKS], v_key[CHUNKS], v_d[CHUNKS];
-#pragma unroll
-  for (int i = 0; i < CHUNKS; ++i) {
-    const int P = (wave * CHUNKS + i) * 512 + lane * 8;
-    const int Lk = swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
-    const int Lv = swz<Cfg::VB, Cfg::VM, Cfg::VS>(P);
-    k_key[i] = Lk / D;
-    k_d[i] = Lk % D;
-    v_key[i] = Lv / D;
-    v_d[i] = Lv % D;
-  }
+  // Direct loads: the lane that fills physical element P of a tile fetches
+  // logical element Sw(P) = key * D + d.  The lane maps are recomputed at every
+  // issue (a few integer operations; the opaque copy of the lane index keeps
+  // the compiler from holding them in registers across the key loop).
+  // Offsets stay 32-bit: the host guarantees 128 * ld < 2^32.
   auto issue = [&](int t, int st) {
     const int64_t kbase = int64_t(t) * BC;
-    const int64_t last = a.sk - 1 - kbase;     // rows past the end repeat the last key / value
+    const int64_t last64 = a.sk - 1 - kbase;   // rows past the end repeat the last key / value
+    const int last = last64 < BC - 1 ? int(last64) : BC - 1;
     const uint16_t* kb = Kz + kbase * a.ldk;
     const uint16_t* vb = Vz + kbase * a.ldv;
     AT_LDS uint16_t* dst = lds + st * STAGE + wave * CHUNKS * 512;
+    int lv = lane;
+    asm volatile("" : "+v"(lv));
+    const uint32_t ldk2 = uint32_t(a.ldk) * 2u, ldv2 = uint32_t(a.ldv) * 2u;
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int64_t r = k_key[i] < last ? k_key[i] : last;
-      dma16(kb, uint32_t((r * a.ldk + k_d[i]) * 2), lds_address(dst + i * 512));
+      const int P = (wave * CHUNKS + i) * 512 + lv * 8;
+      const int Lk = swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
+      const int rk = Lk / D < last ? Lk / D : last;
+      dma16(kb, uint32_t(rk) * ldk2 + uint32_t(Lk % D) * 2u, lds_address(dst + i * 512));
     }
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int64_t r = v_key[i] < last ? v_key[i] : last;
-      dma16(vb, uint32_t((r * a.ldv + v_d[i]) * 2), lds_address(dst + KE + i * 512));
+      const int P = (wave * CHUNKS + i) * 512 + lv * 8;
+      const int Lv = swz<Cfg::VB, Cfg::VM, Cfg::VS>(P);
+      const int rv = Lv / D < last ? Lv / D : last;
+      dma16(vb, uint32_t(rv) * ldv2 + uint32_t(Lv % D) * 2u, lds_address(dst + KE + i * 512));
     }
   };
+
+  // LDS fragment addresses (bytes within a tile).  The XOR swizzles of both
+  // tiles take their source bits from the key row and only flip bits that
+  // the k-step (K tile) or the 32-column block (V tile) occupies, so
+  //   K: Sw(row D + 16 s + 8 h) = Sw(row D + 8 h) ^ (16 s),  row = 32 kb + c
+  //   V: Sw(key D + 32 b + x)   = Sw(key0 D + x) ^ (32 b) + (key - key0) D
+  // with key0 = 4 h + e the lane's first key: one base per lane and operand,
+  // the rest is an XOR and an immediate offset per read.
+  const uint32_t kaddr0 = uint32_t(swz<Cfg::KB, Cfg::KM, Cfg::KS>(c * D + 8 * h)) * 2u;
+  const int e4 = (lane >> 2) & 3;
+  const uint32_t vaddr0 = uint32_t(swz<Cfg::VB, Cfg::VM, Cfg::VS>((4 * h + e4) * D + 16 * ((lane >> 4) & 1) + 4 * (lane & 3))) * 2u;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -193,16 +216,25 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     if (t + 1 < nt) issue(t + 1, (t + 1) & 1);
     const AT_LDS uint16_t* ks = lds + (t & 1) * STAGE;
     const AT_LDS uint16_t* vs = ks + KE;
+    const AT_LDS char* ksb = reinterpret_cast<const AT_LDS char*>(ks);
+    const AT_LDS char* vsb = reinterpret_cast<const AT_LDS char*>(vs);
+    uint32_t ka = kaddr0, va = vaddr0;
+    asm volatile("" : "+v"(ka), "+v"(va));     // per-read addresses are formed here, not kept live
 
-    // S^T = K Q^T: two 32-key blocks x 32 queries.
+    // S^T = K Q^T: two 32-key blocks x 32 queries.  All K fragments of the tile
+    // are requested before the first MFMA, so LDS latency is paid once per tile.
+    u32x4 kf[DS][2];
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[s][kb] = *reinterpret_cast<const AT_LDS u32x4*>(ksb + (ka ^ uint32_t(32 * s)) + kb * 32 * D * 2);
+    __builtin_amdgcn_sched_barrier(0);         // keep the reads ahead of the MFMAs (the scheduler would sink them)
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 kf = *reinterpret_cast<const AT_LDS u32x4*>(ks + swz<Cfg::KB, Cfg::KM, Cfg::KS>((kb * 32 + c) * D + 16 * s + 8 * h));
-        sacc[kb] = mfma_32x32x16<TI>(kf, qf[s], sacc[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_32x32x16<TI>(kf[s][kb], qf[s], sacc[kb]);
     }
 
     // Online softmax for query c: register r of block kb is key
@@ -214,6 +246,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     // smallest normal float, which leaves every valid probability at exactly 1).
     const int64_t remaining = a.sk - int64_t(t) * BC;
     if (remaining < BC) {
+      asm volatile("" ::: "memory");           // a real branch: full tiles skip the selects below
       const int rem = int(remaining);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -242,15 +275,27 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
         for (int r = 0; r < 16; ++r) acc[b][r] *= corr;
       m = m_new;
     }
-    float sum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -m));
-        sacc[kb][r] = p;
-        sum += p;
-      }
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -m));
+    // P^T as MFMA B operands (16-key step u: score registers 8 (u % 2) .. + 7 of
+    // block u / 2), rounded to the input type; the running sum adds the same
+    // rounded values, two per dot-product instruction, so numerator and
+    // denominator see identical weights.
+    u32x4 pf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x16& sp = sacc[u >> 1];
+      const int rr = (u & 1) * 8;
+      pf[u] = u32x4{pack2<TI>(sp[rr + 0], sp[rr + 1]), pack2<TI>(sp[rr + 2], sp[rr + 3]),
+                    pack2<TI>(sp[rr + 4], sp[rr + 5]), pack2<TI>(sp[rr + 6], sp[rr + 7])};
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) sum = dot2_ones<TI>(pf[u][w2], sum);
     sum += __shfl_xor(sum, 32, 64);
     l += sum;
 
@@ -258,20 +303,13 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     // key 16 u + 8 (e / 4) + 4 h + e % 4, the order of the score registers.
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const f32x16& sp = sacc[u >> 1];
-      const int rr = (u & 1) * 8;
-      const u32x4 pf = u32x4{pack2<TI>(sp[rr + 0], sp[rr + 1]), pack2<TI>(sp[rr + 2], sp[rr + 3]),
-                             pack2<TI>(sp[rr + 4], sp[rr + 5]), pack2<TI>(sp[rr + 6], sp[rr + 7])};
-      const int vk = 16 * u + 4 * h + ((lane >> 2) & 3);
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const int vd = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const i16x4_a lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (AT_LDS i16x4_a*)(vs + swz<Cfg::VB, Cfg::VM, Cfg::VS>(vk * D + vd)));
-        const i16x4_a hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (AT_LDS i16x4_a*)(vs + swz<Cfg::VB, Cfg::VM, Cfg::VS>((vk + 8) * D + vd)));
+        const AT_LDS char* vp = vsb + (va ^ uint32_t(64 * b)) + 16 * u * D * 2;
+        const i16x4_a lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AT_LDS i16x4_a*)(vp));
+        const i16x4_a hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AT_LDS i16x4_a*)(vp + 8 * D * 2));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        acc[b] = mfma_32x32x16<TI>(u32x4{l2.x, l2.y, h2.x, h2.y}, pf, acc[b]);
+        acc[b] = mfma_32x32x16<TI>(u32x4{l2.x, l2.y, h2.x, h2.y}, pf[u], acc[b]);
       }
     }
   }

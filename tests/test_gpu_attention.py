@@ -2,9 +2,10 @@
 memory", section "How long a tile lives") against the binary64 oracle, through
 the C ABI.
 
-Bound per output row i: every probability reaches the product with V rounded
-to the input type (relative 2^-8 for bf16, 2^-11 for fp16: at most that times
-max|V| in the weighted mean); the FP32 scores are off by at most
+Bound per output row i: every probability is rounded to the input type
+(relative 2^-9 for bf16, 2^-12 for fp16) and the GPU forms the weighted mean
+with those rounded weights in numerator and denominator alike, which moves the
+mean by at most twice that times max|V| (2^-8, 2^-11); the FP32 scores are off by at most
 Delta = scale * 2^-20 * d * max|Q| * max|K|, which moves the normalised
 weights by at most about 2 Delta (4 Delta max|V| in the mean); 2^-20 covers
 exp2 and the FP32 arithmetic; the output's own rounding adds r |O|.
