@@ -39,7 +39,7 @@ METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
 NORM_SOURCES = ("rms_norm.hip", "norm.hpp", "kernel_common.hpp", "launch.hpp")
 ATTN_SOURCES = ("attention.hip", "attention.hpp", "kernel_common.hpp", "launch.hpp")
-OWN_SOURCES = ("rms_norm.hip", "norm.hpp", "attention.hip", "attention.hpp")
+OWN_SOURCES = ("rms_norm.hip", "norm.hpp", "attention.hip", "attention.hpp", "probe.hip")
 
 
 def kernel_source_hash(workload):
@@ -210,6 +210,8 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[w.in_kind],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["bound"] == "mfma" and w.flops() >= 1e11:
+        roof["mfma_ceiling"] = mfma_ceiling(dev, A, flops, roof["achieved"])
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel_avg_ms"] = kern_ms
     roof["single_launch_ms"] = {"min": float(per_launch.min()), "median": float(np.median(per_launch))}
@@ -231,6 +233,27 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit)
     print(json.dumps(line), flush=True)
+
+
+def mfma_ceiling(dev, operands, flops, achieved):
+    """The matrix-core rate the chip sustains at this workload's size: the library's probe issues
+    the same number of 32x32x16 MFMAs per SIMD as the workload (one wave per SIMD, 16 independent
+    chains, no memory traffic) on 16-byte fragments of the workload's own input values, then on
+    zeros (the multipliers' power, and so the clock the chip settles to, depends on the bits).
+    Context for roofline.frac, which stays relative to the nominal peak."""
+    import layout_algebra_amd as la
+    per_mfma = 32 * 32 * 16 * 2
+    per_wave = max(16, int(round(flops / per_mfma / (256 * 4) / 16)) * 16)
+    sink = torch.empty(256 * 256, dtype=torch.float32, device=dev)
+    ops = operands.reshape(-1)[: 1 << 19]
+    res = {}
+    for name, src in (("tflops", ops), ("tflops_zero_operands", torch.zeros_like(ops))):
+        ms, _, _ = timed_steps(lambda i: la.la_probe_mfma(src, sink, 256, per_wave), 10, 3)
+        res[name] = 256 * 4 * per_wave * per_mfma / (ms * 1e-3) / 1e12
+    res["operands"] = "first %d KiB of the workload's first input" % (ops.numel() * 2 // 1024)
+    res["mfma_per_wave"] = per_wave
+    res["frac"] = achieved / res["tflops"]
+    return res
 
 
 def copy_probe(dev):
@@ -329,7 +352,9 @@ def bench_attention(args, w):
         "config": {"workload": w.name, "batch": w.batch, "sq": w.sq, "sk": w.sk, "d": w.d, "in": w.in_kind,
                    "out": w.out_kind, "scale": w.scale},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[w.in_kind], "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_TFLOPS[w.in_kind], "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
+                     "frac": tflops / PEAK_TFLOPS[w.in_kind],
+                     "mfma_ceiling": mfma_ceiling(dev, Q, w.flops(), tflops),
+                     "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
                      "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
         "wall_s_timed": wall,
     }

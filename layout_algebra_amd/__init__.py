@@ -8,12 +8,12 @@ else.  The library is loaded on first use and a missing library is an error
 Entry points carry the C ABI's names (include/la_gemm.h):
     gemm_plan, gemm_run, gemm_run_reduce, gemm_gate_up_run, gemm_gate_up_swiglu_run, gemm_plan_describe,
     la_rms_norm_run, la_attention_run, gemm_plan_lds_offset, gemm_plan_lds_stage_bytes, gemm_debug_lds_image,
-    la_layout_eval, la_layout_eval_index, la_swizzle_apply, la_tile_plan_offset
+    la_probe_mfma (matrix-core rate probe, a measurement aid), la_layout_eval, la_layout_eval_index, la_swizzle_apply, la_tile_plan_offset
 """
 from ._lib import (  # noqa: F401
     BF16, F16, F32, FLAG_GATE_UP, FLAG_B_KMAJOR, GemmError, Plan, EXPORTED_SYMBOLS, lib_path, load,
     gemm_plan, gemm_run, gemm_run_reduce, gemm_gate_up_run, gemm_gate_up_swiglu_run, gemm_plan_describe,
     gemm_plan_lds_offset,
     gemm_plan_lds_stage_bytes, gemm_debug_lds_image, la_layout_eval, la_layout_eval_index,
-    la_swizzle_apply, la_tile_plan_offset, la_rms_norm_run, la_attention_run,
+    la_swizzle_apply, la_tile_plan_offset, la_rms_norm_run, la_attention_run, la_probe_mfma,
 )

@@ -12,7 +12,7 @@ FLAG_B_KMAJOR = 0x2
 
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
-    "la_rms_norm_run", "la_attention_run", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
+    "la_rms_norm_run", "la_attention_run", "la_probe_mfma", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "gemm_status_string", "gemm_last_error",
 )
@@ -71,6 +71,7 @@ def load():
         "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
         "la_rms_norm_run": ([i64, i64, i32, i32, vp, i64, vp, vp, i64, f32, vp], i32),
         "la_attention_run": ([ctypes.POINTER(_AttnDesc), vp, vp, vp, vp, vp], i32),
+        "la_probe_mfma": ([vp, i64, vp, i64, i64, i32, vp], i32),
         "gemm_plan_describe": ([vp, ctypes.c_char_p, ctypes.c_size_t], i32),
         "gemm_plan_lds_offset": ([vp, i32, i64, i64, p64], i32),
         "gemm_plan_lds_stage_bytes": ([vp, p64], i32),
@@ -305,6 +306,23 @@ def la_attention_run(Q, K, V, O, scale=None, stream=None):
                      float(scale if scale is not None else 1.0 / (d ** 0.5)))
     _check(load().la_attention_run(ctypes.byref(desc), *[ctypes.c_void_p(t.data_ptr()) for t in (Q, K, V, O)],
                                    _stream_ptr(stream)))
+
+
+def la_probe_mfma(operands, sink, workgroups, mfma_per_wave, stream=None):
+    """Matrix-core rate probe: `workgroups` x 4 waves, each issuing mfma_per_wave MFMAs on 16-byte fragments
+    taken from `operands` (a contiguous bf16/f16 tensor on the GPU, its dtype selects the instruction);
+    `sink` is a float32 GPU tensor of at least workgroups * 256 elements."""
+    torch = _torch()
+    if not isinstance(operands, torch.Tensor) or operands.device.type != "cuda" or operands.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("operands must be a bf16/f16 tensor on the GPU")
+    if not operands.is_contiguous():
+        raise ValueError("operands must be contiguous")
+    if not isinstance(sink, torch.Tensor) or sink.device.type != "cuda" or sink.dtype != torch.float32 or \
+            not sink.is_contiguous() or sink.numel() < int(workgroups) * 256:
+        raise ValueError("sink must be a contiguous float32 GPU tensor of at least workgroups * 256 elements")
+    nbytes = (operands.numel() * 2) // 16 * 16
+    _check(load().la_probe_mfma(ctypes.c_void_p(operands.data_ptr()), int(nbytes), ctypes.c_void_p(sink.data_ptr()),
+                                int(workgroups), int(mfma_per_wave), _KIND[operands.dtype], _stream_ptr(stream)))
 
 
 def gemm_debug_lds_image(plan, A, B, B2, tile_m, tile_n, out, stream=None):

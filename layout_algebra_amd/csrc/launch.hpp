@@ -43,7 +43,7 @@ __device__ __forceinline__ TiledArgs at_batch(const TiledArgs& g) {
 
 enum KernelId : int {
   KID_TILED_128 = 0,     // any shape: 128x128x64, 4 waves of 64x64, register-staged, B transposed while staging
-  KID_FAST_256 = 1,      // full tiles: 256x256x64, 8 waves of 128x64, direct-to-LDS, transposing B reads
+  KID_FAST_256 = 1,      // full tiles: 256x256x32, 8 waves of 128x64, direct-to-LDS, transposing B reads
   KID_FAST_GU = 2,       // full tiles, gate/up: 256 x (128 + 128) x 32, 8 waves of 128 x (32 + 32)
   KID_SKINNY_16 = 3,     // M <= 16: 16 x 128 column strips over all of K, 4 waves of 16 x 32, HBM-bound
   KID_FAST_256_KM = 4,   // KID_FAST_256 for B stored [N, K] (K contiguous)
@@ -109,6 +109,11 @@ struct KernelShape {
 // Fill R[0, n) with the identity of `red` (0, -inf or +inf) on `stream`: a
 // kernel, not a memset, so that HIP graphs may capture it.
 hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
+
+// Matrix-core rate probe (measurement aid): `workgroups` x 4 waves, each
+// issuing mfma_per_wave (a multiple of 16) MFMAs on fragments from `ops`.
+hipError_t launch_mfma_probe(const void* ops, int64_t n_frags, float* sink, int64_t workgroups, int64_t mfma_per_wave,
+                             int in_kind, hipStream_t stream);
 
 // Static description of each kernel id; the planner validates these maps.
 KernelShape kernel_shape(int kid);

@@ -1,0 +1,61 @@
+// Matrix-core rate probe: a measurement aid beside the GEMM, not part of it.
+//
+// Every lane loads eight 16-byte operand fragments (four A-side, four B-side)
+// from a caller buffer and then issues v_mfma_f32_32x32x16 in sixteen
+// independent accumulator chains, with no memory traffic in between.  Timed
+// against the same number of MFMAs per SIMD as a GEMM launch, it gives the
+// rate the matrix cores sustain on those operand values at whatever clock the
+// chip settles to under that load (the power drawn by the multipliers depends
+// on the operand bits).  One workgroup of four waves per CU: one wave per SIMD.
+#include "kernel_common.hpp"
+#include "launch.hpp"
+
+namespace lak {
+namespace {
+
+template <class TI>
+__global__ void __launch_bounds__(256) mfma_probe_kernel(const u32x4* __restrict__ ops, int64_t n_frags,
+                                                          float* __restrict__ sink, int64_t iters) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = ops[(t * 8 + i) % n_frags];
+    b[i] = ops[(t * 8 + 4 + i) % n_frags];
+  }
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<TI>(a[i], b[j], acc[i][j]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += acc[i][j][e];
+  sink[t] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(const void* ops, int64_t n_frags, float* sink, int64_t workgroups, int64_t mfma_per_wave,
+                             int in_kind, hipStream_t stream) {
+  const u32x4* p = static_cast<const u32x4*>(ops);
+  const int64_t iters = mfma_per_wave / 16;
+  if (in_kind == IN_BF16) {
+    hipLaunchKernelGGL(mfma_probe_kernel<InBF16>, dim3(unsigned(workgroups)), dim3(256), 0, stream, p, n_frags, sink, iters);
+  } else {
+    hipLaunchKernelGGL(mfma_probe_kernel<InF16>, dim3(unsigned(workgroups)), dim3(256), 0, stream, p, n_frags, sink, iters);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lak

@@ -247,3 +247,25 @@ def test_attention_argument_errors_are_caught_before_launch():
     assert call(ld_k=1 << 25, stride_k=0) == "GEMM_ERR_UNSUPPORTED"
     assert call(batch=0, Q=0, K=0, V=0, O=0) == "GEMM_OK"            # nothing to do, nothing touched
     assert call(sq=0, sk=0, Q=0, K=0, V=0, O=0) == "GEMM_OK"
+
+
+def test_mfma_probe_argument_errors_are_caught_before_launch():
+    lib = la.load()
+    vp = ctypes.c_void_p
+    st = la._lib.STATUS
+
+    def call(ops=0x1000000, nbytes=1 << 20, sink=0x2000000, wg=256, n=4096, t=la.BF16):
+        return st[lib.la_probe_mfma(vp(ops), nbytes, vp(sink), wg, n, t, vp(0))]
+
+    assert call(t=la.F32) == "GEMM_ERR_INVALID_ARG"
+    assert call(nbytes=0) == "GEMM_ERR_INVALID_ARG"
+    assert call(nbytes=24) == "GEMM_ERR_INVALID_ARG"
+    assert call(wg=0) == "GEMM_ERR_INVALID_ARG"
+    assert call(wg=(1 << 20) + 1) == "GEMM_ERR_INVALID_ARG"
+    assert call(n=0) == "GEMM_ERR_INVALID_ARG"
+    assert call(n=24) == "GEMM_ERR_INVALID_ARG"
+    assert call(n=(1 << 24) + 16) == "GEMM_ERR_INVALID_ARG"
+    assert call(ops=0) == "GEMM_ERR_NULL"
+    assert call(sink=0) == "GEMM_ERR_NULL"
+    assert call(ops=0x1000008) == "GEMM_ERR_ALIGNMENT"
+    assert call(sink=0x2000002) == "GEMM_ERR_ALIGNMENT"

@@ -1,0 +1,36 @@
+"""GPU test of the matrix-core rate probe (a measurement aid used by the benchmark).
+
+With every operand element equal to c, each 32x32x16 product adds 16 c^2 to
+every accumulator element, so after mfma_per_wave / 16 products per chain a
+lane's 16 chains x 16 registers sum to 256 * 16 * c^2 * (mfma_per_wave / 16):
+exact in FP32 for the small counts used here.
+"""
+import pytest
+import torch
+
+import layout_algebra_amd as la
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("c", [1.0, 2.0, -0.5])
+def test_probe_accumulates_exact_products(dtype, c):
+    wg, n = 8, 64
+    ops = torch.full((4096,), c, dtype=dtype, device=DEV)
+    sink = torch.full((wg * 256,), float("nan"), dtype=torch.float32, device=DEV)
+    la.la_probe_mfma(ops, sink, wg, n)
+    torch.cuda.synchronize()
+    expect = 256.0 * 16.0 * c * c * (n // 16)
+    assert torch.all(sink.cpu() == expect), sink.cpu()[:8]
+
+
+def test_probe_rejects_bad_arguments():
+    ops = torch.ones(4096, dtype=torch.bfloat16, device=DEV)
+    sink = torch.empty(256, dtype=torch.float32, device=DEV)
+    with pytest.raises(la.GemmError):
+        la.la_probe_mfma(ops, sink, 1, 24)           # not a multiple of 16
+    with pytest.raises(ValueError):
+        la.la_probe_mfma(ops, sink, 2, 16)           # sink too small for 2 workgroups
