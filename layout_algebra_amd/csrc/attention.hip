@@ -114,6 +114,19 @@ __device__ __forceinline__ float dot2_ones<InF16>(uint32_t x, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_a, x), f16x2_a{(_Float16)1.0f, (_Float16)1.0f}, c, false);
 }
 
+// Combine every lane with its partner in the other half-wave (lane l ^ 32) without LDS:
+// v_permlane32_swap with the same register on both sides returns lanes 0-31 twice in one
+// result and lanes 32-63 twice in the other, so f(first, second) is f(x[l], x[l ^ 32]) up to
+// the order of the operands (exact for the maximum and for a two-term sum).
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <class TO>
 __device__ __forceinline__ void store4(void* O, int64_t off, float a, float b, float c, float d);
 template <>
@@ -163,30 +176,43 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
   }
 
   // Direct loads: the lane that fills physical element P of a tile fetches
-  // logical element Sw(P) = key * D + d.  The lane maps are recomputed at every
-  // issue (a few integer operations; the opaque copy of the lane index keeps
-  // the compiler from holding them in registers across the key loop).
-  // Offsets stay 32-bit: the host guarantees 128 * ld < 2^32.
+  // logical element Sw(P) = key * D + d.  A full tile uses the byte offsets
+  // computed here once; the last tile, when partial, recomputes them with rows
+  // past the end clamped to the last key / value row.  Offsets stay 32-bit:
+  // the host guarantees 128 * ld < 2^32.
+  uint32_t ofk[CHUNKS], ofv[CHUNKS];
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    const int P = (wave * CHUNKS + i) * 512 + lane * 8;
+    const int Lk = swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
+    const int Lv = swz<Cfg::VB, Cfg::VM, Cfg::VS>(P);
+    ofk[i] = uint32_t(Lk / D) * uint32_t(a.ldk) * 2u + uint32_t(Lk % D) * 2u;
+    ofv[i] = uint32_t(Lv / D) * uint32_t(a.ldv) * 2u + uint32_t(Lv % D) * 2u;
+  }
   auto issue = [&](int t, int st) {
     const int64_t kbase = int64_t(t) * BC;
-    const int64_t last64 = a.sk - 1 - kbase;   // rows past the end repeat the last key / value
-    const int last = last64 < BC - 1 ? int(last64) : BC - 1;
     const uint16_t* kb = Kz + kbase * a.ldk;
     const uint16_t* vb = Vz + kbase * a.ldv;
     AT_LDS uint16_t* dst = lds + st * STAGE + wave * CHUNKS * 512;
-    int lv = lane;
-    asm volatile("" : "+v"(lv));
+    if (kbase + BC <= a.sk) {
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) dma16(kb, ofk[i], lds_address(dst + i * 512));
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) dma16(vb, ofv[i], lds_address(dst + KE + i * 512));
+      return;
+    }
+    const int last = int(a.sk - 1 - kbase);     // rows past the end repeat the last key / value
     const uint32_t ldk2 = uint32_t(a.ldk) * 2u, ldv2 = uint32_t(a.ldv) * 2u;
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int P = (wave * CHUNKS + i) * 512 + lv * 8;
+      const int P = (wave * CHUNKS + i) * 512 + lane * 8;
       const int Lk = swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
       const int rk = Lk / D < last ? Lk / D : last;
       dma16(kb, uint32_t(rk) * ldk2 + uint32_t(Lk % D) * 2u, lds_address(dst + i * 512));
     }
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int P = (wave * CHUNKS + i) * 512 + lv * 8;
+      const int P = (wave * CHUNKS + i) * 512 + lane * 8;
       const int Lv = swz<Cfg::VB, Cfg::VM, Cfg::VS>(P);
       const int rv = Lv / D < last ? Lv / D : last;
       dma16(vb, uint32_t(rv) * ldv2 + uint32_t(Lv % D) * 2u, lds_address(dst + KE + i * 512));
@@ -259,7 +285,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = halves_max(mx);
     // Lazy reference maximum (log2 units): it moves only when the tile's maximum
     // exceeds it by more than 8, so probabilities stay <= 2^8 and the rescaling
     // of the accumulator and the running sum is skipped for most tiles; the
@@ -296,8 +322,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) sum = dot2_ones<TI>(pf[u][w2], sum);
-    sum += __shfl_xor(sum, 32, 64);
-    l += sum;
+    l += halves_sum(sum);
 
     // O^T += V^T P^T over four 16-key steps; slot e of the lane's 8 k values is
     // key 16 u + 8 (e / 4) + 4 h + e % 4, the order of the score registers.
