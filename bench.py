@@ -94,8 +94,11 @@ def algorithmic_bytes(w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The chip's clock keeps ramping for tens of milliseconds of sustained load: 200 untimed steps
+    # reach the steady state (1100 -> 1250 TFLOP/s at 4096^3 against 10), and 1000 timed steps
+    # (about 0.1 s at 4096^3) average over the power manager's fluctuations.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS) + sorted(synth.NORM_WORKLOADS) + sorted(synth.ATTN_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
