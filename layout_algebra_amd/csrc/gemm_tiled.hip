@@ -339,6 +339,8 @@ hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_u
   switch (kid) {
     case KID_TILED_128:
       return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+    case KID_TILED_64:
+      return by_types<64, 64, 2, 1>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

@@ -13,6 +13,8 @@ KernelShape kernel_shape(int kid) {
   switch (kid) {
     case KID_TILED_128:
       return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 3}, {3, 3, 3}, 1, 0, 0, 2};
+    case KID_TILED_64:
+      return KernelShape{64, 64, 64, 2, 2, 1, 128, 32, 32, 16, {3, 3, 3}, {3, 3, 3}, 1, 0, 0, 2};
     case KID_FAST_256: return fast_shape<CfgFast256>();
     case KID_FAST_GU: return fast_shape<CfgFastGU>();
     case KID_FAST_256_KM: return fast_shape<CfgFast256KM>();
@@ -34,7 +36,8 @@ int64_t stage_elems(const KernelShape& s, bool gate_up) {
 hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, const TiledArgs& args,
                          dim3 grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
-    case KID_TILED_128: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+    case KID_TILED_128:
+    case KID_TILED_64: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     case KID_FAST_256:
     case KID_FAST_GU:
     case KID_FAST_256_KM:

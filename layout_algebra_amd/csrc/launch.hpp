@@ -48,6 +48,7 @@ enum KernelId : int {
   KID_SKINNY_16 = 3,     // M <= 16: 16 x 128 column strips over all of K, 4 waves of 16 x 32, HBM-bound
   KID_FAST_256_KM = 4,   // KID_FAST_256 for B stored [N, K] (K contiguous)
   KID_FAST_GU_KM = 5,    // KID_FAST_GU for weights stored [N, K]
+  KID_TILED_64 = 6,      // any shape, small grids: 64x64x64, 2 waves of 32x64, as KID_TILED_128 otherwise
   KID_COUNT
 };
 

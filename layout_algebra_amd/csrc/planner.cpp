@@ -296,6 +296,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
     if (skinny_fit) p.kid = lak::KID_SKINNY_16;
+    // The general kernel on a grid that leaves most CUs idle (fewer than 128 workgroups of
+    // 128 x 128, e.g. 104 at 1000 x 1537): 64 x 64 tiles give four times as many.
+    if (p.kid == lak::KID_TILED_128) {
+      const int64_t wg128 = ((d.m + 127) / 128) * ((d.n + 127) / 128) * d.batch;
+      if (wg128 < 128) p.kid = lak::KID_TILED_64;
+    }
   }
   p.shape = lak::kernel_shape(p.kid);
   const auto& s = p.shape;
@@ -340,7 +346,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   }
 
   std::ostringstream js;
-  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor"};
+  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled"};
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
      << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc

@@ -107,6 +107,22 @@ def test_shapes_and_types(shape, in_kind, out_kind):
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+def test_general_kernel_both_tile_sizes(in_kind, out_kind):
+    """Ragged shapes on either side of the general kernel's tile switch: fewer than 128 workgroups
+    of 128 x 128 take 64 x 64 tiles (1000 x 1537: 400 of them), more keep 128 x 128 (1536 x 1537:
+    156); alpha, beta and an existing C, every element against the oracle."""
+    for (M, N, K), kernel in (((1000, 1537, 999), "tiled_64x64"), ((1536, 1537, 999), "tiled_128x128")):
+        seed = M + N + K
+        a = synth.uniform((M, K), seed, in_kind)
+        b = synth.uniform((K, N), seed + 1, in_kind)
+        c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+        got = run_gemm(a, b, out_kind, 1.5, -0.5, c, expect=kernel)
+        ref = oracle_gemm(a, b, in_kind, 1.5, -0.5, c.to(torch.float32))
+        assert_close(got, ref, K, a, b, out_kind, "%s %dx%dx%d" % (kernel, M, N, K))
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
 def test_identity_and_permutation_B_are_exact(in_kind):
     K, M = 256, 192
     a = synth.uniform((M, K), 17, in_kind)
@@ -286,7 +302,8 @@ LDS_CASES = {
     "fast_bf16": (512, 512, 256, "bf16", False, 1, 1, "fast_"),
     "fast_f16_last_tile": (768, 512, 128, "f16", False, 2, 1, "fast_"),
     "tiled_bf16_interior": (384, 384, 200, "bf16", False, 1, 1, "tiled_"),
-    "tiled_f16_ragged_edge": (1000, 1537, 999, "f16", False, 7, 12, "tiled_"),
+    "tiled64_f16_ragged_edge": (1000, 1537, 999, "f16", False, 15, 24, "tiled_64x64"),
+    "tiled128_f16_ragged_edge": (1536, 1537, 999, "f16", False, 11, 12, "tiled_128x128"),
     "fast_gate_up": (512, 256, 128, "bf16", True, 1, 1, "fast_gate_up_"),
     "tiled_gate_up_edge": (300, 200, 100, "bf16", True, 2, 1, "tiled_"),
     "skinny_bf16": (16, 512, 256, "bf16", False, 0, 2, "skinny_"),
