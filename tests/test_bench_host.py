@@ -1,0 +1,57 @@
+"""Host-side checks of bench.py: the one-GPU contract and the per-unit work figures its roofline
+divides by (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name,flop", [("square256", 2 * 256 ** 3), ("square4096", 2 * 4096 ** 3),
+                                       ("ragged", 2 * 1000 * 1537 * 999), ("gate_up", 4 * 4096 * 11008 * 4096),
+                                       ("skinny", 2 * 16 * 28672 * 8192)])
+def test_gemm_flops(name, flop):
+    assert synth.WORKLOADS[name].flops() == flop
+
+
+def test_algorithmic_bytes():
+    # every operand read once, C written (and read when beta != 0)
+    assert bench.algorithmic_bytes(synth.WORKLOADS["skinny"]) == 2 * 16 * 8192 + 2 * 8192 * 28672 + 4 * 16 * 28672 == 471_859_200
+    assert bench.algorithmic_bytes(synth.WORKLOADS["square4096"]) == 3 * 2 * 4096 * 4096
+    assert bench.algorithmic_bytes(synth.WORKLOADS["ragged"]) == 2 * (1000 * 999 + 999 * 1537) + 2 * 4 * 1000 * 1537
+    assert bench.algorithmic_bytes(synth.WORKLOADS["gate_up"]) == 2 * 4096 * 4096 + 2 * 2 * 4096 * 11008 + 2 * 2 * 4096 * 11008
+    assert bench.algorithmic_bytes(synth.WORKLOADS["gate_up_swiglu"]) == 2 * 4096 * 4096 + 2 * 2 * 4096 * 11008 + 2 * 4096 * 11008
+
+
+def test_attention_and_norm_work():
+    a = synth.ATTN_WORKLOADS["attention"]
+    assert a.flops() == 4 * 64 * 4096 * 4096 * 128
+    n = synth.NORM_WORKLOADS["rms_norm"]
+    assert n.bytes() == n.M * n.D * 8 + n.D * 4
+
+
+def test_traffic_lines_parse_and_follow_the_source_hash(tmp_path, monkeypatch):
+    # a line is used only while its hash matches the workload's current kernel sources
+    h = bench.kernel_source_hash("square4096")
+    assert len(h) == 16 and h == bench.kernel_source_hash("gate_up")        # same kernel sources
+    assert h != bench.kernel_source_hash("attention")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic.md").write_text("# header\ntraffic square4096: 1234 %s\ntraffic skinny: 99 0000000000000000\n" % h)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w: h)
+    assert bench.measured_traffic("square4096") == 1234
+    assert bench.measured_traffic("skinny") is None          # stale hash
+    assert bench.measured_traffic("gate_up") is None         # no line
