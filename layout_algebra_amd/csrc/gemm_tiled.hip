@@ -15,7 +15,7 @@
 //     each thread transposes a 4 (k) x 8 (n) block in registers while staging.
 //   * Two LDS stages: while the MFMAs consume stage s the next block is
 //     loaded into registers and written to stage s^1; one workgroup barrier
-//     per block separates "all waves finished reading" from "overwrite"
+//     per block keeps every wave's reads of a stage ahead of its refill
 //     (the two synchronisations the Tylo.jl page "Layouts, storage and
 //     ownership" requires in section "Plans describe work, callers establish
 //     readiness").
