@@ -69,6 +69,13 @@ typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
                                     B[n * ldb + k], ldb >= max(1, k) -- the K-contiguous operand
                                     storage of the Tylo.jl page "TMA and Hopper WGMMA" (section
                                     "The same storage contract on both sides") */
+#define GEMM_FLAG_LARGE_TILES 0x4u  /* keep the largest tile the shape allows.  Without it the
+                                    planner moves a GEMM whose grid would leave most of the 256
+                                    CUs idle to 64 x 64 tiles (fewer than 32 workgroups of the
+                                    256-wide full-tile kernels; for the general kernel, always
+                                    with 16-byte loads and below 384 workgroups of 128 x 128 with
+                                    2-byte loads).  For callers that run many small GEMMs on
+                                    concurrent streams, where one GEMM need not fill the chip. */
 
 typedef struct {
   int64_t m, n, k;             /* problem sizes, each >= 0 */

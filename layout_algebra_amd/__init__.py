@@ -11,7 +11,7 @@ Entry points carry the C ABI's names (include/la_gemm.h):
     la_probe_mfma (matrix-core rate probe, a measurement aid), la_layout_eval, la_layout_eval_index, la_swizzle_apply, la_tile_plan_offset
 """
 from ._lib import (  # noqa: F401
-    BF16, F16, F32, FLAG_GATE_UP, FLAG_B_KMAJOR, GemmError, Plan, EXPORTED_SYMBOLS, lib_path, load,
+    BF16, F16, F32, FLAG_GATE_UP, FLAG_B_KMAJOR, FLAG_LARGE_TILES, GemmError, Plan, EXPORTED_SYMBOLS, lib_path, load,
     gemm_plan, gemm_run, gemm_run_reduce, gemm_gate_up_run, gemm_gate_up_swiglu_run, gemm_plan_describe,
     gemm_plan_lds_offset,
     gemm_plan_lds_stage_bytes, gemm_debug_lds_image, la_layout_eval, la_layout_eval_index,

@@ -9,6 +9,7 @@ _LIB_PATH = os.path.join(HERE, "liblagemm.so")
 BF16, F16, F32 = 0, 1, 2
 FLAG_GATE_UP = 0x1
 FLAG_B_KMAJOR = 0x2
+FLAG_LARGE_TILES = 0x4
 
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
@@ -123,14 +124,16 @@ class Plan:
 
 
 def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False, b_kmajor=False,
-              batch=1, stride_a=None, stride_b=None, stride_c=None):
+              batch=1, stride_a=None, stride_b=None, stride_c=None, large_tiles=False):
     """Plan C[m,n] = A[m,k] @ B.  B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed).
-    batch > 1: tensors gain a leading batch dimension with the given element strides (default: packed)."""
+    batch > 1: tensors gain a leading batch dimension with the given element strides (default: packed).
+    large_tiles=True keeps the largest tile the shape allows (GEMM_FLAG_LARGE_TILES)."""
     lda = int(lda if lda is not None else max(1, k))
     ldb = int(ldb if ldb is not None else max(1, k if b_kmajor else n))
     ldc = int(ldc if ldc is not None else max(1, n))
     d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type), lda, ldb, ldc,
-              (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0), int(batch),
+              (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0) |
+              (FLAG_LARGE_TILES if large_tiles else 0), int(batch),
               int(stride_a if stride_a is not None else m * lda),
               int(stride_b if stride_b is not None else (n if b_kmajor else k) * ldb),
               int(stride_c if stride_c is not None else m * ldc))

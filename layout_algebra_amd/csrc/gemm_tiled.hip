@@ -26,10 +26,20 @@
 //   * Epilogue: alpha * acc + beta * C_old in FP32 (C_old read only when
 //     beta != 0), rounded to nearest even for 16-bit outputs, written only
 //     inside [0,M) x [0,N).
+#include <type_traits>
+
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
 namespace lak {
+
+// Sixteen zero bytes in device memory: staging loads of elements outside the
+// matrix read from here, so the loaded registers need no masking afterwards.
+__device__ __attribute__((aligned(16))) uint16_t kZeroChunk[8];
+
+// Eight 16-bit elements of one staging load, packed in pairs.
+struct Chunk8 { u32x4 w; };   // one 16-byte vector load
+struct Chunk1 { u32x4 w; };   // eight 2-byte loads
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
 struct Tiled {
@@ -48,15 +58,19 @@ struct Tiled {
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_CHUNKS * NT * 8 == BM * BK, "A block must split evenly over threads");
   static_assert(B_BLOCKS * NT == (BK / 4) * BN8, "B block must split evenly over threads");
-  static_assert(V == 8 || V == 4 || V == 2 || V == 1, "vector width");
+  static_assert(V == 8 || V == 1, "vector width");
+  typedef typename std::conditional<V == 8, Chunk8, Chunk1>::type Chunk;
 
   // LDS element offset of (row, k) inside one operand block.
   static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 3>(row * BK + k); }
 
   struct Regs {
-    u32x4 a[A_CHUNKS];
-    u32x4 b[NB][BKM ? B_CHUNKS : B_BLOCKS][BKM ? 1 : 4];
+    Chunk a[A_CHUNKS];
+    Chunk b[NB][BKM ? B_CHUNKS : B_BLOCKS][BKM ? 1 : 4];
   };
+
+  static __device__ __forceinline__ u32x4 packed(const Chunk8& c) { return c.w; }
+  static __device__ __forceinline__ u32x4 packed(const Chunk1& c) { return c.w; }
 
   static __device__ __forceinline__ u32x4 pack8(const uint16_t* e) {
     u32x4 w;
@@ -67,33 +81,43 @@ struct Tiled {
     return w;
   }
 
-  // Eight consecutive elements starting at p; `nvalid` of them are in range.
-  static __device__ __forceinline__ u32x4 load8(const uint16_t* p, int nvalid) {
-    if (nvalid >= 8) {
-      if constexpr (V == 8) {
-        return *reinterpret_cast<const u32x4*>(p);
-      } else {
-        uint16_t e[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = p[q];
-        return pack8(e);
-      }
-    }
+  // Eight consecutive elements starting at p, of which the first `nvalid` (0..8)
+  // lie inside the matrix; the others read as 0.
+  // V == 8 (used only when no chunk straddles an edge, so nvalid is 0 or 8):
+  // one 16-byte load whose aligned bytes all lie inside the matrix, or of the
+  // zero chunk.  Only the address is selected and the data is left untouched
+  // until it is written to LDS, so no wait follows the load: a load under a
+  // divergent branch, or a select on its result, makes the compiler wait for
+  // it at once, and with it for every load issued before.
+  // V == 1: eight 2-byte loads at immediate offsets from one address for a
+  // whole chunk; a chunk cut by an edge loads its valid elements one by one.
+  // (Selecting eight addresses instead measured slower: the address
+  // arithmetic per element outweighs the waits it avoids, which only edge
+  // chunks pay.)
+  static __device__ __forceinline__ void load8(Chunk8& c, const uint16_t* p, int nvalid) {
+    c.w = *reinterpret_cast<const u32x4*>(nvalid > 0 ? p : kZeroChunk);
+  }
+  static __device__ __forceinline__ void load8(Chunk1& c, const uint16_t* p, int nvalid) {
     uint16_t e[8];
+    if (nvalid >= 8) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) e[q] = q < nvalid ? p[q] : uint16_t(0);
-    return pack8(e);
+      for (int q = 0; q < 8; ++q) e[q] = p[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e[q] = q < nvalid ? p[q] : uint16_t(0);
+    }
+    c.w = pack8(e);
   }
 
-  static __device__ __forceinline__ void load(Regs& r, const TiledArgs& g, int m0, int n0, int k0, int tid) {
+  static __device__ __forceinline__ void load(Regs& r, const TiledArgs& g, int m0, int n0, int64_t k0, int tid) {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
       const int row = idx >> 3, ch = idx & 7;
       const int64_t gm = m0 + row;
       const int64_t gk = k0 + ch * 8;
-      int nvalid = gm < g.M ? int(min<int64_t>(8, g.K - gk)) : 0;
-      r.a[j] = load8(g.A + gm * g.lda + gk, nvalid);
+      const int nvalid = gm < g.M ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
+      load8(r.a[j], g.A + gm * g.lda + gk, nvalid);
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -106,8 +130,8 @@ struct Tiled {
           const int row = idx >> 3, ch = idx & 7;
           const int64_t gn = n0 + row;
           const int64_t gk = k0 + ch * 8;
-          const int nvalid = gn < g.N ? int(min<int64_t>(8, g.K - gk)) : 0;
-          r.b[s][j][0] = load8(B + gn * g.ldb + gk, nvalid);
+          const int nvalid = gn < g.N ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
+          load8(r.b[s][j][0], B + gn * g.ldb + gk, nvalid);
         }
         continue;
       }
@@ -116,11 +140,11 @@ struct Tiled {
         const int idx = tid + NT * j;
         const int nb = idx % BN8, kb = idx / BN8;
         const int64_t gn = n0 + nb * 8;
-        const int nval = int(min<int64_t>(8, g.N - gn));
+        const int nval = int(max<int64_t>(0, min<int64_t>(8, g.N - gn)));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t gk = k0 + kb * 4 + q;
-          r.b[s][j][q] = load8(B + gk * g.ldb + gn, gk < g.K ? nval : 0);
+          load8(r.b[s][j][q], B + gk * g.ldb + gn, gk < g.K ? nval : 0);
         }
       }
     }
@@ -131,7 +155,7 @@ struct Tiled {
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
       const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4*>(stage + lds_off(row, ch * 8)) = r.a[j];
+      *reinterpret_cast<u32x4*>(stage + lds_off(row, ch * 8)) = packed(r.a[j]);
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -141,7 +165,7 @@ struct Tiled {
         for (int j = 0; j < B_CHUNKS; ++j) {
           const int idx = tid + NT * j;
           const int row = idx >> 3, ch = idx & 7;
-          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = r.b[s][j][0];
+          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = packed(r.b[s][j][0]);
         }
         continue;
       }
@@ -149,7 +173,7 @@ struct Tiled {
       for (int j = 0; j < B_BLOCKS; ++j) {
         const int idx = tid + NT * j;
         const int nb = idx % BN8, kb = idx / BN8;
-        const u32x4* q = r.b[s][j];
+        const u32x4 q[4] = {packed(r.b[s][j][0]), packed(r.b[s][j][1]), packed(r.b[s][j][2]), packed(r.b[s][j][3])};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           // columns 2p (low halves) and 2p+1 (high halves) of the 4 x 8 block
@@ -188,6 +212,16 @@ struct Tiled {
   }
 };
 
+// Workgroup barrier without a memory fence: this wave's LDS accesses are
+// complete (lgkmcnt(0)) but its global loads may stay in flight.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
@@ -209,23 +243,55 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) acc[t][i][j] = f32x16{};
 
+  // 64 x 64 tiles of a plain GEMM with 16-byte loads keep two register sets:
+  // block kt+2 is loaded while block kt is multiplied and block kt+1 (loaded
+  // one step earlier) is written to LDS, so every block has two steps to
+  // arrive.  Everything else keeps one set: block kt+1 is loaded while block
+  // kt is multiplied.  (Two sets would spill for gate/up and halve the
+  // workgroups per CU for 128 x 128 tiles, which measured slower on full
+  // grids; with 2-byte loads two blocks are more loads than a wave can keep
+  // counted in flight, 63.)  Loads and LDS writes happen on every step, also
+  // past the last block, where every element reads as zero and the stage
+  // written is never read again, so that neither sits under a branch and the
+  // compiler can count exactly which loads are still in flight.  The barriers
+  // carry no memory fence: a fence would also wait for the prefetch.
   const int nk = int((g.K + T::BK - 1) / T::BK);
-  typename T::Regs r;
-  if (nk > 0) {
+  if constexpr (V == 8 && BM == 64 && !GU) {
+    typename T::Regs r0, r1;
+    T::load(r0, g, m0, n0, 0, tid);
+    T::load(r1, g, m0, n0, T::BK, tid);
+    T::store(r0, lds, tid);
+    stage_barrier();
+    for (int kt = 0; kt < nk; kt += 2) {
+      // block kt in stage 0, block kt+1 in flight in r1
+      T::load(r0, g, m0, n0, int64_t(kt + 2) * T::BK, tid);
+      T::compute(lds, acc, wm, wn, lane);
+      T::store(r1, lds + T::STAGE, tid);
+      stage_barrier();
+      if (kt + 1 >= nk) break;
+      // block kt+1 in stage 1, block kt+2 in flight in r0
+      T::load(r1, g, m0, n0, int64_t(kt + 3) * T::BK, tid);
+      T::compute(lds + T::STAGE, acc, wm, wn, lane);
+      T::store(r0, lds, tid);
+      stage_barrier();
+    }
+  } else {
+    typename T::Regs r;
     T::load(r, g, m0, n0, 0, tid);
     T::store(r, lds, tid);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t* cur = lds + (kt & 1) * T::STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) T::load(r, g, m0, n0, (kt + 1) * T::BK, tid);
-    T::compute(cur, acc, wm, wn, lane);
-    if (more) T::store(r, lds + ((kt + 1) & 1) * T::STAGE, tid);
-    __syncthreads();
+    stage_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      T::load(r, g, m0, n0, int64_t(kt + 1) * T::BK, tid);
+      T::compute(lds + (kt & 1) * T::STAGE, acc, wm, wn, lane);
+      T::store(r, lds + ((kt + 1) & 1) * T::STAGE, tid);
+      stage_barrier();
+    }
   }
 
-  // Epilogue straight from the accumulator lane map.
+  // Epilogue straight from the accumulator lane map.  The 16 old values of a
+  // 32 x 32 block are all requested before the first is used, from clamped
+  // addresses (element 0 for positions outside C), so their latencies overlap;
+  // only the stores are predicated.
   typedef typename TO::storage St;
   const int lc = lane & 31, lr4 = (lane >> 5) * 4;
   // row reduction: per-lane partials of the 16 rows of each 32-row block
@@ -242,25 +308,41 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
     for (int j = 0; j < T::FN; ++j) {
       const int64_t col = n0 + wn * T::TN + j * 32 + lc;
       const int64_t rbase = m0 + wm * T::TM + i * 32 + lr4;
-      if (col >= g.N) continue;
+      int64_t idx[16];
+      bool ok[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = rbase + 8 * (e >> 2) + (e & 3);
-        if (row >= g.M) continue;
-        const int64_t idx = row * g.ldc + col;
-        if constexpr (GU) {
+        ok[e] = col < g.N && row < g.M;
+        idx[e] = row * g.ldc + col;
+      }
+      if constexpr (GU) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (!ok[e]) continue;
           if (g.act == 1) {
-            static_cast<St*>(g.C)[idx] = to_out<TO>(swiglu(acc[0][i][j][e], acc[1][i][j][e]));
+            static_cast<St*>(g.C)[idx[e]] = to_out<TO>(swiglu(acc[0][i][j][e], acc[1][i][j][e]));
           } else {
-            static_cast<St*>(g.C)[idx] = to_out<TO>(acc[0][i][j][e]);
-            static_cast<St*>(g.C2)[idx] = to_out<TO>(acc[1][i][j][e]);
+            static_cast<St*>(g.C)[idx[e]] = to_out<TO>(acc[0][i][j][e]);
+            static_cast<St*>(g.C2)[idx[e]] = to_out<TO>(acc[1][i][j][e]);
           }
-        } else {
-          St* C = static_cast<St*>(g.C);
-          float v = g.alpha * acc[0][i][j][e];
-          if (g.beta != 0.0f) v += g.beta * from_out<TO>(C[idx]);
-          C[idx] = to_out<TO>(v);
-          if (red != RED_NONE) part[i][e] = red_combine(red, part[i][e], v);
+        }
+      } else {
+        St* C = static_cast<St*>(g.C);
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = g.alpha * acc[0][i][j][e];
+        if (g.beta != 0.0f) {
+          St old[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) old[e] = C[ok[e] ? idx[e] : 0];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[e] += g.beta * from_out<TO>(old[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (ok[e]) C[idx[e]] = to_out<TO>(v[e]);
+          if (red != RED_NONE && ok[e]) part[i][e] = red_combine(red, part[i][e], v[e]);
         }
       }
     }

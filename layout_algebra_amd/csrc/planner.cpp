@@ -239,7 +239,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     fail(err, "unknown dtype");
     return GEMM_ERR_INVALID_ARG;
   }
-  if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR)) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
+  if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR | GEMM_FLAG_LARGE_TILES)) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
   if (d.batch < 1 || d.batch > 65535) { fail(err, "batch must be in 1..65535"); return GEMM_ERR_INVALID_ARG; }
   if (d.stride_a < 0 || d.stride_b < 0 || d.stride_c < 0) { fail(err, "batch strides must be >= 0"); return GEMM_ERR_INVALID_ARG; }
   if (d.batch > 1 && d.m > 0 && d.n > 0) {
@@ -272,7 +272,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   const bool many = d.batch > 1;
   const bool in16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && (!many || (d.stride_a % 8 == 0 && d.stride_b % 8 == 0));
   const bool out16 = d.ldc % 8 == 0 && (!many || d.stride_c % 8 == 0);
-  p.vec = in16 ? 8 : 1;
+  // The general kernel stages 8-element chunks along K (A, K-major B) or N
+  // (N-contiguous B) with one 16-byte load each; it does so only when every
+  // chunk lies wholly inside or wholly outside the matrix, so that no load
+  // reaches past a row's last element.
+  const bool chunks_whole = d.k % 8 == 0 && (kmajor || d.n % 8 == 0);
+  p.vec = in16 && chunks_whole ? 8 : 1;
   p.align_bytes = 2 * p.vec;
 
   // Kernel choice: the full-tile direct-load kernels when every tile is whole
@@ -288,7 +293,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // per-lane source offsets of the direct loads are 32-bit byte offsets
     const int64_t b_rows = kmajor ? fs.bn : fs.bk;   // rows of B one block spans in memory
     const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
+    const bool large = (d.flags & GEMM_FLAG_LARGE_TILES) != 0;
     if (whole && rows16 && off32) p.kid = fk;
+    // Fewer than 32 full-tile workgroups leave most CUs idle: 64 x 64 tiles of
+    // the general kernel give 16 times as many and finish sooner (measured at
+    // 1 to 24 workgroups; from 64 on the full-tile kernel is faster).
+    if (!large && p.kid == fk && (d.m / fs.bm) * (d.n / fs.bn) * d.batch < 32) p.kid = lak::KID_TILED_64;
     // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
     const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
     const bool skinny_fit = !p.gate_up && !kmajor && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
@@ -296,11 +306,13 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
     if (skinny_fit) p.kid = lak::KID_SKINNY_16;
-    // The general kernel on a grid that leaves most CUs idle (fewer than 128 workgroups of
-    // 128 x 128, e.g. 104 at 1000 x 1537): 64 x 64 tiles give four times as many.
-    if (p.kid == lak::KID_TILED_128) {
+    // The general kernel: 64 x 64 tiles (two register sets of prefetch with
+    // 16-byte loads) measured faster than 128 x 128 at every size with 16-byte
+    // loads but 4000 x 4000 x 1000 (3 % slower), and with 2-byte loads up to
+    // grids of about 400 workgroups of 128 x 128 (e.g. 104 at 1000 x 1537).
+    if (!large && p.kid == lak::KID_TILED_128) {
       const int64_t wg128 = ((d.m + 127) / 128) * ((d.n + 127) / 128) * d.batch;
-      if (wg128 < 128) p.kid = lak::KID_TILED_64;
+      if (p.vec == 8 || wg128 < 384) p.kid = lak::KID_TILED_64;
     }
   }
   p.shape = lak::kernel_shape(p.kid);

@@ -147,6 +147,35 @@ def test_invalid_requests_are_rejected():
     assert e.value.name == "GEMM_ERR_UNSUPPORTED"
 
 
+def test_small_grids_take_64x64_tiles_unless_pinned():
+    """Kernel choice by grid size: a grid that would leave most of the 256 CUs idle moves to
+    64 x 64 tiles of the general kernel; GEMM_FLAG_LARGE_TILES keeps the largest tile."""
+    def kern(m, n, k, t=la.BF16, **kw):
+        return la.gemm_plan(m, n, k, t, la.F32, **kw).describe()
+    # full tiles: below 32 workgroups of 256 x 256 (256^3: 1, 1024 x 1536: 24), from 32 on kept
+    for shape in ((256, 256, 256), (1024, 1536, 1024)):
+        assert kern(*shape)["kernel"].startswith("tiled_64x64"), shape
+        assert kern(*shape, large_tiles=True)["kernel"].startswith("fast_256x256"), shape
+    assert kern(2048, 1024, 512)["kernel"].startswith("fast_256x256")          # 32 workgroups
+    assert kern(256, 256, 256, batch=32)["kernel"].startswith("fast_256x256")  # batch counts
+    assert kern(512, 512, 128, gate_up=True)["kernel"].startswith("tiled_64x64")
+    # general kernel with 16-byte loads: 64 x 64 at any grid
+    d = kern(4000, 4000, 1000)
+    assert d["kernel"].startswith("tiled_64x64") and d["vec_elems"] == 8
+    assert kern(4000, 4000, 1000, large_tiles=True)["kernel"].startswith("tiled_128x128")
+    # 2-byte loads: 128 x 128 from 384 of its workgroups on (2000 x 3074: 400), 64 x 64 below
+    d = kern(2000, 3074, 999, la.F16)
+    assert d["kernel"].startswith("tiled_128x128") and d["vec_elems"] == 1
+    assert kern(1536, 1537, 999, la.F16)["kernel"].startswith("tiled_64x64")
+    # a chunk of 8 that would straddle the K (or N) edge narrows the loads to 2 bytes
+    assert kern(512, 512, 1000)["vec_elems"] == 8
+    assert kern(512, 512, 1001)["vec_elems"] == 1 and kern(512, 512, 1001)["align_bytes"] == 2
+    assert kern(512, 516, 1000)["vec_elems"] == 1
+    assert kern(512, 516, 1000, b_kmajor=True)["vec_elems"] == 8
+    # the flag is a known bit
+    assert la.FLAG_LARGE_TILES == 0x4
+
+
 def test_batch_descriptor_is_validated():
     """Batch count and strides: a batch of independent matrices, each addressed by a
     third origin coordinate (Tylo.jl, "TMA and Hopper WGMMA", section "The same
@@ -164,7 +193,7 @@ def test_batch_descriptor_is_validated():
     d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=2, stride_a=256 * 256 + 4).describe()
     assert d["kernel"].startswith("tiled") and d["align_bytes"] == 2
     # the same stride is ignored for a single matrix
-    d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=1, stride_a=256 * 256 + 4).describe()
+    d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=1, stride_a=256 * 256 + 4, large_tiles=True).describe()
     assert d["kernel"].startswith("fast_")
     d = la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=2, stride_c=256 * 256 + 4).describe()
     assert d["kernel"].startswith("tiled") and d["align_bytes"] == 16 and d["out_align_bytes"] == 2

@@ -57,7 +57,8 @@ def test_batched_gemm(case):
     fa, A, sa = strided(a, pa)
     fb, B, sb = strided(b, pb)
     fc, C, sc = strided(c, pc)
-    plan = la.gemm_plan(M, N, K, CODE[ik], CODE[ok], batch=batch, stride_a=sa, stride_b=sb, stride_c=sc)
+    plan = la.gemm_plan(M, N, K, CODE[ik], CODE[ok], batch=batch, stride_a=sa, stride_b=sb, stride_c=sc,
+                        large_tiles=expect.startswith("fast"))
     assert plan.describe()["kernel"].startswith(expect), plan.describe()["kernel"]
     la.gemm_run(plan, A, B, C, 0.5, 1.5)
     torch.cuda.synchronize()
@@ -78,7 +79,7 @@ def test_batched_broadcast_B(shape):
     A = a.to(DEV)
     B = b.to(DEV).unsqueeze(0).expand(batch, K, N)
     C = torch.full((batch, M, N), float("nan"), dtype=torch.float32, device=DEV)
-    plan = la.gemm_plan(M, N, K, la.BF16, la.F32, batch=batch, stride_b=0)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.F32, batch=batch, stride_b=0, large_tiles=M == 256)
     la.gemm_run(plan, A, B, C, 1.0, 0.0)
     torch.cuda.synchronize()
     got = C.cpu()
@@ -92,7 +93,7 @@ def test_batched_bkmajor():
     b = synth.normal((batch, K, N), 312, "bf16", 0.5)
     bt = b.transpose(1, 2).contiguous()
     fb, B, sb = strided(bt, 24)
-    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, b_kmajor=True, batch=batch, stride_b=sb)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, b_kmajor=True, batch=batch, stride_b=sb, large_tiles=True)
     assert plan.describe()["kernel"].startswith("fast_bkmajor_")
     C = torch.full((batch, M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     la.gemm_run(plan, a.to(DEV), B, C, 1.0, 0.0)
@@ -109,7 +110,7 @@ def test_batched_gate_up_and_swiglu(shape):
     x = synth.normal((batch, M, K), 321, "bf16")
     wg = synth.normal((batch, K, N), 322, "bf16", 0.3)
     wu = synth.normal((batch, K, N), 323, "bf16", 0.3)
-    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, batch=batch)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, batch=batch, large_tiles=M == 256)
     X, Wg, Wu = x.to(DEV), wg.to(DEV), wu.to(DEV)
     G = torch.full((batch, M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     U = torch.full_like(G, float("nan"))

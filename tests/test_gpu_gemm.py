@@ -19,13 +19,13 @@ DEV = "cuda:0"
 CODE = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
 
 
-def run_gemm(a, b, out_kind, alpha=1.0, beta=0.0, c=None, b_kmajor=False, expect=None):
+def run_gemm(a, b, out_kind, alpha=1.0, beta=0.0, c=None, b_kmajor=False, expect=None, large_tiles=False):
     """a [M,K], b [K,N] CPU tensors (b is handed to the GPU as [N,K] when b_kmajor);
-    returns the GPU result on the CPU."""
+    returns the GPU result on the CPU.  large_tiles pins the largest tile (GEMM_FLAG_LARGE_TILES)."""
     M, K = a.shape
     N = b.shape[1]
     in_kind = "bf16" if a.dtype == torch.bfloat16 else "f16"
-    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], b_kmajor=b_kmajor)
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], b_kmajor=b_kmajor, large_tiles=large_tiles)
     if expect is not None:
         assert plan.describe()["kernel"].startswith(expect), plan.describe()["kernel"]
     A = a.to(DEV)
@@ -109,17 +109,41 @@ def test_shapes_and_types(shape, in_kind, out_kind):
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
 @pytest.mark.parametrize("out_kind", ["f32", "bf16"])
 def test_general_kernel_both_tile_sizes(in_kind, out_kind):
-    """Ragged shapes on either side of the general kernel's tile switch: fewer than 128 workgroups
-    of 128 x 128 take 64 x 64 tiles (1000 x 1537: 400 of them), more keep 128 x 128 (1536 x 1537:
-    156); alpha, beta and an existing C, every element against the oracle."""
-    for (M, N, K), kernel in (((1000, 1537, 999), "tiled_64x64"), ((1536, 1537, 999), "tiled_128x128")):
+    """Both tile sizes of the general kernel on ragged shapes: 64 x 64 as planned for 1000 x 1537
+    (400 workgroups), 128 x 128 pinned with GEMM_FLAG_LARGE_TILES for 1536 x 1537 (156); alpha,
+    beta and an existing C, every element against the oracle."""
+    for (M, N, K), kernel, large in (((1000, 1537, 999), "tiled_64x64", False),
+                                     ((1536, 1537, 999), "tiled_128x128", True)):
         seed = M + N + K
         a = synth.uniform((M, K), seed, in_kind)
         b = synth.uniform((K, N), seed + 1, in_kind)
         c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
-        got = run_gemm(a, b, out_kind, 1.5, -0.5, c, expect=kernel)
+        got = run_gemm(a, b, out_kind, 1.5, -0.5, c, expect=kernel, large_tiles=large)
         ref = oracle_gemm(a, b, in_kind, 1.5, -0.5, c.to(torch.float32))
         assert_close(got, ref, K, a, b, out_kind, "%s %dx%dx%d" % (kernel, M, N, K))
+
+
+PREFETCH_SHAPES = [(200, 136, 64), (130, 72, 128), (64, 64, 192), (100, 200, 1000), (96, 96, 8), (65, 130, 320),
+                   (70, 90, 999), (129, 67, 257)]
+
+
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", PREFETCH_SHAPES, ids=[str(s) for s in PREFETCH_SHAPES])
+def test_general_kernel_prefetch_depths(shape, out_kind):
+    """64 x 64 tiles of the general kernel over 1 to 16 K blocks, even and odd counts, ragged M and
+    N edges and a K tail: the two-register-set schedule with 16-byte loads (K and N multiples of
+    8) and the one-set schedule with 2-byte loads (the others), every element against the oracle."""
+    M, N, K = shape
+    seed = 3 * M + 5 * N + K
+    a = synth.uniform((M, K), seed, "bf16")
+    b = synth.uniform((K, N), seed + 1, "bf16")
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    d = la.gemm_plan(M, N, K, la.BF16, CODE[out_kind]).describe()
+    assert d["kernel"].startswith("tiled_64x64"), d["kernel"]
+    assert d["vec_elems"] == (8 if K % 8 == 0 and N % 8 == 0 else 1)
+    got = run_gemm(a, b, out_kind, -0.75, 1.5, c, expect="tiled_64x64")
+    ref = oracle_gemm(a, b, "bf16", -0.75, 1.5, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "prefetch %s" % (shape,))
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
@@ -320,7 +344,8 @@ def test_lds_image_matches_planner(case):
     a = synth.uniform((M, K), 21, kind)
     b = synth.uniform((K, N), 22, kind)
     b2 = synth.uniform((K, N), 23, kind) if gu else None
-    plan = la.gemm_plan(M, N, K, CODE[kind], la.F32, gate_up=gu, b_kmajor=km)
+    # the full-tile and 128 x 128 cases are small grids: pin their kernels with the large-tile flag
+    plan = la.gemm_plan(M, N, K, CODE[kind], la.F32, gate_up=gu, b_kmajor=km, large_tiles=not prefix.startswith("tiled_64"))
     d = la.gemm_plan_describe(plan)
     assert d["kernel"].startswith(prefix), d["kernel"]
     bm, bn, bk = d["tile"]
@@ -342,25 +367,30 @@ FAST_SHAPES = [(256, 256, 64), (512, 768, 320), (768, 512, 1024), (256, 1024, 40
 @pytest.mark.parametrize("shape", FAST_SHAPES, ids=[str(s) for s in FAST_SHAPES])
 def test_fast_kernel_shapes(shape, in_kind, out_kind):
     M, N, K = shape
-    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind])
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], large_tiles=True)
     assert plan.describe()["kernel"].startswith("fast_")
     seed = M + 3 * N + 7 * K
     a = synth.normal((M, K), seed, in_kind)
     b = synth.normal((K, N), seed + 1, in_kind, 0.5)
     c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
-    got = run_gemm(a, b, out_kind, -1.25, 0.5, c)
+    got = run_gemm(a, b, out_kind, -1.25, 0.5, c, expect="fast_", large_tiles=True)
     ref = oracle_gemm(a, b, in_kind, -1.25, 0.5, c.to(torch.float32))
     assert_close(got, ref, K, a, b, out_kind, "fast %s" % (shape,))
 
 
+@pytest.mark.parametrize("large", [True, False], ids=["large_tiles", "planned"])
 @pytest.mark.parametrize("shape", [(512, 256, 192), (300, 200, 100), (256, 384, 64)],
                          ids=["fast", "tiled_edges", "fast_min_k"])
-def test_gate_up_small(shape):
+def test_gate_up_small(shape, large):
+    """Pinned to the largest tiles (full-tile gate/up kernel, general 128 x 128) and as planned
+    (64 x 64 tiles for these small grids)."""
     M, N, K = shape
     x = synth.normal((M, K), 31, "bf16")
     wg = synth.normal((K, N), 32, "bf16", 0.3)
     wu = synth.normal((K, N), 33, "bf16", 0.3)
-    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, large_tiles=large)
+    want = ("fast_gate_up_" if M % 256 == 0 else "tiled_128x128") if large else "tiled_64x64"
+    assert plan.describe()["kernel"].startswith(want), plan.describe()["kernel"]
     G = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     U = torch.full_like(G, float("nan"))
     la.gemm_gate_up_run(plan, x.to(DEV), wg.to(DEV), wu.to(DEV), G, U)
@@ -373,14 +403,14 @@ def test_fast_kernel_identity_is_exact():
     K = 512
     a = synth.uniform((256, K), 41, "bf16")
     eye = torch.eye(K, dtype=torch.bfloat16)
-    plan = la.gemm_plan(256, K, K, la.BF16, la.F32)
+    plan = la.gemm_plan(256, K, K, la.BF16, la.F32, large_tiles=True)
     assert plan.describe()["kernel"].startswith("fast_")
-    got = run_gemm(a, eye, "f32")
+    got = run_gemm(a, eye, "f32", expect="fast_", large_tiles=True)
     assert torch.equal(got, a.to(torch.float32))
     perm = torch.randperm(K, generator=torch.Generator().manual_seed(42))
     P = torch.zeros((K, K), dtype=torch.bfloat16)
     P[perm, torch.arange(K)] = 1
-    assert torch.equal(run_gemm(a, P, "bf16"), a[:, perm])
+    assert torch.equal(run_gemm(a, P, "bf16", expect="fast_", large_tiles=True), a[:, perm])
 
 
 SKINNY_SHAPES = [(16, 128, 128), (1, 256, 256), (7, 384, 1024), (16, 1024, 2048), (13, 128, 8192)]
@@ -425,7 +455,7 @@ def test_gate_up_swiglu(shape):
         wg = synth.normal((K, N), 72, "bf16", 0.3)
         wu = synth.normal((K, N), 73, "bf16", 0.3)
         rows = list(range(M))
-    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, large_tiles=(M, N, K) == (512, 256, 192))
     H = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     la.gemm_gate_up_swiglu_run(plan, x.to(DEV), wg.to(DEV), wu.to(DEV), H)
     torch.cuda.synchronize()
@@ -449,7 +479,7 @@ def test_bkmajor_shapes(case, in_kind, out_kind):
     a = synth.normal((M, K), seed, in_kind)
     b = synth.normal((K, N), seed + 1, in_kind, 0.5)
     c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
-    got = run_gemm(a, b, out_kind, 0.5, 1.5, c, b_kmajor=True, expect=expect)
+    got = run_gemm(a, b, out_kind, 0.5, 1.5, c, b_kmajor=True, expect=expect, large_tiles=expect.startswith("fast"))
     ref = oracle_gemm(a, b, in_kind, 0.5, 1.5, c.to(torch.float32))
     assert_close(got, ref, K, a, b, out_kind, "K-major B %s" % ((M, N, K),))
 
@@ -460,7 +490,7 @@ def test_bkmajor_permutation_is_exact():
     perm = torch.randperm(K, generator=torch.Generator().manual_seed(82))
     P = torch.zeros((K, K), dtype=torch.bfloat16)
     P[perm, torch.arange(K)] = 1
-    got = run_gemm(a, P, "bf16", b_kmajor=True, expect="fast_bkmajor_")
+    got = run_gemm(a, P, "bf16", b_kmajor=True, expect="fast_bkmajor_", large_tiles=True)
     assert torch.equal(got, a[:, perm])
 
 
@@ -470,7 +500,7 @@ def test_gate_up_swiglu_bkmajor(shape):
     x = synth.normal((M, K), 97, "bf16")
     wg = synth.normal((K, N), 98, "bf16", 0.3)
     wu = synth.normal((K, N), 99, "bf16", 0.3)
-    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, b_kmajor=True)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, b_kmajor=True, large_tiles=(M, N, K) == (512, 256, 192))
     H = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     la.gemm_gate_up_swiglu_run(plan, x.to(DEV), wg.t().contiguous().to(DEV), wu.t().contiguous().to(DEV), H)
     torch.cuda.synchronize()
@@ -485,7 +515,7 @@ def test_gate_up_bkmajor(shape):
     x = synth.normal((M, K), 91, "bf16")
     wg = synth.normal((K, N), 92, "bf16", 0.3)
     wu = synth.normal((K, N), 93, "bf16", 0.3)
-    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, b_kmajor=True)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, b_kmajor=True, large_tiles=(M, N, K) == (512, 256, 192))
     G = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     U = torch.full_like(G, float("nan"))
     la.gemm_gate_up_run(plan, x.to(DEV), wg.t().contiguous().to(DEV), wu.t().contiguous().to(DEV), G, U)
