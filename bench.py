@@ -3,10 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one GEMM (one launch of the library's kernel) over inputs already
-resident in HBM.  Prints ONE JSON line with the throughput, the roofline of
-the kernel (achieved vs peak, from HIP events around every launch) and the
-oracle's CPU throughput on a bounded sample of the same workload, whose
-output also cross-checks the sampled GPU rows.
+resident in HBM.  The timed steps run as replays of a HIP graph that captured
+consecutive steps, so no host work sits between kernels (--launch eager: one
+library call per step).  Prints ONE JSON line with the throughput, the
+roofline of the kernel (achieved vs peak, from HIP events around the timed
+steps) and the oracle's CPU throughput on a bounded sample of the same
+workload, whose output also cross-checks the sampled GPU rows.
 
 Workloads (seeded synthetic inputs, see synth/):
   square4096  4096^3 bf16 -> bf16            (default; metric workload)
@@ -37,29 +39,39 @@ PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
 
-NORM_SOURCES = ("rms_norm.hip", "norm.hpp", "kernel_common.hpp", "launch.hpp")
-ATTN_SOURCES = ("attention.hip", "attention.hpp", "kernel_common.hpp", "launch.hpp")
-OWN_SOURCES = ("rms_norm.hip", "norm.hpp", "attention.hip", "attention.hpp", "probe.hip")
+SHARED_SOURCES = ("kernel_common.hpp", "launch.hpp")
+NORM_SOURCES = ("rms_norm.hip", "norm.hpp")
+ATTN_SOURCES = ("attention.hip", "attention.hpp")
+# GEMM kernel families by the prefix of the planned kernel's name
+GEMM_SOURCES = {"fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_": ("gemm_tiled.hip",),
+                "skinny_": ("gemm_skinny.hip",)}
+
+
+def workload_sources(workload):
+    """Kernel source files (csrc/) of what a workload runs: the row normalisation's, the
+    attention's, or those of the GEMM kernel family its plan selects, plus the shared headers."""
+    if workload in synth.NORM_WORKLOADS:
+        own = NORM_SOURCES
+    elif workload in synth.ATTN_WORKLOADS:
+        own = ATTN_SOURCES
+    else:
+        import layout_algebra_amd as la
+        w = synth.WORKLOADS[workload]
+        code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+        kernel = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up).describe()["kernel"]
+        own = next(v for k, v in GEMM_SOURCES.items() if kernel.startswith(k))
+    return tuple(sorted(own + SHARED_SOURCES))
 
 
 def kernel_source_hash(workload):
-    """sha1 (first 16 hex) over the HIP sources of the kernels a workload runs: the row
-    normalisation's own files, or every other kernel source for the GEMM workloads.
-    Identifies the kernels the traffic figures belong to."""
-    import glob
+    """sha1 (first 16 hex) over the HIP sources of the kernels a workload runs
+    (workload_sources).  Identifies the kernels the traffic figures belong to."""
     import hashlib
     csrc = os.path.join(ROOT, "layout_algebra_amd", "csrc")
-    files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp")))
-    if workload in synth.NORM_WORKLOADS:
-        files = [f for f in files if os.path.basename(f) in NORM_SOURCES]
-    elif workload in synth.ATTN_WORKLOADS:
-        files = [f for f in files if os.path.basename(f) in ATTN_SOURCES]
-    else:
-        files = [f for f in files if os.path.basename(f) not in OWN_SOURCES]
     h = hashlib.sha1()
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in workload_sources(workload):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -104,6 +116,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--b-kmajor", action="store_true",
                     help="hand B (or the gate/up weights) to the library as [N,K] (K contiguous)")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="timed steps as replays of a captured HIP graph (default), or one library call each")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed region, run a plain elementwise copy of 256 MiB (reads 256 MiB, writes "
                          "256 MiB) three times: the reference dispatch for scaling HBM byte counters")
@@ -170,16 +184,17 @@ def main():
     else:
         check = None
 
-    # Timed region: K steps back to back on the current stream, bracketed by a
-    # synchronize and a pair of HIP events.  Each step is one launch of the
-    # GEMM kernel, so the kernel's average duration is the region's time / K.
+    # Timed region: K steps back to back on the current stream (as replays of a
+    # captured HIP graph unless --launch eager), bracketed by a synchronize and
+    # a pair of HIP events.  Each step is one launch of the GEMM kernel, so the
+    # kernel's average duration is the region's time / K.
+    run = steps_runner(step, args.steps, args.launch)
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_all0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    run()
     t_all1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -224,6 +239,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "strong",
         "vs_baseline": None, "dtype": w.in_kind, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "out": w.out_kind,
+                   "launch": args.launch,
                    "b_order": "nk" if args.b_kmajor else "kn",
                    "alpha": w.alpha, "beta": w.beta, "gate_up": w.gate_up,
                    "kernel": plan.describe()["kernel"], "grid": plan.describe()["grid"]},
@@ -270,19 +286,50 @@ def copy_probe(dev):
     del src, dst
 
 
-def timed_steps(step, steps, warmup):
-    """Warm-up, then `steps` back-to-back steps between two HIP events on the current stream
-    (synchronised on both sides); then up to 20 single steps each between its own event pair."""
+def graph_chunk(steps):
+    """Steps per captured graph: the largest divisor of `steps` up to 50, an even one where there
+    is one (the skinny workload alternates two B buffers from step to step)."""
+    divs = [d for d in range(1, min(steps, 50) + 1) if steps % d == 0]
+    even = [d for d in divs if d % 2 == 0]
+    return max(even) if even else max(divs)
+
+
+def steps_runner(step, steps, launch):
+    """A function that runs `steps` consecutive steps on the current stream: one library call each
+    ("eager"), or steps / S replays of a HIP graph that captured S consecutive steps ("graph": no
+    host work between kernels, so short kernels run back to back).  Capture runs no kernel."""
+    if launch == "eager":
+        def run():
+            for i in range(steps):
+                step(i)
+        return run
+    chunk = graph_chunk(steps)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(chunk):
+            step(i)
+    torch.cuda.synchronize()
+
+    def run():
+        for _ in range(steps // chunk):
+            graph.replay()
+    return run
+
+
+def timed_steps(step, steps, warmup, launch="eager"):
+    """Warm-up (eager), then `steps` back-to-back steps (steps_runner) between two HIP events on the
+    current stream (synchronised on both sides); then up to 20 single steps each between its own
+    event pair."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    run = steps_runner(step, steps, launch)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record(stream)
-    for i in range(steps):
-        step(i)
+    run()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -310,7 +357,7 @@ def bench_norm(args, w):
     def step(i):
         la.la_rms_norm_run(X, G, Y, w.eps)
 
-    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup)
+    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup, args.launch)
     if args.copy_probe:
         copy_probe(dev)
     bytes_ = w.bytes()
@@ -320,7 +367,8 @@ def bench_norm(args, w):
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "D": w.D, "in": w.in_kind, "out": w.out_kind, "eps": w.eps},
+        "config": {"workload": w.name, "M": w.M, "D": w.D, "in": w.in_kind, "out": w.out_kind, "eps": w.eps,
+                   "launch": args.launch},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                      "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
                      "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
@@ -343,7 +391,7 @@ def bench_attention(args, w):
     def step(i):
         la.la_attention_run(Q, K, V, O, w.scale)
 
-    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup)
+    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup, args.launch)
     if args.copy_probe:
         copy_probe(dev)
     tflops = w.flops() / (ms * 1e-3) / 1e12
@@ -352,7 +400,7 @@ def bench_attention(args, w):
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
         "dtype": w.in_kind, "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "sq": w.sq, "sk": w.sk, "d": w.d, "in": w.in_kind,
+        "config": {"workload": w.name, "launch": args.launch, "batch": w.batch, "sq": w.sq, "sk": w.sk, "d": w.d, "in": w.in_kind,
                    "out": w.out_kind, "scale": w.scale},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[w.in_kind], "unit": "TFLOP/s",
                      "frac": tflops / PEAK_TFLOPS[w.in_kind],

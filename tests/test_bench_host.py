@@ -47,6 +47,12 @@ def test_traffic_lines_parse_and_follow_the_source_hash(tmp_path, monkeypatch):
     h = bench.kernel_source_hash("square4096")
     assert len(h) == 16 and h == bench.kernel_source_hash("gate_up")        # same kernel sources
     assert h != bench.kernel_source_hash("attention")
+    # each GEMM workload hashes the sources of the kernel family its plan selects
+    assert "gemm_fast.hpp" in bench.workload_sources("square4096")
+    assert "gemm_tiled.hip" not in bench.workload_sources("square4096")
+    assert "gemm_skinny.hip" in bench.workload_sources("skinny")
+    assert "gemm_tiled.hip" in bench.workload_sources("ragged")
+    assert bench.kernel_source_hash("ragged") != h != bench.kernel_source_hash("skinny")
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "traffic.md").write_text("# header\ntraffic square4096: 1234 %s\ntraffic skinny: 99 0000000000000000\n" % h)
