@@ -61,3 +61,14 @@ def test_traffic_lines_parse_and_follow_the_source_hash(tmp_path, monkeypatch):
     assert bench.measured_traffic("square4096") == 1234
     assert bench.measured_traffic("skinny") is None          # stale hash
     assert bench.measured_traffic("gate_up") is None         # no line
+
+
+def test_graph_chunks_divide_the_timed_steps():
+    """The timed steps replay a captured graph of S steps exactly steps / S times; S is even where
+    an even divisor exists, so the skinny workload's two B buffers keep alternating across replays."""
+    for steps in (1, 2, 5, 7, 20, 37, 100, 999, 1000):
+        s = bench.graph_chunk(steps)
+        assert 1 <= s <= 50 and steps % s == 0, steps
+        if any(d % 2 == 0 and steps % d == 0 for d in range(2, 51)):
+            assert s % 2 == 0, steps
+    assert bench.graph_chunk(1000) == 50 and bench.graph_chunk(999) == 37
