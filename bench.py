@@ -201,6 +201,18 @@ def main():
     total_ms = t_all0.elapsed_time(t_all1)
     ms_per_step = total_ms / args.steps
 
+    # Untimed: the timed launches left the output of their last step; one eager call of that
+    # same step must reproduce it bit for bit (only with beta = 0: otherwise every step
+    # rewrites C from its previous value).
+    replay_equal = None
+    if check is not None:
+        last = (graph_chunk(args.steps) if args.launch == "graph" else args.steps) - 1
+        replayed = result.detach().clone()
+        step(last)
+        torch.cuda.synchronize()
+        replay_equal = bool(torch.equal(replayed, result))
+        del replayed
+
     # Untimed: per-launch event pairs, for the spread of single-launch durations.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(min(args.steps, 20))]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(len(starts))]
@@ -249,6 +261,8 @@ def main():
         "pct_of_bf16_peak": 100.0 * value_tflops / PEAK_TFLOPS[w.in_kind],
     }
 
+    if replay_equal is not None:
+        line["timed_output_equals_eager"] = replay_equal
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit)
     print(json.dumps(line), flush=True)
