@@ -3,16 +3,21 @@
 // Structure (per workgroup, one BM x BN output tile):
 //   * K is walked in blocks of 64.  A block of A (BM x 64) and of B (64 x BN)
 //     is staged cooperatively by every thread, global -> registers -> LDS,
-//     with 16-byte vector loads where the alignment class allows and a zero
-//     for every element outside [0,M) x [0,K) or [0,K) x [0,N) (the
+//     in 8-element chunks: one 16-byte load each when no chunk can straddle an
+//     edge of the matrix, else 2-byte loads; a zero stands for every element
+//     outside [0,M) x [0,K) or [0,K) x [0,N) (the
 //     zero-filled edge semantics of the Tylo.jl page "TMA and Hopper WGMMA",
 //     section "Copy and completion").
 //   * In LDS both operands are stored K-contiguous, one 128-byte row of 64
-//     16-bit values per M row (A) or N column (B), under the swizzle
-//     Swizzle{3,3,3}: element (r, k) sits at 64 r + (k XOR 8 (r mod 8)), the
-//     128-byte row map of the Tylo.jl page "TMA and Hopper WGMMA" (section
-//     "The same storage contract on both sides").  B arrives N-contiguous, so
-//     each thread transposes a 4 (k) x 8 (n) block in registers while staging.
+//     16-bit values per M row (A) or N column (B), under Swizzle{3,3,4}:
+//     element (r, k) sits at 64 r + (k XOR 8 ((r >> 1) mod 8)).  The 128-byte
+//     row map of the Tylo.jl page "TMA and Hopper WGMMA" (section "The same
+//     storage contract on both sides") is Swizzle{3,3,3}, made for 32 banks;
+//     gfx950's LDS has 64, so rows r and r+8 of that map share banks and a
+//     16-byte fragment read of 16 rows is 2-way conflicted.  Taking the XOR
+//     from one row bit higher spreads those 16 rows over all 64 banks.  B
+//     arrives N-contiguous, so each thread transposes a 4 (k) x 8 (n) block in
+//     registers while staging.
 //   * Two LDS stages: while the MFMAs consume stage s the next block is
 //     loaded into registers and written to stage s^1; one workgroup barrier
 //     per block keeps every wave's reads of a stage ahead of its refill
@@ -62,7 +67,7 @@ struct Tiled {
   typedef typename std::conditional<V == 8, Chunk8, Chunk1>::type Chunk;
 
   // LDS element offset of (row, k) inside one operand block.
-  static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 3>(row * BK + k); }
+  static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 4>(row * BK + k); }
 
   struct Regs {
     Chunk a[A_CHUNKS];
