@@ -15,9 +15,15 @@
 //     storage contract on both sides") is Swizzle{3,3,3}, made for 32 banks;
 //     gfx950's LDS has 64, so rows r and r+8 of that map share banks and a
 //     16-byte fragment read of 16 rows is 2-way conflicted.  Taking the XOR
-//     from one row bit higher spreads those 16 rows over all 64 banks.  B
-//     arrives N-contiguous, so each thread transposes a 4 (k) x 8 (n) block in
-//     registers while staging.
+//     from one row bit higher spreads those 16 rows over all 64 banks.  This
+//     holds A, and B stored K-contiguous ([N, K]).  B stored N-contiguous
+//     ([K, N]) stays N-contiguous in LDS, one row of BN values per k, under
+//     Swizzle{1,5,2} (BN = 64) or Swizzle{2,5,2} (BN = 128), and its fragments
+//     are read with ds_read_b64_tr_b16, which transposes 4 x 16 blocks of
+//     16-bit values across each 16-lane group (lanes 4e..4e+3 address row e;
+//     lane i receives element i of rows 0..3): staging writes whole 16-byte
+//     row chunks and both the writes and the transposing reads are free of
+//     bank conflicts.
 //   * Two LDS stages: while the MFMAs consume stage s the next block is
 //     loaded into registers and written to stage s^1; one workgroup barrier
 //     per block keeps every wave's reads of a stage ahead of its refill
@@ -37,6 +43,9 @@
 #include "launch.hpp"
 
 namespace lak {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#define TILED_LDS __attribute__((address_space(3)))
 
 // Sixteen zero bytes in device memory: staging loads of elements outside the
 // matrix read from here, so the loaded registers need no masking afterwards.
@@ -58,20 +67,23 @@ struct Tiled {
   static constexpr int STAGE = A_ELEMS + NB * B_ELEMS;
   static constexpr int A_CHUNKS = BM * BK / 8 / NT;
   static constexpr int BN8 = BN / 8;
-  static constexpr int B_BLOCKS = (BK / 4) * BN8 / NT;
-  static constexpr int B_CHUNKS = BN * BK / 8 / NT;         // K-major B: 8-element K chunks per thread
+  static constexpr int B_CHUNKS = BN * BK / 8 / NT;         // 8-element B chunks per thread (along K or N)
+  static constexpr int BSW = BN == 64 ? 1 : 2;              // N-contiguous B block: Swizzle{BSW,5,2}
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_CHUNKS * NT * 8 == BM * BK, "A block must split evenly over threads");
-  static_assert(B_BLOCKS * NT == (BK / 4) * BN8, "B block must split evenly over threads");
+  static_assert(B_CHUNKS * NT * 8 == BN * BK, "B block must split evenly over threads");
+  static_assert(BN == 64 || BN == 128, "N-contiguous B swizzle is chosen for 64- and 128-wide blocks");
   static_assert(V == 8 || V == 1, "vector width");
   typedef typename std::conditional<V == 8, Chunk8, Chunk1>::type Chunk;
 
   // LDS element offset of (row, k) inside one operand block.
   static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 4>(row * BK + k); }
+  // LDS element offset of (k, n) inside an N-contiguous B block.
+  static __device__ __forceinline__ int b_off_n(int k, int n) { return swz<BSW, 5, 2>(k * BN + n); }
 
   struct Regs {
     Chunk a[A_CHUNKS];
-    Chunk b[NB][BKM ? B_CHUNKS : B_BLOCKS][BKM ? 1 : 4];
+    Chunk b[NB][B_CHUNKS];
   };
 
   static __device__ __forceinline__ u32x4 packed(const Chunk8& c) { return c.w; }
@@ -136,21 +148,19 @@ struct Tiled {
           const int64_t gn = n0 + row;
           const int64_t gk = k0 + ch * 8;
           const int nvalid = gn < g.N ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
-          load8(r.b[s][j][0], B + gn * g.ldb + gk, nvalid);
+          load8(r.b[s][j], B + gn * g.ldb + gk, nvalid);
         }
         continue;
       }
+      // B stored [K, N]: rows k of N values, 8-element chunks along N
 #pragma unroll
-      for (int j = 0; j < B_BLOCKS; ++j) {
+      for (int j = 0; j < B_CHUNKS; ++j) {
         const int idx = tid + NT * j;
-        const int nb = idx % BN8, kb = idx / BN8;
-        const int64_t gn = n0 + nb * 8;
-        const int nval = int(max<int64_t>(0, min<int64_t>(8, g.N - gn)));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t gk = k0 + kb * 4 + q;
-          load8(r.b[s][j][q], B + gk * g.ldb + gn, gk < g.K ? nval : 0);
-        }
+        const int kr = idx / BN8, nc = idx % BN8;
+        const int64_t gk = k0 + kr;
+        const int64_t gn = n0 + nc * 8;
+        const int nvalid = gk < g.K ? int(max<int64_t>(0, min<int64_t>(8, g.N - gn))) : 0;
+        load8(r.b[s][j], B + gk * g.ldb + gn, nvalid);
       }
     }
   }
@@ -170,32 +180,34 @@ struct Tiled {
         for (int j = 0; j < B_CHUNKS; ++j) {
           const int idx = tid + NT * j;
           const int row = idx >> 3, ch = idx & 7;
-          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = packed(r.b[s][j][0]);
+          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = packed(r.b[s][j]);
         }
         continue;
       }
 #pragma unroll
-      for (int j = 0; j < B_BLOCKS; ++j) {
+      for (int j = 0; j < B_CHUNKS; ++j) {
         const int idx = tid + NT * j;
-        const int nb = idx % BN8, kb = idx / BN8;
-        const u32x4 q[4] = {packed(r.b[s][j][0]), packed(r.b[s][j][1]), packed(r.b[s][j][2]), packed(r.b[s][j][3])};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          // columns 2p (low halves) and 2p+1 (high halves) of the 4 x 8 block
-          u32x2 lo, hi;
-          lo.x = (q[0][p] & 0xffffu) | (q[1][p] << 16);
-          lo.y = (q[2][p] & 0xffffu) | (q[3][p] << 16);
-          hi.x = (q[0][p] >> 16) | (q[1][p] & 0xffff0000u);
-          hi.y = (q[2][p] >> 16) | (q[3][p] & 0xffff0000u);
-          *reinterpret_cast<u32x2*>(dst + lds_off(nb * 8 + 2 * p, kb * 4)) = lo;
-          *reinterpret_cast<u32x2*>(dst + lds_off(nb * 8 + 2 * p + 1, kb * 4)) = hi;
-        }
+        const int kr = idx / BN8, nc = idx % BN8;
+        *reinterpret_cast<u32x4*>(dst + b_off_n(kr, nc * 8)) = packed(r.b[s][j]);
       }
     }
   }
 
+  // Four consecutive N values of one K row of an N-contiguous B block, transposed across the
+  // 16-lane group (see the file header).
+  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TILED_LDS i16x4_t*)(p));
+    return __builtin_bit_cast(u32x2, v);
+  }
+
   static __device__ __forceinline__ void compute(const uint16_t* stage, f32x16 (&acc)[NB][FM][FN], int wm, int wn, int lane) {
     const int lr = lane & 31, lk = (lane >> 5) * 8;
+    // N-contiguous B: lane l of 16-lane group g addresses row 8 (g / 2) + (l / 4) % 4 (+ 4 for the
+    // second read) at column 16 (g % 2) + 4 (l % 4) of each 32-column block, and receives the 8 K
+    // values of column l % 32 that the MFMA's B operand expects of lane l.
+    const int g4 = lane >> 4;
+    const int bn = wn * TN + 16 * (g4 & 1) + 4 * (lane & 3);
+    const int bk = 8 * (g4 >> 1) + ((lane >> 2) & 3);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       u32x4 a[FM], b[NB][FN];
@@ -206,7 +218,14 @@ struct Tiled {
       for (int t = 0; t < NB; ++t)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          b[t][j] = *reinterpret_cast<const u32x4*>(stage + A_ELEMS + t * B_ELEMS + lds_off(wn * TN + j * 32 + lr, s * 16 + lk));
+          if constexpr (BKM) {
+            b[t][j] = *reinterpret_cast<const u32x4*>(stage + A_ELEMS + t * B_ELEMS + lds_off(wn * TN + j * 32 + lr, s * 16 + lk));
+          } else {
+            const uint16_t* bs = stage + A_ELEMS + t * B_ELEMS;
+            const u32x2 lo = read_tr(bs + b_off_n(s * 16 + bk, bn + j * 32));
+            const u32x2 hi = read_tr(bs + b_off_n(s * 16 + bk + 4, bn + j * 32));
+            b[t][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+          }
 #pragma unroll
       for (int t = 0; t < NB; ++t)
 #pragma unroll

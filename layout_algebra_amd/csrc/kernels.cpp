@@ -12,9 +12,9 @@ static KernelShape fast_shape() {
 KernelShape kernel_shape(int kid) {
   switch (kid) {
     case KID_TILED_128:
-      return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2};
+      return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {2, 5, 2}};
     case KID_TILED_64:
-      return KernelShape{64, 64, 64, 2, 2, 1, 128, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2};
+      return KernelShape{64, 64, 64, 2, 2, 1, 128, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {1, 5, 2}};
     case KID_FAST_256: return fast_shape<CfgFast256>();
     case KID_FAST_GU: return fast_shape<CfgFastGU>();
     case KID_FAST_256_KM: return fast_shape<CfgFast256KM>();

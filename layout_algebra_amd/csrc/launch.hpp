@@ -105,6 +105,9 @@ struct KernelShape {
   int direct;              // 1: global -> LDS direct loads (whole 1 KB per wave instruction)
   int full_tiles_only;     // 1: M % bm == 0, N % bn == 0, K % bk == 0 required
   int stages;
+  int b_follows_storage = 0;   // 1: the B block keeps the operand's orientation (K-contiguous with sw_b
+                               //    for K-major B, N-contiguous with sw_bn otherwise)
+  int sw_bn[3] = {0, 0, 0};    // Swizzle{B,M,S} of an N-contiguous B block, element offsets over (bk,bn):(bn,1)
 };
 
 // Fill R[0, n) with the identity of `red` (0, -inf or +inf) on `stream`: a

@@ -59,25 +59,23 @@ bool check_copy_a(const gemm_plan_s& p, std::string* err) {
   return true;
 }
 
-// B block: thread t, slot j covers a 4 (k) x 8 (n) block, written as eight
-// 4-element K runs (one per n).
+// N-contiguous B in the general kernel: thread t, slot j covers (row k,
+// 8-element N chunk), written as one 16-byte vector.
 bool check_copy_b(const gemm_plan_s& p, const la::View& v, std::string* err) {
   const auto& s = p.shape;
-  const int blocks = (s.bk / 4) * (s.bn / 8);
-  if (blocks % s.threads) return fail(err, "B block does not split evenly over threads");
+  const int chunks = s.bk * s.bn / 8;
+  if (chunks % s.threads) return fail(err, "B block does not split evenly into 16-byte vectors per thread");
   std::vector<int> hits(static_cast<size_t>(s.bn) * s.bk, 0);
   for (int t = 0; t < s.threads; ++t) {
-    for (int j = 0; j < blocks / s.threads; ++j) {
+    for (int j = 0; j < chunks / s.threads; ++j) {
       const int idx = t + s.threads * j;
-      const int nb = idx % (s.bn / 8), kb = idx / (s.bn / 8);
-      for (int nn = 0; nn < 8; ++nn) {
-        const int64_t o0 = v.at({kb * 4, nb * 8 + nn});
-        if (o0 % 4) return fail(err, "B copy destination is not 8-byte aligned");
-        for (int q = 0; q < 4; ++q) {
-          const int64_t o = v.at({kb * 4 + q, nb * 8 + nn});
-          if (o != o0 + q) return fail(err, "B copy destination is not contiguous along K");
-          if (hits[o]++) return fail(err, "B copy plan writes an LDS element twice");
-        }
+      const int k = idx / (s.bn / 8), nc = idx % (s.bn / 8);
+      const int64_t o0 = v.at({k, nc * 8});
+      if (o0 % 8) return fail(err, "B copy destination is not 16-byte aligned");
+      for (int e = 0; e < 8; ++e) {
+        const int64_t o = v.at({k, nc * 8 + e});
+        if (o != o0 + e) return fail(err, "B copy destination is not contiguous along N");
+        if (hits[o]++) return fail(err, "B copy plan writes an LDS element twice");
       }
     }
   }
@@ -316,6 +314,11 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     }
   }
   p.shape = lak::kernel_shape(p.kid);
+  if (p.shape.b_follows_storage && !kmajor) {
+    // general kernel, B stored N-contiguous: the B block stays N-contiguous in LDS
+    p.shape.b_kmajor = 0;
+    for (int i = 0; i < 3; ++i) p.shape.sw_b[i] = p.shape.sw_bn[i];
+  }
   const auto& s = p.shape;
   // The fast kernels write C with 16-byte vectors, so C rows start on 16 bytes.
   const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
