@@ -12,6 +12,7 @@
 
 #include "../../include/la_gemm.h"
 #include "attention.hpp"
+#include "kernel_table.hpp"
 #include "launch.hpp"
 #include "layout.hpp"
 #include "norm.hpp"

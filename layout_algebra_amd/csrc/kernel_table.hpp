@@ -1,0 +1,33 @@
+// Host-side table of the GEMM kernels: tile shape, waves, MFMA block, LDS
+// maps and copy style of each kernel id, which the planner validates and
+// describes.  No kernel source includes this file.
+#pragma once
+
+#include "launch.hpp"
+
+namespace lak {
+
+struct KernelShape {
+  int bm, bn, bk;          // bn is per weight matrix
+  int nb;                  // weight matrices per launch (2 for gate/up)
+  int waves_m, waves_n;
+  int threads;
+  int mfma_m, mfma_n, mfma_k;
+  int sw_a[3];             // Swizzle{B,M,S} of the A block, element offsets over (bm,bk):(bk,1)
+  int sw_b[3];             // Swizzle{B,M,S} of a B block
+  int b_kmajor;            // 1: B block stored (bn,bk):(bk,1) (K contiguous); 0: (bk,bn):(bn,1)
+  int direct;              // 1: global -> LDS direct loads (whole 1 KB per wave instruction)
+  int full_tiles_only;     // 1: M % bm == 0, N % bn == 0, K % bk == 0 required
+  int stages;
+  int b_follows_storage = 0;   // 1: the B block keeps the operand's orientation (K-contiguous with sw_b
+                               //    for K-major B, N-contiguous with sw_bn otherwise)
+  int sw_bn[3] = {0, 0, 0};    // Swizzle{B,M,S} of an N-contiguous B block, element offsets over (bk,bn):(bn,1)
+};
+
+// Static description of each kernel id; the planner validates these maps.
+KernelShape kernel_shape(int kid);
+
+// LDS elements (16-bit) of one pipeline stage (one A block and one B block per weight).
+int64_t stage_elems(const KernelShape& s, bool gate_up);
+
+}  // namespace lak

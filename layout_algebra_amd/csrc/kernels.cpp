@@ -1,4 +1,5 @@
 // Kernel table and dispatch across kernel families (host code).
+#include "kernel_table.hpp"
 #include "launch.hpp"
 
 namespace lak {

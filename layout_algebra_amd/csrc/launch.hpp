@@ -93,23 +93,6 @@ struct CfgSkinny16 {
   static constexpr int BB = 3, BMb = 4, BS = 3;  // B: Swizzle{3,4,3} over 256-byte rows
 };
 
-struct KernelShape {
-  int bm, bn, bk;          // bn is per weight matrix
-  int nb;                  // weight matrices per launch (2 for gate/up)
-  int waves_m, waves_n;
-  int threads;
-  int mfma_m, mfma_n, mfma_k;
-  int sw_a[3];             // Swizzle{B,M,S} of the A block, element offsets over (bm,bk):(bk,1)
-  int sw_b[3];             // Swizzle{B,M,S} of a B block
-  int b_kmajor;            // 1: B block stored (bn,bk):(bk,1) (K contiguous); 0: (bk,bn):(bn,1)
-  int direct;              // 1: global -> LDS direct loads (whole 1 KB per wave instruction)
-  int full_tiles_only;     // 1: M % bm == 0, N % bn == 0, K % bk == 0 required
-  int stages;
-  int b_follows_storage = 0;   // 1: the B block keeps the operand's orientation (K-contiguous with sw_b
-                               //    for K-major B, N-contiguous with sw_bn otherwise)
-  int sw_bn[3] = {0, 0, 0};    // Swizzle{B,M,S} of an N-contiguous B block, element offsets over (bk,bn):(bn,1)
-};
-
 // Fill R[0, n) with the identity of `red` (0, -inf or +inf) on `stream`: a
 // kernel, not a memset, so that HIP graphs may capture it.
 hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
@@ -118,12 +101,6 @@ hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
 // issuing mfma_per_wave (a multiple of 16) MFMAs on fragments from `ops`.
 hipError_t launch_mfma_probe(const void* ops, int64_t n_frags, float* sink, int64_t workgroups, int64_t mfma_per_wave,
                              int in_kind, hipStream_t stream);
-
-// Static description of each kernel id; the planner validates these maps.
-KernelShape kernel_shape(int kid);
-
-// LDS elements (16-bit) of one pipeline stage (one A block and one B block per weight).
-int64_t stage_elems(const KernelShape& s, bool gate_up);
 
 // Enqueue a GEMM (or, with lds_image, the debug stage dump) on `stream`.
 hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,

@@ -4,6 +4,7 @@
 #include <string>
 
 #include "../../include/la_gemm.h"
+#include "kernel_table.hpp"
 #include "launch.hpp"
 #include "layout.hpp"
 
