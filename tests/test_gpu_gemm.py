@@ -123,6 +123,24 @@ def test_general_kernel_both_tile_sizes(in_kind, out_kind):
         assert_close(got, ref, K, a, b, out_kind, "%s %dx%dx%d" % (kernel, M, N, K))
 
 
+LONG_K = [((70, 100, 65536), False, "tiled_64x64"), ((256, 256, 65536), True, "fast_256x256"),
+          ((16, 128, 65536), False, "skinny_")]
+
+
+@pytest.mark.parametrize("case", LONG_K, ids=[c[2] for c in LONG_K])
+def test_long_k_accumulation(case):
+    """K = 65536 (the longest accumulation chains and K loops of the tests) through each kernel
+    family, zero-mean inputs as in the workloads; the oracle on all rows, or sampled rows of the
+    full-tile case."""
+    (M, N, K), large, kernel = case
+    a = synth.uniform((M, K), 1234 + M, "bf16")
+    b = synth.uniform((K, N), 4321 + N, "bf16")
+    got = run_gemm(a, b, "f32", expect=kernel, large_tiles=large)
+    rows = sample_rows(M, 6, 99) if M > 100 else list(range(M))
+    ref = oracle_gemm(a, b, "bf16", rows=rows)
+    assert_close(got[rows], ref, K, a, b, "f32", "long K %s" % ((M, N, K),))
+
+
 PREFETCH_SHAPES = [(200, 136, 64), (130, 72, 128), (64, 64, 192), (100, 200, 1000), (96, 96, 8), (65, 130, 320),
                    (70, 90, 999), (129, 67, 257)]
 
