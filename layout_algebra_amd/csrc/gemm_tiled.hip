@@ -3,8 +3,11 @@
 // Structure (per workgroup, one BM x BN output tile):
 //   * K is walked in blocks of 64.  A block of A (BM x 64) and of B (64 x BN)
 //     is staged cooperatively by every thread, global -> registers -> LDS,
-//     in 8-element chunks: one 16-byte load each when no chunk can straddle an
-//     edge of the matrix, else 2-byte loads; a zero stands for every element
+//     in 8-element chunks, one 16-byte load each (aligned when rows start on
+//     16 bytes and no chunk is cut by an edge; else at 2-byte alignment, a
+//     chunk cut by an edge loading the 8 elements that end at its last valid
+//     one and shifting them into place on their way to LDS), or 2-byte loads
+//     for rows of at most 8 elements; a zero stands for every element
 //     outside [0,M) x [0,K) or [0,K) x [0,N) (the
 //     zero-filled edge semantics of the Tylo.jl page "TMA and Hopper WGMMA",
 //     section "Copy and completion").
@@ -52,7 +55,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 __device__ __attribute__((aligned(16))) uint16_t kZeroChunk[8];
 
 // Eight 16-bit elements of one staging load, packed in pairs.
-struct Chunk8 { u32x4 w; };   // one 16-byte vector load
+struct Chunk8 { u32x4 w; };   // one aligned 16-byte load
+struct Chunk2 { u32x4 w; };   // one 16-byte load at 2-byte alignment (a cut chunk: shifted window)
 struct Chunk1 { u32x4 w; };   // eight 2-byte loads
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
@@ -73,21 +77,56 @@ struct Tiled {
   static_assert(A_CHUNKS * NT * 8 == BM * BK, "A block must split evenly over threads");
   static_assert(B_CHUNKS * NT * 8 == BN * BK, "B block must split evenly over threads");
   static_assert(BN == 64 || BN == 128, "N-contiguous B swizzle is chosen for 64- and 128-wide blocks");
-  static_assert(V == 8 || V == 1, "vector width");
-  typedef typename std::conditional<V == 8, Chunk8, Chunk1>::type Chunk;
+  static_assert(V == 8 || V == 2 || V == 1, "staging width");
+  typedef typename std::conditional<V == 8, Chunk8, typename std::conditional<V == 2, Chunk2, Chunk1>::type>::type Chunk;
 
   // LDS element offset of (row, k) inside one operand block.
   static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 4>(row * BK + k); }
   // LDS element offset of (k, n) inside an N-contiguous B block.
   static __device__ __forceinline__ int b_off_n(int k, int n) { return swz<BSW, 5, 2>(k * BN + n); }
 
+  // Staging registers of one K block.  sh (V == 2 only): 4 bits per chunk
+  // (slot j of A, then slot A_CHUNKS + s * B_CHUNKS + j of weight s), the
+  // places a chunk cut by an edge is shifted down on its way to LDS.
   struct Regs {
     Chunk a[A_CHUNKS];
     Chunk b[NB][B_CHUNKS];
+    uint64_t sh;
   };
+  static_assert(A_CHUNKS + NB * B_CHUNKS <= 16, "shift counts fit 4 bits per chunk in 64 bits");
 
-  static __device__ __forceinline__ u32x4 packed(const Chunk8& c) { return c.w; }
-  static __device__ __forceinline__ u32x4 packed(const Chunk1& c) { return c.w; }
+  // Element q of the result is element q + sh of w (0 past the end), sh in 1..7.
+  static __device__ __forceinline__ u32x4 shift_down(u32x4 w, int sh) {
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+    const int d = sh >> 1;
+    uint32_t o[5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v1 = i + 1 < 4 ? v[i + 1] : 0u, v2 = i + 2 < 4 ? v[i + 2] : 0u, v3 = i + 3 < 4 ? v[i + 3] : 0u;
+      o[i] = d == 0 ? v[i] : d == 1 ? v1 : d == 2 ? v2 : v3;
+    }
+    o[4] = 0u;
+    if (sh & 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (o[i] >> 16) | (o[i + 1] << 16);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+  }
+
+  // The chunk as it goes to LDS.  CUT (V == 2): the block may hold chunks cut by
+  // an edge (a uniform property of the block); only then do the lanes look at
+  // their shift counts, and only lanes holding a cut chunk branch off to shift
+  // it (the data has arrived by then).
+  template <bool CUT>
+  static __device__ __forceinline__ u32x4 packed(const Chunk8& c, uint64_t, int) { return c.w; }
+  template <bool CUT>
+  static __device__ __forceinline__ u32x4 packed(const Chunk1& c, uint64_t, int) { return c.w; }
+  template <bool CUT>
+  static __device__ __forceinline__ u32x4 packed(const Chunk2& c, uint64_t sh, int slot) {
+    if constexpr (!CUT) return c.w;
+    const int k = int(sh >> (4 * slot)) & 15;
+    return k == 0 ? c.w : shift_down(c.w, k);
+  }
 
   static __device__ __forceinline__ u32x4 pack8(const uint16_t* e) {
     u32x4 w;
@@ -100,21 +139,33 @@ struct Tiled {
 
   // Eight consecutive elements starting at p, of which the first `nvalid` (0..8)
   // lie inside the matrix; the others read as 0.
-  // V == 8 (used only when no chunk straddles an edge, so nvalid is 0 or 8):
+  // V == 8 (rows on 16 bytes, no chunk cut by an edge, so nvalid is 0 or 8):
   // one 16-byte load whose aligned bytes all lie inside the matrix, or of the
-  // zero chunk.  Only the address is selected and the data is left untouched
+  // zero chunk.
+  // V == 2 (any 2-byte alignment, rows of more than 8 elements): one 16-byte
+  // load at 2-byte alignment (gfx9 devices run with unaligned global access
+  // enabled; the compiler emits a single global_load_dwordx4): the chunk
+  // itself when whole, the zero chunk when empty, and for a chunk cut by an
+  // edge the 8 elements that end at its last valid one, which lie in the same
+  // row and are shifted down into place on their way to LDS; the shift count
+  // goes to sh.
+  // In both, only the address is selected and the data is left untouched
   // until it is written to LDS, so no wait follows the load: a load under a
   // divergent branch, or a select on its result, makes the compiler wait for
   // it at once, and with it for every load issued before.
-  // V == 1: eight 2-byte loads at immediate offsets from one address for a
-  // whole chunk; a chunk cut by an edge loads its valid elements one by one.
-  // (Selecting eight addresses instead measured slower: the address
-  // arithmetic per element outweighs the waits it avoids, which only edge
-  // chunks pay.)
-  static __device__ __forceinline__ void load8(Chunk8& c, const uint16_t* p, int nvalid) {
+  // V == 1 (rows of at most 8 elements): eight 2-byte loads at immediate
+  // offsets from one address for a whole chunk; a chunk cut by an edge loads
+  // its valid elements one by one.  (For longer rows this measured slower
+  // than V == 2: the per-chunk branch costs more than the loads.)
+  static __device__ __forceinline__ void load8(Chunk8& c, uint64_t&, int, const uint16_t* p, int nvalid) {
     c.w = *reinterpret_cast<const u32x4*>(nvalid > 0 ? p : kZeroChunk);
   }
-  static __device__ __forceinline__ void load8(Chunk1& c, const uint16_t* p, int nvalid) {
+  static __device__ __forceinline__ void load8(Chunk2& c, uint64_t& sh, int slot, const uint16_t* p, int nvalid) {
+    const int k = nvalid > 0 && nvalid < 8 ? 8 - nvalid : 0;
+    sh |= uint64_t(k) << (4 * slot);
+    __builtin_memcpy(&c.w, nvalid > 0 ? p - k : kZeroChunk, 16);
+  }
+  static __device__ __forceinline__ void load8(Chunk1& c, uint64_t&, int, const uint16_t* p, int nvalid) {
     uint16_t e[8];
     if (nvalid >= 8) {
 #pragma unroll
@@ -127,6 +178,7 @@ struct Tiled {
   }
 
   static __device__ __forceinline__ void load(Regs& r, const TiledArgs& g, int m0, int n0, int64_t k0, int tid) {
+    r.sh = 0;
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
@@ -134,7 +186,7 @@ struct Tiled {
       const int64_t gm = m0 + row;
       const int64_t gk = k0 + ch * 8;
       const int nvalid = gm < g.M ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
-      load8(r.a[j], g.A + gm * g.lda + gk, nvalid);
+      load8(r.a[j], r.sh, j, g.A + gm * g.lda + gk, nvalid);
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -148,7 +200,7 @@ struct Tiled {
           const int64_t gn = n0 + row;
           const int64_t gk = k0 + ch * 8;
           const int nvalid = gn < g.N ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
-          load8(r.b[s][j], B + gn * g.ldb + gk, nvalid);
+          load8(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j, B + gn * g.ldb + gk, nvalid);
         }
         continue;
       }
@@ -160,17 +212,29 @@ struct Tiled {
         const int64_t gk = k0 + kr;
         const int64_t gn = n0 + nc * 8;
         const int nvalid = gk < g.K ? int(max<int64_t>(0, min<int64_t>(8, g.N - gn))) : 0;
-        load8(r.b[s][j], B + gk * g.ldb + gn, nvalid);
+        load8(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j, B + gk * g.ldb + gn, nvalid);
       }
     }
   }
 
-  static __device__ __forceinline__ void store(const Regs& r, uint16_t* stage, int tid) {
+  // Write the staged block to LDS; `cut` (uniform, V == 2 only): the block may
+  // hold chunks cut by an edge.
+  static __device__ __forceinline__ void store(const Regs& r, uint16_t* stage, int tid, bool cut) {
+    if constexpr (V == 2) {
+      if (cut) {
+        store_as<true>(r, stage, tid);
+        return;
+      }
+    }
+    store_as<false>(r, stage, tid);
+  }
+  template <bool CUT>
+  static __device__ __forceinline__ void store_as(const Regs& r, uint16_t* stage, int tid) {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
       const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4*>(stage + lds_off(row, ch * 8)) = packed(r.a[j]);
+      *reinterpret_cast<u32x4*>(stage + lds_off(row, ch * 8)) = packed<CUT>(r.a[j], r.sh, j);
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -180,7 +244,7 @@ struct Tiled {
         for (int j = 0; j < B_CHUNKS; ++j) {
           const int idx = tid + NT * j;
           const int row = idx >> 3, ch = idx & 7;
-          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = packed(r.b[s][j]);
+          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = packed<CUT>(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j);
         }
         continue;
       }
@@ -188,7 +252,7 @@ struct Tiled {
       for (int j = 0; j < B_CHUNKS; ++j) {
         const int idx = tid + NT * j;
         const int kr = idx / BN8, nc = idx % BN8;
-        *reinterpret_cast<u32x4*>(dst + b_off_n(kr, nc * 8)) = packed(r.b[s][j]);
+        *reinterpret_cast<u32x4*>(dst + b_off_n(kr, nc * 8)) = packed<CUT>(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j);
       }
     }
   }
@@ -247,7 +311,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g_in) {
+__global__ void __launch_bounds__(WM * WN * 64, V == 2 ? 2 : 1) gemm_tiled_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * T::STAGE];
@@ -280,34 +344,39 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
   // compiler can count exactly which loads are still in flight.  The barriers
   // carry no memory fence: a fence would also wait for the prefetch.
   const int nk = int((g.K + T::BK - 1) / T::BK);
-  if constexpr (V == 8 && BM == 64 && !GU) {
+  // blocks that may hold chunks cut by an edge (V == 2): the last one when K is not a multiple
+  // of 8, and every block of the tile that holds the N edge of N-contiguous B when N is not
+  const bool n_cut = !BKM && g.N % 8 != 0 && int64_t(n0) + BN > g.N;
+  const bool k_cut = g.K % 8 != 0;
+  auto cut = [&](int blk) { return blk < nk && (n_cut || (k_cut && blk == nk - 1)); };
+  if constexpr (V != 1 && BM == 64 && !GU) {
     typename T::Regs r0, r1;
     T::load(r0, g, m0, n0, 0, tid);
     T::load(r1, g, m0, n0, T::BK, tid);
-    T::store(r0, lds, tid);
+    T::store(r0, lds, tid, cut(0));
     stage_barrier();
     for (int kt = 0; kt < nk; kt += 2) {
       // block kt in stage 0, block kt+1 in flight in r1
       T::load(r0, g, m0, n0, int64_t(kt + 2) * T::BK, tid);
       T::compute(lds, acc, wm, wn, lane);
-      T::store(r1, lds + T::STAGE, tid);
+      T::store(r1, lds + T::STAGE, tid, cut(kt + 1));
       stage_barrier();
       if (kt + 1 >= nk) break;
       // block kt+1 in stage 1, block kt+2 in flight in r0
       T::load(r1, g, m0, n0, int64_t(kt + 3) * T::BK, tid);
       T::compute(lds + T::STAGE, acc, wm, wn, lane);
-      T::store(r0, lds, tid);
+      T::store(r0, lds, tid, cut(kt + 2));
       stage_barrier();
     }
   } else {
     typename T::Regs r;
     T::load(r, g, m0, n0, 0, tid);
-    T::store(r, lds, tid);
+    T::store(r, lds, tid, cut(0));
     stage_barrier();
     for (int kt = 0; kt < nk; ++kt) {
       T::load(r, g, m0, n0, int64_t(kt + 1) * T::BK, tid);
       T::compute(lds + (kt & 1) * T::STAGE, acc, wm, wn, lane);
-      T::store(r, lds + ((kt + 1) & 1) * T::STAGE, tid);
+      T::store(r, lds + ((kt + 1) & 1) * T::STAGE, tid, cut(kt + 1));
       stage_barrier();
     }
   }
@@ -392,7 +461,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
   const int tid = threadIdx.x;
   typename T::Regs r;
   T::load(r, g, g.dbg_tm * BM, g.dbg_tn * BN, 0, tid);
-  T::store(r, lds, tid);
+  T::store(r, lds, tid, true);
   __syncthreads();
   for (int i = tid; i < T::STAGE; i += T::NT) g.dbg_out[i] = lds[i];
 }
@@ -419,6 +488,7 @@ hipError_t by_gu_km(bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t
 template <class TI, class TO, int BM, int BN, int WM, int WN>
 hipError_t by_vec_gu(int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (vec == 8) return by_gu_km<TI, TO, BM, BN, WM, WN, 8>(gu, km, a, grid, s, img);
+  if (vec == 2) return by_gu_km<TI, TO, BM, BN, WM, WN, 2>(gu, km, a, grid, s, img);
   if (vec == 1) return by_gu_km<TI, TO, BM, BN, WM, WN, 1>(gu, km, a, grid, s, img);
   return hipErrorInvalidValue;
 }

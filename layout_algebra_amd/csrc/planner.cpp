@@ -271,12 +271,16 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   const bool in16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && (!many || (d.stride_a % 8 == 0 && d.stride_b % 8 == 0));
   const bool out16 = d.ldc % 8 == 0 && (!many || d.stride_c % 8 == 0);
   // The general kernel stages 8-element chunks along K (A, K-major B) or N
-  // (N-contiguous B) with one 16-byte load each; it does so only when every
-  // chunk lies wholly inside or wholly outside the matrix, so that no load
-  // reaches past a row's last element.
+  // (N-contiguous B), one 16-byte load each: aligned (vec 8) when rows start
+  // on 16 bytes and no chunk is cut by an edge; else at 2-byte alignment
+  // (vec 2), a chunk cut by an edge loading the 8 elements that end at its
+  // last valid one, which stay inside the row only when the row holds more
+  // than 8 elements.  Shorter rows that are not whole chunks take 2-byte
+  // loads (vec 1).
   const bool chunks_whole = d.k % 8 == 0 && (kmajor || d.n % 8 == 0);
-  p.vec = in16 && chunks_whole ? 8 : 1;
-  p.align_bytes = 2 * p.vec;
+  const bool rows_fit = (d.k % 8 == 0 || d.k > 8) && (kmajor || d.n % 8 == 0 || d.n > 8);
+  p.vec = in16 && chunks_whole ? 8 : rows_fit ? 2 : 1;
+  p.align_bytes = p.vec == 8 ? 16 : 2;
 
   // Kernel choice: the full-tile direct-load kernels when every tile is whole
   // and every row starts on 16 bytes; otherwise the general kernel, which
@@ -310,7 +314,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // grids of about 400 workgroups of 128 x 128 (e.g. 104 at 1000 x 1537).
     if (!large && p.kid == lak::KID_TILED_128) {
       const int64_t wg128 = ((d.m + 127) / 128) * ((d.n + 127) / 128) * d.batch;
-      if (p.vec == 8 || wg128 < 384) p.kid = lak::KID_TILED_64;
+      if (p.vec != 1 || wg128 < 384) p.kid = lak::KID_TILED_64;
     }
   }
   p.shape = lak::kernel_shape(p.kid);
@@ -324,6 +328,8 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
                     p.kid == lak::KID_FAST_GU_KM;
   p.out_align_bytes = fast ? 16 : p.out_bytes;
+  // The direct-load kernels need 16-byte rows (their planning checked in16 above).
+  if (fast || p.kid == lak::KID_SKINNY_16) p.align_bytes = 16;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
   if (int64_t(p.tiles_m) * p.tiles_n > (int64_t{1} << 31) - 1) { fail(err, "too many tiles"); return GEMM_ERR_UNSUPPORTED; }

@@ -163,15 +163,21 @@ def test_small_grids_take_64x64_tiles_unless_pinned():
     d = kern(4000, 4000, 1000)
     assert d["kernel"].startswith("tiled_64x64") and d["vec_elems"] == 8
     assert kern(4000, 4000, 1000, large_tiles=True)["kernel"].startswith("tiled_128x128")
-    # 2-byte loads: 128 x 128 from 384 of its workgroups on (2000 x 3074: 400), 64 x 64 below
-    d = kern(2000, 3074, 999, la.F16)
+    # rows on 16 bytes with whole chunks: aligned 16-byte loads
+    assert kern(1000, 1536, 1024)["vec_elems"] == 8 and kern(1000, 1536, 1024)["align_bytes"] == 16
+    # ragged shapes keep 16-byte loads at 2-byte alignment (a chunk cut by an edge loads the 8
+    # elements ending at its last valid one)
+    for shape in ((2000, 3074, 999), (1536, 1537, 999), (512, 512, 1001), (512, 516, 1000)):
+        d = kern(*shape, la.F16)
+        assert d["kernel"].startswith("tiled_64x64") and d["vec_elems"] == 2 and d["align_bytes"] == 2, shape
+    # rows of at most 8 elements that are not whole chunks take 2-byte loads: 128 x 128 from 384 of its
+    # workgroups on (4000 x 4000: 1024), 64 x 64 below
+    d = kern(4000, 4000, 7)
     assert d["kernel"].startswith("tiled_128x128") and d["vec_elems"] == 1
-    assert kern(1536, 1537, 999, la.F16)["kernel"].startswith("tiled_64x64")
-    # a chunk of 8 that would straddle the K (or N) edge narrows the loads to 2 bytes
-    assert kern(512, 512, 1000)["vec_elems"] == 8
-    assert kern(512, 512, 1001)["vec_elems"] == 1 and kern(512, 512, 1001)["align_bytes"] == 2
-    assert kern(512, 516, 1000)["vec_elems"] == 1
-    assert kern(512, 516, 1000, b_kmajor=True)["vec_elems"] == 8
+    assert kern(1000, 1537, 7)["kernel"].startswith("tiled_64x64")
+    assert kern(512, 6, 1000)["vec_elems"] == 1
+    assert kern(512, 6, 1000, b_kmajor=True)["vec_elems"] == 8          # K-major B: chunks run along K
+    assert kern(512, 512, 8)["vec_elems"] == 8 and kern(512, 512, 9)["vec_elems"] == 2
     # the flag is a known bit
     assert la.FLAG_LARGE_TILES == 0x4
 
@@ -203,8 +209,16 @@ def test_run_argument_errors_are_caught_before_launch():
     lib = la.load()
     p = la.gemm_plan(64, 64, 64, la.BF16, la.F32)
     vp = ctypes.c_void_p
-    # misaligned A for a 16-byte alignment class: rejected on the host
-    rc = lib.gemm_run(p.handle, vp(0x1002), vp(0x2000), vp(0x3000), 1.0, 0.0, vp(0))
+    # misaligned A for the full-tile kernel's 16-byte alignment class: rejected on the host
+    pf = la.gemm_plan(256, 256, 64, la.BF16, la.F32, large_tiles=True)
+    assert pf.describe()["align_bytes"] == 16
+    rc = lib.gemm_run(pf.handle, vp(0x1002), vp(0x2000), vp(0x3000), 1.0, 0.0, vp(0))
+    assert la._lib.STATUS[rc] == "GEMM_ERR_ALIGNMENT"
+    # with 2-byte aligned rows the general kernel takes any element-aligned pointer, but not an odd
+    # byte address
+    p2 = la.gemm_plan(64, 64, 63, la.BF16, la.F32)
+    assert p2.describe()["align_bytes"] == 2
+    rc = lib.gemm_run(p2.handle, vp(0x1001), vp(0x2000), vp(0x3000), 1.0, 0.0, vp(0))
     assert la._lib.STATUS[rc] == "GEMM_ERR_ALIGNMENT"
     rc = lib.gemm_run(p.handle, vp(0x1000), vp(0), vp(0x3000), 1.0, 0.0, vp(0))
     assert la._lib.STATUS[rc] == "GEMM_ERR_NULL"

@@ -88,7 +88,7 @@ def test_gate_up_sampled_rows():
 
 
 SHAPES = [(1, 1, 1), (1, 7, 3), (33, 65, 17), (64, 64, 64), (127, 129, 65), (129, 257, 130),
-          (200, 72, 1000), (300, 300, 8), (5, 1000, 333), (257, 31, 64)]
+          (200, 72, 1000), (300, 300, 8), (5, 1000, 333), (257, 31, 64), (200, 300, 5), (300, 6, 200)]
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
@@ -148,9 +148,10 @@ PREFETCH_SHAPES = [(200, 136, 64), (130, 72, 128), (64, 64, 192), (100, 200, 100
 @pytest.mark.parametrize("out_kind", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", PREFETCH_SHAPES, ids=[str(s) for s in PREFETCH_SHAPES])
 def test_general_kernel_prefetch_depths(shape, out_kind):
-    """64 x 64 tiles of the general kernel over 1 to 16 K blocks, even and odd counts, ragged M and
-    N edges and a K tail: the two-register-set schedule with 16-byte loads (K and N multiples of
-    8) and the one-set schedule with 2-byte loads (the others), every element against the oracle."""
+    """64 x 64 tiles of the general kernel (two register sets, 16-byte loads) over 1 to 16 K blocks,
+    even and odd counts, ragged M and N edges and K tails, so that chunks cut by the K or N edge
+    load the 8 elements ending at their last valid one and shift into place; every element
+    against the oracle."""
     M, N, K = shape
     seed = 3 * M + 5 * N + K
     a = synth.uniform((M, K), seed, "bf16")
@@ -158,7 +159,7 @@ def test_general_kernel_prefetch_depths(shape, out_kind):
     c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
     d = la.gemm_plan(M, N, K, la.BF16, CODE[out_kind]).describe()
     assert d["kernel"].startswith("tiled_64x64"), d["kernel"]
-    assert d["vec_elems"] == (8 if K % 8 == 0 and N % 8 == 0 else 1)
+    assert d["vec_elems"] == (8 if K % 8 == 0 and N % 8 == 0 else 2)
     got = run_gemm(a, b, out_kind, -0.75, 1.5, c, expect="tiled_64x64")
     ref = oracle_gemm(a, b, "bf16", -0.75, 1.5, c.to(torch.float32))
     assert_close(got, ref, K, a, b, out_kind, "prefetch %s" % (shape,))
