@@ -118,6 +118,8 @@ def main():
                     help="hand B (or the gate/up weights) to the library as [N,K] (K contiguous)")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="timed steps as replays of a captured HIP graph (default), or one library call each")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock/power reading (amd-smi during untimed replays after the timed region)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed region, run a plain elementwise copy of 256 MiB (reads 256 MiB, writes "
                          "256 MiB) three times: the reference dispatch for scaling HBM byte counters")
@@ -222,6 +224,7 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    clock = clock_sample(run) if not args.no_clock else None
 
     if args.copy_probe:
         copy_probe(dev)
@@ -261,6 +264,9 @@ def main():
         "pct_of_bf16_peak": 100.0 * value_tflops / PEAK_TFLOPS[w.in_kind],
     }
 
+    line["clock"] = clock
+    if roof["bound"] == "mfma":
+        roof["at_measured_clock"] = at_clock(clock, roof["peak"], roof["achieved"])
     if replay_equal is not None:
         line["timed_output_equals_eager"] = replay_equal
     if not args.no_cpu_baseline:
@@ -300,6 +306,65 @@ def copy_probe(dev):
     del src, dst
 
 
+def clock_sample(run, seconds=1.5):
+    """GPU clock and power while the workload runs: `run` (a whole timed region's worth of steps)
+    is replayed, untimed, until amd-smi has been read twice from a child process (about
+    `seconds`).  Returns the median gfx clock over the chip's XCDs per reading, the socket power
+    and the maximum clock, or None when amd-smi is not there or reports nothing."""
+    import shutil
+    import subprocess
+    import threading
+    if shutil.which("amd-smi") is None:
+        return None
+    readings = []
+
+    def sample():
+        time.sleep(seconds / 3)
+        for _ in range(2):
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
+                                     capture_output=True, text=True, timeout=30).stdout
+                readings.append(json.loads(out[out.index("{"):]))
+            except Exception:
+                pass
+            time.sleep(seconds / 3)
+
+    t = threading.Thread(target=sample)
+    t.start()
+    while t.is_alive():
+        run()
+        torch.cuda.synchronize()
+    t.join()
+    clk, power, cmax = [], [], None
+    for r in readings:
+        try:
+            gpu = r["gpu_data"][0] if "gpu_data" in r else r[0]
+            gfx = [v for k, v in gpu["clock"].items() if k.startswith("gfx")]
+            vals = sorted(float(v["clk"]["value"]) for v in gfx if isinstance(v.get("clk", {}).get("value"), (int, float)))
+            if vals:
+                clk.append(vals[len(vals) // 2])
+            cmax = float(gfx[0]["max_clk"]["value"])
+            pw = gpu["power"]["socket_power"]["value"]
+            if isinstance(pw, (int, float)):
+                power.append(float(pw))
+        except Exception:
+            continue
+    if not clk:
+        return None
+    return {"gfx_mhz": clk, "max_mhz": cmax, "socket_power_w": power,
+            "method": "amd-smi metric during untimed replays of the timed steps, after the timed region"}
+
+
+def at_clock(clock, peak, achieved):
+    """For an MFMA-bound kernel: the nominal peak scaled to the clock measured while it ran, and
+    the achieved rate as a fraction of that (context beside roofline.frac, which stays nominal)."""
+    if not clock or not clock.get("max_mhz"):
+        return None
+    mhz = sorted(clock["gfx_mhz"])[len(clock["gfx_mhz"]) // 2]
+    p = peak * mhz / clock["max_mhz"]
+    return {"peak_tflops": p, "frac": achieved / p, "gfx_mhz": mhz}
+
+
 def graph_chunk(steps):
     """Steps per captured graph: the largest divisor of `steps` up to 50, an even one where there
     is one (the skinny workload alternates two B buffers from step to step)."""
@@ -330,7 +395,7 @@ def steps_runner(step, steps, launch):
     return run
 
 
-def timed_steps(step, steps, warmup, launch="eager"):
+def timed_steps(step, steps, warmup, launch="eager", clock=False):
     """Warm-up (eager), then `steps` back-to-back steps (steps_runner) between two HIP events on the
     current stream (synchronised on both sides); then up to 20 single steps each between its own
     event pair."""
@@ -356,6 +421,8 @@ def timed_steps(step, steps, warmup, launch="eager"):
         ends[i].record(stream)
     torch.cuda.synchronize()
     per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    if clock:
+        return ms, wall, per_launch, clock_sample(run)
     return ms, wall, per_launch
 
 
@@ -371,7 +438,7 @@ def bench_norm(args, w):
     def step(i):
         la.la_rms_norm_run(X, G, Y, w.eps)
 
-    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup, args.launch)
+    ms, wall, per_launch, clock = timed_steps(step, args.steps, args.warmup, args.launch, clock=not args.no_clock)
     if args.copy_probe:
         copy_probe(dev)
     bytes_ = w.bytes()
@@ -383,6 +450,7 @@ def bench_norm(args, w):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "D": w.D, "in": w.in_kind, "out": w.out_kind, "eps": w.eps,
                    "launch": args.launch},
+        "clock": clock,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                      "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
                      "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
@@ -405,7 +473,7 @@ def bench_attention(args, w):
     def step(i):
         la.la_attention_run(Q, K, V, O, w.scale)
 
-    ms, wall, per_launch = timed_steps(step, args.steps, args.warmup, args.launch)
+    ms, wall, per_launch, clock = timed_steps(step, args.steps, args.warmup, args.launch, clock=not args.no_clock)
     if args.copy_probe:
         copy_probe(dev)
     tflops = w.flops() / (ms * 1e-3) / 1e12
@@ -414,11 +482,13 @@ def bench_attention(args, w):
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
         "dtype": w.in_kind, "data": "synthetic",
+        "clock": clock,
         "config": {"workload": w.name, "launch": args.launch, "batch": w.batch, "sq": w.sq, "sk": w.sk, "d": w.d, "in": w.in_kind,
                    "out": w.out_kind, "scale": w.scale},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[w.in_kind], "unit": "TFLOP/s",
                      "frac": tflops / PEAK_TFLOPS[w.in_kind],
                      "mfma_ceiling": mfma_ceiling(dev, Q, w.flops(), tflops),
+                     "at_measured_clock": at_clock(clock, PEAK_TFLOPS[w.in_kind], tflops),
                      "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
                      "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
         "wall_s_timed": wall,

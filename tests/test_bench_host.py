@@ -72,3 +72,13 @@ def test_graph_chunks_divide_the_timed_steps():
         if any(d % 2 == 0 and steps % d == 0 for d in range(2, 51)):
             assert s % 2 == 0, steps
     assert bench.graph_chunk(1000) == 50 and bench.graph_chunk(999) == 37
+
+
+def test_peak_scaled_to_the_measured_clock():
+    """The clock-scaled peak is the nominal peak times median gfx clock / maximum clock."""
+    clock = {"gfx_mhz": [1600.0, 1630.0, 1700.0], "max_mhz": 2400.0, "socket_power_w": [1267.0]}
+    r = bench.at_clock(clock, 2516.6, 1239.0)
+    assert r["gfx_mhz"] == 1630.0
+    assert abs(r["peak_tflops"] - 2516.6 * 1630.0 / 2400.0) < 1e-9
+    assert abs(r["frac"] - 1239.0 / r["peak_tflops"]) < 1e-12
+    assert bench.at_clock(None, 2516.6, 1239.0) is None
