@@ -308,9 +308,11 @@ def copy_probe(dev):
 
 def clock_sample(run, seconds=1.5):
     """GPU clock and power while the workload runs: `run` (a whole timed region's worth of steps)
-    is replayed, untimed, until amd-smi has been read twice from a child process (about
-    `seconds`).  Returns the median gfx clock over the chip's XCDs per reading, the socket power
-    and the maximum clock, or None when amd-smi is not there or reports nothing."""
+    is replayed, untimed, until amd-smi has been read three times from a child process (about
+    `seconds`).  Returns the median gfx clock over the chip's XCDs per reading, the socket power,
+    the maximum clock, and `settled_mhz`: the median of the readings after the first (amd-smi's
+    first reading can still show the idle state from before the load began), or None when amd-smi
+    is not there or reports nothing."""
     import shutil
     import subprocess
     import threading
@@ -320,7 +322,7 @@ def clock_sample(run, seconds=1.5):
 
     def sample():
         time.sleep(seconds / 3)
-        for _ in range(2):
+        for _ in range(3):
             try:
                 out = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
                                      capture_output=True, text=True, timeout=30).stdout
@@ -351,7 +353,8 @@ def clock_sample(run, seconds=1.5):
             continue
     if not clk:
         return None
-    return {"gfx_mhz": clk, "max_mhz": cmax, "socket_power_w": power,
+    later = sorted(clk[1:] if len(clk) > 1 else clk)
+    return {"gfx_mhz": clk, "settled_mhz": later[len(later) // 2], "max_mhz": cmax, "socket_power_w": power,
             "method": "amd-smi metric during untimed replays of the timed steps, after the timed region"}
 
 
@@ -360,7 +363,7 @@ def at_clock(clock, peak, achieved):
     the achieved rate as a fraction of that (context beside roofline.frac, which stays nominal)."""
     if not clock or not clock.get("max_mhz"):
         return None
-    mhz = sorted(clock["gfx_mhz"])[len(clock["gfx_mhz"]) // 2]
+    mhz = clock["settled_mhz"]
     p = peak * mhz / clock["max_mhz"]
     return {"peak_tflops": p, "frac": achieved / p, "gfx_mhz": mhz}
 

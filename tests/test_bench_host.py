@@ -76,7 +76,7 @@ def test_graph_chunks_divide_the_timed_steps():
 
 def test_peak_scaled_to_the_measured_clock():
     """The clock-scaled peak is the nominal peak times median gfx clock / maximum clock."""
-    clock = {"gfx_mhz": [1600.0, 1630.0, 1700.0], "max_mhz": 2400.0, "socket_power_w": [1267.0]}
+    clock = {"gfx_mhz": [95.0, 1630.0, 1630.0], "settled_mhz": 1630.0, "max_mhz": 2400.0, "socket_power_w": [1267.0]}
     r = bench.at_clock(clock, 2516.6, 1239.0)
     assert r["gfx_mhz"] == 1630.0
     assert abs(r["peak_tflops"] - 2516.6 * 1630.0 / 2400.0) < 1e-9
