@@ -501,6 +501,18 @@ def bench_attention(args, w):
     print(json.dumps(line), flush=True)
 
 
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where there is none)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def blas_threads():
     """Threads numpy's BLAS runs its matrix products on."""
     try:
@@ -533,7 +545,7 @@ def cpu_baseline_attention(w, x, O, budget_s, gpu_value):
     dt = time.perf_counter() - t0
     value = 4.0 * R * w.sk * w.d / dt / 1e12
     base = {"value": value, "unit": "TFLOP/s", "cores": blas_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": "queries 0..%d of batch entry 0 against all %d keys, numpy binary64 (BLAS matmul), %.2f s"
                       % (R - 1, w.sk, dt),
             "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
@@ -569,7 +581,7 @@ def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):
     isz = 4 if w.in_kind == "f32" else 2
     osz = 4 if w.out_kind == "f32" else 2
     value = (R * w.D * (isz + osz) + w.D * isz) / dt / 1e9
-    base = {"value": value, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    base = {"value": value, "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": "rows 0..%d of %d (D=%d), numpy binary64, %.2f s per run, %d run(s)" % (R - 1, w.M, w.D, dt, reps),
             "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
     got = Y[:R].to("cpu", torch.float64).numpy()
@@ -604,7 +616,7 @@ def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):
         value = bytes_ / dt / 1e9
     else:
         value = flops / dt / 1e12
-    base = {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+    base = {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": "output rows 0..%d of %d (%d x %d outputs, K=%d%s), FP64 triple loop, %.2f s per run, %d run(s)"
                       % (R - 1, w.M, R, w.N, w.K, ", W_gate product only" if w.gate_up else "", dt, reps),
             "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
