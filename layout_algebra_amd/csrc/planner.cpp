@@ -4,10 +4,13 @@
 // the Tylo.jl page "Layouts, storage and ownership" requires in section "Swizzle
 // phase belongs to the allocation"):
 //   1. validate the descriptor (sizes, leading dimensions, dtypes, flags);
-//   2. derive the alignment class: 16-byte vectors only when every row start
-//      is 16-byte aligned, else element-wide accesses (Tylo.jl, section "Three
-//      representations, three addressing rules": vector width follows the
-//      declared alignment of pointer and strides);
+//   2. derive the alignment class, which the run checks pointers against:
+//      16 bytes when every row start is 16-byte aligned, else the element
+//      (Tylo.jl, section "Three representations, three addressing rules":
+//      accesses follow the declared alignment of pointer and strides).  The
+//      general kernel still moves 16 bytes per load for element-aligned rows
+//      longer than 8 elements, since gfx950 executes unaligned vector loads;
+//      only shorter rows fall back to element loads;
 //   3. choose a kernel and its tile grid;
 //   4. build each operand's LDS map as Swizzle o Layout in the operand's own
 //      mathematical coordinates (B in (K, N), section "Three representations,
@@ -284,7 +287,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
 
   // Kernel choice: the full-tile direct-load kernels when every tile is whole
   // and every row starts on 16 bytes; otherwise the general kernel, which
-  // masks edges and narrows its loads to the alignment class.
+  // masks edges and stages with the width chosen above.
   p.kid = lak::KID_TILED_128;
   {
     const int fk = p.gate_up ? (kmajor ? lak::KID_FAST_GU_KM : lak::KID_FAST_GU)
