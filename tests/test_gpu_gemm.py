@@ -141,6 +141,46 @@ def test_long_k_accumulation(case):
     assert_close(got[rows], ref, K, a, b, "f32", "long K %s" % ((M, N, K),))
 
 
+def _view(t_cpu, ld, offset, dev_dtype):
+    """t_cpu [r, c] placed on the GPU as a row-major view with leading dimension ld that starts
+    `offset` elements into a NaN-filled buffer (so its base pointer has only element alignment)."""
+    r, c = t_cpu.shape
+    flat = torch.full((offset + max(r - 1, 0) * ld + c + 5,), float("nan"), dtype=dev_dtype, device=DEV)
+    v = flat.as_strided((r, c), (ld, 1), offset)
+    v.copy_(t_cpu.to(DEV))
+    return v
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_general_kernel_random_layouts(case):
+    """Seeded random shapes (1..300), leading dimensions padded by 0..9 elements, operands starting
+    at element (not 16-byte) offsets inside larger buffers, both B storages, alpha and beta: the
+    general kernel's element-aligned 16-byte staging, cut chunks at K and N edges included; every
+    element against the oracle."""
+    g = torch.Generator().manual_seed(777 + case)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    M, N, K = ri(1, 300), ri(1, 300), ri(1, 300)
+    km = case % 3 == 2
+    in_kind = "bf16" if case % 2 == 0 else "f16"
+    out_kind = ("f32", "bf16", "f32", "f16")[case % 4]
+    lda, ldb, ldc = K + ri(0, 9), (K if km else N) + ri(0, 9), N + ri(0, 9)
+    a = synth.uniform((M, K), 900 + case, in_kind)
+    b = synth.uniform((K, N), 1900 + case, in_kind)
+    c = synth.uniform((M, N), 2900 + case, "f32").to(synth.torch_dtype(out_kind))
+    alpha, beta = 0.5 + ri(0, 3) * 0.25, (0.0, -0.5, 1.0)[case % 3]
+    dt = synth.torch_dtype(in_kind)
+    A = _view(a, lda, ri(0, 7), dt)
+    B = _view(b.t().contiguous() if km else b, ldb, ri(0, 7), dt)
+    C = _view(c, ldc, ri(0, 7), synth.torch_dtype(out_kind))
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], lda=lda, ldb=ldb, ldc=ldc, b_kmajor=km)
+    d = plan.describe()
+    print("case", case, (M, N, K), (lda, ldb, ldc), km, in_kind, out_kind, d["kernel"], d["vec_elems"], flush=True)
+    la.gemm_run(plan, A, B, C, alpha, beta)
+    torch.cuda.synchronize()
+    ref = oracle_gemm(a, b, in_kind, alpha, beta, c.to(torch.float32))
+    assert_close(C.cpu(), ref, K, a, b, out_kind, "random layout case %d" % case)
+
+
 PREFETCH_SHAPES = [(200, 136, 64), (130, 72, 128), (64, 64, 192), (100, 200, 1000), (96, 96, 8), (65, 130, 320),
                    (70, 90, 999), (129, 67, 257)]
 
