@@ -85,15 +85,22 @@ struct Tiled {
   // LDS element offset of (k, n) inside an N-contiguous B block.
   static __device__ __forceinline__ int b_off_n(int k, int n) { return swz<BSW, 5, 2>(k * BN + n); }
 
-  // Staging registers of one K block.  sh (V == 2 only): 4 bits per chunk
-  // (slot j of A, then slot A_CHUNKS + s * B_CHUNKS + j of weight s), the
-  // places a chunk cut by an edge is shifted down on its way to LDS.
+  // Staging registers of one K block.
   struct Regs {
     Chunk a[A_CHUNKS];
     Chunk b[NB][B_CHUNKS];
-    uint64_t sh;
   };
-  static_assert(A_CHUNKS + NB * B_CHUNKS <= 16, "shift counts fit 4 bits per chunk in 64 bits");
+
+  // Chunks of one block cut by an edge (V == 2), the same for every row of the
+  // block: the chunk index along K of A (and of K-major B) in the last K block,
+  // and the column chunk of N-contiguous B in the tile holding N's edge (-1:
+  // none), with the places each is shifted down on its way to LDS.  A thread's
+  // chunks all share one such index (tid mod 8 along K, tid mod BN/8 along N),
+  // so a thread shifts either all of an operand's chunks or none.
+  struct Cut {
+    int a_ch, a_sh, b_nc, b_sh;
+  };
+  static_assert(NT % BN8 == 0 && NT % 8 == 0, "a thread's chunks share their index along K and N");
 
   // Element q of the result is element q + sh of w (0 past the end), sh in 1..7.
   static __device__ __forceinline__ u32x4 shift_down(u32x4 w, int sh) {
@@ -111,21 +118,6 @@ struct Tiled {
       for (int i = 0; i < 4; ++i) o[i] = (o[i] >> 16) | (o[i + 1] << 16);
     }
     return u32x4{o[0], o[1], o[2], o[3]};
-  }
-
-  // The chunk as it goes to LDS.  CUT (V == 2): the block may hold chunks cut by
-  // an edge (a uniform property of the block); only then do the lanes look at
-  // their shift counts, and only lanes holding a cut chunk branch off to shift
-  // it (the data has arrived by then).
-  template <bool CUT>
-  static __device__ __forceinline__ u32x4 packed(const Chunk8& c, uint64_t, int) { return c.w; }
-  template <bool CUT>
-  static __device__ __forceinline__ u32x4 packed(const Chunk1& c, uint64_t, int) { return c.w; }
-  template <bool CUT>
-  static __device__ __forceinline__ u32x4 packed(const Chunk2& c, uint64_t sh, int slot) {
-    if constexpr (!CUT) return c.w;
-    const int k = int(sh >> (4 * slot)) & 15;
-    return k == 0 ? c.w : shift_down(c.w, k);
   }
 
   static __device__ __forceinline__ u32x4 pack8(const uint16_t* e) {
@@ -147,8 +139,7 @@ struct Tiled {
   // enabled; the compiler emits a single global_load_dwordx4): the chunk
   // itself when whole, the zero chunk when empty, and for a chunk cut by an
   // edge the 8 elements that end at its last valid one, which lie in the same
-  // row and are shifted down into place on their way to LDS; the shift count
-  // goes to sh.
+  // row and are shifted down into place on their way to LDS (see Cut).
   // In both, only the address is selected and the data is left untouched
   // until it is written to LDS, so no wait follows the load: a load under a
   // divergent branch, or a select on its result, makes the compiler wait for
@@ -157,15 +148,14 @@ struct Tiled {
   // offsets from one address for a whole chunk; a chunk cut by an edge loads
   // its valid elements one by one.  (For longer rows this measured slower
   // than V == 2: the per-chunk branch costs more than the loads.)
-  static __device__ __forceinline__ void load8(Chunk8& c, uint64_t&, int, const uint16_t* p, int nvalid) {
+  static __device__ __forceinline__ void load8(Chunk8& c, const uint16_t* p, int nvalid) {
     c.w = *reinterpret_cast<const u32x4*>(nvalid > 0 ? p : kZeroChunk);
   }
-  static __device__ __forceinline__ void load8(Chunk2& c, uint64_t& sh, int slot, const uint16_t* p, int nvalid) {
+  static __device__ __forceinline__ void load8(Chunk2& c, const uint16_t* p, int nvalid) {
     const int k = nvalid > 0 && nvalid < 8 ? 8 - nvalid : 0;
-    sh |= uint64_t(k) << (4 * slot);
     __builtin_memcpy(&c.w, nvalid > 0 ? p - k : kZeroChunk, 16);
   }
-  static __device__ __forceinline__ void load8(Chunk1& c, uint64_t&, int, const uint16_t* p, int nvalid) {
+  static __device__ __forceinline__ void load8(Chunk1& c, const uint16_t* p, int nvalid) {
     uint16_t e[8];
     if (nvalid >= 8) {
 #pragma unroll
@@ -178,7 +168,6 @@ struct Tiled {
   }
 
   static __device__ __forceinline__ void load(Regs& r, const TiledArgs& g, int m0, int n0, int64_t k0, int tid) {
-    r.sh = 0;
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
@@ -186,7 +175,7 @@ struct Tiled {
       const int64_t gm = m0 + row;
       const int64_t gk = k0 + ch * 8;
       const int nvalid = gm < g.M ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
-      load8(r.a[j], r.sh, j, g.A + gm * g.lda + gk, nvalid);
+      load8(r.a[j], g.A + gm * g.lda + gk, nvalid);
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -200,7 +189,7 @@ struct Tiled {
           const int64_t gn = n0 + row;
           const int64_t gk = k0 + ch * 8;
           const int nvalid = gn < g.N ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
-          load8(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j, B + gn * g.ldb + gk, nvalid);
+          load8(r.b[s][j], B + gn * g.ldb + gk, nvalid);
         }
         continue;
       }
@@ -212,47 +201,51 @@ struct Tiled {
         const int64_t gk = k0 + kr;
         const int64_t gn = n0 + nc * 8;
         const int nvalid = gk < g.K ? int(max<int64_t>(0, min<int64_t>(8, g.N - gn))) : 0;
-        load8(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j, B + gk * g.ldb + gn, nvalid);
+        load8(r.b[s][j], B + gk * g.ldb + gn, nvalid);
       }
     }
   }
 
-  // Write the staged block to LDS; `cut` (uniform, V == 2 only): the block may
-  // hold chunks cut by an edge.
-  static __device__ __forceinline__ void store(const Regs& r, uint16_t* stage, int tid, bool cut) {
+  // Write the staged block to LDS; `cut` (uniform, V == 2 only): its chunks cut by an edge.
+  static __device__ __forceinline__ void store(const Regs& r, uint16_t* stage, int tid, const Cut& cut) {
+    u32x4 a[A_CHUNKS], b[NB][B_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < A_CHUNKS; ++j) a[j] = r.a[j].w;
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+#pragma unroll
+      for (int j = 0; j < B_CHUNKS; ++j) b[s][j] = r.b[s][j].w;
     if constexpr (V == 2) {
-      if (cut) {
-        store_as<true>(r, stage, tid);
-        return;
+      // one branch per operand; the data has arrived by now
+      if ((tid & 7) == cut.a_ch) {
+#pragma unroll
+        for (int j = 0; j < A_CHUNKS; ++j) a[j] = shift_down(a[j], cut.a_sh);
+      }
+      const bool cut_b = BKM ? (tid & 7) == cut.a_ch : (tid % BN8) == cut.b_nc;
+      if (cut_b) {
+        const int sh = BKM ? cut.a_sh : cut.b_sh;
+#pragma unroll
+        for (int s = 0; s < NB; ++s)
+#pragma unroll
+          for (int j = 0; j < B_CHUNKS; ++j) b[s][j] = shift_down(b[s][j], sh);
       }
     }
-    store_as<false>(r, stage, tid);
-  }
-  template <bool CUT>
-  static __device__ __forceinline__ void store_as(const Regs& r, uint16_t* stage, int tid) {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
-      const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4*>(stage + lds_off(row, ch * 8)) = packed<CUT>(r.a[j], r.sh, j);
+      *reinterpret_cast<u32x4*>(stage + lds_off(idx >> 3, (idx & 7) * 8)) = a[j];
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       uint16_t* dst = stage + A_ELEMS + s * B_ELEMS;
-      if constexpr (BKM) {
-#pragma unroll
-        for (int j = 0; j < B_CHUNKS; ++j) {
-          const int idx = tid + NT * j;
-          const int row = idx >> 3, ch = idx & 7;
-          *reinterpret_cast<u32x4*>(dst + lds_off(row, ch * 8)) = packed<CUT>(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j);
-        }
-        continue;
-      }
 #pragma unroll
       for (int j = 0; j < B_CHUNKS; ++j) {
         const int idx = tid + NT * j;
-        const int kr = idx / BN8, nc = idx % BN8;
-        *reinterpret_cast<u32x4*>(dst + b_off_n(kr, nc * 8)) = packed<CUT>(r.b[s][j], r.sh, A_CHUNKS + s * B_CHUNKS + j);
+        if constexpr (BKM) {
+          *reinterpret_cast<u32x4*>(dst + lds_off(idx >> 3, (idx & 7) * 8)) = b[s][j];
+        } else {
+          *reinterpret_cast<u32x4*>(dst + b_off_n(idx / BN8, (idx % BN8) * 8)) = b[s][j];
+        }
       }
     }
   }
@@ -311,7 +304,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
-__global__ void __launch_bounds__(WM * WN * 64, V == 2 ? 2 : 1) gemm_tiled_kernel(const TiledArgs g_in) {
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * T::STAGE];
@@ -344,11 +337,23 @@ __global__ void __launch_bounds__(WM * WN * 64, V == 2 ? 2 : 1) gemm_tiled_kerne
   // compiler can count exactly which loads are still in flight.  The barriers
   // carry no memory fence: a fence would also wait for the prefetch.
   const int nk = int((g.K + T::BK - 1) / T::BK);
-  // blocks that may hold chunks cut by an edge (V == 2): the last one when K is not a multiple
-  // of 8, and every block of the tile that holds the N edge of N-contiguous B when N is not
-  const bool n_cut = !BKM && g.N % 8 != 0 && int64_t(n0) + BN > g.N;
-  const bool k_cut = g.K % 8 != 0;
-  auto cut = [&](int blk) { return blk < nk && (n_cut || (k_cut && blk == nk - 1)); };
+  // chunks cut by an edge (V == 2): along K in the last block when K is not a multiple of 8,
+  // along N in every block of the tile that holds N's edge when N is not (N-contiguous B)
+  const int64_t n_left = g.N - n0;
+  const bool n_cut = !BKM && n_left < BN && (n_left & 7) != 0;
+  auto cut = [&](int blk) {
+    typename T::Cut c{-1, 0, -1, 0};
+    const int64_t k_left = g.K - int64_t(blk) * T::BK;
+    if (blk < nk && k_left < T::BK && (k_left & 7) != 0) {
+      c.a_ch = int(k_left >> 3);
+      c.a_sh = 8 - int(k_left & 7);
+    }
+    if (blk < nk && n_cut) {
+      c.b_nc = int(n_left >> 3);
+      c.b_sh = 8 - int(n_left & 7);
+    }
+    return c;
+  };
   if constexpr (V != 1 && BM == 64 && !GU) {
     typename T::Regs r0, r1;
     T::load(r0, g, m0, n0, 0, tid);
@@ -461,7 +466,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
   const int tid = threadIdx.x;
   typename T::Regs r;
   T::load(r, g, g.dbg_tm * BM, g.dbg_tn * BN, 0, tid);
-  T::store(r, lds, tid, true);
+  T::store(r, lds, tid, [&] {
+    typename T::Cut c{-1, 0, -1, 0};
+    const int64_t k_left = g.K, n_left = g.N - int64_t(g.dbg_tn) * BN;
+    if (k_left < T::BK && (k_left & 7) != 0) { c.a_ch = int(k_left >> 3); c.a_sh = 8 - int(k_left & 7); }
+    if (!BKM && n_left < BN && (n_left & 7) != 0) { c.b_nc = int(n_left >> 3); c.b_sh = 8 - int(n_left & 7); }
+    return c;
+  }());
   __syncthreads();
   for (int i = tid; i < T::STAGE; i += T::NT) g.dbg_out[i] = lds[i];
 }
