@@ -312,3 +312,15 @@ def test_mfma_probe_argument_errors_are_caught_before_launch():
     assert call(sink=0) == "GEMM_ERR_NULL"
     assert call(ops=0x1000008) == "GEMM_ERR_ALIGNMENT"
     assert call(sink=0x2000002) == "GEMM_ERR_ALIGNMENT"
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch):
+    # Without the built HIP library every entry point raises: there is no CPU path to fall back to.
+    from layout_algebra_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_LIB_PATH", os.path.join(ROOT, "no_such_dir", "liblagemm.so"))
+    for call in (lambda: la.gemm_plan(256, 256, 256),
+                 lambda: la.la_swizzle_apply(3, 3, 4, 0),
+                 lambda: la.la_layout_eval((4, 8), (8, 1), (1, 2))):
+        with pytest.raises(RuntimeError, match="no fallback"):
+            call()
