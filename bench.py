@@ -306,6 +306,12 @@ def copy_probe(dev):
     del src, dst
 
 
+def settled_clock(readings):
+    """Median of the clock readings after the first (the first can still show the idle state)."""
+    import statistics
+    return statistics.median(readings[1:] if len(readings) > 1 else readings)
+
+
 def clock_sample(run, seconds=1.5):
     """GPU clock and power while the workload runs: `run` (a whole timed region's worth of steps)
     is replayed, untimed, until amd-smi has been read three times from a child process (about
@@ -353,8 +359,7 @@ def clock_sample(run, seconds=1.5):
             continue
     if not clk:
         return None
-    later = sorted(clk[1:] if len(clk) > 1 else clk)
-    return {"gfx_mhz": clk, "settled_mhz": later[len(later) // 2], "max_mhz": cmax, "socket_power_w": power,
+    return {"gfx_mhz": clk, "settled_mhz": settled_clock(clk), "max_mhz": cmax, "socket_power_w": power,
             "method": "amd-smi metric during untimed replays of the timed steps, after the timed region"}
 
 

@@ -82,3 +82,9 @@ def test_peak_scaled_to_the_measured_clock():
     assert abs(r["peak_tflops"] - 2516.6 * 1630.0 / 2400.0) < 1e-9
     assert abs(r["frac"] - 1239.0 / r["peak_tflops"]) < 1e-12
     assert bench.at_clock(None, 2516.6, 1239.0) is None
+
+
+def test_settled_clock_is_the_median_after_the_first_reading():
+    assert bench.settled_clock([95.0, 1577.0, 1622.0]) == (1577.0 + 1622.0) / 2
+    assert bench.settled_clock([95.0, 1630.0, 1600.0, 1640.0]) == 1630.0
+    assert bench.settled_clock([1500.0]) == 1500.0
