@@ -287,7 +287,7 @@ def mfma_ceiling(dev, operands, flops, achieved):
     ops = operands.reshape(-1)[: 1 << 19]
     res = {}
     for name, src in (("tflops", ops), ("tflops_zero_operands", torch.zeros_like(ops))):
-        ms, _, _ = timed_steps(lambda i: la.la_probe_mfma(src, sink, 256, per_wave), 10, 3)
+        ms, _, _, _ = timed_steps(lambda i: la.la_probe_mfma(src, sink, 256, per_wave), 10, 3)
         res[name] = 256 * 4 * per_wave * per_mfma / (ms * 1e-3) / 1e12
     res["operands"] = "first %d KiB of the workload's first input" % (ops.numel() * 2 // 1024)
     res["mfma_per_wave"] = per_wave
@@ -406,7 +406,7 @@ def steps_runner(step, steps, launch):
 def timed_steps(step, steps, warmup, launch="eager", clock=False):
     """Warm-up (eager), then `steps` back-to-back steps (steps_runner) between two HIP events on the
     current stream (synchronised on both sides); then up to 20 single steps each between its own
-    event pair."""
+    event pair.  Returns (ms per step, wall seconds, per-launch ms, clock_sample or None)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         step(i)
@@ -429,9 +429,7 @@ def timed_steps(step, steps, warmup, launch="eager", clock=False):
         ends[i].record(stream)
     torch.cuda.synchronize()
     per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-    if clock:
-        return ms, wall, per_launch, clock_sample(run)
-    return ms, wall, per_launch
+    return ms, wall, per_launch, clock_sample(run) if clock else None
 
 
 def bench_norm(args, w):
