@@ -24,6 +24,7 @@
 #include "planner.hpp"
 
 #include <algorithm>
+#include <cstdint>
 #include <cstdio>
 #include <sstream>
 #include <vector>
@@ -335,7 +336,11 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   if (fast || p.kid == lak::KID_SKINNY_16) p.align_bytes = 16;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
-  if (int64_t(p.tiles_m) * p.tiles_n > (int64_t{1} << 31) - 1) { fail(err, "too many tiles"); return GEMM_ERR_UNSUPPORTED; }
+  // one launch: the grid's work-items along x (tiles x threads per tile) must fit in 32 bits
+  if (int64_t(p.tiles_m) * p.tiles_n * s.threads > int64_t(UINT32_MAX)) {
+    fail(err, "too many tiles for one launch");
+    return GEMM_ERR_UNSUPPORTED;
+  }
   p.grid = p.tiles_m * p.tiles_n;
   p.group_m = 8;
 

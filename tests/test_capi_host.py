@@ -145,6 +145,12 @@ def test_invalid_requests_are_rejected():
     with pytest.raises(la.GemmError) as e:
         la.gemm_plan(4, 4, 4, la.F32, la.F32)
     assert e.value.name == "GEMM_ERR_UNSUPPORTED"
+    # a grid of more than 2^32 work-items along x does not fit one launch (8,388,608 tiles of
+    # 256 x 256 at 512 threads each is exactly 2^32); a tile row fewer plans
+    with pytest.raises(la.GemmError, match="too many tiles") as e:
+        la.gemm_plan(256 * 4096, 256 * 2048, 64, la.BF16, la.BF16)
+    assert e.value.name == "GEMM_ERR_UNSUPPORTED"
+    assert la.gemm_plan_describe(la.gemm_plan(256 * 4096, 256 * 2047, 64, la.BF16, la.BF16))["kernel"].startswith("fast")
 
 
 def test_small_grids_take_64x64_tiles_unless_pinned():
