@@ -60,6 +60,7 @@ struct AttnCfg<64> {
 };
 
 constexpr int BR = 128, BC = 64, NW = 4, NTHREADS = NW * 64;
+static_assert(NTHREADS == ATTN_THREADS, "the launch checks size the grid with ATTN_THREADS");
 
 // One direct load: 64 lanes x 16 bytes from base + voff (bytes) into the KB of
 // LDS at lds_addr (wave-uniform, through M0).  Inline assembly keeps the

@@ -20,6 +20,9 @@ struct AttnArgs {
   int q_tiles;           // ceil(sq / 128)
 };
 
+// Threads per workgroup; one workgroup per 128 queries of one batch entry.
+constexpr int ATTN_THREADS = 256;
+
 // in_kind: IN_BF16 or IN_F16; out_kind: OUT_F32, OUT_BF16 or OUT_F16; d: 64 or 128.
 // Rows of Q, K, V, O start on 16 bytes (checked by the caller).
 hipError_t launch_attention(const AttnArgs& a, int d, int in_kind, int out_kind, hipStream_t stream);

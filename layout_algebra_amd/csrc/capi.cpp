@@ -273,7 +273,9 @@ gemm_status la_attention_run(const attn_desc* desc, const void* Q, const void* K
   if (128 * d.ld_k >= (int64_t{1} << 32) || 128 * d.ld_v >= (int64_t{1} << 32))
     return set_err(GEMM_ERR_UNSUPPORTED, "K and V row strides must keep 64 rows below 4 GiB");
   const int64_t q_tiles = (d.sq + 127) / 128;
-  if (d.batch > (int64_t{1} << 31) / q_tiles - 1) return set_err(GEMM_ERR_UNSUPPORTED, "too many query tiles");
+  // one launch: the grid's work-items along x (query tiles x threads per tile) must fit in 32 bits
+  if (d.batch > int64_t(UINT32_MAX) / (q_tiles * lak::ATTN_THREADS))
+    return set_err(GEMM_ERR_UNSUPPORTED, "too many query tiles for one launch");
   const int osz = d.out_type == GEMM_F32 ? 4 : 2;
   // batch entries of O: disjoint blocks, or rows interleaved with disjoint segments
   const bool o_blocks = __int128(d.stride_o) >= __int128(d.sq - 1) * d.ld_o + d.d;

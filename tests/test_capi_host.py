@@ -294,6 +294,10 @@ def test_attention_argument_errors_are_caught_before_launch():
     assert call(stride_o=128) == "GEMM_ERR_INVALID_ARG"            # batch entries of O overlap
     assert call(O=0x3000000 + 4096) == "GEMM_ERR_INVALID_ARG"      # O overlaps V
     assert call(ld_k=1 << 25, stride_k=0) == "GEMM_ERR_UNSUPPORTED"
+    # 2^24 query tiles of 256 threads are 2^32 work-items: more than one launch carries
+    big = dict(batch=1 << 24, sq=128, stride_q=128 * 128, stride_o=128 * 128, stride_k=0, stride_v=0)
+    assert call(**big) == "GEMM_ERR_UNSUPPORTED"
+    assert "too many query tiles" in lib.gemm_last_error().decode()
     assert call(batch=0, Q=0, K=0, V=0, O=0) == "GEMM_OK"            # nothing to do, nothing touched
     assert call(sq=0, sk=0, Q=0, K=0, V=0, O=0) == "GEMM_OK"
 
