@@ -303,7 +303,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
@@ -354,7 +354,37 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
     }
     return c;
   };
-  if constexpr (V != 1 && BM == 64 && !GU) {
+  if constexpr (V != 1 && BM == 64 && !GU && P3) {
+    // three register sets: blocks kt+1 and kt+2 in flight while block kt is
+    // multiplied (240 registers, one wave per SIMD: the planner takes this
+    // only for grids of one to two workgroups per CU, where it measured
+    // 6-9 % faster; larger grids lose the second workgroup per SIMD)
+    typename T::Regs r0, r1, r2;
+    T::load(r0, g, m0, n0, 0, tid);
+    T::load(r1, g, m0, n0, T::BK, tid);
+    T::load(r2, g, m0, n0, 2 * T::BK, tid);
+    T::store(r0, lds, tid, cut(0));
+    stage_barrier();
+    for (int kt = 0; kt < nk; kt += 3) {
+      // block kt in stage kt % 2, blocks kt+1 and kt+2 in flight in r1 and r2
+      uint16_t* s0 = lds + (kt & 1) * T::STAGE;
+      uint16_t* s1 = lds + ((kt + 1) & 1) * T::STAGE;
+      T::load(r0, g, m0, n0, int64_t(kt + 3) * T::BK, tid);
+      T::compute(s0, acc, wm, wn, lane);
+      T::store(r1, s1, tid, cut(kt + 1));
+      stage_barrier();
+      if (kt + 1 >= nk) break;
+      T::load(r1, g, m0, n0, int64_t(kt + 4) * T::BK, tid);
+      T::compute(s1, acc, wm, wn, lane);
+      T::store(r2, s0, tid, cut(kt + 2));
+      stage_barrier();
+      if (kt + 2 >= nk) break;
+      T::load(r2, g, m0, n0, int64_t(kt + 5) * T::BK, tid);
+      T::compute(s0, acc, wm, wn, lane);
+      T::store(r0, s1, tid, cut(kt + 3));
+      stage_barrier();
+    }
+  } else if constexpr (V != 1 && BM == 64 && !GU) {
     typename T::Regs r0, r1;
     T::load(r0, g, m0, n0, 0, tid);
     T::load(r1, g, m0, n0, T::BK, tid);
@@ -480,12 +510,12 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
 // ------------------------------------------------------------------ dispatch
 namespace {
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3 = false>
 hipError_t go(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (img) {
     hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU, BKM>), dim3(1), dim3(WM * WN * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM>), grid, dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM, P3>), grid, dim3(WM * WN * 64), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -519,6 +549,33 @@ hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const 
   return hipErrorInvalidValue;
 }
 
+// 64 x 64 tiles with three K blocks in flight: plain GEMMs with 16-byte loads only.
+template <class TI, class TO>
+hipError_t p3_by_vec(int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (gu) return hipErrorInvalidValue;
+  if (vec == 8)
+    return km ? go<TI, TO, 64, 64, 2, 1, 8, false, true, true>(a, grid, s, img)
+              : go<TI, TO, 64, 64, 2, 1, 8, false, false, true>(a, grid, s, img);
+  if (vec == 2)
+    return km ? go<TI, TO, 64, 64, 2, 1, 2, false, true, true>(a, grid, s, img)
+              : go<TI, TO, 64, 64, 2, 1, 2, false, false, true>(a, grid, s, img);
+  return hipErrorInvalidValue;
+}
+
+hipError_t p3_by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, dim3 grid,
+                       hipStream_t s, bool img) {
+  if (in_kind == IN_BF16) {
+    if (out_kind == OUT_F32) return p3_by_vec<InBF16, OutF32>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_BF16) return p3_by_vec<InBF16, OutBF16>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_F16) return p3_by_vec<InBF16, OutF16>(vec, gu, km, a, grid, s, img);
+  } else if (in_kind == IN_F16) {
+    if (out_kind == OUT_F32) return p3_by_vec<InF16, OutF32>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_BF16) return p3_by_vec<InF16, OutBF16>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_F16) return p3_by_vec<InF16, OutF16>(vec, gu, km, a, grid, s, img);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
@@ -528,6 +585,8 @@ hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_u
       return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     case KID_TILED_64:
       return by_types<64, 64, 2, 1>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+    case KID_TILED_64_P3:
+      return p3_by_types(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,6 +15,7 @@ KernelShape kernel_shape(int kid) {
     case KID_TILED_128:
       return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {2, 5, 2}};
     case KID_TILED_64:
+    case KID_TILED_64_P3:
       return KernelShape{64, 64, 64, 2, 2, 1, 128, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {1, 5, 2}};
     case KID_FAST_256: return fast_shape<CfgFast256>();
     case KID_FAST_GU: return fast_shape<CfgFastGU>();
@@ -38,7 +39,8 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
                          dim3 grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
     case KID_TILED_128:
-    case KID_TILED_64: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+    case KID_TILED_64:
+    case KID_TILED_64_P3: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     case KID_FAST_256:
     case KID_FAST_GU:
     case KID_FAST_256_KM:

@@ -49,6 +49,7 @@ enum KernelId : int {
   KID_FAST_256_KM = 4,   // KID_FAST_256 for B stored [N, K] (K contiguous)
   KID_FAST_GU_KM = 5,    // KID_FAST_GU for weights stored [N, K]
   KID_TILED_64 = 6,      // any shape, small grids: 64x64x64, 2 waves of 32x64, as KID_TILED_128 otherwise
+  KID_TILED_64_P3 = 7,   // KID_TILED_64 with three K blocks in flight (plain GEMM, 16-byte loads)
   KID_COUNT
 };
 

@@ -334,3 +334,20 @@ def test_missing_library_raises_instead_of_falling_back(monkeypatch):
                  lambda: la.la_layout_eval((4, 8), (8, 1), (1, 2))):
         with pytest.raises(RuntimeError, match="no fallback"):
             call()
+
+
+def test_prefetch_depth_follows_the_grid():
+    """The general kernel's 64 x 64 tiles keep three K blocks in flight on grids of 257 to 512
+    workgroups (plain GEMM, 16-byte loads), two on other grids, one with element loads or gate/up."""
+    def depth(m, n, k, **kw):
+        d = la.gemm_plan(m, n, k, la.F16, la.F32, **kw).describe()
+        return d["kernel"], d["grid"] * d["batch"], d["prefetch_blocks"]
+    assert depth(1000, 1537, 999) == ("tiled_64x64x64", 400, 3)
+    assert depth(1024, 1088, 64) == ("tiled_64x64x64", 272, 3)
+    assert depth(1024, 1024, 64)[1:] == (256, 2)
+    assert depth(1536, 1537, 999)[1:] == (600, 2)
+    assert depth(1088, 1920, 64)[1:] == (510, 3)
+    assert depth(1088, 2048, 64)[1:] == (544, 2)
+    assert depth(200, 300, 5)[2] == 1                                  # element loads
+    assert depth(1000, 1537, 999, gate_up=True)[2] == 1                 # gate/up keeps one set
+    assert depth(300, 300, 64, batch=12)[1:] == (300, 3)                # batch entries count as workgroups

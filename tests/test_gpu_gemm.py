@@ -205,6 +205,30 @@ def test_general_kernel_prefetch_depths(shape, out_kind):
     assert_close(got, ref, K, a, b, out_kind, "prefetch %s" % (shape,))
 
 
+DEEP_SHAPES = [(1088, 1088, 64, False), (1088, 1088, 128, False), (1088, 1088, 192, False), (1000, 1100, 130, False),
+               (1030, 1037, 320, False), (1000, 1537, 999, False), (1088, 1030, 456, True), (1030, 1088, 999, True)]
+
+
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", DEEP_SHAPES, ids=[str(s) for s in DEEP_SHAPES])
+def test_general_kernel_three_blocks_in_flight(shape, out_kind):
+    """Grids of 257 to 512 workgroups of 64 x 64 tiles (plain GEMM, 16-byte loads) keep three K
+    blocks in flight: 1 to 16 blocks, block counts of every residue mod 3, K tails and N edges
+    cutting chunks, both B storages; every element against the oracle."""
+    M, N, K, km = shape
+    seed = 7 * M + 3 * N + K + km
+    print("case", shape, out_kind, flush=True)
+    a = synth.uniform((M, K), seed, "f16")
+    b = synth.uniform((K, N), seed + 1, "f16")
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    d = la.gemm_plan(M, N, K, la.F16, CODE[out_kind], b_kmajor=km).describe()
+    assert d["kernel"].startswith("tiled_64x64") and 256 < d["grid"] <= 512, d
+    assert d["prefetch_blocks"] == 3
+    got = run_gemm(a, b, out_kind, 1.25, -0.5, c, b_kmajor=km, expect="tiled_64x64")
+    ref = oracle_gemm(a, b, "f16", 1.25, -0.5, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "three blocks in flight %s" % (shape,))
+
+
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
 def test_identity_and_permutation_B_are_exact(in_kind):
     K, M = 256, 192
