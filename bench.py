@@ -47,25 +47,37 @@ GEMM_SOURCES = {"fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_": ("gemm_ti
                 "skinny_": ("gemm_skinny.hip",)}
 
 
+# host code that decides which instantiation a GEMM plan launches, and with which grid
+PLANNER_SOURCES = ("planner.cpp", "kernels.cpp", "kernel_table.hpp")
+
+
+def gemm_plan_summary(workload):
+    """The planned kernel of a GEMM workload: its name, grid and K blocks in flight."""
+    import layout_algebra_amd as la
+    w = synth.WORKLOADS[workload]
+    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+    d = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up).describe()
+    return "%s grid=%d prefetch=%d" % (d["kernel"], d["grid"], d["prefetch_blocks"])
+
+
 def workload_sources(workload):
-    """Kernel source files (csrc/) of what a workload runs: the row normalisation's, the
-    attention's, or those of the GEMM kernel family its plan selects, plus the shared headers."""
+    """Source files (csrc/) of what a workload runs: the row normalisation's, the attention's, or
+    those of the GEMM kernel family its plan selects plus the planner that selects it, and the
+    shared headers."""
     if workload in synth.NORM_WORKLOADS:
         own = NORM_SOURCES
     elif workload in synth.ATTN_WORKLOADS:
         own = ATTN_SOURCES
     else:
-        import layout_algebra_amd as la
-        w = synth.WORKLOADS[workload]
-        code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
-        kernel = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up).describe()["kernel"]
-        own = next(v for k, v in GEMM_SOURCES.items() if kernel.startswith(k))
+        kernel = gemm_plan_summary(workload).split()[0]
+        own = next(v for k, v in GEMM_SOURCES.items() if kernel.startswith(k)) + PLANNER_SOURCES
     return tuple(sorted(own + SHARED_SOURCES))
 
 
 def kernel_source_hash(workload):
-    """sha1 (first 16 hex) over the HIP sources of the kernels a workload runs
-    (workload_sources).  Identifies the kernels the traffic figures belong to."""
+    """sha1 (first 16 hex) over the sources of what a workload runs (workload_sources) and, for a
+    GEMM, its plan summary (kernel, grid, K blocks in flight).  Identifies the kernels the traffic
+    figures belong to: a planner change that moves a workload to another instantiation changes it."""
     import hashlib
     csrc = os.path.join(ROOT, "layout_algebra_amd", "csrc")
     h = hashlib.sha1()
@@ -73,6 +85,8 @@ def kernel_source_hash(workload):
         h.update(name.encode())
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
+    if workload in synth.WORKLOADS:
+        h.update(gemm_plan_summary(workload).encode())
     return h.hexdigest()[:16]
 
 
@@ -118,6 +132,9 @@ def main():
                     help="hand B (or the gate/up weights) to the library as [N,K] (K contiguous)")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="timed steps as replays of a captured HIP graph (default), or one library call each")
+    ap.add_argument("--preroll-seconds", type=float, default=0.5,
+                    help="after the warm-up steps, replay the timed steps untimed for at least this long, "
+                         "whatever --warmup is, so the timed region starts at the clock the chip settles to")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the clock/power reading (amd-smi during untimed replays after the timed region)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -179,10 +196,13 @@ def main():
     torch.cuda.synchronize()
 
     # parity of the timed launch configuration: run once on the first B, keep the result
+    check_u = None
     if w.beta == 0.0 and not w.act:
         step(0)
         torch.cuda.synchronize()
         check = result.detach().clone()
+        if w.gate_up:
+            check_u = U.detach().clone()
     else:
         check = None
 
@@ -191,6 +211,7 @@ def main():
     # a pair of HIP events.  Each step is one launch of the GEMM kernel, so the
     # kernel's average duration is the region's time / K.
     run = steps_runner(step, args.steps, args.launch)
+    pre = preroll(run, args.preroll_seconds)
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -260,6 +281,7 @@ def main():
                    "kernel": plan.describe()["kernel"], "grid": plan.describe()["grid"]},
         "roofline": roof,
         "wall_s_timed": wall,
+        "preroll": pre,
         "tflops": value_tflops,
         "pct_of_bf16_peak": 100.0 * value_tflops / PEAK_TFLOPS[w.in_kind],
     }
@@ -270,7 +292,8 @@ def main():
     if replay_equal is not None:
         line["timed_output_equals_eager"] = replay_equal
     if not args.no_cpu_baseline:
-        line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit)
+        line["cpu_baseline"], line["parity_sample"] = cpu_baseline(w, x, b_cpu, check, args.cpu_seconds, value, unit,
+                                                                   check_u)
     print(json.dumps(line), flush=True)
 
 
@@ -287,7 +310,7 @@ def mfma_ceiling(dev, operands, flops, achieved):
     ops = operands.reshape(-1)[: 1 << 19]
     res = {}
     for name, src in (("tflops", ops), ("tflops_zero_operands", torch.zeros_like(ops))):
-        ms, _, _, _ = timed_steps(lambda i: la.la_probe_mfma(src, sink, 256, per_wave), 10, 3)
+        ms, _, _, _ = timed_steps(lambda i: la.la_probe_mfma(src, sink, 256, per_wave), 10, 3, preroll_s=0.3)
         res[name] = 256 * 4 * per_wave * per_mfma / (ms * 1e-3) / 1e12
     res["operands"] = "first %d KiB of the workload's first input" % (ops.numel() * 2 // 1024)
     res["mfma_per_wave"] = per_wave
@@ -373,6 +396,21 @@ def at_clock(clock, peak, achieved):
     return {"peak_tflops": p, "frac": achieved / p, "gfx_mhz": mhz}
 
 
+def preroll(run, seconds):
+    """Untimed: call `run` (a whole timed region's worth of steps) until at least `seconds` have
+    passed.  The chip's clock ramps for tens of milliseconds of sustained load and then settles at
+    what its power limit allows; this makes the timed region start there whatever --warmup is."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        run()
+        torch.cuda.synchronize()
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return {"seconds": time.perf_counter() - t0, "replays_of_the_timed_steps": n}
+
+
 def graph_chunk(steps):
     """Steps per captured graph: the largest divisor of `steps` up to 50, an even one where there
     is one (the skinny workload alternates two B buffers from step to step)."""
@@ -403,15 +441,18 @@ def steps_runner(step, steps, launch):
     return run
 
 
-def timed_steps(step, steps, warmup, launch="eager", clock=False):
-    """Warm-up (eager), then `steps` back-to-back steps (steps_runner) between two HIP events on the
-    current stream (synchronised on both sides); then up to 20 single steps each between its own
-    event pair.  Returns (ms per step, wall seconds, per-launch ms, clock_sample or None)."""
+def timed_steps(step, steps, warmup, launch="eager", clock=False, preroll_s=0.0):
+    """Warm-up (eager), an untimed pre-roll of at least preroll_s seconds, then `steps`
+    back-to-back steps (steps_runner) between two HIP events on the current stream (synchronised on
+    both sides); then up to 20 single steps each between its own event pair.  Returns (ms per step,
+    wall seconds, per-launch ms, clock_sample or None)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     run = steps_runner(step, steps, launch)
+    if preroll_s > 0:
+        preroll(run, preroll_s)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -444,7 +485,8 @@ def bench_norm(args, w):
     def step(i):
         la.la_rms_norm_run(X, G, Y, w.eps)
 
-    ms, wall, per_launch, clock = timed_steps(step, args.steps, args.warmup, args.launch, clock=not args.no_clock)
+    ms, wall, per_launch, clock = timed_steps(step, args.steps, args.warmup, args.launch, clock=not args.no_clock,
+                                              preroll_s=args.preroll_seconds)
     if args.copy_probe:
         copy_probe(dev)
     bytes_ = w.bytes()
@@ -461,6 +503,7 @@ def bench_norm(args, w):
                      "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
                      "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
         "wall_s_timed": wall,
+        "preroll": {"seconds_min": args.preroll_seconds},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline_norm(w, inp, Y, args.cpu_seconds, gbs)
@@ -479,7 +522,8 @@ def bench_attention(args, w):
     def step(i):
         la.la_attention_run(Q, K, V, O, w.scale)
 
-    ms, wall, per_launch, clock = timed_steps(step, args.steps, args.warmup, args.launch, clock=not args.no_clock)
+    ms, wall, per_launch, clock = timed_steps(step, args.steps, args.warmup, args.launch, clock=not args.no_clock,
+                                              preroll_s=args.preroll_seconds)
     if args.copy_probe:
         copy_probe(dev)
     tflops = w.flops() / (ms * 1e-3) / 1e12
@@ -498,6 +542,7 @@ def bench_attention(args, w):
                      "traffic": measured_traffic(w.name), "kernel_avg_ms": ms,
                      "single_launch_ms": {"min": float(per_launch.min()), "median": float(np.median(per_launch))}},
         "wall_s_timed": wall,
+        "preroll": {"seconds_min": args.preroll_seconds},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity_sample"] = cpu_baseline_attention(w, x, O, args.cpu_seconds, tflops)
@@ -552,13 +597,15 @@ def cpu_baseline_attention(w, x, O, budget_s, gpu_value):
             "sample": "queries 0..%d of batch entry 0 against all %d keys, numpy binary64 (BLAS matmul), %.2f s"
                       % (R - 1, w.sk, dt),
             "seconds": dt, "gpu_over_cpu": gpu_value / value if value > 0 else None}
-    got = O[0, :R].to("cpu", torch.float64).numpy()
-    delta = w.scale * 2.0 ** -20 * w.d * float(x["Q"].abs().max()) * float(x["K"].abs().max())
-    in_rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}[w.in_kind]
-    out_rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}[w.out_kind]
-    tol = (in_rel + 4.0 * delta + 2.0 ** -20) * float(x["V"][0].abs().max()) + out_rel * np.abs(ref)
-    err = np.abs(got - ref)
-    return base, {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol))}
+    # parity of the timed output on the first rows of the sample, against the per-row bound
+    # built from the oracle's own softmax weights
+    from oracle.tolerance import attention_bound
+    P = min(R, 64)
+    ref_p, tol = attention_bound(q[:P], k, v, w.scale, w.in_kind, w.out_kind)
+    got = O[0, :P].to("cpu", torch.float64).numpy()
+    err = np.abs(got - ref_p)
+    return base, {"rows": P, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol)),
+                  "bound": "per row, from the oracle's softmax weights"}
 
 
 def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):
@@ -594,9 +641,20 @@ def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):
     return base, {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol))}
 
 
-def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):
+def gemm_tolerance(w, a, b, ref):
+    """Agreement bound of a GEMM output: 2^-20 K max|A| max|B| (FP32 accumulation) plus the
+    output's own rounding for 16-bit outputs (for fp32 outputs only when K = 0, where the result is
+    beta * C rounded to fp32)."""
+    acc = 2.0 ** -20 * w.K * float(a.abs().max()) * float(b.abs().max())
+    rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22 if w.K == 0 else 0.0}[w.out_kind]
+    return acc + rel * np.abs(ref)
+
+
+def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit, check_u=None):
     """Time the oracle (as it is) on the first R output rows, R sized to about budget_s seconds;
-    when the whole workload takes less than that, repeat it."""
+    when the whole workload takes less than that, repeat it.  The timed GPU output is compared with
+    those rows; for gate/up the second output (U = x W_up) is compared on the first 64 rows as well
+    (an untimed oracle run)."""
     import oracle
     threads = oracle.max_threads()
     a = x["A"]
@@ -626,10 +684,14 @@ def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit):
     parity = None
     if check is not None:
         got = check[:R].to("cpu", torch.float64).numpy()
-        tol = 2.0 ** -20 * w.K * float(a.abs().max()) * float(b_cpu.abs().max()) + \
-            {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}[w.out_kind] * np.abs(ref)
         err = np.abs(got - ref)
-        parity = {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= tol))}
+        parity = {"rows": R, "max_abs_err": float(err.max()), "ok": bool(np.all(err <= gemm_tolerance(w, a, b_cpu, ref)))}
+        if check_u is not None:
+            ru = list(range(min(R, 64)))
+            ref_u = oracle.gemm_f64(synth.bits(a[ru]), w.in_kind, synth.bits(x["Wu"]), w.in_kind)
+            err_u = np.abs(check_u[:len(ru)].to("cpu", torch.float64).numpy() - ref_u)
+            ok_u = bool(np.all(err_u <= gemm_tolerance(w, a, x["Wu"], ref_u)))
+            parity.update({"U_rows": len(ru), "U_max_abs_err": float(err_u.max()), "ok": parity["ok"] and ok_u})
     return base, parity
 
 

@@ -11,6 +11,7 @@ the seeded inputs the callers pass to both.
 * ``rms_norm_f64`` -- the row normalisation, numpy in binary64.
 * ``gemm_row_reduce_f64`` -- the GEMM with a sum / max / min of every output row.
 * ``attention_f64`` -- softmax attention, numpy in binary64.
+* ``attention_weights_f64`` -- the normalised softmax weights of the same rows.
 * ``layout_ref`` -- the layout algebra written out by enumeration in Python.
 """
 import ctypes
@@ -187,3 +188,23 @@ def attention_f64(q, k, v, scale):
     s = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
     p = np.exp(s - np.max(s, axis=-1, keepdims=True))
     return np.matmul(p, v) / np.sum(p, axis=-1, keepdims=True)
+
+
+def attention_weights_f64(q, k, scale):
+    """The normalised softmax weights of attention_f64, in binary64:
+
+        w[i, j] = p[i, j] / sum_j p[i, j],   p[i, j] = exp(s[i, j] - max_j s[i, j]),
+        s[i, j] = scale * sum_d q[i, d] k[j, d]
+
+    (the weights the Phobos page "Tiles and shared memory" accumulates through
+    the key loop, section "How long a tile lives", normalised as the sum at the
+    end of that loop does).  attention_f64's output is w @ v.
+    q: (..., Sq, D), k: (..., Sk, D); returns w (..., Sq, Sk).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if k.shape[-2] == 0:
+        raise ValueError("attention over zero keys is undefined")
+    s = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
+    p = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return p / np.sum(p, axis=-1, keepdims=True)

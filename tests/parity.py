@@ -3,17 +3,19 @@ oracle on the same 16-bit patterns, and the agreement bound.
 
 Agreement bound (elementwise):
     |gpu - oracle| <= 2^-20 * K * max|A| * max|B|  +  r * |oracle|
-with r = 2^-8 for bf16 outputs (the output's own rounding), 2^-11 for fp16
-outputs, and 2^-22 for fp32 outputs.  The first term is the FP32
-accumulation allowance; the second covers the final rounding into the output
-format (for fp32 outputs it only matters when K = 0, where the first term is
-zero and the result is beta * C rounded to fp32).
+with r = 2^-8 for bf16 outputs (the output's own rounding) and 2^-11 for fp16
+outputs.  The first term is the FP32 accumulation allowance.  FP32 outputs add
+a rounding term only when K = 0, where the first term is zero and the result
+is beta * C rounded to fp32 (r = 2^-22 there); for K > 0 the final FP32
+rounding (at most 2^-24 |out|) must sit well inside the first term, which
+bound() checks instead of silently widening the tolerance.
 """
 import numpy as np
 import torch
 
 import oracle
 import synth
+from oracle.tolerance import attention_bound  # noqa: F401  (re-exported for the tests)
 
 REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}
 
@@ -23,7 +25,16 @@ def max_abs(t):
 
 
 def bound(K, a, b, ref, out_kind):
-    return 2.0 ** -20 * K * max_abs(a) * max_abs(b) + REL[out_kind] * np.abs(ref)
+    acc = 2.0 ** -20 * K * max_abs(a) * max_abs(b)
+    if out_kind == "f32":
+        if K == 0:
+            return REL["f32"] * np.abs(ref)
+        peak = float(np.abs(ref).max()) if np.size(ref) else 0.0
+        if 2.0 ** -22 * peak > acc:
+            raise ValueError("fp32 output: the final rounding (2^-24 of %g) is not covered by the accumulation "
+                             "term %g; these inputs need an output rounding term" % (peak, acc))
+        return np.full(np.shape(ref), acc)
+    return acc + REL[out_kind] * np.abs(ref)
 
 
 def assert_close(gpu, ref, K, a, b, out_kind, what=""):
@@ -45,6 +56,20 @@ def oracle_gemm(a_cpu, b_cpu, in_kind, alpha=1.0, beta=0.0, c_cpu=None, rows=Non
     if c_cpu is not None:
         c = (c_cpu if rows is None else c_cpu[rows]).numpy()
     return oracle.gemm_f64(synth.bits(a), in_kind, synth.bits(b_cpu), in_kind, alpha, beta, c)
+
+
+def band_rows(M, band=256, wave_rows=128, extra=1, seed=0):
+    """Rows that cover every band of `band` output rows (one row-tile of the full-tile kernels):
+    the first and last row of each wave's block of `wave_rows` rows in it, plus `extra` drawn rows
+    per band."""
+    g = torch.Generator().manual_seed(seed)
+    rows = set()
+    for b0 in range(0, M, band):
+        hi = min(M, b0 + band)
+        for w0 in range(b0, hi, wave_rows):
+            rows |= {w0, min(hi, w0 + wave_rows) - 1}
+        rows |= set((b0 + torch.randint(0, hi - b0, (extra,), generator=g)).tolist())
+    return sorted(rows)
 
 
 def sample_rows(M, n, seed):
@@ -82,3 +107,14 @@ def norm_bound(D, y_ref, out_kind):
     r = np.abs(y_ref)
     absolute = 2.0 ** -25 if out_kind == "f16" else 0.0
     return (D + 8) * 2.0 ** -24 * r + REL[out_kind] * r + absolute
+
+
+def attention_workload_rows(w):
+    """(batch entry, query rows) pairs the workload parity test checks: the first and last entry
+    plus up to four drawn ones, each with its first and last query plus up to 24 drawn ones."""
+    g = torch.Generator().manual_seed(99)
+    out = []
+    for z in sorted(set(torch.randint(0, w.batch, (4,), generator=g).tolist()) | {0, w.batch - 1}):
+        rows = sorted(set(torch.randint(0, w.sq, (24,), generator=g).tolist()) | {0, w.sq - 1})
+        out.append((z, rows))
+    return out

@@ -45,8 +45,12 @@ def test_attention_and_norm_work():
 def test_traffic_lines_parse_and_follow_the_source_hash(tmp_path, monkeypatch):
     # a line is used only while its hash matches the workload's current kernel sources
     h = bench.kernel_source_hash("square4096")
-    assert len(h) == 16 and h == bench.kernel_source_hash("gate_up")        # same kernel sources
-    assert h != bench.kernel_source_hash("attention")
+    assert len(h) == 16 and h != bench.kernel_source_hash("attention")
+    # same kernel sources, another instantiation: the plan summary keeps the hashes apart
+    assert bench.workload_sources("square4096") == bench.workload_sources("gate_up")
+    assert h != bench.kernel_source_hash("gate_up")
+    assert "planner.cpp" in bench.workload_sources("ragged") and "planner.cpp" not in bench.workload_sources("attention")
+    assert "prefetch=3" in bench.gemm_plan_summary("ragged")
     # each GEMM workload hashes the sources of the kernel family its plan selects
     assert "gemm_fast.hpp" in bench.workload_sources("square4096")
     assert "gemm_tiled.hip" not in bench.workload_sources("square4096")

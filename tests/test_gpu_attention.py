@@ -2,13 +2,13 @@
 memory", section "How long a tile lives") against the binary64 oracle, through
 the C ABI.
 
-Bound per output row i: every probability is rounded to the input type
-(relative 2^-9 for bf16, 2^-12 for fp16) and the GPU forms the weighted mean
-with those rounded weights in numerator and denominator alike, which moves the
-mean by at most twice that times max|V| (2^-8, 2^-11); the FP32 scores are off by at most
-Delta = scale * 2^-20 * d * max|Q| * max|K|, which moves the normalised
-weights by at most about 2 Delta (4 Delta max|V| in the mean); 2^-20 covers
-exp2 and the FP32 arithmetic; the output's own rounding adds r |O|.
+The bound is computed row by row from the oracle's own softmax weights
+(oracle.tolerance.attention_bound): the rounding of P to the input type and
+the FP32 score error move each weight by a relative eta, which moves the
+output by at most eta times the weighted spread of the row's values around it;
+then the FP32 accumulation and the output's own rounding.  On the benchmarked
+length (4096 keys) it is tight enough that dropping any one 64-key tile breaks
+it on the rows the workload test checks (tests/test_attention_bound.py).
 """
 import math
 
@@ -19,28 +19,21 @@ import torch
 import layout_algebra_amd as la
 import oracle
 import synth
-from parity import REL, exact_values, max_abs
+from parity import attention_bound, attention_workload_rows, exact_values, max_abs
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-IN_REL = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
-
-
-def attn_bound(q, k, v, o_ref, scale, in_kind, out_kind):
-    delta = abs(scale) * 2.0 ** -20 * q.shape[-1] * max_abs(q) * max_abs(k)
-    return (IN_REL[in_kind] + 4.0 * delta + 2.0 ** -20) * max_abs(v) + REL[out_kind] * np.abs(o_ref)
 
 
 def check(got, q, k, v, scale, in_kind, out_kind, what):
-    ref = oracle.attention_f64(exact_values(q), exact_values(k), exact_values(v), scale)
-    tol = attn_bound(q, k, v, ref, scale, in_kind, out_kind)
+    ref, tol = attention_bound(exact_values(q), exact_values(k), exact_values(v), scale, in_kind, out_kind)
     g = got.to(torch.float64).numpy()
     bad = ~(np.abs(g - ref) <= tol)
     if bad.any():
         i = tuple(np.argwhere(bad)[0])
         raise AssertionError("%s: %d elements out of tolerance; first at %s: gpu=%r oracle=%r tol=%r"
-                             % (what, int(bad.sum()), i, g[i], ref[i], tol if np.isscalar(tol) else tol[i]))
+                             % (what, int(bad.sum()), i, g[i], ref[i], tol[i]))
 
 
 def run(q, k, v, out_kind, scale):
@@ -123,9 +116,7 @@ def test_workload_sampled_rows():
     la.la_attention_run(x["Q"].to(DEV), x["K"].to(DEV), x["V"].to(DEV), O, w.scale)
     torch.cuda.synchronize()
     got = O.cpu()
-    g = torch.Generator().manual_seed(99)
-    for z in sorted(set(torch.randint(0, w.batch, (4,), generator=g).tolist()) | {0, w.batch - 1}):
-        rows = sorted(set(torch.randint(0, w.sq, (24,), generator=g).tolist()) | {0, w.sq - 1})
+    for z, rows in attention_workload_rows(w):
         check(got[z, rows], x["Q"][z, rows], x["K"][z], x["V"][z], w.scale, w.in_kind, w.out_kind, "entry %d" % z)
 
 

@@ -69,6 +69,38 @@ def test_batched_gemm(case):
     assert gaps_untouched(fc, batch, M, N, sc)
 
 
+P3_CASES = [
+    # (batch, M, N, K, in, out, pads (A, B, C), staging width): 257 to 512 workgroups of 64 x 64
+    # tiles over the whole batch, where the planner keeps three K blocks in flight
+    (100, 128, 128, 256, "bf16", "bf16", (8, 16, 24), 8),    # 400 workgroups, 16-byte aligned rows
+    (80, 100, 70, 45, "f16", "f32", (3, 5, 7), 2),            # 320 workgroups, 2-byte aligned rows
+]
+
+
+@pytest.mark.parametrize("case", P3_CASES, ids=["vec%d" % c[-1] for c in P3_CASES])
+def test_batched_three_blocks_in_flight(case):
+    batch, M, N, K, ik, ok, (pa, pb, pc), vec = case
+    print("batched three blocks", case, flush=True)
+    seed = 5 * M + 3 * N + K + batch
+    a = synth.normal((batch, M, K), seed, ik)
+    b = synth.normal((batch, K, N), seed + 1, ik, 0.5)
+    c = synth.uniform((batch, M, N), seed + 2, "f32").to(synth.torch_dtype(ok))
+    fa, A, sa = strided(a, pa)
+    fb, B, sb = strided(b, pb)
+    fc, C, sc = strided(c, pc)
+    plan = la.gemm_plan(M, N, K, CODE[ik], CODE[ok], batch=batch, stride_a=sa, stride_b=sb, stride_c=sc)
+    d = plan.describe()
+    assert d["kernel"] == "tiled_64x64x64" and d["prefetch_blocks"] == 3 and d["vec_elems"] == vec, d
+    assert 256 < d["grid"] * batch <= 512
+    la.gemm_run(plan, A, B, C, 0.5, 1.5)
+    torch.cuda.synchronize()
+    got = C.cpu()
+    for z in range(batch):
+        ref = oracle_gemm(a[z], b[z], ik, 0.5, 1.5, c[z].to(torch.float32))
+        assert_close(got[z], ref, K, a[z], b[z], ok, "matrix %d of %s" % (z, case))
+    assert gaps_untouched(fc, batch, M, N, sc)
+
+
 @pytest.mark.parametrize("shape", [(256, 256, 256), (96, 130, 70)], ids=["fast", "tiled"])
 def test_batched_broadcast_B(shape):
     """stride_b = 0: every matrix of A multiplies the same B."""

@@ -10,7 +10,7 @@ import torch
 
 import layout_algebra_amd as la
 import synth
-from parity import assert_close, oracle_gemm, sample_rows, swiglu_bound
+from parity import assert_close, band_rows, oracle_gemm, sample_rows, swiglu_bound
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +59,7 @@ def test_square4096_sampled_rows():
     w = synth.WORKLOADS["square4096"]
     x = synth.make_inputs(w)
     got = run_gemm(x["A"], x["B"], w.out_kind)
-    rows = sample_rows(w.M, 40, 2003)
+    rows = band_rows(w.M, seed=2003)                  # every 256-row tile band, each wave's first and last row
     ref = oracle_gemm(x["A"], x["B"], w.in_kind, rows=rows)
     assert_close(got[rows], ref, w.K, x["A"], x["B"], w.out_kind, "square4096")
 
@@ -81,7 +81,8 @@ def test_gate_up_sampled_rows():
     U = torch.empty_like(G)
     la.gemm_gate_up_run(plan, X, Wg, Wu, G, U)
     torch.cuda.synchronize()
-    rows = sample_rows(w.M, 24, 4004)
+    rows = band_rows(w.M, seed=4004)                  # every 256-row tile band, each wave's first and last row
+    assert len(rows) >= 2 * (w.M // 256)
     for name, W, out in (("G", x["Wg"], G), ("U", x["Wu"], U)):
         ref = oracle_gemm(x["A"], W, "bf16", rows=rows)
         assert_close(out.cpu()[rows], ref, w.K, x["A"], W, "bf16", "gate_up " + name)

@@ -100,3 +100,29 @@ def test_planted_mistakes_fail(kind, monkeypatch):
         except (AssertionError, ValueError):
             failed += 1
     assert failed >= 1, kind
+
+
+# ---- the normalised weights (used by the per-row parity bound of the GPU tests) ----
+
+def test_weights_hand_worked_two_keys():
+    w = oracle.attention_weights_f64([[1.0, 0.0]], [[1.0, 0.0], [0.0, 1.0]], 1.0)
+    e = math.e
+    assert abs(w[0, 0] - e / (e + 1.0)) < 1e-15 and abs(w[0, 1] - 1.0 / (e + 1.0)) < 1e-15
+
+
+def test_weights_equal_keys_are_uniform():
+    q = synth.normal((3, 32), 91, "f32").double().numpy()
+    k = np.tile(synth.normal((1, 32), 92, "f32").double().numpy(), (25, 1))
+    assert np.allclose(oracle.attention_weights_f64(q, k, 0.3), 1.0 / 25, rtol=1e-13, atol=0)
+
+
+def test_weights_match_torch_softmax_and_give_the_output():
+    q = synth.normal((2, 9, 64), 93, "f32").double()
+    k = synth.normal((2, 40, 64), 94, "f32").double()
+    v = synth.normal((2, 40, 64), 95, "f32").double()
+    w = oracle.attention_weights_f64(q.numpy(), k.numpy(), 0.125)
+    want = torch.softmax(0.125 * (q @ k.transpose(-1, -2)), dim=-1).numpy()
+    assert np.allclose(w, want, rtol=1e-13, atol=1e-16)
+    assert np.allclose(w.sum(axis=-1), 1.0, rtol=0, atol=1e-14) and (w >= 0).all()
+    assert np.allclose(w @ v.numpy(), oracle.attention_f64(q.numpy(), k.numpy(), v.numpy(), 0.125), rtol=1e-12,
+                       atol=1e-14)

@@ -4,6 +4,13 @@ Each check is fixed by something other than the oracle itself: values the
 Tylo.jl pages print (tests/golden/layout_pages.json), the pages' closed form for
 128-byte swizzled rows, and brute-force properties that any correct
 implementation of the stated semantics must have.
+
+Parity unpinned: the element offsets of the 64-byte and 32-byte swizzle rows
+(SharedTilePlan with row_bytes 64 or 32, i.e. Swizzle{2,M,3} and Swizzle{1,M,3}).
+No page prints an offset for them, so only invariants check them here
+(bijection onto the tile, involution, the low M bits kept, 16-byte chunks kept
+whole); the planner's C++ copy of the plan is compared with this oracle, not
+with the pages.
 """
 import random
 
