@@ -1,5 +1,5 @@
 // extern "C" boundary of the GEMM library (declarations and contracts in
-// include/la_gemm.h).
+// include/la_gemm.h; the measurement aid in include/la_probe.h).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/la_gemm.h"
+#include "../../include/la_probe.h"
 #include "attention.hpp"
 #include "kernel_table.hpp"
 #include "launch.hpp"

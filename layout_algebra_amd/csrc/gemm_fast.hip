@@ -18,13 +18,7 @@ hipError_t go_fast(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
         return hipGetLastError();
       }
     }
-    if constexpr (C::SCHED == 2) {
-      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
-    } else if constexpr (C::SCHED == 3) {
-      hipLaunchKernelGGL((gemm_fast_sp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((gemm_fast_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
-    }
+    hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -18,10 +18,10 @@
 //  * Large tiles (256 x 256, or 256 x 2*128 for gate/up) with 8 waves: one
 //    tile per CU at 4096^2, two waves per SIMD.
 //  * A multi-stage LDS ring (STAGES buffers) keeps STAGES-1 K blocks in
-//    flight; one workgroup barrier per K block.
-//  * Inside a K block the fragments of sub-step s+1 are read while the MFMAs
-//    of sub-step s run (two register sets), and the instruction scheduler is
-//    told to alternate MFMAs with LDS reads so neither unit idles.
+//    flight.
+//  * Ping-pong wave groups: the 8 waves form two groups of four (one wave of
+//    each group per SIMD); while one group runs a K block's MFMAs the other
+//    reads its fragments and issues its direct loads (gemm_fast_pp_kernel).
 // The LDS maps are Swizzle{AB,AM,AS} o (BM,BK):(BK,1) for A and
 // Swizzle{BB,BMb,BS} o (BK,BN):(BN,1) for B (element offsets).
 #pragma once
@@ -35,17 +35,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LAK_LDS __attribute__((address_space(3)))
 #define LAK_GLB __attribute__((address_space(1)))
 
-// Scheduler group masks (LLVM AMDGPU sched_group_barrier).
-enum : int { SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100 };
-
 template <class TI, class C>
 struct Fast {
   static constexpr int BM = C::BM, BN = C::BN, NB = C::NB, WM = C::WM, WN = C::WN, BK = C::BK;
   static constexpr int STAGES = C::STAGES;
-  static constexpr bool SCHED_HINTS = C::SCHED != 4;     // 4: software pipeline without scheduler groups
-  static constexpr bool DMA_IN_C = C::DMA_IN_C;           // ping-pong: issue direct loads in the C phase
   static constexpr bool BKM = C::BKMAJOR;                 // B stored [N, K] (K contiguous) instead of [K, N]
-  static constexpr int PRIO = C::PRIO;                    // ping-pong: 0 none, 1 raise C phase, 2 raise M phase
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -57,8 +51,6 @@ struct Fast {
   static constexpr int A_LOADS = A_ELEMS / 512 / NW;       // 1 KB (512 elements) per wave instruction
   static constexpr int B_LOADS = B_ELEMS / 512 / NW;
   static constexpr int LOADS_PER_STAGE = A_LOADS + NB * B_LOADS;
-  static constexpr int READS_PER_SUB = FM + (C::BKMAJOR ? 1 : 2) * NB * FN;   // LDS read instructions per sub-step
-  static constexpr int MFMA_PER_SUB = NB * FM * FN;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_LOADS * 512 * NW == A_ELEMS && B_LOADS * 512 * NW == B_ELEMS, "blocks must split into whole KB per wave");
   static_assert(C::AM >= 3 && C::BMb >= 3, "swizzles must keep 16-byte chunks whole");
@@ -182,46 +174,6 @@ struct Fast {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[t][i][j] = mfma_32x32x16<TI>(f.a[i], f.b[t][j], acc[t][i][j]);
   }
-
-  // Ask the scheduler to alternate the MFMAs of one sub-step with the LDS
-  // reads of the next.
-  static __device__ __forceinline__ void interleave() {
-    if constexpr (C::SCHED) {
-      constexpr int pairs = MFMA_PER_SUB < READS_PER_SUB ? MFMA_PER_SUB : READS_PER_SUB;
-#pragma unroll
-      for (int i = 0; i < pairs; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-      }
-      if constexpr (MFMA_PER_SUB > pairs) __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFMA_PER_SUB - pairs, 0);
-      if constexpr (READS_PER_SUB > pairs) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, READS_PER_SUB - pairs, 0);
-    }
-  }
-
-  static __device__ __forceinline__ void compute(const LAK_LDS uint16_t* stage, f32x16 (&acc)[NB][FM][FN], const Lane& ln) {
-    if constexpr (C::SCHED) {
-      Frags f0, f1;
-      read_frags(stage, 0, ln, f0);
-#pragma unroll
-      for (int s = 0; s < SUB; s += 2) {
-        if (s + 1 < SUB) read_frags(stage, s + 1, ln, f1);
-        mma(f0, acc);
-        interleave();
-        if (s + 1 < SUB) {
-          if (s + 2 < SUB) read_frags(stage, s + 2, ln, f0);
-          mma(f1, acc);
-          interleave();
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < SUB; ++s) {
-        Frags f;
-        read_frags(stage, s, ln, f);
-        mma(f, acc);
-      }
-    }
-  }
 };
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits
@@ -343,83 +295,11 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[NB][F::FM][F::FN], const 
                                       col0, win, lane, g.red, g.R);
 }
 
-// The same barrier without waiting for this wave's outstanding LDS reads, for
-// schedules whose in-flight reads only target buffers nobody refills next.
-__device__ __forceinline__ void block_barrier_nowait() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <class TI, class TO, class C, bool RED = false>
-__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_kernel(const TiledArgs g_in) {
-  const TiledArgs g = at_batch(g_in);
-  using F = Fast<TI, C>;
-  constexpr int NB = C::NB;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
-  LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % C::WM, wn = wave / C::WM;
-  int tm, tn;
-  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-  const int64_t m0 = int64_t(tm) * C::BM, n0 = int64_t(tn) * C::BN;
-
-  typename F::Src src;
-  F::make_src(src, wave, lane, g.lda, g.ldb);
-  const typename F::Lane ln(wm, wn, lane);
-  const uint16_t* a_tile = g.A + m0 * g.lda;
-  const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
-  const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
-
-  f32x16 acc[NB][F::FM][F::FN];
-#pragma unroll
-  for (int t = 0; t < NB; ++t)
-#pragma unroll
-    for (int i = 0; i < F::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < F::FN; ++j) acc[t][i][j] = f32x16{};
-
-  // Pipeline over K blocks with STAGES LDS buffers.  Iteration kt: wait until
-  // this wave's loads of block kt have landed, barrier (then every wave's
-  // loads of block kt are visible and every wave has finished reading block
-  // kt-1), refill the buffer of block kt-1 with block kt+STAGES-1, compute kt.
-  const int nk = int(g.K / F::BK);
-#pragma unroll
-  for (int p = 0; p < F::STAGES - 1; ++p) {
-    if (p < nk) {
-      const int64_t k1 = int64_t(p) * F::BK;
-      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb), NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
-    }
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    // loads issued after block kt: blocks kt+1 .. min(kt+STAGES-2, nk-1)
-    if (kt + F::STAGES - 2 <= nk - 1) {
-      wait_vmcnt<(F::STAGES - 2) * F::LOADS_PER_STAGE>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    block_barrier();
-    const int kn = kt + F::STAGES - 1;
-    if (kn < nk) {
-      const int64_t k1 = int64_t(kn) * F::BK;
-      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
-               NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
-    }
-    F::compute(lds + (kt % F::STAGES) * F::STAGE, acc, ln);
-  }
-
-  block_barrier();                         // every wave is done with the stage buffers
-  epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
-}
-
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each
 // group per SIMD).  Each K block is handled in two phases per group:
 //   M: read all fragments of the block from LDS into registers and issue this
 //      wave's share of the global->LDS loads of a later block;
-//   C: run the block's MFMAs back to back at raised wave priority.
+//   C: run the block's MFMAs back to back.
 // Group 1 runs one phase behind group 0, so on every SIMD one wave feeds the
 // matrix core while the other moves data.  Every phase starts with a
 // workgroup barrier (s_barrier without a memory fence, so direct loads stay in
@@ -494,146 +374,26 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   for (int kt = 0; kt < nk; ++kt) {
     if (group == 0) wait_block<F>(kt, nk);
     phase_barrier();                       // M(kt)
-    if (F::PRIO == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < F::SUB; ++s) F::read_frags(lds + (kt % F::STAGES) * F::STAGE, s, ln, f[s]);
     const int kn = kt + F::STAGES - 1;
-    if (!F::DMA_IN_C && kn < nk) {
+    if (kn < nk) {
       const int64_t k1 = int64_t(kn) * F::BK;
       F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
                NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): fragments in registers
-    if (F::PRIO == 2) __builtin_amdgcn_s_setprio(0);
     if (group == 1) {
       if (kt + 1 < nk) wait_block<F>(kt + 1, nk);
     }
     phase_barrier();                       // C(kt)
-    if (F::DMA_IN_C && kn < nk) {
-      // the buffer of block kt-1 was read by both groups before this phase began
-      const int64_t k1 = int64_t(kn) * F::BK;
-      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
-               NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
-    }
-    if (F::PRIO == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < F::SUB; ++s) F::mma(f[s], acc);
-    if (F::PRIO == 1) __builtin_amdgcn_s_setprio(0);
   }
   if (group == 0) phase_barrier();         // t = 2 nk: group 0 idles while group 1 finishes
 
   // After the last phase barrier every M phase (all LDS reads) is complete,
   // so the waves may reuse the stage buffers as epilogue windows.
-  epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
-}
-
-// Software-pipelined schedule.  Every wave keeps two fragment sets of one
-// 16-deep MFMA sub-step each: while the MFMAs of sub-step s run on one set,
-// the LDS reads of the next sub-step fill the other, alternating one MFMA and
-// one LDS read (scheduler groups), so LDS latency hides behind the wave's own
-// matrix work.  The next sub-step of the last one in block kt is sub-step 0
-// of block kt+1; one barrier per K block, placed before that last sub-step,
-// guarantees that block kt+1 has landed (each wave waited for its own loads
-// of it) and that every wave has finished reading block kt-1, whose buffer is
-// then refilled with block kt+STAGES-1.
-template <class F>
-__device__ __forceinline__ void wait_block_ahead(int kb, int nk) {
-  // loads issued so far: blocks .. min(kb+STAGES-3, nk-1); those newer than kb may stay in flight
-  if (kb + F::STAGES - 3 <= nk - 1) {
-    wait_vmcnt<(F::STAGES - 3) * F::LOADS_PER_STAGE>();
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-template <class F, class TI>
-__device__ __forceinline__ void sp_substep(const LAK_LDS uint16_t* next_stage, int next_s, const typename F::Lane& ln,
-                                           const typename F::Frags& cur, typename F::Frags& nxt,
-                                           f32x16 (&acc)[F::NB][F::FM][F::FN]) {
-  F::read_frags(next_stage, next_s, ln, nxt);
-  F::mma(cur, acc);
-  if constexpr (F::SCHED_HINTS) F::interleave();
-}
-
-template <class TI, class TO, class C, bool RED = false>
-__global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_sp_kernel(const TiledArgs g_in) {
-  const TiledArgs g = at_batch(g_in);
-  using F = Fast<TI, C>;
-  constexpr int NB = C::NB;
-  static_assert(C::STAGES >= 3, "the software pipeline reads one block ahead");
-  static_assert(F::SUB % 2 == 0, "sub-steps alternate between two fragment sets");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
-  LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % C::WM, wn = wave / C::WM;
-  int tm, tn;
-  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-  const int64_t m0 = int64_t(tm) * C::BM, n0 = int64_t(tn) * C::BN;
-
-  typename F::Src src;
-  F::make_src(src, wave, lane, g.lda, g.ldb);
-  const typename F::Lane ln(wm, wn, lane);
-  const uint16_t* a_tile = g.A + m0 * g.lda;
-  const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
-  const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
-
-  f32x16 acc[NB][F::FM][F::FN];
-#pragma unroll
-  for (int t = 0; t < NB; ++t)
-#pragma unroll
-    for (int i = 0; i < F::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < F::FN; ++j) acc[t][i][j] = f32x16{};
-
-  const int nk = int(g.K / F::BK);
-#pragma unroll
-  for (int p = 0; p < F::STAGES - 1; ++p) {
-    if (p < nk) {
-      const int64_t k1 = int64_t(p) * F::BK;
-      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb), NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
-    }
-  }
-  if (F::STAGES - 2 <= nk - 1) {          // block 0 landed; blocks 1 .. STAGES-2 may still fly
-    wait_vmcnt<(F::STAGES - 2) * F::LOADS_PER_STAGE>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  block_barrier();
-  typename F::Frags f0, f1;
-  F::read_frags(lds, 0, ln, f0);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    const LAK_LDS uint16_t* cur = lds + (kt % F::STAGES) * F::STAGE;
-    // after the last block the look-ahead reads re-read the current buffer (valid, unused)
-    const LAK_LDS uint16_t* nxt = more ? lds + ((kt + 1) % F::STAGES) * F::STAGE : cur;
-#pragma unroll
-    for (int s = 0; s < F::SUB; s += 2) {
-      // even sub-step s: compute from f0, read sub-step s+1 (same block) into f1
-      sp_substep<F, TI>(cur, s + 1, ln, f0, f1, acc);
-      if (s + 2 == F::SUB) {
-        // last sub-step of the block reads block kt+1: make it visible, recycle block kt-1's buffer
-        // (this wave's reads of block kt-1 were consumed by its MFMAs of block kt-1; the reads
-        // still in flight target block kt, which is not refilled here)
-        if (more) wait_block_ahead<F>(kt + 1, nk);
-        block_barrier_nowait();
-        const int kn = kt + F::STAGES - 1;
-        if (kn < nk) {
-          const int64_t k1 = int64_t(kn) * F::BK;
-          F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
-                   NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
-        }
-        sp_substep<F, TI>(nxt, 0, ln, f1, f0, acc);
-      } else {
-        sp_substep<F, TI>(cur, s + 2, ln, f1, f0, acc);
-      }
-    }
-  }
-
-  block_barrier();                         // every wave is done with the stage buffers
   epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 

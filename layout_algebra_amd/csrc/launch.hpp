@@ -58,21 +58,18 @@ enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
 // Compile-time parameters of the fast kernels (one source of truth for the
 // template instantiations and the planner's table).
-// SCHED: 0 = compiler schedule, 1 = interleave hints, 2 = ping-pong wave groups.
 // Swizzles were chosen with the LDS bank-conflict counter: gfx950 serves LDS
 // reads from 64 four-byte banks (256 bytes per cycle), so a 16-byte read of
 // 16 lanes must touch 16 distinct 16-byte slots of a 256-byte window.
 struct CfgFast256 {
-  static constexpr int BM = 256, BN = 256, NB = 1, WM = 2, WN = 4, BK = 32, STAGES = 4, SCHED = 2;
-  static constexpr bool DMA_IN_C = false, BKMAJOR = false;
-  static constexpr int PRIO = 0;
+  static constexpr int BM = 256, BN = 256, NB = 1, WM = 2, WN = 4, BK = 32, STAGES = 4;
+  static constexpr bool BKMAJOR = false;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 3;  // B: Swizzle{2,5,3} over 512-byte rows
 };
 struct CfgFastGU {
-  static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4, BK = 32, STAGES = 4, SCHED = 2;
-  static constexpr bool DMA_IN_C = false, BKMAJOR = false;
-  static constexpr int PRIO = 0;
+  static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4, BK = 32, STAGES = 4;
+  static constexpr bool BKMAJOR = false;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 2;  // B: Swizzle{2,5,2} over 256-byte rows
 };
