@@ -643,10 +643,11 @@ def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):
 
 def gemm_tolerance(w, a, b, ref):
     """Agreement bound of a GEMM output: 2^-20 K max|A| max|B| (FP32 accumulation) plus the
-    output's own rounding for 16-bit outputs (for fp32 outputs only when K = 0, where the result is
-    beta * C rounded to fp32)."""
+    output's own rounding for 16-bit outputs (for fp32 outputs only where the result carries
+    beta * C_old or K = 0, whose final fp32 rounding no accumulation term covers)."""
     acc = 2.0 ** -20 * w.K * float(a.abs().max()) * float(b.abs().max())
-    rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22 if w.K == 0 else 0.0}[w.out_kind]
+    f32_rel = 2.0 ** -22 if (w.K == 0 or w.beta != 0.0) else 0.0
+    rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": f32_rel}[w.out_kind]
     return acc + rel * np.abs(ref)
 
 

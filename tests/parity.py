@@ -5,10 +5,12 @@ Agreement bound (elementwise):
     |gpu - oracle| <= 2^-20 * K * max|A| * max|B|  +  r * |oracle|
 with r = 2^-8 for bf16 outputs (the output's own rounding) and 2^-11 for fp16
 outputs.  The first term is the FP32 accumulation allowance.  FP32 outputs add
-a rounding term only when K = 0, where the first term is zero and the result
-is beta * C rounded to fp32 (r = 2^-22 there); for K > 0 the final FP32
-rounding (at most 2^-24 |out|) must sit well inside the first term, which
-bound() checks instead of silently widening the tolerance.
+a rounding term (r = 2^-22) only where the result carries beta * C_old
+(beta != 0) or K = 0: there the final FP32 rounding of the beta * C_old term
+is not part of any accumulation (with K = 1 and beta = 1.25 it exceeds the
+first term).  With beta = 0 and K > 0 the final FP32 rounding (at most
+2^-24 |out|) must sit well inside the first term, which bound() checks instead
+of silently widening the tolerance.
 """
 import numpy as np
 import torch
@@ -24,11 +26,11 @@ def max_abs(t):
     return float(t.abs().max()) if t.numel() else 0.0
 
 
-def bound(K, a, b, ref, out_kind):
+def bound(K, a, b, ref, out_kind, beta=0.0):
     acc = 2.0 ** -20 * K * max_abs(a) * max_abs(b)
     if out_kind == "f32":
-        if K == 0:
-            return REL["f32"] * np.abs(ref)
+        if beta != 0.0 or K == 0:
+            return acc + REL["f32"] * np.abs(ref)
         peak = float(np.abs(ref).max()) if np.size(ref) else 0.0
         if 2.0 ** -22 * peak > acc:
             raise ValueError("fp32 output: the final rounding (2^-24 of %g) is not covered by the accumulation "
@@ -37,9 +39,9 @@ def bound(K, a, b, ref, out_kind):
     return acc + REL[out_kind] * np.abs(ref)
 
 
-def assert_close(gpu, ref, K, a, b, out_kind, what=""):
+def assert_close(gpu, ref, K, a, b, out_kind, what="", beta=0.0):
     g = gpu.detach().to("cpu", torch.float64).numpy()
-    tol = bound(K, a, b, ref, out_kind)
+    tol = bound(K, a, b, ref, out_kind, beta)
     err = np.abs(g - ref)
     bad = ~(err <= tol)
     if bad.any():

@@ -65,7 +65,7 @@ def test_batched_gemm(case):
     got = C.cpu()
     for z in range(batch):
         ref = oracle_gemm(a[z], b[z], ik, 0.5, 1.5, c[z].to(torch.float32))
-        assert_close(got[z], ref, K, a[z], b[z], ok, "matrix %d of %s" % (z, case))
+        assert_close(got[z], ref, K, a[z], b[z], ok, "matrix %d of %s" % (z, case), beta=1.5)
     assert gaps_untouched(fc, batch, M, N, sc)
 
 
@@ -97,7 +97,7 @@ def test_batched_three_blocks_in_flight(case):
     got = C.cpu()
     for z in range(batch):
         ref = oracle_gemm(a[z], b[z], ik, 0.5, 1.5, c[z].to(torch.float32))
-        assert_close(got[z], ref, K, a[z], b[z], ok, "matrix %d of %s" % (z, case))
+        assert_close(got[z], ref, K, a[z], b[z], ok, "matrix %d of %s" % (z, case), beta=1.5)
     assert gaps_untouched(fc, batch, M, N, sc)
 
 

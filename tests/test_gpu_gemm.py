@@ -52,7 +52,7 @@ def test_workload_full_parity(name):
     print("case", name, flush=True)
     got = run_gemm(x["A"], x["B"], w.out_kind, w.alpha, w.beta, x.get("C"))
     ref = oracle_gemm(x["A"], x["B"], w.in_kind, w.alpha, w.beta, x.get("C"))
-    assert_close(got, ref, w.K, x["A"], x["B"], w.out_kind, name)
+    assert_close(got, ref, w.K, x["A"], x["B"], w.out_kind, name, beta=w.beta)
 
 
 def test_square4096_sampled_rows():
@@ -104,7 +104,7 @@ def test_shapes_and_types(shape, in_kind, out_kind):
     alpha, beta = 0.75, 1.25
     got = run_gemm(a, b, out_kind, alpha, beta, c)
     ref = oracle_gemm(a, b, in_kind, alpha, beta, c.to(torch.float32))
-    assert_close(got, ref, K, a, b, out_kind, "shape %s" % (shape,))
+    assert_close(got, ref, K, a, b, out_kind, "shape %s" % (shape,), beta=beta)
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
@@ -121,7 +121,7 @@ def test_general_kernel_both_tile_sizes(in_kind, out_kind):
         c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
         got = run_gemm(a, b, out_kind, 1.5, -0.5, c, expect=kernel, large_tiles=large)
         ref = oracle_gemm(a, b, in_kind, 1.5, -0.5, c.to(torch.float32))
-        assert_close(got, ref, K, a, b, out_kind, "%s %dx%dx%d" % (kernel, M, N, K))
+        assert_close(got, ref, K, a, b, out_kind, "%s %dx%dx%d" % (kernel, M, N, K), beta=-0.5)
 
 
 LONG_K = [((70, 100, 65536), False, "tiled_64x64"), ((256, 256, 65536), True, "fast_256x256"),
@@ -179,7 +179,7 @@ def test_general_kernel_random_layouts(case):
     la.gemm_run(plan, A, B, C, alpha, beta)
     torch.cuda.synchronize()
     ref = oracle_gemm(a, b, in_kind, alpha, beta, c.to(torch.float32))
-    assert_close(C.cpu(), ref, K, a, b, out_kind, "random layout case %d" % case)
+    assert_close(C.cpu(), ref, K, a, b, out_kind, "random layout case %d" % case, beta=beta)
 
 
 PREFETCH_SHAPES = [(200, 136, 64), (130, 72, 128), (64, 64, 192), (100, 200, 1000), (96, 96, 8), (65, 130, 320),
@@ -203,7 +203,7 @@ def test_general_kernel_prefetch_depths(shape, out_kind):
     assert d["vec_elems"] == (8 if K % 8 == 0 and N % 8 == 0 else 2)
     got = run_gemm(a, b, out_kind, -0.75, 1.5, c, expect="tiled_64x64")
     ref = oracle_gemm(a, b, "bf16", -0.75, 1.5, c.to(torch.float32))
-    assert_close(got, ref, K, a, b, out_kind, "prefetch %s" % (shape,))
+    assert_close(got, ref, K, a, b, out_kind, "prefetch %s" % (shape,), beta=1.5)
 
 
 DEEP_SHAPES = [(1088, 1088, 64, False), (1088, 1088, 128, False), (1088, 1088, 192, False), (1000, 1100, 130, False),
@@ -227,7 +227,7 @@ def test_general_kernel_three_blocks_in_flight(shape, out_kind):
     assert d["prefetch_blocks"] == 3
     got = run_gemm(a, b, out_kind, 1.25, -0.5, c, b_kmajor=km, expect="tiled_64x64")
     ref = oracle_gemm(a, b, "f16", 1.25, -0.5, c.to(torch.float32))
-    assert_close(got, ref, K, a, b, out_kind, "three blocks in flight %s" % (shape,))
+    assert_close(got, ref, K, a, b, out_kind, "three blocks in flight %s" % (shape,), beta=-0.5)
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
@@ -297,7 +297,7 @@ def test_ragged_never_writes_outside_C():
     assert torch.all(big[:M, N:] == 12345.0)
     assert torch.all(big[M:, :] == 12345.0)
     ref = oracle_gemm(x["A"], x["B"], "f16", w.alpha, w.beta, x["C"])
-    assert_close(big[:M, :N], ref, K, x["A"], x["B"], "f32", "ragged window")
+    assert_close(big[:M, :N], ref, K, x["A"], x["B"], "f32", "ragged window", beta=w.beta)
 
 
 def test_deterministic_and_plan_reuse():
@@ -459,7 +459,7 @@ def test_fast_kernel_shapes(shape, in_kind, out_kind):
     c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
     got = run_gemm(a, b, out_kind, -1.25, 0.5, c, expect="fast_", large_tiles=True)
     ref = oracle_gemm(a, b, in_kind, -1.25, 0.5, c.to(torch.float32))
-    assert_close(got, ref, K, a, b, out_kind, "fast %s" % (shape,))
+    assert_close(got, ref, K, a, b, out_kind, "fast %s" % (shape,), beta=0.5)
 
 
 @pytest.mark.parametrize("large", [True, False], ids=["large_tiles", "planned"])
@@ -513,7 +513,7 @@ def test_skinny_kernel_shapes(shape, in_kind, out_kind):
     c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
     got = run_gemm(a, b, out_kind, 0.5, -2.0, c)
     ref = oracle_gemm(a, b, in_kind, 0.5, -2.0, c.to(torch.float32))
-    assert_close(got, ref, K, a, b, out_kind, "skinny %s" % (shape,))
+    assert_close(got, ref, K, a, b, out_kind, "skinny %s" % (shape,), beta=-2.0)
 
 
 def test_skinny_identity_is_exact():
@@ -565,7 +565,7 @@ def test_bkmajor_shapes(case, in_kind, out_kind):
     c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
     got = run_gemm(a, b, out_kind, 0.5, 1.5, c, b_kmajor=True, expect=expect, large_tiles=expect.startswith("fast"))
     ref = oracle_gemm(a, b, in_kind, 0.5, 1.5, c.to(torch.float32))
-    assert_close(got, ref, K, a, b, out_kind, "K-major B %s" % ((M, N, K),))
+    assert_close(got, ref, K, a, b, out_kind, "K-major B %s" % ((M, N, K),), beta=1.5)
 
 
 def test_bkmajor_permutation_is_exact():

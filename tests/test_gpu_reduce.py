@@ -53,7 +53,7 @@ def check(op, a, b, in_kind, out_kind, alpha, beta, c, got_c, got_r, what):
     K = a.shape[1]
     cin = None if c is None else c.to(torch.float32).numpy()
     out, r = oracle.gemm_row_reduce_f64(synth.bits(a), in_kind, synth.bits(b), in_kind, op, alpha, beta, cin)
-    assert_close(got_c, out, K, a, b, out_kind, what + " C")
+    assert_close(got_c, out, K, a, b, out_kind, what + " C", beta=beta)
     tol = red_bound(op, K, a, b, out)
     err = np.abs(got_r - r)
     bad = ~(err <= tol)
