@@ -240,6 +240,35 @@ gemm_status la_tile_plan_offset(int elem_bytes, int64_t d1, int64_t d2, int inne
                                 int row_bytes, int64_t c1, int64_t c2,
                                 int64_t* out_offset, int64_t* out_transfer_bytes);
 
+/* ---- the same algebra on the pages' own notation, host only ----
+ * A layout is written as the Tylo.jl page "Layouts, storage and ownership"
+ * writes it: "shape:stride" with nested tuples, e.g. "(16,32):(32,1)" or
+ * "((8,4),5):((1,8),128)" (section "Static layout notation").  A coordinate is a
+ * nested tuple congruent to the shape, an integer per mode, or one integer
+ * index split first mode fastest (section "A layout is a function").  Strings
+ * are NUL-terminated; results are written to `out` (at most len bytes with the
+ * NUL; GEMM_ERR_RESOURCE if they do not fit).  Malformed text, coordinates
+ * outside the domain and tiles that do not divide their mode return
+ * GEMM_ERR_INVALID_ARG with a description in gemm_last_error().
+ * la_layout_eval_str: offset of `coord`.
+ * la_layout_tile_str: tile() with one extent per flat top-level mode: mode i
+ *   of extent s and stride d becomes (tile[i], s / tile[i]) : (d, tile[i] * d).
+ * la_layout_coalesce_str: coalesce(): unit modes dropped, (s0:d0)(s1:d1)
+ *   merged when d1 = s0 * d0, the same map on the linear domain.
+ * la_layout_permute_str: permutedims: the top-level modes reversed.
+ * la_layout_cosize_str: 1 + the largest offset (non-negative strides).
+ * la_view_window_eval: Swizzle{b,m,s} o layout, windowed at `origin` with
+ *   `extent` (rank values, one per top-level mode, inside the parent's domain;
+ *   section "Swizzle phase belongs to the allocation": the window keeps the
+ *   parent's map and origin), evaluated at `coord` (rank values). */
+gemm_status la_layout_eval_str(const char* layout, const char* coord, int64_t* out_offset);
+gemm_status la_layout_tile_str(const char* layout, const int64_t* tile, int32_t rank, char* out, size_t len);
+gemm_status la_layout_coalesce_str(const char* layout, char* out, size_t len);
+gemm_status la_layout_permute_str(const char* layout, char* out, size_t len);
+gemm_status la_layout_cosize_str(const char* layout, int64_t* out_cosize);
+gemm_status la_view_window_eval(int32_t b, int32_t m, int32_t s, const char* layout, const int64_t* origin,
+                                const int64_t* extent, int32_t rank, const int64_t* coord, int64_t* out_offset);
+
 const char* gemm_status_string(gemm_status s);
 const char* gemm_last_error(void);
 

@@ -15,6 +15,8 @@ EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
     "la_rms_norm_run", "la_attention_run", "la_probe_mfma", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
+    "la_layout_eval_str", "la_layout_tile_str", "la_layout_coalesce_str", "la_layout_permute_str",
+    "la_layout_cosize_str", "la_view_window_eval",
     "gemm_status_string", "gemm_last_error",
 )
 
@@ -81,6 +83,12 @@ def load():
         "la_layout_eval_index": ([p64, p64, i32, i64, p64], i32),
         "la_swizzle_apply": ([i32, i32, i32, i64, p64], i32),
         "la_tile_plan_offset": ([i32, i64, i64, i32, i32, i64, i64, p64, p64], i32),
+        "la_layout_eval_str": ([ctypes.c_char_p, ctypes.c_char_p, p64], i32),
+        "la_layout_tile_str": ([ctypes.c_char_p, p64, i32, ctypes.c_char_p, ctypes.c_size_t], i32),
+        "la_layout_coalesce_str": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_size_t], i32),
+        "la_layout_permute_str": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_size_t], i32),
+        "la_layout_cosize_str": ([ctypes.c_char_p, p64], i32),
+        "la_view_window_eval": ([i32, i32, i32, ctypes.c_char_p, p64, p64, i32, p64, p64], i32),
         "gemm_status_string": ([i32], ctypes.c_char_p),
         "gemm_last_error": ([], ctypes.c_char_p),
     }
@@ -143,7 +151,7 @@ def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, g
 
 
 def gemm_plan_describe(plan):
-    buf = ctypes.create_string_buffer(4096)
+    buf = ctypes.create_string_buffer(16384)
     _check(load().gemm_plan_describe(plan.handle, buf, len(buf)))
     return json.loads(buf.value.decode())
 
@@ -359,3 +367,58 @@ def la_tile_plan_offset(elem_bytes, shape, inner_axis, row_bytes, coord):
     _check(load().la_tile_plan_offset(int(elem_bytes), int(shape[0]), int(shape[1]), int(inner_axis), int(row_bytes),
                                       int(coord[0]), int(coord[1]), ctypes.byref(off), ctypes.byref(tb)))
     return off.value, tb.value
+
+
+# layouts in the pages' notation ("shape:stride", nested tuples)
+def _nested(x):
+    """A Python int or nested tuple/list -> the pages' tuple text."""
+    if isinstance(x, (list, tuple)):
+        return "(" + ",".join(_nested(v) for v in x) + ")"
+    return str(int(x))
+
+
+def _layout_text(layout):
+    """A "shape:stride" string, or a (shape, stride) pair of ints / nested tuples."""
+    if isinstance(layout, str):
+        return layout
+    shape, stride = layout
+    return _nested(shape) + ":" + _nested(stride)
+
+
+def _text_out(fn, *args):
+    buf = ctypes.create_string_buffer(4096)
+    _check(fn(*args, buf, len(buf)))
+    return buf.value.decode()
+
+
+def la_layout_eval_str(layout, coord):
+    out = ctypes.c_int64()
+    c = coord if isinstance(coord, str) else _nested(coord)
+    _check(load().la_layout_eval_str(_layout_text(layout).encode(), c.encode(), ctypes.byref(out)))
+    return out.value
+
+
+def la_layout_tile_str(layout, tile):
+    return _text_out(load().la_layout_tile_str, _layout_text(layout).encode(), _i64s(tile), len(tile))
+
+
+def la_layout_coalesce_str(layout):
+    return _text_out(load().la_layout_coalesce_str, _layout_text(layout).encode())
+
+
+def la_layout_permute_str(layout):
+    return _text_out(load().la_layout_permute_str, _layout_text(layout).encode())
+
+
+def la_layout_cosize_str(layout):
+    out = ctypes.c_int64()
+    _check(load().la_layout_cosize_str(_layout_text(layout).encode(), ctypes.byref(out)))
+    return out.value
+
+
+def la_view_window_eval(swizzle, layout, origin, extent, coord):
+    out = ctypes.c_int64()
+    b, m, s = swizzle
+    _check(load().la_view_window_eval(int(b), int(m), int(s), _layout_text(layout).encode(), _i64s(origin),
+                                      _i64s(extent), len(origin), _i64s(coord), ctypes.byref(out)))
+    return out.value

@@ -405,4 +405,76 @@ gemm_status la_tile_plan_offset(int elem_bytes, int64_t d1, int64_t d2, int inne
   return GEMM_OK;
 }
 
+namespace {
+gemm_status copy_out(const std::string& text, char* out, size_t len) {
+  if (text.size() + 1 > len) return set_err(GEMM_ERR_RESOURCE, "output buffer of " + std::to_string(len) + " bytes is too small");
+  std::memcpy(out, text.c_str(), text.size() + 1);
+  return GEMM_OK;
+}
+}  // namespace
+
+gemm_status la_layout_eval_str(const char* layout, const char* coord, int64_t* out_offset) {
+  if (!layout || !coord || !out_offset) return set_err(GEMM_ERR_NULL, "NULL argument");
+  try {
+    *out_offset = la::parse_layout(layout)(la::parse_tree(coord));
+  } catch (const std::exception& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+  return GEMM_OK;
+}
+
+gemm_status la_layout_tile_str(const char* layout, const int64_t* tile, int32_t rank, char* out, size_t len) {
+  if (!layout || !tile || !out) return set_err(GEMM_ERR_NULL, "NULL argument");
+  if (rank <= 0 || rank > 16) return set_err(GEMM_ERR_INVALID_ARG, "rank must be 1..16");
+  try {
+    return copy_out(la::tile(la::parse_layout(layout), std::vector<int64_t>(tile, tile + rank)).str(), out, len);
+  } catch (const std::exception& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+}
+
+gemm_status la_layout_coalesce_str(const char* layout, char* out, size_t len) {
+  if (!layout || !out) return set_err(GEMM_ERR_NULL, "NULL argument");
+  try {
+    return copy_out(la::coalesce(la::parse_layout(layout)).str(), out, len);
+  } catch (const std::exception& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+}
+
+gemm_status la_layout_permute_str(const char* layout, char* out, size_t len) {
+  if (!layout || !out) return set_err(GEMM_ERR_NULL, "NULL argument");
+  try {
+    return copy_out(la::permute(la::parse_layout(layout)).str(), out, len);
+  } catch (const std::exception& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+}
+
+gemm_status la_layout_cosize_str(const char* layout, int64_t* out_cosize) {
+  if (!layout || !out_cosize) return set_err(GEMM_ERR_NULL, "NULL argument");
+  try {
+    *out_cosize = la::cosize(la::parse_layout(layout));
+  } catch (const std::exception& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+  return GEMM_OK;
+}
+
+gemm_status la_view_window_eval(int32_t b, int32_t m, int32_t s, const char* layout, const int64_t* origin,
+                                const int64_t* extent, int32_t rank, const int64_t* coord, int64_t* out_offset) {
+  if (!layout || !origin || !extent || !coord || !out_offset) return set_err(GEMM_ERR_NULL, "NULL argument");
+  if (rank <= 0 || rank > 16) return set_err(GEMM_ERR_INVALID_ARG, "rank must be 1..16");
+  if (!la::Swizzle::valid(b, m, s) || b > 16 || m > 30 || s > 30)
+    return set_err(GEMM_ERR_INVALID_ARG, "Swizzle fields overlap or a parameter is out of range");
+  try {
+    const la::View parent(la::Swizzle(b, m, s), la::parse_layout(layout));
+    const la::View w = parent.window(std::vector<int64_t>(origin, origin + rank), std::vector<int64_t>(extent, extent + rank));
+    *out_offset = w.at(std::vector<int64_t>(coord, coord + rank));
+  } catch (const std::exception& e) {
+    return set_err(GEMM_ERR_INVALID_ARG, e.what());
+  }
+  return GEMM_OK;
+}
+
 }  // extern "C"

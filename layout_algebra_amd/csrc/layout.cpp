@@ -105,6 +105,64 @@ int64_t Layout::at(const std::vector<int64_t>& top) const {
   return off;
 }
 
+namespace {
+
+void skip_spaces(const std::string& t, size_t& i) {
+  while (i < t.size() && (t[i] == ' ' || t[i] == '\t')) ++i;
+}
+
+Tree parse_node(const std::string& t, size_t& i, int depth) {
+  if (depth > 64) throw LayoutError("nesting too deep in '" + t + "'");
+  skip_spaces(t, i);
+  if (i < t.size() && t[i] == '(') {
+    ++i;
+    std::vector<Tree> kids;
+    for (;;) {
+      kids.push_back(parse_node(t, i, depth + 1));
+      skip_spaces(t, i);
+      if (i < t.size() && t[i] == ',') { ++i; continue; }
+      if (i < t.size() && t[i] == ')') { ++i; break; }
+      throw LayoutError("expected ',' or ')' at position " + std::to_string(i) + " of '" + t + "'");
+    }
+    // a one-element tuple is that element (as the pages write (n,) for a single mode)
+    return kids.size() == 1 ? kids[0] : Tree::T(std::move(kids));
+  }
+  size_t j = i;
+  if (j < t.size() && t[j] == '-') ++j;
+  const size_t digits = j;
+  while (j < t.size() && t[j] >= '0' && t[j] <= '9') ++j;
+  if (j == digits || j - digits > 18) throw LayoutError("expected an integer at position " + std::to_string(i) + " of '" + t + "'");
+  const int64_t v = std::stoll(t.substr(i, j - i));
+  i = j;
+  return Tree::L(v);
+}
+
+}  // namespace
+
+Tree parse_tree(const std::string& text) {
+  size_t i = 0;
+  Tree r = parse_node(text, i, 0);
+  skip_spaces(text, i);
+  if (i != text.size()) throw LayoutError("trailing characters in '" + text + "'");
+  return r;
+}
+
+Layout parse_layout(const std::string& text) {
+  // the colon that separates shape and stride sits outside every parenthesis
+  int depth = 0;
+  size_t colon = std::string::npos;
+  for (size_t i = 0; i < text.size(); ++i) {
+    if (text[i] == '(') ++depth;
+    else if (text[i] == ')') --depth;
+    else if (text[i] == ':' && depth == 0) {
+      if (colon != std::string::npos) throw LayoutError("more than one ':' in '" + text + "'");
+      colon = i;
+    }
+  }
+  if (colon == std::string::npos) throw LayoutError("a layout is written shape:stride, got '" + text + "'");
+  return Layout(parse_tree(text.substr(0, colon)), parse_tree(text.substr(colon + 1)));
+}
+
 Layout permute(const Layout& l) {
   if (l.shape().leaf) return l;
   std::vector<Tree> s(l.shape().kids.rbegin(), l.shape().kids.rend());

@@ -72,6 +72,11 @@ class Layout {
   Tree shape_, stride_;
 };
 
+// The pages' notation: "shape:stride" with nested tuples, e.g. "((8,4),5):((1,8),128)";
+// a coordinate is a nested tuple or an integer ("((3,2),1)", "(3,7)", "5").
+Tree parse_tree(const std::string& text);
+Layout parse_layout(const std::string& text);
+
 Layout permute(const Layout& l);                              // reverse top-level modes
 Layout tile(const Layout& l, const std::vector<int64_t>& t);  // per flat top-level mode
 Layout coalesce(const Layout& l);

@@ -20,7 +20,20 @@
 //   5. check the copy plans (every 16-byte LDS vector written exactly once,
 //      contiguous and aligned; section "Plans describe work, callers establish
 //      readiness") and the MFMA ownership (every C element of the tile owned by
-//      exactly one (wave, lane, register)).
+//      exactly one (wave, lane, register));
+//   6. build each operand's global view with tile() (section "A layout is a
+//      function": tile splits a mode into (within-tile, tile-index)), derive the
+//      global elements one wave instruction of the copy plan reads, check them
+//      against the kernel's per-lane chunk map, and reduce that copy layout with
+//      coalesce() (coalescing is host-side planning) to its contiguous runs;
+//   7. model each operand's LDS ring as one allocation and every stage as a
+//      window of it (section "Swizzle phase belongs to the allocation": a window
+//      keeps the parent's map and origin), checking that each stage sees the same
+//      swizzled map as the block plan;
+//   8. check the epilogue's store plan on every class of tile (interior, last
+//      row of tiles, last column, corner): every element of C inside [0,M)x[0,N)
+//      written exactly once, nothing outside it; and reduce one store
+//      instruction to its contiguous runs.
 #include "planner.hpp"
 
 #include <algorithm>
@@ -220,6 +233,258 @@ bool check_block(const la::View& v, int64_t base, int64_t block_elems, const cha
   return true;
 }
 
+// ---- step 6: global views and coalesced copy plans ----
+
+// Elements one wave instruction reads, as a layout whose first mode is the
+// contiguous run: `rows` rows of `cols` elements, row stride `ld`, columns
+// fastest (first mode fastest), reduced by coalesce().
+la::Layout copy_instr_layout(int64_t rows, int64_t cols, int64_t ld) {
+  return la::coalesce(la::permute(la::Layout::row_major(rows, cols, ld)));
+}
+
+// Contiguous run of a coalesced copy layout, in elements (its first mode when
+// that mode has stride 1).
+int64_t run_elems(const la::Layout& c) {
+  std::vector<int64_t> sh, st;
+  la::leaves(c.shape(), sh);
+  la::leaves(c.stride(), st);
+  return st.empty() || st[0] != 1 ? 1 : sh[0];
+}
+
+// The kernel's copy of one block of an operand: for wave instruction `ins`, the
+// tile coordinates (row, col) of the 8-element chunk each lane moves (the
+// chunk runs along the operand's contiguous direction).
+struct CopyChunk { int64_t row, col; };
+
+// The set of global elements (relative to the tile origin, through the tiled
+// global view's within-tile mode) that wave instruction `ins` reads must equal
+// the image of its copy layout placed at its first row.  `along_cols`: the
+// chunk is 8 consecutive columns of (rows, cols) (else 8 consecutive rows).
+bool check_instr_reads(const la::Layout& glob, const std::vector<CopyChunk>& chunks, bool along_cols,
+                       const la::Layout& instr, std::string* err, const char* name) {
+  std::vector<int64_t> got;
+  int64_t r0 = INT64_MAX, c0 = INT64_MAX;
+  for (const CopyChunk& ch : chunks) {
+    r0 = std::min(r0, ch.row);
+    c0 = std::min(c0, ch.col);
+    for (int e = 0; e < 8; ++e) {
+      const int64_t r = along_cols ? ch.row : ch.row + e, c = along_cols ? ch.col + e : ch.col;
+      got.push_back(glob.at({r, c}));
+    }
+  }
+  const int64_t base = glob.at({r0, c0});
+  std::vector<int64_t> want;
+  for (int64_t i = 0; i < instr.size(); ++i) want.push_back(base + instr(i));
+  std::sort(got.begin(), got.end());
+  std::sort(want.begin(), want.end());
+  if (got != want) return fail(err, std::string(name) + " copy: a wave instruction does not read its planned rows");
+  return true;
+}
+
+// Inverse of an LDS block map: physical element -> (row, col) of the block.
+std::vector<CopyChunk> lds_inverse(const la::View& v, int64_t rows, int64_t cols) {
+  std::vector<CopyChunk> inv(static_cast<size_t>(rows * cols));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) inv[v.at({r, c})] = CopyChunk{r, c};
+  return inv;
+}
+
+// Within-tile mode of a tiled global view (coordinate (r, c) of tile (0, 0)).
+struct TileView {
+  la::Layout tiled;
+  int64_t at(int64_t r, int64_t c) const { return tiled.at({r, c}); }
+};
+
+bool plan_copies(gemm_plan_s& p, std::string* err) {
+  const auto& s = p.shape;
+  const gemm_desc& d = p.d;
+  const int eb = 2;
+  // covering extents: tile() needs whole tiles; coordinates past M, N or K are
+  // the edges the general kernel masks
+  const int64_t Mc = std::max<int64_t>(1, p.tiles_m) * s.bm, Nc = std::max<int64_t>(1, p.tiles_n) * s.bn;
+  const int64_t Kc = std::max<int64_t>(1, (d.k + s.bk - 1) / s.bk) * s.bk;
+  p.glob_a = la::tile(la::Layout::row_major(Mc, Kc, d.lda), {s.bm, s.bk});
+  p.glob_b = p.b_kmajor ? la::tile(la::Layout::col_major(Kc, Nc, d.ldb), {s.bk, s.bn})
+                        : la::tile(la::Layout::row_major(Kc, Nc, d.ldb), {s.bk, s.bn});
+  p.glob_c = la::tile(la::Layout::row_major(Mc, Nc, d.ldc), {s.bm, s.bn});
+  // within-tile maps of tile (0, 0): coordinate ((r, 0), (c, 0)) of the tiled view
+  auto inner = [](const la::Layout& t, int64_t r, int64_t c) {
+    return t(la::Tree::T({la::Tree::T({la::Tree::L(r), la::Tree::L(0)}), la::Tree::T({la::Tree::L(c), la::Tree::L(0)})}));
+  };
+  const la::Layout ga = la::Layout::flat({s.bm, s.bk}, {inner(p.glob_a, 1, 0), inner(p.glob_a, 0, 1)});
+  // B in (k, n) coordinates of the block
+  const la::Layout gb = la::Layout::flat({s.bk, s.bn}, {inner(p.glob_b, 1, 0), inner(p.glob_b, 0, 1)});
+
+  // Per-instruction copy layouts: a wave instruction moves 64 x 16 bytes.
+  // Rows of an operand block as stored in memory: A rows of BK along K;
+  // B rows of BN along N ([K, N]) or of BK along K ([N, K]).
+  const int64_t a_cols = s.bk, b_cols = s.b_kmajor ? s.bk : s.bn;
+  const int64_t b_ld = d.ldb;
+  const int64_t per_instr = 64 * 8;
+  if (per_instr % a_cols || per_instr % b_cols) return fail(err, "a copy instruction does not cover whole rows");
+  const la::Layout ca = copy_instr_layout(per_instr / a_cols, a_cols, d.lda);
+  const la::Layout cb = copy_instr_layout(per_instr / b_cols, b_cols, b_ld);
+  const int64_t na = int64_t(s.bm) * s.bk / per_instr, nbk = int64_t(s.bk) * s.bn / per_instr;
+
+  std::vector<std::vector<CopyChunk>> ia(na), ib(nbk);
+  if (s.direct) {
+    // lane l of instruction `ins` fills physical elements [512 ins + 8 l, +8)
+    const std::vector<CopyChunk> inva = lds_inverse(p.lds_a, s.bm, s.bk);
+    const std::vector<CopyChunk> invb = lds_inverse(p.lds_b, s.bk, s.bn);
+    for (int64_t ins = 0; ins < na; ++ins)
+      for (int l = 0; l < 64; ++l) ia[ins].push_back(inva[per_instr * ins + 8 * l]);
+    for (int64_t ins = 0; ins < nbk; ++ins)
+      for (int l = 0; l < 64; ++l) ib[ins].push_back(invb[per_instr * ins + 8 * l]);
+  } else {
+    // register-staged: slot j of thread t moves chunk t + threads * j (row-major over chunks);
+    // a wave instruction is one slot of 64 consecutive threads
+    const int T = s.threads;
+    for (int64_t ins = 0; ins < na; ++ins) {
+      const int64_t j = ins / (T / 64), w = ins % (T / 64);
+      for (int l = 0; l < 64; ++l) {
+        const int64_t idx = w * 64 + l + T * j;
+        ia[ins].push_back(CopyChunk{idx / (s.bk / 8), (idx % (s.bk / 8)) * 8});
+      }
+    }
+    for (int64_t ins = 0; ins < nbk; ++ins) {
+      const int64_t j = ins / (T / 64), w = ins % (T / 64);
+      for (int l = 0; l < 64; ++l) {
+        const int64_t idx = w * 64 + l + T * j;
+        if (s.b_kmajor) ib[ins].push_back(CopyChunk{(idx % (s.bk / 8)) * 8, idx / (s.bk / 8)});
+        else ib[ins].push_back(CopyChunk{idx / (s.bn / 8), (idx % (s.bn / 8)) * 8});
+      }
+    }
+  }
+  for (const auto& ch : ia)
+    if (!check_instr_reads(ga, ch, true, ca, err, "A")) return false;
+  for (const auto& ch : ib)
+    if (!check_instr_reads(gb, ch, !s.b_kmajor, cb, err, "B")) return false;
+  std::ostringstream js;
+  js << "{\"A\":{\"instr\":\"" << ca.str() << "\",\"run_bytes\":" << run_elems(ca) * eb << ",\"instrs_per_block\":" << na << "}"
+     << ",\"B\":{\"instr\":\"" << cb.str() << "\",\"run_bytes\":" << run_elems(cb) * eb << ",\"instrs_per_block\":" << nbk << "}}";
+  p.copy_json = js.str();
+  return true;
+}
+
+// ---- step 7: the LDS ring as one allocation, stages as windows ----
+
+// Ring of `stages` blocks of (rows, cols), block base `base` inside a stage of
+// `stage` elements.  The allocation map is Swizzle o ((rows, cols, stages) :
+// (ld_r, ld_c, stage)) applied to offsets relative to the block base; stage s
+// is the window at origin (0, 0, s).  Every window must give stage * s plus the
+// block map: the stage bases sit on the swizzle period, so the phase is the
+// allocation's.
+bool check_ring(const la::View& block, int64_t rows, int64_t cols, int64_t stage, int stages, const char* name,
+                std::string* err) {
+  std::vector<int64_t> sh, st;
+  la::leaves(block.base().stride(), st);
+  const la::View ring(block.swizzle(), la::Layout::flat({rows, cols, int64_t(stages)}, {st[0], st[1], stage}));
+  for (int sidx = 0; sidx < stages; ++sidx) {
+    const la::View w = ring.window({0, 0, sidx}, {rows, cols, 1});
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; ++c)
+        if (w.at({r, c, 0}) != int64_t(sidx) * stage + block.at({r, c}))
+          return fail(err, std::string(name) + " ring: a stage window does not keep the allocation's swizzle phase");
+  }
+  return true;
+}
+
+// ---- step 8: store plans ----
+
+// One store of the epilogue: lane `lane` of store instruction `ins` writes
+// `n` consecutive elements of row `row` starting at column `col` (tile
+// coordinates), guarded by the kernel's mask.
+struct Store { int64_t ins; int lane; int64_t row, col; int n; };
+
+std::vector<Store> store_plan(const gemm_plan_s& p) {
+  const auto& s = p.shape;
+  std::vector<Store> out;
+  const int tm = s.bm / s.waves_m, tn = s.bn / s.waves_n;
+  int64_t ins = 0;
+  const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
+                    p.kid == lak::KID_FAST_GU_KM;
+  for (int w = 0; w < s.waves_m * s.waves_n; ++w) {
+    const int wm = w % s.waves_m, wn = w / s.waves_m;
+    if (fast) {
+      // rows of 8 consecutive outputs per lane, read back from the wave's LDS window
+      const int ch = tn / 8, rpp = 64 / ch;
+      for (int i = 0; i < tm / 32; ++i)
+        for (int q = 0; q < 32 / rpp; ++q, ++ins)
+          for (int l = 0; l < 64; ++l) out.push_back(Store{ins, l, wm * tm + 32 * i + q * rpp + l / ch, wn * tn + (l % ch) * 8, 8});
+    } else if (s.mfma_m == 32) {
+      // straight from the 32 x 32 accumulator lane map, one element per lane and register
+      for (int i = 0; i < tm / 32; ++i)
+        for (int j = 0; j < tn / 32; ++j)
+          for (int e = 0; e < 16; ++e, ++ins)
+            for (int l = 0; l < 64; ++l)
+              out.push_back(Store{ins, l, wm * tm + 32 * i + 4 * (l / 32) + 8 * (e / 4) + e % 4, wn * tn + 32 * j + l % 32, 1});
+    } else {
+      // 16 x 16 accumulator lane map
+      for (int j = 0; j < tn / 16; ++j)
+        for (int r = 0; r < 4; ++r, ++ins)
+          for (int l = 0; l < 64; ++l)
+            out.push_back(Store{ins, l, wm * tm + 4 * (l / 16) + r, wn * tn + 16 * j + l % 16, 1});
+    }
+  }
+  return out;
+}
+
+bool plan_stores(gemm_plan_s& p, std::string* err) {
+  const auto& s = p.shape;
+  const gemm_desc& d = p.d;
+  const std::vector<Store> plan = store_plan(p);
+  // the kernels' store mask: element (row, col) of tile (tm, tn) is written
+  // when it lies inside C (the full-tile kernels only run whole tiles)
+  auto check_tile = [&](int64_t tm, int64_t tn) {
+    const int64_t rows = std::min<int64_t>(s.bm, d.m - tm * s.bm), cols = std::min<int64_t>(s.bn, d.n - tn * s.bn);
+    std::vector<int> hits(static_cast<size_t>(s.bm) * s.bn, 0);
+    for (const Store& st : plan)
+      for (int e = 0; e < st.n; ++e) {
+        const int64_t r = st.row, c = st.col + e;
+        if (r < 0 || r >= s.bm || c < 0 || c >= s.bn) return fail(err, "store plan leaves its tile");
+        if (r < rows && c < cols) ++hits[r * s.bn + c];
+      }
+    for (int64_t r = 0; r < s.bm; ++r)
+      for (int64_t c = 0; c < s.bn; ++c) {
+        const int h = hits[r * s.bn + c];
+        if (r < rows && c < cols ? h != 1 : h != 0)
+          return fail(err, "store plan does not write every element of C inside its tile exactly once");
+      }
+    return true;
+  };
+  int classes = 0;
+  if (d.m > 0 && d.n > 0) {
+    const int64_t lm = p.tiles_m - 1, ln = p.tiles_n - 1;
+    const int64_t cls[4][2] = {{0, 0}, {lm, 0}, {0, ln}, {lm, ln}};
+    for (int c = 0; c < 4; ++c) {
+      bool seen = false;
+      for (int c2 = 0; c2 < c; ++c2) seen |= cls[c2][0] == cls[c][0] && cls[c2][1] == cls[c][1];
+      if (seen) continue;
+      if (!check_tile(cls[c][0], cls[c][1])) return false;
+      ++classes;
+    }
+  }
+  // one store instruction reduced to its contiguous runs
+  std::vector<int64_t> offs;
+  for (const Store& st : plan)
+    if (st.ins == 0)
+      for (int e = 0; e < st.n; ++e) offs.push_back(p.glob_c.at({st.row, st.col + e}));
+  std::sort(offs.begin(), offs.end());
+  int64_t runs = offs.empty() ? 0 : 1, longest = offs.empty() ? 0 : 1, cur = 1;
+  for (size_t i = 1; i < offs.size(); ++i) {
+    if (offs[i] == offs[i - 1] + 1) { ++cur; } else { ++runs; cur = 1; }
+    longest = std::max(longest, cur);
+  }
+  const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
+                    p.kid == lak::KID_FAST_GU_KM;
+  std::ostringstream js;
+  js << "{\"style\":\"" << (fast ? "lds_rows" : s.mfma_m == 32 ? "mfma32" : "mfma16") << "\",\"elems_per_lane\":"
+     << (fast ? 8 : 1) << ",\"runs_per_instr\":" << runs << ",\"run_bytes\":" << longest * p.out_bytes
+     << ",\"tile_classes_checked\":" << classes << "}";
+  p.store_json = js.str();
+  return true;
+}
+
 const char* dtype_name(int t) {
   switch (t) {
     case GEMM_BF16: return "bf16";
@@ -389,6 +654,13 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
       return GEMM_ERR_RESOURCE;
     }
     if (!check_fragment_reads(p, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
+    if (!plan_copies(p, err)) return GEMM_ERR_RESOURCE;
+    if (!check_ring(p.lds_a, s.bm, s.bk, p.stage_elems, s.stages, "A", err) ||
+        !(s.b_kmajor ? check_ring(la::View(p.lds_b.swizzle(), la::Layout::row_major(s.bn, s.bk, s.bk)), s.bn, s.bk,
+                                  p.stage_elems, s.stages, "B", err)
+                     : check_ring(p.lds_b, s.bk, s.bn, p.stage_elems, s.stages, "B", err)))
+      return GEMM_ERR_RESOURCE;
+    if (!plan_stores(p, err)) return GEMM_ERR_RESOURCE;
   } catch (const la::LayoutError& e) {
     fail(err, e.what());
     return GEMM_ERR_RESOURCE;
@@ -414,6 +686,9 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
      << ",\"direct_loads\":" << (s.direct ? "true" : "false")
      << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
      << ",\"prefetch_blocks\":" << prefetch_blocks(p)
+     << ",\"global_a\":\"" << p.glob_a.str() << "\",\"global_b\":\"" << p.glob_b.str() << "\",\"global_c\":\""
+     << p.glob_c.str() << "\""
+     << ",\"copy\":" << p.copy_json << ",\"store\":" << p.store_json
      << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes
      << ",\"out_align_bytes\":" << p.out_align_bytes << "}";
   p.json = js.str();

@@ -23,6 +23,8 @@ struct gemm_plan_s {
   lak::KernelShape shape{};
   la::View lds_a, lds_b, lds_b2;     // operand block maps in (row, col) tile coordinates
   int64_t base_a = 0, base_b = 0, base_b2 = 0;  // element offsets of each block in a stage
+  la::Layout glob_a, glob_b, glob_c;  // operands in global memory, tiled by the kernel's tile (covering extents)
+  std::string copy_json, store_json;  // copy and store plans as described (coalesced per wave instruction)
   std::string json;
 };
 

@@ -40,8 +40,10 @@ def test_exports_every_declared_symbol():
 def test_page_values_through_the_c_abi(case):
     if case["kind"] == "eval":
         shape, stride, coord = tup(case["shape"]), tup(case["stride"]), tup(case["coord"])
+        # the pages' notation, nested as printed (no flattening)
+        assert la.la_layout_eval_str((shape, stride), coord) == case["expect"]
         if any(isinstance(s, tuple) for s in shape):
-            # flatten the nested pin into flat modes: ((8,4),5) -> (8,4,5)
+            # and through the flat-array entry point: ((8,4),5) -> (8,4,5)
             fs, fd, fc = L.leaves(shape), L.leaves(stride), L.leaves(coord)
             assert la.la_layout_eval(fs, fd, fc) == case["expect"]
         else:
@@ -89,6 +91,123 @@ def test_layout_eval_matches_reference_on_random_layouts():
             assert la.la_layout_eval(shape, stride, list(coord)) == ref(idx)
     with pytest.raises(la.GemmError):
         la.la_layout_eval([4, 4], [4, 1], [4, 0])
+
+
+@pytest.mark.parametrize("case", [c for c in layout_cases() if c["kind"] in ("tile_eq", "permute_eq", "swizzle_window_eq")],
+                         ids=lambda c: c["id"])
+def test_page_equalities_through_the_c_abi(case):
+    """tile(), permutedims and a swizzled window, as the pages print them, through the C ABI."""
+    lay = (tup(case["shape"]), tup(case["stride"]))
+    if case["kind"] == "tile_eq":
+        tiled = la.la_layout_tile_str(lay, tup(case["tile"]))
+        got = la.la_layout_eval_str(tiled, tup(case["tiled_coord"]))
+        assert got == la.la_layout_eval_str(lay, tup(case["flat_coord"])) == 375
+    elif case["kind"] == "permute_eq":
+        perm = la.la_layout_permute_str(lay)
+        assert la.la_layout_eval_str(perm, tup(case["permuted_coord"])) == la.la_layout_eval_str(lay, tup(case["coord"]))
+    else:
+        sw, ext = tup(case["swizzle"]), L.Layout(*lay).top_extents()
+        w = la.la_view_window_eval(sw, lay, tup(case["origin"]), tup(case["wshape"]), tup(case["wcoord"]))
+        whole = la.la_view_window_eval(sw, lay, (0,) * len(ext), ext, tup(case["coord"]))
+        assert w == whole == 115
+
+
+def _random_tree(rng, depth=0):
+    if depth >= 2 or rng.random() < 0.6:
+        return rng.randint(1, 5)
+    return tuple(_random_tree(rng, depth + 1) for _ in range(rng.randint(2, 3)))
+
+
+def _strides_like(rng, shape):
+    if isinstance(shape, int):
+        return rng.randint(0, 60)
+    return tuple(_strides_like(rng, s) for s in shape)
+
+
+def _as_text(x):
+    return "(" + ",".join(_as_text(v) for v in x) + ")" if isinstance(x, tuple) else str(x)
+
+
+def _map_of(text_layout, n):
+    return [la.la_layout_eval_str(text_layout, str(i)) for i in range(n)]
+
+
+def test_nested_algebra_matches_the_reference():
+    """Random nested layouts: evaluation (natural coordinates and integer indices), tile(),
+    coalesce(), permutedims and cosize through the C ABI against the oracle's enumeration."""
+    rng = random.Random(23)
+    for _ in range(150):
+        rank = rng.randint(1, 3)
+        shape = tuple(_random_tree(rng) for _ in range(rank)) if rank > 1 else _random_tree(rng)
+        stride = _strides_like(rng, shape)
+        ref = L.Layout(shape, stride)
+        text = _as_text(shape) + ":" + _as_text(stride)
+        n = ref.size()
+        if n > 300:
+            continue
+        for i in range(n):
+            assert la.la_layout_eval_str(text, str(i)) == ref(i)
+            assert la.la_layout_eval_str(text, _as_text(L.split_index(i, shape))) == ref(i)
+        # coalesce: the same map on [0, size), and the oracle's reduced modes
+        co = la.la_layout_coalesce_str(text)
+        rco = L.coalesce(ref)
+        assert co == _as_text(rco.shape) + ":" + _as_text(rco.stride)
+        assert _map_of(co, n) == [ref(i) for i in range(n)]
+        # permutedims: a coordinate with its top-level modes reversed maps to the same offset
+        if rank > 1:
+            pe = la.la_layout_permute_str(text)
+            rp = L.permutedims(ref)
+            assert pe == _as_text(rp.shape) + ":" + _as_text(rp.stride)
+        assert la.la_layout_cosize_str(text) == L.cosize(ref)
+    # tile(): flat modes, divisors
+    for _ in range(100):
+        rank = rng.randint(1, 3)
+        tiles = [rng.choice([1, 2, 3, 4]) for _ in range(rank)]
+        shape = tuple(t * rng.randint(1, 4) for t in tiles)
+        stride = tuple(rng.randint(0, 50) for _ in range(rank))
+        ref = L.tile(L.Layout(shape if rank > 1 else shape[0], stride if rank > 1 else stride[0]), tiles)
+        got = la.la_layout_tile_str(_as_text(shape) + ":" + _as_text(stride), tiles)
+        assert got == _as_text(ref.shape) + ":" + _as_text(ref.stride)
+    with pytest.raises(la.GemmError):
+        la.la_layout_tile_str("(6,4):(4,1)", [4, 2])           # 4 does not divide 6
+    with pytest.raises(la.GemmError):
+        la.la_layout_eval_str("((8,4),5):((1,8),128)", "((8,0),0)")   # outside the mode
+    with pytest.raises(la.GemmError):
+        la.la_layout_eval_str("(8,4):(1,8", "(0,0)")           # malformed text
+    with pytest.raises(la.GemmError):
+        la.la_view_window_eval((2, 3, 2), "(32,32):(32,1)", (20, 0), (16, 16), (0, 0))   # window leaves the parent
+
+
+@pytest.mark.parametrize("name", ["square4096", "gate_up", "ragged", "skinny", "square256"])
+def test_plans_describe_global_views_copies_and_stores(name):
+    """Each plan tiles its operands' global views, checks and coalesces the copy of one wave
+    instruction, and checks its store plan on every class of tile."""
+    w = synth.WORKLOADS[name]
+    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+    d = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up).describe()
+    bm, bn, bk = d["tile"]
+    # the tiled global view of A: ((BM, M/BM), (BK, K/BK)) : ((lda, BM lda), (1, BK)) over the covering extents
+    ga = L.Layout(*_split_layout(d["global_a"]))
+    tm, tk = min(1, d["tiles"][0] - 1), min(1, (w.K + bk - 1) // bk - 1)
+    assert ga(((3, tm), (5, tk))) == (3 + tm * bm) * d["lda"] + 5 + tk * bk
+    # copy runs: a wave instruction reads whole rows of the block (coalesced)
+    for op in ("A", "B"):
+        c = d["copy"][op]
+        assert c["run_bytes"] >= 64 and c["instrs_per_block"] >= 1
+    assert d["store"]["tile_classes_checked"] >= (1 if d["tiles"] == [1, 1] else 2)
+    assert d["store"]["run_bytes"] >= 64
+
+
+def _split_layout(text):
+    """"shape:stride" text -> (shape, stride) as ints / nested tuples."""
+    import ast
+    depth = 0
+    for i, ch in enumerate(text):
+        depth += ch == "("
+        depth -= ch == ")"
+        if ch == ":" and depth == 0:
+            return ast.literal_eval(text[:i]), ast.literal_eval(text[i + 1:])
+    raise ValueError(text)
 
 
 def test_tile_plan_rejects_what_the_page_forbids():
