@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--b-kmajor", action="store_true",
                     help="hand B (or the gate/up weights) to the library as [N,K] (K contiguous)")
+    ap.add_argument("--a-transposed", action="store_true",
+                    help="hand A (or x) to the library as [K,M] (M contiguous)")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="timed steps as replays of a captured HIP graph (default), or one library call each")
     ap.add_argument("--preroll-seconds", type=float, default=0.5,
@@ -160,9 +162,10 @@ def main():
     torch.cuda.set_device(dev)
 
     x = synth.make_inputs(w)
-    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up, b_kmajor=args.b_kmajor)
+    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up, b_kmajor=args.b_kmajor,
+                        a_transposed=args.a_transposed)
     dev_b = (lambda t: t.t().contiguous().to(dev)) if args.b_kmajor else (lambda t: t.to(dev))
-    A = x["A"].to(dev)
+    A = x["A"].t().contiguous().to(dev) if args.a_transposed else x["A"].to(dev)
     out_dt = synth.torch_dtype(w.out_kind)
     if w.gate_up:
         Wg, Wu = dev_b(x["Wg"]), dev_b(x["Wu"])
@@ -277,6 +280,7 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "out": w.out_kind,
                    "launch": args.launch,
                    "b_order": "nk" if args.b_kmajor else "kn",
+                   "a_order": "km" if args.a_transposed else "mk",
                    "alpha": w.alpha, "beta": w.beta, "gate_up": w.gate_up,
                    "kernel": plan.describe()["kernel"], "grid": plan.describe()["grid"]},
         "roofline": roof,

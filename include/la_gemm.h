@@ -14,7 +14,8 @@
  *
  * Storage (all row-major, element strides, zero-based, as on the Tylo.jl page
  * "Layouts, storage and ownership", section "A layout is a function"):
- *   A  [M, K]  element (i, k) at A[i * lda + k]          (K contiguous)
+ *   A  [M, K]  element (i, k) at A[i * lda + k]          (K contiguous; or, with
+ *              GEMM_FLAG_A_TRANSPOSED, at A[k * lda + i], M contiguous)
  *   B  [K, N]  element (k, j) at B[k * ldb + j]          (N contiguous; or, with
  *              GEMM_FLAG_B_KMAJOR, at B[j * ldb + k], K contiguous)
  *   C  [M, N]  element (i, j) at C[i * ldc + j]
@@ -69,6 +70,13 @@ typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
                                     B[n * ldb + k], ldb >= max(1, k) -- the K-contiguous operand
                                     storage of the Tylo.jl page "TMA and Hopper WGMMA" (section
                                     "The same storage contract on both sides") */
+#define GEMM_FLAG_A_TRANSPOSED 0x8u  /* A (and X) stored [K, M]: element (i, k) at A[k * lda + i],
+                                    lda >= max(1, m) -- a layout is a function and either major order
+                                    is the same matrix (Tylo.jl "Layouts, storage and ownership",
+                                    section "A layout is a function": permutedims swaps the modes).
+                                    Not combined with GEMM_FLAG_B_KMAJOR; needs m to be a multiple of
+                                    8 or larger than 8 (16-byte staging along M); never the skinny
+                                    kernel.  Otherwise rejected with GEMM_ERR_UNSUPPORTED */
 #define GEMM_FLAG_LARGE_TILES 0x4u  /* keep the largest tile the shape allows.  Without it the
                                     planner moves a GEMM whose grid would leave most of the 256
                                     CUs idle to 64 x 64 tiles (fewer than 32 workgroups of the
@@ -81,8 +89,8 @@ typedef struct {
   int64_t m, n, k;             /* problem sizes, each >= 0 */
   int32_t a_type, b_type;      /* gemm_dtype; equal, BF16 or F16 */
   int32_t c_type;              /* gemm_dtype of C (and of G, U): F32, BF16 or F16 */
-  int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k), ldb >= max(1,n) (max(1,k) for
-                                  K-major B), ldc >= max(1,n) */
+  int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k) (max(1,m) for A stored [K,M]),
+                                  ldb >= max(1,n) (max(1,k) for K-major B), ldc >= max(1,n) */
   uint32_t flags;              /* GEMM_FLAG_* */
   int64_t batch;               /* >= 1: independent GEMMs per run (1..65535); matrix b of each operand
                                   starts stride_* elements after matrix b-1 (a batch coordinate, as the

@@ -10,6 +10,7 @@ BF16, F16, F32 = 0, 1, 2
 FLAG_GATE_UP = 0x1
 FLAG_B_KMAJOR = 0x2
 FLAG_LARGE_TILES = 0x4
+FLAG_A_TRANSPOSED = 0x8
 
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
@@ -132,17 +133,18 @@ class Plan:
 
 
 def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False, b_kmajor=False,
-              batch=1, stride_a=None, stride_b=None, stride_c=None, large_tiles=False):
-    """Plan C[m,n] = A[m,k] @ B.  B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed).
+              batch=1, stride_a=None, stride_b=None, stride_c=None, large_tiles=False, a_transposed=False):
+    """Plan C[m,n] = A @ B.  A is an [m,k] tensor, or with a_transposed=True a [k,m] tensor (A transposed);
+    B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed).
     batch > 1: tensors gain a leading batch dimension with the given element strides (default: packed).
     large_tiles=True keeps the largest tile the shape allows (GEMM_FLAG_LARGE_TILES)."""
-    lda = int(lda if lda is not None else max(1, k))
+    lda = int(lda if lda is not None else max(1, m if a_transposed else k))
     ldb = int(ldb if ldb is not None else max(1, k if b_kmajor else n))
     ldc = int(ldc if ldc is not None else max(1, n))
     d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type), lda, ldb, ldc,
               (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0) |
-              (FLAG_LARGE_TILES if large_tiles else 0), int(batch),
-              int(stride_a if stride_a is not None else m * lda),
+              (FLAG_LARGE_TILES if large_tiles else 0) | (FLAG_A_TRANSPOSED if a_transposed else 0), int(batch),
+              int(stride_a if stride_a is not None else (k if a_transposed else m) * lda),
               int(stride_b if stride_b is not None else (n if b_kmajor else k) * ldb),
               int(stride_c if stride_c is not None else m * ldc))
     h = ctypes.c_void_p()
@@ -203,6 +205,13 @@ def _check_matrix(t, name, rows, cols, ld, kind, batch=1, bstride=0):
             raise ValueError("%s must have batch stride %d (strides %s)" % (name, bstride, t.stride()))
 
 
+def _check_a(t, name, d):
+    if d.flags & FLAG_A_TRANSPOSED:
+        _check_matrix(t, name + " ([k,m], A transposed)", d.k, d.m, d.lda, d.a_type, d.batch, d.stride_a)
+    else:
+        _check_matrix(t, name, d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
+
+
 def _check_b(t, name, d):
     if d.flags & FLAG_B_KMAJOR:
         _check_matrix(t, name + " ([n,k], K-major)", d.n, d.k, d.ldb, d.b_type, d.batch, d.stride_b)
@@ -213,7 +222,7 @@ def _check_b(t, name, d):
 def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
     """C = alpha * A @ B + beta * C, enqueued on `stream` (default: current)."""
     d = plan.desc
-    _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
+    _check_a(A, "A", d)
     _check_b(B, "B", d)
     _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_run(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
@@ -229,7 +238,7 @@ def gemm_run_reduce(plan, A, B, C, alpha=1.0, beta=0.0, op="sum", R=None, stream
     d = plan.desc
     if op not in REDUCE_OPS:
         raise ValueError("op must be one of %s" % sorted(REDUCE_OPS))
-    _check_matrix(A, "A", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
+    _check_a(A, "A", d)
     _check_b(B, "B", d)
     _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     want = (d.m,) if d.batch == 1 else (d.batch, d.m)
@@ -244,7 +253,7 @@ def gemm_run_reduce(plan, A, B, C, alpha=1.0, beta=0.0, op="sum", R=None, stream
 def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
     """G = X @ W_gate and U = X @ W_up in one launch."""
     d = plan.desc
-    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
+    _check_a(X, "X", d)
     _check_b(W_gate, "W_gate", d)
     _check_b(W_up, "W_up", d)
     _check_matrix(G, "G", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
@@ -256,7 +265,7 @@ def gemm_gate_up_run(plan, X, W_gate, W_up, G, U, stream=None):
 def gemm_gate_up_swiglu_run(plan, X, W_gate, W_up, H, stream=None):
     """H = silu(X @ W_gate) * (X @ W_up) in one launch (activation fused into the epilogue)."""
     d = plan.desc
-    _check_matrix(X, "X", d.m, d.k, d.lda, d.a_type, d.batch, d.stride_a)
+    _check_a(X, "X", d)
     _check_b(W_gate, "W_gate", d)
     _check_b(W_up, "W_up", d)
     _check_matrix(H, "H", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)

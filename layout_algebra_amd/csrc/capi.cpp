@@ -50,7 +50,7 @@ lak::TiledArgs base_args(const gemm_plan_s& p) {
 
 gemm_status launch(const gemm_plan_s& p, const lak::TiledArgs& a, void* stream, bool image) {
   const dim3 grid(static_cast<unsigned>(p.grid), image ? 1u : static_cast<unsigned>(p.d.batch));
-  const hipError_t e = lak::launch_kernel(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, p.b_kmajor, a, grid,
+  const hipError_t e = lak::launch_kernel(p.kid, p.in_kind, p.out_kind, p.vec, p.gate_up, p.b_kmajor, p.a_trans, a, grid,
                                          static_cast<hipStream_t>(stream), image);
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GEMM_OK;

@@ -46,6 +46,8 @@ hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args
     case KID_FAST_GU: return by_types<CfgFastGU>(in_kind, out_kind, args, grid, stream, lds_image);
     case KID_FAST_256_KM: return by_types<CfgFast256KM>(in_kind, out_kind, args, grid, stream, lds_image);
     case KID_FAST_GU_KM: return by_types<CfgFastGUKM>(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_256_AT: return by_types<CfgFast256AT>(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_GU_AT: return by_types<CfgFastGUAT>(in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,7 +14,9 @@
 //    blocks of 16-bit values across each 16-lane group on the way out of LDS:
 //    lanes 4e..4e+3 of the group point at row e (16 values) and lane i
 //    receives element i of rows 0..3.  Two such reads give the 8 K values.
-//  * A fragments are plain 16-byte LDS reads (K is contiguous in A).
+//  * A fragments are plain 16-byte LDS reads (K is contiguous in A).  A stored
+//    [K, M] (M contiguous) stays M-contiguous in LDS and is read with the same
+//    transposing reads as B.
 //  * Large tiles (256 x 256, or 256 x 2*128 for gate/up) with 8 waves: one
 //    tile per CU at 4096^2, two waves per SIMD.
 //  * A multi-stage LDS ring (STAGES buffers) keeps STAGES-1 K blocks in
@@ -40,6 +42,7 @@ struct Fast {
   static constexpr int BM = C::BM, BN = C::BN, NB = C::NB, WM = C::WM, WN = C::WN, BK = C::BK;
   static constexpr int STAGES = C::STAGES;
   static constexpr bool BKM = C::BKMAJOR;                 // B stored [N, K] (K contiguous) instead of [K, N]
+  static constexpr bool ATR = C::ATRANS;                  // A stored [K, M] (M contiguous) instead of [M, K]
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -57,7 +60,15 @@ struct Fast {
   static_assert(BK % 16 == 0 && STAGES >= 2, "K block and pipeline depth");
   static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
 
-  static __device__ __forceinline__ int a_off(int r, int k) { return swz<C::AB, C::AM, C::AS>(r * BK + k); }
+  // A block in LDS: K-contiguous rows of BK per m, or (A stored [K, M]) M-contiguous rows of BM per k.
+  static __device__ __forceinline__ int a_off(int r, int k) {
+    return ATR ? swz<C::AB, C::AM, C::AS>(k * BM + r) : swz<C::AB, C::AM, C::AS>(r * BK + k);
+  }
+  // Global A: origin of the tile at row m0, and the element step of K block k1.
+  static __device__ __forceinline__ const uint16_t* a_origin(const uint16_t* A, int64_t m0, int64_t lda) {
+    return ATR ? A + m0 : A + m0 * lda;
+  }
+  static __device__ __forceinline__ int64_t a_step(int64_t k1, int64_t lda) { return ATR ? k1 * lda : k1; }
   // B block in LDS: N-contiguous rows of BN per k, or (K-major B) K-contiguous rows of BK per n.
   static __device__ __forceinline__ int b_off(int k, int n) {
     return BKM ? swz<C::BB, C::BMb, C::BS>(n * BK + k) : swz<C::BB, C::BMb, C::BS>(k * BN + n);
@@ -80,7 +91,7 @@ struct Fast {
     for (int i = 0; i < A_LOADS; ++i) {
       const int P = (wave * A_LOADS + i) * 512 + lane * 8;     // physical element this lane fills
       const int L = swz<C::AB, C::AM, C::AS>(P);               // logical element it must hold
-      s.a[i] = uint32_t((L / BK) * lda + (L % BK));
+      s.a[i] = ATR ? uint32_t((L / BM) * lda + (L % BM)) : uint32_t((L / BK) * lda + (L % BK));
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -130,12 +141,13 @@ struct Fast {
 
   // Lane-dependent parts of the fragment addresses.
   struct Lane {
-    int ar, ak, bn, bk, br;
+    int ar, ak, bn, bk, br, am;
     __device__ __forceinline__ Lane(int wm, int wn, int lane) {
       ar = wm * TM + (lane & 31);                // A: row l % 32 of each 32-row block
       ak = (lane >> 5) * 8;                      // A: K half of the 16-wide sub-step
       const int g = lane >> 4;                   // B (N-contiguous): 16-lane group
       bn = wn * TN + 16 * (g & 1) + 4 * (lane & 3);
+      am = wm * TM + 16 * (g & 1) + 4 * (lane & 3);   // A (M-contiguous): as bn, along M
       bk = 8 * (g >> 1) + ((lane >> 2) & 3);
       br = wn * TN + (lane & 31);                // B (K-contiguous): column l % 32 of each 32-column block
     }
@@ -148,7 +160,16 @@ struct Fast {
 
   static __device__ __forceinline__ void read_frags(const LAK_LDS uint16_t* stage, int s, const Lane& ln, Frags& f) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) f.a[i] = read_b128(stage + a_off(ln.ar + i * 32, s * 16 + ln.ak));
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (ATR) {
+        // M-contiguous A rows: transposing reads, lane mapping as for N-contiguous B
+        const u32x2 lo = read_tr(stage + a_off(ln.am + i * 32, s * 16 + ln.bk));
+        const u32x2 hi = read_tr(stage + a_off(ln.am + i * 32, s * 16 + ln.bk + 4));
+        f.a[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        f.a[i] = read_b128(stage + a_off(ln.ar + i * 32, s * 16 + ln.ak));
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const LAK_LDS uint16_t* bs = stage + A_ELEMS + t * B_ELEMS;
@@ -346,7 +367,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   typename F::Src src;
   F::make_src(src, wave, lane, g.lda, g.ldb);
   const typename F::Lane ln(wm, wn, lane);
-  const uint16_t* a_tile = g.A + m0 * g.lda;
+  const uint16_t* a_tile = F::a_origin(g.A, m0, g.lda);
   const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
   const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
 
@@ -363,7 +384,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   for (int p = 0; p < F::STAGES - 1; ++p) {
     if (p < nk) {
       const int64_t k1 = int64_t(p) * F::BK;
-      F::issue(src, lds + p * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb), NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
+      F::issue(src, lds + p * F::STAGE, a_tile + F::a_step(k1, g.lda), b_tile + F::b_step(k1, g.ldb),
+               NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
   }
   if (group == 1) {
@@ -379,7 +401,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
     const int kn = kt + F::STAGES - 1;
     if (kn < nk) {
       const int64_t k1 = int64_t(kn) * F::BK;
-      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + k1, b_tile + F::b_step(k1, g.ldb),
+      F::issue(src, lds + (kn % F::STAGES) * F::STAGE, a_tile + F::a_step(k1, g.lda), b_tile + F::b_step(k1, g.ldb),
                NB > 1 ? b2_tile + F::b_step(k1, g.ldb) : nullptr, wave);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): fragments in registers
@@ -409,8 +431,8 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_lds_image(const 
   typename F::Src src;
   F::make_src(src, wave, lane, g.lda, g.ldb);
   const int64_t m0 = int64_t(g.dbg_tm) * C::BM, n0 = int64_t(g.dbg_tn) * C::BN;
-  F::issue(src, lds, g.A + m0 * g.lda, F::b_origin(g.B, n0, g.ldb), C::NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr,
-           wave);
+  F::issue(src, lds, F::a_origin(g.A, m0, g.lda), F::b_origin(g.B, n0, g.ldb),
+           C::NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr, wave);
   wait_vmcnt<0>();
   block_barrier();
   for (int i = tid; i < F::STAGE; i += F::NT) g.dbg_out[i] = lds[i];

@@ -26,7 +26,9 @@
 //     16-bit values across each 16-lane group (lanes 4e..4e+3 address row e;
 //     lane i receives element i of rows 0..3): staging writes whole 16-byte
 //     row chunks and both the writes and the transposing reads are free of
-//     bank conflicts.
+//     bank conflicts.  A stored [K, M] (M contiguous) is kept M-contiguous the
+//     same way, one row of BM values per k under the same swizzle, staged in
+//     8-element chunks along M and read with the same transposing reads.
 //   * Two LDS stages: while the MFMAs consume stage s the next block is
 //     loaded into registers and written to stage s^1; one workgroup barrier
 //     per block keeps every wave's reads of a stage ahead of its refill
@@ -59,7 +61,7 @@ struct Chunk8 { u32x4 w; };   // one aligned 16-byte load
 struct Chunk2 { u32x4 w; };   // one 16-byte load at 2-byte alignment (a cut chunk: shifted window)
 struct Chunk1 { u32x4 w; };   // eight 2-byte loads
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool AT = false>
 struct Tiled {
   static constexpr int NT = WM * WN * 64;
   static constexpr int BK = 64;
@@ -73,6 +75,10 @@ struct Tiled {
   static constexpr int BN8 = BN / 8;
   static constexpr int B_CHUNKS = BN * BK / 8 / NT;         // 8-element B chunks per thread (along K or N)
   static constexpr int BSW = BN == 64 ? 1 : 2;              // N-contiguous B block: Swizzle{BSW,5,2}
+  static constexpr int BM8 = BM / 8;
+  static constexpr int ASW = BM == 64 ? 1 : 2;              // M-contiguous A block: Swizzle{ASW,5,2}
+  static_assert(!AT || (!BKM && V != 1), "A stored [K, M] pairs with B stored [K, N] and 16-byte staging");
+  static_assert(!AT || NT % BM8 == 0, "a thread's A chunks share their index along M");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_CHUNKS * NT * 8 == BM * BK, "A block must split evenly over threads");
   static_assert(B_CHUNKS * NT * 8 == BN * BK, "B block must split evenly over threads");
@@ -84,6 +90,8 @@ struct Tiled {
   static __device__ __forceinline__ int lds_off(int row, int k) { return swz<3, 3, 4>(row * BK + k); }
   // LDS element offset of (k, n) inside an N-contiguous B block.
   static __device__ __forceinline__ int b_off_n(int k, int n) { return swz<BSW, 5, 2>(k * BN + n); }
+  // LDS element offset of (k, m) inside an M-contiguous A block.
+  static __device__ __forceinline__ int a_off_m(int k, int m) { return swz<ASW, 5, 2>(k * BM + m); }
 
   // Staging registers of one K block.
   struct Regs {
@@ -171,11 +179,20 @@ struct Tiled {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
-      const int row = idx >> 3, ch = idx & 7;
-      const int64_t gm = m0 + row;
-      const int64_t gk = k0 + ch * 8;
-      const int nvalid = gm < g.M ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
-      load8(r.a[j], g.A + gm * g.lda + gk, nvalid);
+      if constexpr (AT) {
+        // A stored [K, M]: rows k of M values, 8-element chunks along M
+        const int kr = idx / BM8, mc = idx % BM8;
+        const int64_t gk = k0 + kr;
+        const int64_t gm = m0 + mc * 8;
+        const int nvalid = gk < g.K ? int(max<int64_t>(0, min<int64_t>(8, g.M - gm))) : 0;
+        load8(r.a[j], g.A + gk * g.lda + gm, nvalid);
+      } else {
+        const int row = idx >> 3, ch = idx & 7;
+        const int64_t gm = m0 + row;
+        const int64_t gk = k0 + ch * 8;
+        const int nvalid = gm < g.M ? int(max<int64_t>(0, min<int64_t>(8, g.K - gk))) : 0;
+        load8(r.a[j], g.A + gm * g.lda + gk, nvalid);
+      }
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -217,7 +234,7 @@ struct Tiled {
       for (int j = 0; j < B_CHUNKS; ++j) b[s][j] = r.b[s][j].w;
     if constexpr (V == 2) {
       // one branch per operand; the data has arrived by now
-      if ((tid & 7) == cut.a_ch) {
+      if ((AT ? tid % BM8 : tid & 7) == cut.a_ch) {
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j) a[j] = shift_down(a[j], cut.a_sh);
       }
@@ -233,7 +250,11 @@ struct Tiled {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int idx = tid + NT * j;
-      *reinterpret_cast<u32x4*>(stage + lds_off(idx >> 3, (idx & 7) * 8)) = a[j];
+      if constexpr (AT) {
+        *reinterpret_cast<u32x4*>(stage + a_off_m(idx / BM8, (idx % BM8) * 8)) = a[j];
+      } else {
+        *reinterpret_cast<u32x4*>(stage + lds_off(idx >> 3, (idx & 7) * 8)) = a[j];
+      }
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -269,8 +290,17 @@ struct Tiled {
     for (int s = 0; s < BK / 16; ++s) {
       u32x4 a[FM], b[NB][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(stage + lds_off(wm * TM + i * 32 + lr, s * 16 + lk));
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (AT) {
+          // M-contiguous A: transposing reads, lane mapping as for N-contiguous B along M
+          const int am = wm * TM + 16 * (g4 & 1) + 4 * (lane & 3) + i * 32;
+          const u32x2 lo = read_tr(stage + a_off_m(s * 16 + bk, am));
+          const u32x2 hi = read_tr(stage + a_off_m(s * 16 + bk + 4, am));
+          a[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          a[i] = *reinterpret_cast<const u32x4*>(stage + lds_off(wm * TM + i * 32 + lr, s * 16 + lk));
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NB; ++t)
 #pragma unroll
@@ -303,10 +333,10 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3, bool AT = false>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
-  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
+  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM, AT>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * T::STAGE];
 
   const int tid = threadIdx.x;
@@ -338,15 +368,22 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
   // carry no memory fence: a fence would also wait for the prefetch.
   const int nk = int((g.K + T::BK - 1) / T::BK);
   // chunks cut by an edge (V == 2): along K in the last block when K is not a multiple of 8,
-  // along N in every block of the tile that holds N's edge when N is not (N-contiguous B)
-  const int64_t n_left = g.N - n0;
+  // along N in every block of the tile that holds N's edge when N is not (N-contiguous B), and
+  // for A stored [K, M] along M in every block of the tile that holds M's edge (A's K runs
+  // along its rows there, so it has no K cut)
+  const int64_t n_left = g.N - n0, m_left = g.M - m0;
   const bool n_cut = !BKM && n_left < BN && (n_left & 7) != 0;
+  const bool m_cut = AT && m_left < BM && (m_left & 7) != 0;
   auto cut = [&](int blk) {
     typename T::Cut c{-1, 0, -1, 0};
     const int64_t k_left = g.K - int64_t(blk) * T::BK;
-    if (blk < nk && k_left < T::BK && (k_left & 7) != 0) {
+    if (!AT && blk < nk && k_left < T::BK && (k_left & 7) != 0) {
       c.a_ch = int(k_left >> 3);
       c.a_sh = 8 - int(k_left & 7);
+    }
+    if (blk < nk && m_cut) {
+      c.a_ch = int(m_left >> 3);
+      c.a_sh = 8 - int(m_left & 7);
     }
     if (blk < nk && n_cut) {
       c.b_nc = int(n_left >> 3);
@@ -489,17 +526,18 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
 
 // Debug: stage K block 0 of tile (dbg_tm, dbg_tn) with the kernel's own
 // staging code and copy the LDS stage out verbatim.
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool AT = false>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const TiledArgs g) {
-  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM>;
+  using T = Tiled<TI, TO, BM, BN, WM, WN, V, GU, BKM, AT>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[T::STAGE];
   const int tid = threadIdx.x;
   typename T::Regs r;
   T::load(r, g, g.dbg_tm * BM, g.dbg_tn * BN, 0, tid);
   T::store(r, lds, tid, [&] {
     typename T::Cut c{-1, 0, -1, 0};
-    const int64_t k_left = g.K, n_left = g.N - int64_t(g.dbg_tn) * BN;
-    if (k_left < T::BK && (k_left & 7) != 0) { c.a_ch = int(k_left >> 3); c.a_sh = 8 - int(k_left & 7); }
+    const int64_t k_left = g.K, n_left = g.N - int64_t(g.dbg_tn) * BN, m_left = g.M - int64_t(g.dbg_tm) * BM;
+    if (!AT && k_left < T::BK && (k_left & 7) != 0) { c.a_ch = int(k_left >> 3); c.a_sh = 8 - int(k_left & 7); }
+    if (AT && m_left < BM && (m_left & 7) != 0) { c.a_ch = int(m_left >> 3); c.a_sh = 8 - int(m_left & 7); }
     if (!BKM && n_left < BN && (n_left & 7) != 0) { c.b_nc = int(n_left >> 3); c.b_sh = 8 - int(n_left & 7); }
     return c;
   }());
@@ -510,41 +548,50 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
 // ------------------------------------------------------------------ dispatch
 namespace {
 
-template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3 = false>
+template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3 = false, bool AT = false>
 hipError_t go(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (img) {
-    hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU, BKM>), dim3(1), dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_tiled_lds_image<TI, TO, BM, BN, WM, WN, V, GU, BKM, AT>), dim3(1), dim3(WM * WN * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM, P3>), grid, dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<TI, TO, BM, BN, WM, WN, V, GU, BKM, P3, AT>), grid, dim3(WM * WN * 64), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V>
-hipError_t by_gu_km(bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+hipError_t by_gu_km(bool gu, bool km, bool at, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (at) {
+    // A stored [K, M]: B stored [K, N], 16-byte staging (the planner rejects the rest)
+    if constexpr (V != 1) {
+      if (km) return hipErrorInvalidValue;
+      return gu ? go<TI, TO, BM, BN, WM, WN, V, true, false, false, true>(a, grid, s, img)
+                : go<TI, TO, BM, BN, WM, WN, V, false, false, false, true>(a, grid, s, img);
+    }
+    return hipErrorInvalidValue;
+  }
   if (gu) return km ? go<TI, TO, BM, BN, WM, WN, V, true, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, V, true, false>(a, grid, s, img);
   return km ? go<TI, TO, BM, BN, WM, WN, V, false, true>(a, grid, s, img) : go<TI, TO, BM, BN, WM, WN, V, false, false>(a, grid, s, img);
 }
 
 template <class TI, class TO, int BM, int BN, int WM, int WN>
-hipError_t by_vec_gu(int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
-  if (vec == 8) return by_gu_km<TI, TO, BM, BN, WM, WN, 8>(gu, km, a, grid, s, img);
-  if (vec == 2) return by_gu_km<TI, TO, BM, BN, WM, WN, 2>(gu, km, a, grid, s, img);
-  if (vec == 1) return by_gu_km<TI, TO, BM, BN, WM, WN, 1>(gu, km, a, grid, s, img);
+hipError_t by_vec_gu(int vec, bool gu, bool km, bool at, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (vec == 8) return by_gu_km<TI, TO, BM, BN, WM, WN, 8>(gu, km, at, a, grid, s, img);
+  if (vec == 2) return by_gu_km<TI, TO, BM, BN, WM, WN, 2>(gu, km, at, a, grid, s, img);
+  if (vec == 1) return by_gu_km<TI, TO, BM, BN, WM, WN, 1>(gu, km, at, a, grid, s, img);
   return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, hipStream_t s,
-                    bool img) {
+hipError_t by_types(int in_kind, int out_kind, int vec, bool gu, bool km, bool at, const TiledArgs& a, dim3 grid,
+                    hipStream_t s, bool img) {
   if (in_kind == IN_BF16) {
-    if (out_kind == OUT_F32) return by_vec_gu<InBF16, OutF32, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
-    if (out_kind == OUT_BF16) return by_vec_gu<InBF16, OutBF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
-    if (out_kind == OUT_F16) return by_vec_gu<InBF16, OutF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_F32) return by_vec_gu<InBF16, OutF32, BM, BN, WM, WN>(vec, gu, km, at, a, grid, s, img);
+    if (out_kind == OUT_BF16) return by_vec_gu<InBF16, OutBF16, BM, BN, WM, WN>(vec, gu, km, at, a, grid, s, img);
+    if (out_kind == OUT_F16) return by_vec_gu<InBF16, OutF16, BM, BN, WM, WN>(vec, gu, km, at, a, grid, s, img);
   } else if (in_kind == IN_F16) {
-    if (out_kind == OUT_F32) return by_vec_gu<InF16, OutF32, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
-    if (out_kind == OUT_BF16) return by_vec_gu<InF16, OutBF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
-    if (out_kind == OUT_F16) return by_vec_gu<InF16, OutF16, BM, BN, WM, WN>(vec, gu, km, a, grid, s, img);
+    if (out_kind == OUT_F32) return by_vec_gu<InF16, OutF32, BM, BN, WM, WN>(vec, gu, km, at, a, grid, s, img);
+    if (out_kind == OUT_BF16) return by_vec_gu<InF16, OutBF16, BM, BN, WM, WN>(vec, gu, km, at, a, grid, s, img);
+    if (out_kind == OUT_F16) return by_vec_gu<InF16, OutF16, BM, BN, WM, WN>(vec, gu, km, at, a, grid, s, img);
   }
   return hipErrorInvalidValue;
 }
@@ -578,14 +625,15 @@ hipError_t p3_by_types(int in_kind, int out_kind, int vec, bool gu, bool km, con
 
 }  // namespace
 
-hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
+hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
                         const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
     case KID_TILED_128:
-      return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+      return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_TILED_64:
-      return by_types<64, 64, 2, 1>(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+      return by_types<64, 64, 2, 1>(in_kind, out_kind, vec, gate_up, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_TILED_64_P3:
+      if (a_trans) return hipErrorInvalidValue;
       return p3_by_types(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }

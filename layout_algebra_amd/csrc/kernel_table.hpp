@@ -22,6 +22,9 @@ struct KernelShape {
   int b_follows_storage = 0;   // 1: the B block keeps the operand's orientation (K-contiguous with sw_b
                                //    for K-major B, N-contiguous with sw_bn otherwise)
   int sw_bn[3] = {0, 0, 0};    // Swizzle{B,M,S} of an N-contiguous B block, element offsets over (bk,bn):(bn,1)
+  int a_trans = 0;             // 1: the A block stored (bk,bm):(bm,1) (M contiguous, A stored [K, M]) under sw_a
+  int a_follows_storage = 0;   // 1: the kernel keeps A M-contiguous with sw_am when A is stored [K, M]
+  int sw_am[3] = {0, 0, 0};    // Swizzle{B,M,S} of an M-contiguous A block, element offsets over (bk,bm):(bm,1)
 };
 
 // Static description of each kernel id; the planner validates these maps.

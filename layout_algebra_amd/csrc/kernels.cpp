@@ -6,21 +6,27 @@ namespace lak {
 
 template <class C>
 static KernelShape fast_shape() {
-  return KernelShape{C::BM, C::BN, C::BK, C::NB, C::WM, C::WN, C::WM * C::WN * 64, 32, 32, 16,
-                     {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS}, C::BKMAJOR ? 1 : 0, 1, 1, C::STAGES};
+  KernelShape s{C::BM, C::BN, C::BK, C::NB, C::WM, C::WN, C::WM * C::WN * 64, 32, 32, 16,
+                {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS}, C::BKMAJOR ? 1 : 0, 1, 1, C::STAGES};
+  s.a_trans = C::ATRANS ? 1 : 0;
+  return s;
 }
 
 KernelShape kernel_shape(int kid) {
   switch (kid) {
     case KID_TILED_128:
-      return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {2, 5, 2}};
+      return KernelShape{128, 128, 64, 2, 2, 2, 256, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {2, 5, 2},
+                         0, 1, {2, 5, 2}};
     case KID_TILED_64:
     case KID_TILED_64_P3:
-      return KernelShape{64, 64, 64, 2, 2, 1, 128, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {1, 5, 2}};
+      return KernelShape{64, 64, 64, 2, 2, 1, 128, 32, 32, 16, {3, 3, 4}, {3, 3, 4}, 1, 0, 0, 2, 1, {1, 5, 2},
+                         0, 1, {1, 5, 2}};
     case KID_FAST_256: return fast_shape<CfgFast256>();
     case KID_FAST_GU: return fast_shape<CfgFastGU>();
     case KID_FAST_256_KM: return fast_shape<CfgFast256KM>();
     case KID_FAST_GU_KM: return fast_shape<CfgFastGUKM>();
+    case KID_FAST_256_AT: return fast_shape<CfgFast256AT>();
+    case KID_FAST_GU_AT: return fast_shape<CfgFastGUAT>();
     case KID_SKINNY_16: {
       using C = CfgSkinny16;
       return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
@@ -35,16 +41,19 @@ int64_t stage_elems(const KernelShape& s, bool gate_up) {
   return int64_t(s.bm) * s.bk + int64_t(gate_up ? 2 : 1) * s.bn * s.bk;
 }
 
-hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, const TiledArgs& args,
-                         dim3 grid, hipStream_t stream, bool lds_image) {
+hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
+                         const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image) {
   switch (kid) {
     case KID_TILED_128:
     case KID_TILED_64:
-    case KID_TILED_64_P3: return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
+    case KID_TILED_64_P3:
+      return launch_tiled(kid, in_kind, out_kind, vec, gate_up, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_FAST_256:
     case KID_FAST_GU:
     case KID_FAST_256_KM:
-    case KID_FAST_GU_KM: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_GU_KM:
+    case KID_FAST_256_AT:
+    case KID_FAST_GU_AT: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_SKINNY_16: return launch_skinny(in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }

@@ -50,6 +50,8 @@ enum KernelId : int {
   KID_FAST_GU_KM = 5,    // KID_FAST_GU for weights stored [N, K]
   KID_TILED_64 = 6,      // any shape, small grids: 64x64x64, 2 waves of 32x64, as KID_TILED_128 otherwise
   KID_TILED_64_P3 = 7,   // KID_TILED_64 with three K blocks in flight (plain GEMM, 16-byte loads)
+  KID_FAST_256_AT = 8,   // KID_FAST_256 for A stored [K, M] (M contiguous)
+  KID_FAST_GU_AT = 9,    // KID_FAST_GU for X stored [K, M]
   KID_COUNT
 };
 
@@ -63,13 +65,13 @@ enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 // 16 lanes must touch 16 distinct 16-byte slots of a 256-byte window.
 struct CfgFast256 {
   static constexpr int BM = 256, BN = 256, NB = 1, WM = 2, WN = 4, BK = 32, STAGES = 4;
-  static constexpr bool BKMAJOR = false;
+  static constexpr bool BKMAJOR = false, ATRANS = false;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 3;  // B: Swizzle{2,5,3} over 512-byte rows
 };
 struct CfgFastGU {
   static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4, BK = 32, STAGES = 4;
-  static constexpr bool BKMAJOR = false;
+  static constexpr bool BKMAJOR = false, ATRANS = false;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 2;  // B: Swizzle{2,5,2} over 256-byte rows
 };
@@ -82,6 +84,18 @@ struct CfgFast256KM : CfgFast256 {
 struct CfgFastGUKM : CfgFastGU {
   static constexpr bool BKMAJOR = true;
   static constexpr int BB = 2, BMb = 3, BS = 4;
+};
+
+// A stored [K, M] (M contiguous): the A block keeps the storage's orientation in
+// LDS, rows of BM values per k, under the swizzle of the N-contiguous 256-wide B
+// block (Swizzle{2,5,3} over 512-byte rows), and is read with transposing reads.
+struct CfgFast256AT : CfgFast256 {
+  static constexpr bool ATRANS = true;
+  static constexpr int AB = 2, AM = 5, AS = 3;
+};
+struct CfgFastGUAT : CfgFastGU {
+  static constexpr bool ATRANS = true;
+  static constexpr int AB = 2, AM = 5, AS = 3;
 };
 
 struct CfgSkinny16 {
@@ -101,11 +115,11 @@ hipError_t launch_mfma_probe(const void* ops, int64_t n_frags, float* sink, int6
                              int in_kind, hipStream_t stream);
 
 // Enqueue a GEMM (or, with lds_image, the debug stage dump) on `stream`.
-hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
+hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
                          const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
 
 // Per-family launchers.
-hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor,
+hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
                         const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
 hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid,
                        hipStream_t stream, bool lds_image);

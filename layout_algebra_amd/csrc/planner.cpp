@@ -59,6 +59,13 @@ int prefetch_blocks(const gemm_plan_s& p) {
   }
 }
 
+bool fail(std::string* err, const std::string& msg);
+
+bool fast_kid(int kid) {
+  return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
+         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT;
+}
+
 bool fail(std::string* err, const std::string& msg) {
   if (err) *err = msg;
   return false;
@@ -79,6 +86,31 @@ bool check_copy_a(const gemm_plan_s& p, std::string* err) {
       for (int e = 0; e < 8; ++e) {
         const int64_t o = p.lds_a.at({row, ch * 8 + e});
         if (o != o0 + e) return fail(err, "A copy destination is not contiguous");
+        if (hits[o]++) return fail(err, "A copy plan writes an LDS element twice");
+      }
+    }
+  }
+  for (int h : hits)
+    if (h != 1) return fail(err, "A copy plan leaves an LDS element unwritten");
+  return true;
+}
+
+// A stored [K, M] in the general kernel: thread t, slot j covers (row k,
+// 8-element M chunk), written as one 16-byte vector (like N-contiguous B).
+bool check_copy_a_t(const gemm_plan_s& p, std::string* err) {
+  const auto& s = p.shape;
+  const int chunks = s.bk * s.bm / 8;
+  if (chunks % s.threads) return fail(err, "A block does not split evenly into 16-byte vectors per thread");
+  std::vector<int> hits(static_cast<size_t>(s.bm) * s.bk, 0);
+  for (int t = 0; t < s.threads; ++t) {
+    for (int j = 0; j < chunks / s.threads; ++j) {
+      const int idx = t + s.threads * j;
+      const int k = idx / (s.bm / 8), mc = idx % (s.bm / 8);
+      const int64_t o0 = p.lds_a.at({mc * 8, k});
+      if (o0 % 8) return fail(err, "A copy destination is not 16-byte aligned");
+      for (int e = 0; e < 8; ++e) {
+        const int64_t o = p.lds_a.at({mc * 8 + e, k});
+        if (o != o0 + e) return fail(err, "A copy destination is not contiguous along M");
         if (hits[o]++) return fail(err, "A copy plan writes an LDS element twice");
       }
     }
@@ -171,13 +203,24 @@ bool check_copy_direct(const la::View& v, int64_t rows, int64_t cols, bool conti
 // contiguous and aligned in the LDS map.
 bool check_fragment_reads(const gemm_plan_s& p, std::string* err) {
   const auto& s = p.shape;
-  for (int64_t r = 0; r < s.bm; ++r)
-    for (int64_t k = 0; k < s.bk; k += 8) {
-      const int64_t o = p.lds_a.at({r, k});
-      if (o % 8) return fail(err, "A fragment read is not 16-byte aligned");
-      for (int e = 1; e < 8; ++e)
-        if (p.lds_a.at({r, k + e}) != o + e) return fail(err, "A fragment read is not contiguous");
-    }
+  if (s.a_trans) {
+    // M-contiguous A: transposing reads of 4 consecutive M values of one K row
+    for (int64_t k = 0; k < s.bk; ++k)
+      for (int64_t m = 0; m < s.bm; m += 4) {
+        const int64_t o = p.lds_a.at({m, k});
+        if (o % 4) return fail(err, "A transposing read is not 8-byte aligned");
+        for (int e = 1; e < 4; ++e)
+          if (p.lds_a.at({m + e, k}) != o + e) return fail(err, "A transposing read is not contiguous");
+      }
+  } else {
+    for (int64_t r = 0; r < s.bm; ++r)
+      for (int64_t k = 0; k < s.bk; k += 8) {
+        const int64_t o = p.lds_a.at({r, k});
+        if (o % 8) return fail(err, "A fragment read is not 16-byte aligned");
+        for (int e = 1; e < 8; ++e)
+          if (p.lds_a.at({r, k + e}) != o + e) return fail(err, "A fragment read is not contiguous");
+      }
+  }
   if (!s.b_kmajor) {
     for (int64_t k = 0; k < s.bk; ++k)
       for (int64_t n = 0; n < s.bn; n += 4) {
@@ -303,7 +346,8 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
   // the edges the general kernel masks
   const int64_t Mc = std::max<int64_t>(1, p.tiles_m) * s.bm, Nc = std::max<int64_t>(1, p.tiles_n) * s.bn;
   const int64_t Kc = std::max<int64_t>(1, (d.k + s.bk - 1) / s.bk) * s.bk;
-  p.glob_a = la::tile(la::Layout::row_major(Mc, Kc, d.lda), {s.bm, s.bk});
+  p.glob_a = s.a_trans ? la::tile(la::Layout::col_major(Mc, Kc, d.lda), {s.bm, s.bk})
+                       : la::tile(la::Layout::row_major(Mc, Kc, d.lda), {s.bm, s.bk});
   p.glob_b = p.b_kmajor ? la::tile(la::Layout::col_major(Kc, Nc, d.ldb), {s.bk, s.bn})
                         : la::tile(la::Layout::row_major(Kc, Nc, d.ldb), {s.bk, s.bn});
   p.glob_c = la::tile(la::Layout::row_major(Mc, Nc, d.ldc), {s.bm, s.bn});
@@ -318,7 +362,7 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
   // Per-instruction copy layouts: a wave instruction moves 64 x 16 bytes.
   // Rows of an operand block as stored in memory: A rows of BK along K;
   // B rows of BN along N ([K, N]) or of BK along K ([N, K]).
-  const int64_t a_cols = s.bk, b_cols = s.b_kmajor ? s.bk : s.bn;
+  const int64_t a_cols = s.a_trans ? s.bm : s.bk, b_cols = s.b_kmajor ? s.bk : s.bn;
   const int64_t b_ld = d.ldb;
   const int64_t per_instr = 64 * 8;
   if (per_instr % a_cols || per_instr % b_cols) return fail(err, "a copy instruction does not cover whole rows");
@@ -343,7 +387,8 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
       const int64_t j = ins / (T / 64), w = ins % (T / 64);
       for (int l = 0; l < 64; ++l) {
         const int64_t idx = w * 64 + l + T * j;
-        ia[ins].push_back(CopyChunk{idx / (s.bk / 8), (idx % (s.bk / 8)) * 8});
+        if (s.a_trans) ia[ins].push_back(CopyChunk{(idx % (s.bm / 8)) * 8, idx / (s.bm / 8)});
+        else ia[ins].push_back(CopyChunk{idx / (s.bk / 8), (idx % (s.bk / 8)) * 8});
       }
     }
     for (int64_t ins = 0; ins < nbk; ++ins) {
@@ -356,7 +401,7 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
     }
   }
   for (const auto& ch : ia)
-    if (!check_instr_reads(ga, ch, true, ca, err, "A")) return false;
+    if (!check_instr_reads(ga, ch, !s.a_trans, ca, err, "A")) return false;
   for (const auto& ch : ib)
     if (!check_instr_reads(gb, ch, !s.b_kmajor, cb, err, "B")) return false;
   std::ostringstream js;
@@ -401,8 +446,7 @@ std::vector<Store> store_plan(const gemm_plan_s& p) {
   std::vector<Store> out;
   const int tm = s.bm / s.waves_m, tn = s.bn / s.waves_n;
   int64_t ins = 0;
-  const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
-                    p.kid == lak::KID_FAST_GU_KM;
+  const bool fast = fast_kid(p.kid);
   for (int w = 0; w < s.waves_m * s.waves_n; ++w) {
     const int wm = w % s.waves_m, wn = w / s.waves_m;
     if (fast) {
@@ -475,8 +519,7 @@ bool plan_stores(gemm_plan_s& p, std::string* err) {
     if (offs[i] == offs[i - 1] + 1) { ++cur; } else { ++runs; cur = 1; }
     longest = std::max(longest, cur);
   }
-  const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
-                    p.kid == lak::KID_FAST_GU_KM;
+  const bool fast = fast_kid(p.kid);
   std::ostringstream js;
   js << "{\"style\":\"" << (fast ? "lds_rows" : s.mfma_m == 32 ? "mfma32" : "mfma16") << "\",\"elems_per_lane\":"
      << (fast ? 8 : 1) << ",\"runs_per_instr\":" << runs << ",\"run_bytes\":" << longest * p.out_bytes
@@ -500,8 +543,10 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p = gemm_plan_s{};
   p.d = d;
   if (d.m < 0 || d.n < 0 || d.k < 0) { fail(err, "m, n and k must be >= 0"); return GEMM_ERR_INVALID_ARG; }
-  if (d.lda < std::max<int64_t>(1, d.k)) { fail(err, "lda must be >= max(1, k)"); return GEMM_ERR_INVALID_ARG; }
   const bool kmajor = (d.flags & GEMM_FLAG_B_KMAJOR) != 0;
+  const bool atrans = (d.flags & GEMM_FLAG_A_TRANSPOSED) != 0;
+  if (!atrans && d.lda < std::max<int64_t>(1, d.k)) { fail(err, "lda must be >= max(1, k)"); return GEMM_ERR_INVALID_ARG; }
+  if (atrans && d.lda < std::max<int64_t>(1, d.m)) { fail(err, "lda must be >= max(1, m) for A stored [K, M]"); return GEMM_ERR_INVALID_ARG; }
   if (!kmajor && d.ldb < std::max<int64_t>(1, d.n)) { fail(err, "ldb must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
   if (kmajor && d.ldb < std::max<int64_t>(1, d.k)) { fail(err, "ldb must be >= max(1, k) for K-major B"); return GEMM_ERR_INVALID_ARG; }
   if (d.ldc < std::max<int64_t>(1, d.n)) { fail(err, "ldc must be >= max(1, n)"); return GEMM_ERR_INVALID_ARG; }
@@ -518,7 +563,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     fail(err, "unknown dtype");
     return GEMM_ERR_INVALID_ARG;
   }
-  if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR | GEMM_FLAG_LARGE_TILES)) { fail(err, "unknown flag bits"); return GEMM_ERR_INVALID_ARG; }
+  if (d.flags & ~(GEMM_FLAG_GATE_UP | GEMM_FLAG_B_KMAJOR | GEMM_FLAG_LARGE_TILES | GEMM_FLAG_A_TRANSPOSED)) {
+    fail(err, "unknown flag bits");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (atrans && kmajor) {
+    fail(err, "A stored [K, M] together with B stored [N, K] is not implemented");
+    return GEMM_ERR_UNSUPPORTED;
+  }
   if (d.batch < 1 || d.batch > 65535) { fail(err, "batch must be in 1..65535"); return GEMM_ERR_INVALID_ARG; }
   if (d.stride_a < 0 || d.stride_b < 0 || d.stride_c < 0) { fail(err, "batch strides must be >= 0"); return GEMM_ERR_INVALID_ARG; }
   if (d.batch > 1 && d.m > 0 && d.n > 0) {
@@ -543,6 +595,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
 
   p.gate_up = (d.flags & GEMM_FLAG_GATE_UP) != 0;
   p.b_kmajor = kmajor;
+  p.a_trans = atrans;
   p.in_kind = d.a_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16;
   p.out_kind = d.c_type == GEMM_F32 ? lak::OUT_F32 : d.c_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16;
   p.out_bytes = d.c_type == GEMM_F32 ? 4 : 2;
@@ -558,24 +611,31 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   // last valid one, which stay inside the row only when the row holds more
   // than 8 elements.  Shorter rows that are not whole chunks take 2-byte
   // loads (vec 1).
-  const bool chunks_whole = d.k % 8 == 0 && (kmajor || d.n % 8 == 0);
-  const bool rows_fit = (d.k % 8 == 0 || d.k > 8) && (kmajor || d.n % 8 == 0 || d.n > 8);
+  // (A stored [K, M] is staged in chunks along M instead of K.)
+  const int64_t a_row = atrans ? d.m : d.k;
+  const bool chunks_whole = a_row % 8 == 0 && (kmajor || d.n % 8 == 0);
+  const bool rows_fit = (a_row % 8 == 0 || a_row > 8) && (kmajor || d.n % 8 == 0 || d.n > 8);
   p.vec = in16 && chunks_whole ? 8 : rows_fit ? 2 : 1;
   p.align_bytes = p.vec == 8 ? 16 : 2;
+  if (atrans && p.vec == 1) {
+    fail(err, "A stored [K, M] needs m to be a multiple of 8 or larger than 8 (and n likewise)");
+    return GEMM_ERR_UNSUPPORTED;
+  }
 
   // Kernel choice: the full-tile direct-load kernels when every tile is whole
   // and every row starts on 16 bytes; otherwise the general kernel, which
   // masks edges and stages with the width chosen above.
   p.kid = lak::KID_TILED_128;
   {
-    const int fk = p.gate_up ? (kmajor ? lak::KID_FAST_GU_KM : lak::KID_FAST_GU)
-                             : (kmajor ? lak::KID_FAST_256_KM : lak::KID_FAST_256);
+    const int fk = p.gate_up ? (kmajor ? lak::KID_FAST_GU_KM : atrans ? lak::KID_FAST_GU_AT : lak::KID_FAST_GU)
+                             : (kmajor ? lak::KID_FAST_256_KM : atrans ? lak::KID_FAST_256_AT : lak::KID_FAST_256);
     const lak::KernelShape fs = lak::kernel_shape(fk);
     const bool whole = d.m > 0 && d.n > 0 && d.k > 0 && d.m % fs.bm == 0 && d.n % fs.bn == 0 && d.k % fs.bk == 0;
     const bool rows16 = in16 && out16;
     // per-lane source offsets of the direct loads are 32-bit byte offsets
     const int64_t b_rows = kmajor ? fs.bn : fs.bk;   // rows of B one block spans in memory
-    const bool off32 = 2 * int64_t(fs.bm) * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
+    const int64_t a_rows = atrans ? fs.bk : fs.bm;   // rows of A one block spans in memory
+    const bool off32 = 2 * a_rows * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
     const bool large = (d.flags & GEMM_FLAG_LARGE_TILES) != 0;
     if (whole && rows16 && off32) p.kid = fk;
     // Fewer than 32 full-tile workgroups leave most CUs idle: 64 x 64 tiles of
@@ -584,7 +644,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     if (!large && p.kid == fk && (d.m / fs.bm) * (d.n / fs.bn) * d.batch < 32) p.kid = lak::KID_TILED_64;
     // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
     const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
-    const bool skinny_fit = !p.gate_up && !kmajor && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
+    const bool skinny_fit = !p.gate_up && !kmajor && !atrans && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
                             d.k % ks.bk == 0 && in16 &&
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
@@ -604,10 +664,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     p.shape.b_kmajor = 0;
     for (int i = 0; i < 3; ++i) p.shape.sw_b[i] = p.shape.sw_bn[i];
   }
+  if (p.shape.a_follows_storage && atrans) {
+    // general kernel, A stored [K, M]: the A block stays M-contiguous in LDS
+    p.shape.a_trans = 1;
+    for (int i = 0; i < 3; ++i) p.shape.sw_a[i] = p.shape.sw_am[i];
+  }
   const auto& s = p.shape;
   // The fast kernels write C with 16-byte vectors, so C rows start on 16 bytes.
-  const bool fast = p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_GU || p.kid == lak::KID_FAST_256_KM ||
-                    p.kid == lak::KID_FAST_GU_KM;
+  const bool fast = fast_kid(p.kid);
   p.out_align_bytes = fast ? 16 : p.out_bytes;
   // The direct-load kernels need 16-byte rows (their planning checked in16 above).
   if (fast || p.kid == lak::KID_SKINNY_16) p.align_bytes = 16;
@@ -626,13 +690,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   // waves per CU; at 256 and fewer it measured no gain, above 512 the second
   // workgroup per SIMD is worth more)
   const int64_t wgs = int64_t(p.grid) * d.batch;
-  if (p.kid == lak::KID_TILED_64 && p.vec != 1 && !p.gate_up && wgs > 256 && wgs <= 512) p.kid = lak::KID_TILED_64_P3;
+  if (p.kid == lak::KID_TILED_64 && p.vec != 1 && !p.gate_up && !atrans && wgs > 256 && wgs <= 512) p.kid = lak::KID_TILED_64_P3;
   p.group_m = 8;
 
   try {
     const la::Swizzle swa(s.sw_a[0], s.sw_a[1], s.sw_a[2]);
     const la::Swizzle swb(s.sw_b[0], s.sw_b[1], s.sw_b[2]);
-    p.lds_a = la::View(swa, la::Layout::row_major(s.bm, s.bk, s.bk));           // (m, k) -> m*BK + k
+    p.lds_a = s.a_trans ? la::View(swa, la::Layout::col_major(s.bm, s.bk, s.bm))   // (m, k) -> k*BM + m
+                        : la::View(swa, la::Layout::row_major(s.bm, s.bk, s.bk));  // (m, k) -> m*BK + k
     p.lds_b = s.b_kmajor ? la::View(swb, la::Layout::col_major(s.bk, s.bn, s.bk))   // (k, n) -> n*BK + k
                          : la::View(swb, la::Layout::row_major(s.bk, s.bn, s.bn));  // (k, n) -> k*BN + n
     p.lds_b2 = p.lds_b;
@@ -647,15 +712,18 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
         (p.gate_up && !check_block(p.lds_b2, p.base_b2, int64_t(s.bn) * s.bk, "W_up", err)))
       return GEMM_ERR_RESOURCE;
     if (s.direct) {
-      if (!check_copy_direct(p.lds_a, s.bm, s.bk, true, "A", err) ||
+      if (!check_copy_direct(p.lds_a, s.bm, s.bk, !s.a_trans, "A", err) ||
           !check_copy_direct(p.lds_b, s.bk, s.bn, !s.b_kmajor, "B", err))
         return GEMM_ERR_RESOURCE;
-    } else if (!check_copy_a(p, err) || !(p.b_kmajor ? check_copy_b_rows(p, p.lds_b, err) : check_copy_b(p, p.lds_b, err))) {
+    } else if (!(s.a_trans ? check_copy_a_t(p, err) : check_copy_a(p, err)) ||
+               !(p.b_kmajor ? check_copy_b_rows(p, p.lds_b, err) : check_copy_b(p, p.lds_b, err))) {
       return GEMM_ERR_RESOURCE;
     }
     if (!check_fragment_reads(p, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
     if (!plan_copies(p, err)) return GEMM_ERR_RESOURCE;
-    if (!check_ring(p.lds_a, s.bm, s.bk, p.stage_elems, s.stages, "A", err) ||
+    if (!(s.a_trans ? check_ring(la::View(p.lds_a.swizzle(), la::Layout::row_major(s.bk, s.bm, s.bm)), s.bk, s.bm,
+                                 p.stage_elems, s.stages, "A", err)
+                    : check_ring(p.lds_a, s.bm, s.bk, p.stage_elems, s.stages, "A", err)) ||
         !(s.b_kmajor ? check_ring(la::View(p.lds_b.swizzle(), la::Layout::row_major(s.bn, s.bk, s.bk)), s.bn, s.bk,
                                   p.stage_elems, s.stages, "B", err)
                      : check_ring(p.lds_b, s.bk, s.bn, p.stage_elems, s.stages, "B", err)))
@@ -668,12 +736,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
 
   std::ostringstream js;
   static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
-                                      "tiled"};
+                                      "tiled", "fast_atrans", "fast_gate_up_atrans"};
+  static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
      << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc
      << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"out\":\"" << dtype_name(d.c_type) << "\""
      << ",\"gate_up\":" << (p.gate_up ? "true" : "false")
+     << ",\"a_order\":\"" << (p.a_trans ? "km" : "mk") << "\""
      << ",\"b_order\":\"" << (p.b_kmajor ? "nk" : "kn") << "\""
      << ",\"batch\":" << d.batch
      << ",\"tile\":[" << s.bm << "," << s.bn << "," << s.bk << "]"
@@ -711,4 +781,8 @@ gemm_status lds_offset(const gemm_plan_s& p, int operand, int64_t row, int64_t c
   return GEMM_OK;
 }
 
+}  // namespace plan
+
+namespace plan {
+bool is_fast(int kid) { return fast_kid(kid); }
 }  // namespace plan

@@ -18,6 +18,7 @@ struct gemm_plan_s {
   int out_align_bytes = 4;   // required alignment of the C / G / U pointers
   bool gate_up = false;
   bool b_kmajor = false;     // B (and the gate/up weights) stored [N, K]
+  bool a_trans = false;      // A (and X) stored [K, M]
   int tiles_m = 0, tiles_n = 0, grid = 0, group_m = 8;
   int64_t stage_elems = 0, lds_bytes = 0;
   lak::KernelShape shape{};
@@ -29,6 +30,9 @@ struct gemm_plan_s {
 };
 
 namespace plan {
+
+// The full-tile direct-load kernels (LDS-staged 16-byte epilogue stores).
+bool is_fast(int kid);
 
 // Build a plan; on failure returns a status and sets *err.
 gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err);
