@@ -132,6 +132,9 @@ def main():
                     help="hand B (or the gate/up weights) to the library as [N,K] (K contiguous)")
     ap.add_argument("--a-transposed", action="store_true",
                     help="hand A (or x) to the library as [K,M] (M contiguous)")
+    ap.add_argument("--gate-up-as-two-gemms", action="store_true",
+                    help="gate_up workload only: run each step as two separate GEMM launches (x W_gate, then x W_up) "
+                         "instead of the fused launch, for comparing their HBM traffic")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="timed steps as replays of a captured HIP graph (default), or one library call each")
     ap.add_argument("--preroll-seconds", type=float, default=0.5,
@@ -162,8 +165,12 @@ def main():
     torch.cuda.set_device(dev)
 
     x = synth.make_inputs(w)
-    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up, b_kmajor=args.b_kmajor,
-                        a_transposed=args.a_transposed)
+    two = args.gate_up_as_two_gemms
+    if two and (not w.gate_up or w.act):
+        print("--gate-up-as-two-gemms applies to the gate_up workload only", file=sys.stderr)
+        sys.exit(2)
+    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up and not two,
+                        b_kmajor=args.b_kmajor, a_transposed=args.a_transposed)
     dev_b = (lambda t: t.t().contiguous().to(dev)) if args.b_kmajor else (lambda t: t.to(dev))
     A = x["A"].t().contiguous().to(dev) if args.a_transposed else x["A"].to(dev)
     out_dt = synth.torch_dtype(w.out_kind)
@@ -173,6 +180,12 @@ def main():
         if w.act == "swiglu":
             def step(i):
                 la.gemm_gate_up_swiglu_run(plan, A, Wg, Wu, G)
+        elif two:
+            U = torch.empty_like(G)
+
+            def step(i):
+                la.gemm_run(plan, A, Wg, G)
+                la.gemm_run(plan, A, Wu, U)
         else:
             U = torch.empty_like(G)
 
@@ -282,6 +295,7 @@ def main():
                    "b_order": "nk" if args.b_kmajor else "kn",
                    "a_order": "km" if args.a_transposed else "mk",
                    "alpha": w.alpha, "beta": w.beta, "gate_up": w.gate_up,
+                   "gate_up_as_two_gemms": two,
                    "kernel": plan.describe()["kernel"], "grid": plan.describe()["grid"]},
         "roofline": roof,
         "wall_s_timed": wall,
