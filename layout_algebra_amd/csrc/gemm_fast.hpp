@@ -18,7 +18,10 @@
 //    [K, M] (M contiguous) stays M-contiguous in LDS and is read with the same
 //    transposing reads as B.
 //  * Large tiles (256 x 256, or 256 x 2*128 for gate/up) with 8 waves: one
-//    tile per CU at 4096^2, two waves per SIMD.
+//    tile per CU at 4096^2, two waves per SIMD.  For gate/up the waves split
+//    by weight: waves 0-3 own 64-column slices of the W_gate product, waves 4-7
+//    the same slices of the W_up product (the same 128 x 64 wave tile as the
+//    plain kernel, so both outputs leave in 128-byte row segments).
 //  * A multi-stage LDS ring (STAGES buffers) keeps STAGES-1 K blocks in
 //    flight.
 //  * Ping-pong wave groups: the 8 waves form two groups of four (one wave of
@@ -45,12 +48,20 @@ struct Fast {
   static constexpr bool ATR = C::ATRANS;                  // A stored [K, M] (M contiguous) instead of [M, K]
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
-  static constexpr int TM = BM / WM, TN = BN / WN;
+  // waves split by weight (gate/up): NBW weights per wave, WNW waves along N per weight
+  static constexpr bool WSPLIT = C::WSPLIT;
+  static constexpr int NBW = WSPLIT ? 1 : NB, WNW = WSPLIT ? WN / NB : WN;
+  static_assert(!WSPLIT || (NB == 2 && WN % NB == 0), "waves split by weight need two weights");
+  static constexpr int TM = BM / WM, TN = BN / WNW;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int SUB = BK / 16;                      // MFMA K sub-steps per K block
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BK * BN;
   static constexpr int STAGE = A_ELEMS + NB * B_ELEMS;     // 16-bit elements
+  // LDS of the kernel (16-bit elements): the stage ring, or for waves split by weight the SwiGLU
+  // exchange of the epilogue (two regions of 4 x FN x 64 x 16 floats plus a window per wave) if larger
+  static constexpr int XCHG = WSPLIT ? (2 * 4 * (BN / (WN / NB) / 32) * 64 * 16 + NW * 32 * (BN / (WN / NB) + 8)) * 2 : 0;
+  static constexpr int LDS_ELEMS = STAGES * STAGE > XCHG ? STAGES * STAGE : XCHG;
   static constexpr int A_LOADS = A_ELEMS / 512 / NW;       // 1 KB (512 elements) per wave instruction
   static constexpr int B_LOADS = B_ELEMS / 512 / NW;
   static constexpr int LOADS_PER_STAGE = A_LOADS + NB * B_LOADS;
@@ -141,8 +152,10 @@ struct Fast {
 
   // Lane-dependent parts of the fragment addresses.
   struct Lane {
-    int ar, ak, bn, bk, br, am;
-    __device__ __forceinline__ Lane(int wm, int wn, int lane) {
+    int ar, ak, bn, bk, br, am, tw;
+    __device__ __forceinline__ Lane(int wm, int wn_all, int lane) {
+      tw = WSPLIT ? wn_all / WNW : 0;            // weight block this wave reads (split waves)
+      const int wn = WSPLIT ? wn_all % WNW : wn_all;
       ar = wm * TM + (lane & 31);                // A: row l % 32 of each 32-row block
       ak = (lane >> 5) * 8;                      // A: K half of the 16-wide sub-step
       const int g = lane >> 4;                   // B (N-contiguous): 16-lane group
@@ -155,7 +168,7 @@ struct Fast {
 
   struct Frags {
     u32x4 a[FM];
-    u32x4 b[NB][FN];
+    u32x4 b[NBW][FN];
   };
 
   static __device__ __forceinline__ void read_frags(const LAK_LDS uint16_t* stage, int s, const Lane& ln, Frags& f) {
@@ -171,8 +184,8 @@ struct Fast {
       }
     }
 #pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const LAK_LDS uint16_t* bs = stage + A_ELEMS + t * B_ELEMS;
+    for (int t = 0; t < NBW; ++t) {
+      const LAK_LDS uint16_t* bs = stage + A_ELEMS + (WSPLIT ? ln.tw : t) * B_ELEMS;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (BKM) {
@@ -187,9 +200,9 @@ struct Fast {
     }
   }
 
-  static __device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[NB][FM][FN]) {
+  static __device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[NBW][FM][FN]) {
 #pragma unroll
-    for (int t = 0; t < NB; ++t)
+    for (int t = 0; t < NBW; ++t)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -230,7 +243,7 @@ __device__ __forceinline__ void block_barrier() {
 // RED: also fold the row reduction `red` of the FP32 values into R (a separate
 // instantiation, so that launches without it run exactly the plain epilogue).
 template <class TO, class F, bool RED = false>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, float alpha, float beta,
+__device__ __forceinline__ void store_band(const f32x16 (&accb)[F::FN], void* Cv, int64_t ldc, float alpha, float beta,
                                            bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane,
                                            int red = RED_NONE, float* R = nullptr) {
   constexpr int TN = F::TN;
@@ -239,81 +252,156 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], vo
   St* C = static_cast<St*>(Cv);
   const int lc = lane & 31, lr4 = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < F::FM; ++i) {
+  for (int j = 0; j < F::FN; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) win[(8 * (e >> 2) + lr4 + (e & 3)) * PITCH + j * 32 + lc] = alpha * accb[j][e];
+  __builtin_amdgcn_s_waitcnt(0xC07F);                // this wave's LDS writes are done
+  constexpr int CH = TN / 8;                         // 8-element chunks per row
+  constexpr int ROWS_PER_PASS = 64 / CH;
+#pragma unroll
+  for (int q = 0; q < 32 / ROWS_PER_PASS; ++q) {
+    const int r = q * ROWS_PER_PASS + lane / CH;
+    const int c = (lane % CH) * 8;
+    const LAK_LDS float* src = win + r * PITCH + c;
+    const f32x4 lo = *reinterpret_cast<const LAK_LDS f32x4*>(src);
+    const f32x4 hi = *reinterpret_cast<const LAK_LDS f32x4*>(src + 4);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    St* dst = C + (row0 + r) * ldc + col0 + c;
+    if (use_beta) {
+      if constexpr (sizeof(St) == 4) {
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(dst);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(dst + 4);
+        const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += beta * o[e];
+      } else {
+        const u32x4 ow = *reinterpret_cast<const u32x4*>(dst);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+      }
+    }
+    if constexpr (RED) {
+      // row reduction: the lane's 8 values, then the CH lanes sharing row r
+      float p = v[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) p = red_combine(red, p, v[e]);
+      p = red_lanes<CH>(red, p);
+      if (lane % CH == 0) red_commit(red, R + row0 + r, p);
+    }
+    if constexpr (sizeof(St) == 4) {
+      __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
+      __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(dst + 4));
+    } else {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = uint32_t(to_out<TO>(v[2 * e])) | (uint32_t(to_out<TO>(v[2 * e + 1])) << 16);
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                // reads done before the next band overwrites the window
+}
+
+template <class TO, class F, bool RED = false>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, float alpha, float beta,
+                                           bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane,
+                                           int red = RED_NONE, float* R = nullptr) {
+#pragma unroll
+  for (int i = 0; i < F::FM; ++i)
+    store_band<TO, F, RED>(acc[i], Cv, ldc, alpha, beta, use_beta, row0 + i * 32, col0, win, lane, red, R);
+}
+
+// SwiGLU epilogue of waves split by weight (see epilogue): wave of weight TW (0: W_gate, 1: W_up)
+// gives bands GIVE and takes its partner's half of bands OWN, through regions rg[TW] (written)
+// and rg[1 - TW] (read), each of 4 waves x FN blocks x 4 quads x 64 lanes of f32x4.
+template <class TO, class F, int TW>
+__device__ __forceinline__ void swiglu_exchange(f32x16 (&acc)[F::NBW][F::FM][F::FN], const TiledArgs& g, LAK_LDS f32x4* rg,
+                                                int64_t row0, int64_t col0, LAK_LDS float* xwin, int slot, int lane) {
+  constexpr int REG = 4 * F::FN * 4 * 64;
+  LAK_LDS f32x4* give = rg + TW * REG;
+  const LAK_LDS f32x4* take = rg + (1 - TW) * REG;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    // the W_gate wave gives band it and evaluates band it + 2; the W_up wave the other way round
+    const int give_band = TW == 0 ? it : it + 2, own_band = TW == 0 ? it + 2 : it;
 #pragma unroll
     for (int j = 0; j < F::FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) win[(8 * (e >> 2) + lr4 + (e & 3)) * PITCH + j * 32 + lc] = alpha * acc[i][j][e];
-    __builtin_amdgcn_s_waitcnt(0xC07F);              // this wave's LDS writes are done
-    constexpr int CH = TN / 8;                       // 8-element chunks per row
-    constexpr int ROWS_PER_PASS = 64 / CH;
-#pragma unroll
-    for (int q = 0; q < 32 / ROWS_PER_PASS; ++q) {
-      const int r = q * ROWS_PER_PASS + lane / CH;
-      const int c = (lane % CH) * 8;
-      const LAK_LDS float* src = win + r * PITCH + c;
-      const f32x4 lo = *reinterpret_cast<const LAK_LDS f32x4*>(src);
-      const f32x4 hi = *reinterpret_cast<const LAK_LDS f32x4*>(src + 4);
-      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      St* dst = C + (row0 + i * 32 + r) * ldc + col0 + c;
-      if (use_beta) {
-        if constexpr (sizeof(St) == 4) {
-          const f32x4 o0 = *reinterpret_cast<const f32x4*>(dst);
-          const f32x4 o1 = *reinterpret_cast<const f32x4*>(dst + 4);
-          const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += beta * o[e];
-        } else {
-          const u32x4 ow = *reinterpret_cast<const u32x4*>(dst);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
-        }
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& a = acc[0][give_band][j];
+        give[((slot * F::FN + j) * 4 + q) * 64 + lane] = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
       }
-      if constexpr (RED) {
-        // row reduction: the lane's 8 values, then the CH lanes sharing row r
-        float p = v[0];
+    block_barrier();                                 // both halves of the exchange are in LDS
+    f32x16 h[F::FN];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) p = red_combine(red, p, v[e]);
-        p = red_lanes<CH>(red, p);
-        if (lane % CH == 0) red_commit(red, R + row0 + i * 32 + r, p);
-      }
-      if constexpr (sizeof(St) == 4) {
-        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
-        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(dst + 4));
-      } else {
-        u32x4 w;
+    for (int j = 0; j < F::FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = uint32_t(to_out<TO>(v[2 * e])) | (uint32_t(to_out<TO>(v[2 * e + 1])) << 16);
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 o = take[((slot * F::FN + j) * 4 + q) * 64 + lane];
+        const f32x16& m = acc[0][own_band][j];
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)   // gate first: the wave's own value for TW == 0, the partner's otherwise
+          h[j][4 * q + e] = TW == 0 ? swiglu(m[4 * q + e], ov[e]) : swiglu(ov[e], m[4 * q + e]);
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);              // reads done before the next band overwrites the window
+    store_band<TO, F>(h, g.C, g.ldc, 1.0f, 0.0f, false, row0 + own_band * 32, col0, xwin, lane);
+    block_barrier();                                 // every wave has read its half before the next band is given
   }
 }
 
-template <class TO, class F, int NB, bool RED = false>
-__device__ __forceinline__ void epilogue(f32x16 (&acc)[NB][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
+template <class TO, class F, bool RED = false>
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[F::NBW][F::FM][F::FN], const TiledArgs& g, int64_t m0, int64_t n0,
                                          int wm, int wn, int wave, int lane, LAK_LDS uint16_t* lds) {
+  constexpr int NB = F::NB;
   static_assert(F::NW * 32 * (F::TN + 8) * 4 <= F::STAGES * F::STAGE * 2, "epilogue windows must fit in the stage buffers");
   LAK_LDS float* win = reinterpret_cast<LAK_LDS float*>(lds) + wave * 32 * (F::TN + 8);
-  const int64_t row0 = m0 + wm * F::TM, col0 = n0 + wn * F::TN;
-  if constexpr (NB == 2) {
-    if (g.act == 1) {
-      // fused activation: the gate and up accumulators of one element sit in the same lane
-#pragma unroll
-      for (int i = 0; i < F::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < F::FN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[0][i][j][e] = swiglu(acc[0][i][j][e], acc[1][i][j][e]);
-      store_tile<TO, F>(acc[0], g.C, g.ldc, 1.0f, 0.0f, false, row0, col0, win, lane);
+  const int64_t row0 = m0 + wm * F::TM;
+  if constexpr (F::WSPLIT) {
+    // waves split by weight: wave (wm, wn) holds the W_gate (wn < WNW) or W_up product of
+    // columns (wn mod WNW) * TN .. + TN of the tile
+    const int tw = wn / F::WNW;
+    const int64_t col0 = n0 + (wn % F::WNW) * F::TN;
+    if (g.act == 0) {
+      store_tile<TO, F>(acc[0], tw == 0 ? g.C : g.C2, g.ldc, 1.0f, 0.0f, false, row0, col0, win, lane);
       return;
     }
-  }
+    // SwiGLU: silu(g) * u needs the W_gate and W_up accumulators of an element together, and they
+    // sit in the paired waves w and w + 4 (same wm, same column slice).  Each pair splits the
+    // work: for bands 0 and 1 (32 rows each) the W_gate wave hands its FP32 values to the W_up
+    // wave, for bands 2 and 3 the other way round, through two LDS regions in the lanes' own
+    // register order; each wave evaluates its bands in FP32 and stores H through its window
+    // (after the regions).  All waves pass the same four barriers.
+    static_assert(F::NW == 8 && F::WNW * F::WM == 4 && F::FM == 4, "four waves per weight, four bands");
+    constexpr int REG = 4 * F::FN * 4 * 64;          // f32x4 per region: 4 waves x FN blocks x 4 quads x 64 lanes
+    static_assert((2 * REG * 4 + F::NW * 32 * (F::TN + 8)) * 4 <= F::LDS_ELEMS * 2, "SwiGLU exchange must fit in LDS");
+    LAK_LDS float* xwin = reinterpret_cast<LAK_LDS float*>(lds) + 2 * REG * 4 + wave * 32 * (F::TN + 8);
+    // one instantiation per weight, so every band index below is a compile-time constant (a
+    // runtime index into the accumulator array would move it to scratch memory)
+    if (tw == 0) {
+      swiglu_exchange<TO, F, 0>(acc, g, reinterpret_cast<LAK_LDS f32x4*>(lds), row0, col0, xwin, wave & 3, lane);
+    } else {
+      swiglu_exchange<TO, F, 1>(acc, g, reinterpret_cast<LAK_LDS f32x4*>(lds), row0, col0, xwin, wave & 3, lane);
+    }
+    return;
+  } else {
+    const int64_t col0 = n0 + wn * F::TN;
+    if constexpr (NB == 2) {
+      if (g.act == 1) {
+        // fused activation: the gate and up accumulators of one element sit in the same lane
 #pragma unroll
-  for (int t = 0; t < NB; ++t)
-    store_tile<TO, F, RED && NB == 1>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f, row0,
-                                      col0, win, lane, g.red, g.R);
+        for (int i = 0; i < F::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < F::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[0][i][j][e] = swiglu(acc[0][i][j][e], acc[1][i][j][e]);
+        store_tile<TO, F>(acc[0], g.C, g.ldc, 1.0f, 0.0f, false, row0, col0, win, lane);
+        return;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+      store_tile<TO, F, RED && NB == 1>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f,
+                                        row0, col0, win, lane, g.red, g.R);
+  }
 }
 
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each
@@ -352,7 +440,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   using F = Fast<TI, C>;
   constexpr int NB = C::NB;
   static_assert(C::WM * C::WN == 8, "ping-pong needs two groups of four waves");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::STAGES * F::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[F::LDS_ELEMS];
   LAK_LDS uint16_t* lds = (LAK_LDS uint16_t*)lds_raw;
 
   const int tid = threadIdx.x;
@@ -371,9 +459,9 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
   const uint16_t* b2_tile = NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr;
 
-  f32x16 acc[NB][F::FM][F::FN];
+  f32x16 acc[F::NBW][F::FM][F::FN];
 #pragma unroll
-  for (int t = 0; t < NB; ++t)
+  for (int t = 0; t < F::NBW; ++t)
 #pragma unroll
     for (int i = 0; i < F::FM; ++i)
 #pragma unroll
@@ -416,7 +504,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
 
   // After the last phase barrier every M phase (all LDS reads) is complete,
   // so the waves may reuse the stage buffers as epilogue windows.
-  epilogue<TO, F, NB, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
+  epilogue<TO, F, RED>(acc, g, m0, n0, wm, wn, wave, lane, lds);
 }
 
 // Debug: K block 0 of tile (dbg_tm, dbg_tn) staged by the kernel's own code, then copied out.

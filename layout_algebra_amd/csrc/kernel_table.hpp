@@ -25,6 +25,8 @@ struct KernelShape {
   int a_trans = 0;             // 1: the A block stored (bk,bm):(bm,1) (M contiguous, A stored [K, M]) under sw_a
   int a_follows_storage = 0;   // 1: the kernel keeps A M-contiguous with sw_am when A is stored [K, M]
   int sw_am[3] = {0, 0, 0};    // Swizzle{B,M,S} of an M-contiguous A block, element offsets over (bk,bm):(bm,1)
+  int wave_split = 0;          // 1 (gate/up): wave (wm, wn) owns a (bm/waves_m) x (nb*bn/waves_n) slice of the tile
+                               //    seen as [W_gate block | W_up block], i.e. one weight per wave
 };
 
 // Static description of each kernel id; the planner validates these maps.

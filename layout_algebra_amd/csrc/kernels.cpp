@@ -9,6 +9,7 @@ static KernelShape fast_shape() {
   KernelShape s{C::BM, C::BN, C::BK, C::NB, C::WM, C::WN, C::WM * C::WN * 64, 32, 32, 16,
                 {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS}, C::BKMAJOR ? 1 : 0, 1, 1, C::STAGES};
   s.a_trans = C::ATRANS ? 1 : 0;
+  s.wave_split = C::WSPLIT ? 1 : 0;
   return s;
 }
 

@@ -65,13 +65,15 @@ enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 // 16 lanes must touch 16 distinct 16-byte slots of a 256-byte window.
 struct CfgFast256 {
   static constexpr int BM = 256, BN = 256, NB = 1, WM = 2, WN = 4, BK = 32, STAGES = 4;
-  static constexpr bool BKMAJOR = false, ATRANS = false;
+  static constexpr bool BKMAJOR = false, ATRANS = false, WSPLIT = false;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 3;  // B: Swizzle{2,5,3} over 512-byte rows
 };
+// Gate/up: waves split by weight (WSPLIT): waves 0-3 (wn 0, 1) hold 128 x 64 slices of the
+// W_gate product, waves 4-7 (wn 2, 3) the same slices of the W_up product.
 struct CfgFastGU {
   static constexpr int BM = 256, BN = 128, NB = 2, WM = 2, WN = 4, BK = 32, STAGES = 4;
-  static constexpr bool BKMAJOR = false, ATRANS = false;
+  static constexpr bool BKMAJOR = false, ATRANS = false, WSPLIT = true;
   static constexpr int AB = 2, AM = 3, AS = 4;   // A: Swizzle{2,3,4} over 64-byte rows
   static constexpr int BB = 2, BMb = 5, BS = 2;  // B: Swizzle{2,5,2} over 256-byte rows
 };

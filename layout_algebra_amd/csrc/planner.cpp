@@ -248,10 +248,13 @@ bool check_fragment_reads(const gemm_plan_s& p, std::string* err) {
 bool check_ownership(const gemm_plan_s& p, std::string* err) {
   const auto& s = p.shape;
   const int mm = s.mfma_m;
-  const int tm = s.bm / s.waves_m, tn = s.bn / s.waves_n;
+  // waves split by weight: the tile is [W_gate block | W_up block], nb * bn columns
+  const int cols = s.wave_split ? s.nb * s.bn : s.bn;
+  const int tm = s.bm / s.waves_m, tn = cols / s.waves_n;
   if (tm % mm || tn % mm) return fail(err, "wave tile is not a multiple of the MFMA block");
+  if (s.wave_split && s.bn % tn) return fail(err, "a wave's slice straddles the two weights");
   const int regs = mm == 32 ? 16 : 4;
-  std::vector<int> hits(static_cast<size_t>(s.bm) * s.bn, 0);
+  std::vector<int> hits(static_cast<size_t>(s.bm) * cols, 0);
   for (int w = 0; w < s.waves_m * s.waves_n; ++w) {
     const int wm = w % s.waves_m, wn = w / s.waves_m;
     for (int i = 0; i < tm / mm; ++i)
@@ -261,7 +264,7 @@ bool check_ownership(const gemm_plan_s& p, std::string* err) {
             const int row = mm == 32 ? wm * tm + 32 * i + 8 * (r / 4) + 4 * (l / 32) + r % 4
                                      : wm * tm + 16 * i + 4 * (l / 16) + r;
             const int col = mm == 32 ? wn * tn + 32 * j + l % 32 : wn * tn + 16 * j + l % 16;
-            ++hits[static_cast<size_t>(row) * s.bn + col];
+            ++hits[static_cast<size_t>(row) * cols + col];
           }
   }
   for (int h : hits)
@@ -444,7 +447,8 @@ struct Store { int64_t ins; int lane; int64_t row, col; int n; };
 std::vector<Store> store_plan(const gemm_plan_s& p) {
   const auto& s = p.shape;
   std::vector<Store> out;
-  const int tm = s.bm / s.waves_m, tn = s.bn / s.waves_n;
+  // waves split by weight: columns of [W_gate block | W_up block]; column c is column c mod bn of output c / bn
+  const int tm = s.bm / s.waves_m, tn = (s.wave_split ? s.nb * s.bn : s.bn) / s.waves_n;
   int64_t ins = 0;
   const bool fast = fast_kid(p.kid);
   for (int w = 0; w < s.waves_m * s.waves_n; ++w) {
@@ -479,19 +483,20 @@ bool plan_stores(gemm_plan_s& p, std::string* err) {
   const std::vector<Store> plan = store_plan(p);
   // the kernels' store mask: element (row, col) of tile (tm, tn) is written
   // when it lies inside C (the full-tile kernels only run whole tiles)
+  const int64_t wcols = s.wave_split ? int64_t(s.nb) * s.bn : s.bn;   // store-plan columns per tile
   auto check_tile = [&](int64_t tm, int64_t tn) {
     const int64_t rows = std::min<int64_t>(s.bm, d.m - tm * s.bm), cols = std::min<int64_t>(s.bn, d.n - tn * s.bn);
-    std::vector<int> hits(static_cast<size_t>(s.bm) * s.bn, 0);
+    std::vector<int> hits(static_cast<size_t>(s.bm) * wcols, 0);
     for (const Store& st : plan)
       for (int e = 0; e < st.n; ++e) {
         const int64_t r = st.row, c = st.col + e;
-        if (r < 0 || r >= s.bm || c < 0 || c >= s.bn) return fail(err, "store plan leaves its tile");
-        if (r < rows && c < cols) ++hits[r * s.bn + c];
+        if (r < 0 || r >= s.bm || c < 0 || c >= wcols) return fail(err, "store plan leaves its tile");
+        if (r < rows && c % s.bn < cols) ++hits[r * wcols + c];
       }
     for (int64_t r = 0; r < s.bm; ++r)
-      for (int64_t c = 0; c < s.bn; ++c) {
-        const int h = hits[r * s.bn + c];
-        if (r < rows && c < cols ? h != 1 : h != 0)
+      for (int64_t c = 0; c < wcols; ++c) {
+        const int h = hits[r * wcols + c];
+        if (r < rows && c % s.bn < cols ? h != 1 : h != 0)
           return fail(err, "store plan does not write every element of C inside its tile exactly once");
       }
     return true;
@@ -512,7 +517,7 @@ bool plan_stores(gemm_plan_s& p, std::string* err) {
   std::vector<int64_t> offs;
   for (const Store& st : plan)
     if (st.ins == 0)
-      for (int e = 0; e < st.n; ++e) offs.push_back(p.glob_c.at({st.row, st.col + e}));
+      for (int e = 0; e < st.n; ++e) offs.push_back(p.glob_c.at({st.row, (st.col + e) % s.bn}));
   std::sort(offs.begin(), offs.end());
   int64_t runs = offs.empty() ? 0 : 1, longest = offs.empty() ? 0 : 1, cur = 1;
   for (size_t i = 1; i < offs.size(); ++i) {
@@ -706,6 +711,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     p.base_b2 = p.base_b + int64_t(s.bn) * s.bk;
     p.stage_elems = lak::stage_elems(s, p.gate_up);
     p.lds_bytes = int64_t(s.stages) * p.stage_elems * 2;
+    if (s.wave_split) {
+      // the SwiGLU epilogue of waves split by weight exchanges FP32 bands through two regions of
+      // 4 waves x (tn / 32) blocks x 64 lanes x 16 floats, plus a 32 x (tn + 8) float window per wave
+      const int64_t tn = int64_t(s.nb) * s.bn / s.waves_n, nw = int64_t(s.waves_m) * s.waves_n;
+      p.lds_bytes = std::max(p.lds_bytes, (2 * 4 * (tn / 32) * 64 * 16 + nw * 32 * (tn + 8)) * 4);
+    }
     if (p.lds_bytes > kMaxLdsBytes) { fail(err, "LDS footprint exceeds 160 KiB"); return GEMM_ERR_RESOURCE; }
     if (!check_block(p.lds_a, p.base_a, int64_t(s.bm) * s.bk, "A", err) ||
         !check_block(p.lds_b, p.base_b, int64_t(s.bn) * s.bk, "B", err) ||
@@ -754,6 +765,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
      << ",\"swizzle_a\":[" << s.sw_a[0] << "," << s.sw_a[1] << "," << s.sw_a[2] << "]"
      << ",\"swizzle_b\":[" << s.sw_b[0] << "," << s.sw_b[1] << "," << s.sw_b[2] << "]"
      << ",\"direct_loads\":" << (s.direct ? "true" : "false")
+     << ",\"waves_split_by_weight\":" << (s.wave_split ? "true" : "false")
      << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
      << ",\"prefetch_blocks\":" << prefetch_blocks(p)
      << ",\"global_a\":\"" << p.glob_a.str() << "\",\"global_b\":\"" << p.glob_b.str() << "\",\"global_c\":\""
