@@ -6,7 +6,8 @@ and the CPU-baseline leg of ``bench.py`` may import this package.  It shares
 no code with the HIP library and never imports it; the two meet only through
 the seeded inputs the callers pass to both.
 
-* ``gemm_f64``  -- FP64 triple loop (C, OpenMP over rows), see ``gemm_f64.c``.
+* ``gemm_f64``  -- FP64 triple loop (C, OpenMP over rows), see ``gemm_f64.c``;
+  inputs are 16-bit bf16/fp16 patterns or 32-bit binary32 words.
 * ``gate_up_swiglu_f64`` -- the gate/up products with the SwiGLU activation.
 * ``rms_norm_f64`` -- the row normalisation, numpy in binary64.
 * ``gemm_row_reduce_f64`` -- the GEMM with a sum / max / min of every output row.
@@ -23,6 +24,7 @@ from . import layout_ref  # noqa: F401  (re-exported for the tests)
 
 BF16 = 0
 F16 = 1
+F32 = 2
 
 _lib = None
 
@@ -42,6 +44,8 @@ def _load():
     lib.oracle_gemm_f64.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [vp, ctypes.c_int, i64, vp]
     lib.oracle_decode.restype = None
+    lib.oracle_decode32.argtypes = [vp, i64, vp]
+    lib.oracle_decode32.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -53,33 +57,42 @@ def _type_code(kind: str) -> int:
         return BF16
     if kind == "f16":
         return F16
-    raise ValueError("oracle inputs are 16-bit patterns of kind 'bf16' or 'f16', got %r" % (kind,))
+    if kind == "f32":
+        return F32
+    raise ValueError("oracle inputs are patterns of kind 'bf16', 'f16' or 'f32', got %r" % (kind,))
 
 
-def _as_u16(x) -> np.ndarray:
+def _as_bits(x, kind: str) -> np.ndarray:
     a = np.ascontiguousarray(x)
-    if a.dtype != np.uint16:
-        raise TypeError("pass raw 16-bit patterns as a uint16 array, got %s" % a.dtype)
+    want = np.uint32 if kind == "f32" else np.uint16
+    if a.dtype != want:
+        raise TypeError("pass raw %s patterns as a %s array, got %s" % (kind, np.dtype(want).name, a.dtype))
     return a
 
 
 def decode(bits, kind: str) -> np.ndarray:
-    """Exact float64 values of 16-bit patterns of the given format."""
-    b = _as_u16(bits)
+    """Exact float64 values of 16-bit (bf16, f16) or 32-bit (f32) patterns of the given format."""
+    b = _as_bits(bits, kind)
     out = np.empty(b.shape, dtype=np.float64)
-    _load().oracle_decode(b.ctypes.data, _type_code(kind), b.size, out.ctypes.data)
+    if kind == "f32":
+        _load().oracle_decode32(b.ctypes.data, b.size, out.ctypes.data)
+    else:
+        _load().oracle_decode(b.ctypes.data, _type_code(kind), b.size, out.ctypes.data)
     return out
 
 
 def gemm_f64(a_bits, a_kind, b_bits, b_kind, alpha=1.0, beta=0.0, c=None, nthreads=0):
-    """out = alpha * A @ B + beta * C in FP64 (k ascending), from 16-bit patterns.
+    """out = alpha * A @ B + beta * C in FP64 (k ascending), from input patterns.
 
-    ``a_bits`` is (M, K) uint16, ``b_bits`` is (K, N) uint16 (N contiguous),
+    ``a_bits`` is (M, K), ``b_bits`` is (K, N) (N contiguous): uint16 patterns
+    of kind 'bf16' / 'f16', or uint32 words of kind 'f32' (both operands then);
     ``c`` is (M, N) float32 or None (only read when beta != 0).
     Returns an (M, N) float64 array.
     """
-    a = _as_u16(a_bits)
-    b = _as_u16(b_bits)
+    if (a_kind == "f32") != (b_kind == "f32"):
+        raise ValueError("A and B must both be 16-bit patterns or both be 'f32' words")
+    a = _as_bits(a_bits, a_kind)
+    b = _as_bits(b_bits, b_kind)
     if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
         raise ValueError("shape mismatch: A %s, B %s" % (a.shape, b.shape))
     M, K = a.shape

@@ -11,7 +11,8 @@
  *     out[i,j] = alpha * sum_{k=0}^{K-1} a(i,k) * b(k,j)  +  beta * c(i,j)
  *
  * with every product and partial sum in IEEE binary64, k ascending, a(i,k)
- * and b(k,j) the exact values of the 16-bit input patterns, and c(i,j) the
+ * and b(k,j) the exact values of the input patterns (16-bit bfloat16 or
+ * binary16, or 32-bit binary32 words), and c(i,j) the
  * FP32 value of the existing output.  The beta term is left out entirely when
  * beta == 0 (the existing output is then never read, so NaN there cannot leak
  * in).  This is the epilogue form "alpha * accumulator + beta * old C" of the
@@ -24,10 +25,14 @@
  * B is K-outer/N-inner with row stride ldb (element (k,j) at k*ldb + j);
  * C and out are row-major with strides ldc and ldo.
  *
- * The 16-bit decoders below are written from the formats' definitions:
+ * The decoders below are written from the formats' definitions:
  *   bfloat16 = the upper half of an IEEE binary32 pattern;
  *   binary16 = 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits,
- *              subnormals scaled by 2^-24, exponent 31 = Inf/NaN.
+ *              subnormals scaled by 2^-24, exponent 31 = Inf/NaN;
+ *   binary32 = 1 sign bit, 8 exponent bits (bias 127), 23 fraction bits,
+ *              subnormals scaled by 2^-149, exponent 255 = Inf/NaN.
+ * Both operands have the same element width: 16-bit patterns (A and B each
+ * bfloat16 or binary16) or 32-bit words (both binary32).
  */
 #include <math.h>
 #include <stdint.h>
@@ -39,6 +44,7 @@
 
 #define ORACLE_BF16 0
 #define ORACLE_F16 1
+#define ORACLE_F32 2
 
 double oracle_bf16_to_f64(uint16_t bits) {
   uint32_t word = ((uint32_t)bits) << 16;
@@ -62,8 +68,29 @@ double oracle_f16_to_f64(uint16_t bits) {
   return sign ? -mag : mag;
 }
 
+double oracle_f32_to_f64(uint32_t bits) {
+  int sign = (int)(bits >> 31);
+  int expo = (int)((bits >> 23) & 0xff);
+  uint32_t frac = bits & 0x7fffffu;
+  double mag;
+  if (expo == 0) {
+    mag = ldexp((double)frac, -149);                  /* zero or subnormal */
+  } else if (expo == 255) {
+    mag = frac ? NAN : INFINITY;
+  } else {
+    mag = ldexp((double)(frac | 0x800000u), expo - 150); /* (1 + f/2^23) * 2^(e-127) */
+  }
+  return sign ? -mag : mag;
+}
+
 static double decode(uint16_t bits, int type) {
   return type == ORACLE_BF16 ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);
+}
+
+/* Element idx of an operand stored as 16-bit patterns or 32-bit words. */
+static double element(const void* base, int type, int64_t idx) {
+  if (type == ORACLE_F32) return oracle_f32_to_f64(((const uint32_t*)base)[idx]);
+  return decode(((const uint16_t*)base)[idx], type);
 }
 
 /* Decode n 16-bit patterns (test helper: lets the suite compare the decoders
@@ -72,19 +99,24 @@ void oracle_decode(const uint16_t* src, int type, int64_t n, double* dst) {
   for (int64_t i = 0; i < n; ++i) dst[i] = decode(src[i], type);
 }
 
+/* Decode n binary32 words (same purpose). */
+void oracle_decode32(const uint32_t* src, int64_t n, double* dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = oracle_f32_to_f64(src[i]);
+}
+
 /*
  * Returns 0 on success, -1 on a bad argument.  nthreads <= 0 lets OpenMP pick.
  * C may be NULL when beta == 0.
  */
 int oracle_gemm_f64(int64_t M, int64_t N, int64_t K,
-                    const uint16_t* A, int a_type, int64_t lda,
-                    const uint16_t* B, int b_type, int64_t ldb,
+                    const void* A, int a_type, int64_t lda,
+                    const void* B, int b_type, int64_t ldb,
                     const float* C, int64_t ldc,
                     double alpha, double beta,
                     double* out, int64_t ldo, int nthreads) {
   if (M < 0 || N < 0 || K < 0) return -1;
-  if ((a_type != ORACLE_BF16 && a_type != ORACLE_F16) ||
-      (b_type != ORACLE_BF16 && b_type != ORACLE_F16)) return -1;
+  if (a_type < ORACLE_BF16 || a_type > ORACLE_F32 || b_type < ORACLE_BF16 || b_type > ORACLE_F32) return -1;
+  if ((a_type == ORACLE_F32) != (b_type == ORACLE_F32)) return -1;
   if (beta != 0.0 && C == NULL && M > 0 && N > 0) return -1;
   if (M == 0 || N == 0) return 0;
 
@@ -106,9 +138,8 @@ int oracle_gemm_f64(int64_t M, int64_t N, int64_t K,
       for (int64_t i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-          const double a = decode(A[i * lda + k], a_type);
-          const uint16_t* brow = B + k * ldb;
-          for (int64_t j = 0; j < N; ++j) acc[j] += a * decode(brow[j], b_type);
+          const double a = element(A, a_type, i * lda + k);
+          for (int64_t j = 0; j < N; ++j) acc[j] += a * element(B, b_type, k * ldb + j);
         }
         for (int64_t j = 0; j < N; ++j) {
           double v = alpha * acc[j];

@@ -7,7 +7,7 @@ receive the very same 16-bit patterns produced here.
 Recipe: values are sampled in float32 on the CPU with a seeded
 ``torch.Generator`` (uniform via ``rand``, normal via ``randn`` scaled by the
 standard deviation) and rounded once to bf16/fp16 with torch's
-round-to-nearest-even conversion.
+round-to-nearest-even conversion (float32 inputs keep the sampled values).
 """
 import math
 from dataclasses import dataclass, field
@@ -186,7 +186,9 @@ def make_inputs(w: Workload):
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw 16-bit patterns of a CPU bf16/fp16 tensor as a uint16 numpy array."""
+    """Raw patterns of a CPU tensor: bf16/fp16 as a uint16 numpy array, float32 as uint32."""
+    if t.dtype == torch.float32:
+        return t.contiguous().view(torch.int32).numpy().view(np.uint32)
     if t.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(t.dtype)
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)

@@ -1,7 +1,8 @@
 """Pins for the FP64 oracle GEMM (oracle/gemm_f64.c).
 
 The oracle is checked against things it does not compute itself:
-  * torch's and numpy's own bf16/fp16 decoding, for all 65,536 patterns;
+  * torch's and numpy's own bf16/fp16 decoding, for all 65,536 patterns, and
+    numpy's binary32 decoding on every exponent with edge and random fractions;
   * exact rational arithmetic (fractions) on tiny shapes;
   * closed forms: ones x ones = K, identity and permutation B, alpha = 0;
   * numpy's float64 matmul (a library routine) on moderate shapes.
@@ -42,6 +43,41 @@ def test_decode_f16_exhaustive():
     assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
 
 
+def _f32_patterns():
+    """Every sign and exponent with the edge fractions (0, 1, 2, all ones, the top bit, one below it)
+    and 64 drawn fractions each, plus a million random words."""
+    rng = np.random.default_rng(32)
+    fr = np.concatenate([np.array([0, 1, 2, 0x7FFFFF, 0x400000, 0x3FFFFF], dtype=np.uint32),
+                         rng.integers(0, 1 << 23, 64, dtype=np.uint32)])
+    se = np.arange(512, dtype=np.uint32) << 23          # sign and exponent fields
+    grid = (se[:, None] | fr[None, :]).ravel()
+    return np.concatenate([grid, rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)])
+
+
+def test_decode_f32_against_numpy():
+    b = _f32_patterns()
+    mine = oracle.decode(b, "f32")
+    with np.errstate(invalid="ignore"):      # signalling NaN patterns
+        ref = b.view(np.float32).astype(np.float64)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    # hand values from the format's definition
+    assert oracle.decode(np.array([0x3F800000, 0x00000001, 0x007FFFFF, 0x7F7FFFFF, 0xC0490FDB], dtype=np.uint32),
+                         "f32").tolist() == [1.0, 2.0 ** -149, (2.0 ** 23 - 1) * 2.0 ** -149,
+                                             (2.0 - 2.0 ** -23) * 2.0 ** 127, -3.1415927410125732]
+
+
+def test_mixed_element_widths_are_rejected():
+    a = synth.uniform((2, 3), 1, "f32")
+    b = synth.uniform((3, 2), 2, "bf16")
+    with pytest.raises(ValueError):
+        oracle.gemm_f64(synth.bits(a), "f32", synth.bits(b), "bf16")
+    with pytest.raises(TypeError):
+        oracle.gemm_f64(synth.bits(b.t().contiguous()), "f32", synth.bits(a.t().contiguous()), "f32")
+
+
 def _exact(a_t, b_t, alpha, beta, c):
     """Exact rational alpha*A@B + beta*C from torch's decoding."""
     A = [[Fraction(float(v)) for v in row] for row in a_t.to(torch.float64).tolist()]
@@ -67,7 +103,7 @@ def _exact(a_t, b_t, alpha, beta, c):
     return out, mag
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
 def test_exact_rational_tiny_shapes(kind):
     seed = 100
     for M in range(1, 5):
@@ -98,7 +134,7 @@ def test_exact_rational_odd_shapes_with_beta_zero():
                 assert abs(got[i, j] - float(exact[i][j])) <= float(mag[i][j]) * (K + 3) * 2.0 ** -53
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
 def test_ones_times_ones_is_K(kind):
     for (M, N, K) in [(5, 7, 13), (3, 4, 4096)]:
         a = torch.ones((M, K), dtype=synth.torch_dtype(kind))
@@ -115,7 +151,7 @@ def test_ones_A_gives_column_sums():
     np.testing.assert_allclose(got, np.broadcast_to(colsum, got.shape), rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
 def test_identity_and_permutation_B(kind):
     K, M = 48, 20
     a = synth.uniform((M, K), 5, kind)
@@ -148,7 +184,7 @@ def test_alpha_beta_special_cases():
     assert oracle.gemm_f64(synth.bits(a[:0]), "f16", synth.bits(b), "f16").shape == (0, N)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
 def test_matches_numpy_float64_matmul(kind):
     for (M, N, K), seed in [((37, 53, 129), 1), ((64, 80, 257), 2), ((5, 300, 64), 3)]:
         a = synth.normal((M, K), seed, kind)
