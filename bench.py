@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+# MI355X dense MFMA: bf16/f16 256 CU x 4096 FLOP/clk x 2.4 GHz; fp32 256 CU x 256 FLOP/clk x 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
@@ -43,8 +44,8 @@ SHARED_SOURCES = ("kernel_common.hpp", "launch.hpp")
 NORM_SOURCES = ("rms_norm.hip", "norm.hpp")
 ATTN_SOURCES = ("attention.hip", "attention.hpp")
 # GEMM kernel families by the prefix of the planned kernel's name
-GEMM_SOURCES = {"fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_": ("gemm_tiled.hip",),
-                "skinny_": ("gemm_skinny.hip",)}
+GEMM_SOURCES = {"fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_f32": ("gemm_f32.hip",),
+                "tiled_": ("gemm_tiled.hip",), "skinny_": ("gemm_skinny.hip",)}
 
 
 # host code that decides which instantiation a GEMM plan launches, and with which grid
@@ -280,7 +281,7 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[w.in_kind],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    if roof["bound"] == "mfma" and w.flops() >= 1e11:
+    if roof["bound"] == "mfma" and w.flops() >= 1e11 and w.in_kind != "f32":
         roof["mfma_ceiling"] = mfma_ceiling(dev, A, flops, roof["achieved"])
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel_avg_ms"] = kern_ms

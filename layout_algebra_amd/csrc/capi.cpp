@@ -332,7 +332,7 @@ gemm_status gemm_plan_lds_offset(gemm_plan_t plan, int operand, int64_t row, int
 
 gemm_status gemm_plan_lds_stage_bytes(gemm_plan_t plan, int64_t* out_bytes) {
   if (!plan || !out_bytes) return set_err(GEMM_ERR_NULL, "plan and out_bytes must not be NULL");
-  *out_bytes = plan->stage_elems * 2;
+  *out_bytes = plan->stage_elems * plan->in_bytes;
   return GEMM_OK;
 }
 

@@ -453,74 +453,33 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(const TiledArg
     }
   }
 
-  // Epilogue straight from the accumulator lane map.  The 16 old values of a
-  // 32 x 32 block are all requested before the first is used, from clamped
-  // addresses (element 0 for positions outside C), so their latencies overlap;
-  // only the stores are predicated.
-  typedef typename TO::storage St;
-  const int lc = lane & 31, lr4 = (lane >> 5) * 4;
-  // row reduction: per-lane partials of the 16 rows of each 32-row block
-  // (columns j*32 + lc of the wave's sub-tile), then across the 32 lanes of each half
-  const int red = GU ? RED_NONE : g.red;
-  float part[T::FM][16];
+  // Epilogue straight from the accumulator lane map (epilogue_mfma32 for a
+  // plain GEMM; gate/up writes G and U, or silu(G) * U, with no row reduction).
+  if constexpr (GU) {
+    typedef typename TO::storage St;
+    const int lc = lane & 31, lr4 = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
+    for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[i][e] = red_identity(red);
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      const int64_t col = n0 + wn * T::TN + j * 32 + lc;
-      const int64_t rbase = m0 + wm * T::TM + i * 32 + lr4;
-      int64_t idx[16];
-      bool ok[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = rbase + 8 * (e >> 2) + (e & 3);
-        ok[e] = col < g.N && row < g.M;
-        idx[e] = row * g.ldc + col;
-      }
-      if constexpr (GU) {
+      for (int j = 0; j < T::FN; ++j) {
+        const int64_t col = n0 + wn * T::TN + j * 32 + lc;
+        const int64_t rbase = m0 + wm * T::TM + i * 32 + lr4;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          if (!ok[e]) continue;
+          const int64_t row = rbase + 8 * (e >> 2) + (e & 3);
+          if (col >= g.N || row >= g.M) continue;
+          const int64_t idx = row * g.ldc + col;
           if (g.act == 1) {
-            static_cast<St*>(g.C)[idx[e]] = to_out<TO>(swiglu(acc[0][i][j][e], acc[1][i][j][e]));
+            static_cast<St*>(g.C)[idx] = to_out<TO>(swiglu(acc[0][i][j][e], acc[1][i][j][e]));
           } else {
-            static_cast<St*>(g.C)[idx[e]] = to_out<TO>(acc[0][i][j][e]);
-            static_cast<St*>(g.C2)[idx[e]] = to_out<TO>(acc[1][i][j][e]);
+            static_cast<St*>(g.C)[idx] = to_out<TO>(acc[0][i][j][e]);
+            static_cast<St*>(g.C2)[idx] = to_out<TO>(acc[1][i][j][e]);
           }
-        }
-      } else {
-        St* C = static_cast<St*>(g.C);
-        float v[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = g.alpha * acc[0][i][j][e];
-        if (g.beta != 0.0f) {
-          St old[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) old[e] = C[ok[e] ? idx[e] : 0];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) v[e] += g.beta * from_out<TO>(old[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (ok[e]) C[idx[e]] = to_out<TO>(v[e]);
-          if (red != RED_NONE && ok[e]) part[i][e] = red_combine(red, part[i][e], v[e]);
         }
       }
     }
-  }
-  if (red != RED_NONE) {
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = red_lanes<32>(red, part[i][e]);
-        const int64_t row = m0 + wm * T::TM + i * 32 + lr4 + 8 * (e >> 2) + (e & 3);
-        if (lc == 0 && row < g.M) red_commit(red, g.R + row, p);
-      }
+  } else {
+    epilogue_mfma32<TO, T::FM, T::FN>(g, acc[0], m0 + wm * T::TM, n0 + wn * T::TN, lane, g.red);
   }
 }
 

@@ -101,6 +101,71 @@ __device__ __forceinline__ void red_commit(int op, float* p, float v) {
   }
 }
 
+// Epilogue of one wave's FM x FN grid of 32 x 32 accumulator blocks, straight
+// from the accumulator lane map (register e of lane l: row 8*(e/4) + 4*(l/32) +
+// e%4, column l % 32 of its block): C = alpha * acc + beta * C_old in FP32
+// (C_old read only when beta != 0), written only inside [0,M) x [0,N), and,
+// when red != RED_NONE, every row's partial folded into R.  r0 / c0: the
+// wave's first row and column in C.  The 16 old values of a block are all
+// requested before the first is used, from clamped addresses (element 0 for
+// positions outside C), so their latencies overlap; only the stores are
+// predicated.
+template <class TO, int FM, int FN>
+__device__ __forceinline__ void epilogue_mfma32(const TiledArgs& g, const f32x16 (&acc)[FM][FN], int64_t r0, int64_t c0,
+                                                int lane, int red) {
+  typedef typename TO::storage St;
+  const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+  // row reduction: per-lane partials of the 16 rows of each 32-row block
+  // (columns j*32 + lc of the wave's sub-tile), then across the 32 lanes of each half
+  float part[FM][16];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[i][e] = red_identity(red);
+  St* C = static_cast<St*>(g.C);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = c0 + j * 32 + lc;
+      const int64_t rbase = r0 + i * 32 + lr4;
+      int64_t idx[16];
+      bool ok[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = rbase + 8 * (e >> 2) + (e & 3);
+        ok[e] = col < g.N && row < g.M;
+        idx[e] = row * g.ldc + col;
+      }
+      float v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = g.alpha * acc[i][j][e];
+      if (g.beta != 0.0f) {
+        St old[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) old[e] = C[ok[e] ? idx[e] : 0];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] += g.beta * from_out<TO>(old[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (ok[e]) C[idx[e]] = to_out<TO>(v[e]);
+        if (red != RED_NONE && ok[e]) part[i][e] = red_combine(red, part[i][e], v[e]);
+      }
+    }
+  }
+  if (red != RED_NONE) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = red_lanes<32>(red, part[i][e]);
+        const int64_t row = r0 + i * 32 + lr4 + 8 * (e >> 2) + (e & 3);
+        if (lc == 0 && row < g.M) red_commit(red, g.R + row, p);
+      }
+  }
+}
+
 // SwiGLU combination of one gate and one up accumulator, in FP32:
 // silu(g) * u with silu(g) = g / (1 + e^-g).
 __device__ __forceinline__ float swiglu(float gate, float up) { return gate / (1.0f + expf(-gate)) * up; }

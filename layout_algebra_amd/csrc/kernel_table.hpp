@@ -27,12 +27,15 @@ struct KernelShape {
   int sw_am[3] = {0, 0, 0};    // Swizzle{B,M,S} of an M-contiguous A block, element offsets over (bk,bm):(bm,1)
   int wave_split = 0;          // 1 (gate/up): wave (wm, wn) owns a (bm/waves_m) x (nb*bn/waves_n) slice of the tile
                                //    seen as [W_gate block | W_up block], i.e. one weight per wave
+  int in_bytes = 2;            // bytes per input element (2: bf16 / f16, 4: binary32)
+  int k_sub = 0;               // K-contiguous blocks stored as bk / k_sub sub-blocks of k_sub values per row
+                               //    ((rows, (k_sub, bk/k_sub)) : (k_sub, (1, rows*k_sub))); 0: one row of bk
 };
 
 // Static description of each kernel id; the planner validates these maps.
 KernelShape kernel_shape(int kid);
 
-// LDS elements (16-bit) of one pipeline stage (one A block and one B block per weight).
+// LDS elements of one pipeline stage (one A block and one B block per weight).
 int64_t stage_elems(const KernelShape& s, bool gate_up);
 
 }  // namespace lak

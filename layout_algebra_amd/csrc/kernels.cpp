@@ -28,6 +28,15 @@ KernelShape kernel_shape(int kid) {
     case KID_FAST_GU_KM: return fast_shape<CfgFastGUKM>();
     case KID_FAST_256_AT: return fast_shape<CfgFast256AT>();
     case KID_FAST_GU_AT: return fast_shape<CfgFastGUAT>();
+    case KID_TILED_F32: {
+      // K-contiguous blocks: two 64-byte rows of 16 binary32 values per row under Swizzle{2,2,4};
+      // M/N-contiguous blocks: rows of 128 values under Swizzle{1,5,5}
+      KernelShape s{128, 128, 32, 1, 2, 2, 256, 32, 32, 2, {2, 2, 4}, {2, 2, 4}, 1, 0, 0, 2, 1, {1, 5, 5},
+                    0, 1, {1, 5, 5}};
+      s.in_bytes = 4;
+      s.k_sub = 16;
+      return s;
+    }
     case KID_SKINNY_16: {
       using C = CfgSkinny16;
       return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
@@ -56,6 +65,7 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_FAST_256_AT:
     case KID_FAST_GU_AT: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_SKINNY_16: return launch_skinny(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

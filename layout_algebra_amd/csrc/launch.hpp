@@ -11,7 +11,7 @@ enum : int { RED_NONE = 0, RED_SUM = 1, RED_MAX = 2, RED_MIN = 3 };
 
 // Everything one launch needs; plain values only.
 struct TiledArgs {
-  const uint16_t* A;     // [M, K] row-major, lda
+  const uint16_t* A;     // [M, K] row-major, lda (binary32 inputs: the same address, read as 32-bit words)
   const uint16_t* B;     // [K, N] N contiguous, ldb (W_gate for gate/up)
   const uint16_t* B2;    // W_up for gate/up, else unused
   void* C;               // [M, N] row-major, ldc (G for gate/up)
@@ -28,13 +28,16 @@ struct TiledArgs {
   uint16_t* dbg_out;     // LDS-image debug launch: destination of one stage
 };
 
-// The matrices of batch entry blockIdx.y (grid dimension y = batch count).
+// The matrices of batch entry blockIdx.y (grid dimension y = batch count);
+// IB: bytes per input element (the A / B pointers count 16-bit units).
+template <int IB = 2>
 __device__ __forceinline__ TiledArgs at_batch(const TiledArgs& g) {
+  static_assert(IB == 2 || IB == 4, "16- or 32-bit input elements");
   TiledArgs r = g;
   const int64_t z = blockIdx.y;
-  r.A = g.A + z * g.sa;
-  r.B = g.B + z * g.sb;
-  r.B2 = g.B2 ? g.B2 + z * g.sb : nullptr;
+  r.A = g.A + z * g.sa * (IB / 2);
+  r.B = g.B + z * g.sb * (IB / 2);
+  r.B2 = g.B2 ? g.B2 + z * g.sb * (IB / 2) : nullptr;
   r.C = g.C ? static_cast<void*>(static_cast<char*>(g.C) + z * g.sc * g.out_bytes) : nullptr;
   r.C2 = g.C2 ? static_cast<void*>(static_cast<char*>(g.C2) + z * g.sc * g.out_bytes) : nullptr;
   r.R = g.R ? g.R + z * g.M : nullptr;
@@ -52,10 +55,11 @@ enum KernelId : int {
   KID_TILED_64_P3 = 7,   // KID_TILED_64 with three K blocks in flight (plain GEMM, 16-byte loads)
   KID_FAST_256_AT = 8,   // KID_FAST_256 for A stored [K, M] (M contiguous)
   KID_FAST_GU_AT = 9,    // KID_FAST_GU for X stored [K, M]
+  KID_TILED_F32 = 10,    // binary32 A and B, any shape: 128x128x32, 4 waves of 64x64, v_mfma_f32_32x32x2_f32
   KID_COUNT
 };
 
-enum InKind : int { IN_BF16 = 0, IN_F16 = 1 };
+enum InKind : int { IN_BF16 = 0, IN_F16 = 1, IN_F32 = 2 };
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
 // Compile-time parameters of the fast kernels (one source of truth for the
@@ -127,5 +131,7 @@ hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args
                        hipStream_t stream, bool lds_image);
 hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                          bool lds_image);
+hipError_t launch_f32(int out_kind, int vec, bool b_kmajor, bool a_trans, const TiledArgs& args, dim3 grid,
+                      hipStream_t stream, bool lds_image);
 
 }  // namespace lak

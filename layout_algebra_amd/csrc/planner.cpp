@@ -54,12 +54,18 @@ int prefetch_blocks(const gemm_plan_s& p) {
   switch (p.kid) {
     case lak::KID_TILED_64_P3: return 3;
     case lak::KID_TILED_64: return p.vec != 1 && !p.gate_up ? 2 : 1;
-    case lak::KID_TILED_128: return 1;
+    case lak::KID_TILED_128:
+    case lak::KID_TILED_F32: return 1;
     default: return p.shape.stages - 1;
   }
 }
 
 bool fail(std::string* err, const std::string& msg);
+
+// The kernel's copy of one block of an operand: for wave instruction `ins`, the
+// tile coordinates (row, col) of the chunk each lane moves (8 16-bit or 4
+// binary32 elements, running along the operand's contiguous direction).
+struct CopyChunk { int64_t row, col; };
 
 bool fast_kid(int kid) {
   return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
@@ -196,6 +202,67 @@ bool check_copy_direct(const la::View& v, int64_t rows, int64_t cols, bool conti
   return true;
 }
 
+// Staging chunks of the binary32 kernel (4 elements, 16 bytes): slot j of
+// thread t moves chunk idx = t + threads * j, and a wave instruction moves 64
+// consecutive chunks.  Returned in storage coordinates (row of the operand as
+// it sits in memory, first element along that row).  K-contiguous block (rows
+// of bk values): instruction idx / 64 covers 8 rows; within it lane l stages
+// row 4 (l / 32) + (l % 16) / 4, sub-block (l / 16) % 2, chunk l % 4, so each
+// 16-lane group writes 4 whole 64-byte rows of one sub-block.  M/N-contiguous
+// block (rows of `row_len` values per k): row idx / (row_len / 4), chunk
+// idx % (row_len / 4).
+CopyChunk f32_chunk(const lak::KernelShape& s, bool kcontig, int64_t row_len, int64_t idx) {
+  if (kcontig) {
+    const int64_t l = idx % 64, q = l / 16, w = l % 16;
+    return CopyChunk{(idx / 64) * 8 + (q / 2) * 4 + w / 4, (q % 2) * s.k_sub + (w % 4) * 4};
+  }
+  return CopyChunk{idx / (row_len / 4), (idx % (row_len / 4)) * 4};
+}
+
+// Binary32 copy plan of one operand block: every 16-byte LDS vector written
+// once, by a chunk of 4 consecutive elements of one storage row.  `v` maps
+// the operand's mathematical (row, col) coordinates; `rows_are_math_rows`:
+// a storage row is a mathematical row (A [M, K], and B [K, N] in (k, n)).
+bool check_copy_f32(const gemm_plan_s& p, const la::View& v, int64_t srows, int64_t scols, bool kcontig,
+                    bool rows_are_math_rows, const char* name, std::string* err) {
+  const auto& s = p.shape;
+  const int64_t chunks = srows * scols / 4;
+  if (chunks % s.threads) return fail(err, std::string(name) + " block does not split evenly into 16-byte vectors per thread");
+  std::vector<int> hits(static_cast<size_t>(srows * scols), 0);
+  for (int64_t idx = 0; idx < chunks; ++idx) {
+    const CopyChunk c = f32_chunk(s, kcontig, scols, idx);
+    if (c.row >= srows || c.col + 4 > scols) return fail(err, std::string(name) + " copy chunk outside its block");
+    auto at = [&](int64_t e) { return rows_are_math_rows ? v.at({c.row, c.col + e}) : v.at({c.col + e, c.row}); };
+    const int64_t o0 = at(0);
+    if (o0 % 4) return fail(err, std::string(name) + " copy destination is not 16-byte aligned");
+    for (int e = 0; e < 4; ++e) {
+      const int64_t o = at(e);
+      if (o != o0 + e) return fail(err, std::string(name) + " copy destination is not contiguous");
+      if (o < 0 || o >= srows * scols || hits[o]++) return fail(err, std::string(name) + " copy plan writes an LDS word twice");
+    }
+  }
+  for (int h : hits)
+    if (h != 1) return fail(err, std::string(name) + " copy plan leaves an LDS word unwritten");
+  return true;
+}
+
+// LDS -> register reads of the binary32 kernel: a K-contiguous block is read
+// 4 K values (16 bytes) per lane, which must be contiguous and aligned; an
+// M/N-contiguous block one value per lane (nothing to check beyond the map's
+// injectivity).  `v` in mathematical coordinates, K the second (A) or first (B) mode.
+bool check_fragment_reads_f32(const la::View& v, int64_t others, int64_t bk, bool k_second, const char* name,
+                              std::string* err) {
+  for (int64_t r = 0; r < others; ++r)
+    for (int64_t k = 0; k < bk; k += 4) {
+      auto at = [&](int64_t kk) { return k_second ? v.at({r, kk}) : v.at({kk, r}); };
+      const int64_t o = at(k);
+      if (o % 4) return fail(err, std::string(name) + " fragment read is not 16-byte aligned");
+      for (int e = 1; e < 4; ++e)
+        if (at(k + e) != o + e) return fail(err, std::string(name) + " fragment read is not contiguous");
+    }
+  return true;
+}
+
 // LDS -> register reads of the fast kernels.  A: lane l of fragment row block
 // reads 8 consecutive K values of row l % 32 as one 16-byte chunk.  B:
 // transposing reads, where lanes 4e..4e+3 of each 16-lane group address 4
@@ -297,23 +364,19 @@ int64_t run_elems(const la::Layout& c) {
   return st.empty() || st[0] != 1 ? 1 : sh[0];
 }
 
-// The kernel's copy of one block of an operand: for wave instruction `ins`, the
-// tile coordinates (row, col) of the 8-element chunk each lane moves (the
-// chunk runs along the operand's contiguous direction).
-struct CopyChunk { int64_t row, col; };
 
 // The set of global elements (relative to the tile origin, through the tiled
 // global view's within-tile mode) that wave instruction `ins` reads must equal
 // the image of its copy layout placed at its first row.  `along_cols`: the
-// chunk is 8 consecutive columns of (rows, cols) (else 8 consecutive rows).
+// chunk is ce consecutive columns of (rows, cols) (else ce consecutive rows).
 bool check_instr_reads(const la::Layout& glob, const std::vector<CopyChunk>& chunks, bool along_cols,
-                       const la::Layout& instr, std::string* err, const char* name) {
+                       const la::Layout& instr, int ce, std::string* err, const char* name) {
   std::vector<int64_t> got;
   int64_t r0 = INT64_MAX, c0 = INT64_MAX;
   for (const CopyChunk& ch : chunks) {
     r0 = std::min(r0, ch.row);
     c0 = std::min(c0, ch.col);
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < ce; ++e) {
       const int64_t r = along_cols ? ch.row : ch.row + e, c = along_cols ? ch.col + e : ch.col;
       got.push_back(glob.at({r, c}));
     }
@@ -344,7 +407,7 @@ struct TileView {
 bool plan_copies(gemm_plan_s& p, std::string* err) {
   const auto& s = p.shape;
   const gemm_desc& d = p.d;
-  const int eb = 2;
+  const int eb = s.in_bytes, ce = 16 / eb;   // bytes per element, elements per 16-byte chunk
   // covering extents: tile() needs whole tiles; coordinates past M, N or K are
   // the edges the general kernel masks
   const int64_t Mc = std::max<int64_t>(1, p.tiles_m) * s.bm, Nc = std::max<int64_t>(1, p.tiles_n) * s.bn;
@@ -367,14 +430,26 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
   // B rows of BN along N ([K, N]) or of BK along K ([N, K]).
   const int64_t a_cols = s.a_trans ? s.bm : s.bk, b_cols = s.b_kmajor ? s.bk : s.bn;
   const int64_t b_ld = d.ldb;
-  const int64_t per_instr = 64 * 8;
+  const int64_t per_instr = 64 * ce;
   if (per_instr % a_cols || per_instr % b_cols) return fail(err, "a copy instruction does not cover whole rows");
   const la::Layout ca = copy_instr_layout(per_instr / a_cols, a_cols, d.lda);
   const la::Layout cb = copy_instr_layout(per_instr / b_cols, b_cols, b_ld);
   const int64_t na = int64_t(s.bm) * s.bk / per_instr, nbk = int64_t(s.bk) * s.bn / per_instr;
 
   std::vector<std::vector<CopyChunk>> ia(na), ib(nbk);
-  if (s.direct) {
+  if (eb == 4) {
+    // binary32 kernel: storage coordinates -> block coordinates (A (m, k), B (k, n))
+    for (int64_t ins = 0; ins < na; ++ins)
+      for (int l = 0; l < 64; ++l) {
+        const CopyChunk c = f32_chunk(s, !s.a_trans, a_cols, ins * 64 + l);
+        ia[ins].push_back(s.a_trans ? CopyChunk{c.col, c.row} : c);
+      }
+    for (int64_t ins = 0; ins < nbk; ++ins)
+      for (int l = 0; l < 64; ++l) {
+        const CopyChunk c = f32_chunk(s, s.b_kmajor, b_cols, ins * 64 + l);
+        ib[ins].push_back(s.b_kmajor ? CopyChunk{c.col, c.row} : c);
+      }
+  } else if (s.direct) {
     // lane l of instruction `ins` fills physical elements [512 ins + 8 l, +8)
     const std::vector<CopyChunk> inva = lds_inverse(p.lds_a, s.bm, s.bk);
     const std::vector<CopyChunk> invb = lds_inverse(p.lds_b, s.bk, s.bn);
@@ -404,9 +479,9 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
     }
   }
   for (const auto& ch : ia)
-    if (!check_instr_reads(ga, ch, !s.a_trans, ca, err, "A")) return false;
+    if (!check_instr_reads(ga, ch, !s.a_trans, ca, ce, err, "A")) return false;
   for (const auto& ch : ib)
-    if (!check_instr_reads(gb, ch, !s.b_kmajor, cb, err, "B")) return false;
+    if (!check_instr_reads(gb, ch, !s.b_kmajor, cb, ce, err, "B")) return false;
   std::ostringstream js;
   js << "{\"A\":{\"instr\":\"" << ca.str() << "\",\"run_bytes\":" << run_elems(ca) * eb << ",\"instrs_per_block\":" << na << "}"
      << ",\"B\":{\"instr\":\"" << cb.str() << "\",\"run_bytes\":" << run_elems(cb) * eb << ",\"instrs_per_block\":" << nbk << "}}";
@@ -418,15 +493,17 @@ bool plan_copies(gemm_plan_s& p, std::string* err) {
 
 // Ring of `stages` blocks of (rows, cols), block base `base` inside a stage of
 // `stage` elements.  The allocation map is Swizzle o ((rows, cols, stages) :
-// (ld_r, ld_c, stage)) applied to offsets relative to the block base; stage s
+// (ld_r, ld_c, stage)) applied to offsets relative to the block base (the row
+// and column modes as the block map has them, nested or flat); stage s
 // is the window at origin (0, 0, s).  Every window must give stage * s plus the
 // block map: the stage bases sit on the swizzle period, so the phase is the
 // allocation's.
 bool check_ring(const la::View& block, int64_t rows, int64_t cols, int64_t stage, int stages, const char* name,
                 std::string* err) {
-  std::vector<int64_t> sh, st;
-  la::leaves(block.base().stride(), st);
-  const la::View ring(block.swizzle(), la::Layout::flat({rows, cols, int64_t(stages)}, {st[0], st[1], stage}));
+  const la::Layout& bl = block.base();
+  const la::View ring(block.swizzle(),
+                      la::Layout(la::Tree::T({bl.shape().mode(0), bl.shape().mode(1), la::Tree::L(stages)}),
+                                 la::Tree::T({bl.stride().mode(0), bl.stride().mode(1), la::Tree::L(stage)})));
   for (int sidx = 0; sidx < stages; ++sidx) {
     const la::View w = ring.window({0, 0, sidx}, {rows, cols, 1});
     for (int64_t r = 0; r < rows; ++r)
@@ -572,8 +649,9 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     fail(err, "unknown flag bits");
     return GEMM_ERR_INVALID_ARG;
   }
-  if (atrans && kmajor) {
-    fail(err, "A stored [K, M] together with B stored [N, K] is not implemented");
+  const bool in32 = d.a_type == GEMM_F32 && d.b_type == GEMM_F32;
+  if (atrans && kmajor && !in32) {
+    fail(err, "A stored [K, M] together with B stored [N, K] is implemented for binary32 inputs only");
     return GEMM_ERR_UNSUPPORTED;
   }
   if (d.batch < 1 || d.batch > 65535) { fail(err, "batch must be in 1..65535"); return GEMM_ERR_INVALID_ARG; }
@@ -588,8 +666,12 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
       return GEMM_ERR_INVALID_ARG;
     }
   }
-  if (d.a_type != d.b_type || d.a_type == GEMM_F32) {
-    fail(err, "A and B must both be bf16 or both be f16");
+  if (d.a_type != d.b_type) {
+    fail(err, "A and B must both be bf16, both be f16 or both be f32");
+    return GEMM_ERR_UNSUPPORTED;
+  }
+  if (in32 && (d.flags & GEMM_FLAG_GATE_UP)) {
+    fail(err, "binary32 inputs are planned for plain GEMMs only (no gate/up)");
     return GEMM_ERR_UNSUPPORTED;
   }
   // 32-bit tile ids and in-tile offsets; global offsets are 64-bit.
@@ -601,7 +683,8 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p.gate_up = (d.flags & GEMM_FLAG_GATE_UP) != 0;
   p.b_kmajor = kmajor;
   p.a_trans = atrans;
-  p.in_kind = d.a_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16;
+  p.in_kind = d.a_type == GEMM_BF16 ? lak::IN_BF16 : d.a_type == GEMM_F16 ? lak::IN_F16 : lak::IN_F32;
+  p.in_bytes = in32 ? 4 : 2;
   p.out_kind = d.c_type == GEMM_F32 ? lak::OUT_F32 : d.c_type == GEMM_BF16 ? lak::OUT_BF16 : lak::OUT_F16;
   p.out_bytes = d.c_type == GEMM_F32 ? 4 : 2;
   // Batch strides move every row start of matrix b by b*stride, so with more
@@ -609,6 +692,17 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   const bool many = d.batch > 1;
   const bool in16 = d.lda % 8 == 0 && d.ldb % 8 == 0 && (!many || (d.stride_a % 8 == 0 && d.stride_b % 8 == 0));
   const bool out16 = d.ldc % 8 == 0 && (!many || d.stride_c % 8 == 0);
+  if (in32) {
+    // Binary32 inputs: one kernel for every shape and storage order, staging
+    // 4-element chunks along each operand's contiguous direction: one 16-byte
+    // load each when every row starts on 16 bytes and no chunk is cut by an
+    // edge (vec 4), else four 4-byte loads (vec 1).
+    const bool rows16 = d.lda % 4 == 0 && d.ldb % 4 == 0 && (!many || (d.stride_a % 4 == 0 && d.stride_b % 4 == 0));
+    const bool whole = (atrans ? d.m : d.k) % 4 == 0 && (kmajor ? d.k : d.n) % 4 == 0;
+    p.vec = rows16 && whole ? 4 : 1;
+    p.align_bytes = p.vec == 4 ? 16 : 4;
+    p.kid = lak::KID_TILED_F32;
+  }
   // The general kernel stages 8-element chunks along K (A, K-major B) or N
   // (N-contiguous B), one 16-byte load each: aligned (vec 8) when rows start
   // on 16 bytes and no chunk is cut by an edge; else at 2-byte alignment
@@ -618,6 +712,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   // loads (vec 1).
   // (A stored [K, M] is staged in chunks along M instead of K.)
   const int64_t a_row = atrans ? d.m : d.k;
+  if (!in32) {
   const bool chunks_whole = a_row % 8 == 0 && (kmajor || d.n % 8 == 0);
   const bool rows_fit = (a_row % 8 == 0 || a_row > 8) && (kmajor || d.n % 8 == 0 || d.n > 8);
   p.vec = in16 && chunks_whole ? 8 : rows_fit ? 2 : 1;
@@ -663,6 +758,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
       if (p.vec != 1 || wg128 < 384) p.kid = lak::KID_TILED_64;
     }
   }
+  }  // 16-bit inputs
   p.shape = lak::kernel_shape(p.kid);
   if (p.shape.b_follows_storage && !kmajor) {
     // general kernel, B stored N-contiguous: the B block stays N-contiguous in LDS
@@ -701,16 +797,32 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   try {
     const la::Swizzle swa(s.sw_a[0], s.sw_a[1], s.sw_a[2]);
     const la::Swizzle swb(s.sw_b[0], s.sw_b[1], s.sw_b[2]);
+    using la::Tree;
+    // K-contiguous block of `rows` rows: one row of bk values, or bk / k_sub sub-blocks of k_sub
+    // values per row ((rows, (k_sub, bk/k_sub)) : (k_sub, (1, rows*k_sub)), the K mode nested)
+    auto kmode = [&](int64_t rows, Tree& sh, Tree& st) {
+      if (s.k_sub) {
+        sh = Tree::T({Tree::L(s.k_sub), Tree::L(s.bk / s.k_sub)});
+        st = Tree::T({Tree::L(1), Tree::L(rows * s.k_sub)});
+      } else {
+        sh = Tree::L(s.bk);
+        st = Tree::L(1);
+      }
+    };
+    const int64_t krow = s.k_sub ? s.k_sub : s.bk;   // stride between rows of a K-contiguous block
+    Tree ksh, kst;
+    kmode(s.bm, ksh, kst);
     p.lds_a = s.a_trans ? la::View(swa, la::Layout::col_major(s.bm, s.bk, s.bm))   // (m, k) -> k*BM + m
-                        : la::View(swa, la::Layout::row_major(s.bm, s.bk, s.bk));  // (m, k) -> m*BK + k
-    p.lds_b = s.b_kmajor ? la::View(swb, la::Layout::col_major(s.bk, s.bn, s.bk))   // (k, n) -> n*BK + k
+                        : la::View(swa, la::Layout(Tree::T({Tree::L(s.bm), ksh}), Tree::T({Tree::L(krow), kst})));  // (m, k) -> m*BK + k
+    kmode(s.bn, ksh, kst);
+    p.lds_b = s.b_kmajor ? la::View(swb, la::Layout(Tree::T({ksh, Tree::L(s.bn)}), Tree::T({kst, Tree::L(krow)})))  // (k, n) -> n*BK + k
                          : la::View(swb, la::Layout::row_major(s.bk, s.bn, s.bn));  // (k, n) -> k*BN + n
     p.lds_b2 = p.lds_b;
     p.base_a = 0;
     p.base_b = int64_t(s.bm) * s.bk;
     p.base_b2 = p.base_b + int64_t(s.bn) * s.bk;
     p.stage_elems = lak::stage_elems(s, p.gate_up);
-    p.lds_bytes = int64_t(s.stages) * p.stage_elems * 2;
+    p.lds_bytes = int64_t(s.stages) * p.stage_elems * s.in_bytes;
     if (s.wave_split) {
       // the SwiGLU epilogue of waves split by weight exchanges FP32 bands through two regions of
       // 4 waves x (tn / 32) blocks x 64 lanes x 16 floats, plus a 32 x (tn + 8) float window per wave
@@ -722,7 +834,13 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
         !check_block(p.lds_b, p.base_b, int64_t(s.bn) * s.bk, "B", err) ||
         (p.gate_up && !check_block(p.lds_b2, p.base_b2, int64_t(s.bn) * s.bk, "W_up", err)))
       return GEMM_ERR_RESOURCE;
-    if (s.direct) {
+    if (s.in_bytes == 4) {
+      if (!(s.a_trans ? check_copy_f32(p, p.lds_a, s.bk, s.bm, false, false, "A", err)
+                      : check_copy_f32(p, p.lds_a, s.bm, s.bk, true, true, "A", err)) ||
+          !(s.b_kmajor ? check_copy_f32(p, p.lds_b, s.bn, s.bk, true, false, "B", err)
+                       : check_copy_f32(p, p.lds_b, s.bk, s.bn, false, true, "B", err)))
+        return GEMM_ERR_RESOURCE;
+    } else if (s.direct) {
       if (!check_copy_direct(p.lds_a, s.bm, s.bk, !s.a_trans, "A", err) ||
           !check_copy_direct(p.lds_b, s.bk, s.bn, !s.b_kmajor, "B", err))
         return GEMM_ERR_RESOURCE;
@@ -730,12 +848,21 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
                !(p.b_kmajor ? check_copy_b_rows(p, p.lds_b, err) : check_copy_b(p, p.lds_b, err))) {
       return GEMM_ERR_RESOURCE;
     }
-    if (!check_fragment_reads(p, err) || !check_ownership(p, err)) return GEMM_ERR_RESOURCE;
+    if (s.in_bytes == 4) {
+      if ((!s.a_trans && !check_fragment_reads_f32(p.lds_a, s.bm, s.bk, true, "A", err)) ||
+          (s.b_kmajor && !check_fragment_reads_f32(p.lds_b, s.bn, s.bk, false, "B", err)))
+        return GEMM_ERR_RESOURCE;
+    } else if (!check_fragment_reads(p, err)) {
+      return GEMM_ERR_RESOURCE;
+    }
+    if (!check_ownership(p, err)) return GEMM_ERR_RESOURCE;
     if (!plan_copies(p, err)) return GEMM_ERR_RESOURCE;
-    if (!(s.a_trans ? check_ring(la::View(p.lds_a.swizzle(), la::Layout::row_major(s.bk, s.bm, s.bm)), s.bk, s.bm,
+    // rings in storage order: (k, m) for A stored [K, M], (n, k) for B stored [N, K] (permute()
+    // reverses the block map's modes)
+    if (!(s.a_trans ? check_ring(la::View(p.lds_a.swizzle(), la::permute(p.lds_a.base())), s.bk, s.bm,
                                  p.stage_elems, s.stages, "A", err)
                     : check_ring(p.lds_a, s.bm, s.bk, p.stage_elems, s.stages, "A", err)) ||
-        !(s.b_kmajor ? check_ring(la::View(p.lds_b.swizzle(), la::Layout::row_major(s.bn, s.bk, s.bk)), s.bn, s.bk,
+        !(s.b_kmajor ? check_ring(la::View(p.lds_b.swizzle(), la::permute(p.lds_b.base())), s.bn, s.bk,
                                   p.stage_elems, s.stages, "B", err)
                      : check_ring(p.lds_b, s.bk, s.bn, p.stage_elems, s.stages, "B", err)))
       return GEMM_ERR_RESOURCE;
@@ -747,7 +874,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
 
   std::ostringstream js;
   static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
-                                      "tiled", "fast_atrans", "fast_gate_up_atrans"};
+                                      "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -771,6 +898,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
      << ",\"global_a\":\"" << p.glob_a.str() << "\",\"global_b\":\"" << p.glob_b.str() << "\",\"global_c\":\""
      << p.glob_c.str() << "\""
      << ",\"copy\":" << p.copy_json << ",\"store\":" << p.store_json
+     << ",\"in_bytes\":" << s.in_bytes << ",\"k_sub\":" << s.k_sub
      << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes
      << ",\"out_align_bytes\":" << p.out_align_bytes << "}";
   p.json = js.str();

@@ -12,6 +12,7 @@ struct gemm_plan_s {
   gemm_desc d;
   int kid = 0;
   int in_kind = 0, out_kind = 0;
+  int in_bytes = 2;          // bytes per A / B element (2: bf16 / f16, 4: binary32)
   int vec = 1;               // elements per global vector load of A and B
   int align_bytes = 2;       // required alignment of the A / B / W pointers
   int out_bytes = 4;         // bytes per C element

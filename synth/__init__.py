@@ -45,7 +45,7 @@ class Workload:
     M: int
     N: int
     K: int
-    in_kind: str                 # "bf16" or "f16"
+    in_kind: str                 # "bf16", "f16" or "f32"
     out_kind: str                # "f32" or "bf16"
     alpha: float
     beta: float
@@ -83,6 +83,10 @@ WORKLOADS = {
         "gate_up_swiglu", 4096, 11008, 4096, "bf16", "bf16", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (4001, 4002, 4003),
         gate_up=True, act="swiglu", notes="silu(x W_gate) * (x W_up), one bf16 output"),
+    "square4096_f32": Workload(
+        "square4096_f32", 4096, 4096, 4096, "f32", "f32", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0 / math.sqrt(4096)), Dist("normal", 0.0, 1.0 / math.sqrt(4096)),
+        (2101, 2102), notes="4096^3 GEMM, binary32 in and out"),
     "skinny": Workload(
         "skinny", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5001, 5002, 5003),

@@ -264,9 +264,16 @@ def test_invalid_requests_are_rejected():
         with pytest.raises(la.GemmError) as e:
             la.gemm_plan(**kw)
         assert e.value.name == "GEMM_ERR_INVALID_ARG"
-    with pytest.raises(la.GemmError) as e:
-        la.gemm_plan(4, 4, 4, la.F32, la.F32)
+    # binary32 inputs: plain GEMMs only, and never mixed with 16-bit inputs
+    with pytest.raises(la.GemmError, match="plain GEMMs only") as e:
+        la.gemm_plan(4, 4, 4, la.F32, la.F32, gate_up=True)
     assert e.value.name == "GEMM_ERR_UNSUPPORTED"
+    lib = la._lib
+    for a_t, b_t in ((la.BF16, la.F32), (la.F32, la.F16), (la.BF16, la.F16)):
+        d = lib._Desc(4, 4, 4, a_t, b_t, la.F32, 4, 4, 4, 0, 1, 16, 16, 16)
+        h = ctypes.c_void_p()
+        assert lib.load().gemm_plan(ctypes.byref(d), ctypes.byref(h)) == 3, (a_t, b_t)   # GEMM_ERR_UNSUPPORTED
+        assert not h.value
     # a grid of more than 2^32 work-items along x does not fit one launch (8,388,608 tiles of
     # 256 x 256 at 512 threads each is exactly 2^32); a tile row fewer plans
     with pytest.raises(la.GemmError, match="too many tiles") as e:
@@ -473,3 +480,64 @@ def test_prefetch_depth_follows_the_grid():
     assert depth(200, 300, 5)[2] == 1                                  # element loads
     assert depth(1000, 1537, 999, gate_up=True)[2] == 1                 # gate/up keeps one set
     assert depth(300, 300, 64, batch=12)[1:] == (300, 3)                # batch entries count as workgroups
+
+
+def _slots_256(offsets_words):
+    """16-byte slots (mod 256 bytes, i.e. of gfx950's 64 four-byte banks) that a set of 16-byte reads at
+    these word offsets touches."""
+    return {(o * 4 // 16) % 16 for o in offsets_words}
+
+
+def test_binary32_plan_maps_and_64_byte_rows():
+    """The binary32 kernel's A block: two sub-blocks of 16 values per M row, i.e. 64-byte rows of the
+    page's 64-byte fp32 plan, with the XOR taken from row bits 2-3 (Swizzle{2,2,4}) instead of 1-2
+    (the page's Swizzle{2,2,3}); every map checked element by element against the XOR written out."""
+    p = la.gemm_plan(1000, 1537, 999, la.F32, la.F32)
+    d = p.describe()
+    assert d["kernel"] == "tiled_f32_128x128x32" and d["in"] == "f32" and d["in_bytes"] == 4 and d["k_sub"] == 16
+    assert d["mfma"] == "32x32x2" and d["tile"] == [128, 128, 32] and d["stages"] == 2
+    assert d["lds_a"] == "(128,(16,2)):(16,(1,2048))" and d["swizzle_a"] == [2, 2, 4]
+    assert d["lds_b"] == "(32,128):(128,1)" and d["swizzle_b"] == [1, 5, 5]
+    assert d["lds_bytes"] == 2 * 8192 * 4 and la.gemm_plan_lds_stage_bytes(p) == 8192 * 4
+    assert (d["vec_elems"], d["align_bytes"]) == (1, 4)
+    for m in range(128):
+        for k in range(32):
+            want = 2048 * (k // 16) + 16 * m + ((k % 16) ^ (4 * ((m >> 2) & 3)))
+            assert la.gemm_plan_lds_offset(p, 0, m, k) == want
+    for k in range(32):
+        for n in range(128):
+            assert la.gemm_plan_lds_offset(p, 1, k, n) == 8192 // 2 + 128 * k + (n ^ (32 * ((k >> 3) & 1)))
+    # the page's 64-byte fp32 plan over the same 16 x 128 sub-block (inner axis 1 = K)
+    page = {(k, m): la.la_tile_plan_offset(4, (16, 128), 1, 64, (k, m))[0] for k in range(16) for m in range(128)}
+    assert all(page[(k, m)] == 16 * m + (k ^ (4 * ((m >> 1) & 3))) for (k, m) in page)
+    # 16-byte fragment reads of 16 consecutive rows at one K chunk: all 16 slots of the 256-byte
+    # bank window under the kernel's map, only 8 under the page's
+    for r0 in range(0, 128, 16):
+        for kc in range(0, 16, 4):
+            ours = [la.gemm_plan_lds_offset(p, 0, r0 + i, kc) for i in range(16)]
+            theirs = [page[(kc, r0 + i)] for i in range(16)]
+            assert len(_slots_256(ours)) == 16 and len(_slots_256(theirs)) == 8
+    # 4-byte reads of the N-contiguous B block: lanes 0-31 read row k, lanes 32-63 row k + 8, 32
+    # consecutive columns each: all 64 banks
+    for k in range(8):
+        for c0 in range(0, 128, 32):
+            offs = [la.gemm_plan_lds_offset(p, 1, k + 8 * (l // 32), c0 + l % 32) for l in range(64)]
+            assert len({o % 64 for o in offs}) == 64
+
+
+def test_binary32_storage_orders_and_staging_width():
+    def plan(m, n, k, **kw):
+        return la.gemm_plan(m, n, k, la.F32, la.F32, **kw).describe()
+    d = plan(4096, 4096, 4096)
+    assert (d["vec_elems"], d["align_bytes"], d["grid"]) == (4, 16, 1024)
+    assert d["copy"]["A"]["run_bytes"] == 128 and d["copy"]["B"]["run_bytes"] == 512
+    d = plan(300, 260, 200, a_transposed=True, b_kmajor=True)
+    assert d["a_order"] == "km" and d["b_order"] == "nk" and d["vec_elems"] == 4
+    assert d["lds_a"] == "(128,32):(1,128)" and d["swizzle_a"] == [1, 5, 5]
+    assert d["lds_b"] == "((16,2),128):((1,2048),16)" and d["swizzle_b"] == [2, 2, 4]
+    # a row stride that is not a multiple of 4 elements, or a contiguous extent cut by a chunk: 4-byte loads
+    assert plan(256, 256, 64, lda=66)["vec_elems"] == 1
+    assert plan(256, 256, 62)["vec_elems"] == 1
+    assert plan(256, 254, 64)["vec_elems"] == 1
+    assert plan(254, 256, 64, a_transposed=True)["vec_elems"] == 1
+    assert plan(254, 256, 64)["vec_elems"] == 4
