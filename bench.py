@@ -281,7 +281,7 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[w.in_kind],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    if roof["bound"] == "mfma" and w.flops() >= 1e11 and w.in_kind != "f32":
+    if roof["bound"] == "mfma" and w.flops() >= 1e11:
         roof["mfma_ceiling"] = mfma_ceiling(dev, A, flops, roof["achieved"])
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel_avg_ms"] = kern_ms
@@ -318,12 +318,13 @@ def main():
 
 def mfma_ceiling(dev, operands, flops, achieved):
     """The matrix-core rate the chip sustains at this workload's size: the library's probe issues
-    the same number of 32x32x16 MFMAs per SIMD as the workload (one wave per SIMD, 16 independent
+    the same number of MFMAs per SIMD as the workload (32x32x16 for 16-bit inputs, 32x32x2 for
+    binary32; one wave per SIMD, 16 independent
     chains, no memory traffic) on 16-byte fragments of the workload's own input values, then on
     zeros (the multipliers' power, and so the clock the chip settles to, depends on the bits).
     Context for roofline.frac, which stays relative to the nominal peak."""
     import layout_algebra_amd as la
-    per_mfma = 32 * 32 * 16 * 2
+    per_mfma = 32 * 32 * (2 if operands.dtype == torch.float32 else 16) * 2
     per_wave = max(16, int(round(flops / per_mfma / (256 * 4) / 16)) * 16)
     sink = torch.empty(256 * 256, dtype=torch.float32, device=dev)
     ops = operands.reshape(-1)[: 1 << 19]
@@ -331,7 +332,7 @@ def mfma_ceiling(dev, operands, flops, achieved):
     for name, src in (("tflops", ops), ("tflops_zero_operands", torch.zeros_like(ops))):
         ms, _, _, _ = timed_steps(lambda i: la.la_probe_mfma(src, sink, 256, per_wave), 10, 3, preroll_s=0.3)
         res[name] = 256 * 4 * per_wave * per_mfma / (ms * 1e-3) / 1e12
-    res["operands"] = "first %d KiB of the workload's first input" % (ops.numel() * 2 // 1024)
+    res["operands"] = "first %d KiB of the workload's first input" % (ops.numel() * ops.element_size() // 1024)
     res["mfma_per_wave"] = per_wave
     res["frac"] = achieved / res["tflops"]
     return res

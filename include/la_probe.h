@@ -23,7 +23,8 @@ extern "C" {
  * above.  Launches `workgroups` workgroups of 4 waves (one wave per SIMD of a
  * CU); every lane loads eight 16-byte operand fragments from `operands`
  * (fragment f at byte 16 * (f mod (operand_bytes / 16))) and issues
- * mfma_per_wave v_mfma_f32_32x32x16 instructions (bf16 or f16 per in_type) in
+ * mfma_per_wave v_mfma_f32_32x32x16 instructions (bf16 or f16 per in_type),
+ * or v_mfma_f32_32x32x2_f32 on the first word of each fragment (GEMM_F32), in
  * 16 independent accumulator chains, with no other memory traffic, then
  * writes the sum of its accumulators to sink[lane id] (workgroups * 256
  * floats, device memory).  Timed by the caller, it gives the rate the matrix

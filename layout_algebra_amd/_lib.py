@@ -330,17 +330,18 @@ def la_attention_run(Q, K, V, O, scale=None, stream=None):
 
 def la_probe_mfma(operands, sink, workgroups, mfma_per_wave, stream=None):
     """Matrix-core rate probe: `workgroups` x 4 waves, each issuing mfma_per_wave MFMAs on 16-byte fragments
-    taken from `operands` (a contiguous bf16/f16 tensor on the GPU, its dtype selects the instruction);
+    taken from `operands` (a contiguous bf16/f16/f32 tensor on the GPU, its dtype selects the instruction);
     `sink` is a float32 GPU tensor of at least workgroups * 256 elements."""
     torch = _torch()
-    if not isinstance(operands, torch.Tensor) or operands.device.type != "cuda" or operands.dtype not in (torch.bfloat16, torch.float16):
-        raise ValueError("operands must be a bf16/f16 tensor on the GPU")
+    if not isinstance(operands, torch.Tensor) or operands.device.type != "cuda" or \
+            operands.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError("operands must be a bf16/f16/f32 tensor on the GPU")
     if not operands.is_contiguous():
         raise ValueError("operands must be contiguous")
     if not isinstance(sink, torch.Tensor) or sink.device.type != "cuda" or sink.dtype != torch.float32 or \
             not sink.is_contiguous() or sink.numel() < int(workgroups) * 256:
         raise ValueError("sink must be a contiguous float32 GPU tensor of at least workgroups * 256 elements")
-    nbytes = (operands.numel() * 2) // 16 * 16
+    nbytes = (operands.numel() * operands.element_size()) // 16 * 16
     _check(load().la_probe_mfma(ctypes.c_void_p(operands.data_ptr()), int(nbytes), ctypes.c_void_p(sink.data_ptr()),
                                 int(workgroups), int(mfma_per_wave), _KIND[operands.dtype], _stream_ptr(stream)))
 

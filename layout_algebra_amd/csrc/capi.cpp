@@ -231,7 +231,8 @@ gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type
 
 gemm_status la_probe_mfma(const void* operands, int64_t operand_bytes, float* sink, int64_t workgroups,
                           int64_t mfma_per_wave, int32_t in_type, void* stream) {
-  if (in_type != GEMM_BF16 && in_type != GEMM_F16) return set_err(GEMM_ERR_INVALID_ARG, "in_type must be GEMM_BF16 or GEMM_F16");
+  if (in_type != GEMM_BF16 && in_type != GEMM_F16 && in_type != GEMM_F32)
+    return set_err(GEMM_ERR_INVALID_ARG, "in_type must be GEMM_BF16, GEMM_F16 or GEMM_F32");
   if (operand_bytes < 16 || operand_bytes % 16) return set_err(GEMM_ERR_INVALID_ARG, "operand_bytes must be a positive multiple of 16");
   if (workgroups < 1 || workgroups > (int64_t{1} << 20)) return set_err(GEMM_ERR_INVALID_ARG, "workgroups must be in 1..2^20");
   if (mfma_per_wave < 16 || mfma_per_wave % 16 || mfma_per_wave > (int64_t{1} << 24))
@@ -239,7 +240,8 @@ gemm_status la_probe_mfma(const void* operands, int64_t operand_bytes, float* si
   if (!operands || !sink) return set_err(GEMM_ERR_NULL, "operands and sink must not be NULL");
   if (!aligned(operands, 16) || !aligned(sink, 4)) return set_err(GEMM_ERR_ALIGNMENT, "operands must be 16-byte aligned, sink 4-byte aligned");
   const hipError_t e = lak::launch_mfma_probe(operands, operand_bytes / 16, sink, workgroups, mfma_per_wave,
-                                              in_type == GEMM_BF16 ? lak::IN_BF16 : lak::IN_F16, static_cast<hipStream_t>(stream));
+                                              in_type == GEMM_BF16 ? lak::IN_BF16 : in_type == GEMM_F16 ? lak::IN_F16 : lak::IN_F32,
+                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GEMM_OK;
 }

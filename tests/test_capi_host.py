@@ -439,7 +439,7 @@ def test_mfma_probe_argument_errors_are_caught_before_launch():
     def call(ops=0x1000000, nbytes=1 << 20, sink=0x2000000, wg=256, n=4096, t=la.BF16):
         return st[lib.la_probe_mfma(vp(ops), nbytes, vp(sink), wg, n, t, vp(0))]
 
-    assert call(t=la.F32) == "GEMM_ERR_INVALID_ARG"
+    assert call(t=3) == "GEMM_ERR_INVALID_ARG" and call(t=-1) == "GEMM_ERR_INVALID_ARG"
     assert call(nbytes=0) == "GEMM_ERR_INVALID_ARG"
     assert call(nbytes=24) == "GEMM_ERR_INVALID_ARG"
     assert call(wg=0) == "GEMM_ERR_INVALID_ARG"
