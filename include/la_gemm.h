@@ -74,9 +74,10 @@ typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
                                     lda >= max(1, m) -- a layout is a function and either major order
                                     is the same matrix (Tylo.jl "Layouts, storage and ownership",
                                     section "A layout is a function": permutedims swaps the modes).
-                                    Not combined with GEMM_FLAG_B_KMAJOR; needs m to be a multiple of
-                                    8 or larger than 8 (16-byte staging along M); never the skinny
-                                    kernel.  Otherwise rejected with GEMM_ERR_UNSUPPORTED */
+                                    With 16-bit inputs: not combined with GEMM_FLAG_B_KMAJOR, and m
+                                    a multiple of 8 or larger than 8 (16-byte staging along M); never
+                                    the skinny kernel.  Otherwise rejected with GEMM_ERR_UNSUPPORTED.
+                                    Binary32 inputs take every combination */
 #define GEMM_FLAG_LARGE_TILES 0x4u  /* keep the largest tile the shape allows.  Without it the
                                     planner moves a GEMM whose grid would leave most of the 256
                                     CUs idle to 64 x 64 tiles (fewer than 32 workgroups of the
@@ -87,7 +88,12 @@ typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
 
 typedef struct {
   int64_t m, n, k;             /* problem sizes, each >= 0 */
-  int32_t a_type, b_type;      /* gemm_dtype; equal, BF16 or F16 */
+  int32_t a_type, b_type;      /* gemm_dtype; equal: BF16, F16, or F32 (binary32 inputs: plain GEMMs
+                                  and row reductions only, any shape and storage order, staged
+                                  through 64-byte rows of 16 values -- the 64-byte fp32 plan of the
+                                  Tylo.jl page "TMA and Hopper WGMMA", section "The same storage
+                                  contract on both sides" -- and multiplied on the FP32 matrix cores;
+                                  gate/up plans and mixed widths are GEMM_ERR_UNSUPPORTED) */
   int32_t c_type;              /* gemm_dtype of C (and of G, U): F32, BF16 or F16 */
   int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k) (max(1,m) for A stored [K,M]),
                                   ldb >= max(1,n) (max(1,k) for K-major B), ldc >= max(1,n) */
@@ -102,7 +108,7 @@ typedef struct {
                                   not: stride_c >= (m-1)*ldc + n (blocks), or stride_c >= n and
                                   ldc >= (batch-1)*stride_c + n (interleaved rows).  They join
                                   lda/ldb/ldc in the alignment class (16-byte vectors need
-                                  multiples of 8) */
+                                  multiples of 8 elements, 4 for binary32) */
 } gemm_desc;
 
 typedef struct gemm_plan_s* gemm_plan_t;   /* opaque, immutable, host-only */
