@@ -108,7 +108,7 @@ def measured_traffic(workload):
 
 def algorithmic_bytes(w):
     """Compulsory HBM bytes of one step: every operand read once, C written (and read if beta != 0)."""
-    eb = 2
+    eb = 4 if w.in_kind == "f32" else 2
     ob = 4 if w.out_kind == "f32" else 2
     nb = 2 if w.gate_up else 1
     nout = 1 if w.act == "swiglu" else nb

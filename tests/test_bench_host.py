@@ -30,6 +30,7 @@ def test_algorithmic_bytes():
     # every operand read once, C written (and read when beta != 0)
     assert bench.algorithmic_bytes(synth.WORKLOADS["skinny"]) == 2 * 16 * 8192 + 2 * 8192 * 28672 + 4 * 16 * 28672 == 471_859_200
     assert bench.algorithmic_bytes(synth.WORKLOADS["square4096"]) == 3 * 2 * 4096 * 4096
+    assert bench.algorithmic_bytes(synth.WORKLOADS["square4096_f32"]) == 3 * 4 * 4096 * 4096
     assert bench.algorithmic_bytes(synth.WORKLOADS["ragged"]) == 2 * (1000 * 999 + 999 * 1537) + 2 * 4 * 1000 * 1537
     assert bench.algorithmic_bytes(synth.WORKLOADS["gate_up"]) == 2 * 4096 * 4096 + 2 * 2 * 4096 * 11008 + 2 * 2 * 4096 * 11008
     assert bench.algorithmic_bytes(synth.WORKLOADS["gate_up_swiglu"]) == 2 * 4096 * 4096 + 2 * 2 * 4096 * 11008 + 2 * 4096 * 11008
