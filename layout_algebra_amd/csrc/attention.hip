@@ -10,7 +10,18 @@
 //    whole key loop (global -> registers once).
 //  * Key and value tiles of 64 rows are staged global -> LDS with direct loads
 //    (global_load_lds_dwordx4, 1 KB per wave instruction, swizzle applied on
-//    the source side as in the GEMM), two stages, one barrier per tile.
+//    the source side as in the GEMM), each in a ring of two slots, one barrier
+//    per tile.
+//  * Software pipeline across key tiles: while tile t's probabilities are
+//    formed (vector ALU), the scores of tile t+1 run on the matrix cores, and
+//    tile t+1's maximum is taken after tile t's product with V.  K(t+1) and
+//    V(t) are resident together, so K and V have rings of their own: after the
+//    barrier that opens tile t, V(t+1) goes into the slot V(t-1) left and
+//    K(t+2) into the slot K(t) left (both read completely before that
+//    barrier).  The arithmetic and its order are those of the plain loop
+//    (scores, lazy reference update, probabilities, sum, product per tile), so
+//    the result is the same bit for bit; the overlap took the 4096-key
+//    workload from 570-605 to 490-530 us on the boxes measured.
 //  * Scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16): in the
 //    32x32 result layout a lane holds 16 keys of ONE query, so the row maximum
 //    and sum are in-lane reductions plus one swap with the other half-wave,
@@ -37,6 +48,8 @@
 // LDS bank conflicts: K tiles use Swizzle{4,3,4} (D = 128) / {3,3,4} (D = 64)
 // for 16-byte fragment reads of 16 consecutive keys; V tiles use
 // Swizzle{2,5,2} for the transposing reads of 4 keys x 16 columns.
+#include <type_traits>
+
 #include "attention.hpp"
 #include "kernel_common.hpp"
 
@@ -146,14 +159,12 @@ __device__ __forceinline__ void store4<OutF16>(void* O, int64_t off, float a, fl
 template <class TI, class TO, int D>
 __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a) {
   using Cfg = AttnCfg<D>;
-  constexpr int KE = BC * D;                   // elements of one K (or V) tile
-  constexpr int STAGE = 2 * KE;
-  constexpr int CHUNKS = KE / 512 / NW;        // 1 KB direct loads per wave per tile and operand
-  constexpr int DS = D / 16;                   // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;                   // 32-row blocks of O^T
-  static_assert(CHUNKS * 512 * NW == KE, "tile must split into whole KB per wave");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[2 * STAGE];
-  AT_LDS uint16_t* lds = (AT_LDS uint16_t*)lds_raw;
+  constexpr int KE = BC * D;
+  constexpr int CHUNKS = KE / 512 / NW;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[4 * KE];
+  AT_LDS uint16_t* lds = (AT_LDS uint16_t*)lds_raw;      // K slots 0, 1, then V slots 0, 1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,8 +177,6 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
   const uint16_t* Kz = a.K + z * a.bk;
   const uint16_t* Vz = a.V + z * a.bv;
 
-  // Q^T fragments of this wave's 32 queries: lane (c, h) holds query q0 + c,
-  // head-dimension elements 16 s + 8 h .. + 7 for every k-step s.
   u32x4 qf[DS];
   {
     const int64_t q = q0 + c;
@@ -175,12 +184,6 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     for (int s = 0; s < DS; ++s)
       qf[s] = q < a.sq ? *reinterpret_cast<const u32x4*>(Qz + q * a.ldq + 16 * s + 8 * h) : u32x4{0u, 0u, 0u, 0u};
   }
-
-  // Direct loads: the lane that fills physical element P of a tile fetches
-  // logical element Sw(P) = key * D + d.  A full tile uses the byte offsets
-  // computed here once; the last tile, when partial, recomputes them with rows
-  // past the end clamped to the last key / value row.  Offsets stay 32-bit:
-  // the host guarantees 128 * ld < 2^32.
   uint32_t ofk[CHUNKS], ofv[CHUNKS];
 #pragma unroll
   for (int i = 0; i < CHUNKS; ++i) {
@@ -190,43 +193,28 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
     ofk[i] = uint32_t(Lk / D) * uint32_t(a.ldk) * 2u + uint32_t(Lk % D) * 2u;
     ofv[i] = uint32_t(Lv / D) * uint32_t(a.ldv) * 2u + uint32_t(Lv % D) * 2u;
   }
-  auto issue = [&](int t, int st) {
+  // one operand tile (K: kv = 0, V: kv = 1) of key tile t into its slot
+  auto issue1 = [&](int kv, int t, int slot) {
     const int64_t kbase = int64_t(t) * BC;
-    const uint16_t* kb = Kz + kbase * a.ldk;
-    const uint16_t* vb = Vz + kbase * a.ldv;
-    AT_LDS uint16_t* dst = lds + st * STAGE + wave * CHUNKS * 512;
+    const int64_t ld = kv ? a.ldv : a.ldk;
+    const uint16_t* src = (kv ? Vz : Kz) + kbase * ld;
+    AT_LDS uint16_t* dst = lds + (2 * kv + slot) * KE + wave * CHUNKS * 512;
     if (kbase + BC <= a.sk) {
 #pragma unroll
-      for (int i = 0; i < CHUNKS; ++i) dma16(kb, ofk[i], lds_address(dst + i * 512));
-#pragma unroll
-      for (int i = 0; i < CHUNKS; ++i) dma16(vb, ofv[i], lds_address(dst + KE + i * 512));
+      for (int i = 0; i < CHUNKS; ++i) dma16(src, kv ? ofv[i] : ofk[i], lds_address(dst + i * 512));
       return;
     }
-    const int last = int(a.sk - 1 - kbase);     // rows past the end repeat the last key / value
-    const uint32_t ldk2 = uint32_t(a.ldk) * 2u, ldv2 = uint32_t(a.ldv) * 2u;
+    const int last = int(a.sk - 1 - kbase);
+    const uint32_t ld2 = uint32_t(ld) * 2u;
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
       const int P = (wave * CHUNKS + i) * 512 + lane * 8;
-      const int Lk = swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
-      const int rk = Lk / D < last ? Lk / D : last;
-      dma16(kb, uint32_t(rk) * ldk2 + uint32_t(Lk % D) * 2u, lds_address(dst + i * 512));
-    }
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int P = (wave * CHUNKS + i) * 512 + lane * 8;
-      const int Lv = swz<Cfg::VB, Cfg::VM, Cfg::VS>(P);
-      const int rv = Lv / D < last ? Lv / D : last;
-      dma16(vb, uint32_t(rv) * ldv2 + uint32_t(Lv % D) * 2u, lds_address(dst + KE + i * 512));
+      const int L = kv ? swz<Cfg::VB, Cfg::VM, Cfg::VS>(P) : swz<Cfg::KB, Cfg::KM, Cfg::KS>(P);
+      const int r = L / D < last ? L / D : last;
+      dma16(src, uint32_t(r) * ld2 + uint32_t(L % D) * 2u, lds_address(dst + i * 512));
     }
   };
 
-  // LDS fragment addresses (bytes within a tile).  The XOR swizzles of both
-  // tiles take their source bits from the key row and only flip bits that
-  // the k-step (K tile) or the 32-column block (V tile) occupies, so
-  //   K: Sw(row D + 16 s + 8 h) = Sw(row D + 8 h) ^ (16 s),  row = 32 kb + c
-  //   V: Sw(key D + 32 b + x)   = Sw(key0 D + x) ^ (32 b) + (key - key0) D
-  // with key0 = 4 h + e the lane's first key: one base per lane and operand,
-  // the rest is an XOR and an immediate offset per read.
   const uint32_t kaddr0 = uint32_t(swz<Cfg::KB, Cfg::KM, Cfg::KS>(c * D + 8 * h)) * 2u;
   const int e4 = (lane >> 2) & 3;
   const uint32_t vaddr0 = uint32_t(swz<Cfg::VB, Cfg::VM, Cfg::VS>((4 * h + e4) * D + 16 * ((lane >> 4) & 1) + 4 * (lane & 3))) * 2u;
@@ -236,65 +224,50 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
   for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
   float m = -__builtin_inff(), l = 0.0f;
 
-  const int nt = int((a.sk + BC - 1) / BC);
-  issue(0, 0);
-  for (int t = 0; t < nt; ++t) {
-    barrier_after_loads();                     // tile t is in LDS; every wave is done with tile t - 1
-    if (t + 1 < nt) issue(t + 1, (t + 1) & 1);
-    const AT_LDS uint16_t* ks = lds + (t & 1) * STAGE;
-    const AT_LDS uint16_t* vs = ks + KE;
-    const AT_LDS char* ksb = reinterpret_cast<const AT_LDS char*>(ks);
-    const AT_LDS char* vsb = reinterpret_cast<const AT_LDS char*>(vs);
-    uint32_t ka = kaddr0, va = vaddr0;
-    asm volatile("" : "+v"(ka), "+v"(va));     // per-read addresses are formed here, not kept live
-
-    // S^T = K Q^T: two 32-key blocks x 32 queries.  All K fragments of the tile
-    // are requested before the first MFMA, so LDS latency is paid once per tile.
+  // S^T = K Q^T of the tile in K slot `slot`
+  auto scores = [&](int slot, f32x16 (&s)[2]) {
+    const AT_LDS char* ksb = reinterpret_cast<const AT_LDS char*>(lds + slot * KE);
+    uint32_t ka = kaddr0;
+    asm volatile("" : "+v"(ka));
     u32x4 kf[DS][2];
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
+    for (int st = 0; st < DS; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        kf[s][kb] = *reinterpret_cast<const AT_LDS u32x4*>(ksb + (ka ^ uint32_t(32 * s)) + kb * 32 * D * 2);
-    __builtin_amdgcn_sched_barrier(0);         // keep the reads ahead of the MFMAs (the scheduler would sink them)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        kf[st][kb] = *reinterpret_cast<const AT_LDS u32x4*>(ksb + (ka ^ uint32_t(32 * st)) + kb * 32 * D * 2);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
+    for (int st = 0; st < DS; ++st)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_32x32x16<TI>(kf[s][kb], qf[s], sacc[kb]);
-    }
-
-    // Online softmax for query c: register r of block kb is key
-    // kb * 32 + 8 (r / 4) + 4 h + r % 4 of this tile; the other half-wave holds the rest.
-    // Scores stay raw; with c = scale * log2(e) >= 0, max(c s) = c max(s) and
-    // p = exp2(c s - m) is one fused multiply-add and one exp2 per score.
-    // Keys past the end (only in the last tile) score -inf: they drop out of the
-    // maximum and exp2(k * -inf - m) = 0 (k > 0; a zero scale is passed as the
-    // smallest normal float, which leaves every valid probability at exactly 1).
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_32x32x16<TI>(kf[st][kb], qf[st], s[kb]);
+  };
+  // keys past the end of tile t score -inf
+  auto mask = [&](int t, f32x16 (&s)[2]) {
     const int64_t remaining = a.sk - int64_t(t) * BC;
     if (remaining < BC) {
-      asm volatile("" ::: "memory");           // a real branch: full tiles skip the selects below
+      asm volatile("" ::: "memory");
       const int rem = int(remaining);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= rem) sacc[kb][r] = -__builtin_inff();
+          if (kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= rem) s[kb][r] = -__builtin_inff();
     }
+  };
+  auto tile_max = [&](const f32x16 (&s)[2]) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = halves_max(mx);
-    // Lazy reference maximum (log2 units): it moves only when the tile's maximum
-    // exceeds it by more than 8, so probabilities stay <= 2^8 and the rescaling
-    // of the accumulator and the running sum is skipped for most tiles; the
-    // quotient acc / l does not depend on the reference.
-    const float m_tile = mx * a.scale_log2;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return halves_max(mx) * a.scale_log2;
+  };
+  // lazy reference maximum: rescale acc and l only when the tile's maximum exceeds m by more than 8
+  auto update_ref = [&](float m_tile) {
     if (__any(m_tile > m + 8.0f)) {
       const float m_new = m_tile > m + 8.0f ? m_tile : m;
-      const float corr = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile (m = -inf)
+      const float corr = __builtin_amdgcn_exp2f(m - m_new);
       l *= corr;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
@@ -302,45 +275,97 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
         for (int r = 0; r < 16; ++r) acc[b][r] *= corr;
       m = m_new;
     }
+  };
+  // probabilities of one 32-key block, packed as the MFMA operands of two 16-key steps; returns their sum
+  auto probs = [&](f32x16& sb, u32x4& p0, u32x4& p1) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -m));
-    // P^T as MFMA B operands (16-key step u: score registers 8 (u % 2) .. + 7 of
-    // block u / 2), rounded to the input type; the running sum adds the same
-    // rounded values, two per dot-product instruction, so numerator and
-    // denominator see identical weights.
-    u32x4 pf[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f32x16& sp = sacc[u >> 1];
-      const int rr = (u & 1) * 8;
-      pf[u] = u32x4{pack2<TI>(sp[rr + 0], sp[rr + 1]), pack2<TI>(sp[rr + 2], sp[rr + 3]),
-                    pack2<TI>(sp[rr + 4], sp[rr + 5]), pack2<TI>(sp[rr + 6], sp[rr + 7])};
-    }
+    for (int r = 0; r < 16; ++r) sb[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r], a.scale_log2, -m));
+    p0 = u32x4{pack2<TI>(sb[0], sb[1]), pack2<TI>(sb[2], sb[3]), pack2<TI>(sb[4], sb[5]), pack2<TI>(sb[6], sb[7])};
+    p1 = u32x4{pack2<TI>(sb[8], sb[9]), pack2<TI>(sb[10], sb[11]), pack2<TI>(sb[12], sb[13]), pack2<TI>(sb[14], sb[15])};
     float sum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int w2 = 0; w2 < 4; ++w2) sum = dot2_ones<TI>(p0[w2], sum);
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) sum = dot2_ones<TI>(pf[u][w2], sum);
-    l += halves_sum(sum);
-
-    // O^T += V^T P^T over four 16-key steps; slot e of the lane's 8 k values is
-    // key 16 u + 8 (e / 4) + 4 h + e % 4, the order of the score registers.
+    for (int w2 = 0; w2 < 4; ++w2) sum = dot2_ones<TI>(p1[w2], sum);
+    return sum;
+  };
+  // O^T += V^T P^T over the 16-key steps u0, u0 + 1 of the tile in V slot `slot`
+  auto pv = [&](int slot, int u0, const u32x4& p0, const u32x4& p1) {
+    const AT_LDS char* vsb = reinterpret_cast<const AT_LDS char*>(lds + (2 + slot) * KE);
+    uint32_t va = vaddr0;
+    asm volatile("" : "+v"(va));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int du = 0; du < 2; ++du) {
+      const int u = u0 + du;
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         const AT_LDS char* vp = vsb + (va ^ uint32_t(64 * b)) + 16 * u * D * 2;
         const i16x4_a lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AT_LDS i16x4_a*)(vp));
         const i16x4_a hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AT_LDS i16x4_a*)(vp + 8 * D * 2));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        acc[b] = mfma_32x32x16<TI>(u32x4{l2.x, l2.y, h2.x, h2.y}, pf[u], acc[b]);
+        acc[b] = mfma_32x32x16<TI>(u32x4{l2.x, l2.y, h2.x, h2.y}, du ? p1 : p0, acc[b]);
       }
     }
+  };
+
+  // prologue: K(0), V(0), K(1) in flight; wait for K(0) only, then tile 0's scores and reference
+  const int nt = int((a.sk + BC - 1) / BC);
+  issue1(0, 0, 0);
+  issue1(1, 0, 0);
+  if (nt > 1) {
+    issue1(0, 1, 1);
+    __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | ((2 * CHUNKS) & 0xF) | (((2 * CHUNKS) >> 4) << 14));  // K(0) landed
+  } else {
+    __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (CHUNKS & 0xF) | ((CHUNKS >> 4) << 14));
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  f32x16 sA[2], sB[2];
+  scores(0, sA);
+  mask(0, sA);
+  update_ref(tile_max(sA));
+
+  // One key tile t: s holds its scores (reference already updated); with a next tile, sn receives
+  // tile t+1's scores, computed while tile t's first half of probabilities is formed.  Whether a
+  // next tile exists is a compile-time property of each call (the last tile is peeled), so the
+  // scores and the probabilities sit in one basic block, where the compiler interleaves them.
+  auto step = [&](int t, f32x16 (&s)[2], f32x16 (&sn)[2], auto has_next) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    barrier_after_loads();                    // V(t) and K(t+1) in LDS; tile t-1 and S(t) fully read
+    if constexpr (NEXT) {
+      issue1(1, t + 1, (t + 1) & 1);
+      if (t + 2 < nt) issue1(0, t + 2, t & 1);
+    }
+    u32x4 p0, p1, p2, p3;
+    float sum;
+    if constexpr (NEXT) scores((t + 1) & 1, sn);
+    sum = probs(s[0], p0, p1);
+    pv(t & 1, 0, p0, p1);
+    sum = sum + probs(s[1], p2, p3);
+    l += halves_sum(sum);
+    pv(t & 1, 2, p2, p3);
+    if constexpr (NEXT) {
+      mask(t + 1, sn);
+      update_ref(tile_max(sn));
+    }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  // unrolled by two so that the score registers of tiles t and t+1 trade roles without copies
+  int t = 0;
+  for (; t + 2 < nt; t += 2) {
+    step(t, sA, sB, yes{});
+    step(t + 1, sB, sA, yes{});
+  }
+  if (t + 1 < nt) {
+    step(t, sA, sB, yes{});
+    step(t + 1, sB, sA, no{});
+  } else {
+    step(t, sA, sB, no{});
   }
 
-  // O[q, d] = acc / l: register r of block b is d = 32 b + 8 (r / 4) + 4 h + r % 4.
   const int64_t q = q0 + c;
   if (q < a.sq) {
     const float inv = 1.0f / l;
@@ -355,6 +380,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(const AttnArgs a)
       }
   }
 }
+
 
 template <class TI, class TO, int D>
 hipError_t go(const AttnArgs& a, hipStream_t s) {
