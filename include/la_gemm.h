@@ -81,10 +81,12 @@ typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
 #define GEMM_FLAG_LARGE_TILES 0x4u  /* keep the largest tile the shape allows.  Without it the
                                     planner moves a GEMM whose grid would leave most of the 256
                                     CUs idle to 64 x 64 tiles (fewer than 32 workgroups of the
-                                    256-wide full-tile kernels; for the general kernel, always
-                                    with 16-byte loads and below 384 workgroups of 128 x 128 with
-                                    2-byte loads).  For callers that run many small GEMMs on
-                                    concurrent streams, where one GEMM need not fill the chip. */
+                                    256-wide full-tile kernels, 64 when M or N ends inside a tile;
+                                    for the general kernel, always with 16-byte loads and below
+                                    384 workgroups of 128 x 128 with 2-byte loads), and keeps
+                                    shapes whose 256-wide tiles would pad M x N by more than 1.3x
+                                    on the general kernel.  For callers that run many small GEMMs
+                                    on concurrent streams, where one GEMM need not fill the chip. */
 
 typedef struct {
   int64_t m, n, k;             /* problem sizes, each >= 0 */

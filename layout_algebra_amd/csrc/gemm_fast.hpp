@@ -1,5 +1,6 @@
-// Fast tiled GEMM for gfx950: full tiles only (M % BM == 0, N % BN == 0,
-// K % BK == 0, 16-byte aligned rows).
+// Fast tiled GEMM for gfx950: K % BK == 0 and 16-byte aligned rows; M and N
+// may end inside a tile (edge tiles load clamped source rows and columns and
+// store only inside C, see Fast::a_limit and store_band).
 //
 // Differences from the general kernel (gemm_tiled.hip):
 //  * Operands go global -> LDS directly (global_load_lds_dwordx4): each wave
@@ -97,18 +98,35 @@ struct Fast {
     uint32_t b[B_LOADS];
   };
 
-  static __device__ __forceinline__ void make_src(Src& s, int wave, int lane, int64_t lda, int64_t ldb) {
+  // Source limits of a tile at (m0, n0) that may cross M or N (K is a multiple
+  // of BK): the last row of A (A stored [K, M]: the last 8-element chunk along
+  // M) and the last 8-element chunk of a B row (B stored [N, K]: the last row)
+  // a lane may read.  Elements past the edge are loaded from the clamped
+  // position instead: they only ever meet rows or columns of C that are not
+  // stored (C[i, j] depends on row i of A and column j of B alone), and every
+  // address stays inside the operand.
+  static __device__ __forceinline__ int a_limit(int64_t M, int64_t m0) {
+    const int64_t left = M - m0;                       // >= 1
+    return ATR ? int(min<int64_t>(BM, (left + 7) & ~int64_t(7)) - 8) : int(min<int64_t>(BM, left) - 1);
+  }
+  static __device__ __forceinline__ int b_limit(int64_t N, int64_t n0) {
+    const int64_t left = N - n0;                       // >= 1
+    return BKM ? int(min<int64_t>(BN, left) - 1) : int(min<int64_t>(BN, (left + 7) & ~int64_t(7)) - 8);
+  }
+
+  static __device__ __forceinline__ void make_src(Src& s, int wave, int lane, int64_t lda, int64_t ldb, int a_lim,
+                                                  int b_lim) {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int P = (wave * A_LOADS + i) * 512 + lane * 8;     // physical element this lane fills
       const int L = swz<C::AB, C::AM, C::AS>(P);               // logical element it must hold
-      s.a[i] = ATR ? uint32_t((L / BM) * lda + (L % BM)) : uint32_t((L / BK) * lda + (L % BK));
+      s.a[i] = ATR ? uint32_t((L / BM) * lda + min(L % BM, a_lim)) : uint32_t(min(L / BK, a_lim) * lda + (L % BK));
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int P = (wave * B_LOADS + i) * 512 + lane * 8;
       const int L = swz<C::BB, C::BMb, C::BS>(P);
-      s.b[i] = BKM ? uint32_t((L / BK) * ldb + (L % BK)) : uint32_t((L / BN) * ldb + (L % BN));
+      s.b[i] = BKM ? uint32_t(min(L / BK, b_lim) * ldb + (L % BK)) : uint32_t((L / BN) * ldb + min(L % BN, b_lim));
     }
   }
 
@@ -242,10 +260,12 @@ __device__ __forceinline__ void block_barrier() {
 // 108.1 -> 106.7 us, gate/up 607.9 -> 592.6 us measured).
 // RED: also fold the row reduction `red` of the FP32 values into R (a separate
 // instantiation, so that launches without it run exactly the plain epilogue).
+// Rows from M on and columns from N on are not written (C_old is not read
+// there either); a row segment of 8 cut by N is written element by element.
 template <class TO, class F, bool RED = false>
-__device__ __forceinline__ void store_band(const f32x16 (&accb)[F::FN], void* Cv, int64_t ldc, float alpha, float beta,
-                                           bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane,
-                                           int red = RED_NONE, float* R = nullptr) {
+__device__ __forceinline__ void store_band(const f32x16 (&accb)[F::FN], void* Cv, int64_t ldc, int64_t M, int64_t N,
+                                           float alpha, float beta, bool use_beta, int64_t row0, int64_t col0,
+                                           LAK_LDS float* win, int lane, int red = RED_NONE, float* R = nullptr) {
   constexpr int TN = F::TN;
   constexpr int PITCH = TN + 8;                      // floats: rows r and r+4 land 32 banks apart
   typedef typename TO::storage St;
@@ -266,48 +286,70 @@ __device__ __forceinline__ void store_band(const f32x16 (&accb)[F::FN], void* Cv
     const f32x4 lo = *reinterpret_cast<const LAK_LDS f32x4*>(src);
     const f32x4 hi = *reinterpret_cast<const LAK_LDS f32x4*>(src + 4);
     float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    St* dst = C + (row0 + r) * ldc + col0 + c;
+    const int64_t row = row0 + r;
+    const int64_t nleft = N - (col0 + c);              // valid columns from this chunk on
+    if (row >= M || nleft <= 0) continue;
+    St* dst = C + row * ldc + col0 + c;
+    const bool whole = nleft >= 8;
     if (use_beta) {
-      if constexpr (sizeof(St) == 4) {
-        const f32x4 o0 = *reinterpret_cast<const f32x4*>(dst);
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(dst + 4);
-        const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      if (whole) {
+        if constexpr (sizeof(St) == 4) {
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(dst);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(dst + 4);
+          const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += beta * o[e];
+          for (int e = 0; e < 8; ++e) v[e] += beta * o[e];
+        } else {
+          const u32x4 ow = *reinterpret_cast<const u32x4*>(dst);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+        }
       } else {
-        const u32x4 ow = *reinterpret_cast<const u32x4*>(dst);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += beta * from_out<TO>(static_cast<St>((ow[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+        for (int e = 0; e < 8; ++e)
+          if (e < nleft) v[e] += beta * from_out<TO>(dst[e]);
       }
     }
     if constexpr (RED) {
-      // row reduction: the lane's 8 values, then the CH lanes sharing row r
+      // row reduction: the lane's valid values, then the CH lanes sharing row r (a lane whose
+      // chunk lies past N has left the loop; the reduction runs over the lanes still active)
       float p = v[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) p = red_combine(red, p, v[e]);
-      p = red_lanes<CH>(red, p);
-      if (lane % CH == 0) red_commit(red, R + row0 + r, p);
+      for (int e = 1; e < 8; ++e)
+        if (e < nleft) p = red_combine(red, p, v[e]);
+      if (whole && N - col0 >= F::TN && M - row0 >= 32) {
+        p = red_lanes<CH>(red, p);
+        if (lane % CH == 0) red_commit(red, R + row, p);
+      } else {
+        red_commit(red, R + row, p);
+      }
     }
-    if constexpr (sizeof(St) == 4) {
-      __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
-      __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(dst + 4));
-    } else {
-      u32x4 w;
+    if (whole) {
+      if constexpr (sizeof(St) == 4) {
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(dst + 4));
+      } else {
+        u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = uint32_t(to_out<TO>(v[2 * e])) | (uint32_t(to_out<TO>(v[2 * e + 1])) << 16);
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
+        for (int e = 0; e < 4; ++e) w[e] = uint32_t(to_out<TO>(v[2 * e])) | (uint32_t(to_out<TO>(v[2 * e + 1])) << 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < nleft) dst[e] = to_out<TO>(v[e]);
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);                // reads done before the next band overwrites the window
 }
 
 template <class TO, class F, bool RED = false>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, float alpha, float beta,
-                                           bool use_beta, int64_t row0, int64_t col0, LAK_LDS float* win, int lane,
-                                           int red = RED_NONE, float* R = nullptr) {
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[F::FM][F::FN], void* Cv, int64_t ldc, int64_t M, int64_t N,
+                                           float alpha, float beta, bool use_beta, int64_t row0, int64_t col0,
+                                           LAK_LDS float* win, int lane, int red = RED_NONE, float* R = nullptr) {
 #pragma unroll
   for (int i = 0; i < F::FM; ++i)
-    store_band<TO, F, RED>(acc[i], Cv, ldc, alpha, beta, use_beta, row0 + i * 32, col0, win, lane, red, R);
+    store_band<TO, F, RED>(acc[i], Cv, ldc, M, N, alpha, beta, use_beta, row0 + i * 32, col0, win, lane, red, R);
 }
 
 // SwiGLU epilogue of waves split by weight (see epilogue): wave of weight TW (0: W_gate, 1: W_up)
@@ -343,7 +385,7 @@ __device__ __forceinline__ void swiglu_exchange(f32x16 (&acc)[F::NBW][F::FM][F::
         for (int e = 0; e < 4; ++e)   // gate first: the wave's own value for TW == 0, the partner's otherwise
           h[j][4 * q + e] = TW == 0 ? swiglu(m[4 * q + e], ov[e]) : swiglu(ov[e], m[4 * q + e]);
       }
-    store_band<TO, F>(h, g.C, g.ldc, 1.0f, 0.0f, false, row0 + own_band * 32, col0, xwin, lane);
+    store_band<TO, F>(h, g.C, g.ldc, g.M, g.N, 1.0f, 0.0f, false, row0 + own_band * 32, col0, xwin, lane);
     block_barrier();                                 // every wave has read its half before the next band is given
   }
 }
@@ -361,7 +403,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[F::NBW][F::FM][F::FN], co
     const int tw = wn / F::WNW;
     const int64_t col0 = n0 + (wn % F::WNW) * F::TN;
     if (g.act == 0) {
-      store_tile<TO, F>(acc[0], tw == 0 ? g.C : g.C2, g.ldc, 1.0f, 0.0f, false, row0, col0, win, lane);
+      store_tile<TO, F>(acc[0], tw == 0 ? g.C : g.C2, g.ldc, g.M, g.N, 1.0f, 0.0f, false, row0, col0, win, lane);
       return;
     }
     // SwiGLU: silu(g) * u needs the W_gate and W_up accumulators of an element together, and they
@@ -393,13 +435,13 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[F::NBW][F::FM][F::FN], co
           for (int j = 0; j < F::FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[0][i][j][e] = swiglu(acc[0][i][j][e], acc[1][i][j][e]);
-        store_tile<TO, F>(acc[0], g.C, g.ldc, 1.0f, 0.0f, false, row0, col0, win, lane);
+        store_tile<TO, F>(acc[0], g.C, g.ldc, g.M, g.N, 1.0f, 0.0f, false, row0, col0, win, lane);
         return;
       }
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t)
-      store_tile<TO, F, RED && NB == 1>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.alpha, g.beta, NB == 1 && g.beta != 0.0f,
+      store_tile<TO, F, RED && NB == 1>(acc[t], t == 0 ? g.C : g.C2, g.ldc, g.M, g.N, g.alpha, g.beta, NB == 1 && g.beta != 0.0f,
                                         row0, col0, win, lane, g.red, g.R);
   }
 }
@@ -453,7 +495,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
   const int64_t m0 = int64_t(tm) * C::BM, n0 = int64_t(tn) * C::BN;
 
   typename F::Src src;
-  F::make_src(src, wave, lane, g.lda, g.ldb);
+  F::make_src(src, wave, lane, g.lda, g.ldb, F::a_limit(g.M, m0), F::b_limit(g.N, n0));
   const typename F::Lane ln(wm, wn, lane);
   const uint16_t* a_tile = F::a_origin(g.A, m0, g.lda);
   const uint16_t* b_tile = F::b_origin(g.B, n0, g.ldb);
@@ -516,9 +558,9 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_lds_image(const 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  typename F::Src src;
-  F::make_src(src, wave, lane, g.lda, g.ldb);
   const int64_t m0 = int64_t(g.dbg_tm) * C::BM, n0 = int64_t(g.dbg_tn) * C::BN;
+  typename F::Src src;
+  F::make_src(src, wave, lane, g.lda, g.ldb, F::a_limit(g.M, m0), F::b_limit(g.N, n0));
   F::issue(src, lds, F::a_origin(g.A, m0, g.lda), F::b_origin(g.B, n0, g.ldb),
            C::NB > 1 ? F::b_origin(g.B2, n0, g.ldb) : nullptr, wave);
   wait_vmcnt<0>();

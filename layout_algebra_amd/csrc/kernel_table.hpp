@@ -17,7 +17,7 @@ struct KernelShape {
   int sw_b[3];             // Swizzle{B,M,S} of a B block
   int b_kmajor;            // 1: B block stored (bn,bk):(bk,1) (K contiguous); 0: (bk,bn):(bn,1)
   int direct;              // 1: global -> LDS direct loads (whole 1 KB per wave instruction)
-  int full_tiles_only;     // 1: M % bm == 0, N % bn == 0, K % bk == 0 required
+  int full_tiles_only;     // 1: K % bk == 0 required (M and N may end inside a tile: clamped loads, masked stores)
   int stages;
   int b_follows_storage = 0;   // 1: the B block keeps the operand's orientation (K-contiguous with sw_b
                                //    for K-major B, N-contiguous with sw_bn otherwise)

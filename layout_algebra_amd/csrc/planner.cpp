@@ -559,7 +559,7 @@ bool plan_stores(gemm_plan_s& p, std::string* err) {
   const gemm_desc& d = p.d;
   const std::vector<Store> plan = store_plan(p);
   // the kernels' store mask: element (row, col) of tile (tm, tn) is written
-  // when it lies inside C (the full-tile kernels only run whole tiles)
+  // when it lies inside C (all kernels mask their stores at M and N)
   const int64_t wcols = s.wave_split ? int64_t(s.nb) * s.bn : s.bn;   // store-plan columns per tile
   auto check_tile = [&](int64_t tm, int64_t tn) {
     const int64_t rows = std::min<int64_t>(s.bm, d.m - tm * s.bm), cols = std::min<int64_t>(s.bn, d.n - tn * s.bn);
@@ -722,9 +722,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     return GEMM_ERR_UNSUPPORTED;
   }
 
-  // Kernel choice: the full-tile direct-load kernels when every tile is whole
-  // and every row starts on 16 bytes; otherwise the general kernel, which
-  // masks edges and stages with the width chosen above.
+  // Kernel choice: the full-tile direct-load kernels when K is a multiple of
+  // their K block and every row starts on 16 bytes; M and N may end inside a
+  // tile (edge tiles read clamped source rows and columns and store only
+  // inside C), as long as the rows of the operand read in 16-byte chunks along
+  // M or N hold whole chunks (N % 8 for B stored [K, N], M % 8 for A stored
+  // [K, M]: no chunk reaches past a row's last element) and the tiles' padding
+  // stays small.  Otherwise the general kernel, which masks edges and stages
+  // with the width chosen above.
   p.kid = lak::KID_TILED_128;
   {
     const int fk = p.gate_up ? (kmajor ? lak::KID_FAST_GU_KM : atrans ? lak::KID_FAST_GU_AT : lak::KID_FAST_GU)
@@ -737,11 +742,19 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     const int64_t a_rows = atrans ? fs.bk : fs.bm;   // rows of A one block spans in memory
     const bool off32 = 2 * a_rows * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
     const bool large = (d.flags & GEMM_FLAG_LARGE_TILES) != 0;
-    if (whole && rows16 && off32) p.kid = fk;
+    const int64_t ftm = (d.m + fs.bm - 1) / fs.bm, ftn = (d.n + fs.bn - 1) / fs.bn;
+    const bool edges = d.m > 0 && d.n > 0 && d.k > 0 && d.k % fs.bk == 0 && (kmajor || d.n % 8 == 0) &&
+                       (!atrans || d.m % 8 == 0);
+    // padded tile area within 1.3x of M x N (4000^2: 1.05x; 1000 rows: 1.02x), unless the
+    // caller keeps the largest tile
+    const bool little_padding = 10 * __int128(ftm * fs.bm) * (ftn * fs.bn) <= 13 * __int128(d.m) * d.n;
+    if ((whole || (edges && (little_padding || large))) && rows16 && off32) p.kid = fk;
     // Fewer than 32 full-tile workgroups leave most CUs idle: 64 x 64 tiles of
     // the general kernel give 16 times as many and finish sooner (measured at
-    // 1 to 24 workgroups; from 64 on the full-tile kernel is faster).
-    if (!large && p.kid == fk && (d.m / fs.bm) * (d.n / fs.bn) * d.batch < 32) p.kid = lak::KID_TILED_64;
+    // 1 to 24 workgroups; from 64 on the full-tile kernel is faster).  With
+    // edge tiles the bar is 64 workgroups (measured: 40 edge tiles 11.1 us on
+    // the general kernel against 15.0; 96 tiles 16.9 against 12.1).
+    if (!large && p.kid == fk && ftm * ftn * d.batch < (whole ? 32 : 64)) p.kid = lak::KID_TILED_64;
     // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
     const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
     const bool skinny_fit = !p.gate_up && !kmajor && !atrans && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
