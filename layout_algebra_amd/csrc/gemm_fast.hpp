@@ -1,6 +1,7 @@
-// Fast tiled GEMM for gfx950: K % BK == 0 and 16-byte aligned rows; M and N
-// may end inside a tile (edge tiles load clamped source rows and columns and
-// store only inside C, see Fast::a_limit and store_band).
+// Fast tiled GEMM for gfx950: 16-byte aligned rows; M and N may end inside a
+// tile (edge tiles load clamped source rows and columns and store only inside
+// C, see Fast::a_limit and store_band), and K may end inside a K block (the
+// remaining K % BK values are added after the main loop, Fast::k_tail).
 //
 // Differences from the general kernel (gemm_tiled.hip):
 //  * Operands go global -> LDS directly (global_load_lds_dwordx4): each wave
@@ -215,6 +216,63 @@ struct Fast {
           f.b[t][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
       }
+    }
+  }
+
+  // Eight K values k .. k+7 of one row of a K-contiguous operand (p points at
+  // element k), zero from K on; k is a multiple of 8 and the row starts on 16
+  // bytes, so a whole chunk is one 16-byte load.
+  static __device__ __forceinline__ u32x4 tail_contig(const uint16_t* p, int64_t valid) {
+    if (valid >= 8) return *reinterpret_cast<const u32x4*>(p);
+    uint16_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = q < valid ? p[q] : uint16_t(0);
+    return u32x4{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16), e[4] | (uint32_t(e[5]) << 16),
+                 e[6] | (uint32_t(e[7]) << 16)};
+  }
+  // The same along a column of an operand stored K-outer (element k + q at p[q * ld]).
+  static __device__ __forceinline__ u32x4 tail_strided(const uint16_t* p, int64_t ld, int64_t valid) {
+    uint16_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = q < valid ? p[q * ld] : uint16_t(0);
+    return u32x4{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16), e[4] | (uint32_t(e[5]) << 16),
+                 e[6] | (uint32_t(e[7]) << 16)};
+  }
+
+  // K values past the last whole K block (K % BK of them), added after the main
+  // loop straight from global memory into MFMA fragments: lane l of a 32-row
+  // (or 32-column) block holds row (column) l % 32 and the 8 K values from
+  // 8 (l / 32) on of each 16-wide step, zero from K on; rows past M and
+  // columns past N read the last valid one (they reach no stored output).
+  // Nothing goes through LDS, so the main loop's schedule is untouched.
+  static __device__ __forceinline__ void k_tail(f32x16 (&acc)[NBW][FM][FN], const TiledArgs& g, int64_t m0, int64_t n0,
+                                                int wm, int wn_all, int lane) {
+    const int64_t k0 = (g.K / BK) * BK;
+    if (k0 == g.K) return;
+    const int tw = WSPLIT ? wn_all / WNW : 0;
+    const int wn = WSPLIT ? wn_all % WNW : wn_all;
+    const int l32 = lane & 31, h8 = (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      const int64_t kl = k0 + 16 * s + h8;              // this lane's first K value of the step
+      if (k0 + 16 * s >= g.K) break;                    // wave-uniform
+      const int64_t valid = g.K - kl;
+      Frags f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = min<int64_t>(m0 + wm * TM + i * 32 + l32, g.M - 1);
+        f.a[i] = ATR ? tail_strided(g.A + kl * g.lda + m, g.lda, valid) : tail_contig(g.A + m * g.lda + kl, valid);
+      }
+#pragma unroll
+      for (int t = 0; t < NBW; ++t) {
+        const uint16_t* B = (WSPLIT ? tw : t) == 0 ? g.B : g.B2;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = min<int64_t>(n0 + wn * TN + j * 32 + l32, g.N - 1);
+          f.b[t][j] = BKM ? tail_contig(B + n * g.ldb + kl, valid) : tail_strided(B + kl * g.ldb + n, g.ldb, valid);
+        }
+      }
+      mma(f, acc);
     }
   }
 
@@ -543,6 +601,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
     for (int s = 0; s < F::SUB; ++s) F::mma(f[s], acc);
   }
   if (group == 0) phase_barrier();         // t = 2 nk: group 0 idles while group 1 finishes
+  F::k_tail(acc, g, m0, n0, wm, wn, lane);
 
   // After the last phase barrier every M phase (all LDS reads) is complete,
   // so the waves may reuse the stage buffers as epilogue windows.

@@ -722,14 +722,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     return GEMM_ERR_UNSUPPORTED;
   }
 
-  // Kernel choice: the full-tile direct-load kernels when K is a multiple of
-  // their K block and every row starts on 16 bytes; M and N may end inside a
-  // tile (edge tiles read clamped source rows and columns and store only
-  // inside C), as long as the rows of the operand read in 16-byte chunks along
-  // M or N hold whole chunks (N % 8 for B stored [K, N], M % 8 for A stored
-  // [K, M]: no chunk reaches past a row's last element) and the tiles' padding
-  // stays small.  Otherwise the general kernel, which masks edges and stages
-  // with the width chosen above.
+  // Kernel choice: the full-tile direct-load kernels when every row starts on
+  // 16 bytes; M and N may end inside a tile (edge tiles read clamped source
+  // rows and columns and store only inside C), as long as the rows of the
+  // operand read in 16-byte chunks along M or N hold whole chunks (N % 8 for B
+  // stored [K, N], M % 8 for A stored [K, M]: no chunk reaches past a row's
+  // last element) and the tiles' padding stays small; K may end inside a K
+  // block from K = 256 on.  Otherwise the general kernel, which masks edges
+  // and stages with the width chosen above.
   p.kid = lak::KID_TILED_128;
   {
     const int fk = p.gate_up ? (kmajor ? lak::KID_FAST_GU_KM : atrans ? lak::KID_FAST_GU_AT : lak::KID_FAST_GU)
@@ -743,8 +743,10 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     const bool off32 = 2 * a_rows * d.lda < (int64_t{1} << 32) && 2 * b_rows * d.ldb < (int64_t{1} << 32);
     const bool large = (d.flags & GEMM_FLAG_LARGE_TILES) != 0;
     const int64_t ftm = (d.m + fs.bm - 1) / fs.bm, ftn = (d.n + fs.bn - 1) / fs.bn;
-    const bool edges = d.m > 0 && d.n > 0 && d.k > 0 && d.k % fs.bk == 0 && (kmajor || d.n % 8 == 0) &&
-                       (!atrans || d.m % 8 == 0);
+    // K ending inside a K block: the kernels add the last K % 32 values after the main loop from
+    // global memory (one short pass per tile), taken only where that pass is a small part of K
+    const bool k_ok = d.k > 0 && (d.k % fs.bk == 0 || d.k >= 256);
+    const bool edges = d.m > 0 && d.n > 0 && k_ok && (kmajor || d.n % 8 == 0) && (!atrans || d.m % 8 == 0);
     // padded tile area within 1.3x of M x N (4000^2: 1.05x; 1000 rows: 1.02x), unless the
     // caller keeps the largest tile
     const bool little_padding = 10 * __int128(ftm * fs.bm) * (ftn * fs.bn) <= 13 * __int128(d.m) * d.n;

@@ -294,10 +294,20 @@ def test_small_grids_take_64x64_tiles_unless_pinned():
     assert kern(2048, 1024, 512)["kernel"].startswith("fast_256x256")          # 32 workgroups
     assert kern(256, 256, 256, batch=32)["kernel"].startswith("fast_256x256")  # batch counts
     assert kern(512, 512, 128, gate_up=True)["kernel"].startswith("tiled_64x64")
+    # edge tiles on the full-tile kernel: M and N inside a tile, K ending inside a K block from
+    # K = 256 on, padding within 1.3x and at least 64 workgroups
+    assert kern(4000, 4000, 1000)["kernel"].startswith("fast_256x256")
+    assert kern(4000, 4000, 200)["kernel"].startswith("tiled_64x64")          # short K with a tail
+    assert kern(1088, 1920, 512)["kernel"].startswith("tiled_64x64")         # 40 edge tiles
+    assert kern(1088, 1920, 512, large_tiles=True)["kernel"].startswith("fast_256x256")
+    assert kern(300, 520, 96)["kernel"].startswith("tiled_")                 # 2.5x padding
+    assert kern(300, 520, 96, large_tiles=True)["kernel"].startswith("fast_256x256")
+    assert kern(4000, 4004, 1024)["kernel"].startswith("tiled_")             # B rows cut inside a chunk
+    assert kern(4000, 4004, 1024, b_kmajor=True, ldc=4008)["kernel"].startswith("fast_bkmajor")  # C rows on 16 bytes
     # general kernel with 16-byte loads: 64 x 64 at any grid
-    d = kern(4000, 4000, 1000)
+    d = kern(4000, 4000, 200)
     assert d["kernel"].startswith("tiled_64x64") and d["vec_elems"] == 8
-    assert kern(4000, 4000, 1000, large_tiles=True)["kernel"].startswith("tiled_128x128")
+    assert kern(4000, 4000, 200, large_tiles=True)["kernel"].startswith("tiled_128x128")
     # rows on 16 bytes with whole chunks: aligned 16-byte loads
     assert kern(1000, 1536, 1024)["vec_elems"] == 8 and kern(1000, 1536, 1024)["align_bytes"] == 16
     # ragged shapes keep 16-byte loads at 2-byte alignment (a chunk cut by an edge loads the 8

@@ -205,3 +205,77 @@ def test_edge_tile_lds_image_on_valid_positions(case):
     got = out.cpu().numpy().view(np.uint16).astype(np.uint32)
     assert valid.sum() > 0 and not valid.all()
     assert np.array_equal(got[valid], img[valid])
+
+
+K_TAIL = [
+    # (M, N, K, B stored [N, K], A stored [K, M]): K % 32 = 8 (one half step) or 24 (a step and a half)
+    (300, 520, 264, False, False),
+    (300, 520, 280, False, False),
+    (512, 512, 1000, False, False),    # whole tiles in M and N, K tail only
+    (700, 300, 296, True, False),      # K-major B: contiguous tail loads for both operands
+    (264, 520, 280, False, True),      # A stored [K, M]: strided tail loads for both operands
+]
+
+
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("case", K_TAIL, ids=[str(c) for c in K_TAIL])
+def test_full_tile_kernel_k_tail(case, out_kind):
+    """K ending inside a 32-deep K block: the last K % 32 values are added after the main loop."""
+    M, N, K, km, at = case
+    print("k tail", case, out_kind, flush=True)
+    seed = 11 * M + 3 * N + K
+    a = synth.uniform((M, K), seed, "bf16")
+    b = synth.uniform((K, N), seed + 1, "bf16")
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got, d = run_edge(a, b, out_kind, 0.5, 2.0, c, b_kmajor=km, a_trans=at)
+    assert d["kernel"].startswith("fast"), d["kernel"]
+    ref = oracle_gemm(a, b, "bf16", 0.5, 2.0, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "k tail %s" % (case,), beta=2.0)
+
+
+def test_k_tail_identity_is_exact():
+    """With K = 264 the identity's last 8 columns sit in the tail: the product must still equal A."""
+    M, K = 512, 264
+    a = synth.uniform((M, K), 91, "bf16")
+    eye = torch.eye(K, dtype=torch.bfloat16)
+    got, d = run_edge(a, eye, "f32", 1.0, 0.0, None)
+    assert d["kernel"].startswith("fast"), d["kernel"]
+    assert torch.equal(got, a.to(torch.float32))
+
+
+def test_gate_up_swiglu_k_tail():
+    M, N, K = 512, 384, 296
+    x = synth.normal((M, K), 95, "bf16")
+    wg = synth.normal((K, N), 96, "bf16", 0.3)
+    wu = synth.normal((K, N), 97, "bf16", 0.3)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.BF16, gate_up=True, large_tiles=True)
+    assert plan.describe()["kernel"].startswith("fast_gate_up"), plan.describe()["kernel"]
+    G = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    U = torch.full_like(G, float("nan"))
+    H = torch.full_like(G, float("nan"))
+    la.gemm_gate_up_run(plan, x.to(DEV), wg.to(DEV), wu.to(DEV), G, U)
+    la.gemm_gate_up_swiglu_run(plan, x.to(DEV), wg.to(DEV), wu.to(DEV), H)
+    torch.cuda.synchronize()
+    g_ref, u_ref = oracle_gemm(x, wg, "bf16"), oracle_gemm(x, wu, "bf16")
+    assert_close(G.cpu(), g_ref, K, x, wg, "bf16", "gate k tail")
+    assert_close(U.cpu(), u_ref, K, x, wu, "bf16", "up k tail")
+    with np.errstate(over="ignore"):
+        h_ref = g_ref / (1.0 + np.exp(-g_ref)) * u_ref
+    err = np.abs(H.cpu().double().numpy() - h_ref)
+    assert np.all(err <= swiglu_bound(K, x, wg, wu, g_ref, u_ref, h_ref, "bf16"))
+
+
+def test_planned_4000_by_1000_with_k_tail():
+    """4000 x 4000 x 1000 as planned: edge tiles in M and N and a K tail of 8; rows covering every band."""
+    M = N = 4000
+    K = 1000
+    a = synth.normal((M, K), 98, "bf16", 1.0 / 32)
+    b = synth.normal((K, N), 99, "bf16", 1.0 / 32)
+    plan = la.gemm_plan(M, N, K, la.BF16, la.F32)
+    assert plan.describe()["kernel"].startswith("fast_256x256"), plan.describe()["kernel"]
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    la.gemm_run(plan, a.to(DEV), b.to(DEV), C)
+    torch.cuda.synchronize()
+    rows = band_rows(M, band=256, wave_rows=128, extra=1, seed=100)
+    ref = oracle_gemm(a, b, "bf16", rows=rows)
+    assert_close(C.cpu()[rows], ref, K, a, b, "f32", "4000x4000x1000 rows")
