@@ -11,14 +11,21 @@ hipError_t go_fast(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
     hipLaunchKernelGGL((gemm_fast_lds_image<TI, TO, C>),
                        dim3(1), dim3(NT), 0, s, a);
   } else {
+    const bool kt = a.K % C::BK != 0;
     if constexpr (C::NB == 1) {
       // row reductions (single-output plans only) run their own instantiation
       if (a.red != RED_NONE) {
-        hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, true>), grid, dim3(NT), 0, s, a);
+        if (kt)
+          hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, true, true>), grid, dim3(NT), 0, s, a);
+        else
+          hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, true, false>), grid, dim3(NT), 0, s, a);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C>), grid, dim3(NT), 0, s, a);
+    if (kt)
+      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, false, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, false, false>), grid, dim3(NT), 0, s, a);
   }
   return hipGetLastError();
 }

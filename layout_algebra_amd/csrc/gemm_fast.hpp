@@ -244,35 +244,40 @@ struct Fast {
   // (or 32-column) block holds row (column) l % 32 and the 8 K values from
   // 8 (l / 32) on of each 16-wide step, zero from K on; rows past M and
   // columns past N read the last valid one (they reach no stored output).
-  // Nothing goes through LDS, so the main loop's schedule is untouched.
+  // Nothing goes through LDS, so the main loop's schedule is untouched.  Per
+  // step the B fragments are loaded first, then one A fragment at a time with
+  // its products, which keeps the tail within the main loop's registers.
   static __device__ __forceinline__ void k_tail(f32x16 (&acc)[NBW][FM][FN], const TiledArgs& g, int64_t m0, int64_t n0,
                                                 int wm, int wn_all, int lane) {
     const int64_t k0 = (g.K / BK) * BK;
-    if (k0 == g.K) return;
     const int tw = WSPLIT ? wn_all / WNW : 0;
     const int wn = WSPLIT ? wn_all % WNW : wn_all;
     const int l32 = lane & 31, h8 = (lane >> 5) * 8;
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      const int64_t kl = k0 + 16 * s + h8;              // this lane's first K value of the step
       if (k0 + 16 * s >= g.K) break;                    // wave-uniform
+      const int64_t kl = k0 + 16 * s + h8;              // this lane's first K value of the step
       const int64_t valid = g.K - kl;
-      Frags f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = min<int64_t>(m0 + wm * TM + i * 32 + l32, g.M - 1);
-        f.a[i] = ATR ? tail_strided(g.A + kl * g.lda + m, g.lda, valid) : tail_contig(g.A + m * g.lda + kl, valid);
-      }
+      u32x4 fb[NBW][FN];
 #pragma unroll
       for (int t = 0; t < NBW; ++t) {
         const uint16_t* B = (WSPLIT ? tw : t) == 0 ? g.B : g.B2;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int64_t n = min<int64_t>(n0 + wn * TN + j * 32 + l32, g.N - 1);
-          f.b[t][j] = BKM ? tail_contig(B + n * g.ldb + kl, valid) : tail_strided(B + kl * g.ldb + n, g.ldb, valid);
+          fb[t][j] = BKM ? tail_contig(B + n * g.ldb + kl, valid) : tail_strided(B + kl * g.ldb + n, g.ldb, valid);
         }
       }
-      mma(f, acc);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = min<int64_t>(m0 + wm * TM + i * 32 + l32, g.M - 1);
+        const u32x4 fa =
+            ATR ? tail_strided(g.A + kl * g.lda + m, g.lda, valid) : tail_contig(g.A + m * g.lda + kl, valid);
+#pragma unroll
+        for (int t = 0; t < NBW; ++t)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[t][i][j] = mfma_32x32x16<TI>(fa, fb[t][j], acc[t][i][j]);
+      }
     }
   }
 
@@ -534,7 +539,10 @@ __device__ __forceinline__ void wait_block(int kt, int nk) {
   }
 }
 
-template <class TI, class TO, class C, bool RED = false>
+// KT: K ends inside a K block (K % BK != 0), so the kernel adds the last values
+// after the main loop; a separate instantiation because the tail's registers
+// would otherwise push the whole-block kernels into spills.
+template <class TI, class TO, class C, bool RED = false, bool KT = false>
 __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
   using F = Fast<TI, C>;
@@ -601,7 +609,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
     for (int s = 0; s < F::SUB; ++s) F::mma(f[s], acc);
   }
   if (group == 0) phase_barrier();         // t = 2 nk: group 0 idles while group 1 finishes
-  F::k_tail(acc, g, m0, n0, wm, wn, lane);
+  if constexpr (KT) F::k_tail(acc, g, m0, n0, wm, wn, lane);
 
   // After the last phase barrier every M phase (all LDS reads) is complete,
   // so the waves may reuse the stage buffers as epilogue windows.

@@ -279,3 +279,41 @@ def test_planned_4000_by_1000_with_k_tail():
     rows = band_rows(M, band=256, wave_rows=128, extra=1, seed=100)
     ref = oracle_gemm(a, b, "bf16", rows=rows)
     assert_close(C.cpu()[rows], ref, K, a, b, "f32", "4000x4000x1000 rows")
+
+
+def _random_edge_cases(n, seed):
+    """Seeded shapes for the full-tile kernels: M, N anywhere in 1..1100 (M % 8 for A stored [K, M],
+    N % 8 for B stored [K, N]), K a multiple of 8 from 32 to 1200 (a multiple of 32 below 256)."""
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for i in range(n):
+        km = bool(torch.randint(0, 2, (1,), generator=g))
+        at = (not km) and bool(torch.randint(0, 3, (1,), generator=g) == 0)
+        M = int(torch.randint(1, 1101, (1,), generator=g))
+        N = int(torch.randint(1, 1101, (1,), generator=g))
+        if at:
+            M = max(8, M // 8 * 8)
+        if not km:
+            N = max(8, N // 8 * 8)
+        K = int(torch.randint(4, 151, (1,), generator=g)) * 8
+        if K < 256:
+            K = max(32, K // 32 * 32)
+        out.append((M, N, K, km, at))
+    return out
+
+
+RANDOM_EDGE = _random_edge_cases(24, 2027)
+
+
+@pytest.mark.parametrize("case", RANDOM_EDGE, ids=[str(c) for c in RANDOM_EDGE])
+def test_full_tile_kernel_random_shapes(case):
+    M, N, K, km, at = case
+    print("random edges", case, flush=True)
+    seed = 13 * M + 7 * N + K
+    a = synth.normal((M, K), seed, "f16")
+    b = synth.normal((K, N), seed + 1, "f16", 0.5)
+    c = synth.uniform((M, N), seed + 2, "f32")
+    got, d = run_edge(a, b, "f32", -0.5, 0.25, c, b_kmajor=km, a_trans=at)
+    assert d["kernel"].startswith("fast"), d["kernel"]
+    ref = oracle_gemm(a, b, "f16", -0.5, 0.25, c)
+    assert_close(got, ref, K, a, b, "f32", "random edges %s" % (case,), beta=0.25)
