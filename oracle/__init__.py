@@ -7,7 +7,8 @@ no code with the HIP library and never imports it; the two meet only through
 the seeded inputs the callers pass to both.
 
 * ``gemm_f64``  -- FP64 triple loop (C, OpenMP over rows), see ``gemm_f64.c``;
-  inputs are 16-bit bf16/fp16 patterns or 32-bit binary32 words.
+  inputs are 16-bit bf16/fp16 patterns, 32-bit binary32 words or 8-bit
+  E4M3 / E5M2 codes.
 * ``gate_up_swiglu_f64`` -- the gate/up products with the SwiGLU activation.
 * ``rms_norm_f64`` -- the row normalisation, numpy in binary64.
 * ``gemm_row_reduce_f64`` -- the GEMM with a sum / max / min of every output row.
@@ -25,6 +26,11 @@ from . import layout_ref  # noqa: F401  (re-exported for the tests)
 BF16 = 0
 F16 = 1
 F32 = 2
+F8E4M3 = 3
+F8E5M2 = 4
+_CODES = {"bf16": BF16, "f16": F16, "f32": F32, "f8e4m3": F8E4M3, "f8e5m2": F8E5M2}
+_WIDTH = {"bf16": 2, "f16": 2, "f32": 4, "f8e4m3": 1, "f8e5m2": 1}
+_STORE = {1: np.uint8, 2: np.uint16, 4: np.uint32}
 
 _lib = None
 
@@ -46,6 +52,8 @@ def _load():
     lib.oracle_decode.restype = None
     lib.oracle_decode32.argtypes = [vp, i64, vp]
     lib.oracle_decode32.restype = None
+    lib.oracle_decode8.argtypes = [vp, ctypes.c_int, i64, vp]
+    lib.oracle_decode8.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -53,29 +61,29 @@ def _load():
 
 
 def _type_code(kind: str) -> int:
-    if kind == "bf16":
-        return BF16
-    if kind == "f16":
-        return F16
-    if kind == "f32":
-        return F32
-    raise ValueError("oracle inputs are patterns of kind 'bf16', 'f16' or 'f32', got %r" % (kind,))
+    if kind not in _CODES:
+        raise ValueError("oracle inputs are patterns of kind %s, got %r" % (", ".join(map(repr, _CODES)), kind))
+    return _CODES[kind]
 
 
 def _as_bits(x, kind: str) -> np.ndarray:
     a = np.ascontiguousarray(x)
-    want = np.uint32 if kind == "f32" else np.uint16
+    want = _STORE[_WIDTH[kind]] if kind in _WIDTH else None
+    if want is None:
+        _type_code(kind)
     if a.dtype != want:
         raise TypeError("pass raw %s patterns as a %s array, got %s" % (kind, np.dtype(want).name, a.dtype))
     return a
 
 
 def decode(bits, kind: str) -> np.ndarray:
-    """Exact float64 values of 16-bit (bf16, f16) or 32-bit (f32) patterns of the given format."""
+    """Exact float64 values of 16-bit (bf16, f16), 32-bit (f32) or 8-bit (f8e4m3, f8e5m2) patterns."""
     b = _as_bits(bits, kind)
     out = np.empty(b.shape, dtype=np.float64)
     if kind == "f32":
         _load().oracle_decode32(b.ctypes.data, b.size, out.ctypes.data)
+    elif _WIDTH[kind] == 1:
+        _load().oracle_decode8(b.ctypes.data, _type_code(kind), b.size, out.ctypes.data)
     else:
         _load().oracle_decode(b.ctypes.data, _type_code(kind), b.size, out.ctypes.data)
     return out
@@ -85,12 +93,14 @@ def gemm_f64(a_bits, a_kind, b_bits, b_kind, alpha=1.0, beta=0.0, c=None, nthrea
     """out = alpha * A @ B + beta * C in FP64 (k ascending), from input patterns.
 
     ``a_bits`` is (M, K), ``b_bits`` is (K, N) (N contiguous): uint16 patterns
-    of kind 'bf16' / 'f16', or uint32 words of kind 'f32' (both operands then);
+    of kind 'bf16' / 'f16', uint32 words of kind 'f32' (both operands then), or
+    uint8 codes of kind 'f8e4m3' / 'f8e5m2' (each operand either);
     ``c`` is (M, N) float32 or None (only read when beta != 0).
     Returns an (M, N) float64 array.
     """
-    if (a_kind == "f32") != (b_kind == "f32"):
-        raise ValueError("A and B must both be 16-bit patterns or both be 'f32' words")
+    _type_code(a_kind), _type_code(b_kind)
+    if _WIDTH[a_kind] != _WIDTH[b_kind]:
+        raise ValueError("A and B must have the same element width (16-bit patterns, 'f32' words or 8-bit codes)")
     a = _as_bits(a_bits, a_kind)
     b = _as_bits(b_bits, b_kind)
     if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:

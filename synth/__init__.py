@@ -2,12 +2,13 @@
 
 This module only draws random numbers and names shapes; it holds none of the
 method's arithmetic.  Both the HIP path (through its callers) and the oracle
-receive the very same 16-bit patterns produced here.
+receive the very same bit patterns produced here.
 
 Recipe: values are sampled in float32 on the CPU with a seeded
 ``torch.Generator`` (uniform via ``rand``, normal via ``randn`` scaled by the
-standard deviation) and rounded once to bf16/fp16 with torch's
-round-to-nearest-even conversion (float32 inputs keep the sampled values).
+standard deviation) and rounded once to bf16/fp16 or to the 8-bit E4M3 / E5M2
+codes with torch's round-to-nearest-even conversions (float32 inputs keep the
+sampled values; the distributions stay far inside the 8-bit formats' range).
 """
 import math
 from dataclasses import dataclass, field
@@ -15,7 +16,9 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
+          "f8e4m3": torch.float8_e4m3fn, "f8e5m2": torch.float8_e5m2}
+BYTE_KINDS = ("f8e4m3", "f8e5m2")
 
 
 def torch_dtype(kind: str) -> torch.dtype:
@@ -45,7 +48,7 @@ class Workload:
     M: int
     N: int
     K: int
-    in_kind: str                 # "bf16", "f16" or "f32"
+    in_kind: str                 # "bf16", "f16", "f32", "f8e4m3" or "f8e5m2"
     out_kind: str                # "f32" or "bf16"
     alpha: float
     beta: float
@@ -190,9 +193,12 @@ def make_inputs(w: Workload):
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw patterns of a CPU tensor: bf16/fp16 as a uint16 numpy array, float32 as uint32."""
+    """Raw patterns of a CPU tensor: bf16/fp16 as a uint16 numpy array, float32 as uint32,
+    E4M3 / E5M2 as uint8."""
     if t.dtype == torch.float32:
         return t.contiguous().view(torch.int32).numpy().view(np.uint32)
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        return t.contiguous().view(torch.uint8).numpy()
     if t.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(t.dtype)
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)

@@ -1,8 +1,9 @@
 """Pins for the FP64 oracle GEMM (oracle/gemm_f64.c).
 
 The oracle is checked against things it does not compute itself:
-  * torch's and numpy's own bf16/fp16 decoding, for all 65,536 patterns, and
-    numpy's binary32 decoding on every exponent with edge and random fractions;
+  * torch's and numpy's own bf16/fp16 decoding, for all 65,536 patterns,
+    numpy's binary32 decoding on every exponent with edge and random fractions,
+    and torch's E4M3 / E5M2 decoding for all 256 codes of each;
   * exact rational arithmetic (fractions) on tiny shapes;
   * closed forms: ones x ones = K, identity and permutation B, alpha = 0;
   * numpy's float64 matmul (a library routine) on moderate shapes.
@@ -69,6 +70,40 @@ def test_decode_f32_against_numpy():
                                              (2.0 - 2.0 ** -23) * 2.0 ** 127, -3.1415927410125732]
 
 
+_E4M3_HAND = [  # code -> value from the format's definition (bias 7, 3 fraction bits, subnormals 2^-9)
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6), (0x38, 1.0), (0x3C, 1.5),
+    (0x40, 2.0), (0x7E, 448.0), (0xFE, -448.0), (0xB8, -1.0), (0x77, 240.0), (0x78, 256.0)]
+_E5M2_HAND = [  # bias 15, 2 fraction bits, subnormals 2^-16
+    (0x00, 0.0), (0x01, 2.0 ** -16), (0x03, 3 * 2.0 ** -16), (0x04, 2.0 ** -14), (0x3C, 1.0), (0x3E, 1.5),
+    (0x40, 2.0), (0x7B, 57344.0), (0xFB, -57344.0), (0x7C, np.inf), (0xFC, -np.inf), (0xBC, -1.0)]
+
+
+@pytest.mark.parametrize("kind,hand,tdt", [("f8e4m3", _E4M3_HAND, torch.float8_e4m3fn),
+                                           ("f8e5m2", _E5M2_HAND, torch.float8_e5m2)])
+def test_decode_f8_against_torch_and_hand_values(kind, hand, tdt):
+    b = np.arange(256, dtype=np.uint8)
+    mine = oracle.decode(b, kind)
+    ref = torch.from_numpy(b.copy()).view(tdt).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    codes = np.array([c for c, _ in hand], dtype=np.uint8)
+    assert oracle.decode(codes, kind).tolist() == [v for _, v in hand]
+    nan_codes = [0x7F, 0xFF] if kind == "f8e4m3" else [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]
+    assert np.isnan(oracle.decode(np.array(nan_codes, dtype=np.uint8), kind)).all()
+    assert int(np.isnan(mine).sum()) == len(nan_codes)
+
+
+def test_e5m2_is_the_upper_byte_of_binary16():
+    """E5M2 shares binary16's sign, exponent field and bias: code c is the binary16 pattern c << 8."""
+    c = np.arange(256, dtype=np.uint16)
+    a = oracle.decode(c.astype(np.uint8), "f8e5m2")
+    h = oracle.decode((c << 8).astype(np.uint16), "f16")
+    assert np.array_equal(np.isnan(a), np.isnan(h))
+    assert np.array_equal(a[~np.isnan(a)], h[~np.isnan(h)])
+
+
 def test_mixed_element_widths_are_rejected():
     a = synth.uniform((2, 3), 1, "f32")
     b = synth.uniform((3, 2), 2, "bf16")
@@ -76,6 +111,22 @@ def test_mixed_element_widths_are_rejected():
         oracle.gemm_f64(synth.bits(a), "f32", synth.bits(b), "bf16")
     with pytest.raises(TypeError):
         oracle.gemm_f64(synth.bits(b.t().contiguous()), "f32", synth.bits(a.t().contiguous()), "f32")
+    f8 = synth.uniform((3, 2), 3, "f8e4m3")
+    with pytest.raises(ValueError):
+        oracle.gemm_f64(synth.bits(synth.uniform((2, 3), 4, "bf16")), "bf16", synth.bits(f8), "f8e4m3")
+
+
+def test_mixed_byte_formats_match_numpy_float64_matmul():
+    """A in E4M3 and B in E5M2 (the two 8-bit formats may differ per operand)."""
+    a = synth.normal((33, 70), 11, "f8e4m3", 2.0)
+    b = synth.normal((70, 29), 12, "f8e5m2", 0.5)
+    got = oracle.gemm_f64(synth.bits(a), "f8e4m3", synth.bits(b), "f8e5m2", -1.5)
+    ref = -1.5 * (a.to(torch.float64).numpy() @ b.to(torch.float64).numpy())
+    scale = 1.5 * (np.abs(a.to(torch.float64).numpy()) @ np.abs(b.to(torch.float64).numpy()))
+    assert np.all(np.abs(got - ref) <= scale * 1e-13)
+    # the same values stored as binary32 words give the same result (the decoders agree)
+    got32 = oracle.gemm_f64(synth.bits(a.to(torch.float32)), "f32", synth.bits(b.to(torch.float32)), "f32", -1.5)
+    assert np.array_equal(got, got32)
 
 
 def _exact(a_t, b_t, alpha, beta, c):
@@ -103,7 +154,7 @@ def _exact(a_t, b_t, alpha, beta, c):
     return out, mag
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32", "f8e4m3", "f8e5m2"])
 def test_exact_rational_tiny_shapes(kind):
     seed = 100
     for M in range(1, 5):
@@ -134,7 +185,7 @@ def test_exact_rational_odd_shapes_with_beta_zero():
                 assert abs(got[i, j] - float(exact[i][j])) <= float(mag[i][j]) * (K + 3) * 2.0 ** -53
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32", "f8e4m3", "f8e5m2"])
 def test_ones_times_ones_is_K(kind):
     for (M, N, K) in [(5, 7, 13), (3, 4, 4096)]:
         a = torch.ones((M, K), dtype=synth.torch_dtype(kind))
@@ -151,7 +202,7 @@ def test_ones_A_gives_column_sums():
     np.testing.assert_allclose(got, np.broadcast_to(colsum, got.shape), rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32", "f8e4m3", "f8e5m2"])
 def test_identity_and_permutation_B(kind):
     K, M = 48, 20
     a = synth.uniform((M, K), 5, kind)
@@ -184,7 +235,7 @@ def test_alpha_beta_special_cases():
     assert oracle.gemm_f64(synth.bits(a[:0]), "f16", synth.bits(b), "f16").shape == (0, N)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32", "f8e4m3", "f8e5m2"])
 def test_matches_numpy_float64_matmul(kind):
     for (M, N, K), seed in [((37, 53, 129), 1), ((64, 80, 257), 2), ((5, 300, 64), 3)]:
         a = synth.normal((M, K), seed, kind)
