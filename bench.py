@@ -34,8 +34,10 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 
-# MI355X dense MFMA: bf16/f16 256 CU x 4096 FLOP/clk x 2.4 GHz; fp32 256 CU x 256 FLOP/clk x 2.4 GHz
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+# MI355X dense MFMA: bf16/f16 256 CU x 4096 FLOP/clk x 2.4 GHz; fp32 256 CU x 256 FLOP/clk x 2.4 GHz;
+# 8-bit E4M3 / E5M2 256 CU x 8192 FLOP/clk x 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "f8e4m3": 5033.2, "f8e5m2": 5033.2}
+IN_BYTES = {"bf16": 2, "f16": 2, "f32": 4, "f8e4m3": 1, "f8e5m2": 1}
 PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense BF16 MFMA peak, 4096^3 GEMM"
 
@@ -44,7 +46,8 @@ SHARED_SOURCES = ("kernel_common.hpp", "launch.hpp")
 NORM_SOURCES = ("rms_norm.hip", "norm.hpp")
 ATTN_SOURCES = ("attention.hip", "attention.hpp")
 # GEMM kernel families by the prefix of the planned kernel's name
-GEMM_SOURCES = {"fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_f32": ("gemm_f32.hip",),
+GEMM_SOURCES = {"fast_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"), "fast_": ("gemm_fast.hip", "gemm_fast.hpp"),
+                "tiled_f32": ("gemm_f32.hip",),
                 "tiled_": ("gemm_tiled.hip",), "skinny_": ("gemm_skinny.hip",)}
 
 
@@ -56,9 +59,14 @@ def gemm_plan_summary(workload):
     """The planned kernel of a GEMM workload: its name, grid and K blocks in flight."""
     import layout_algebra_amd as la
     w = synth.WORKLOADS[workload]
-    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
-    d = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up).describe()
+    d = la.gemm_plan(w.M, w.N, w.K, type_code(w.in_kind), type_code(w.out_kind), gate_up=w.gate_up,
+                     b_kmajor=w.b_kmajor).describe()
     return "%s grid=%d prefetch=%d" % (d["kernel"], d["grid"], d["prefetch_blocks"])
+
+
+def type_code(kind):
+    import layout_algebra_amd as la
+    return {"bf16": la.BF16, "f16": la.F16, "f32": la.F32, "f8e4m3": la.F8E4M3, "f8e5m2": la.F8E5M2}[kind]
 
 
 def workload_sources(workload):
@@ -108,7 +116,7 @@ def measured_traffic(workload):
 
 def algorithmic_bytes(w):
     """Compulsory HBM bytes of one step: every operand read once, C written (and read if beta != 0)."""
-    eb = 4 if w.in_kind == "f32" else 2
+    eb = IN_BYTES[w.in_kind]
     ob = 4 if w.out_kind == "f32" else 2
     nb = 2 if w.gate_up else 1
     nout = 1 if w.act == "swiglu" else nb
@@ -161,8 +169,8 @@ def main():
 
     import layout_algebra_amd as la
     w = synth.WORKLOADS[args.workload]
-    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
     dev = torch.device("cuda:0")
+    b_kmajor = args.b_kmajor or w.b_kmajor
     torch.cuda.set_device(dev)
 
     x = synth.make_inputs(w)
@@ -170,9 +178,9 @@ def main():
     if two and (not w.gate_up or w.act):
         print("--gate-up-as-two-gemms applies to the gate_up workload only", file=sys.stderr)
         sys.exit(2)
-    plan = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up and not two,
-                        b_kmajor=args.b_kmajor, a_transposed=args.a_transposed)
-    dev_b = (lambda t: t.t().contiguous().to(dev)) if args.b_kmajor else (lambda t: t.to(dev))
+    plan = la.gemm_plan(w.M, w.N, w.K, type_code(w.in_kind), type_code(w.out_kind), gate_up=w.gate_up and not two,
+                        b_kmajor=b_kmajor, a_transposed=args.a_transposed)
+    dev_b = (lambda t: t.t().contiguous().to(dev)) if b_kmajor else (lambda t: t.to(dev))
     A = x["A"].t().contiguous().to(dev) if args.a_transposed else x["A"].to(dev)
     out_dt = synth.torch_dtype(w.out_kind)
     if w.gate_up:
@@ -293,7 +301,7 @@ def main():
         "vs_baseline": None, "dtype": w.in_kind, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "out": w.out_kind,
                    "launch": args.launch,
-                   "b_order": "nk" if args.b_kmajor else "kn",
+                   "b_order": "nk" if b_kmajor else "kn",
                    "a_order": "km" if args.a_transposed else "mk",
                    "alpha": w.alpha, "beta": w.beta, "gate_up": w.gate_up,
                    "gate_up_as_two_gemms": two,
@@ -319,12 +327,13 @@ def main():
 def mfma_ceiling(dev, operands, flops, achieved):
     """The matrix-core rate the chip sustains at this workload's size: the library's probe issues
     the same number of MFMAs per SIMD as the workload (32x32x16 for 16-bit inputs, 32x32x2 for
-    binary32; one wave per SIMD, 16 independent
+    binary32, 32x32x64 for E4M3; one wave per SIMD, 16 independent
     chains, no memory traffic) on 16-byte fragments of the workload's own input values, then on
     zeros (the multipliers' power, and so the clock the chip settles to, depends on the bits).
     Context for roofline.frac, which stays relative to the nominal peak."""
     import layout_algebra_amd as la
-    per_mfma = 32 * 32 * (2 if operands.dtype == torch.float32 else 16) * 2
+    depth = {torch.float32: 2, torch.float8_e4m3fn: 64}.get(operands.dtype, 16)
+    per_mfma = 32 * 32 * depth * 2
     per_wave = max(16, int(round(flops / per_mfma / (256 * 4) / 16)) * 16)
     sink = torch.empty(256 * 256, dtype=torch.float32, device=dev)
     ops = operands.reshape(-1)[: 1 << 19]
@@ -662,10 +671,12 @@ def cpu_baseline_norm(w, inp, Y, budget_s, gpu_value):
 
 
 def gemm_tolerance(w, a, b, ref):
-    """Agreement bound of a GEMM output: 2^-20 K max|A| max|B| (FP32 accumulation) plus the
-    output's own rounding for 16-bit outputs (for fp32 outputs only where the result carries
-    beta * C_old or K = 0, whose final fp32 rounding no accumulation term covers)."""
-    acc = 2.0 ** -20 * w.K * float(a.abs().max()) * float(b.abs().max())
+    """Agreement bound of a GEMM output: 2^-20 K max|A| max|B| (FP32 accumulation; 2^-14 for
+    one-byte inputs, whose 64-deep products the matrix core adds with less than binary32
+    precision) plus the output's own rounding for 16-bit outputs (for fp32 outputs only where the
+    result carries beta * C_old or K = 0, whose final fp32 rounding no accumulation term covers)."""
+    e = -14 if IN_BYTES[w.in_kind] == 1 else -20     # one-byte products: the matrix core's own precision
+    acc = 2.0 ** e * w.K * float(a.float().abs().max()) * float(b.float().abs().max())
     f32_rel = 2.0 ** -22 if (w.K == 0 or w.beta != 0.0) else 0.0
     rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": f32_rel}[w.out_kind]
     return acc + rel * np.abs(ref)

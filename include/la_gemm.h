@@ -62,7 +62,13 @@ typedef enum {
   GEMM_ERR_HIP = 6            /* the HIP runtime reported an error */
 } gemm_status;
 
-typedef enum { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 } gemm_dtype;
+typedef enum {
+  GEMM_BF16 = 0,
+  GEMM_F16 = 1,
+  GEMM_F32 = 2,
+  GEMM_F8E4M3 = 3,   /* OCP 8-bit E4M3 (bias 7, no infinities, largest 448): inputs only */
+  GEMM_F8E5M2 = 4    /* OCP 8-bit E5M2 (bias 15, binary16's upper byte): inputs only */
+} gemm_dtype;
 
 /* Flags for gemm_desc.flags. */
 #define GEMM_FLAG_GATE_UP 0x1u   /* plan is for gemm_gate_up_run / gemm_gate_up_swiglu_run */
@@ -95,7 +101,15 @@ typedef struct {
                                   through 64-byte rows of 16 values -- the 64-byte fp32 plan of the
                                   Tylo.jl page "TMA and Hopper WGMMA", section "The same storage
                                   contract on both sides" -- and multiplied on the FP32 matrix cores;
-                                  gate/up plans and mixed widths are GEMM_ERR_UNSUPPORTED) */
+                                  gate/up plans and mixed widths are GEMM_ERR_UNSUPPORTED); or each
+                                  of F8E4M3 / F8E5M2 (one-byte codes, the formats may differ: plain
+                                  GEMMs and row reductions with A stored [M, K] and B stored [N, K]
+                                  (GEMM_FLAG_B_KMAJOR), lda, ldb and the A / B batch strides
+                                  multiples of 16, ldc and stride_c multiples of 8, k a multiple of
+                                  64 below 512 and of 16 from 512 on; staged through the same
+                                  page's 64-byte rows (64 codes) and multiplied 64 deep per matrix
+                                  instruction, which adds its 64 products with less than binary32
+                                  precision; anything else is GEMM_ERR_UNSUPPORTED) */
   int32_t c_type;              /* gemm_dtype of C (and of G, U): F32, BF16 or F16 */
   int64_t lda, ldb, ldc;       /* element strides: lda >= max(1,k) (max(1,m) for A stored [K,M]),
                                   ldb >= max(1,n) (max(1,k) for K-major B), ldc >= max(1,n) */

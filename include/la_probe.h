@@ -24,8 +24,9 @@ extern "C" {
  * CU); every lane loads eight 16-byte operand fragments from `operands`
  * (fragment f at byte 16 * (f mod (operand_bytes / 16))) and issues
  * mfma_per_wave v_mfma_f32_32x32x16 instructions (bf16 or f16 per in_type),
- * or v_mfma_f32_32x32x2_f32 on the first word of each fragment (GEMM_F32), in
- * 16 independent accumulator chains, with no other memory traffic, then
+ * v_mfma_f32_32x32x2_f32 on the first word of each fragment (GEMM_F32), or
+ * v_mfma_f32_32x32x64_f8f6f4 on E4M3 codes (GEMM_F8E4M3; operand i of each side
+ * is fragments i and (i + 1) mod 4 of that side), in 16 independent accumulator chains, with no other memory traffic, then
  * writes the sum of its accumulators to sink[lane id] (workgroups * 256
  * floats, device memory).  Timed by the caller, it gives the rate the matrix
  * cores sustain on those operand values at the clock the chip settles to

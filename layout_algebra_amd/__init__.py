@@ -13,7 +13,7 @@ Entry points carry the C ABI's names (include/la_gemm.h):
     la_view_window_eval (the pages' "shape:stride" notation)
 """
 from ._lib import (  # noqa: F401
-    BF16, F16, F32, FLAG_GATE_UP, FLAG_B_KMAJOR, FLAG_LARGE_TILES, FLAG_A_TRANSPOSED, GemmError, Plan, EXPORTED_SYMBOLS, lib_path, load,
+    BF16, F16, F32, F8E4M3, F8E5M2, FLAG_GATE_UP, FLAG_B_KMAJOR, FLAG_LARGE_TILES, FLAG_A_TRANSPOSED, GemmError, Plan, EXPORTED_SYMBOLS, lib_path, load,
     gemm_plan, gemm_run, gemm_run_reduce, gemm_gate_up_run, gemm_gate_up_swiglu_run, gemm_plan_describe,
     gemm_plan_lds_offset,
     gemm_plan_lds_stage_bytes, gemm_debug_lds_image, la_layout_eval, la_layout_eval_index,

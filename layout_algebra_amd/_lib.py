@@ -6,7 +6,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liblagemm.so")
 
-BF16, F16, F32 = 0, 1, 2
+BF16, F16, F32, F8E4M3, F8E5M2 = 0, 1, 2, 3, 4
 FLAG_GATE_UP = 0x1
 FLAG_B_KMAJOR = 0x2
 FLAG_LARGE_TILES = 0x4
@@ -133,15 +133,16 @@ class Plan:
 
 
 def gemm_plan(m, n, k, in_type=BF16, c_type=F32, lda=None, ldb=None, ldc=None, gate_up=False, b_kmajor=False,
-              batch=1, stride_a=None, stride_b=None, stride_c=None, large_tiles=False, a_transposed=False):
+              batch=1, stride_a=None, stride_b=None, stride_c=None, large_tiles=False, a_transposed=False, b_type=None):
     """Plan C[m,n] = A @ B.  A is an [m,k] tensor, or with a_transposed=True a [k,m] tensor (A transposed);
     B is a [k,n] tensor, or with b_kmajor=True a [n,k] tensor (B transposed).
+    in_type is A's element type and B's unless b_type is given (the two one-byte formats may differ).
     batch > 1: tensors gain a leading batch dimension with the given element strides (default: packed).
     large_tiles=True keeps the largest tile the shape allows (GEMM_FLAG_LARGE_TILES)."""
     lda = int(lda if lda is not None else max(1, m if a_transposed else k))
     ldb = int(ldb if ldb is not None else max(1, k if b_kmajor else n))
     ldc = int(ldc if ldc is not None else max(1, n))
-    d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type), int(c_type), lda, ldb, ldc,
+    d = _Desc(int(m), int(n), int(k), int(in_type), int(in_type if b_type is None else b_type), int(c_type), lda, ldb, ldc,
               (FLAG_GATE_UP if gate_up else 0) | (FLAG_B_KMAJOR if b_kmajor else 0) |
               (FLAG_LARGE_TILES if large_tiles else 0) | (FLAG_A_TRANSPOSED if a_transposed else 0), int(batch),
               int(stride_a if stride_a is not None else (k if a_transposed else m) * lda),
@@ -177,7 +178,8 @@ _KIND = {}
 def _torch():
     import torch
     if not _KIND:
-        _KIND.update({torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32})
+        _KIND.update({torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32,
+                      torch.float8_e4m3fn: F8E4M3, torch.float8_e5m2: F8E5M2})
     return torch
 
 
@@ -330,12 +332,12 @@ def la_attention_run(Q, K, V, O, scale=None, stream=None):
 
 def la_probe_mfma(operands, sink, workgroups, mfma_per_wave, stream=None):
     """Matrix-core rate probe: `workgroups` x 4 waves, each issuing mfma_per_wave MFMAs on 16-byte fragments
-    taken from `operands` (a contiguous bf16/f16/f32 tensor on the GPU, its dtype selects the instruction);
+    taken from `operands` (a contiguous bf16/f16/f32/E4M3 tensor on the GPU, its dtype selects the instruction);
     `sink` is a float32 GPU tensor of at least workgroups * 256 elements."""
     torch = _torch()
     if not isinstance(operands, torch.Tensor) or operands.device.type != "cuda" or \
-            operands.dtype not in (torch.bfloat16, torch.float16, torch.float32):
-        raise ValueError("operands must be a bf16/f16/f32 tensor on the GPU")
+            operands.dtype not in (torch.bfloat16, torch.float16, torch.float32, torch.float8_e4m3fn):
+        raise ValueError("operands must be a bf16/f16/f32/float8_e4m3fn tensor on the GPU")
     if not operands.is_contiguous():
         raise ValueError("operands must be contiguous")
     if not isinstance(sink, torch.Tensor) or sink.device.type != "cuda" or sink.dtype != torch.float32 or \

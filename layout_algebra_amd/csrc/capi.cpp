@@ -32,18 +32,18 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 
 lak::TiledArgs base_args(const gemm_plan_s& p) {
   lak::TiledArgs a{};
-  a.M = p.d.m;
-  a.N = p.d.n;
-  a.K = p.d.k;
-  a.lda = p.d.lda;
-  a.ldb = p.d.ldb;
-  a.ldc = p.d.ldc;
+  a.M = p.kd.m;
+  a.N = p.kd.n;
+  a.K = p.kd.k;
+  a.lda = p.kd.lda;
+  a.ldb = p.kd.ldb;
+  a.ldc = p.kd.ldc;
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
   a.group_m = p.group_m;
-  a.sa = p.d.stride_a;
-  a.sb = p.d.stride_b;
-  a.sc = p.d.stride_c;
+  a.sa = p.kd.stride_a;
+  a.sb = p.kd.stride_b;
+  a.sc = p.kd.stride_c;
   a.out_bytes = p.out_bytes;
   return a;
 }
@@ -231,8 +231,8 @@ gemm_status la_rms_norm_run(int64_t m, int64_t d, int32_t x_type, int32_t y_type
 
 gemm_status la_probe_mfma(const void* operands, int64_t operand_bytes, float* sink, int64_t workgroups,
                           int64_t mfma_per_wave, int32_t in_type, void* stream) {
-  if (in_type != GEMM_BF16 && in_type != GEMM_F16 && in_type != GEMM_F32)
-    return set_err(GEMM_ERR_INVALID_ARG, "in_type must be GEMM_BF16, GEMM_F16 or GEMM_F32");
+  if (in_type != GEMM_BF16 && in_type != GEMM_F16 && in_type != GEMM_F32 && in_type != GEMM_F8E4M3)
+    return set_err(GEMM_ERR_INVALID_ARG, "in_type must be GEMM_BF16, GEMM_F16, GEMM_F32 or GEMM_F8E4M3");
   if (operand_bytes < 16 || operand_bytes % 16) return set_err(GEMM_ERR_INVALID_ARG, "operand_bytes must be a positive multiple of 16");
   if (workgroups < 1 || workgroups > (int64_t{1} << 20)) return set_err(GEMM_ERR_INVALID_ARG, "workgroups must be in 1..2^20");
   if (mfma_per_wave < 16 || mfma_per_wave % 16 || mfma_per_wave > (int64_t{1} << 24))
@@ -240,7 +240,8 @@ gemm_status la_probe_mfma(const void* operands, int64_t operand_bytes, float* si
   if (!operands || !sink) return set_err(GEMM_ERR_NULL, "operands and sink must not be NULL");
   if (!aligned(operands, 16) || !aligned(sink, 4)) return set_err(GEMM_ERR_ALIGNMENT, "operands must be 16-byte aligned, sink 4-byte aligned");
   const hipError_t e = lak::launch_mfma_probe(operands, operand_bytes / 16, sink, workgroups, mfma_per_wave,
-                                              in_type == GEMM_BF16 ? lak::IN_BF16 : in_type == GEMM_F16 ? lak::IN_F16 : lak::IN_F32,
+                                              in_type == GEMM_BF16 ? lak::IN_BF16 : in_type == GEMM_F16 ? lak::IN_F16
+                                              : in_type == GEMM_F32 ? lak::IN_F32 : lak::IN_F8,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GEMM_OK;

@@ -276,8 +276,34 @@ struct Fast {
 #pragma unroll
         for (int t = 0; t < NBW; ++t)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[t][i][j] = mfma_32x32x16<TI>(fa, fb[t][j], acc[t][i][j]);
+          for (int j = 0; j < FN; ++j) acc[t][i][j] = mma1(fa, fb[t][j], acc[t][i][j]);
       }
+    }
+  }
+
+  // One product of a 16-value step of 16-bit elements; for one-byte elements
+  // (16-bit units holding byte pairs) the step is 32 values in the lower half
+  // of a 64-deep product whose upper half is zero.
+  static __device__ __forceinline__ f32x16 mma1(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (TI::f8) return mfma_f8_32x32x64<TI>(a, u32x4{}, b, u32x4{}, c);
+    else return mfma_32x32x16<TI>(a, b, c);
+  }
+
+  // The products of one whole K block: SUB steps of 16 16-bit values, or for
+  // one-byte elements one 64-deep product over both steps' reads.
+  static __device__ __forceinline__ void mma_block(const Frags (&f)[SUB], f32x16 (&acc)[NBW][FM][FN]) {
+    if constexpr (TI::f8) {
+      static_assert(SUB == 2, "a 64-deep one-byte product takes the two 16-byte reads of a 32-unit block");
+#pragma unroll
+      for (int t = 0; t < NBW; ++t)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[t][i][j] = mfma_f8_32x32x64<TI>(f[0].a[i], f[1].a[i], f[0].b[t][j], f[1].b[t][j], acc[t][i][j]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) mma(f[s], acc);
     }
   }
 
@@ -605,8 +631,7 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_pp_kernel(const 
       if (kt + 1 < nk) wait_block<F>(kt + 1, nk);
     }
     phase_barrier();                       // C(kt)
-#pragma unroll
-    for (int s = 0; s < F::SUB; ++s) F::mma(f[s], acc);
+    F::mma_block(f, acc);
   }
   if (group == 0) phase_barrier();         // t = 2 nk: group 0 idles while group 1 finishes
   if constexpr (KT) F::k_tail(acc, g, m0, n0, wm, wn, lane);

@@ -14,10 +14,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Input element tags: both are 16-bit patterns in memory.
-struct InBF16 {};
-struct InF16 {};
+// Input element tags: 16-bit patterns in memory ...
+struct InBF16 { static constexpr bool f8 = false; };
+struct InF16 { static constexpr bool f8 = false; };
+// ... or one-byte codes, A and B each in the OCP 8-bit format FA / FB
+// (0: E4M3, 1: E5M2, the matrix core's format selectors for A and B).
+template <int FA, int FB>
+struct InF8 {
+  static constexpr bool f8 = true;
+  static constexpr int fmt_a = FA, fmt_b = FB;
+};
 
 // Output element tags.
 struct OutF32 { typedef float storage; };
@@ -37,6 +45,20 @@ __device__ __forceinline__ f32x16 mfma_32x32x16<InBF16>(u32x4 a, u32x4 b, f32x16
 template <>
 __device__ __forceinline__ f32x16 mfma_32x32x16<InF16>(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x64_f8f6f4 on 8-bit A and B: 32x32 FP32 block += (32x64) x
+// (64x32).  Lane l holds row (A) / column (B) l % 32 and 32 K values, the
+// result lane map is that of the 32x32x16 products.  A and B place K the same
+// way (byte q of lane l of A meets byte q of lane l's half of B), so any
+// assignment of K values to (lane half, byte) that both operands share gives
+// the product; callers concatenate two 16-byte K-contiguous reads.  Scale
+// operands 0 select the unscaled form of the instruction (no block scaling).
+template <class TI>
+__device__ __forceinline__ f32x16 mfma_f8_32x32x64(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi, f32x16 c) {
+  const i32x8 a{int(a_lo.x), int(a_lo.y), int(a_lo.z), int(a_lo.w), int(a_hi.x), int(a_hi.y), int(a_hi.z), int(a_hi.w)};
+  const i32x8 b{int(b_lo.x), int(b_lo.y), int(b_lo.z), int(b_lo.w), int(b_hi.x), int(b_hi.y), int(b_hi.z), int(b_hi.w)};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, TI::fmt_a, TI::fmt_b, 0, 0, 0, 0);
 }
 
 // v_mfma_f32_16x16x32_{bf16,f16}: lane l holds row/column l % 16 and eight

@@ -37,6 +37,19 @@ KernelShape kernel_shape(int kid) {
       s.k_sub = 16;
       return s;
     }
+    case KID_FAST_F8: {
+      // the K-major full-tile kernel seen in one-byte elements: a K block of 64 codes per row
+      // (64-byte rows) under Swizzle{2,4,4} (16-byte chunks, rows 4 apart in bits 8-9), one
+      // 32x32x64 product per block
+      KernelShape s = fast_shape<CfgFast256KM>();
+      s.bk = 2 * CfgFast256KM::BK;
+      s.mfma_k = 64;
+      s.sw_a[0] = s.sw_b[0] = 2;
+      s.sw_a[1] = s.sw_b[1] = 4;
+      s.sw_a[2] = s.sw_b[2] = 4;
+      s.in_bytes = 1;
+      return s;
+    }
     case KID_SKINNY_16: {
       using C = CfgSkinny16;
       return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
@@ -66,6 +79,7 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_FAST_GU_AT: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_SKINNY_16: return launch_skinny(in_kind, out_kind, args, grid, stream, lds_image);
     case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
+    case KID_FAST_F8: return launch_fast_f8(in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

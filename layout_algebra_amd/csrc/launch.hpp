@@ -56,10 +56,12 @@ enum KernelId : int {
   KID_FAST_256_AT = 8,   // KID_FAST_256 for A stored [K, M] (M contiguous)
   KID_FAST_GU_AT = 9,    // KID_FAST_GU for X stored [K, M]
   KID_TILED_F32 = 10,    // binary32 A and B, any shape: 128x128x32, 4 waves of 64x64, v_mfma_f32_32x32x2_f32
+  KID_FAST_F8 = 11,      // one-byte A [M, K] and B [N, K]: KID_FAST_256_KM on byte pairs, 256x256x64, v_mfma_f32_32x32x64_f8f6f4
   KID_COUNT
 };
 
-enum InKind : int { IN_BF16 = 0, IN_F16 = 1, IN_F32 = 2 };
+// One-byte inputs: IN_F8 + 2 * (A is E5M2) + (B is E5M2).
+enum InKind : int { IN_BF16 = 0, IN_F16 = 1, IN_F32 = 2, IN_F8 = 3 };
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
 // Compile-time parameters of the fast kernels (one source of truth for the
@@ -131,6 +133,8 @@ hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args
                        hipStream_t stream, bool lds_image);
 hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                          bool lds_image);
+hipError_t launch_fast_f8(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
+                          bool lds_image);
 hipError_t launch_f32(int out_kind, int vec, bool b_kmajor, bool a_trans, const TiledArgs& args, dim3 grid,
                       hipStream_t stream, bool lds_image);
 

@@ -69,7 +69,7 @@ struct CopyChunk { int64_t row, col; };
 
 bool fast_kid(int kid) {
   return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
-         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT;
+         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8;
 }
 
 bool fail(std::string* err, const std::string& msg) {
@@ -615,15 +615,150 @@ const char* dtype_name(int t) {
     case GEMM_BF16: return "bf16";
     case GEMM_F16: return "f16";
     case GEMM_F32: return "f32";
+    case GEMM_F8E4M3: return "f8e4m3";
+    case GEMM_F8E5M2: return "f8e5m2";
     default: return "?";
   }
 }
 
+// The plan as JSON (gemm_plan_describe): sizes, kernel, tile, layouts, copy and store plans.
+std::string describe(const gemm_plan_s& p) {
+  const gemm_desc& d = p.d;
+  const auto& s = p.shape;
+  std::ostringstream js;
+  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
+                                      "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8"};
+  static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
+  js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
+     << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
+     << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc
+     << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"in_b\":\"" << dtype_name(d.b_type) << "\""
+     << ",\"out\":\"" << dtype_name(d.c_type) << "\""
+     << ",\"gate_up\":" << (p.gate_up ? "true" : "false")
+     << ",\"a_order\":\"" << (p.a_trans ? "km" : "mk") << "\""
+     << ",\"b_order\":\"" << (p.b_kmajor ? "nk" : "kn") << "\""
+     << ",\"batch\":" << d.batch
+     << ",\"tile\":[" << s.bm << "," << s.bn << "," << s.bk << "]"
+     << ",\"waves\":[" << s.waves_m << "," << s.waves_n << "],\"threads\":" << s.threads
+     << ",\"mfma\":\"" << s.mfma_m << "x" << s.mfma_n << "x" << s.mfma_k << "\""
+     << ",\"tiles\":[" << p.tiles_m << "," << p.tiles_n << "],\"grid\":" << p.grid << ",\"group_m\":" << p.group_m
+     << ",\"stages\":" << s.stages << ",\"stage_elems\":" << p.stage_elems << ",\"lds_bytes\":" << p.lds_bytes
+     << ",\"swizzle_a\":[" << s.sw_a[0] << "," << s.sw_a[1] << "," << s.sw_a[2] << "]"
+     << ",\"swizzle_b\":[" << s.sw_b[0] << "," << s.sw_b[1] << "," << s.sw_b[2] << "]"
+     << ",\"direct_loads\":" << (s.direct ? "true" : "false")
+     << ",\"waves_split_by_weight\":" << (s.wave_split ? "true" : "false")
+     << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
+     << ",\"prefetch_blocks\":" << prefetch_blocks(p)
+     << ",\"global_a\":\"" << p.glob_a.str() << "\",\"global_b\":\"" << p.glob_b.str() << "\",\"global_c\":\""
+     << p.glob_c.str() << "\""
+     << ",\"copy\":" << p.copy_json << ",\"store\":" << p.store_json
+     << ",\"in_bytes\":" << s.in_bytes << ",\"k_sub\":" << s.k_sub
+     << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes
+     << ",\"out_align_bytes\":" << p.out_align_bytes << "}";
+  return js.str();
+}
+
+bool is_f8(int32_t t) { return t == GEMM_F8E4M3 || t == GEMM_F8E5M2; }
+
 }  // namespace
+
+// One-byte inputs (OCP E4M3 / E5M2, A and B each either): both operands
+// K-contiguous (A [M, K], B [N, K]), every row on 16 bytes.  Copies and
+// fragment reads move whole 16-byte chunks, so the kernel addresses a row of
+// codes as 16-bit units holding byte pairs: the plan is the K-major 16-bit
+// full-tile plan of the pair view (K, lda, ldb and the A / B batch strides
+// halved), checked by the same steps, then described in one-byte elements
+// after checking that every byte's LDS offset is its pair's offset doubled
+// plus its position in the pair.  The 64-code rows of a K block are the
+// 64-byte swizzle rows of the Tylo.jl page "TMA and Hopper WGMMA" (section
+// "The same storage contract on both sides"), Swizzle{2,4,4}.
+static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
+  auto unsupported = [&](const char* m) { fail(err, m); return GEMM_ERR_UNSUPPORTED; };
+  if (!is_f8(d.a_type) || !is_f8(d.b_type))
+    return unsupported("A and B must both be one-byte (E4M3 or E5M2) or both be wider");
+  if (d.flags & GEMM_FLAG_GATE_UP) return unsupported("one-byte inputs are planned for plain GEMMs and row reductions only");
+  if (!(d.flags & GEMM_FLAG_B_KMAJOR) || (d.flags & GEMM_FLAG_A_TRANSPOSED))
+    return unsupported("one-byte inputs need A stored [M, K] and B stored [N, K] (GEMM_FLAG_B_KMAJOR): both K-contiguous");
+  const bool many = d.batch > 1;
+  if (d.lda % 16 || d.ldb % 16 || (many && (d.stride_a % 16 || d.stride_b % 16)))
+    return unsupported("one-byte inputs need lda, ldb (and the A and B batch strides) to be multiples of 16");
+  if (d.ldc % 8 || (many && d.stride_c % 8))
+    return unsupported("one-byte inputs need ldc (and stride_c) to be multiples of 8: C rows on 16 bytes");
+  if (d.k % 16) return unsupported("one-byte inputs need k to be a multiple of 16");
+  if (d.k % 64 && d.k < 512)
+    return unsupported("one-byte inputs need k to be a multiple of 64 below 512 (from 512 on the last k % 64 are added "
+                       "after the main loop)");
+  gemm_desc v = d;
+  v.k = d.k / 2;
+  v.lda = d.lda / 2;
+  v.ldb = d.ldb / 2;
+  v.stride_a = d.stride_a / 2;
+  v.stride_b = d.stride_b / 2;
+  v.a_type = v.b_type = GEMM_BF16;
+  v.flags |= GEMM_FLAG_LARGE_TILES;          // the full-tile kernel at every grid size
+  const gemm_status st = build(v, p, err);
+  if (st != GEMM_OK) return st;
+  const bool runs = d.m > 0 && d.n > 0 && d.k > 0;
+  if (runs && p.kid != lak::KID_FAST_256_KM)
+    return unsupported("one-byte inputs: operand rows too far apart for the kernel's 32-bit byte offsets");
+  p.d = d;
+  p.kd = v;
+  p.in_bytes = 1;
+  if (p.kid == lak::KID_FAST_256_KM) {
+    const lak::KernelShape s8 = lak::kernel_shape(lak::KID_FAST_F8);
+    try {
+      using la::Tree;
+      const la::Swizzle swa(s8.sw_a[0], s8.sw_a[1], s8.sw_a[2]), swb(s8.sw_b[0], s8.sw_b[1], s8.sw_b[2]);
+      const la::View a8(swa, la::Layout(Tree::T({Tree::L(s8.bm), Tree::L(s8.bk)}), Tree::T({Tree::L(s8.bk), Tree::L(1)})));
+      const la::View b8(swb, la::Layout(Tree::T({Tree::L(s8.bk), Tree::L(s8.bn)}), Tree::T({Tree::L(1), Tree::L(s8.bk)})));
+      for (int64_t r = 0; r < s8.bm; ++r)
+        for (int64_t k = 0; k < s8.bk; ++k)
+          if (a8.at({r, k}) != 2 * p.lds_a.at({r, k / 2}) + k % 2) {
+            fail(err, "one-byte A map differs from its byte-pair map at (" + std::to_string(r) + ", " + std::to_string(k) + ")");
+            return GEMM_ERR_RESOURCE;
+          }
+      for (int64_t k = 0; k < s8.bk; ++k)
+        for (int64_t n = 0; n < s8.bn; ++n)
+          if (b8.at({k, n}) != 2 * p.lds_b.at({k / 2, n}) + k % 2) {
+            fail(err, "one-byte B map differs from its byte-pair map at (" + std::to_string(k) + ", " + std::to_string(n) + ")");
+            return GEMM_ERR_RESOURCE;
+          }
+      if (!check_block(a8, 0, int64_t(s8.bm) * s8.bk, "A", err) || !check_block(b8, 0, int64_t(s8.bn) * s8.bk, "B", err))
+        return GEMM_ERR_RESOURCE;
+      p.lds_a = a8;
+      p.lds_b = p.lds_b2 = b8;
+      p.base_b = int64_t(s8.bm) * s8.bk;
+      p.base_b2 = p.base_b + int64_t(s8.bn) * s8.bk;
+      p.stage_elems *= 2;
+      const int64_t Mc = int64_t(p.tiles_m) * s8.bm, Nc = int64_t(p.tiles_n) * s8.bn;
+      const int64_t Kc = (d.k + s8.bk - 1) / s8.bk * s8.bk;
+      p.glob_a = la::tile(la::Layout::row_major(Mc, Kc, d.lda), {s8.bm, s8.bk});
+      p.glob_b = la::tile(la::Layout::col_major(Kc, Nc, d.ldb), {s8.bk, s8.bn});
+      // a wave instruction moves 1 KiB: 16 rows of one 64-code K block row each
+      const la::Layout ca = copy_instr_layout(1024 / s8.bk, s8.bk, d.lda), cb = copy_instr_layout(1024 / s8.bk, s8.bk, d.ldb);
+      const int64_t per_block = int64_t(s8.bm) * s8.bk / 1024;
+      std::ostringstream js;
+      js << "{\"A\":{\"instr\":\"" << ca.str() << "\",\"run_bytes\":" << s8.bk << ",\"instrs_per_block\":" << per_block << "}"
+         << ",\"B\":{\"instr\":\"" << cb.str() << "\",\"run_bytes\":" << s8.bk << ",\"instrs_per_block\":" << per_block << "}}";
+      p.copy_json = js.str();
+    } catch (const la::LayoutError& e) {
+      fail(err, e.what());
+      return GEMM_ERR_RESOURCE;
+    }
+    p.kid = lak::KID_FAST_F8;
+    p.shape = s8;
+    p.vec = 16;
+    p.in_kind = lak::IN_F8 + 2 * (d.a_type == GEMM_F8E5M2 ? 1 : 0) + (d.b_type == GEMM_F8E5M2 ? 1 : 0);
+  }
+  // (k == 0, or nothing to compute: the pair view's plan, which reads no element of A or B)
+  p.json = describe(p);
+  return GEMM_OK;
+}
 
 gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p = gemm_plan_s{};
   p.d = d;
+  p.kd = d;
   if (d.m < 0 || d.n < 0 || d.k < 0) { fail(err, "m, n and k must be >= 0"); return GEMM_ERR_INVALID_ARG; }
   const bool kmajor = (d.flags & GEMM_FLAG_B_KMAJOR) != 0;
   const bool atrans = (d.flags & GEMM_FLAG_A_TRANSPOSED) != 0;
@@ -639,8 +774,8 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     fail(err, "leading dimensions and batch strides must be <= 2^40 elements");
     return GEMM_ERR_UNSUPPORTED;
   }
-  if ((d.a_type != GEMM_BF16 && d.a_type != GEMM_F16 && d.a_type != GEMM_F32) ||
-      (d.b_type != GEMM_BF16 && d.b_type != GEMM_F16 && d.b_type != GEMM_F32) ||
+  auto in_type = [](int32_t t) { return t >= GEMM_BF16 && t <= GEMM_F8E5M2; };
+  if (!in_type(d.a_type) || !in_type(d.b_type) ||
       (d.c_type != GEMM_BF16 && d.c_type != GEMM_F16 && d.c_type != GEMM_F32)) {
     fail(err, "unknown dtype");
     return GEMM_ERR_INVALID_ARG;
@@ -649,6 +784,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     fail(err, "unknown flag bits");
     return GEMM_ERR_INVALID_ARG;
   }
+  if (is_f8(d.a_type) || is_f8(d.b_type)) return build_f8(d, p, err);
   const bool in32 = d.a_type == GEMM_F32 && d.b_type == GEMM_F32;
   if (atrans && kmajor && !in32) {
     fail(err, "A stored [K, M] together with B stored [N, K] is implemented for binary32 inputs only");
@@ -887,36 +1023,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     return GEMM_ERR_RESOURCE;
   }
 
-  std::ostringstream js;
-  static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
-                                      "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32"};
-  static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
-  js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
-     << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
-     << ",\"lda\":" << d.lda << ",\"ldb\":" << d.ldb << ",\"ldc\":" << d.ldc
-     << ",\"in\":\"" << dtype_name(d.a_type) << "\",\"out\":\"" << dtype_name(d.c_type) << "\""
-     << ",\"gate_up\":" << (p.gate_up ? "true" : "false")
-     << ",\"a_order\":\"" << (p.a_trans ? "km" : "mk") << "\""
-     << ",\"b_order\":\"" << (p.b_kmajor ? "nk" : "kn") << "\""
-     << ",\"batch\":" << d.batch
-     << ",\"tile\":[" << s.bm << "," << s.bn << "," << s.bk << "]"
-     << ",\"waves\":[" << s.waves_m << "," << s.waves_n << "],\"threads\":" << s.threads
-     << ",\"mfma\":\"" << s.mfma_m << "x" << s.mfma_n << "x" << s.mfma_k << "\""
-     << ",\"tiles\":[" << p.tiles_m << "," << p.tiles_n << "],\"grid\":" << p.grid << ",\"group_m\":" << p.group_m
-     << ",\"stages\":" << s.stages << ",\"stage_elems\":" << p.stage_elems << ",\"lds_bytes\":" << p.lds_bytes
-     << ",\"swizzle_a\":[" << s.sw_a[0] << "," << s.sw_a[1] << "," << s.sw_a[2] << "]"
-     << ",\"swizzle_b\":[" << s.sw_b[0] << "," << s.sw_b[1] << "," << s.sw_b[2] << "]"
-     << ",\"direct_loads\":" << (s.direct ? "true" : "false")
-     << ",\"waves_split_by_weight\":" << (s.wave_split ? "true" : "false")
-     << ",\"lds_a\":\"" << p.lds_a.base().str() << "\",\"lds_b\":\"" << p.lds_b.base().str() << "\""
-     << ",\"prefetch_blocks\":" << prefetch_blocks(p)
-     << ",\"global_a\":\"" << p.glob_a.str() << "\",\"global_b\":\"" << p.glob_b.str() << "\",\"global_c\":\""
-     << p.glob_c.str() << "\""
-     << ",\"copy\":" << p.copy_json << ",\"store\":" << p.store_json
-     << ",\"in_bytes\":" << s.in_bytes << ",\"k_sub\":" << s.k_sub
-     << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes
-     << ",\"out_align_bytes\":" << p.out_align_bytes << "}";
-  p.json = js.str();
+  p.json = describe(p);
   return GEMM_OK;
 }
 

@@ -10,9 +10,11 @@
 
 struct gemm_plan_s {
   gemm_desc d;
+  gemm_desc kd;              // what the kernel runs on: d, or for one-byte inputs d with k, lda, ldb and the
+                             // A / B batch strides counted in 16-bit units (byte pairs)
   int kid = 0;
   int in_kind = 0, out_kind = 0;
-  int in_bytes = 2;          // bytes per A / B element (2: bf16 / f16, 4: binary32)
+  int in_bytes = 2;          // bytes per A / B element (2: bf16 / f16, 4: binary32, 1: E4M3 / E5M2)
   int vec = 1;               // elements per global vector load of A and B
   int align_bytes = 2;       // required alignment of the A / B / W pointers
   int out_bytes = 4;         // bytes per C element

@@ -58,6 +58,7 @@ class Workload:
     dist_c: Dist = None          # existing C when beta != 0
     gate_up: bool = False
     act: str = ""                # gate/up epilogue activation: "" (G and U) or "swiglu" (one output)
+    b_kmajor: bool = False       # B stored [N, K] (K contiguous; one-byte inputs need it)
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -90,6 +91,11 @@ WORKLOADS = {
         "square4096_f32", 4096, 4096, 4096, "f32", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0 / math.sqrt(4096)), Dist("normal", 0.0, 1.0 / math.sqrt(4096)),
         (2101, 2102), notes="4096^3 GEMM, binary32 in and out"),
+    # one-byte inputs: A [M, K] and B stored [N, K], both K-contiguous
+    "square4096_f8": Workload(
+        "square4096_f8", 4096, 4096, 4096, "f8e4m3", "bf16", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 1.0),
+        (2201, 2202), b_kmajor=True, notes="4096^3 GEMM, E4M3 in (B stored [N, K]), bf16 out"),
     "skinny": Workload(
         "skinny", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5001, 5002, 5003),

@@ -217,11 +217,13 @@ def test_tile_plan_rejects_what_the_page_forbids():
             la.la_tile_plan_offset(args[0], args[1], args[2], args[3], (0, 0))
 
 
+CODES = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32, "f8e4m3": la.F8E4M3, "f8e5m2": la.F8E5M2}
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_plans_build(name):
     w = synth.WORKLOADS[name]
-    code = {"bf16": la.BF16, "f16": la.F16, "f32": la.F32}
-    p = la.gemm_plan(w.M, w.N, w.K, code[w.in_kind], code[w.out_kind], gate_up=w.gate_up)
+    p = la.gemm_plan(w.M, w.N, w.K, CODES[w.in_kind], CODES[w.out_kind], gate_up=w.gate_up, b_kmajor=w.b_kmajor)
     d = p.describe()
     assert d["m"] == w.M and d["n"] == w.N and d["k"] == w.K
     assert d["lds_bytes"] <= 163840
@@ -449,7 +451,7 @@ def test_mfma_probe_argument_errors_are_caught_before_launch():
     def call(ops=0x1000000, nbytes=1 << 20, sink=0x2000000, wg=256, n=4096, t=la.BF16):
         return st[lib.la_probe_mfma(vp(ops), nbytes, vp(sink), wg, n, t, vp(0))]
 
-    assert call(t=3) == "GEMM_ERR_INVALID_ARG" and call(t=-1) == "GEMM_ERR_INVALID_ARG"
+    assert call(t=la.F8E5M2) == "GEMM_ERR_INVALID_ARG" and call(t=-1) == "GEMM_ERR_INVALID_ARG"
     assert call(nbytes=0) == "GEMM_ERR_INVALID_ARG"
     assert call(nbytes=24) == "GEMM_ERR_INVALID_ARG"
     assert call(wg=0) == "GEMM_ERR_INVALID_ARG"
@@ -551,3 +553,59 @@ def test_binary32_storage_orders_and_staging_width():
     assert plan(256, 254, 64)["vec_elems"] == 1
     assert plan(254, 256, 64, a_transposed=True)["vec_elems"] == 1
     assert plan(254, 256, 64)["vec_elems"] == 4
+
+
+def _swz(off, b, m, s):
+    """Swizzle{B,M,S} written out: bits [M+S, M+S+B) XORed into bits [M, M+B)."""
+    return off ^ (((off >> (m + s)) & ((1 << b) - 1)) << m)
+
+
+@pytest.mark.parametrize("fa,fb", [(la.F8E4M3, la.F8E4M3), (la.F8E4M3, la.F8E5M2), (la.F8E5M2, la.F8E5M2)])
+def test_one_byte_plans_describe_64_byte_rows(fa, fb):
+    """One-byte inputs: the K-major full-tile kernel on byte pairs, described in codes: K blocks of
+    64 codes (64-byte rows) under Swizzle{2,4,4}, one 32x32x64 product per block; every LDS offset
+    the library reports is the written-out swizzle of m*64 + k (A) and n*64 + k (B)."""
+    p = la.gemm_plan(4096, 4096, 4096, fa, la.BF16, b_kmajor=True, b_type=fb)
+    d = p.describe()
+    names = {la.F8E4M3: "f8e4m3", la.F8E5M2: "f8e5m2"}
+    assert d["kernel"] == "fast_f8_256x256x64" and d["in"] == names[fa] and d["in_b"] == names[fb]
+    assert d["tile"] == [256, 256, 64] and d["mfma"] == "32x32x64" and d["in_bytes"] == 1
+    assert d["swizzle_a"] == [2, 4, 4] and d["swizzle_b"] == [2, 4, 4]
+    assert d["lds_a"] == "(256,64):(64,1)" and d["lds_b"] == "(64,256):(1,64)"
+    assert d["stage_elems"] == 2 * 256 * 64 and d["lds_bytes"] == 4 * 2 * 256 * 64
+    assert d["copy"]["A"]["run_bytes"] == 64 and d["copy"]["A"]["instrs_per_block"] == 16
+    assert la.gemm_plan_lds_stage_bytes(p) == 2 * 256 * 64
+    for (r, k) in [(0, 0), (1, 17), (4, 16), (7, 63), (255, 40), (130, 33)]:
+        assert la.gemm_plan_lds_offset(p, 0, r, k) == _swz(r * 64 + k, 2, 4, 4)
+        assert la.gemm_plan_lds_offset(p, 1, k, r) == 256 * 64 + _swz(r * 64 + k, 2, 4, 4)
+    # 16-lane groups of a 16-byte read: rows r..r+15 at one K chunk hit distinct 16-byte slots of
+    # each 256-byte window (the bank rule the 16-bit swizzles were chosen by)
+    for k0 in (0, 16, 32, 48):
+        slots = [(_swz(r * 64 + k0, 2, 4, 4) % 256) // 16 for r in range(4)]
+        assert len(set(slots)) == 4
+
+
+def test_one_byte_plans_shapes_and_rejections():
+    def plan(m, n, k, **kw):
+        kw.setdefault("b_kmajor", True)
+        return la.gemm_plan(m, n, k, la.F8E4M3, la.F32, ldc=max(8, (n + 7) // 8 * 8),
+                            lda=max(16, (k + 15) // 16 * 16), ldb=max(16, (k + 15) // 16 * 16), **kw)
+    # edges in M and N, a K tail of 16 / 48 codes from k = 512 on, small grids: all on the one kernel
+    for m, n, k in [(300, 520, 512), (777, 1000, 1040), (513, 64, 1008), (64, 64, 64), (1, 1, 64)]:
+        assert plan(m, n, k).describe()["kernel"] == "fast_f8_256x256x64", (m, n, k)
+    # k = 0 reads neither operand (C = beta * C on the general kernel); m = 0 launches nothing
+    assert plan(100, 100, 0).describe()["k"] == 0
+    for m, n, k, kw in [(256, 256, 96, {}),                      # k % 64 below 512
+                        (256, 256, 520, {}),                     # k % 16
+                        (256, 256, 256, {"b_kmajor": False}),    # B stored [K, N]
+                        (256, 256, 256, {"a_transposed": True}),
+                        (256, 256, 256, {"gate_up": True})]:
+        with pytest.raises(la.GemmError) as e:
+            plan(m, n, k, **kw)
+        assert "GEMM_ERR_UNSUPPORTED" in str(e.value)
+    with pytest.raises(la.GemmError):      # rows not on 16 bytes
+        la.gemm_plan(256, 256, 256, la.F8E4M3, la.F32, b_kmajor=True, lda=264)
+    with pytest.raises(la.GemmError):      # one-byte A with a 16-bit B
+        la.gemm_plan(256, 256, 256, la.F8E4M3, la.F32, b_kmajor=True, b_type=la.BF16)
+    with pytest.raises(la.GemmError):      # not an output type
+        la.gemm_plan(256, 256, 256, la.BF16, la.F8E4M3)

@@ -1,0 +1,148 @@
+"""GPU parity of one-byte inputs (OCP E4M3 / E5M2, A and B each either) against the oracle.
+
+The plans run the K-major full-tile kernel on byte pairs with one 32x32x64
+product per K block of 64 codes (A [M, K], B stored [N, K]).  Cases cover every
+format pair and output type, whole tiles, M and N ending inside a tile, a K
+tail (16 and 48 codes past the last whole block, from K = 512 on), beta != 0
+on padded C rows whose padding must stay untouched, batches, the row
+reductions, the staged LDS image against the plan's one-byte map, and the
+4096^3 workload on rows covering every tile band.  The agreement bound's
+accumulation term is 2^-14 K max|A| max|B| (the matrix core's measured
+precision on 64-deep one-byte products; see tests/parity.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import layout_algebra_amd as la
+import synth
+from parity import assert_close, band_rows, oracle_gemm
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+CODE = {"f8e4m3": la.F8E4M3, "f8e5m2": la.F8E5M2, "bf16": la.BF16, "f16": la.F16, "f32": la.F32}
+PAIRS = [("f8e4m3", "f8e4m3"), ("f8e4m3", "f8e5m2"), ("f8e5m2", "f8e4m3"), ("f8e5m2", "f8e5m2")]
+
+
+def inputs(M, N, K, ka, kb, seed):
+    a = synth.normal((M, K), seed, ka, 1.0)
+    b = synth.normal((K, N), seed + 1, kb, 0.5)
+    return a, b
+
+
+def run_f8(a, b, ka, kb, out_kind, alpha=1.0, beta=0.0, c=None, batch_dims=None):
+    M, K = a.shape
+    N = b.shape[1]
+    ld = (N + 7) // 8 * 8 + 8
+    Cbuf = torch.full((M, ld), float("nan"), dtype=synth.torch_dtype(out_kind), device=DEV)
+    C = Cbuf[:, :N]
+    if c is not None:
+        C.copy_(c.to(DEV))
+    plan = la.gemm_plan(M, N, K, CODE[ka], CODE[out_kind], ldc=ld, b_kmajor=True, b_type=CODE[kb])
+    d = plan.describe()
+    la.gemm_run(plan, a.to(DEV), b.t().contiguous().to(DEV), C, alpha, beta)
+    torch.cuda.synchronize()
+    assert torch.isnan(Cbuf[:, N:].cpu().float()).all(), "a store landed in C's row padding"
+    return C.cpu(), d
+
+
+CASES = [
+    # (M, N, K)
+    (256, 256, 64),       # one tile, one K block
+    (512, 768, 1024),     # whole tiles
+    (300, 520, 512),      # M and N edges
+    (777, 1000, 1040),    # edges and a K tail of 16 codes
+    (513, 264, 1008),     # a K tail of 48 codes (one full 32-code step and a half step)
+    (64, 64, 640),        # a single edge tile
+]
+
+
+@pytest.mark.parametrize("ka,kb", PAIRS, ids=["%s-%s" % p for p in PAIRS])
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_one_byte_gemm_f32_out_with_beta(case, ka, kb):
+    M, N, K = case
+    print("f8", case, ka, kb, flush=True)
+    a, b = inputs(M, N, K, ka, kb, 3 * M + 5 * N + K)
+    c = synth.uniform((M, N), M + N, "f32")
+    got, d = run_f8(a, b, ka, kb, "f32", 0.75, -1.25, c)
+    assert d["kernel"] == "fast_f8_256x256x64"
+    ref = oracle_gemm(a, b, ka, 0.75, -1.25, c, b_kind=kb)
+    assert_close(got, ref, K, a, b, "f32", "f8 %s %s %s" % (case, ka, kb), beta=-1.25)
+
+
+@pytest.mark.parametrize("out_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("case", [(512, 768, 1024), (777, 1000, 1040)], ids=["whole", "edges_tail"])
+def test_one_byte_gemm_16bit_out(case, out_kind):
+    M, N, K = case
+    print("f8 out", case, out_kind, flush=True)
+    a, b = inputs(M, N, K, "f8e4m3", "f8e4m3", 11 * M + N)
+    a = (a.to(torch.float32) / 8).to(torch.float8_e4m3fn)     # keep f16 outputs far from overflow
+    got, _ = run_f8(a, b, "f8e4m3", "f8e4m3", out_kind)
+    ref = oracle_gemm(a, b, "f8e4m3")
+    assert_close(got, ref, K, a, b, out_kind, "f8 out %s %s" % (case, out_kind))
+
+
+def test_one_byte_exact_small_integers():
+    """Integers below 16 are exact in both formats and every partial sum below 2^11 is exact in
+    any accumulation of at least 12 bits: the products must come back bit for bit."""
+    M, N, K = 300, 260, 1040
+    g = torch.Generator().manual_seed(5)
+    a = torch.randint(-3, 4, (M, K), generator=g).to(torch.float32).to(torch.float8_e4m3fn)
+    b = torch.randint(-3, 4, (K, N), generator=g).to(torch.float32).to(torch.float8_e5m2)
+    got, _ = run_f8(a, b, "f8e4m3", "f8e5m2", "f32")
+    ref = oracle_gemm(a, b, "f8e4m3", b_kind="f8e5m2")
+    assert np.abs(ref).max() < 2 ** 11
+    assert np.array_equal(got.double().numpy(), ref)
+
+
+def test_one_byte_batched_and_reduced():
+    M, N, K, batch = 300, 264, 576, 3
+    print("f8 batch", flush=True)
+    a = synth.normal((batch, M, K), 21, "f8e4m3")
+    b = synth.normal((batch, K, N), 22, "f8e5m2", 0.5)
+    plan = la.gemm_plan(M, N, K, la.F8E4M3, la.F32, b_kmajor=True, b_type=la.F8E5M2, batch=batch)
+    C = torch.empty((batch, M, N), dtype=torch.float32, device=DEV)
+    R = torch.empty((batch, M), dtype=torch.float32, device=DEV)
+    la.gemm_run_reduce(plan, a.to(DEV), b.transpose(1, 2).contiguous().to(DEV), C, op="max", R=R)
+    torch.cuda.synchronize()
+    for z in range(batch):
+        ref = oracle_gemm(a[z], b[z], "f8e4m3", b_kind="f8e5m2")
+        assert_close(C[z].cpu(), ref, K, a[z], b[z], "f32", "f8 batch %d" % z)
+        # the row maxima are maxima of the FP32 outputs the kernel stored
+        assert torch.equal(R[z].cpu(), C[z].cpu().max(dim=1).values)
+
+
+def test_one_byte_lds_image_matches_the_plan():
+    """K block 0 of tile (1, 2) staged by the kernel's own copy code: byte lds_offset(A, r, k) holds
+    A[256 + r, k] and byte lds_offset(B, k, n) holds B[k, 512 + n] (edge rows and columns clamped)."""
+    M, N, K = 600, 700, 512
+    a, b = inputs(M, N, K, "f8e4m3", "f8e5m2", 7)
+    plan = la.gemm_plan(M, N, K, la.F8E4M3, la.F32, b_kmajor=True, b_type=la.F8E5M2, ldc=704)
+    nbytes = la.gemm_plan_lds_stage_bytes(plan)
+    out = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    la.gemm_debug_lds_image(plan, a.to(DEV), b.t().contiguous().to(DEV), None, 1, 2, out)
+    torch.cuda.synchronize()
+    img = out.cpu().numpy()
+    ab, bb = synth.bits(a), synth.bits(b)
+    for r in range(256):
+        row = min(256 + r, M - 1)
+        for k in range(64):
+            assert img[la.gemm_plan_lds_offset(plan, 0, r, k)] == ab[row, k], (r, k)
+    for n in range(0, 256, 3):
+        col = min(512 + n, N - 1)
+        for k in range(64):
+            assert img[la.gemm_plan_lds_offset(plan, 1, k, n)] == bb[k, col], (k, n)
+
+
+def test_square4096_f8_workload_rows():
+    w = synth.WORKLOADS["square4096_f8"]
+    x = synth.make_inputs(w)
+    print("f8 4096", flush=True)
+    plan = la.gemm_plan(w.M, w.N, w.K, la.F8E4M3, la.BF16, b_kmajor=True)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=DEV)
+    la.gemm_run(plan, x["A"].to(DEV), x["B"].t().contiguous().to(DEV), C)
+    torch.cuda.synchronize()
+    rows = band_rows(w.M, band=256, wave_rows=128, extra=1, seed=44)
+    ref = oracle_gemm(x["A"], x["B"], w.in_kind, rows=rows)
+    assert_close(C.cpu()[rows], ref, w.K, x["A"], x["B"], "bf16", "square4096_f8 rows")
