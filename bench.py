@@ -46,8 +46,8 @@ SHARED_SOURCES = ("kernel_common.hpp", "launch.hpp")
 NORM_SOURCES = ("rms_norm.hip", "norm.hpp")
 ATTN_SOURCES = ("attention.hip", "attention.hpp")
 # GEMM kernel families by the prefix of the planned kernel's name
-GEMM_SOURCES = {"fast_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"), "fast_": ("gemm_fast.hip", "gemm_fast.hpp"),
-                "tiled_f32": ("gemm_f32.hip",),
+GEMM_SOURCES = {"fast_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"), "fast_gate_up_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"),
+                "fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_f32": ("gemm_f32.hip",),
                 "tiled_": ("gemm_tiled.hip",), "skinny_": ("gemm_skinny.hip",)}
 
 

@@ -103,8 +103,9 @@ typedef struct {
                                   contract on both sides" -- and multiplied on the FP32 matrix cores;
                                   gate/up plans and mixed widths are GEMM_ERR_UNSUPPORTED); or each
                                   of F8E4M3 / F8E5M2 (one-byte codes, the formats may differ: plain
-                                  GEMMs and row reductions with A stored [M, K] and B stored [N, K]
-                                  (GEMM_FLAG_B_KMAJOR), lda, ldb and the A / B batch strides
+                                  GEMMs, row reductions and gate/up with A (X) stored [M, K] and B
+                                  (the weights) stored [N, K] (GEMM_FLAG_B_KMAJOR), lda, ldb and the
+                                  A / B batch strides
                                   multiples of 16, ldc and stride_c multiples of 8, k a multiple of
                                   64 below 512 and of 16 from 512 on; staged through the same
                                   page's 64-byte rows (64 codes) and multiplied 64 deep per matrix

@@ -37,11 +37,12 @@ KernelShape kernel_shape(int kid) {
       s.k_sub = 16;
       return s;
     }
-    case KID_FAST_F8: {
-      // the K-major full-tile kernel seen in one-byte elements: a K block of 64 codes per row
+    case KID_FAST_F8:
+    case KID_FAST_GU_F8: {
+      // the K-major full-tile kernels seen in one-byte elements: a K block of 64 codes per row
       // (64-byte rows) under Swizzle{2,4,4} (16-byte chunks, rows 4 apart in bits 8-9), one
       // 32x32x64 product per block
-      KernelShape s = fast_shape<CfgFast256KM>();
+      KernelShape s = kid == KID_FAST_F8 ? fast_shape<CfgFast256KM>() : fast_shape<CfgFastGUKM>();
       s.bk = 2 * CfgFast256KM::BK;
       s.mfma_k = 64;
       s.sw_a[0] = s.sw_b[0] = 2;
@@ -79,7 +80,8 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_FAST_GU_AT: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_SKINNY_16: return launch_skinny(in_kind, out_kind, args, grid, stream, lds_image);
     case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
-    case KID_FAST_F8: return launch_fast_f8(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_F8:
+    case KID_FAST_GU_F8: return launch_fast_f8(kid, in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

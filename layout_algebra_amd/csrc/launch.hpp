@@ -57,6 +57,7 @@ enum KernelId : int {
   KID_FAST_GU_AT = 9,    // KID_FAST_GU for X stored [K, M]
   KID_TILED_F32 = 10,    // binary32 A and B, any shape: 128x128x32, 4 waves of 64x64, v_mfma_f32_32x32x2_f32
   KID_FAST_F8 = 11,      // one-byte A [M, K] and B [N, K]: KID_FAST_256_KM on byte pairs, 256x256x64, v_mfma_f32_32x32x64_f8f6f4
+  KID_FAST_GU_F8 = 12,   // one-byte gate/up, weights [N, K]: KID_FAST_GU_KM on byte pairs
   KID_COUNT
 };
 
@@ -133,7 +134,7 @@ hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args
                        hipStream_t stream, bool lds_image);
 hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                          bool lds_image);
-hipError_t launch_fast_f8(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
+hipError_t launch_fast_f8(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                           bool lds_image);
 hipError_t launch_f32(int out_kind, int vec, bool b_kmajor, bool a_trans, const TiledArgs& args, dim3 grid,
                       hipStream_t stream, bool lds_image);

@@ -69,7 +69,7 @@ struct CopyChunk { int64_t row, col; };
 
 bool fast_kid(int kid) {
   return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
-         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8;
+         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8 || kid == lak::KID_FAST_GU_F8;
 }
 
 bool fail(std::string* err, const std::string& msg) {
@@ -627,7 +627,8 @@ std::string describe(const gemm_plan_s& p) {
   const auto& s = p.shape;
   std::ostringstream js;
   static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
-                                      "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8"};
+                                      "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8",
+                                      "fast_gate_up_f8"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -662,8 +663,9 @@ bool is_f8(int32_t t) { return t == GEMM_F8E4M3 || t == GEMM_F8E5M2; }
 
 }  // namespace
 
-// One-byte inputs (OCP E4M3 / E5M2, A and B each either): both operands
-// K-contiguous (A [M, K], B [N, K]), every row on 16 bytes.  Copies and
+// One-byte inputs (OCP E4M3 / E5M2, A and B each either; plain GEMMs, row
+// reductions and gate/up): both operands K-contiguous (A [M, K], B and the
+// gate/up weights [N, K]), every row on 16 bytes.  Copies and
 // fragment reads move whole 16-byte chunks, so the kernel addresses a row of
 // codes as 16-bit units holding byte pairs: the plan is the K-major 16-bit
 // full-tile plan of the pair view (K, lda, ldb and the A / B batch strides
@@ -676,7 +678,6 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   auto unsupported = [&](const char* m) { fail(err, m); return GEMM_ERR_UNSUPPORTED; };
   if (!is_f8(d.a_type) || !is_f8(d.b_type))
     return unsupported("A and B must both be one-byte (E4M3 or E5M2) or both be wider");
-  if (d.flags & GEMM_FLAG_GATE_UP) return unsupported("one-byte inputs are planned for plain GEMMs and row reductions only");
   if (!(d.flags & GEMM_FLAG_B_KMAJOR) || (d.flags & GEMM_FLAG_A_TRANSPOSED))
     return unsupported("one-byte inputs need A stored [M, K] and B stored [N, K] (GEMM_FLAG_B_KMAJOR): both K-contiguous");
   const bool many = d.batch > 1;
@@ -699,13 +700,15 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   const gemm_status st = build(v, p, err);
   if (st != GEMM_OK) return st;
   const bool runs = d.m > 0 && d.n > 0 && d.k > 0;
-  if (runs && p.kid != lak::KID_FAST_256_KM)
+  const int pair_kid = p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
+  if (runs && p.kid != pair_kid)
     return unsupported("one-byte inputs: operand rows too far apart for the kernel's 32-bit byte offsets");
   p.d = d;
   p.kd = v;
   p.in_bytes = 1;
-  if (p.kid == lak::KID_FAST_256_KM) {
-    const lak::KernelShape s8 = lak::kernel_shape(lak::KID_FAST_F8);
+  if (p.kid == pair_kid) {
+    const int kid8 = p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
+    const lak::KernelShape s8 = lak::kernel_shape(kid8);
     try {
       using la::Tree;
       const la::Swizzle swa(s8.sw_a[0], s8.sw_a[1], s8.sw_a[2]), swb(s8.sw_b[0], s8.sw_b[1], s8.sw_b[2]);
@@ -725,6 +728,11 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
           }
       if (!check_block(a8, 0, int64_t(s8.bm) * s8.bk, "A", err) || !check_block(b8, 0, int64_t(s8.bn) * s8.bk, "B", err))
         return GEMM_ERR_RESOURCE;
+      // the W_up block follows W_gate's in each stage, as in the pair view
+      if (p.gate_up && 2 * (p.base_b2 - p.base_b) != int64_t(s8.bn) * s8.bk) {
+        fail(err, "one-byte W_up block does not follow W_gate's");
+        return GEMM_ERR_RESOURCE;
+      }
       p.lds_a = a8;
       p.lds_b = p.lds_b2 = b8;
       p.base_b = int64_t(s8.bm) * s8.bk;
@@ -736,16 +744,16 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
       p.glob_b = la::tile(la::Layout::col_major(Kc, Nc, d.ldb), {s8.bk, s8.bn});
       // a wave instruction moves 1 KiB: 16 rows of one 64-code K block row each
       const la::Layout ca = copy_instr_layout(1024 / s8.bk, s8.bk, d.lda), cb = copy_instr_layout(1024 / s8.bk, s8.bk, d.ldb);
-      const int64_t per_block = int64_t(s8.bm) * s8.bk / 1024;
+      const int64_t per_a = int64_t(s8.bm) * s8.bk / 1024, per_b = int64_t(s8.bn) * s8.bk / 1024;
       std::ostringstream js;
-      js << "{\"A\":{\"instr\":\"" << ca.str() << "\",\"run_bytes\":" << s8.bk << ",\"instrs_per_block\":" << per_block << "}"
-         << ",\"B\":{\"instr\":\"" << cb.str() << "\",\"run_bytes\":" << s8.bk << ",\"instrs_per_block\":" << per_block << "}}";
+      js << "{\"A\":{\"instr\":\"" << ca.str() << "\",\"run_bytes\":" << s8.bk << ",\"instrs_per_block\":" << per_a << "}"
+         << ",\"B\":{\"instr\":\"" << cb.str() << "\",\"run_bytes\":" << s8.bk << ",\"instrs_per_block\":" << per_b << "}}";
       p.copy_json = js.str();
     } catch (const la::LayoutError& e) {
       fail(err, e.what());
       return GEMM_ERR_RESOURCE;
     }
-    p.kid = lak::KID_FAST_F8;
+    p.kid = kid8;
     p.shape = s8;
     p.vec = 16;
     p.in_kind = lak::IN_F8 + 2 * (d.a_type == GEMM_F8E5M2 ? 1 : 0) + (d.b_type == GEMM_F8E5M2 ? 1 : 0);

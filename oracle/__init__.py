@@ -129,17 +129,19 @@ def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
 
-def gate_up_swiglu_f64(x_bits, w_gate_bits, w_up_bits, kind, nthreads=0):
+def gate_up_swiglu_f64(x_bits, w_gate_bits, w_up_bits, kind, nthreads=0, w_kind=None):
     """H = silu(X @ W_gate) * (X @ W_up) with silu(g) = g / (1 + exp(-g)), all in binary64.
 
     The activation composed into the gate/up epilogue (Tylo.jl "Layouts, storage
     and ownership", section "Plans describe work, callers establish readiness":
     scaling and activation become part of the epilogue).  G and U are the
     oracle's own FP64 products; the activation is applied elementwise.
+    ``w_kind`` (default ``kind``) is the weights' format when it differs from X's.
     Returns (H, G, U) as float64 arrays.
     """
-    g = gemm_f64(x_bits, kind, w_gate_bits, kind, nthreads=nthreads)
-    u = gemm_f64(x_bits, kind, w_up_bits, kind, nthreads=nthreads)
+    wk = w_kind or kind
+    g = gemm_f64(x_bits, kind, w_gate_bits, wk, nthreads=nthreads)
+    u = gemm_f64(x_bits, kind, w_up_bits, wk, nthreads=nthreads)
     with np.errstate(over="ignore"):
         h = g / (1.0 + np.exp(-g)) * u
     return h, g, u

@@ -96,6 +96,10 @@ WORKLOADS = {
         "square4096_f8", 4096, 4096, 4096, "f8e4m3", "bf16", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 1.0),
         (2201, 2202), b_kmajor=True, notes="4096^3 GEMM, E4M3 in (B stored [N, K]), bf16 out"),
+    "gate_up_f8": Workload(
+        "gate_up_f8", 4096, 11008, 4096, "f8e4m3", "bf16", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.25), (4101, 4102, 4103),
+        gate_up=True, b_kmajor=True, notes="x[4096,4096] E4M3 times W_gate and W_up stored [11008,4096] E4M3"),
     "skinny": Workload(
         "skinny", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5001, 5002, 5003),

@@ -99,11 +99,12 @@ def sample_rows(M, n, seed):
 
 def swiglu_bound(K, x, w_gate, w_up, g_ref, u_ref, h_ref, out_kind):
     """Agreement bound for silu(G) * U: each accumulator may be off by
-    e = 2^-20 K max|X| max|W|; |d silu / dg| <= 1.1, so
+    e = 2^-20 K max|X| max|W| (2^-14 for one-byte inputs); |d silu / dg| <= 1.1, so
     |dH| <= 1.1 |U| e + |silu(G)| e, plus the FP32 evaluation of the
     activation (2^-20 |H|) and the output rounding (REL |H|)."""
-    e_g = 2.0 ** -20 * K * max_abs(x) * max_abs(w_gate)
-    e_u = 2.0 ** -20 * K * max_abs(x) * max_abs(w_up)
+    e = 2.0 ** ACC_EXP[kind_of(x)]
+    e_g = e * K * max_abs(x) * max_abs(w_gate)
+    e_u = e * K * max_abs(x) * max_abs(w_up)
     with np.errstate(over="ignore"):
         silu = g_ref / (1.0 + np.exp(-g_ref))
     return 1.1 * np.abs(u_ref) * e_g + np.abs(silu) * e_u + (2.0 ** -20 + REL[out_kind]) * np.abs(h_ref)

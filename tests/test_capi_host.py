@@ -598,8 +598,7 @@ def test_one_byte_plans_shapes_and_rejections():
     for m, n, k, kw in [(256, 256, 96, {}),                      # k % 64 below 512
                         (256, 256, 520, {}),                     # k % 16
                         (256, 256, 256, {"b_kmajor": False}),    # B stored [K, N]
-                        (256, 256, 256, {"a_transposed": True}),
-                        (256, 256, 256, {"gate_up": True})]:
+                        (256, 256, 256, {"a_transposed": True})]:
         with pytest.raises(la.GemmError) as e:
             plan(m, n, k, **kw)
         assert "GEMM_ERR_UNSUPPORTED" in str(e.value)
@@ -609,3 +608,18 @@ def test_one_byte_plans_shapes_and_rejections():
         la.gemm_plan(256, 256, 256, la.F8E4M3, la.F32, b_kmajor=True, b_type=la.BF16)
     with pytest.raises(la.GemmError):      # not an output type
         la.gemm_plan(256, 256, 256, la.BF16, la.F8E4M3)
+
+
+def test_one_byte_gate_up_plans():
+    """Gate/up on one-byte X and weights: the waves-split-by-weight kernel on byte pairs, W_up's
+    block after W_gate's in each stage, every offset the written-out swizzle of n*64 + k."""
+    p = la.gemm_plan(4096, 11008, 4096, la.F8E4M3, la.BF16, gate_up=True, b_kmajor=True)
+    d = p.describe()
+    assert d["kernel"] == "fast_gate_up_f8_256x128x64" and d["tile"] == [256, 128, 64] and d["gate_up"]
+    assert d["waves_split_by_weight"] and d["in_bytes"] == 1 and d["mfma"] == "32x32x64"
+    assert d["lds_b"] == "(64,128):(1,64)"
+    for (n, k) in [(0, 0), (5, 17), (127, 63), (64, 32)]:
+        assert la.gemm_plan_lds_offset(p, 1, k, n) == 256 * 64 + _swz(n * 64 + k, 2, 4, 4)
+        assert la.gemm_plan_lds_offset(p, 2, k, n) == 256 * 64 + 128 * 64 + _swz(n * 64 + k, 2, 4, 4)
+    with pytest.raises(la.GemmError):      # weights stored [K, N]
+        la.gemm_plan(256, 256, 256, la.F8E4M3, la.BF16, gate_up=True)

@@ -5,8 +5,9 @@ product per K block of 64 codes (A [M, K], B stored [N, K]).  Cases cover every
 format pair and output type, whole tiles, M and N ending inside a tile, a K
 tail (16 and 48 codes past the last whole block, from K = 512 on), beta != 0
 on padded C rows whose padding must stay untouched, batches, the row
-reductions, the staged LDS image against the plan's one-byte map, and the
-4096^3 workload on rows covering every tile band.  The agreement bound's
+reductions, the staged LDS image against the plan's one-byte map, the
+4096^3 workload on rows covering every tile band, and the fused gate/up with
+its SwiGLU epilogue (X and weights one-byte, the formats mixed).  The agreement bound's
 accumulation term is 2^-14 K max|A| max|B| (the matrix core's measured
 precision on 64-deep one-byte products; see tests/parity.py).
 """
@@ -15,6 +16,7 @@ import pytest
 import torch
 
 import layout_algebra_amd as la
+import oracle
 import synth
 from parity import assert_close, band_rows, oracle_gemm
 
@@ -146,3 +148,39 @@ def test_square4096_f8_workload_rows():
     rows = band_rows(w.M, band=256, wave_rows=128, extra=1, seed=44)
     ref = oracle_gemm(x["A"], x["B"], w.in_kind, rows=rows)
     assert_close(C.cpu()[rows], ref, w.K, x["A"], x["B"], "bf16", "square4096_f8 rows")
+
+
+GU_CASES = [
+    # (M, N, K, x format, weight format)
+    (512, 1024, 1024, "f8e4m3", "f8e4m3"),     # whole tiles
+    (300, 520, 1040, "f8e4m3", "f8e5m2"),      # M and N edges, a K tail of 16 codes
+    (777, 261, 512, "f8e5m2", "f8e4m3"),       # odd N (weights are K-major: any N)
+]
+
+
+@pytest.mark.parametrize("case", GU_CASES, ids=[str(c) for c in GU_CASES])
+def test_one_byte_gate_up_and_swiglu(case):
+    """Fused gate/up on one-byte X and weights (both K-contiguous): G, U and silu(G) * U, bf16 out,
+    in padded rows whose padding must stay untouched."""
+    from parity import swiglu_bound
+    M, N, K, kx, kw = case
+    print("f8 gate/up", case, flush=True)
+    x = synth.normal((M, K), 61 + M, kx, 1.0)
+    wg = synth.normal((K, N), 62 + N, kw, 0.25)
+    wu = synth.normal((K, N), 63 + K, kw, 0.25)
+    ld = (N + 7) // 8 * 8 + 8
+    bufs = [torch.full((M, ld), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    G, U, H = (b[:, :N] for b in bufs)
+    plan = la.gemm_plan(M, N, K, CODE[kx], la.BF16, ldc=ld, gate_up=True, b_kmajor=True, b_type=CODE[kw])
+    assert plan.describe()["kernel"] == "fast_gate_up_f8_256x128x64", plan.describe()["kernel"]
+    X, Wg, Wu = x.to(DEV), wg.t().contiguous().to(DEV), wu.t().contiguous().to(DEV)
+    la.gemm_gate_up_run(plan, X, Wg, Wu, G, U)
+    la.gemm_gate_up_swiglu_run(plan, X, Wg, Wu, H)
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert torch.isnan(b[:, N:].float().cpu()).all(), "a store landed in the row padding"
+    h_ref, g_ref, u_ref = oracle.gate_up_swiglu_f64(synth.bits(x), synth.bits(wg), synth.bits(wu), kx, w_kind=kw)
+    assert_close(G.cpu(), g_ref, K, x, wg, "bf16", "f8 gate %s" % (case,))
+    assert_close(U.cpu(), u_ref, K, x, wu, "bf16", "f8 up %s" % (case,))
+    err = np.abs(H.cpu().double().numpy() - h_ref)
+    assert np.all(err <= swiglu_bound(K, x, wg, wu, g_ref, u_ref, h_ref, "bf16")), float(err.max())
