@@ -184,3 +184,48 @@ def test_one_byte_gate_up_and_swiglu(case):
     assert_close(U.cpu(), u_ref, K, x, wu, "bf16", "f8 up %s" % (case,))
     err = np.abs(H.cpu().double().numpy() - h_ref)
     assert np.all(err <= swiglu_bound(K, x, wg, wu, g_ref, u_ref, h_ref, "bf16")), float(err.max())
+
+
+def test_one_byte_k_zero_and_broadcast_batch():
+    """K = 0 reads neither operand (C = beta * C); a batch with B broadcast (stride 0)."""
+    M, N = 300, 264
+    c = synth.uniform((M, N), 77, "f32")
+    plan = la.gemm_plan(M, N, 0, la.F8E4M3, la.F32, b_kmajor=True, lda=16, ldb=16)
+    C = c.clone().to(DEV)
+    dummy = torch.zeros((M, 0), dtype=torch.float8_e4m3fn, device=DEV)
+    la.gemm_run(plan, dummy, torch.zeros((N, 0), dtype=torch.float8_e4m3fn, device=DEV), C, 2.0, -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), (-0.5 * c.double()).float())
+    K, batch = 1024, 3
+    a = synth.normal((batch, M, K), 78, "f8e4m3")
+    b = synth.normal((K, N), 79, "f8e4m3", 0.5)
+    plan = la.gemm_plan(M, N, K, la.F8E4M3, la.BF16, b_kmajor=True, batch=batch, stride_b=0)
+    Cb = torch.empty((batch, M, N), dtype=torch.bfloat16, device=DEV)
+    Bt = b.t().contiguous().to(DEV)
+    la.gemm_run(plan, a.to(DEV), Bt.expand(batch, N, K), Cb)
+    torch.cuda.synchronize()
+    for z in range(batch):
+        ref = oracle_gemm(a[z], b, "f8e4m3")
+        assert_close(Cb[z].cpu(), ref, K, a[z], b, "bf16", "f8 broadcast %d" % z)
+
+
+def test_one_byte_gate_up_lds_image():
+    """Stage 0 of a gate/up tile: byte lds_offset(W_up, k, n) holds W_up[k, 128 + n] of tile column 1."""
+    M, N, K = 300, 300, 512
+    x = synth.normal((M, K), 81, "f8e4m3")
+    wg = synth.normal((K, N), 82, "f8e4m3")
+    wu = synth.normal((K, N), 83, "f8e4m3")
+    plan = la.gemm_plan(M, N, K, la.F8E4M3, la.BF16, gate_up=True, b_kmajor=True, ldc=304)
+    out = torch.zeros(la.gemm_plan_lds_stage_bytes(plan), dtype=torch.uint8, device=DEV)
+    la.gemm_debug_lds_image(plan, x.to(DEV), wg.t().contiguous().to(DEV), wu.t().contiguous().to(DEV), 1, 1, out)
+    torch.cuda.synchronize()
+    img = out.cpu().numpy()
+    xb, gb, ub = synth.bits(x), synth.bits(wg), synth.bits(wu)
+    for r in range(0, 256, 5):
+        for k in range(64):
+            assert img[la.gemm_plan_lds_offset(plan, 0, r, k)] == xb[min(256 + r, M - 1), k]
+    for n in range(128):
+        col = min(128 + n, N - 1)
+        for k in range(64):
+            assert img[la.gemm_plan_lds_offset(plan, 1, k, n)] == gb[k, col]
+            assert img[la.gemm_plan_lds_offset(plan, 2, k, n)] == ub[k, col]
