@@ -29,6 +29,9 @@
 //  * Ping-pong wave groups: the 8 waves form two groups of four (one wave of
 //    each group per SIMD); while one group runs a K block's MFMAs the other
 //    reads its fragments and issues its direct loads (gemm_fast_pp_kernel).
+//  * One-byte inputs (gemm_fast_f8.hip) run the K-major configurations on
+//    byte pairs seen as 16-bit units; only the products change (mma_block,
+//    mma1: one 32x32x64 product per K block instead of two 32x32x16).
 // The LDS maps are Swizzle{AB,AM,AS} o (BM,BK):(BK,1) for A and
 // Swizzle{BB,BMb,BS} o (BK,BN):(BN,1) for B (element offsets).
 #pragma once
