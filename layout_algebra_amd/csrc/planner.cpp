@@ -705,8 +705,8 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
     return unsupported("one-byte inputs: operand rows too far apart for the kernel's 32-bit byte offsets");
   p.d = d;
   p.kd = v;
-  p.in_bytes = 1;
   if (p.kid == pair_kid) {
+    p.in_bytes = 1;
     const int kid8 = p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
     const lak::KernelShape s8 = lak::kernel_shape(kid8);
     try {
@@ -758,7 +758,7 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
     p.vec = 16;
     p.in_kind = lak::IN_F8 + 2 * (d.a_type == GEMM_F8E5M2 ? 1 : 0) + (d.b_type == GEMM_F8E5M2 ? 1 : 0);
   }
-  // (k == 0, or nothing to compute: the pair view's plan, which reads no element of A or B)
+  // (k == 0, or nothing to compute: the pair view's plan, maps and all, which reads no element of A or B)
   p.json = describe(p);
   return GEMM_OK;
 }

@@ -229,3 +229,33 @@ def test_one_byte_gate_up_lds_image():
         for k in range(64):
             assert img[la.gemm_plan_lds_offset(plan, 1, k, n)] == gb[k, col]
             assert img[la.gemm_plan_lds_offset(plan, 2, k, n)] == ub[k, col]
+
+
+def _random_f8_cases(n, seed):
+    """Seeded one-byte shapes: M, N in 1..1100, K a multiple of 64 from 64 to 1024 or of 16 from
+    512 to 1600, formats, output type and beta drawn."""
+    g = torch.Generator().manual_seed(seed)
+    draw = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    out = []
+    for _ in range(n):
+        M, N = draw(1, 1100), draw(1, 1100)
+        K = draw(1, 16) * 64 if draw(0, 1) else draw(32, 100) * 16
+        ka, kb = PAIRS[draw(0, 3)]
+        out.append((M, N, K, ka, kb, ["f32", "bf16", "f16"][draw(0, 2)], [0.0, 0.5][draw(0, 1)]))
+    return out
+
+
+RANDOM_F8 = _random_f8_cases(16, 808)
+
+
+@pytest.mark.parametrize("case", RANDOM_F8, ids=[str(c) for c in RANDOM_F8])
+def test_one_byte_random_shapes(case):
+    M, N, K, ka, kb, out_kind, beta = case
+    print("f8 random", case, flush=True)
+    a, b = inputs(M, N, K, ka, kb, 5 * M + 3 * N + K)
+    a = (a.to(torch.float32) / 4).to(synth.torch_dtype(ka))          # f16 outputs stay far from overflow
+    c = synth.uniform((M, N), M * N, "f32").to(synth.torch_dtype(out_kind)) if beta else None
+    got, d = run_f8(a, b, ka, kb, out_kind, 1.0, beta, c)
+    assert d["kernel"] == "fast_f8_256x256x64"
+    ref = oracle_gemm(a, b, ka, 1.0, beta, c.to(torch.float32) if c is not None else None, b_kind=kb)
+    assert_close(got, ref, K, a, b, out_kind, "f8 random %s" % (case,), beta=beta)
