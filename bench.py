@@ -15,6 +15,8 @@ Workloads (seeded synthetic inputs, see synth/):
   gate_up     x[4096,4096] @ W_gate, W_up [4096,11008] -> bf16
   gate_up_swiglu  the same with silu(G) * U fused into the epilogue (one output)
   skinny      16 x 28672 x 8192 bf16 -> fp32 (HBM-bound; two B buffers rotate)
+  skinny_kmajor, skinny_f8  the same with B stored [28672, 8192] (bf16, E4M3)
+  square4096_f32, square4096_f8, gate_up_f8  binary32 and one-byte inputs
   square256, ragged
   rms_norm       row normalisation of 2^20 f32 rows of 256 (HBM-bound)
   rms_norm_bf16  row normalisation of 65536 bf16 rows of 4096 (HBM-bound)
@@ -204,9 +206,9 @@ def main():
         b_cpu = x["Wg"]
     else:
         Bs = [dev_b(x["B"])]
-        if w.name == "skinny":
+        if w.name.startswith("skinny"):
             # a second B buffer so consecutive steps do not hit B in the 256 MB last-level cache
-            Bs.append(dev_b(synth.Dist("normal", 0.0, 0.02).sample((w.K, w.N), w.seeds[2], synth.torch_dtype(w.in_kind))))
+            Bs.append(dev_b(w.dist_b.sample((w.K, w.N), w.seeds[2], synth.torch_dtype(w.in_kind))))
         C0 = x["C"].to(dev) if "C" in x else None
         C = torch.empty((w.M, w.N), dtype=out_dt, device=dev) if C0 is None else C0.clone()
 
@@ -278,8 +280,8 @@ def main():
     flops = w.flops()
     value_tflops = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = ms_per_step
-    if w.name == "skinny":
-        metric, unit = "achieved HBM GB/s, skinny 16x28672x8192 GEMM", "GB/s"
+    if w.name.startswith("skinny"):
+        metric, unit = "achieved HBM GB/s, %s %dx%dx%d GEMM" % (w.name, w.M, w.N, w.K), "GB/s"
         bytes_ = algorithmic_bytes(w)
         value = bytes_ / (ms_per_step * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": bytes_ / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -705,7 +707,7 @@ def cpu_baseline(w, x, b_cpu, check, budget_s, gpu_value, unit, check_u=None):
     dt = (time.perf_counter() - t0) / reps
     flops = 2.0 * R * w.N * w.K
     if unit == "GB/s":
-        bytes_ = (R * w.K + w.K * w.N) * 2 + R * w.N * 4
+        bytes_ = (R * w.K + w.K * w.N) * IN_BYTES[w.in_kind] + R * w.N * 4
         value = bytes_ / dt / 1e9
     else:
         value = flops / dt / 1e12

@@ -13,7 +13,12 @@
 //    results discarded;
 //  * each of the 4 waves owns 32 columns: two v_mfma_f32_16x16x32 blocks per
 //    32-wide K step, A fragments as 16-byte LDS reads, B fragments through
-//    the transposing ds_read_b64_tr_b16 (B is N-contiguous);
+//    the transposing ds_read_b64_tr_b16 (B N-contiguous) or, for B stored
+//    [N, K], as 16-byte reads of its K-contiguous rows like A's (the strip is
+//    then 128 rows of B, each a 256-byte row per K block under A's swizzle);
+//  * one-byte inputs (B stored [N, K]) run the K-major kernel on byte pairs:
+//    two 16-byte reads of consecutive 32-unit steps form the 32-byte operands
+//    of one v_mfma_f32_16x16x128_f8f6f4 (A and B place K alike);
 //  * FP32 accumulators stay in registers; the epilogue applies alpha/beta
 //    and writes only rows < M.
 #include "kernel_common.hpp"
@@ -82,6 +87,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
   int tm, tn;
   grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), 1, g.tiles_n, 1, tm, tn);
   const int64_t n0 = int64_t(tn) * BN;
+  constexpr bool BKM = C::BKMAJOR;
 
   // per-lane source offsets (bytes, 32-bit) of the direct loads
   uint32_t sa[A_LOADS], sb[B_LOADS];
@@ -94,12 +100,13 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int L = swz<C::BB, C::BMb, C::BS>((wave * B_LOADS + i) * 512 + lane * 8);
-    sb[i] = uint32_t(((L / BN) * g.ldb + L % BN) * 2);
+    // B block in LDS: (k, n) at k * BN + n, or for B stored [N, K] at n * BK + k
+    sb[i] = BKM ? uint32_t(((L / BK) * g.ldb + L % BK) * 2) : uint32_t(((L / BN) * g.ldb + L % BN) * 2);
   }
   auto issue = [&](int kb, int buf) {
     const int64_t k1 = int64_t(kb) * BK;
     const uint16_t* a_blk = g.A + k1;
-    const uint16_t* b_blk = g.B + k1 * g.ldb + n0;
+    const uint16_t* b_blk = BKM ? g.B + n0 * g.ldb + k1 : g.B + k1 * g.ldb + n0;
     SK_LDS uint16_t* st = lds + buf * STAGE;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) sk_dma16<false>(a_blk, sa[i], st + (wave * A_LOADS + i) * 512);
@@ -128,18 +135,38 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
     sk_barrier();
     if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
     const SK_LDS uint16_t* st = lds + (kt % S) * STAGE;
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      const u32x4 a = *reinterpret_cast<const SK_LDS u32x4*>(st + swz<C::AB, C::AM, C::AS>(ar * BK + s * 32 + ak));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const SK_LDS uint16_t* bs = st + A_ELEMS;
+    const SK_LDS uint16_t* bs = st + A_ELEMS;
+    // one 32-wide K step: A and B fragments of lane l (8 K values from 8 (l / 16))
+    auto a_frag = [&](int s) {
+      return *reinterpret_cast<const SK_LDS u32x4*>(st + swz<C::AB, C::AM, C::AS>(ar * BK + s * 32 + ak));
+    };
+    auto b_frag = [&](int s, int j) {
+      if constexpr (BKM) {
+        return *reinterpret_cast<const SK_LDS u32x4*>(
+            bs + swz<C::BB, C::BMb, C::BS>((wave * TN + j * 16 + ar) * BK + s * 32 + ak));
+      } else {
         const i16x4_s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (SK_LDS i16x4_s*)(bs + swz<C::BB, C::BMb, C::BS>((s * 32 + bk) * BN + bn + j * 16)));
         const i16x4_s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (SK_LDS i16x4_s*)(bs + swz<C::BB, C::BMb, C::BS>((s * 32 + bk + 4) * BN + bn + j * 16)));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        acc[j] = mfma_16x16x32<TI>(a, u32x4{l2.x, l2.y, h2.x, h2.y}, acc[j]);
+        return u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    };
+    if constexpr (TI::f8) {
+      // byte pairs: steps s and s + 1 (64 units = 128 codes) form one 16x16x128 product
+#pragma unroll
+      for (int s = 0; s < BK / 32; s += 2) {
+        const u32x4 a0 = a_frag(s), a1 = a_frag(s + 1);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[j] = mfma_f8_16x16x128<TI>(a0, a1, b_frag(s, j), b_frag(s + 1, j), acc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < BK / 32; ++s) {
+        const u32x4 a = a_frag(s);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[j] = mfma_16x16x32<TI>(a, b_frag(s, j), acc[j]);
       }
     }
   }
@@ -197,34 +224,52 @@ __global__ void __launch_bounds__(256) gemm_skinny_lds_image(const TiledArgs g) 
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int L = swz<C::BB, C::BMb, C::BS>((wave * B_LOADS + i) * 512 + lane * 8);
-    sk_dma16<false>(g.B + n0, uint32_t(((L / BN) * g.ldb + L % BN) * 2), lds + A_ELEMS + (wave * B_LOADS + i) * 512);
+    const uint32_t off = C::BKMAJOR ? uint32_t(((L / BK) * g.ldb + L % BK) * 2) : uint32_t(((L / BN) * g.ldb + L % BN) * 2);
+    sk_dma16<false>(C::BKMAJOR ? g.B + n0 * g.ldb : g.B + n0, off, lds + A_ELEMS + (wave * B_LOADS + i) * 512);
   }
   sk_wait_vmcnt<0>();
   sk_barrier();
   for (int i = tid; i < STAGE; i += 256) g.dbg_out[i] = lds[i];
 }
 
-template <class TI, class TO>
+template <class C, class TI, class TO>
 hipError_t go_skinny(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
   if (img) {
-    hipLaunchKernelGGL((gemm_skinny_lds_image<TI, TO, CfgSkinny16>), dim3(1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_lds_image<TI, TO, C>), dim3(1), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_skinny_kernel<TI, TO, CfgSkinny16>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<TI, TO, C>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
+template <class C, class TI>
+hipError_t by_out(int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (out_kind == OUT_F32) return go_skinny<C, TI, OutF32>(a, grid, s, img);
+  if (out_kind == OUT_BF16) return go_skinny<C, TI, OutBF16>(a, grid, s, img);
+  if (out_kind == OUT_F16) return go_skinny<C, TI, OutF16>(a, grid, s, img);
+  return hipErrorInvalidValue;
+}
+
+template <class C>
+hipError_t by_in(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (in_kind == IN_BF16) return by_out<C, InBF16>(out_kind, a, grid, s, img);
+  if (in_kind == IN_F16) return by_out<C, InF16>(out_kind, a, grid, s, img);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
-  if (in_kind == IN_BF16) {
-    if (out_kind == OUT_F32) return go_skinny<InBF16, OutF32>(a, grid, s, img);
-    if (out_kind == OUT_BF16) return go_skinny<InBF16, OutBF16>(a, grid, s, img);
-    if (out_kind == OUT_F16) return go_skinny<InBF16, OutF16>(a, grid, s, img);
-  } else if (in_kind == IN_F16) {
-    if (out_kind == OUT_F32) return go_skinny<InF16, OutF32>(a, grid, s, img);
-    if (out_kind == OUT_BF16) return go_skinny<InF16, OutBF16>(a, grid, s, img);
-    if (out_kind == OUT_F16) return go_skinny<InF16, OutF16>(a, grid, s, img);
+hipError_t launch_skinny(int kid, int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (kid == KID_SKINNY_16) return by_in<CfgSkinny16>(in_kind, out_kind, a, grid, s, img);
+  if (kid == KID_SKINNY_16_KM) return by_in<CfgSkinny16KM>(in_kind, out_kind, a, grid, s, img);
+  if (kid == KID_SKINNY_F8) {
+    switch (in_kind - IN_F8) {
+      case 0: return by_out<CfgSkinny16KM, InF8<0, 0>>(out_kind, a, grid, s, img);
+      case 1: return by_out<CfgSkinny16KM, InF8<0, 1>>(out_kind, a, grid, s, img);
+      case 2: return by_out<CfgSkinny16KM, InF8<1, 0>>(out_kind, a, grid, s, img);
+      case 3: return by_out<CfgSkinny16KM, InF8<1, 1>>(out_kind, a, grid, s, img);
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipErrorInvalidValue;
 }

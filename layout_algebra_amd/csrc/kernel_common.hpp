@@ -61,6 +61,18 @@ __device__ __forceinline__ f32x16 mfma_f8_32x32x64(u32x4 a_lo, u32x4 a_hi, u32x4
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, TI::fmt_a, TI::fmt_b, 0, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x128_f8f6f4 on 8-bit A and B: 16x16 FP32 block += (16x128) x
+// (128x16).  Lane l holds row (A) / column (B) l % 16 and 32 K values; A and B
+// place K the same way (byte q of lane l of A meets byte q of lane l's group of
+// B), the result lane map is that of the 16x16x32 products.  Scale operands 0
+// select the unscaled form.
+template <class TI>
+__device__ __forceinline__ f32x4 mfma_f8_16x16x128(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi, f32x4 c) {
+  const i32x8 a{int(a_lo.x), int(a_lo.y), int(a_lo.z), int(a_lo.w), int(a_hi.x), int(a_hi.y), int(a_hi.z), int(a_hi.w)};
+  const i32x8 b{int(b_lo.x), int(b_lo.y), int(b_lo.z), int(b_lo.w), int(b_hi.x), int(b_hi.y), int(b_hi.z), int(b_hi.w)};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, TI::fmt_a, TI::fmt_b, 0, 0, 0, 0);
+}
+
 // v_mfma_f32_16x16x32_{bf16,f16}: lane l holds row/column l % 16 and eight
 // consecutive K values starting at 8 * (l / 16); result register r of lane l
 // is row 4*(l/16) + r, column l % 16.

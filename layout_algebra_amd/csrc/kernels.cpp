@@ -56,6 +56,20 @@ KernelShape kernel_shape(int kid) {
       return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
                          0, 1, 1, C::STAGES};
     }
+    case KID_SKINNY_16_KM: {
+      using C = CfgSkinny16KM;
+      return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
+                         1, 1, 1, C::STAGES};
+    }
+    case KID_SKINNY_F8: {
+      // the K-major skinny kernel seen in one-byte elements: 512-code (512-byte) rows under
+      // Swizzle{4,4,5} (16-byte chunks, 16 rows -> 16 slots), one 16x16x128 product per 64 units
+      using C = CfgSkinny16KM;
+      KernelShape s{16, C::BN, 2 * C::BK, 1, 1, 4, 256, 16, 16, 128, {C::AB, C::AM + 1, C::AS}, {C::BB, C::BMb + 1, C::BS},
+                    1, 1, 1, C::STAGES};
+      s.in_bytes = 1;
+      return s;
+    }
     default:
       return KernelShape{};
   }
@@ -78,7 +92,9 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_FAST_GU_KM:
     case KID_FAST_256_AT:
     case KID_FAST_GU_AT: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
-    case KID_SKINNY_16: return launch_skinny(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_SKINNY_16:
+    case KID_SKINNY_16_KM:
+    case KID_SKINNY_F8: return launch_skinny(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_FAST_F8:
     case KID_FAST_GU_F8: return launch_fast_f8(kid, in_kind, out_kind, args, grid, stream, lds_image);

@@ -58,6 +58,8 @@ enum KernelId : int {
   KID_TILED_F32 = 10,    // binary32 A and B, any shape: 128x128x32, 4 waves of 64x64, v_mfma_f32_32x32x2_f32
   KID_FAST_F8 = 11,      // one-byte A [M, K] and B [N, K]: KID_FAST_256_KM on byte pairs, 256x256x64, v_mfma_f32_32x32x64_f8f6f4
   KID_FAST_GU_F8 = 12,   // one-byte gate/up, weights [N, K]: KID_FAST_GU_KM on byte pairs
+  KID_SKINNY_16_KM = 13, // KID_SKINNY_16 for B stored [N, K]: B strips of 128 K-contiguous rows
+  KID_SKINNY_F8 = 14,    // one-byte M <= 16, B [N, K]: KID_SKINNY_16_KM on byte pairs, v_mfma_f32_16x16x128_f8f6f4
   KID_COUNT
 };
 
@@ -110,8 +112,21 @@ struct CfgFastGUAT : CfgFastGU {
 struct CfgSkinny16 {
   static constexpr int BN = 128, BK = 128, STAGES = 4;
   static constexpr bool B_NT = true;             // non-temporal B loads: +10% HBM throughput (measured)
+  static constexpr bool BKMAJOR = false;
   static constexpr int AB = 4, AM = 3, AS = 4;   // A: Swizzle{4,3,4} over 256-byte rows (16 rows -> 16 slots)
   static constexpr int BB = 3, BMb = 4, BS = 3;  // B: Swizzle{3,4,3} over 256-byte rows
+};
+// B stored [N, K]: strips of 64 B rows, each a K-contiguous 512-byte row per K block of 256,
+// read like A's (plain 16-byte reads of 16 consecutive rows) under the same swizzle; two stages
+// (80 KB) so that two workgroups share a CU.  Measured on 16 x 28672 x 8192 bf16 (one box): 128
+// rows x 256-byte rows x 4 stages 83.4 us, 128 x 512 B x 2 stages 74.4, 64 x 512 B x 4 stages
+// 73.4, x 3 stages 73.0, x 2 stages 71.0 (6.6 TB/s), 64 x 1 KB x 2 stages 77.9, 64 x 256 B x
+// 4 stages 77.3: longer runs of each row per visit and more workgroups in flight both count.
+struct CfgSkinny16KM : CfgSkinny16 {
+  static constexpr int BN = 64, BK = 256, STAGES = 2;
+  static constexpr bool BKMAJOR = true;
+  static constexpr int AB = 4, AM = 3, AS = 5;   // 512-byte rows: 16 rows -> 16 slots
+  static constexpr int BB = 4, BMb = 3, BS = 5;
 };
 
 // Fill R[0, n) with the identity of `red` (0, -inf or +inf) on `stream`: a
@@ -132,7 +147,7 @@ hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_u
                         const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
 hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid,
                        hipStream_t stream, bool lds_image);
-hipError_t launch_skinny(int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
+hipError_t launch_skinny(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                          bool lds_image);
 hipError_t launch_fast_f8(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
                           bool lds_image);

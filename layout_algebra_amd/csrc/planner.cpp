@@ -628,7 +628,7 @@ std::string describe(const gemm_plan_s& p) {
   std::ostringstream js;
   static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
                                       "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8",
-                                      "fast_gate_up_f8"};
+                                      "fast_gate_up_f8", "skinny_bkmajor", "skinny_f8"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -700,14 +700,15 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   const gemm_status st = build(v, p, err);
   if (st != GEMM_OK) return st;
   const bool runs = d.m > 0 && d.n > 0 && d.k > 0;
-  const int pair_kid = p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
+  const bool skinny = p.kid == lak::KID_SKINNY_16_KM;
+  const int pair_kid = skinny ? lak::KID_SKINNY_16_KM : p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
   if (runs && p.kid != pair_kid)
     return unsupported("one-byte inputs: operand rows too far apart for the kernel's 32-bit byte offsets");
   p.d = d;
   p.kd = v;
   if (p.kid == pair_kid) {
     p.in_bytes = 1;
-    const int kid8 = p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
+    const int kid8 = skinny ? lak::KID_SKINNY_F8 : p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
     const lak::KernelShape s8 = lak::kernel_shape(kid8);
     try {
       using la::Tree;
@@ -742,7 +743,7 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
       const int64_t Kc = (d.k + s8.bk - 1) / s8.bk * s8.bk;
       p.glob_a = la::tile(la::Layout::row_major(Mc, Kc, d.lda), {s8.bm, s8.bk});
       p.glob_b = la::tile(la::Layout::col_major(Kc, Nc, d.ldb), {s8.bk, s8.bn});
-      // a wave instruction moves 1 KiB: 16 rows of one 64-code K block row each
+      // a wave instruction moves 1 KiB: 1024 / bk rows of one K block row each
       const la::Layout ca = copy_instr_layout(1024 / s8.bk, s8.bk, d.lda), cb = copy_instr_layout(1024 / s8.bk, s8.bk, d.ldb);
       const int64_t per_a = int64_t(s8.bm) * s8.bk / 1024, per_b = int64_t(s8.bn) * s8.bk / 1024;
       std::ostringstream js;
@@ -901,13 +902,15 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // edge tiles the bar is 64 workgroups (measured: 40 edge tiles 11.1 us on
     // the general kernel against 15.0; 96 tiles 16.9 against 12.1).
     if (!large && p.kid == fk && ftm * ftn * d.batch < (whole ? 32 : 64)) p.kid = lak::KID_TILED_64;
-    // M <= 16: stream B once through the skinny kernel (HBM-bound shape).
-    const lak::KernelShape ks = lak::kernel_shape(lak::KID_SKINNY_16);
-    const bool skinny_fit = !p.gate_up && !kmajor && !atrans && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
+    // M <= 16: stream B once through the skinny kernel (HBM-bound shape); B stored [N, K] streams
+    // strips of 128 K-contiguous rows
+    const int sk = kmajor ? lak::KID_SKINNY_16_KM : lak::KID_SKINNY_16;
+    const lak::KernelShape ks = lak::kernel_shape(sk);
+    const bool skinny_fit = !p.gate_up && !atrans && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
                             d.k % ks.bk == 0 && in16 &&
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
-                            2 * int64_t(ks.bk) * d.ldb < (int64_t{1} << 32);
-    if (skinny_fit) p.kid = lak::KID_SKINNY_16;
+                            2 * int64_t(kmajor ? ks.bn : ks.bk) * d.ldb < (int64_t{1} << 32);
+    if (skinny_fit) p.kid = sk;
     // The general kernel: 64 x 64 tiles (two register sets of prefetch with
     // 16-byte loads) measured faster than 128 x 128 at every size with 16-byte
     // loads but 4000 x 4000 x 1000 (3 % slower), and with 2-byte loads up to
@@ -934,7 +937,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   const bool fast = fast_kid(p.kid);
   p.out_align_bytes = fast ? 16 : p.out_bytes;
   // The direct-load kernels need 16-byte rows (their planning checked in16 above).
-  if (fast || p.kid == lak::KID_SKINNY_16) p.align_bytes = 16;
+  if (fast || p.kid == lak::KID_SKINNY_16 || p.kid == lak::KID_SKINNY_16_KM) p.align_bytes = 16;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
   // one launch: the grid's work-items along x (tiles x threads per tile) must fit in 32 bits

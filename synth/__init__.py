@@ -104,6 +104,15 @@ WORKLOADS = {
         "skinny", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5001, 5002, 5003),
         notes="M=16 bandwidth-bound GEMM"),
+    # the same with the weights stored [N, K] (the usual storage of a linear layer's weight)
+    "skinny_kmajor": Workload(
+        "skinny_kmajor", 16, 28672, 8192, "bf16", "f32", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5101, 5102, 5103), b_kmajor=True,
+        notes="M=16 bandwidth-bound GEMM, B stored [28672, 8192]"),
+    "skinny_f8": Workload(
+        "skinny_f8", 16, 28672, 8192, "f8e4m3", "f32", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.25), (5201, 5202, 5203), b_kmajor=True,
+        notes="M=16 bandwidth-bound GEMM, E4M3 A and B, B stored [28672, 8192]"),
 }
 
 

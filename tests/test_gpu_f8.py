@@ -259,3 +259,52 @@ def test_one_byte_random_shapes(case):
     assert d["kernel"] == "fast_f8_256x256x64"
     ref = oracle_gemm(a, b, ka, 1.0, beta, c.to(torch.float32) if c is not None else None, b_kind=kb)
     assert_close(got, ref, K, a, b, out_kind, "f8 random %s" % (case,), beta=beta)
+
+
+SKINNY_F8 = [
+    # (M, N, K, A format, B format)
+    (16, 64, 512, "f8e4m3", "f8e4m3"),
+    (1, 384, 1024, "f8e4m3", "f8e5m2"),
+    (7, 1024, 2048, "f8e5m2", "f8e4m3"),
+    (13, 192, 8192, "f8e5m2", "f8e5m2"),
+]
+
+
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("case", SKINNY_F8, ids=[str(c) for c in SKINNY_F8])
+def test_one_byte_skinny(case, out_kind):
+    """M <= 16 with one-byte A and B stored [N, K]: the K-major skinny kernel on byte pairs, one
+    16x16x128 product per two 32-unit steps (64-row strips, K blocks of 512 codes)."""
+    M, N, K, ka, kb = case
+    print("f8 skinny", case, out_kind, flush=True)
+    a, b = inputs(M, N, K, ka, kb, 17 * M + N + K)
+    c = synth.uniform((M, N), M + 2 * N, "f32").to(synth.torch_dtype(out_kind))
+    got, d = run_f8(a, b, ka, kb, out_kind, 1.25, -0.5, c)
+    assert d["kernel"] == "skinny_f8_16x64x512", d["kernel"]
+    ref = oracle_gemm(a, b, ka, 1.25, -0.5, c.to(torch.float32), b_kind=kb)
+    assert_close(got, ref, K, a, b, out_kind, "f8 skinny %s" % (case,), beta=-0.5)
+
+
+def test_one_byte_skinny_workload_and_lds_image():
+    w = synth.WORKLOADS["skinny_f8"]
+    x = synth.make_inputs(w)
+    print("f8 skinny workload", flush=True)
+    plan = la.gemm_plan(w.M, w.N, w.K, la.F8E4M3, la.F32, b_kmajor=True)
+    assert plan.describe()["kernel"] == "skinny_f8_16x64x512"
+    A, Bt = x["A"].to(DEV), x["B"].t().contiguous().to(DEV)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    la.gemm_run(plan, A, Bt, C)
+    torch.cuda.synchronize()
+    ref = oracle_gemm(x["A"], x["B"], "f8e4m3")
+    assert_close(C.cpu(), ref, w.K, x["A"], x["B"], "f32", "skinny_f8 workload")
+    # stage 0 of column strip 5: byte lds_offset(B, k, n) holds B[k, 320 + n], A's rows likewise
+    out = torch.zeros(la.gemm_plan_lds_stage_bytes(plan), dtype=torch.uint8, device=DEV)
+    la.gemm_debug_lds_image(plan, A, Bt, None, 0, 5, out)
+    torch.cuda.synchronize()
+    img, ab, bb = out.cpu().numpy(), synth.bits(x["A"]), synth.bits(x["B"])
+    for r in range(16):
+        for k in range(0, 512, 7):
+            assert img[la.gemm_plan_lds_offset(plan, 0, r, k)] == ab[r, k]
+    for n in range(0, 64, 3):
+        for k in range(512):
+            assert img[la.gemm_plan_lds_offset(plan, 1, k, n)] == bb[k, 320 + n]

@@ -415,6 +415,7 @@ LDS_CASES = {
     "fast_gate_up": (512, 256, 128, "bf16", True, 1, 1, "fast_gate_up_"),
     "tiled_gate_up_edge": (300, 200, 100, "bf16", True, 2, 1, "tiled_"),
     "skinny_bf16": (16, 512, 256, "bf16", False, 0, 2, "skinny_"),
+    "skinny_bkmajor_f16": (16, 512, 256, "f16", False, 0, 3, "skinny_bkmajor_", True),
     "fast_bkmajor": (512, 512, 256, "bf16", False, 1, 1, "fast_bkmajor_", True),
     "fast_gate_up_bkmajor": (512, 256, 128, "f16", True, 1, 1, "fast_gate_up_bkmajor_", True),
     "tiled_bkmajor_edge": (300, 200, 100, "bf16", False, 2, 1, "tiled_", True),
@@ -514,6 +515,37 @@ def test_skinny_kernel_shapes(shape, in_kind, out_kind):
     got = run_gemm(a, b, out_kind, 0.5, -2.0, c)
     ref = oracle_gemm(a, b, in_kind, 0.5, -2.0, c.to(torch.float32))
     assert_close(got, ref, K, a, b, out_kind, "skinny %s" % (shape,), beta=-2.0)
+
+
+SKINNY_KM_SHAPES = [(16, 64, 256), (1, 256, 256), (7, 384, 1024), (16, 1024, 2048), (13, 192, 8192)]
+
+
+@pytest.mark.parametrize("in_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SKINNY_KM_SHAPES, ids=[str(s) for s in SKINNY_KM_SHAPES])
+def test_skinny_kernel_kmajor_b(shape, in_kind, out_kind):
+    """B stored [N, K] (a linear layer's weight): strips of 128 K-contiguous B rows."""
+    M, N, K = shape
+    plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], b_kmajor=True)
+    assert plan.describe()["kernel"].startswith("skinny_bkmajor_"), plan.describe()["kernel"]
+    seed = 13 * M + N + 3 * K
+    a = synth.normal((M, K), seed, in_kind)
+    b = synth.normal((K, N), seed + 1, in_kind, 0.05)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got = run_gemm(a, b, out_kind, -0.75, 1.5, c, b_kmajor=True)
+    ref = oracle_gemm(a, b, in_kind, -0.75, 1.5, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "skinny kmajor %s" % (shape,), beta=1.5)
+
+
+def test_skinny_kmajor_permutation_is_exact():
+    K = 512
+    a = synth.uniform((9, K), 52, "bf16")
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(53))
+    P = torch.zeros((K, K), dtype=torch.bfloat16)
+    P[perm, torch.arange(K)] = 1
+    plan = la.gemm_plan(9, K, K, la.BF16, la.F32, b_kmajor=True)
+    assert plan.describe()["kernel"].startswith("skinny_bkmajor_")
+    assert torch.equal(run_gemm(a, P, "f32", b_kmajor=True), a.to(torch.float32)[:, perm])
 
 
 def test_skinny_identity_is_exact():
