@@ -524,7 +524,7 @@ SKINNY_KM_SHAPES = [(16, 64, 256), (1, 256, 256), (7, 384, 1024), (16, 1024, 204
 @pytest.mark.parametrize("out_kind", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", SKINNY_KM_SHAPES, ids=[str(s) for s in SKINNY_KM_SHAPES])
 def test_skinny_kernel_kmajor_b(shape, in_kind, out_kind):
-    """B stored [N, K] (a linear layer's weight): strips of 128 K-contiguous B rows."""
+    """B stored [N, K] (a linear layer's weight): strips of 64 K-contiguous B rows."""
     M, N, K = shape
     plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], b_kmajor=True)
     assert plan.describe()["kernel"].startswith("skinny_bkmajor_"), plan.describe()["kernel"]
@@ -583,7 +583,7 @@ def test_gate_up_swiglu(shape):
 
 
 KM_SHAPES = [((256, 256, 64), "fast_bkmajor_"), ((512, 768, 320), "fast_bkmajor_"), ((33, 65, 17), "tiled_"),
-             ((1000, 1537, 999), "tiled_"), ((16, 1024, 2048), "tiled_"), ((256, 1024, 4096), "fast_bkmajor_")]
+             ((1000, 1537, 999), "tiled_"), ((17, 1024, 2048), "tiled_"), ((256, 1024, 4096), "fast_bkmajor_")]
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
