@@ -71,8 +71,8 @@ __device__ __forceinline__ void sk_dma16(const uint16_t* base, uint32_t voff, co
 template <class TI, class TO, class C>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) {
   const TiledArgs g = at_batch(g_in);
-  constexpr int BM = 16, BN = C::BN, BK = C::BK, S = C::STAGES;
-  constexpr int NW = 4;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES;
+  constexpr int NW = 4, FM = BM / 16;
   constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
   constexpr int A_LOADS = A_ELEMS / 512 / NW, B_LOADS = B_ELEMS / 512 / NW;
   constexpr int LPS = A_LOADS + B_LOADS;
@@ -114,10 +114,12 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
     for (int i = 0; i < B_LOADS; ++i) sk_dma16<C::B_NT>(b_blk, sb[i], st + A_ELEMS + (wave * B_LOADS + i) * 512);
   };
 
-  f32x4 acc[FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) acc[j] = f32x4{};
-  const int ar = lane & 15, ak = (lane >> 4) * 8;          // A: row l % 16, 8 K values from 8 (l / 16)
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
+  const int ar = lane & 15, ak = (lane >> 4) * 8;          // A: row l % 16 of each 16-row block, 8 K values from 8 (l / 16)
   const int g4 = lane >> 4;
   const int bk = 8 * g4 + ((lane >> 2) & 3);              // B: K row this lane addresses
   const int bn = wave * TN + 4 * (lane & 3);               // B: first of its 4 N values
@@ -137,8 +139,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
     const SK_LDS uint16_t* st = lds + (kt % S) * STAGE;
     const SK_LDS uint16_t* bs = st + A_ELEMS;
     // one 32-wide K step: A and B fragments of lane l (8 K values from 8 (l / 16))
-    auto a_frag = [&](int s) {
-      return *reinterpret_cast<const SK_LDS u32x4*>(st + swz<C::AB, C::AM, C::AS>(ar * BK + s * 32 + ak));
+    auto a_frag = [&](int s, int i) {
+      return *reinterpret_cast<const SK_LDS u32x4*>(st + swz<C::AB, C::AM, C::AS>((16 * i + ar) * BK + s * 32 + ak));
     };
     auto b_frag = [&](int s, int j) {
       if constexpr (BKM) {
@@ -157,57 +159,69 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const TiledArgs g_in) 
       // byte pairs: steps s and s + 1 (64 units = 128 codes) form one 16x16x128 product
 #pragma unroll
       for (int s = 0; s < BK / 32; s += 2) {
-        const u32x4 a0 = a_frag(s), a1 = a_frag(s + 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[j] = mfma_f8_16x16x128<TI>(a0, a1, b_frag(s, j), b_frag(s + 1, j), acc[j]);
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 b0 = b_frag(s, j), b1 = b_frag(s + 1, j);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j] = mfma_f8_16x16x128<TI>(a_frag(s, i), a_frag(s + 1, i), b0, b1, acc[i][j]);
+        }
       }
     } else {
 #pragma unroll
       for (int s = 0; s < BK / 32; ++s) {
-        const u32x4 a = a_frag(s);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[j] = mfma_16x16x32<TI>(a, b_frag(s, j), acc[j]);
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 b = b_frag(s, j);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j] = mfma_16x16x32<TI>(a_frag(s, i), b, acc[i][j]);
+        }
       }
     }
   }
 
-  // 16x16 result lane map: register r of lane l is row 4 (l / 16) + r, column l % 16.
+  // 16x16 result lane map: register r of lane l is row 4 (l / 16) + r, column l % 16 of its block.
   typedef typename TO::storage St;
   St* Cp = static_cast<St*>(g.C);
   const int red = g.red;
-  float part[4];
+  float part[FM][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) part[r] = red_identity(red);
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[i][r] = red_identity(red);
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int64_t col = n0 + wave * TN + j * 16 + (lane & 15);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = 4 * (lane >> 4) + r;
-      if (row < g.M) {
-        const int64_t idx = row * g.ldc + col;
-        float v = g.alpha * acc[j][r];
-        if (g.beta != 0.0f) v += g.beta * from_out<TO>(Cp[idx]);
-        Cp[idx] = to_out<TO>(v);
-        if (red != RED_NONE) part[r] = red_combine(red, part[r], v);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = 16 * i + 4 * (lane >> 4) + r;
+        if (row < g.M) {
+          const int64_t idx = row * g.ldc + col;
+          float v = g.alpha * acc[i][j][r];
+          if (g.beta != 0.0f) v += g.beta * from_out<TO>(Cp[idx]);
+          Cp[idx] = to_out<TO>(v);
+          if (red != RED_NONE) part[i][r] = red_combine(red, part[i][r], v);
+        }
       }
-    }
   }
   if (red != RED_NONE) {
     // the 16 lanes of a row group hold its 16 columns of each j block
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = red_lanes<16>(red, part[r]);
-      const int64_t row = 4 * (lane >> 4) + r;
-      if ((lane & 15) == 0 && row < g.M) red_commit(red, g.R + row, p);
-    }
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = red_lanes<16>(red, part[i][r]);
+        const int64_t row = 16 * i + 4 * (lane >> 4) + r;
+        if ((lane & 15) == 0 && row < g.M) red_commit(red, g.R + row, p);
+      }
   }
 }
 
 // Debug: K block 0 of column strip dbg_tn, staged by the kernel's own code.
 template <class TI, class TO, class C>
 __global__ void __launch_bounds__(256) gemm_skinny_lds_image(const TiledArgs g) {
-  constexpr int BM = 16, BN = C::BN, BK = C::BK, NW = 4;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NW = 4;
   constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
   constexpr int A_LOADS = A_ELEMS / 512 / NW, B_LOADS = B_ELEMS / 512 / NW;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[STAGE];
@@ -257,21 +271,35 @@ hipError_t by_in(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipSt
   return hipErrorInvalidValue;
 }
 
+template <class C>
+hipError_t by_formats(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  switch (in_kind - IN_F8) {
+    case 0: return by_out<C, InF8<0, 0>>(out_kind, a, grid, s, img);
+    case 1: return by_out<C, InF8<0, 1>>(out_kind, a, grid, s, img);
+    case 2: return by_out<C, InF8<1, 0>>(out_kind, a, grid, s, img);
+    case 3: return by_out<C, InF8<1, 1>>(out_kind, a, grid, s, img);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_skinny(int kid, int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
-  if (kid == KID_SKINNY_16) return by_in<CfgSkinny16>(in_kind, out_kind, a, grid, s, img);
-  if (kid == KID_SKINNY_16_KM) return by_in<CfgSkinny16KM>(in_kind, out_kind, a, grid, s, img);
-  if (kid == KID_SKINNY_F8) {
-    switch (in_kind - IN_F8) {
-      case 0: return by_out<CfgSkinny16KM, InF8<0, 0>>(out_kind, a, grid, s, img);
-      case 1: return by_out<CfgSkinny16KM, InF8<0, 1>>(out_kind, a, grid, s, img);
-      case 2: return by_out<CfgSkinny16KM, InF8<1, 0>>(out_kind, a, grid, s, img);
-      case 3: return by_out<CfgSkinny16KM, InF8<1, 1>>(out_kind, a, grid, s, img);
-      default: return hipErrorInvalidValue;
-    }
+  switch (kid) {
+    case KID_SKINNY_16: return by_in<CfgSkinny16>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_32: return by_in<CfgSkinny32>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_64: return by_in<CfgSkinny64>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_16_KM: return by_in<CfgSkinny16KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_32_KM: return by_in<CfgSkinny32KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_64_KM: return by_in<CfgSkinny64KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_F8: return by_formats<CfgSkinny16KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_F8_32: return by_formats<CfgSkinny32KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_F8_64: return by_formats<CfgSkinny64KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_128: return by_in<CfgSkinny128>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_128_KM: return by_in<CfgSkinny128KM>(in_kind, out_kind, a, grid, s, img);
+    case KID_SKINNY_F8_128: return by_formats<CfgSkinny128KM>(in_kind, out_kind, a, grid, s, img);
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace lak

@@ -13,6 +13,23 @@ static KernelShape fast_shape() {
   return s;
 }
 
+// The skinny kernels (M <= BM rows, one strip of BN columns per workgroup).  One-byte inputs run
+// the K-major configurations on byte pairs: K blocks of 2 BK codes, the swizzle's chunk field one
+// bit higher (16-byte chunks of codes), one 16x16x128 product per two 32-unit steps.
+template <class C>
+static KernelShape skinny_shape(bool one_byte) {
+  KernelShape s{C::BM, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
+                C::BKMAJOR ? 1 : 0, 1, 1, C::STAGES};
+  if (one_byte) {
+    s.bk = 2 * C::BK;
+    s.mfma_k = 128;
+    s.sw_a[1] += 1;
+    s.sw_b[1] += 1;
+    s.in_bytes = 1;
+  }
+  return s;
+}
+
 KernelShape kernel_shape(int kid) {
   switch (kid) {
     case KID_TILED_128:
@@ -51,25 +68,18 @@ KernelShape kernel_shape(int kid) {
       s.in_bytes = 1;
       return s;
     }
-    case KID_SKINNY_16: {
-      using C = CfgSkinny16;
-      return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
-                         0, 1, 1, C::STAGES};
-    }
-    case KID_SKINNY_16_KM: {
-      using C = CfgSkinny16KM;
-      return KernelShape{16, C::BN, C::BK, 1, 1, 4, 256, 16, 16, 32, {C::AB, C::AM, C::AS}, {C::BB, C::BMb, C::BS},
-                         1, 1, 1, C::STAGES};
-    }
-    case KID_SKINNY_F8: {
-      // the K-major skinny kernel seen in one-byte elements: 512-code (512-byte) rows under
-      // Swizzle{4,4,5} (16-byte chunks, 16 rows -> 16 slots), one 16x16x128 product per 64 units
-      using C = CfgSkinny16KM;
-      KernelShape s{16, C::BN, 2 * C::BK, 1, 1, 4, 256, 16, 16, 128, {C::AB, C::AM + 1, C::AS}, {C::BB, C::BMb + 1, C::BS},
-                    1, 1, 1, C::STAGES};
-      s.in_bytes = 1;
-      return s;
-    }
+    case KID_SKINNY_16: return skinny_shape<CfgSkinny16>(false);
+    case KID_SKINNY_32: return skinny_shape<CfgSkinny32>(false);
+    case KID_SKINNY_64: return skinny_shape<CfgSkinny64>(false);
+    case KID_SKINNY_16_KM: return skinny_shape<CfgSkinny16KM>(false);
+    case KID_SKINNY_32_KM: return skinny_shape<CfgSkinny32KM>(false);
+    case KID_SKINNY_64_KM: return skinny_shape<CfgSkinny64KM>(false);
+    case KID_SKINNY_F8: return skinny_shape<CfgSkinny16KM>(true);
+    case KID_SKINNY_F8_32: return skinny_shape<CfgSkinny32KM>(true);
+    case KID_SKINNY_F8_64: return skinny_shape<CfgSkinny64KM>(true);
+    case KID_SKINNY_128: return skinny_shape<CfgSkinny128>(false);
+    case KID_SKINNY_128_KM: return skinny_shape<CfgSkinny128KM>(false);
+    case KID_SKINNY_F8_128: return skinny_shape<CfgSkinny128KM>(true);
     default:
       return KernelShape{};
   }
@@ -93,8 +103,17 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_FAST_256_AT:
     case KID_FAST_GU_AT: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_SKINNY_16:
+    case KID_SKINNY_32:
+    case KID_SKINNY_64:
     case KID_SKINNY_16_KM:
-    case KID_SKINNY_F8: return launch_skinny(kid, in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_SKINNY_32_KM:
+    case KID_SKINNY_64_KM:
+    case KID_SKINNY_F8:
+    case KID_SKINNY_F8_32:
+    case KID_SKINNY_F8_64:
+    case KID_SKINNY_128:
+    case KID_SKINNY_128_KM:
+    case KID_SKINNY_F8_128: return launch_skinny(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_FAST_F8:
     case KID_FAST_GU_F8: return launch_fast_f8(kid, in_kind, out_kind, args, grid, stream, lds_image);

@@ -60,6 +60,15 @@ enum KernelId : int {
   KID_FAST_GU_F8 = 12,   // one-byte gate/up, weights [N, K]: KID_FAST_GU_KM on byte pairs
   KID_SKINNY_16_KM = 13, // KID_SKINNY_16 for B stored [N, K]: B strips of 128 K-contiguous rows
   KID_SKINNY_F8 = 14,    // one-byte M <= 16, B [N, K]: KID_SKINNY_16_KM on byte pairs, v_mfma_f32_16x16x128_f8f6f4
+  KID_SKINNY_32 = 15,    // KID_SKINNY_16 with 32 rows of A (M <= 32)
+  KID_SKINNY_64 = 16,    // ... 64 rows (M <= 64)
+  KID_SKINNY_32_KM = 17, // KID_SKINNY_16_KM with 32 rows of A
+  KID_SKINNY_64_KM = 18, // ... 64 rows
+  KID_SKINNY_F8_32 = 19, // KID_SKINNY_32_KM on byte pairs
+  KID_SKINNY_F8_64 = 20, // KID_SKINNY_64_KM on byte pairs
+  KID_SKINNY_128 = 21,   // KID_SKINNY_16 with 128 rows of A (M <= 128)
+  KID_SKINNY_128_KM = 22,// KID_SKINNY_16_KM with 128 rows of A
+  KID_SKINNY_F8_128 = 23,// KID_SKINNY_128_KM on byte pairs
   KID_COUNT
 };
 
@@ -110,7 +119,7 @@ struct CfgFastGUAT : CfgFastGU {
 };
 
 struct CfgSkinny16 {
-  static constexpr int BN = 128, BK = 128, STAGES = 4;
+  static constexpr int BM = 16, BN = 128, BK = 128, STAGES = 4;
   static constexpr bool B_NT = true;             // non-temporal B loads: +10% HBM throughput (measured)
   static constexpr bool BKMAJOR = false;
   static constexpr int AB = 4, AM = 3, AS = 4;   // A: Swizzle{4,3,4} over 256-byte rows (16 rows -> 16 slots)
@@ -127,6 +136,40 @@ struct CfgSkinny16KM : CfgSkinny16 {
   static constexpr bool BKMAJOR = true;
   static constexpr int AB = 4, AM = 3, AS = 5;   // 512-byte rows: 16 rows -> 16 slots
   static constexpr int BB = 4, BMb = 3, BS = 5;
+};
+// 32 and 64 rows of A (M <= 32, M <= 64: batches of a few dozen rows), each wave holding two or
+// four 16-row blocks per 16 columns.  Measured on M x 28672 x 8192 bf16 against the general kernel
+// these shapes took before (one box): M = 32 B [K, N] 78.7 us (3 stages; 4 stages 79.1) against
+// 105.9, B [N, K] 78.5 us (64-row strips, K blocks of 128, 3 stages, 72 KB) against 104.4 (512-byte
+// rows, 2 stages: 83.9); M = 64 B [K, N] 85.9 against 116.6, B [N, K] 91.3 (K blocks of 128, 2
+// stages, 64 KB; 256-deep blocks 94.0, 128-row strips 93.5) against 106.4.
+struct CfgSkinny32 : CfgSkinny16 {
+  static constexpr int BM = 32, STAGES = 3;      // 120 KB
+};
+struct CfgSkinny64 : CfgSkinny16 {
+  static constexpr int BM = 64, STAGES = 3;      // 144 KB
+};
+struct CfgSkinny32KM : CfgSkinny16KM {
+  static constexpr int BM = 32, BK = 128, STAGES = 3;   // 72 KB: two workgroups per CU
+  static constexpr int AS = 4, BS = 4;           // 256-byte rows
+};
+struct CfgSkinny64KM : CfgSkinny16KM {
+  static constexpr int BM = 64, BK = 128, STAGES = 2;   // 64 KB: two workgroups per CU
+  static constexpr int AS = 4, BS = 4;
+};
+// 128 rows of A: 128-column strips, K blocks of 64 (128-byte rows: Swizzle{3,3,4}, rows 2k and
+// 2k+1 share a 256-byte window), 4 stages (128 KB).  Measured on 128 x 28672 x 8192 bf16 (one box):
+// B [K, N] 97.9 us (3 stages 102.0; K blocks of 128, 2 stages 109.0) against 188.4 on the general
+// kernel; B [N, K] 104.8 us (3 stages 106.4; 64-column strips with K blocks of 128, 3 stages 129.9)
+// against 148.8.
+struct CfgSkinny128 : CfgSkinny16 {
+  static constexpr int BM = 128, BK = 64, STAGES = 4;
+  static constexpr int AB = 3, AM = 3, AS = 4;
+};
+struct CfgSkinny128KM : CfgSkinny16KM {
+  static constexpr int BM = 128, BN = 128, BK = 64, STAGES = 4;
+  static constexpr int AB = 3, AM = 3, AS = 4;
+  static constexpr int BB = 3, BMb = 3, BS = 4;
 };
 
 // Fill R[0, n) with the identity of `red` (0, -inf or +inf) on `stream`: a

@@ -72,6 +72,13 @@ bool fast_kid(int kid) {
          kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8 || kid == lak::KID_FAST_GU_F8;
 }
 
+bool skinny_kid(int kid) {
+  return kid == lak::KID_SKINNY_16 || kid == lak::KID_SKINNY_32 || kid == lak::KID_SKINNY_64 ||
+         kid == lak::KID_SKINNY_16_KM || kid == lak::KID_SKINNY_32_KM || kid == lak::KID_SKINNY_64_KM ||
+         kid == lak::KID_SKINNY_F8 || kid == lak::KID_SKINNY_F8_32 || kid == lak::KID_SKINNY_F8_64 ||
+         kid == lak::KID_SKINNY_128 || kid == lak::KID_SKINNY_128_KM || kid == lak::KID_SKINNY_F8_128;
+}
+
 bool fail(std::string* err, const std::string& msg) {
   if (err) *err = msg;
   return false;
@@ -544,11 +551,12 @@ std::vector<Store> store_plan(const gemm_plan_s& p) {
             for (int l = 0; l < 64; ++l)
               out.push_back(Store{ins, l, wm * tm + 32 * i + 4 * (l / 32) + 8 * (e / 4) + e % 4, wn * tn + 32 * j + l % 32, 1});
     } else {
-      // 16 x 16 accumulator lane map
+      // 16 x 16 accumulator lane map, 16-row blocks i of the wave's rows
       for (int j = 0; j < tn / 16; ++j)
-        for (int r = 0; r < 4; ++r, ++ins)
-          for (int l = 0; l < 64; ++l)
-            out.push_back(Store{ins, l, wm * tm + 4 * (l / 16) + r, wn * tn + 16 * j + l % 16, 1});
+        for (int i = 0; i < tm / 16; ++i)
+          for (int r = 0; r < 4; ++r, ++ins)
+            for (int l = 0; l < 64; ++l)
+              out.push_back(Store{ins, l, wm * tm + 16 * i + 4 * (l / 16) + r, wn * tn + 16 * j + l % 16, 1});
     }
   }
   return out;
@@ -628,7 +636,9 @@ std::string describe(const gemm_plan_s& p) {
   std::ostringstream js;
   static const char* const kNames[] = {"tiled", "fast", "fast_gate_up", "skinny", "fast_bkmajor", "fast_gate_up_bkmajor", "tiled",
                                       "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8",
-                                      "fast_gate_up_f8", "skinny_bkmajor", "skinny_f8"};
+                                      "fast_gate_up_f8", "skinny_bkmajor", "skinny_f8", "skinny", "skinny",
+                                      "skinny_bkmajor", "skinny_bkmajor", "skinny_f8", "skinny_f8", "skinny",
+                                      "skinny_bkmajor", "skinny_f8"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -700,15 +710,19 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   const gemm_status st = build(v, p, err);
   if (st != GEMM_OK) return st;
   const bool runs = d.m > 0 && d.n > 0 && d.k > 0;
-  const bool skinny = p.kid == lak::KID_SKINNY_16_KM;
-  const int pair_kid = skinny ? lak::KID_SKINNY_16_KM : p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
+  // the pair view's kernel and its one-byte counterpart
+  int pair_kid = p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
+  int kid8 = p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
+  if (p.kid == lak::KID_SKINNY_16_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8;
+  if (p.kid == lak::KID_SKINNY_32_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_32;
+  if (p.kid == lak::KID_SKINNY_64_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_64;
+  if (p.kid == lak::KID_SKINNY_128_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_128;
   if (runs && p.kid != pair_kid)
     return unsupported("one-byte inputs: operand rows too far apart for the kernel's 32-bit byte offsets");
   p.d = d;
   p.kd = v;
   if (p.kid == pair_kid) {
     p.in_bytes = 1;
-    const int kid8 = skinny ? lak::KID_SKINNY_F8 : p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
     const lak::KernelShape s8 = lak::kernel_shape(kid8);
     try {
       using la::Tree;
@@ -902,11 +916,18 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // edge tiles the bar is 64 workgroups (measured: 40 edge tiles 11.1 us on
     // the general kernel against 15.0; 96 tiles 16.9 against 12.1).
     if (!large && p.kid == fk && ftm * ftn * d.batch < (whole ? 32 : 64)) p.kid = lak::KID_TILED_64;
-    // M <= 16: stream B once through the skinny kernel (HBM-bound shape); B stored [N, K] streams
-    // strips of 128 K-contiguous rows
-    const int sk = kmajor ? lak::KID_SKINNY_16_KM : lak::KID_SKINNY_16;
+    // M <= 128: stream B once through the skinny kernel with 16, 32, 64 or 128 rows of A
+    // (HBM-bound shapes); B stored [N, K] streams strips of K-contiguous rows.  With more than 32
+    // rows only on grids of at least 128 strips: measured ahead of the general kernel on 28672 x
+    // 8192 operands (224 or 448 strips), level with or behind it on 4096 x 14336 (32 or 64 strips),
+    // where a strip's K loop is long and most CUs idle; with 32 rows ahead on both.
+    const int sk = d.m <= 16 ? (kmajor ? lak::KID_SKINNY_16_KM : lak::KID_SKINNY_16)
+                 : d.m <= 32 ? (kmajor ? lak::KID_SKINNY_32_KM : lak::KID_SKINNY_32)
+                 : d.m <= 64 ? (kmajor ? lak::KID_SKINNY_64_KM : lak::KID_SKINNY_64)
+                             : (kmajor ? lak::KID_SKINNY_128_KM : lak::KID_SKINNY_128);
     const lak::KernelShape ks = lak::kernel_shape(sk);
-    const bool skinny_fit = !p.gate_up && !atrans && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
+    const bool wide = d.m <= 32 || (d.n / ks.bn) * d.batch >= 128;
+    const bool skinny_fit = !p.gate_up && !atrans && wide && d.m >= 1 && d.m <= ks.bm && d.n % ks.bn == 0 && d.k > 0 &&
                             d.k % ks.bk == 0 && in16 &&
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(kmajor ? ks.bn : ks.bk) * d.ldb < (int64_t{1} << 32);
@@ -937,7 +958,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   const bool fast = fast_kid(p.kid);
   p.out_align_bytes = fast ? 16 : p.out_bytes;
   // The direct-load kernels need 16-byte rows (their planning checked in16 above).
-  if (fast || p.kid == lak::KID_SKINNY_16 || p.kid == lak::KID_SKINNY_16_KM) p.align_bytes = 16;
+  if (fast || skinny_kid(p.kid)) p.align_bytes = 16;
   p.tiles_m = static_cast<int>((d.m + s.bm - 1) / s.bm);
   p.tiles_n = static_cast<int>((d.n + s.bn - 1) / s.bn);
   // one launch: the grid's work-items along x (tiles x threads per tile) must fit in 32 bits

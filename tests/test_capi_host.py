@@ -284,6 +284,25 @@ def test_invalid_requests_are_rejected():
     assert la.gemm_plan_describe(la.gemm_plan(256 * 4096, 256 * 2047, 64, la.BF16, la.BF16))["kernel"].startswith("fast")
 
 
+def test_skinny_rows_and_grid_guard():
+    """M <= 32 always streams B through the skinny kernel; 33 <= M <= 128 only on grids of at
+    least 128 column strips (64-column strips for B stored [N, K] up to 64 rows, else 128)."""
+    def kern(m, n, k, km=False, t=la.BF16):
+        return la.gemm_plan(m, n, k, t, la.F32, b_kmajor=km).describe()["kernel"]
+    assert kern(32, 4096, 14336).startswith("skinny_32x128x")
+    assert kern(32, 4096, 14336, True).startswith("skinny_bkmajor_32x64x")
+    assert kern(64, 4096, 14336).startswith("tiled_64x64")
+    assert kern(64, 4096, 14336, True).startswith("tiled_64x64")
+    assert kern(64, 8192, 4096, True).startswith("skinny_bkmajor_64x64x")    # 128 strips
+    assert kern(64, 8192, 4096).startswith("tiled_64x64")                   # 64 strips
+    assert kern(64, 16384, 4096).startswith("skinny_64x128x")
+    assert kern(65, 28672, 8192).startswith("skinny_128x128x64")
+    assert kern(128, 28672, 8192, True).startswith("skinny_bkmajor_128x128x64")
+    assert kern(128, 28672, 8192, True, la.F8E4M3).startswith("skinny_f8_128x128x128")
+    assert kern(129, 28672, 8192).startswith("tiled_64x64")
+    assert kern(128, 28672, 8160).startswith("tiled_")                      # K not a multiple of 64
+
+
 def test_small_grids_take_64x64_tiles_unless_pinned():
     """Kernel choice by grid size: a grid that would leave most of the 256 CUs idle moves to
     64 x 64 tiles of the general kernel; GEMM_FLAG_LARGE_TILES keeps the largest tile."""

@@ -267,20 +267,25 @@ SKINNY_F8 = [
     (1, 384, 1024, "f8e4m3", "f8e5m2"),
     (7, 1024, 2048, "f8e5m2", "f8e4m3"),
     (13, 192, 8192, "f8e5m2", "f8e5m2"),
+    (20, 128, 512, "f8e4m3", "f8e4m3"),     # 32 rows of A
+    (40, 8192, 1024, "f8e4m3", "f8e5m2"),   # 64 rows of A (from 33 rows on: 128 strips or more)
+    (64, 8192, 256, "f8e5m2", "f8e4m3"),
+    (100, 16384, 512, "f8e4m3", "f8e4m3"),  # 128 rows of A
 ]
 
 
 @pytest.mark.parametrize("out_kind", ["f32", "bf16"])
 @pytest.mark.parametrize("case", SKINNY_F8, ids=[str(c) for c in SKINNY_F8])
 def test_one_byte_skinny(case, out_kind):
-    """M <= 16 with one-byte A and B stored [N, K]: the K-major skinny kernel on byte pairs, one
-    16x16x128 product per two 32-unit steps (64-row strips, K blocks of 512 codes)."""
+    """M <= 128 with one-byte A and B stored [N, K]: the K-major skinny kernel on byte pairs, one
+    16x16x128 product per two 32-unit steps."""
     M, N, K, ka, kb = case
     print("f8 skinny", case, out_kind, flush=True)
     a, b = inputs(M, N, K, ka, kb, 17 * M + N + K)
     c = synth.uniform((M, N), M + 2 * N, "f32").to(synth.torch_dtype(out_kind))
     got, d = run_f8(a, b, ka, kb, out_kind, 1.25, -0.5, c)
-    assert d["kernel"] == "skinny_f8_16x64x512", d["kernel"]
+    assert d["kernel"].startswith(("skinny_f8_%dx64x" % (16 if M <= 16 else 32 if M <= 32 else 64)) if M <= 64
+                                  else "skinny_f8_128x128x"), d["kernel"]
     ref = oracle_gemm(a, b, ka, 1.25, -0.5, c.to(torch.float32), b_kind=kb)
     assert_close(got, ref, K, a, b, out_kind, "f8 skinny %s" % (case,), beta=-0.5)
 

@@ -416,6 +416,10 @@ LDS_CASES = {
     "tiled_gate_up_edge": (300, 200, 100, "bf16", True, 2, 1, "tiled_"),
     "skinny_bf16": (16, 512, 256, "bf16", False, 0, 2, "skinny_"),
     "skinny_bkmajor_f16": (16, 512, 256, "f16", False, 0, 3, "skinny_bkmajor_", True),
+    "skinny_64_bf16": (64, 16384, 256, "bf16", False, 0, 2, "skinny_64x"),
+    "skinny_128_bf16": (128, 16384, 256, "bf16", False, 0, 7, "skinny_128x"),
+    "skinny_bkmajor_128_f16": (128, 16384, 256, "f16", False, 0, 9, "skinny_bkmajor_128x", True),
+    "skinny_bkmajor_32_f16": (32, 512, 256, "f16", False, 0, 5, "skinny_bkmajor_32x", True),
     "fast_bkmajor": (512, 512, 256, "bf16", False, 1, 1, "fast_bkmajor_", True),
     "fast_gate_up_bkmajor": (512, 256, 128, "f16", True, 1, 1, "fast_gate_up_bkmajor_", True),
     "tiled_bkmajor_edge": (300, 200, 100, "bf16", False, 2, 1, "tiled_", True),
@@ -537,6 +541,30 @@ def test_skinny_kernel_kmajor_b(shape, in_kind, out_kind):
     assert_close(got, ref, K, a, b, out_kind, "skinny kmajor %s" % (shape,), beta=1.5)
 
 
+# more than 32 rows of A plan the skinny kernel on grids of at least 128 column strips only
+SKINNY_MID_SHAPES = [(17, 256, 256), (32, 384, 1024), (32, 4096, 2048), (33, 16384, 512), (48, 16384, 1024),
+                     (64, 16384, 256), (65, 16384, 512), (100, 16384, 256), (128, 16384, 1024)]
+
+
+@pytest.mark.parametrize("km", [False, True], ids=["kn", "nk"])
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SKINNY_MID_SHAPES, ids=[str(s) for s in SKINNY_MID_SHAPES])
+def test_skinny_kernel_32_to_128_rows(shape, out_kind, km):
+    """17 <= M <= 128: the skinny kernel with 32, 64 or 128 rows of A (rows past M read row M - 1
+    and are not stored), both storages of B."""
+    M, N, K = shape
+    plan = la.gemm_plan(M, N, K, la.BF16, CODE[out_kind], b_kmajor=km)
+    want = "skinny_%s%dx" % ("bkmajor_" if km else "", 32 if M <= 32 else 64 if M <= 64 else 128)
+    assert plan.describe()["kernel"].startswith(want), plan.describe()["kernel"]
+    seed = 19 * M + N + 5 * K
+    a = synth.normal((M, K), seed, "bf16")
+    b = synth.normal((K, N), seed + 1, "bf16", 0.05)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got = run_gemm(a, b, out_kind, 1.5, -0.25, c, b_kmajor=km)
+    ref = oracle_gemm(a, b, "bf16", 1.5, -0.25, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "skinny %s %s" % (shape, km), beta=-0.25)
+
+
 def test_skinny_kmajor_permutation_is_exact():
     K = 512
     a = synth.uniform((9, K), 52, "bf16")
@@ -583,7 +611,7 @@ def test_gate_up_swiglu(shape):
 
 
 KM_SHAPES = [((256, 256, 64), "fast_bkmajor_"), ((512, 768, 320), "fast_bkmajor_"), ((33, 65, 17), "tiled_"),
-             ((1000, 1537, 999), "tiled_"), ((17, 1024, 2048), "tiled_"), ((256, 1024, 4096), "fast_bkmajor_")]
+             ((1000, 1537, 999), "tiled_"), ((65, 1024, 2048), "tiled_"), ((256, 1024, 4096), "fast_bkmajor_")]
 
 
 @pytest.mark.parametrize("in_kind", ["bf16", "f16"])
