@@ -148,6 +148,33 @@ void gemm_plan_destroy(gemm_plan_t plan);
 gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
                      float alpha, float beta, void* stream);
 
+/* Bytes of device workspace gemm_run_split needs for this plan: split * m * n * 4
+ * (the FP32 partial products), 0 when the plan has no split form. */
+gemm_status gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out_bytes);
+
+/* gemm_run with the sum over k cut into `split` equal ranges (gemm_plan_describe:
+ * "split_k", "split_kernel", "split_grid", "workspace_bytes").  The result is the
+ * same C = alpha * A * B + beta * C (the epilogue of the Phobos page "Tiles
+ * and shared memory", section "var and let") with the sum over k grouped by
+ * range: the accumulator is built from K slices of A and B (section "Making a
+ * tile", slices A[r :+ 64, kt :+ 16]), the ranges are runs of whole K slices,
+ * and their FP32 partial sums are added in range order, so only the order of
+ * the FP32 additions differs from gemm_run (deterministic: the same inputs
+ * give the same bits).  The planner gives a plan a split form for the skinny shapes (m <= 128,
+ * a single matrix, B streamed once) whose column strips leave most CUs idle:
+ * strips x split workgroups fill the CUs.  One launch writes the ranges'
+ * products into `workspace` (split slices of m x n FP32 values), a second sums
+ * them into C with alpha, beta and the rounding.
+ * `workspace` is a device buffer of at least gemm_plan_workspace_bytes bytes,
+ * 16-byte aligned, owned by the caller, overlapping no operand; its contents on
+ * entry do not matter and are overwritten.  Runs that share a workspace must be
+ * ordered (same stream, or synchronised).  A plan without a split form runs as
+ * gemm_run (workspace may be NULL).  Errors as gemm_run, plus GEMM_ERR_NULL /
+ * GEMM_ERR_INVALID_ARG / GEMM_ERR_ALIGNMENT for a missing, short or misaligned
+ * workspace; nothing is enqueued then.  Allocates nothing; capturable. */
+gemm_status gemm_run_split(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha,
+                           float beta, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Row reductions for gemm_run_reduce. */
 typedef enum { GEMM_REDUCE_SUM = 1, GEMM_REDUCE_MAX = 2, GEMM_REDUCE_MIN = 3 } gemm_reduce_op;
 

@@ -13,7 +13,7 @@ FLAG_LARGE_TILES = 0x4
 FLAG_A_TRANSPOSED = 0x8
 
 EXPORTED_SYMBOLS = (
-    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
+    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_plan_workspace_bytes", "gemm_run_split", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
     "la_rms_norm_run", "la_attention_run", "la_probe_mfma", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "la_layout_eval_str", "la_layout_tile_str", "la_layout_coalesce_str", "la_layout_permute_str",
@@ -71,6 +71,8 @@ def load():
         "gemm_plan_destroy": ([vp], None),
         "gemm_run": ([vp, vp, vp, vp, f32, f32, vp], i32),
         "gemm_run_reduce": ([vp, vp, vp, vp, f32, f32, i32, vp, vp], i32),
+        "gemm_plan_workspace_bytes": ([vp, p64], i32),
+        "gemm_run_split": ([vp, vp, vp, vp, f32, f32, vp, i64, vp], i32),
         "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
         "la_rms_norm_run": ([i64, i64, i32, i32, vp, i64, vp, vp, i64, f32, vp], i32),
@@ -229,6 +231,34 @@ def gemm_run(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
     _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
     _check(load().gemm_run(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                            ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), _stream_ptr(stream)))
+
+
+def gemm_plan_workspace_bytes(plan):
+    """Bytes of workspace gemm_run_split needs for `plan` (0: no split form)."""
+    out = ctypes.c_int64(0)
+    _check(load().gemm_plan_workspace_bytes(plan.handle, ctypes.byref(out)))
+    return out.value
+
+
+def gemm_run_split(plan, A, B, C, alpha=1.0, beta=0.0, workspace=None, stream=None):
+    """gemm_run with K split into the plan's ranges (partial products in `workspace`, a GPU tensor
+    of at least gemm_plan_workspace_bytes(plan) bytes; allocated here when None)."""
+    torch = _torch()
+    d = plan.desc
+    _check_a(A, "A", d)
+    _check_b(B, "B", d)
+    _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
+    need = gemm_plan_workspace_bytes(plan)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=C.device) if need else None
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda"
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    wp = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().gemm_run_split(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                                 ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), wp, wb, _stream_ptr(stream)))
+    return workspace
 
 
 REDUCE_OPS = {"sum": 1, "max": 2, "min": 3}

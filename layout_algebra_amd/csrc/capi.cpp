@@ -56,6 +56,46 @@ gemm_status launch(const gemm_plan_s& p, const lak::TiledArgs& a, void* stream, 
   return GEMM_OK;
 }
 
+// The checks gemm_run makes before anything is enqueued.
+gemm_status check_run(const gemm_plan_s& p, const void* A, const void* B, const void* C) {
+  if (!C) return set_err(GEMM_ERR_NULL, "C is NULL");
+  if (p.d.k > 0 && (!A || !B)) return set_err(GEMM_ERR_NULL, "A or B is NULL");
+  if (!aligned(A, p.align_bytes) || !aligned(B, p.align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "A and B must be " + std::to_string(p.align_bytes) + "-byte aligned for this plan");
+  if (!aligned(C, p.out_align_bytes))
+    return set_err(GEMM_ERR_ALIGNMENT, "C must be " + std::to_string(p.out_align_bytes) + "-byte aligned for this plan");
+  return GEMM_OK;
+}
+
+// The split form of a plan (p.split > 1, inputs checked): S partial products into the workspace
+// W (S slices of m x n FP32 values), one launch of the skinny kernel with the K ranges along y,
+// then their sum in range order with alpha, beta and the rounding into C.
+gemm_status run_split(const gemm_plan_s& p, const void* A, const void* B, void* C, float alpha, float beta, void* W,
+                      void* stream) {
+  lak::TiledArgs a = base_args(p);
+  const int64_t ks = p.kd.k / p.split;     // K per range, in the kernel's units (byte pairs for one-byte codes)
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.K = ks;
+  a.sa = ks;                                // range z starts ks units further along A's rows
+  a.sb = p.b_kmajor ? ks : ks * p.kd.ldb;   // ... and along B's rows ([N, K]) or down its rows ([K, N])
+  a.C = W;
+  a.ldc = p.d.n;
+  a.sc = p.d.m * p.d.n;
+  a.out_bytes = 4;
+  a.alpha = 1.0f;
+  a.beta = 0.0f;
+  a.tiles_m = 1;
+  a.tiles_n = p.split_tiles_n;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = lak::launch_kernel(p.split_kid, p.in_kind, lak::OUT_F32, p.vec, false, p.b_kmajor, false, a,
+                                    dim3(static_cast<unsigned>(p.split_tiles_n), static_cast<unsigned>(p.split)), s, false);
+  if (e == hipSuccess)
+    e = lak::launch_split_sum(static_cast<const float*>(W), p.split, p.d.m, p.d.n, C, p.d.ldc, p.out_kind, alpha, beta, s);
+  if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,6 +150,27 @@ gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, fl
   a.alpha = alpha;
   a.beta = beta;
   return launch(p, a, stream, false);
+}
+
+gemm_status gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out_bytes) {
+  if (!plan || !out_bytes) return set_err(GEMM_ERR_NULL, "plan and out_bytes must not be NULL");
+  *out_bytes = plan->ws_bytes;
+  return GEMM_OK;
+}
+
+gemm_status gemm_run_split(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha, float beta,
+                           void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");
+  const gemm_plan_s& p = *plan;
+  if (p.split <= 1) return gemm_run(plan, A, B, C, alpha, beta, stream);
+  const gemm_status st = check_run(p, A, B, C);
+  if (st != GEMM_OK) return st;
+  if (!workspace) return set_err(GEMM_ERR_NULL, "workspace is NULL (this plan needs " + std::to_string(p.ws_bytes) + " bytes)");
+  if (workspace_bytes < p.ws_bytes)
+    return set_err(GEMM_ERR_INVALID_ARG, "workspace of " + std::to_string(workspace_bytes) + " bytes; this plan needs " +
+                                             std::to_string(p.ws_bytes));
+  if (!aligned(workspace, 16)) return set_err(GEMM_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  return run_split(p, A, B, C, alpha, beta, workspace, stream);
 }
 
 gemm_status gemm_run_reduce(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha, float beta,

@@ -176,6 +176,11 @@ struct CfgSkinny128KM : CfgSkinny16KM {
 // kernel, not a memset, so that HIP graphs may capture it.
 hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
 
+// C = alpha * sum over z < S of P[z * M * N ...] + beta * C (P: S FP32 slices of M x N, row stride N;
+// N a multiple of 4, P 16-byte aligned), rounded to C's type.
+hipError_t launch_split_sum(const float* P, int S, int64_t M, int64_t N, void* C, int64_t ldc, int out_kind,
+                            float alpha, float beta, hipStream_t stream);
+
 // Matrix-core rate probe (measurement aid): `workgroups` x 4 waves, each
 // issuing mfma_per_wave (a multiple of 16) MFMAs on fragments from `ops`.
 hipError_t launch_mfma_probe(const void* ops, int64_t n_frags, float* sink, int64_t workgroups, int64_t mfma_per_wave,

@@ -665,7 +665,14 @@ std::string describe(const gemm_plan_s& p) {
      << ",\"copy\":" << p.copy_json << ",\"store\":" << p.store_json
      << ",\"in_bytes\":" << s.in_bytes << ",\"k_sub\":" << s.k_sub
      << ",\"vec_elems\":" << p.vec << ",\"align_bytes\":" << p.align_bytes
-     << ",\"out_align_bytes\":" << p.out_align_bytes << "}";
+     << ",\"out_align_bytes\":" << p.out_align_bytes
+     << ",\"split_k\":" << p.split;
+  if (p.split > 1) {
+    const lak::KernelShape ss = lak::kernel_shape(p.split_kid);
+    js << ",\"split_kernel\":\"" << kNames[p.split_kid] << "_" << ss.bm << "x" << ss.bn << "x" << ss.bk << "\""
+       << ",\"split_grid\":[" << p.split_tiles_n << "," << p.split << "]";
+  }
+  js << ",\"workspace_bytes\":" << p.ws_bytes << "}";
   return js.str();
 }
 
@@ -719,6 +726,18 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   if (p.kid == lak::KID_SKINNY_128_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_128;
   if (runs && p.kid != pair_kid)
     return unsupported("one-byte inputs: operand rows too far apart for the kernel's 32-bit byte offsets");
+  // the split form's partial products on byte pairs (the ranges cut K in pairs, an even count of codes)
+  if (p.split > 1) {
+    const int sk = p.split_kid;
+    p.split_kid = sk == lak::KID_SKINNY_16_KM ? lak::KID_SKINNY_F8
+                : sk == lak::KID_SKINNY_32_KM ? lak::KID_SKINNY_F8_32
+                : sk == lak::KID_SKINNY_64_KM ? lak::KID_SKINNY_F8_64
+                : sk == lak::KID_SKINNY_128_KM ? lak::KID_SKINNY_F8_128 : -1;
+    if (p.split_kid < 0) {
+      fail(err, "one-byte split form without a one-byte skinny kernel");
+      return GEMM_ERR_RESOURCE;
+    }
+  }
   p.d = d;
   p.kd = v;
   if (p.kid == pair_kid) {
@@ -932,6 +951,26 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
                             2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
                             2 * int64_t(kmajor ? ks.bn : ks.bk) * d.ldb < (int64_t{1} << 32);
     if (skinny_fit) p.kid = sk;
+    // Split K for the skinny shapes on grids that leave CUs idle (a single matrix): workgroups
+    // = strips x split doubled while they fit the CUs' workgroup slots (256 CUs, two workgroups
+    // each for stages of at most 80 KiB), each range keeping at least 4 K blocks.
+    const bool skinny_shape_fit = !p.gate_up && !atrans && d.batch == 1 && d.m >= 1 && d.m <= ks.bm && d.n > 0 &&
+                                  d.n % ks.bn == 0 && d.k > 0 && d.k % ks.bk == 0 && in16 &&
+                                  2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
+                                  2 * int64_t(kmajor ? ks.bn : ks.bk) * d.ldb < (int64_t{1} << 32);
+    if (skinny_shape_fit) {
+      const int64_t strips = d.n / ks.bn, nk = d.k / ks.bk;
+      const int64_t lds = 2 * int64_t(ks.stages) * lak::stage_elems(ks, false);
+      const int64_t slots = 256 * (lds <= 80 * 1024 ? 2 : 1);
+      int split = 1;
+      while (strips * split * 2 <= slots && nk % (2 * split) == 0 && nk / (2 * split) >= 4 && split < 16) split *= 2;
+      if (split > 1) {
+        p.split = split;
+        p.split_kid = sk;
+        p.split_tiles_n = static_cast<int>(strips);
+        p.ws_bytes = int64_t(split) * d.m * d.n * 4;
+      }
+    }
     // The general kernel: 64 x 64 tiles (two register sets of prefetch with
     // 16-byte loads) measured faster than 128 x 128 at every size with 16-byte
     // loads but 4000 x 4000 x 1000 (3 % slower), and with 2-byte loads up to
