@@ -177,7 +177,7 @@ struct CfgSkinny128KM : CfgSkinny16KM {
 hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
 
 // C = alpha * sum over z < S of P[z * M * N ...] + beta * C (P: S FP32 slices of M x N, row stride N;
-// N a multiple of 4, P 16-byte aligned), rounded to C's type.
+// N a multiple of 4, P 16-byte aligned; S one of 1, 2, 4, 8, 16), rounded to C's type.
 hipError_t launch_split_sum(const float* P, int S, int64_t M, int64_t N, void* C, int64_t ldc, int out_kind,
                             float alpha, float beta, hipStream_t stream);
 

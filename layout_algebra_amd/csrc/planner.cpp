@@ -952,8 +952,14 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
                             2 * int64_t(kmajor ? ks.bn : ks.bk) * d.ldb < (int64_t{1} << 32);
     if (skinny_fit) p.kid = sk;
     // Split K for the skinny shapes on grids that leave CUs idle (a single matrix): workgroups
-    // = strips x split doubled while they fit the CUs' workgroup slots (256 CUs, two workgroups
-    // each for stages of at most 80 KiB), each range keeping at least 4 K blocks.
+    // = strips x split doubled while they fit one per CU (two per CU for the 16-row K-major
+    // configuration, whose 80 KiB of stages seat two), each range keeping at least 4 K blocks.
+    // Measured on one box (bf16, B stored [N, K] unless noted), 4096 x 14336: 16 rows 512
+    // workgroups 21.5 us against 256 24.0; 32 rows 256 workgroups 24.4 against 512 26.1; 128 rows
+    // 256 workgroups 37.3 against 128 48.9; B [K, N], 64 rows 256 workgroups 32.7 against 512
+    // 36.6; 11008 x 4096: 16 rows 344 workgroups 20.8 against 688 21.5; B [K, N], 64 rows 172
+    // workgroups 27.4 against 344 33.4.  (Against the rule: 64 rows, 4096 x 14336, 512 workgroups
+    // 31.4 us, 256 36.3.)
     const bool skinny_shape_fit = !p.gate_up && !atrans && d.batch == 1 && d.m >= 1 && d.m <= ks.bm && d.n > 0 &&
                                   d.n % ks.bn == 0 && d.k > 0 && d.k % ks.bk == 0 && in16 &&
                                   2 * int64_t(ks.bm) * d.lda < (int64_t{1} << 32) &&
@@ -961,7 +967,7 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     if (skinny_shape_fit) {
       const int64_t strips = d.n / ks.bn, nk = d.k / ks.bk;
       const int64_t lds = 2 * int64_t(ks.stages) * lak::stage_elems(ks, false);
-      const int64_t slots = 256 * (lds <= 80 * 1024 ? 2 : 1);
+      const int64_t slots = 256 * (ks.bm == 16 && lds <= 80 * 1024 ? 2 : 1);
       int split = 1;
       while (strips * split * 2 <= slots && nk % (2 * split) == 0 && nk / (2 * split) >= 4 && split < 16) split *= 2;
       if (split > 1) {
