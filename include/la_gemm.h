@@ -175,6 +175,21 @@ gemm_status gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out_bytes);
 gemm_status gemm_run_split(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha,
                            float beta, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* gemm_run_split for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * partial products go to a workspace array the library holds on each GPU for
+ * the life of the process (16 MiB, enough for every split form the planner
+ * makes), instead of a caller-provided buffer.  The array of the current
+ * device is used; its address is looked up on the first call on that device.
+ * Calls that overlap on one GPU (concurrent streams, or two threads) share the
+ * array and race: order them (one stream, or synchronise between them).  The
+ * array needs no clearing (each run overwrites what it reads).  Same results
+ * (bit for bit) and errors as gemm_run_split; a plan whose workspace would
+ * exceed the array is GEMM_ERR_RESOURCE, nothing enqueued.  A plan without a
+ * split form runs as gemm_run.  Calls no allocating routine. */
+gemm_status gemm_run_split_noalloc(gemm_plan_t plan, const void* A, const void* B, void* C,
+                                   float alpha, float beta, void* stream);
+
 /* Row reductions for gemm_run_reduce. */
 typedef enum { GEMM_REDUCE_SUM = 1, GEMM_REDUCE_MAX = 2, GEMM_REDUCE_MIN = 3 } gemm_reduce_op;
 

@@ -13,7 +13,7 @@ FLAG_LARGE_TILES = 0x4
 FLAG_A_TRANSPOSED = 0x8
 
 EXPORTED_SYMBOLS = (
-    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_plan_workspace_bytes", "gemm_run_split", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
+    "gemm_plan", "gemm_plan_destroy", "gemm_run", "gemm_plan_workspace_bytes", "gemm_run_split", "gemm_run_split_noalloc", "gemm_run_reduce", "gemm_gate_up_run", "gemm_gate_up_swiglu_run", "gemm_plan_describe",
     "la_rms_norm_run", "la_attention_run", "la_probe_mfma", "gemm_plan_lds_offset", "gemm_debug_lds_image", "gemm_plan_lds_stage_bytes",
     "la_layout_eval", "la_layout_eval_index", "la_swizzle_apply", "la_tile_plan_offset",
     "la_layout_eval_str", "la_layout_tile_str", "la_layout_coalesce_str", "la_layout_permute_str",
@@ -73,6 +73,7 @@ def load():
         "gemm_run_reduce": ([vp, vp, vp, vp, f32, f32, i32, vp, vp], i32),
         "gemm_plan_workspace_bytes": ([vp, p64], i32),
         "gemm_run_split": ([vp, vp, vp, vp, f32, f32, vp, i64, vp], i32),
+        "gemm_run_split_noalloc": ([vp, vp, vp, vp, f32, f32, vp], i32),
         "gemm_gate_up_run": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "gemm_gate_up_swiglu_run": ([vp, vp, vp, vp, vp, vp], i32),
         "la_rms_norm_run": ([i64, i64, i32, i32, vp, i64, vp, vp, i64, f32, vp], i32),
@@ -259,6 +260,17 @@ def gemm_run_split(plan, A, B, C, alpha=1.0, beta=0.0, workspace=None, stream=No
     _check(load().gemm_run_split(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                                  ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), wp, wb, _stream_ptr(stream)))
     return workspace
+
+
+def gemm_run_split_noalloc(plan, A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """gemm_run_split with the library's per-GPU workspace array: allocates nothing (calls that
+    overlap on one GPU race on that array)."""
+    d = plan.desc
+    _check_a(A, "A", d)
+    _check_b(B, "B", d)
+    _check_matrix(C, "C", d.m, d.n, d.ldc, d.c_type, d.batch, d.stride_c)
+    _check(load().gemm_run_split_noalloc(plan.handle, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                                         ctypes.c_void_p(C.data_ptr()), float(alpha), float(beta), _stream_ptr(stream)))
 
 
 REDUCE_OPS = {"sum": 1, "max": 2, "min": 3}

@@ -173,6 +173,22 @@ gemm_status gemm_run_split(gemm_plan_t plan, const void* A, const void* B, void*
   return run_split(p, A, B, C, alpha, beta, workspace, stream);
 }
 
+gemm_status gemm_run_split_noalloc(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha, float beta,
+                                   void* stream) {
+  if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");
+  const gemm_plan_s& p = *plan;
+  if (p.split <= 1) return gemm_run(plan, A, B, C, alpha, beta, stream);
+  const gemm_status st = check_run(p, A, B, C);
+  if (st != GEMM_OK) return st;
+  if (p.ws_bytes > lak::kSplitScratchBytes)
+    return set_err(GEMM_ERR_RESOURCE, "this plan's workspace of " + std::to_string(p.ws_bytes) + " bytes exceeds the " +
+                                          std::to_string(lak::kSplitScratchBytes) + "-byte scratch of gemm_run_split_noalloc");
+  void* W = nullptr;
+  const hipError_t e = lak::split_scratch(&W);
+  if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("scratch lookup failed: ") + hipGetErrorString(e));
+  return run_split(p, A, B, C, alpha, beta, W, stream);
+}
+
 gemm_status gemm_run_reduce(gemm_plan_t plan, const void* A, const void* B, void* C, float alpha, float beta,
                             int32_t op, float* R, void* stream) {
   if (!plan) return set_err(GEMM_ERR_NULL, "plan is NULL");

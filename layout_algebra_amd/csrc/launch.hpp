@@ -181,6 +181,13 @@ hipError_t launch_reduce_init(float* R, int64_t n, int red, hipStream_t stream);
 hipError_t launch_split_sum(const float* P, int S, int64_t M, int64_t N, void* C, int64_t ldc, int out_kind,
                             float alpha, float beta, hipStream_t stream);
 
+// Bytes of the per-GPU workspace array behind gemm_run_split_noalloc: the largest split form the
+// planner makes (128 rows x 128-column strips x 256 workgroups x 4 bytes).
+constexpr int64_t kSplitScratchBytes = int64_t(16) << 20;
+
+// Device address of the current device's workspace array (looked up once per device).
+hipError_t split_scratch(void** out);
+
 // Matrix-core rate probe (measurement aid): `workgroups` x 4 waves, each
 // issuing mfma_per_wave (a multiple of 16) MFMAs on fragments from `ops`.
 hipError_t launch_mfma_probe(const void* ops, int64_t n_frags, float* sink, int64_t workgroups, int64_t mfma_per_wave,

@@ -8,11 +8,22 @@
 // first is used (S is a template parameter: one memory latency per thread, not
 // S of them), summed in range order (the result does not depend on
 // scheduling), then alpha, beta and the rounding of the GEMM epilogue.
+#include <mutex>
+
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
 namespace lak {
 namespace {
+
+// Workspace of gemm_run_split_noalloc: one array per GPU, held by the loaded code object until the
+// process ends.  Host code never passes the array's name to a kernel (on the host it names a
+// stand-in, not the device memory): split_scratch() looks up each device's address once.
+static __device__ __align__(256) unsigned char scratch[kSplitScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
 
 template <class TO, int S>
 __global__ void __launch_bounds__(256) split_sum_kernel(const float* __restrict__ P, int64_t M, int64_t N, void* C,
@@ -54,6 +65,23 @@ hipError_t go_sum(const float* P, int S, int64_t M, int64_t N, void* C, int64_t 
 }
 
 }  // namespace
+
+hipError_t split_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_split_sum(const float* P, int S, int64_t M, int64_t N, void* C, int64_t ldc, int out_kind,
                             float alpha, float beta, hipStream_t stream) {

@@ -303,6 +303,26 @@ def test_skinny_rows_and_grid_guard():
     assert kern(128, 28672, 8160).startswith("tiled_")                      # K not a multiple of 64
 
 
+def test_split_form_workspace_bound():
+    """Every split form the planner makes fits the 16 MiB array of gemm_run_split_noalloc:
+    workspace = split * m * n * 4 with strips * split at most 256 (512 for 16 rows)."""
+    worst = 0
+    for m in (1, 16, 17, 32, 33, 64, 65, 100, 128):
+        for n in (64, 1024, 4096, 8128, 8192, 11008, 16320):
+            for k in (1024, 4096, 14336, 65536):
+                for km in (False, True):
+                    try:
+                        d = la.gemm_plan(m, n, k, la.BF16, la.F32, b_kmajor=km).describe()
+                    except la.GemmError:
+                        continue
+                    assert d["workspace_bytes"] == (d["split_k"] * m * n * 4 if d["split_k"] > 1 else 0), d
+                    if d["split_k"] > 1:
+                        assert d["split_grid"][0] * d["split_grid"][1] <= (512 if d["split_kernel"].startswith(
+                            ("skinny_bkmajor_16x", "skinny_f8_16x")) else 256), d
+                    worst = max(worst, d["workspace_bytes"])
+    assert 0 < worst <= 16 << 20
+
+
 def test_small_grids_take_64x64_tiles_unless_pinned():
     """Kernel choice by grid size: a grid that would leave most of the 256 CUs idle moves to
     64 x 64 tiles of the general kernel; GEMM_FLAG_LARGE_TILES keeps the largest tile."""
