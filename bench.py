@@ -16,6 +16,7 @@ Workloads (seeded synthetic inputs, see synth/):
   gate_up_swiglu  the same with silu(G) * U fused into the epilogue (one output)
   skinny      16 x 28672 x 8192 bf16 -> fp32 (HBM-bound; two B buffers rotate)
   skinny_kmajor, skinny_f8  the same with B stored [28672, 8192] (bf16, E4M3)
+  skinny_split  32 x 4096 x 14336 bf16 -> fp32, B stored [4096, 14336], K split (gemm_run_split)
   square4096_f32, square4096_f8, gate_up_f8  binary32 and one-byte inputs
   square256, ragged
   rms_norm       row normalisation of 2^20 f32 rows of 256 (HBM-bound)
@@ -55,6 +56,8 @@ GEMM_SOURCES = {"fast_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"), "fast_gate_up_
 
 # host code that decides which instantiation a GEMM plan launches, and with which grid
 PLANNER_SOURCES = ("planner.cpp", "kernels.cpp", "kernel_table.hpp")
+# the split form's range sum and the host code that launches both kernels
+SPLIT_SOURCES = ("split_sum.hip", "capi.cpp")
 
 
 def gemm_plan_summary(workload):
@@ -63,6 +66,8 @@ def gemm_plan_summary(workload):
     w = synth.WORKLOADS[workload]
     d = la.gemm_plan(w.M, w.N, w.K, type_code(w.in_kind), type_code(w.out_kind), gate_up=w.gate_up,
                      b_kmajor=w.b_kmajor).describe()
+    if w.split:
+        return "%s grid=%s split=%d" % (d["split_kernel"], d["split_grid"], d["split_k"])
     return "%s grid=%d prefetch=%d" % (d["kernel"], d["grid"], d["prefetch_blocks"])
 
 
@@ -82,6 +87,8 @@ def workload_sources(workload):
     else:
         kernel = gemm_plan_summary(workload).split()[0]
         own = next(v for k, v in GEMM_SOURCES.items() if kernel.startswith(k)) + PLANNER_SOURCES
+        if synth.WORKLOADS[workload].split:
+            own += SPLIT_SOURCES
     return tuple(sorted(own + SHARED_SOURCES))
 
 
@@ -211,9 +218,15 @@ def main():
             Bs.append(dev_b(w.dist_b.sample((w.K, w.N), w.seeds[2], synth.torch_dtype(w.in_kind))))
         C0 = x["C"].to(dev) if "C" in x else None
         C = torch.empty((w.M, w.N), dtype=out_dt, device=dev) if C0 is None else C0.clone()
+        if w.split:
+            # K cut into the plan's ranges: partial products into a workspace allocated here, once
+            ws = torch.empty(la.gemm_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
 
-        def step(i):
-            la.gemm_run(plan, A, Bs[i % len(Bs)], C, w.alpha, w.beta)
+            def step(i):
+                la.gemm_run_split(plan, A, Bs[i % len(Bs)], C, w.alpha, w.beta, ws)
+        else:
+            def step(i):
+                la.gemm_run(plan, A, Bs[i % len(Bs)], C, w.alpha, w.beta)
         result = C
         b_cpu = x["B"]
 
@@ -315,6 +328,10 @@ def main():
         "pct_of_bf16_peak": 100.0 * value_tflops / PEAK_TFLOPS[w.in_kind],
     }
 
+    if w.split:
+        d = plan.describe()
+        line["config"].update({"kernel": d["split_kernel"], "grid": d["split_grid"], "split_k": d["split_k"],
+                               "workspace_bytes": d["workspace_bytes"]})
     line["clock"] = clock
     if roof["bound"] == "mfma":
         roof["at_measured_clock"] = at_clock(clock, roof["peak"], roof["achieved"])

@@ -59,6 +59,7 @@ class Workload:
     gate_up: bool = False
     act: str = ""                # gate/up epilogue activation: "" (G and U) or "swiglu" (one output)
     b_kmajor: bool = False       # B stored [N, K] (K contiguous; one-byte inputs need it)
+    split: bool = False          # run with K cut into the plan's ranges (gemm_run_split)
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -113,6 +114,11 @@ WORKLOADS = {
         "skinny_f8", 16, 28672, 8192, "f8e4m3", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.25), (5201, 5202, 5203), b_kmajor=True,
         notes="M=16 bandwidth-bound GEMM, E4M3 A and B, B stored [28672, 8192]"),
+    # a decode batch of 32 through a 14336 -> 4096 projection: 64 strips of B, K cut into ranges
+    "skinny_split": Workload(
+        "skinny_split", 32, 4096, 14336, "bf16", "f32", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.02), (5301, 5302, 5303), b_kmajor=True, split=True,
+        notes="M=32 bandwidth-bound GEMM on a small grid, B stored [4096, 14336], K split"),
 }
 
 

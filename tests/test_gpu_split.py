@@ -6,8 +6,8 @@ second kernel sums the ranges in order with alpha, beta and the rounding.  Only
 the order of the FP32 additions differs from a single pass, so the bound is the
 plain GEMM's (tests/parity.py).  Cases: 1 to 128 rows of A, both storages of B,
 bf16 / fp16 inputs with fp32 / bf16 / fp16 outputs, alpha and beta with C in
-padded rows that must stay untouched, one-byte inputs, the decode shape
-32 x 4096 x 14336 with B stored [N, K] in full, determinism, the workspace
+padded rows that must stay untouched, one-byte inputs, the skinny_split workload
+(32 x 4096 x 14336, B stored [N, K]) in full, determinism, the workspace
 checks of the C ABI, plans without a split form, and graph replays.
 """
 import ctypes
@@ -110,14 +110,19 @@ def test_split_one_byte(case):
 
 
 def test_split_decode_shape_full():
-    """32 x 4096 x 14336 with B stored [N, K] (a down projection at a decode batch of 32), in full."""
-    M, N, K = 32, 4096, 14336
-    a = synth.normal((M, K), 501, "bf16")
-    b = synth.normal((K, N), 502, "bf16", 0.02)
-    got, d = run_split(a, b, "bf16", "bf16", True)
+    """The skinny_split workload (32 x 4096 x 14336, B stored [N, K]: a down projection at a decode
+    batch of 32) in full, in the launch configuration the bench times (plan, workspace, entry point)."""
+    w = synth.WORKLOADS["skinny_split"]
+    x = synth.make_inputs(w)
+    plan = la.gemm_plan(w.M, w.N, w.K, la.BF16, la.F32, b_kmajor=True)
+    d = plan.describe()
     assert d["split_k"] == 4 and d["split_grid"] == [64, 4], d
-    ref = oracle_gemm(a, b, "bf16")
-    assert_close(got, ref, K, a, b, "bf16", "split decode shape")
+    ws = torch.empty(la.gemm_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.float32, device=DEV)
+    la.gemm_run_split(plan, x["A"].to(DEV), x["B"].t().contiguous().to(DEV), C, w.alpha, w.beta, ws)
+    torch.cuda.synchronize()
+    ref = oracle_gemm(x["A"], x["B"], "bf16")
+    assert_close(C.cpu(), ref, w.K, x["A"], x["B"], "f32", "skinny_split workload")
 
 
 def test_split_is_deterministic_and_matches_single_pass_within_rounding():
