@@ -160,9 +160,10 @@ gemm_status gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out_bytes);
  * tile", slices A[r :+ 64, kt :+ 16]), the ranges are runs of whole K slices,
  * and their FP32 partial sums are added in range order, so only the order of
  * the FP32 additions differs from gemm_run (deterministic: the same inputs
- * give the same bits).  The planner gives a plan a split form for the skinny shapes (m <= 128,
- * a single matrix, B streamed once) whose column strips leave most CUs idle:
- * strips x split workgroups fill the CUs.  One launch writes the ranges'
+ * give the same bits).  The planner gives a plan a split form where a single
+ * matrix's grid leaves most CUs idle: the skinny shapes (m <= 128, B streamed
+ * once) on few column strips, and other shapes with at most 64 tiles of the
+ * 256-wide kernel (n a multiple of 8, K cut into whole K blocks).  One launch writes the ranges'
  * products into `workspace` (split slices of m x n FP32 values), a second sums
  * them into C with alpha, beta and the rounding.
  * `workspace` is a device buffer of at least gemm_plan_workspace_bytes bytes,
@@ -178,7 +179,7 @@ gemm_status gemm_run_split(gemm_plan_t plan, const void* A, const void* B, void*
 /* gemm_run_split for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * partial products go to a workspace array the library holds on each GPU for
- * the life of the process (16 MiB, enough for every split form the planner
+ * the life of the process (64 MiB, enough for every split form the planner
  * makes), instead of a caller-provided buffer.  The array of the current
  * device is used; its address is looked up on the first call on that device.
  * Calls that overlap on one GPU (concurrent streams, or two threads) share the

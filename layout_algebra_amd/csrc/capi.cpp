@@ -68,8 +68,8 @@ gemm_status check_run(const gemm_plan_s& p, const void* A, const void* B, const 
 }
 
 // The split form of a plan (p.split > 1, inputs checked): S partial products into the workspace
-// W (S slices of m x n FP32 values), one launch of the skinny kernel with the K ranges along y,
-// then their sum in range order with alpha, beta and the rounding into C.
+// W (S slices of m x n FP32 values), one launch of the skinny or 256-wide kernel with the K ranges
+// along y, then their sum in range order with alpha, beta and the rounding into C.
 gemm_status run_split(const gemm_plan_s& p, const void* A, const void* B, void* C, float alpha, float beta, void* W,
                       void* stream) {
   lak::TiledArgs a = base_args(p);
@@ -85,11 +85,13 @@ gemm_status run_split(const gemm_plan_s& p, const void* A, const void* B, void* 
   a.out_bytes = 4;
   a.alpha = 1.0f;
   a.beta = 0.0f;
-  a.tiles_m = 1;
+  a.tiles_m = p.split_tiles_m;
   a.tiles_n = p.split_tiles_n;
+  a.group_m = 8;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned tiles = static_cast<unsigned>(p.split_tiles_m) * static_cast<unsigned>(p.split_tiles_n);
   hipError_t e = lak::launch_kernel(p.split_kid, p.in_kind, lak::OUT_F32, p.vec, false, p.b_kmajor, false, a,
-                                    dim3(static_cast<unsigned>(p.split_tiles_n), static_cast<unsigned>(p.split)), s, false);
+                                    dim3(tiles, static_cast<unsigned>(p.split)), s, false);
   if (e == hipSuccess)
     e = lak::launch_split_sum(static_cast<const float*>(W), p.split, p.d.m, p.d.n, C, p.d.ldc, p.out_kind, alpha, beta, s);
   if (e != hipSuccess) return set_err(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));

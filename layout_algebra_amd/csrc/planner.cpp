@@ -670,7 +670,7 @@ std::string describe(const gemm_plan_s& p) {
   if (p.split > 1) {
     const lak::KernelShape ss = lak::kernel_shape(p.split_kid);
     js << ",\"split_kernel\":\"" << kNames[p.split_kid] << "_" << ss.bm << "x" << ss.bn << "x" << ss.bk << "\""
-       << ",\"split_grid\":[" << p.split_tiles_n << "," << p.split << "]";
+       << ",\"split_grid\":[" << int64_t(p.split_tiles_m) * p.split_tiles_n << "," << p.split << "]";
   }
   js << ",\"workspace_bytes\":" << p.ws_bytes << "}";
   return js.str();
@@ -730,11 +730,12 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   if (p.split > 1) {
     const int sk = p.split_kid;
     p.split_kid = sk == lak::KID_SKINNY_16_KM ? lak::KID_SKINNY_F8
+                : sk == lak::KID_FAST_256_KM ? lak::KID_FAST_F8
                 : sk == lak::KID_SKINNY_32_KM ? lak::KID_SKINNY_F8_32
                 : sk == lak::KID_SKINNY_64_KM ? lak::KID_SKINNY_F8_64
                 : sk == lak::KID_SKINNY_128_KM ? lak::KID_SKINNY_F8_128 : -1;
     if (p.split_kid < 0) {
-      fail(err, "one-byte split form without a one-byte skinny kernel");
+      fail(err, "one-byte split form without a one-byte kernel");
       return GEMM_ERR_RESOURCE;
     }
   }
@@ -927,7 +928,11 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     const bool edges = d.m > 0 && d.n > 0 && k_ok && (kmajor || d.n % 8 == 0) && (!atrans || d.m % 8 == 0);
     // padded tile area within 1.3x of M x N (4000^2: 1.05x; 1000 rows: 1.02x), unless the
     // caller keeps the largest tile
-    const bool little_padding = 10 * __int128(ftm * fs.bm) * (ftn * fs.bn) <= 13 * __int128(d.m) * d.n;
+    // (up to 4/3 on grids of 80 tiles or more: M = 192 or 384 against 256-row tiles measured ahead on
+    // the 256-wide kernel from 86 tiles on, e.g. 384 x 28672 x 8192 217 against 343 us, 384 x 11008 x
+    // 4096 74 against 80; behind at 43 tiles, 192 x 11008 x 4096 73 against 50)
+    const __int128 padded = __int128(ftm * fs.bm) * (ftn * fs.bn), area = __int128(d.m) * d.n;
+    const bool little_padding = 10 * padded <= 13 * area || (ftm * ftn >= 80 && 3 * padded <= 4 * area);
     if ((whole || (edges && (little_padding || large))) && rows16 && off32) p.kid = fk;
     // Fewer than 32 full-tile workgroups leave most CUs idle: 64 x 64 tiles of
     // the general kernel give 16 times as many and finish sooner (measured at
@@ -974,6 +979,27 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
         p.split = split;
         p.split_kid = sk;
         p.split_tiles_n = static_cast<int>(strips);
+        p.ws_bytes = int64_t(split) * d.m * d.n * 4;
+      }
+    }
+    // Split K for the 256-wide kernel on grids of at most 64 tiles (a single matrix the skinny
+    // kernel does not take): the smallest power-of-two split count that gives 128 workgroups or
+    // more (at most 8), each range whole K blocks, at least 8 of them; FP32 partials in rows of n
+    // values (n % 8 == 0: the kernel's 8-value row chunks).  Measured on one box, single pass -> split (partials + a library sum)
+    // against torch.matmul, us: 512 x 4096 x 14336 240 -> 91 (4 ranges; 8: 97) | 85;
+    // 256 x 4096 x 14336 99 (general kernel) -> 60 (8; 16: 77) | 52; 1024 x 4096 x 14336 240 -> 154
+    // (2; 4: 147) | 123; 256 x 11008 x 4096 74 -> 58 (2; 4: 58) | 40; with 86 tiles and more no gain
+    // (512 x 11008 x 4096 77 -> 83, 256 x 28672 x 8192 206 -> 193, 512 x 28672 x 8192 226 -> 303).
+    const int64_t ftiles = ftm * ftn;
+    if (p.split == 1 && !p.gate_up && !atrans && d.batch == 1 && (whole || edges) && in16 && off32 &&
+        d.n % 8 == 0 && ftiles <= 64) {
+      int split = 1;
+      while (ftiles * split < 128 && split < 8) split *= 2;
+      if (split > 1 && d.k % (int64_t(fs.bk) * split) == 0 && d.k / (int64_t(fs.bk) * split) >= 8) {
+        p.split = split;
+        p.split_kid = fk;
+        p.split_tiles_m = static_cast<int>(ftm);
+        p.split_tiles_n = static_cast<int>(ftn);
         p.ws_bytes = int64_t(split) * d.m * d.n * 4;
       }
     }

@@ -24,11 +24,12 @@ struct gemm_plan_s {
   bool a_trans = false;      // A (and X) stored [K, M]
   int tiles_m = 0, tiles_n = 0, grid = 0, group_m = 8;
   // gemm_run_split: K cut into `split` equal ranges, each range's FP32 partial product written by
-  // the skinny kernel `split_kid` (one column strip of split_tiles_n per workgroup, the ranges along
-  // the launch's y dimension) into ws_bytes = split * m * n * 4 bytes of workspace, then summed in
-  // range order by a second kernel that applies alpha, beta and the rounding.  split = 1: the plan
-  // has no split form and gemm_run_split runs as gemm_run.
-  int split = 1, split_kid = 0, split_tiles_n = 0;
+  // kernel `split_kid` (the skinny kernel: one column strip per workgroup; or the 256-wide kernel:
+  // one tile per workgroup; split_tiles_m x split_tiles_n of them, the ranges along the launch's y
+  // dimension) into ws_bytes = split * m * n * 4 bytes of workspace, then summed in range order by
+  // a second kernel that applies alpha, beta and the rounding.  split = 1: the plan has no split
+  // form and gemm_run_split runs as gemm_run.
+  int split = 1, split_kid = 0, split_tiles_m = 1, split_tiles_n = 0;
   int64_t ws_bytes = 0;
   int64_t stage_elems = 0, lds_bytes = 0;
   lak::KernelShape shape{};

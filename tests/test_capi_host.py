@@ -304,10 +304,12 @@ def test_skinny_rows_and_grid_guard():
 
 
 def test_split_form_workspace_bound():
-    """Every split form the planner makes fits the 16 MiB array of gemm_run_split_noalloc:
-    workspace = split * m * n * 4 with strips * split at most 256 (512 for 16 rows)."""
+    """Every split form the planner makes fits the 64 MiB array of gemm_run_split_noalloc:
+    workspace = split * m * n * 4 with fewer than 256 workgroups of at most 256 x 256 outputs (skinny
+    strips x split at most 256, 512 for 16 rows; 256-wide tiles x split below 256)."""
     worst = 0
-    for m in (1, 16, 17, 32, 33, 64, 65, 100, 128):
+    kinds = set()
+    for m in (1, 16, 17, 32, 33, 64, 65, 100, 128, 129, 192, 256, 300, 512, 1000, 1024, 2048):
         for n in (64, 1024, 4096, 8128, 8192, 11008, 16320):
             for k in (1024, 4096, 14336, 65536):
                 for km in (False, True):
@@ -317,10 +319,40 @@ def test_split_form_workspace_bound():
                         continue
                     assert d["workspace_bytes"] == (d["split_k"] * m * n * 4 if d["split_k"] > 1 else 0), d
                     if d["split_k"] > 1:
-                        assert d["split_grid"][0] * d["split_grid"][1] <= (512 if d["split_kernel"].startswith(
-                            ("skinny_bkmajor_16x", "skinny_f8_16x")) else 256), d
+                        sk = d["split_kernel"]
+                        kinds.add(sk.split("_")[0])
+                        wgs = d["split_grid"][0] * d["split_grid"][1]
+                        if sk.startswith("skinny"):
+                            assert m <= 128 and wgs <= (512 if sk.startswith(("skinny_bkmajor_16x", "skinny_f8_16x")) else 256), d
+                        else:
+                            assert sk.startswith("fast_") and d["split_grid"][0] <= 64 and wgs < 256, d
+                            assert d["split_k"] <= 8 and k % (32 * d["split_k"]) == 0 and n % 8 == 0, d
                     worst = max(worst, d["workspace_bytes"])
-    assert 0 < worst <= 16 << 20
+    assert kinds == {"skinny", "fast"}
+    assert 0 < worst <= 64 << 20
+
+
+def test_fast_split_form_and_padding_rule():
+    """The 256-wide kernel's split form on grids of at most 64 tiles, and edge tiles padded up to 4/3
+    kept on the 256-wide kernel from 80 tiles on."""
+    def plan(m, n, k, km=False):
+        return la.gemm_plan(m, n, k, la.BF16, la.BF16, b_kmajor=km).describe()
+    d = plan(512, 4096, 14336, True)
+    assert d["kernel"].startswith("fast_bkmajor_") and d["split_k"] == 4 and d["split_grid"] == [32, 4]
+    assert d["split_kernel"] == "fast_bkmajor_256x256x32"
+    d = plan(256, 4096, 14336)
+    assert d["kernel"].startswith("tiled_64x64") and d["split_k"] == 8 and d["split_kernel"] == "fast_256x256x32"
+    d = plan(1024, 4096, 14336)
+    assert d["split_k"] == 2 and d["split_grid"] == [64, 2]
+    assert plan(512, 11008, 4096)["split_k"] == 1                               # 86 tiles
+    assert plan(4096, 4096, 4096)["split_k"] == 1
+    assert plan(512, 4096, 512)["split_k"] == 1                                 # ranges under 8 K blocks
+    assert plan(384, 28672, 8192)["kernel"].startswith("fast_256x256")          # 224 tiles, padding 4/3
+    assert plan(384, 11008, 4096)["kernel"].startswith("fast_256x256")          # 86 tiles
+    assert plan(192, 11008, 4096)["kernel"].startswith("tiled_64x64")           # 43 tiles
+    assert plan(320, 28672, 8192)["kernel"].startswith("tiled_64x64")           # padding 1.6
+    d = la.gemm_plan(512, 4096, 14336, la.F8E4M3, la.BF16, b_kmajor=True).describe()
+    assert d["kernel"] == "fast_f8_256x256x64" and d["split_k"] == 4 and d["split_kernel"] == "fast_f8_256x256x64"
 
 
 def test_small_grids_take_64x64_tiles_unless_pinned():

@@ -4,7 +4,9 @@ The plan's split form writes each K range's FP32 partial product into a
 caller-owned workspace (one launch, ranges along the grid's y dimension) and a
 second kernel sums the ranges in order with alpha, beta and the rounding.  Only
 the order of the FP32 additions differs from a single pass, so the bound is the
-plain GEMM's (tests/parity.py).  Cases: 1 to 128 rows of A, both storages of B,
+plain GEMM's (tests/parity.py).  Cases: the skinny kernel's split form for 1 to
+128 rows of A and the 256-wide kernel's (at most 64 tiles, M and N edges, one-byte
+inputs, a 512 x 4096 x 14336 prefill shape on sampled rows), both storages of B,
 bf16 / fp16 inputs with fp32 / bf16 / fp16 outputs, alpha and beta with C in
 padded rows that must stay untouched, one-byte inputs, the skinny_split workload
 (32 x 4096 x 14336, B stored [N, K]) in full, determinism, the workspace
@@ -18,7 +20,7 @@ import torch
 
 import layout_algebra_amd as la
 import synth
-from parity import assert_close, oracle_gemm
+from parity import assert_close, band_rows, oracle_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +76,53 @@ def test_split_shapes(case, out_kind):
     assert d["workspace_bytes"] == d["split_k"] * M * N * 4
     ref = oracle_gemm(a, b, "bf16", 0.75, -1.25, c.to(torch.float32))
     assert_close(got, ref, K, a, b, out_kind, "split %s" % (case,), beta=-1.25)
+
+
+FAST = [
+    # (M, N, K, B stored [N, K]): the 256-wide kernel's split form (at most 64 tiles)
+    (256, 1024, 4096, False),
+    (300, 520, 2048, False),      # M and N edges
+    (129, 4096, 2048, True),      # one row past the skinny range, M edge
+    (1000, 1024, 4096, True),
+    (512, 2048, 8192, False),
+]
+
+
+@pytest.mark.parametrize("out_kind", ["f32", "bf16"])
+@pytest.mark.parametrize("case", FAST, ids=[str(c) for c in FAST])
+def test_fast_split_shapes(case, out_kind):
+    M, N, K, km = case
+    print("fast split", case, out_kind, flush=True)
+    seed = 29 * M + N + 3 * K + km
+    a = synth.normal((M, K), seed, "bf16")
+    b = synth.normal((K, N), seed + 1, "bf16", 0.05)
+    c = synth.uniform((M, N), seed + 2, "f32").to(synth.torch_dtype(out_kind))
+    got, d = run_split(a, b, "bf16", out_kind, km, 1.5, 0.5, c)
+    assert d["split_k"] > 1 and d["split_kernel"].startswith("fast_"), d
+    ref = oracle_gemm(a, b, "bf16", 1.5, 0.5, c.to(torch.float32))
+    assert_close(got, ref, K, a, b, out_kind, "fast split %s" % (case,), beta=0.5)
+
+
+def test_fast_split_prefill_shape_sampled_rows():
+    """512 x 4096 x 14336, B stored [N, K] (4 ranges over 32 tiles), on rows covering both tile bands."""
+    M, N, K = 512, 4096, 14336
+    a = synth.normal((M, K), 551, "bf16")
+    b = synth.normal((K, N), 552, "bf16", 0.02)
+    got, d = run_split(a, b, "bf16", "bf16", True)
+    assert d["split_k"] == 4 and d["split_grid"] == [32, 4], d
+    rows = band_rows(M, seed=553)
+    ref = oracle_gemm(a, b, "bf16", rows=rows)
+    assert_close(got[rows], ref, K, a, b, "bf16", "fast split prefill shape")
+
+
+def test_fast_split_one_byte():
+    M, N, K = 512, 2048, 4096
+    a = synth.normal((M, K), 561, "f8e4m3", 1.0)
+    b = synth.normal((K, N), 562, "f8e5m2", 0.5)
+    got, d = run_split(a, b, "f8e4m3", "bf16", True, b_kind="f8e5m2")
+    assert d["split_k"] > 1 and d["split_kernel"] == "fast_f8_256x256x64", d
+    ref = oracle_gemm(a, b, "f8e4m3", b_kind="f8e5m2")
+    assert_close(got, ref, K, a, b, "bf16", "fast split f8")
 
 
 @pytest.mark.parametrize("case", [(16, 2048, 4096, True), (64, 1024, 2048, False)], ids=["nk", "kn"])

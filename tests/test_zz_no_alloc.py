@@ -31,7 +31,8 @@ def _case(M, N, K, km, out_type, out_kind, seed):
 @pytest.mark.parametrize("first,second", [
     ((128, 2048, 4096, True, "bf16"), (16, 1024, 2048, True, "bf16")),
     ((64, 4096, 14336, False, "f32"), (1, 4096, 4096, False, "f32")),
-], ids=["nk", "kn"])
+    ((512, 4096, 8192, True, "bf16"), (300, 520, 2048, False, "bf16")),   # the 256-wide kernel's split form
+], ids=["nk", "kn", "tiles"])
 def test_noalloc_matches_split_on_two_calls(first, second):
     lib = la.load()
     vp = ctypes.c_void_p
