@@ -55,6 +55,8 @@ hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args
     case KID_FAST_GU_KM: return by_types<CfgFastGUKM>(in_kind, out_kind, args, grid, stream, lds_image);
     case KID_FAST_256_AT: return by_types<CfgFast256AT>(in_kind, out_kind, args, grid, stream, lds_image);
     case KID_FAST_GU_AT: return by_types<CfgFastGUAT>(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_128: return by_types<CfgFast128>(in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_128_KM: return by_types<CfgFast128KM>(in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

@@ -69,6 +69,8 @@ enum KernelId : int {
   KID_SKINNY_128 = 21,   // KID_SKINNY_16 with 128 rows of A (M <= 128)
   KID_SKINNY_128_KM = 22,// KID_SKINNY_16_KM with 128 rows of A
   KID_SKINNY_F8_128 = 23,// KID_SKINNY_128_KM on byte pairs
+  KID_FAST_128 = 24,     // KID_FAST_256 with 128-row tiles: 8 waves of 64 x 64
+  KID_FAST_128_KM = 25,  // KID_FAST_128 for B stored [N, K]
   KID_COUNT
 };
 
@@ -100,6 +102,14 @@ struct CfgFastGU {
 struct CfgFast256KM : CfgFast256 {
   static constexpr bool BKMAJOR = true;
   static constexpr int BB = 2, BMb = 3, BS = 4;
+};
+// 128 x 256 tiles (twice the tiles of the 256-wide kernel for mid-size M): 8 waves (2 x 4) of 64 x 64,
+// the same K blocks, swizzles and ping-pong; 4 stages of 24 KiB.
+struct CfgFast128 : CfgFast256 {
+  static constexpr int BM = 128;
+};
+struct CfgFast128KM : CfgFast256KM {
+  static constexpr int BM = 128;
 };
 struct CfgFastGUKM : CfgFastGU {
   static constexpr bool BKMAJOR = true;

@@ -69,7 +69,8 @@ struct CopyChunk { int64_t row, col; };
 
 bool fast_kid(int kid) {
   return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
-         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8 || kid == lak::KID_FAST_GU_F8;
+         kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8 || kid == lak::KID_FAST_GU_F8 ||
+         kid == lak::KID_FAST_128 || kid == lak::KID_FAST_128_KM;
 }
 
 bool skinny_kid(int kid) {
@@ -638,7 +639,7 @@ std::string describe(const gemm_plan_s& p) {
                                       "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8",
                                       "fast_gate_up_f8", "skinny_bkmajor", "skinny_f8", "skinny", "skinny",
                                       "skinny_bkmajor", "skinny_bkmajor", "skinny_f8", "skinny_f8", "skinny",
-                                      "skinny_bkmajor", "skinny_f8"};
+                                      "skinny_bkmajor", "skinny_f8", "fast", "fast_bkmajor"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -940,6 +941,15 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
     // edge tiles the bar is 64 workgroups (measured: 40 edge tiles 11.1 us on
     // the general kernel against 15.0; 96 tiles 16.9 against 12.1).
     if (!large && p.kid == fk && ftm * ftn * d.batch < (whole ? 32 : 64)) p.kid = lak::KID_TILED_64;
+    // Up to 128 tiles of 256 x 256 (plain GEMMs, A stored [M, K]): 128-row tiles, twice as many
+    // workgroups on the otherwise idle CUs.  Measured on one box (bf16 -> bf16, 256-row -> 128-row
+    // tiles, us): 192 x 28672 x 8192 188.9 -> 148.6 (B [N, K] 193.3 -> 165.4); 256 x 28672 x 8192
+    // 210.3 -> 161.3; 384 x 11008 x 4096 69.9 -> 56.6; 512 x 11008 x 4096 70.1 -> 62.0;
+    // 1024 x 4096 x 14336 224.0 -> 173.6 (278.8 -> 215.7); 2048 x 4096 x 4096 79.3 -> 73.2; from
+    // 172 tiles on slower (1024 x 11008 x 4096 88.5 -> 117.3, 384 x 28672 x 8192 209.7 -> 265.9,
+    // 4096^3 109.4 -> 136.5).
+    if (!large && (p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_256_KM) && ftm * ftn * d.batch <= 128)
+      p.kid = kmajor ? lak::KID_FAST_128_KM : lak::KID_FAST_128;
     // M <= 128: stream B once through the skinny kernel with 16, 32, 64 or 128 rows of A
     // (HBM-bound shapes); B stored [N, K] streams strips of K-contiguous rows.  With more than 32
     // rows only on grids of at least 128 strips: measured ahead of the general kernel on 28672 x

@@ -333,12 +333,12 @@ def test_split_form_workspace_bound():
 
 
 def test_fast_split_form_and_padding_rule():
-    """The 256-wide kernel's split form on grids of at most 64 tiles, and edge tiles padded up to 4/3
-    kept on the 256-wide kernel from 80 tiles on."""
+    """The 256-wide kernel's split form on grids of at most 64 tiles; edge tiles padded up to 4/3
+    kept on the 256-wide kernel from 80 tiles on; 128-row tiles for grids of at most 128 tiles."""
     def plan(m, n, k, km=False):
         return la.gemm_plan(m, n, k, la.BF16, la.BF16, b_kmajor=km).describe()
     d = plan(512, 4096, 14336, True)
-    assert d["kernel"].startswith("fast_bkmajor_") and d["split_k"] == 4 and d["split_grid"] == [32, 4]
+    assert d["kernel"] == "fast_bkmajor_128x256x32" and d["split_k"] == 4 and d["split_grid"] == [32, 4]
     assert d["split_kernel"] == "fast_bkmajor_256x256x32"
     d = plan(256, 4096, 14336)
     assert d["kernel"].startswith("tiled_64x64") and d["split_k"] == 8 and d["split_kernel"] == "fast_256x256x32"
@@ -348,11 +348,18 @@ def test_fast_split_form_and_padding_rule():
     assert plan(4096, 4096, 4096)["split_k"] == 1
     assert plan(512, 4096, 512)["split_k"] == 1                                 # ranges under 8 K blocks
     assert plan(384, 28672, 8192)["kernel"].startswith("fast_256x256")          # 224 tiles, padding 4/3
-    assert plan(384, 11008, 4096)["kernel"].startswith("fast_256x256")          # 86 tiles
+    assert plan(384, 11008, 4096)["kernel"].startswith("fast_128x256")          # 86 tiles of 256 rows
     assert plan(192, 11008, 4096)["kernel"].startswith("tiled_64x64")           # 43 tiles
     assert plan(320, 28672, 8192)["kernel"].startswith("tiled_64x64")           # padding 1.6
     d = la.gemm_plan(512, 4096, 14336, la.F8E4M3, la.BF16, b_kmajor=True).describe()
     assert d["kernel"] == "fast_f8_256x256x64" and d["split_k"] == 4 and d["split_kernel"] == "fast_f8_256x256x64"
+    assert plan(192, 28672, 8192)["kernel"] == "fast_128x256x32"                 # 112 tiles of 256 rows
+    assert plan(2048, 4096, 4096, True)["kernel"] == "fast_bkmajor_128x256x32"   # 128 tiles
+    assert plan(1024, 11008, 4096)["kernel"] == "fast_256x256x32"                # 172 tiles
+    assert plan(4096, 4096, 4096)["kernel"] == "fast_256x256x32"
+    d = la.gemm_plan(2048, 1024, 512, la.BF16, la.BF16, large_tiles=True).describe()
+    assert d["kernel"] == "fast_256x256x32"                                      # pinned: the largest tile
+    assert la.gemm_plan(256, 256, 256, la.BF16, la.BF16, batch=64).describe()["kernel"] == "fast_128x256x32"
 
 
 def test_small_grids_take_64x64_tiles_unless_pinned():
@@ -364,12 +371,12 @@ def test_small_grids_take_64x64_tiles_unless_pinned():
     for shape in ((256, 256, 256), (1024, 1536, 1024)):
         assert kern(*shape)["kernel"].startswith("tiled_64x64"), shape
         assert kern(*shape, large_tiles=True)["kernel"].startswith("fast_256x256"), shape
-    assert kern(2048, 1024, 512)["kernel"].startswith("fast_256x256")          # 32 workgroups
-    assert kern(256, 256, 256, batch=32)["kernel"].startswith("fast_256x256")  # batch counts
+    assert kern(2048, 1024, 512)["kernel"].startswith("fast_128x256")          # 32 workgroups (128-row tiles)
+    assert kern(256, 256, 256, batch=32)["kernel"].startswith("fast_128x256")  # batch counts
     assert kern(512, 512, 128, gate_up=True)["kernel"].startswith("tiled_64x64")
     # edge tiles on the full-tile kernel: M and N inside a tile, K ending inside a K block from
     # K = 256 on, padding within 1.3x and at least 64 workgroups
-    assert kern(4000, 4000, 1000)["kernel"].startswith("fast_256x256")
+    assert kern(4000, 4000, 1000)["kernel"].startswith("fast_256x256")       # 256 tiles
     assert kern(4000, 4000, 200)["kernel"].startswith("tiled_64x64")          # short K with a tail
     assert kern(1088, 1920, 512)["kernel"].startswith("tiled_64x64")         # 40 edge tiles
     assert kern(1088, 1920, 512, large_tiles=True)["kernel"].startswith("fast_256x256")
