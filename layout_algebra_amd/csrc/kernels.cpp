@@ -57,11 +57,13 @@ KernelShape kernel_shape(int kid) {
       return s;
     }
     case KID_FAST_F8:
+    case KID_FAST_F8_128:
     case KID_FAST_GU_F8: {
       // the K-major full-tile kernels seen in one-byte elements: a K block of 64 codes per row
       // (64-byte rows) under Swizzle{2,4,4} (16-byte chunks, rows 4 apart in bits 8-9), one
       // 32x32x64 product per block
-      KernelShape s = kid == KID_FAST_F8 ? fast_shape<CfgFast256KM>() : fast_shape<CfgFastGUKM>();
+      KernelShape s = kid == KID_FAST_F8 ? fast_shape<CfgFast256KM>()
+                    : kid == KID_FAST_F8_128 ? fast_shape<CfgFast128KM>() : fast_shape<CfgFastGUKM>();
       s.bk = 2 * CfgFast256KM::BK;
       s.mfma_k = 64;
       s.sw_a[0] = s.sw_b[0] = 2;
@@ -120,6 +122,7 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_SKINNY_F8_128: return launch_skinny(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_FAST_F8:
+    case KID_FAST_F8_128:
     case KID_FAST_GU_F8: return launch_fast_f8(kid, in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }

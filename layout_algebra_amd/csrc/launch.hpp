@@ -71,6 +71,7 @@ enum KernelId : int {
   KID_SKINNY_F8_128 = 23,// KID_SKINNY_128_KM on byte pairs
   KID_FAST_128 = 24,     // KID_FAST_256 with 128-row tiles: 8 waves of 64 x 64
   KID_FAST_128_KM = 25,  // KID_FAST_128 for B stored [N, K]
+  KID_FAST_F8_128 = 26,  // KID_FAST_128_KM on byte pairs (one-byte inputs)
   KID_COUNT
 };
 

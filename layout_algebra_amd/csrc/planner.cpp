@@ -70,7 +70,7 @@ struct CopyChunk { int64_t row, col; };
 bool fast_kid(int kid) {
   return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
          kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8 || kid == lak::KID_FAST_GU_F8 ||
-         kid == lak::KID_FAST_128 || kid == lak::KID_FAST_128_KM;
+         kid == lak::KID_FAST_128 || kid == lak::KID_FAST_128_KM || kid == lak::KID_FAST_F8_128;
 }
 
 bool skinny_kid(int kid) {
@@ -639,7 +639,7 @@ std::string describe(const gemm_plan_s& p) {
                                       "tiled", "fast_atrans", "fast_gate_up_atrans", "tiled_f32", "fast_f8",
                                       "fast_gate_up_f8", "skinny_bkmajor", "skinny_f8", "skinny", "skinny",
                                       "skinny_bkmajor", "skinny_bkmajor", "skinny_f8", "skinny_f8", "skinny",
-                                      "skinny_bkmajor", "skinny_f8", "fast", "fast_bkmajor"};
+                                      "skinny_bkmajor", "skinny_f8", "fast", "fast_bkmajor", "fast_f8"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -714,13 +714,24 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   v.stride_a = d.stride_a / 2;
   v.stride_b = d.stride_b / 2;
   v.a_type = v.b_type = GEMM_BF16;
-  v.flags |= GEMM_FLAG_LARGE_TILES;          // the full-tile kernel at every grid size
-  const gemm_status st = build(v, p, err);
+  // The pair view's own choice where it has a one-byte form (the K-major 256-wide kernel, its
+  // 128-row tiles, the skinny kernels), else the full-tile kernel at every grid size.
+  auto has_f8_form = [](int kid) {
+    return kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM || kid == lak::KID_FAST_128_KM ||
+           kid == lak::KID_SKINNY_16_KM || kid == lak::KID_SKINNY_32_KM || kid == lak::KID_SKINNY_64_KM ||
+           kid == lak::KID_SKINNY_128_KM;
+  };
+  gemm_status st = build(v, p, err);
+  if (st != GEMM_OK || !has_f8_form(p.kid)) {
+    v.flags |= GEMM_FLAG_LARGE_TILES;
+    st = build(v, p, err);
+  }
   if (st != GEMM_OK) return st;
   const bool runs = d.m > 0 && d.n > 0 && d.k > 0;
   // the pair view's kernel and its one-byte counterpart
   int pair_kid = p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
   int kid8 = p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
+  if (p.kid == lak::KID_FAST_128_KM) pair_kid = p.kid, kid8 = lak::KID_FAST_F8_128;
   if (p.kid == lak::KID_SKINNY_16_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8;
   if (p.kid == lak::KID_SKINNY_32_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_32;
   if (p.kid == lak::KID_SKINNY_64_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_64;

@@ -3,8 +3,9 @@ for plain GEMMs whose grid of 256 x 256 tiles would hold at most 128 of them.
 
 Cases, each planned without flags (the planner's own choice is asserted): whole tiles, M and N
 ending inside a tile, a K tail, B stored [K, N] and [N, K], bf16 and fp16 inputs, fp32 / bf16 /
-fp16 outputs with alpha, beta and C in NaN-padded rows, a batch, the three row reductions, and
-the staged LDS image of an edge tile against the planner's map.
+fp16 outputs with alpha, beta and C in NaN-padded rows, a batch, the three row reductions, the
+staged LDS image of an edge tile against the planner's map, and one-byte inputs (the K-major
+configuration on byte pairs) with edges and a K tail.
 """
 import numpy as np
 import pytest
@@ -123,3 +124,34 @@ def test_fast128_lds_image_of_an_edge_tile():
                 assert got[la.gemm_plan_lds_offset(plan, 1, k, n)] == bbits[k, tn * 256 + n], (k, n)
                 checked += 1
     assert checked == (M - tm * 128) * 32 + 32 * (N - tn * 256)
+
+
+F8_SHAPES = [
+    # (M, N, K, A format, B format): one-byte inputs on 128-row tiles (B stored [N, K])
+    (1024, 4096, 2048, "f8e4m3", "f8e4m3"),
+    (1024, 4096, 1040, "f8e4m3", "f8e5m2"),  # a K tail of 16 codes
+    (1000, 4104, 1024, "f8e5m2", "f8e4m3"),  # M and N edges
+]
+
+
+@pytest.mark.parametrize("out_kind", ["bf16", "f32"])
+@pytest.mark.parametrize("case", F8_SHAPES, ids=[str(c) for c in F8_SHAPES])
+def test_fast128_one_byte(case, out_kind):
+    M, N, K, ka, kb = case
+    print("fast128 f8", case, out_kind, flush=True)
+    a = synth.normal((M, K), 101 + M, ka, 1.0)
+    b = synth.normal((K, N), 102 + N, kb, 0.5)
+    c = synth.uniform((M, N), 103 + K, "f32").to(synth.torch_dtype(out_kind))
+    ld = N + 8
+    plan = la.gemm_plan(M, N, K, la.F8E4M3 if ka == "f8e4m3" else la.F8E5M2, CODE[out_kind], ldc=ld, b_kmajor=True,
+                        b_type=la.F8E4M3 if kb == "f8e4m3" else la.F8E5M2)
+    assert plan.describe()["kernel"] == "fast_f8_128x256x64", plan.describe()["kernel"]
+    Cbuf = torch.full((M, ld), float("nan"), dtype=synth.torch_dtype(out_kind), device=DEV)
+    C = Cbuf[:, :N]
+    C.copy_(c.to(DEV))
+    la.gemm_run(plan, a.to(DEV), b.t().contiguous().to(DEV), C, 1.0, 0.5)
+    torch.cuda.synchronize()
+    assert torch.isnan(Cbuf[:, N:].cpu().float()).all(), "a store landed in C's row padding"
+    rows = band_rows(M, band=128, wave_rows=64, seed=M + N)
+    ref = oracle_gemm(a, b, ka, 1.0, 0.5, c.to(torch.float32), rows=rows, b_kind=kb)
+    assert_close(C.cpu()[rows], ref, K, a, b, out_kind, "fast128 f8 %s" % (case,), beta=0.5)
