@@ -17,6 +17,7 @@ Workloads (seeded synthetic inputs, see synth/):
   skinny      16 x 28672 x 8192 bf16 -> fp32 (HBM-bound; two B buffers rotate)
   skinny_kmajor, skinny_f8  the same with B stored [28672, 8192] (bf16, E4M3)
   skinny_split  32 x 4096 x 14336 bf16 -> fp32, B stored [4096, 14336], K split (gemm_run_split)
+  prefill_384   384 x 11008 x 4096 bf16 -> bf16 (128-row tiles of the 256-wide kernel)
   square4096_f32, square4096_f8, gate_up_f8  binary32 and one-byte inputs
   square256, ragged
   rms_norm       row normalisation of 2^20 f32 rows of 256 (HBM-bound)

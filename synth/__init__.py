@@ -114,6 +114,11 @@ WORKLOADS = {
         "skinny_f8", 16, 28672, 8192, "f8e4m3", "f32", 1.0, 0.0,
         Dist("normal", 0.0, 1.0), Dist("normal", 0.0, 0.25), (5201, 5202, 5203), b_kmajor=True,
         notes="M=16 bandwidth-bound GEMM, E4M3 A and B, B stored [28672, 8192]"),
+    # 384 tokens through a 4096 -> 11008 projection: 129 tiles of 128 x 256 (86 of 256 x 256)
+    "prefill_384": Workload(
+        "prefill_384", 384, 11008, 4096, "bf16", "bf16", 1.0, 0.0,
+        Dist("normal", 0.0, 1.0 / 64), Dist("normal", 0.0, 1.0 / 64), (5401, 5402),
+        notes="mid-size M: 384 x 11008 x 4096 GEMM on 128-row tiles"),
     # a decode batch of 32 through a 14336 -> 4096 projection: 64 strips of B, K cut into ranges
     "skinny_split": Workload(
         "skinny_split", 32, 4096, 14336, "bf16", "f32", 1.0, 0.0,

@@ -4,8 +4,9 @@ for plain GEMMs whose grid of 256 x 256 tiles would hold at most 128 of them.
 Cases, each planned without flags (the planner's own choice is asserted): whole tiles, M and N
 ending inside a tile, a K tail, B stored [K, N] and [N, K], bf16 and fp16 inputs, fp32 / bf16 /
 fp16 outputs with alpha, beta and C in NaN-padded rows, a batch, the three row reductions, the
-staged LDS image of an edge tile against the planner's map, and one-byte inputs (the K-major
-configuration on byte pairs) with edges and a K tail.
+staged LDS image of an edge tile against the planner's map, one-byte inputs (the K-major
+configuration on byte pairs) with edges and a K tail, and the prefill_384 workload in full as the
+bench runs it.
 """
 import numpy as np
 import pytest
@@ -155,3 +156,16 @@ def test_fast128_one_byte(case, out_kind):
     rows = band_rows(M, band=128, wave_rows=64, seed=M + N)
     ref = oracle_gemm(a, b, ka, 1.0, 0.5, c.to(torch.float32), rows=rows, b_kind=kb)
     assert_close(C.cpu()[rows], ref, K, a, b, out_kind, "fast128 f8 %s" % (case,), beta=0.5)
+
+
+def test_prefill_workload_full():
+    """The prefill_384 workload (384 x 11008 x 4096 bf16) in full, planned as the bench plans it."""
+    w = synth.WORKLOADS["prefill_384"]
+    x = synth.make_inputs(w)
+    plan = la.gemm_plan(w.M, w.N, w.K, la.BF16, la.BF16)
+    assert plan.describe()["kernel"] == "fast_128x256x32" and plan.describe()["grid"] == 129
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    la.gemm_run(plan, x["A"].to(DEV), x["B"].to(DEV), C)
+    torch.cuda.synchronize()
+    ref = oracle_gemm(x["A"], x["B"], "bf16")
+    assert_close(C.cpu(), ref, w.K, x["A"], x["B"], "bf16", "prefill_384 workload")
