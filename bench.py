@@ -51,8 +51,10 @@ NORM_SOURCES = ("rms_norm.hip", "norm.hpp")
 ATTN_SOURCES = ("attention.hip", "attention.hpp")
 # GEMM kernel families by the prefix of the planned kernel's name
 GEMM_SOURCES = {"fast_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"), "fast_gate_up_f8": ("gemm_fast_f8.hip", "gemm_fast.hpp"),
-                "fast_": ("gemm_fast.hip", "gemm_fast.hpp"), "tiled_f32": ("gemm_f32.hip",),
-                "tiled_": ("gemm_tiled.hip",), "skinny_": ("gemm_skinny.hip",)}
+                "fast_": ("gemm_fast.hip", "gemm_fast_gu.hip", "gemm_fast_128.hip", "gemm_fast.hpp"),
+                "tiled_f32": ("gemm_f32.hip",),
+                "tiled_": ("gemm_tiled.hpp", "gemm_tiled_64.hip", "gemm_tiled_128.hip", "gemm_tiled_p3.hip"),
+                "skinny_": ("gemm_skinny.hip",)}
 
 
 # host code that decides which instantiation a GEMM plan launches, and with which grid

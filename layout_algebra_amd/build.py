@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblagemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["layout.cpp", "planner.cpp", "capi.cpp", "kernels.cpp", "gemm_tiled.hip", "gemm_f32.hip", "gemm_fast.hip", "gemm_fast_f8.hip", "gemm_skinny.hip", "rms_norm.hip", "row_reduce.hip", "split_sum.hip", "attention.hip", "probe.hip"]
+SOURCES = ["layout.cpp", "planner.cpp", "capi.cpp", "kernels.cpp", "gemm_tiled_64.hip", "gemm_tiled_128.hip", "gemm_tiled_p3.hip", "gemm_f32.hip", "gemm_fast.hip", "gemm_fast_gu.hip", "gemm_fast_128.hip", "gemm_fast_f8.hip", "gemm_skinny.hip", "rms_norm.hip", "row_reduce.hip", "split_sum.hip", "attention.hip", "probe.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument"]

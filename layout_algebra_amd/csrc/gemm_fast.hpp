@@ -3,7 +3,7 @@
 // C, see Fast::a_limit and store_band), and K may end inside a K block (the
 // remaining K % BK values are added after the main loop, Fast::k_tail).
 //
-// Differences from the general kernel (gemm_tiled.hip):
+// Differences from the general kernel (gemm_tiled.hpp):
 //  * Operands go global -> LDS directly (global_load_lds_dwordx4): each wave
 //    instruction moves 64 x 16 bytes into one contiguous kilobyte of LDS, lane
 //    l landing at byte 16 l.  The swizzle is therefore applied on the source
@@ -662,5 +662,57 @@ __global__ void __launch_bounds__(C::WM * C::WN * 64) gemm_fast_lds_image(const 
   block_barrier();
   for (int i = tid; i < F::STAGE; i += F::NT) g.dbg_out[i] = lds[i];
 }
+
+// ------------------------------------------------------------------ launch
+// Launch of one configuration for every input / output type (instantiated by gemm_fast.hip,
+// gemm_fast_gu.hip and gemm_fast_128.hip, one translation unit per group of configurations).
+namespace {
+
+template <class C, class TI, class TO>
+hipError_t go_fast(const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  constexpr int NT = C::WM * C::WN * 64;
+  if (img) {
+    hipLaunchKernelGGL((gemm_fast_lds_image<TI, TO, C>),
+                       dim3(1), dim3(NT), 0, s, a);
+  } else {
+    const bool kt = a.K % C::BK != 0;
+    if constexpr (C::NB == 1) {
+      // row reductions (single-output plans only) run their own instantiation
+      if (a.red != RED_NONE) {
+        if (kt)
+          hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, true, true>), grid, dim3(NT), 0, s, a);
+        else
+          hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, true, false>), grid, dim3(NT), 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    if (kt)
+      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, false, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_fast_pp_kernel<TI, TO, C, false, false>), grid, dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t by_types(int in_kind, int out_kind, const TiledArgs& a, dim3 grid, hipStream_t s, bool img) {
+  if (in_kind == IN_BF16) {
+    if (out_kind == OUT_F32) return go_fast<C, InBF16, OutF32>(a, grid, s, img);
+    if (out_kind == OUT_BF16) return go_fast<C, InBF16, OutBF16>(a, grid, s, img);
+    if (out_kind == OUT_F16) return go_fast<C, InBF16, OutF16>(a, grid, s, img);
+  } else if (in_kind == IN_F16) {
+    if (out_kind == OUT_F32) return go_fast<C, InF16, OutF32>(a, grid, s, img);
+    if (out_kind == OUT_BF16) return go_fast<C, InF16, OutBF16>(a, grid, s, img);
+    if (out_kind == OUT_F16) return go_fast<C, InF16, OutF16>(a, grid, s, img);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fast_gu(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
+                          bool lds_image);
+hipError_t launch_fast_128(int kid, int in_kind, int out_kind, const TiledArgs& args, dim3 grid, hipStream_t stream,
+                           bool lds_image);
 
 }  // namespace lak

@@ -42,6 +42,10 @@
 //   * Epilogue: alpha * acc + beta * C_old in FP32 (C_old read only when
 //     beta != 0), rounded to nearest even for 16-bit outputs, written only
 //     inside [0,M) x [0,N).
+// The kernels' instantiations are spread over gemm_tiled_{64,128,p3}.hip (one
+// translation unit per tile configuration, compiled in parallel).
+#pragma once
+
 #include <type_traits>
 
 #include "kernel_common.hpp"
@@ -54,7 +58,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // Sixteen zero bytes in device memory: staging loads of elements outside the
 // matrix read from here, so the loaded registers need no masking afterwards.
-__device__ __attribute__((aligned(16))) uint16_t kZeroChunk[8];
+static __device__ __attribute__((aligned(16))) uint16_t kZeroChunk[8];
 
 // Eight 16-bit elements of one staging load, packed in pairs.
 struct Chunk8 { u32x4 w; };   // one aligned 16-byte load
@@ -505,6 +509,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_lds_image(const Tiled
 }
 
 // ------------------------------------------------------------------ dispatch
+// The general kernel's tile configurations, each in its own translation unit (launch_tiled, in
+// gemm_tiled_p3.hip, picks one by kernel id).
+hipError_t launch_tiled_128(int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
+                            const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
+hipError_t launch_tiled_64(int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
+                           const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image);
+
 namespace {
 
 template <class TI, class TO, int BM, int BN, int WM, int WN, int V, bool GU, bool BKM, bool P3 = false, bool AT = false>
@@ -568,8 +579,8 @@ hipError_t p3_by_vec(int vec, bool gu, bool km, const TiledArgs& a, dim3 grid, h
   return hipErrorInvalidValue;
 }
 
-hipError_t p3_by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, dim3 grid,
-                       hipStream_t s, bool img) {
+inline hipError_t p3_by_types(int in_kind, int out_kind, int vec, bool gu, bool km, const TiledArgs& a, dim3 grid,
+                              hipStream_t s, bool img) {
   if (in_kind == IN_BF16) {
     if (out_kind == OUT_F32) return p3_by_vec<InBF16, OutF32>(vec, gu, km, a, grid, s, img);
     if (out_kind == OUT_BF16) return p3_by_vec<InBF16, OutBF16>(vec, gu, km, a, grid, s, img);
@@ -583,19 +594,5 @@ hipError_t p3_by_types(int in_kind, int out_kind, int vec, bool gu, bool km, con
 }
 
 }  // namespace
-
-hipError_t launch_tiled(int kid, int in_kind, int out_kind, int vec, bool gate_up, bool b_kmajor, bool a_trans,
-                        const TiledArgs& args, dim3 grid, hipStream_t stream, bool lds_image) {
-  switch (kid) {
-    case KID_TILED_128:
-      return by_types<128, 128, 2, 2>(in_kind, out_kind, vec, gate_up, b_kmajor, a_trans, args, grid, stream, lds_image);
-    case KID_TILED_64:
-      return by_types<64, 64, 2, 1>(in_kind, out_kind, vec, gate_up, b_kmajor, a_trans, args, grid, stream, lds_image);
-    case KID_TILED_64_P3:
-      if (a_trans) return hipErrorInvalidValue;
-      return p3_by_types(in_kind, out_kind, vec, gate_up, b_kmajor, args, grid, stream, lds_image);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 }  // namespace lak

@@ -54,9 +54,9 @@ def test_traffic_lines_parse_and_follow_the_source_hash(tmp_path, monkeypatch):
     assert "prefetch=3" in bench.gemm_plan_summary("ragged")
     # each GEMM workload hashes the sources of the kernel family its plan selects
     assert "gemm_fast.hpp" in bench.workload_sources("square4096")
-    assert "gemm_tiled.hip" not in bench.workload_sources("square4096")
+    assert "gemm_tiled.hpp" not in bench.workload_sources("square4096")
     assert "gemm_skinny.hip" in bench.workload_sources("skinny")
-    assert "gemm_tiled.hip" in bench.workload_sources("ragged")
+    assert "gemm_tiled.hpp" in bench.workload_sources("ragged")
     assert bench.kernel_source_hash("ragged") != h != bench.kernel_source_hash("skinny")
     prof = tmp_path / "profiles"
     prof.mkdir()
