@@ -68,3 +68,31 @@ def test_noalloc_without_split_form_runs_as_gemm_run():
     la.gemm_run_split_noalloc(plan, A, B, C2)
     torch.cuda.synchronize()
     assert torch.equal(C1.cpu(), C2.cpu())
+
+
+def test_noalloc_under_graph_capture():
+    """The call this entry point is for: captured into a HIP graph (torch's capture forbids allocating
+    calls on the capturing thread), replayed four times with eager work between the replays, each
+    replay equal bit for bit to an eager gemm_run_split of the same inputs."""
+    M, N, K = 16, 2048, 4096
+    a, b, c, plan, A, B = _case(M, N, K, True, la.BF16, "bf16", 971)
+    C0 = c.to(DEV)
+    want = C0.clone()
+    ws = torch.empty(la.gemm_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    la.gemm_run_split(plan, A, B, want, 1.0, 0.5, ws)
+    C = C0.clone()
+    la.gemm_run_split_noalloc(plan, A, B, C, 1.0, 0.5)       # first call on this device: address lookup
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), want.cpu())
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            la.gemm_run_split_noalloc(plan, A, B, C, 1.0, 0.5, stream=s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        C.copy_(C0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C.cpu(), want.cpu()), "replay %d" % i
