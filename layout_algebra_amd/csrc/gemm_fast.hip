@@ -14,7 +14,9 @@ hipError_t launch_fast(int kid, int in_kind, int out_kind, const TiledArgs& args
     case KID_FAST_GU_KM:
     case KID_FAST_GU_AT: return launch_fast_gu(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_FAST_128:
-    case KID_FAST_128_KM: return launch_fast_128(kid, in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_128_KM:
+    case KID_FAST_128_KM64:
+    case KID_FAST_128_K64: return launch_fast_128(kid, in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }
 }

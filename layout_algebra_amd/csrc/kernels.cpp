@@ -47,6 +47,8 @@ KernelShape kernel_shape(int kid) {
     case KID_FAST_GU_AT: return fast_shape<CfgFastGUAT>();
     case KID_FAST_128: return fast_shape<CfgFast128>();
     case KID_FAST_128_KM: return fast_shape<CfgFast128KM>();
+    case KID_FAST_128_KM64: return fast_shape<CfgFast128KM64>();
+    case KID_FAST_128_K64: return fast_shape<CfgFast128K64>();
     case KID_TILED_F32: {
       // K-contiguous blocks: two 64-byte rows of 16 binary32 values per row under Swizzle{2,2,4};
       // M/N-contiguous blocks: rows of 128 values under Swizzle{1,5,5}
@@ -107,7 +109,9 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_FAST_256_AT:
     case KID_FAST_GU_AT:
     case KID_FAST_128:
-    case KID_FAST_128_KM: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
+    case KID_FAST_128_KM:
+    case KID_FAST_128_KM64:
+    case KID_FAST_128_K64: return launch_fast(kid, in_kind, out_kind, args, grid, stream, lds_image);
     case KID_SKINNY_16:
     case KID_SKINNY_32:
     case KID_SKINNY_64:

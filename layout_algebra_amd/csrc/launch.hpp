@@ -72,6 +72,8 @@ enum KernelId : int {
   KID_FAST_128 = 24,     // KID_FAST_256 with 128-row tiles: 8 waves of 64 x 64
   KID_FAST_128_KM = 25,  // KID_FAST_128 for B stored [N, K]
   KID_FAST_F8_128 = 26,  // KID_FAST_128_KM on byte pairs (one-byte inputs)
+  KID_FAST_128_KM64 = 27,  // KID_FAST_128_KM with K blocks of 64 (128-byte row segments of A and B)
+  KID_FAST_128_K64 = 28,   // KID_FAST_128 with K blocks of 64 (128-byte row segments of A)
   KID_COUNT
 };
 
@@ -111,6 +113,20 @@ struct CfgFast128 : CfgFast256 {
 };
 struct CfgFast128KM : CfgFast256KM {
   static constexpr int BM = 128;
+};
+// The same tiles with K blocks of 64 (16-bit inputs, K a multiple of 64): 3 stages of 48 KiB, A (and
+// K-major B) rows of 128 bytes under Swizzle{3,3,4}.  Measured against K blocks of 32 on one box
+// (bf16 -> bf16, us, B [N, K] / [K, N]): 1024 x 4096 x 14336 168.6 -> 150.2 / 174.1 -> 155.4;
+// 256 x 28672 x 8192 179.0 -> 153.3 / 162.4 -> 147.0; 384 x 11008 x 4096 58.0 -> 52.1 / 58.6 -> 53.7;
+// 1024 x 4096 x 2048 29.8 -> 29.6 / 32.1 -> 30.6.
+struct CfgFast128K64 : CfgFast128 {
+  static constexpr int BK = 64, STAGES = 3;
+  static constexpr int AB = 3, AM = 3, AS = 4;   // A: 128-byte rows; B keeps its 512-byte rows
+};
+struct CfgFast128KM64 : CfgFast128KM {
+  static constexpr int BK = 64, STAGES = 3;
+  static constexpr int AB = 3, AM = 3, AS = 4;   // 128-byte rows
+  static constexpr int BB = 3, BMb = 3, BS = 4;
 };
 struct CfgFastGUKM : CfgFastGU {
   static constexpr bool BKMAJOR = true;

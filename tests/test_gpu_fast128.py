@@ -1,5 +1,6 @@
 """GPU parity of the 256-wide kernel with 128-row tiles (8 waves of 64 x 64), which the planner takes
-for plain GEMMs whose grid of 256 x 256 tiles would hold at most 128 of them.
+for plain GEMMs whose grid of 256 x 256 tiles would hold at most 128 of them (K blocks of 64 when
+K is a multiple of 64, else of 32).
 
 Cases, each planned without flags (the planner's own choice is asserted): whole tiles, M and N
 ending inside a tile, a K tail, B stored [K, N] and [N, K], bf16 and fp16 inputs, fp32 / bf16 /
@@ -35,7 +36,8 @@ SHAPES = [
 def _plan(M, N, K, km, in_kind, out_kind, ldc):
     plan = la.gemm_plan(M, N, K, CODE[in_kind], CODE[out_kind], b_kmajor=km, ldc=ldc)
     d = plan.describe()
-    assert d["kernel"] == ("fast_bkmajor_128x256x32" if km else "fast_128x256x32"), d["kernel"]
+    bk = 64 if K % 64 == 0 else 32      # K blocks of 64 when K allows
+    assert d["kernel"] == ("fast_bkmajor_128x256x%d" if km else "fast_128x256x%d") % bk, d["kernel"]
     return plan
 
 
@@ -69,7 +71,7 @@ def test_fast128_batch():
     a = synth.normal((Z, M, K), 71, "bf16", 0.25)
     b = synth.normal((K, N), 72, "bf16", 0.25)
     plan = la.gemm_plan(M, N, K, la.BF16, la.F32, batch=Z, stride_b=0)
-    assert plan.describe()["kernel"] == "fast_128x256x32"
+    assert plan.describe()["kernel"] == "fast_128x256x64"
     C = torch.full((Z, M, N), float("nan"), dtype=torch.float32, device=DEV)
     Bb = torch.as_strided(b.to(DEV), (Z, K, N), (0, N, 1))
     la.gemm_run(plan, a.to(DEV), Bb, C)
@@ -85,7 +87,7 @@ def test_fast128_row_reductions(op):
     a = synth.normal((M, K), 81, "bf16", 0.25)
     b = synth.normal((K, N), 82, "bf16", 0.25)
     plan = la.gemm_plan(M, N, K, la.BF16, la.F32)
-    assert plan.describe()["kernel"] == "fast_128x256x32"
+    assert plan.describe()["kernel"] == "fast_128x256x64"
     C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
     R = torch.full((M,), 12345.0, dtype=torch.float32, device=DEV)
     la.gemm_run_reduce(plan, a.to(DEV), b.to(DEV), C, 1.0, 0.0, op, R)
@@ -106,7 +108,8 @@ def test_fast128_lds_image_of_an_edge_tile():
     b = synth.uniform((K, N), 92, "bf16")
     plan = la.gemm_plan(M, N, K, la.BF16, la.F32, b_kmajor=True)
     d = plan.describe()
-    assert d["kernel"] == "fast_bkmajor_128x256x32" and d["tile"] == [128, 256, 32], d
+    assert d["kernel"] == "fast_bkmajor_128x256x64" and d["tile"] == [128, 256, 64], d
+    bk = 64
     tm, tn = (M + 127) // 128 - 1, (N + 255) // 256 - 1
     img = torch.zeros(la.gemm_plan_lds_stage_bytes(plan) // 2, dtype=torch.int16, device=DEV)
     la.gemm_debug_lds_image(plan, a.to(DEV), b.t().contiguous().to(DEV), None, tm, tn, img)
@@ -115,16 +118,16 @@ def test_fast128_lds_image_of_an_edge_tile():
     abits, bbits = synth.bits(a), synth.bits(b)
     checked = 0
     for r in range(128):
-        for k in range(32):
+        for k in range(bk):
             if tm * 128 + r < M:
                 assert got[la.gemm_plan_lds_offset(plan, 0, r, k)] == abits[tm * 128 + r, k], (r, k)
                 checked += 1
-    for k in range(32):
+    for k in range(bk):
         for n in range(256):
             if tn * 256 + n < N:
                 assert got[la.gemm_plan_lds_offset(plan, 1, k, n)] == bbits[k, tn * 256 + n], (k, n)
                 checked += 1
-    assert checked == (M - tm * 128) * 32 + 32 * (N - tn * 256)
+    assert checked == (M - tm * 128) * bk + bk * (N - tn * 256)
 
 
 F8_SHAPES = [
@@ -163,7 +166,7 @@ def test_prefill_workload_full():
     w = synth.WORKLOADS["prefill_384"]
     x = synth.make_inputs(w)
     plan = la.gemm_plan(w.M, w.N, w.K, la.BF16, la.BF16)
-    assert plan.describe()["kernel"] == "fast_128x256x32" and plan.describe()["grid"] == 129
+    assert plan.describe()["kernel"] == "fast_128x256x64" and plan.describe()["grid"] == 129
     C = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device=DEV)
     la.gemm_run(plan, x["A"].to(DEV), x["B"].to(DEV), C)
     torch.cuda.synchronize()
