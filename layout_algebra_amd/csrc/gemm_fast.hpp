@@ -296,14 +296,17 @@ struct Fast {
   // one-byte elements one 64-deep product over both steps' reads.
   static __device__ __forceinline__ void mma_block(const Frags (&f)[SUB], f32x16 (&acc)[NBW][FM][FN]) {
     if constexpr (TI::f8) {
-      static_assert(SUB == 2, "a 64-deep one-byte product takes the two 16-byte reads of a 32-unit block");
+      // a 64-deep one-byte product takes the two 16-byte reads of a 32-unit step pair
+      static_assert(SUB % 2 == 0, "one-byte products pair the sub-steps");
 #pragma unroll
-      for (int t = 0; t < NBW; ++t)
+      for (int s = 0; s < SUB; s += 2)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int t = 0; t < NBW; ++t)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[t][i][j] = mfma_f8_32x32x64<TI>(f[0].a[i], f[1].a[i], f[0].b[t][j], f[1].b[t][j], acc[t][i][j]);
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[t][i][j] = mfma_f8_32x32x64<TI>(f[s].a[i], f[s + 1].a[i], f[s].b[t][j], f[s + 1].b[t][j], acc[t][i][j]);
     } else {
 #pragma unroll
       for (int s = 0; s < SUB; ++s) mma(f[s], acc);

@@ -68,6 +68,7 @@ hipError_t launch_fast_f8(int kid, int in_kind, int out_kind, const TiledArgs& a
   if (kid == KID_FAST_F8) return by_formats<CfgFast256KM>(in_kind, out_kind, args, grid, stream, lds_image);
   if (kid == KID_FAST_GU_F8) return by_formats<CfgFastGUKM>(in_kind, out_kind, args, grid, stream, lds_image);
   if (kid == KID_FAST_F8_128) return by_formats<CfgFast128KM>(in_kind, out_kind, args, grid, stream, lds_image);
+  if (kid == KID_FAST_F8_128_K64) return by_formats<CfgFast128KM64>(in_kind, out_kind, args, grid, stream, lds_image);
   return hipErrorInvalidValue;
 }
 

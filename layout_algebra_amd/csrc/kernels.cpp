@@ -58,6 +58,19 @@ KernelShape kernel_shape(int kid) {
       s.k_sub = 16;
       return s;
     }
+    case KID_FAST_F8_128_K64: {
+      // KID_FAST_128_KM64 in one-byte elements: K blocks of 128 codes (128-byte rows) under
+      // Swizzle{3,4,4} (the pair view's Swizzle{3,3,4} with 16-code chunks), two 32x32x64 products
+      // per 32x32 block and K block
+      KernelShape s = fast_shape<CfgFast128KM64>();
+      s.bk = 2 * CfgFast128KM64::BK;
+      s.mfma_k = 64;
+      s.sw_a[0] = s.sw_b[0] = 3;
+      s.sw_a[1] = s.sw_b[1] = 4;
+      s.sw_a[2] = s.sw_b[2] = 4;
+      s.in_bytes = 1;
+      return s;
+    }
     case KID_FAST_F8:
     case KID_FAST_F8_128:
     case KID_FAST_GU_F8: {
@@ -127,6 +140,7 @@ hipError_t launch_kernel(int kid, int in_kind, int out_kind, int vec, bool gate_
     case KID_TILED_F32: return launch_f32(out_kind, vec, b_kmajor, a_trans, args, grid, stream, lds_image);
     case KID_FAST_F8:
     case KID_FAST_F8_128:
+    case KID_FAST_F8_128_K64:
     case KID_FAST_GU_F8: return launch_fast_f8(kid, in_kind, out_kind, args, grid, stream, lds_image);
     default: return hipErrorInvalidValue;
   }

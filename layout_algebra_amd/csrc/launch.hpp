@@ -74,6 +74,7 @@ enum KernelId : int {
   KID_FAST_F8_128 = 26,  // KID_FAST_128_KM on byte pairs (one-byte inputs)
   KID_FAST_128_KM64 = 27,  // KID_FAST_128_KM with K blocks of 64 (128-byte row segments of A and B)
   KID_FAST_128_K64 = 28,   // KID_FAST_128 with K blocks of 64 (128-byte row segments of A)
+  KID_FAST_F8_128_K64 = 29,  // KID_FAST_128_KM64 on byte pairs (K blocks of 128 codes)
   KID_COUNT
 };
 

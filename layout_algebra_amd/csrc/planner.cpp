@@ -71,7 +71,7 @@ bool fast_kid(int kid) {
   return kid == lak::KID_FAST_256 || kid == lak::KID_FAST_GU || kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM ||
          kid == lak::KID_FAST_256_AT || kid == lak::KID_FAST_GU_AT || kid == lak::KID_FAST_F8 || kid == lak::KID_FAST_GU_F8 ||
          kid == lak::KID_FAST_128 || kid == lak::KID_FAST_128_KM || kid == lak::KID_FAST_F8_128 ||
-         kid == lak::KID_FAST_128_KM64 || kid == lak::KID_FAST_128_K64;
+         kid == lak::KID_FAST_128_KM64 || kid == lak::KID_FAST_128_K64 || kid == lak::KID_FAST_F8_128_K64;
 }
 
 bool skinny_kid(int kid) {
@@ -641,7 +641,7 @@ std::string describe(const gemm_plan_s& p) {
                                       "fast_gate_up_f8", "skinny_bkmajor", "skinny_f8", "skinny", "skinny",
                                       "skinny_bkmajor", "skinny_bkmajor", "skinny_f8", "skinny_f8", "skinny",
                                       "skinny_bkmajor", "skinny_f8", "fast", "fast_bkmajor", "fast_f8",
-                                      "fast_bkmajor", "fast"};
+                                      "fast_bkmajor", "fast", "fast_f8"};
   static_assert(sizeof(kNames) / sizeof(kNames[0]) == lak::KID_COUNT, "one name per kernel id");
   js << "{\"kernel\":\"" << kNames[p.kid] << "_" << s.bm << "x" << s.bn << "x" << s.bk << "\""
      << ",\"m\":" << d.m << ",\"n\":" << d.n << ",\"k\":" << d.k
@@ -694,8 +694,6 @@ bool is_f8(int32_t t) { return t == GEMM_F8E4M3 || t == GEMM_F8E5M2; }
 // plus its position in the pair.  The 64-code rows of a K block are the
 // 64-byte swizzle rows of the Tylo.jl page "TMA and Hopper WGMMA" (section
 // "The same storage contract on both sides"), Swizzle{2,4,4}.
-static gemm_status build_impl(const gemm_desc& d, gemm_plan_s& p, std::string* err, bool pair_view);
-
 static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   auto unsupported = [&](const char* m) { fail(err, m); return GEMM_ERR_UNSUPPORTED; };
   if (!is_f8(d.a_type) || !is_f8(d.b_type))
@@ -722,13 +720,14 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   // 128-row tiles, the skinny kernels), else the full-tile kernel at every grid size.
   auto has_f8_form = [](int kid) {
     return kid == lak::KID_FAST_256_KM || kid == lak::KID_FAST_GU_KM || kid == lak::KID_FAST_128_KM ||
+           kid == lak::KID_FAST_128_KM64 ||
            kid == lak::KID_SKINNY_16_KM || kid == lak::KID_SKINNY_32_KM || kid == lak::KID_SKINNY_64_KM ||
            kid == lak::KID_SKINNY_128_KM;
   };
-  gemm_status st = build_impl(v, p, err, true);
+  gemm_status st = build(v, p, err);
   if (st != GEMM_OK || !has_f8_form(p.kid)) {
     v.flags |= GEMM_FLAG_LARGE_TILES;
-    st = build_impl(v, p, err, true);
+    st = build(v, p, err);
   }
   if (st != GEMM_OK) return st;
   const bool runs = d.m > 0 && d.n > 0 && d.k > 0;
@@ -736,6 +735,7 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   int pair_kid = p.gate_up ? lak::KID_FAST_GU_KM : lak::KID_FAST_256_KM;
   int kid8 = p.gate_up ? lak::KID_FAST_GU_F8 : lak::KID_FAST_F8;
   if (p.kid == lak::KID_FAST_128_KM) pair_kid = p.kid, kid8 = lak::KID_FAST_F8_128;
+  if (p.kid == lak::KID_FAST_128_KM64) pair_kid = p.kid, kid8 = lak::KID_FAST_F8_128_K64;
   if (p.kid == lak::KID_SKINNY_16_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8;
   if (p.kid == lak::KID_SKINNY_32_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_32;
   if (p.kid == lak::KID_SKINNY_64_KM) pair_kid = p.kid, kid8 = lak::KID_SKINNY_F8_64;
@@ -814,11 +814,7 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
   return GEMM_OK;
 }
 
-gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) { return build_impl(d, p, err, false); }
-
-// pair_view: d is the 16-bit view of a one-byte request (build_f8), which keeps to the kernels
-// that have a one-byte form
-static gemm_status build_impl(const gemm_desc& d, gemm_plan_s& p, std::string* err, bool pair_view) {
+gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
   p = gemm_plan_s{};
   p.d = d;
   p.kd = d;
@@ -969,9 +965,9 @@ static gemm_status build_impl(const gemm_desc& d, gemm_plan_s& p, std::string* e
     // 4096^3 109.4 -> 136.5).
     if (!large && (p.kid == lak::KID_FAST_256 || p.kid == lak::KID_FAST_256_KM) && ftm * ftn * d.batch <= 128)
       p.kid = kmajor ? lak::KID_FAST_128_KM : lak::KID_FAST_128;
-    // with K a multiple of 64, K blocks of 64 (longer row segments per block; the one-byte pair
-    // view keeps blocks of 32 pairs, whose 64-code products take two 16-pair sub-steps)
-    if (!pair_view && d.k % 64 == 0 && (p.kid == lak::KID_FAST_128 || p.kid == lak::KID_FAST_128_KM))
+    // with K a multiple of 64, K blocks of 64 (longer row segments per block; for the one-byte pair
+    // view 64 pairs, 128 codes)
+    if (d.k % 64 == 0 && (p.kid == lak::KID_FAST_128 || p.kid == lak::KID_FAST_128_KM))
       p.kid = kmajor ? lak::KID_FAST_128_KM64 : lak::KID_FAST_128_K64;
     // M <= 128: stream B once through the skinny kernel with 16, 32, 64 or 128 rows of A
     // (HBM-bound shapes); B stored [N, K] streams strips of K-contiguous rows.  With more than 32

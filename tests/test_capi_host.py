@@ -352,10 +352,10 @@ def test_fast_split_form_and_padding_rule():
     assert plan(192, 11008, 4096)["kernel"].startswith("tiled_64x64")           # 43 tiles
     assert plan(320, 28672, 8192)["kernel"].startswith("tiled_64x64")           # padding 1.6
     d = la.gemm_plan(512, 4096, 14336, la.F8E4M3, la.BF16, b_kmajor=True).describe()
-    assert d["kernel"] == "fast_f8_128x256x64" and d["split_k"] == 4 and d["split_kernel"] == "fast_f8_256x256x64"
+    assert d["kernel"] == "fast_f8_128x256x128" and d["split_k"] == 4 and d["split_kernel"] == "fast_f8_256x256x64"
     assert plan(192, 28672, 8192)["kernel"] == "fast_128x256x64"                 # 112 tiles of 256 rows
     f8 = lambda m, n, k: la.gemm_plan(m, n, k, la.F8E4M3, la.BF16, b_kmajor=True).describe()["kernel"]
-    assert f8(1024, 4096, 2048) == "fast_f8_128x256x64" and f8(4096, 4096, 4096) == "fast_f8_256x256x64"
+    assert f8(1024, 4096, 2048) == "fast_f8_128x256x128" and f8(1024, 4096, 1040) == "fast_f8_128x256x64" and f8(4096, 4096, 4096) == "fast_f8_256x256x64"
     assert f8(256, 256, 64) == "fast_f8_256x256x64"                             # small grid: no one-byte general kernel
     assert plan(1000, 4096, 1000, True)["kernel"] == "fast_bkmajor_128x256x32"  # K not a multiple of 64
     assert plan(2048, 4096, 4096, True)["kernel"] == "fast_bkmajor_128x256x64"   # 128 tiles
