@@ -747,6 +747,8 @@ static gemm_status build_f8(const gemm_desc& d, gemm_plan_s& p, std::string* err
     const int sk = p.split_kid;
     p.split_kid = sk == lak::KID_SKINNY_16_KM ? lak::KID_SKINNY_F8
                 : sk == lak::KID_FAST_256_KM ? lak::KID_FAST_F8
+                : sk == lak::KID_FAST_128_KM ? lak::KID_FAST_F8_128
+                : sk == lak::KID_FAST_128_KM64 ? lak::KID_FAST_F8_128_K64
                 : sk == lak::KID_SKINNY_32_KM ? lak::KID_SKINNY_F8_32
                 : sk == lak::KID_SKINNY_64_KM ? lak::KID_SKINNY_F8_64
                 : sk == lak::KID_SKINNY_128_KM ? lak::KID_SKINNY_F8_128 : -1;
@@ -1011,23 +1013,35 @@ gemm_status build(const gemm_desc& d, gemm_plan_s& p, std::string* err) {
         p.ws_bytes = int64_t(split) * d.m * d.n * 4;
       }
     }
-    // Split K for the 256-wide kernel on grids of at most 64 tiles (a single matrix the skinny
-    // kernel does not take): the smallest power-of-two split count that gives 128 workgroups or
-    // more (at most 8), each range whole K blocks, at least 8 of them; FP32 partials in rows of n
-    // values (n % 8 == 0: the kernel's 8-value row chunks).  Measured on one box, single pass -> split (partials + a library sum)
-    // against torch.matmul, us: 512 x 4096 x 14336 240 -> 91 (4 ranges; 8: 97) | 85;
-    // 256 x 4096 x 14336 99 (general kernel) -> 60 (8; 16: 77) | 52; 1024 x 4096 x 14336 240 -> 154
-    // (2; 4: 147) | 123; 256 x 11008 x 4096 74 -> 58 (2; 4: 58) | 40; with 86 tiles and more no gain
-    // (512 x 11008 x 4096 77 -> 83, 256 x 28672 x 8192 206 -> 193, 512 x 28672 x 8192 226 -> 303).
-    const int64_t ftiles = ftm * ftn;
+    // Split K for the full-tile kernel on grids of at most 128 tiles of 256 x 256 (a single matrix
+    // the skinny kernel does not take), on 128-row tiles: the largest power-of-two split count (at
+    // most 8) that keeps 128-row tiles x split within 256 workgroups and gives each range at least
+    // 1024 of K in whole K blocks (of 64 when K allows, else of 32); FP32 partials in rows of n values (n % 8
+    // == 0: the kernel's 8-value row chunks).  Measured on one box (bf16, partials + a library sum
+    // against the 256-row split, us, B [N, K] / [K, N]): 512 x 4096 x 14336 4 ranges 71.6 + 8 /
+    // 72.9 + 8 against 88.0 / 83.5; 1024 x 4096 x 14336 2 ranges 120.5 + 8 against 147.7;
+    // 256 x 11008 x 4096 2 ranges 40.2 + 8 against 51.3; 256 x 4096 x 14336 8 ranges 47.2 + 8
+    // against 55.7.  Earlier, on 256-row tiles: 512 x 4096 x 14336 240 (single pass) -> 91 against
+    // torch.matmul 85; grids of 86 tiles of 256 and more gained nothing (512 x 11008 x 4096 77 ->
+    // 83), where 128-row tiles x 2 exceed 256 workgroups anyway.
+    const int64_t ftiles = ftm * ftn, htm = (d.m + 127) / 128;
     if (p.split == 1 && !p.gate_up && !atrans && d.batch == 1 && (whole || edges) && in16 && off32 &&
-        d.n % 8 == 0 && ftiles <= 64) {
+        d.n % 8 == 0 && ftiles <= 128) {
       int split = 1;
-      while (ftiles * split < 128 && split < 8) split *= 2;
-      if (split > 1 && d.k % (int64_t(fs.bk) * split) == 0 && d.k / (int64_t(fs.bk) * split) >= 8) {
+      while (split < 8 && htm * ftn * split * 2 <= 256) split *= 2;
+      // the largest such count whose ranges are whole K blocks (of 64 first) and at least 1024 deep
+      // (shorter ranges do not repay the partial sums' traffic and second launch)
+      bool k64 = false;
+      for (; split > 1; split /= 2) {
+        if (d.k / split < 1024) continue;
+        if (d.k % (int64_t(64) * split) == 0) { k64 = true; break; }
+        if (d.k % (int64_t(32) * split) == 0) break;
+      }
+      if (split > 1) {
         p.split = split;
-        p.split_kid = fk;
-        p.split_tiles_m = static_cast<int>(ftm);
+        p.split_kid = kmajor ? (k64 ? lak::KID_FAST_128_KM64 : lak::KID_FAST_128_KM)
+                             : (k64 ? lak::KID_FAST_128_K64 : lak::KID_FAST_128);
+        p.split_tiles_m = static_cast<int>(htm);
         p.split_tiles_n = static_cast<int>(ftn);
         p.ws_bytes = int64_t(split) * d.m * d.n * 4;
       }

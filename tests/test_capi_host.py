@@ -305,8 +305,8 @@ def test_skinny_rows_and_grid_guard():
 
 def test_split_form_workspace_bound():
     """Every split form the planner makes fits the 64 MiB array of gemm_run_split_noalloc:
-    workspace = split * m * n * 4 with fewer than 256 workgroups of at most 256 x 256 outputs (skinny
-    strips x split at most 256, 512 for 16 rows; 256-wide tiles x split below 256)."""
+    workspace = split * m * n * 4 with at most 256 workgroups of at most 128 x 256 outputs (skinny
+    strips x split at most 256, 512 for 16 rows; 128-row tiles x split at most 256)."""
     worst = 0
     kinds = set()
     for m in (1, 16, 17, 32, 33, 64, 65, 100, 128, 129, 192, 256, 300, 512, 1000, 1024, 2048):
@@ -325,8 +325,9 @@ def test_split_form_workspace_bound():
                         if sk.startswith("skinny"):
                             assert m <= 128 and wgs <= (512 if sk.startswith(("skinny_bkmajor_16x", "skinny_f8_16x")) else 256), d
                         else:
-                            assert sk.startswith("fast_") and d["split_grid"][0] <= 64 and wgs < 256, d
+                            assert sk.startswith(("fast_128x256", "fast_bkmajor_128x256")) and wgs <= 256, d
                             assert d["split_k"] <= 8 and k % (32 * d["split_k"]) == 0 and n % 8 == 0, d
+                            assert k // d["split_k"] >= 1024 and k % (d["split_k"] * int(sk.rsplit("x", 1)[1])) == 0, d
                     worst = max(worst, d["workspace_bytes"])
     assert kinds == {"skinny", "fast"}
     assert 0 < worst <= 64 << 20
@@ -338,21 +339,25 @@ def test_fast_split_form_and_padding_rule():
     def plan(m, n, k, km=False):
         return la.gemm_plan(m, n, k, la.BF16, la.BF16, b_kmajor=km).describe()
     d = plan(512, 4096, 14336, True)
-    assert d["kernel"] == "fast_bkmajor_128x256x64" and d["split_k"] == 4 and d["split_grid"] == [32, 4]
-    assert d["split_kernel"] == "fast_bkmajor_256x256x32"
+    assert d["kernel"] == "fast_bkmajor_128x256x64" and d["split_k"] == 4 and d["split_grid"] == [64, 4]
+    assert d["split_kernel"] == "fast_bkmajor_128x256x64"
     d = plan(256, 4096, 14336)
-    assert d["kernel"].startswith("tiled_64x64") and d["split_k"] == 8 and d["split_kernel"] == "fast_256x256x32"
+    assert d["kernel"].startswith("tiled_64x64") and d["split_k"] == 8 and d["split_kernel"] == "fast_128x256x64"
+    d = plan(300, 520, 2048)                                                     # ranges of 1024
+    assert d["split_k"] == 2 and d["split_kernel"] == "fast_128x256x64" and d["split_grid"] == [9, 2]
+    d = plan(300, 520, 2112)                                                     # ranges of 33 blocks of 32
+    assert d["split_k"] == 2 and d["split_kernel"] == "fast_128x256x32"
     d = plan(1024, 4096, 14336)
-    assert d["split_k"] == 2 and d["split_grid"] == [64, 2]
-    assert plan(512, 11008, 4096)["split_k"] == 1                               # 86 tiles
+    assert d["split_k"] == 2 and d["split_grid"] == [128, 2]
+    assert plan(512, 11008, 4096)["split_k"] == 1                               # 172 tiles of 128 rows
     assert plan(4096, 4096, 4096)["split_k"] == 1
-    assert plan(512, 4096, 512)["split_k"] == 1                                 # ranges under 8 K blocks
+    assert plan(512, 4096, 512)["split_k"] == 1                                 # ranges under 1024
     assert plan(384, 28672, 8192)["kernel"].startswith("fast_256x256")          # 224 tiles, padding 4/3
     assert plan(384, 11008, 4096)["kernel"].startswith("fast_128x256")          # 86 tiles of 256 rows
     assert plan(192, 11008, 4096)["kernel"].startswith("tiled_64x64")           # 43 tiles
     assert plan(320, 28672, 8192)["kernel"].startswith("tiled_64x64")           # padding 1.6
     d = la.gemm_plan(512, 4096, 14336, la.F8E4M3, la.BF16, b_kmajor=True).describe()
-    assert d["kernel"] == "fast_f8_128x256x128" and d["split_k"] == 4 and d["split_kernel"] == "fast_f8_256x256x64"
+    assert d["kernel"] == "fast_f8_128x256x128" and d["split_k"] == 4 and d["split_kernel"] == "fast_f8_128x256x128"
     assert plan(192, 28672, 8192)["kernel"] == "fast_128x256x64"                 # 112 tiles of 256 rows
     f8 = lambda m, n, k: la.gemm_plan(m, n, k, la.F8E4M3, la.BF16, b_kmajor=True).describe()["kernel"]
     assert f8(1024, 4096, 2048) == "fast_f8_128x256x128" and f8(1024, 4096, 1040) == "fast_f8_128x256x64" and f8(4096, 4096, 4096) == "fast_f8_256x256x64"

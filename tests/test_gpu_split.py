@@ -5,8 +5,8 @@ caller-owned workspace (one launch, ranges along the grid's y dimension) and a
 second kernel sums the ranges in order with alpha, beta and the rounding.  Only
 the order of the FP32 additions differs from a single pass, so the bound is the
 plain GEMM's (tests/parity.py).  Cases: the skinny kernel's split form for 1 to
-128 rows of A and the 256-wide kernel's (at most 64 tiles, M and N edges, one-byte
-inputs, a 512 x 4096 x 14336 prefill shape on sampled rows), both storages of B,
+128 rows of A and the full-tile kernel's on 128-row tiles (M and N edges, K blocks of
+64 and 32, one-byte inputs, a 512 x 4096 x 14336 prefill shape on sampled rows), both storages of B,
 bf16 / fp16 inputs with fp32 / bf16 / fp16 outputs, alpha and beta with C in
 padded rows that must stay untouched, one-byte inputs, the skinny_split workload
 (32 x 4096 x 14336, B stored [N, K]) in full, determinism, the workspace
@@ -82,6 +82,7 @@ FAST = [
     # (M, N, K, B stored [N, K]): the 256-wide kernel's split form (at most 64 tiles)
     (256, 1024, 4096, False),
     (300, 520, 2048, False),      # M and N edges
+    (300, 520, 2112, True),       # ranges of 1056: K blocks of 32
     (129, 4096, 2048, True),      # one row past the skinny range, M edge
     (1000, 1024, 4096, True),
     (512, 2048, 8192, False),
@@ -109,7 +110,7 @@ def test_fast_split_prefill_shape_sampled_rows():
     a = synth.normal((M, K), 551, "bf16")
     b = synth.normal((K, N), 552, "bf16", 0.02)
     got, d = run_split(a, b, "bf16", "bf16", True)
-    assert d["split_k"] == 4 and d["split_grid"] == [32, 4], d
+    assert d["split_k"] == 4 and d["split_grid"] == [64, 4] and d["split_kernel"] == "fast_bkmajor_128x256x64", d
     rows = band_rows(M, seed=553)
     ref = oracle_gemm(a, b, "bf16", rows=rows)
     assert_close(got[rows], ref, K, a, b, "bf16", "fast split prefill shape")
@@ -120,7 +121,7 @@ def test_fast_split_one_byte():
     a = synth.normal((M, K), 561, "f8e4m3", 1.0)
     b = synth.normal((K, N), 562, "f8e5m2", 0.5)
     got, d = run_split(a, b, "f8e4m3", "bf16", True, b_kind="f8e5m2")
-    assert d["split_k"] > 1 and d["split_kernel"] == "fast_f8_256x256x64", d
+    assert d["split_k"] > 1 and d["split_kernel"].startswith("fast_f8_128x256x"), d
     ref = oracle_gemm(a, b, "f8e4m3", b_kind="f8e5m2")
     assert_close(got, ref, K, a, b, "bf16", "fast split f8")
 
