@@ -162,8 +162,9 @@ gemm_status gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out_bytes);
  * the FP32 additions differs from gemm_run (deterministic: the same inputs
  * give the same bits).  The planner gives a plan a split form where a single
  * matrix's grid leaves most CUs idle: the skinny shapes (m <= 128, B streamed
- * once) on few column strips, and other shapes with at most 64 tiles of the
- * 256-wide kernel (n a multiple of 8, K cut into whole K blocks).  One launch writes the ranges'
+ * once) on few column strips, and other shapes with at most 128 tiles of the
+ * 256-wide kernel, split on 128-row tiles (n a multiple of 8, K cut into
+ * ranges of whole K blocks, at least 1024 deep).  One launch writes the ranges'
  * products into `workspace` (split slices of m x n FP32 values), a second sums
  * them into C with alpha, beta and the rounding.
  * `workspace` is a device buffer of at least gemm_plan_workspace_bytes bytes,

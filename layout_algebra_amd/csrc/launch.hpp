@@ -210,7 +210,7 @@ hipError_t launch_split_sum(const float* P, int S, int64_t M, int64_t N, void* C
                             float alpha, float beta, hipStream_t stream);
 
 // Bytes of the per-GPU workspace array behind gemm_run_split_noalloc: the largest split form the
-// planner makes (fewer than 256 workgroups of at most 256 x 256 FP32 values each).
+// planner makes (at most 256 workgroups of at most 128 x 256 FP32 values each) with room to spare.
 constexpr int64_t kSplitScratchBytes = int64_t(64) << 20;
 
 // Device address of the current device's workspace array (looked up once per device).
