@@ -116,12 +116,15 @@ def test_fast_split_prefill_shape_sampled_rows():
     assert_close(got[rows], ref, K, a, b, "bf16", "fast split prefill shape")
 
 
-def test_fast_split_one_byte():
-    M, N, K = 512, 2048, 4096
+@pytest.mark.parametrize("K,blk", [(4096, 128), (4224, 64)], ids=["blocks128", "blocks64"])
+def test_fast_split_one_byte(K, blk):
+    """One-byte split forms on 128-row tiles: ranges of 1024 pairs (blocks of 128 codes) and of 1056
+    pairs (blocks of 64 codes)."""
+    M, N = 512, 2048
     a = synth.normal((M, K), 561, "f8e4m3", 1.0)
     b = synth.normal((K, N), 562, "f8e5m2", 0.5)
     got, d = run_split(a, b, "f8e4m3", "bf16", True, b_kind="f8e5m2")
-    assert d["split_k"] > 1 and d["split_kernel"].startswith("fast_f8_128x256x"), d
+    assert d["split_k"] == 2 and d["split_kernel"] == "fast_f8_128x256x%d" % blk, d
     ref = oracle_gemm(a, b, "f8e4m3", b_kind="f8e5m2")
     assert_close(got, ref, K, a, b, "bf16", "fast split f8")
 
